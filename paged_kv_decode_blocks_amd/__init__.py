@@ -1,0 +1,246 @@
+"""paged_kv_decode_blocks_amd -- paged-KV decode attention for AMD MI355X (gfx950).
+
+A thin ctypes binding over ``libpkv.so``, whose C ABI is declared in
+``include/pkv.h``.  This module only marshals arguments: it turns torch tensors
+into device pointers, element strides and the current HIP stream, and raises
+on a non-OK status.  Every step of the computation runs in the library's HIP
+kernels; there is no CPU or PyTorch fallback, and a missing library is an error.
+
+Entry points (same names as the C ABI without the ``pkv_`` prefix):
+  kv_append                 write each request's new K/V token into its slot
+  paged_decode_attention    attention of one query per head over the paged history
+  append_decode_attention   both, as one decode step (single attention launch)
+  decode_workspace_bytes    workspace size of a split-KV call
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "PkvError", "LIB_PATH", "load_library", "library_loaded", "kv_append", "paged_decode_attention",
+    "append_decode_attention", "decode_workspace_bytes", "last_launch", "version",
+    "PKV_F32", "PKV_F16", "PKV_BF16", "EXPORTED_SYMBOLS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkv.so")
+
+PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+BLOCK_SIZE = 16
+
+EXPORTED_SYMBOLS = (
+    "pkv_version", "pkv_status_string", "pkv_last_error", "pkv_last_launch", "pkv_kv_append",
+    "pkv_decode_workspace_bytes", "pkv_paged_decode_attention", "pkv_append_decode_attention",
+)
+
+_lib = None
+
+
+class PkvError(RuntimeError):
+    """A libpkv call returned a non-OK status (or the library is missing)."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def load_library(path: Optional[str] = None):
+    """Load libpkv.so (built in-tree by ``build.py``) and declare its signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise PkvError(-100, f"libpkv.so not found at {p}; build it with paged_kv_decode_blocks_amd.build.build()")
+    lib = ctypes.CDLL(p)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.pkv_version.argtypes = []
+    lib.pkv_version.restype = ctypes.c_int
+    lib.pkv_status_string.argtypes = [ctypes.c_int]
+    lib.pkv_status_string.restype = ctypes.c_char_p
+    lib.pkv_last_error.argtypes = []
+    lib.pkv_last_error.restype = ctypes.c_char_p
+    lib.pkv_last_launch.argtypes = []
+    lib.pkv_last_launch.restype = ctypes.c_char_p
+    lib.pkv_kv_append.argtypes = [ctypes.c_int, P, P, I64, P, P, P, I32, P, I32, I32, I32, I32, I32, P]
+    lib.pkv_kv_append.restype = ctypes.c_int
+    lib.pkv_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
+    lib.pkv_decode_workspace_bytes.restype = SZ
+    lib.pkv_paged_decode_attention.argtypes = [ctypes.c_int, P, P, I64, P, P, P, I32, P,
+                                               I32, I32, I32, I32, I32, I32, I32, ctypes.c_float, I32,
+                                               P, SZ, P]
+    lib.pkv_paged_decode_attention.restype = ctypes.c_int
+    lib.pkv_append_decode_attention.argtypes = [ctypes.c_int, P, P, I64, P, P, I64, P, P, P, I32, P,
+                                                I32, I32, I32, I32, I32, I32, I32, ctypes.c_float, I32,
+                                                P, SZ, P]
+    lib.pkv_append_decode_attention.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def library_loaded() -> bool:
+    return _lib is not None
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        lib = load_library()
+        raise PkvError(rc, f"{what}: {lib.pkv_status_string(rc).decode()}: {lib.pkv_last_error().decode()}")
+
+
+def version() -> int:
+    return int(load_library().pkv_version())
+
+
+def last_launch() -> str:
+    return load_library().pkv_last_launch().decode()
+
+
+def decode_workspace_bytes(B: int, H_q: int, D: int, max_context_len: int, partition_size: int) -> int:
+    return int(load_library().pkv_decode_workspace_bytes(B, H_q, D, max_context_len, partition_size))
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
+    if t.dtype not in m:
+        raise PkvError(-3, f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _require(cond: bool, msg: str):
+    if not cond:
+        raise PkvError(-2, msg)
+
+
+def _rows(t, name: str, heads: int, D: int):
+    """Row stride (elements) of a [B, heads, D] view whose heads are D apart and elements contiguous."""
+    _require(t.dim() == 3 and t.shape[1] == heads and t.shape[2] == D, f"{name} must be [B, {heads}, {D}]")
+    _require(t.stride(2) == 1 and (heads == 1 or t.stride(1) == D), f"{name}: heads must be contiguous rows of D")
+    return t.stride(0) if t.shape[0] > 1 else heads * D
+
+
+def _pool_dims(k_pool, v_pool):
+    _require(k_pool.dim() == 4 and k_pool.shape == v_pool.shape, "k_pool/v_pool must be [n_blocks, H_kv, 16, D]")
+    _require(k_pool.is_contiguous() and v_pool.is_contiguous(), "pools must be contiguous")
+    _require(k_pool.dtype == v_pool.dtype, "k_pool and v_pool dtypes differ")
+    n_blocks, H_kv, bs, D = k_pool.shape
+    return n_blocks, H_kv, bs, D
+
+
+def _int32_2d(t, name):
+    torch = _torch()
+    _require(t.dtype == torch.int32 and t.dim() == 2 and t.stride(1) == 1, f"{name} must be int32 [B, W] rows")
+    return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], 1)
+
+
+def _int32_1d(t, name, B):
+    torch = _torch()
+    _require(t.dtype == torch.int32 and t.dim() == 1 and t.shape[0] == B and (B <= 1 or t.stride(0) == 1),
+             f"{name} must be contiguous int32 [B]")
+
+
+def kv_append(k_new, v_new, k_pool, v_pool, block_tables, positions, *, stream=None):
+    """Write k_new/v_new [B, H_kv, D] into slot positions[b] of each request's block (bit copy)."""
+    n_blocks, H_kv, bs, D = _pool_dims(k_pool, v_pool)
+    B = k_new.shape[0]
+    _require(k_new.dtype == k_pool.dtype and v_new.dtype == k_pool.dtype, "k_new/v_new dtype must match the pools")
+    rs = _rows(k_new, "k_new", H_kv, D)
+    _require(_rows(v_new, "v_new", H_kv, D) == rs, "k_new and v_new must share a row stride")
+    bts = _int32_2d(block_tables, "block_tables")
+    _int32_1d(positions, "positions", B)
+    rc = load_library().pkv_kv_append(_dtype_code(k_pool), _ptr(k_new), _ptr(v_new), rs, _ptr(k_pool), _ptr(v_pool),
+                                      _ptr(block_tables), bts, _ptr(positions), B, H_kv, D, bs, n_blocks,
+                                      _stream(stream))
+    _check(rc, "kv_append")
+
+
+def _workspace(B, H_q, D, max_context_len, partition_size, workspace, device):
+    need = decode_workspace_bytes(B, H_q, D, max_context_len, partition_size)
+    if need == 0:
+        return None, 0
+    if workspace is None:
+        torch = _torch()
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def paged_decode_attention(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_context_len: int,
+                           *, partition_size: int = 0, out=None, workspace=None, stream=None):
+    """out[b, h, :] = softmax(scale * q[b, h] . K_t) V over the request's context_lens[b] paged tokens (float32).
+
+    ``max_context_len`` is a host-known bound on context_lens.  With
+    ``partition_size`` > 0 the context is split and merged by log-sum-exp; a
+    workspace is allocated here unless one is passed (pass one to keep the
+    call allocation-free).
+    """
+    torch = _torch()
+    n_blocks, H_kv, bs, D = _pool_dims(k_pool, v_pool)
+    B, H_q = q.shape[0], q.shape[1]
+    _require(q.dtype == k_pool.dtype, "q dtype must match the pools")
+    qrs = _rows(q, "q", H_q, D)
+    bts = _int32_2d(block_tables, "block_tables")
+    _int32_1d(context_lens, "context_lens", B)
+    if out is None:
+        out = torch.empty((B, H_q, D), dtype=torch.float32, device=q.device)
+    _require(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, H_q, D),
+             "out must be contiguous float32 [B, H_q, D]")
+    ws, ws_bytes = _workspace(B, H_q, D, max_context_len, partition_size, workspace, q.device)
+    rc = load_library().pkv_paged_decode_attention(
+        _dtype_code(q), _ptr(out), _ptr(q), qrs, _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), bts,
+        _ptr(context_lens), B, H_q, H_kv, D, bs, n_blocks, int(max_context_len), float(scale),
+        int(partition_size), _ptr(ws), ws_bytes, _stream(stream))
+    _check(rc, "paged_decode_attention")
+    return out
+
+
+def append_decode_attention(q, k_new, v_new, k_pool, v_pool, block_tables, positions, scale: float,
+                            max_context_len: int, *, partition_size: int = 0, out=None, workspace=None,
+                            stream=None):
+    """One decode step: write the new token at positions[b], attend over positions[b] + 1 tokens."""
+    torch = _torch()
+    n_blocks, H_kv, bs, D = _pool_dims(k_pool, v_pool)
+    B, H_q = q.shape[0], q.shape[1]
+    for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new")):
+        _require(t.dtype == k_pool.dtype, f"{nm} dtype must match the pools")
+    qrs = _rows(q, "q", H_q, D)
+    nrs = _rows(k_new, "k_new", H_kv, D)
+    _require(_rows(v_new, "v_new", H_kv, D) == nrs, "k_new and v_new must share a row stride")
+    bts = _int32_2d(block_tables, "block_tables")
+    _int32_1d(positions, "positions", B)
+    if out is None:
+        out = torch.empty((B, H_q, D), dtype=torch.float32, device=q.device)
+    _require(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, H_q, D),
+             "out must be contiguous float32 [B, H_q, D]")
+    ws, ws_bytes = _workspace(B, H_q, D, max_context_len, partition_size, workspace, q.device)
+    rc = load_library().pkv_append_decode_attention(
+        _dtype_code(q), _ptr(out), _ptr(q), qrs, _ptr(k_new), _ptr(v_new), nrs, _ptr(k_pool), _ptr(v_pool),
+        _ptr(block_tables), bts, _ptr(positions), B, H_q, H_kv, D, bs, n_blocks, int(max_context_len),
+        float(scale), int(partition_size), _ptr(ws), ws_bytes, _stream(stream))
+    _check(rc, "append_decode_attention")
+    return out

@@ -1,0 +1,307 @@
+// api.cpp -- the C ABI of libpkv (declared in include/pkv.h).
+//
+// Host-side only: argument validation, launch geometry and dispatch to the
+// gfx950 kernels.  Nothing here synchronises, copies device memory to the host
+// or allocates; every kernel is enqueued on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "pkv.h"
+#include "pkv_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+thread_local char g_launch[256] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int elem_bytes(int dtype) {
+    switch (dtype) {
+    case PKV_F32: return 4;
+    case PKV_F16: return 2;
+    case PKV_BF16: return 2;
+    default: return 0;
+    }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int env_int(const char* name, int fallback) {
+    const char* v = getenv(name);
+    if (!v || !*v) return fallback;
+    return atoi(v);
+}
+
+constexpr int32_t kMaxContext = 1 << 24;   // keeps every token index well inside int32
+
+struct Plan {
+    int32_t part_tokens;
+    int32_t n_parts;
+    bool grouped;     // matrix-core path (one workgroup per KV head and G query heads)
+    int nw, ch;
+    unsigned grid;
+    size_t ws_o, ws_lse, ws_total;
+};
+
+// Launch geometry.  Unsplit: one partition spanning the padded context.
+Plan make_plan(int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t max_ctx, int32_t partition_size) {
+    Plan p{};
+    const int32_t padded = max_ctx <= 0 ? pkv::kBlockSize
+                                        : (max_ctx + pkv::kBlockSize - 1) / pkv::kBlockSize * pkv::kBlockSize;
+    if (partition_size <= 0 || partition_size >= padded) {
+        p.part_tokens = padded;
+        p.n_parts = 1;
+    } else {
+        p.part_tokens = partition_size;
+        p.n_parts = (max_ctx + partition_size - 1) / partition_size;
+    }
+    const int32_t G = H_q / H_kv;
+    p.grouped = G > 1 && dtype != PKV_F32;
+    const int32_t blocks = p.part_tokens / pkv::kBlockSize;
+    if (p.grouped) {
+        p.nw = env_int("PKV_GQA_NW", 4);
+        p.ch = env_int("PKV_GQA_CH", 1);
+        if (!pkv::gqa_variant_exists(p.nw, p.ch)) { p.nw = 4; p.ch = 1; }
+        p.grid = (unsigned)((int64_t)p.n_parts * B * H_kv);
+    } else {
+        int ch = 2;
+        int nw = 4;
+        while (nw < 16 && blocks >= 2 * nw * ch) nw *= 2;   // at least two chunks per wave before widening
+        p.nw = env_int("PKV_MHA_NW", nw);
+        p.ch = env_int("PKV_MHA_CH", ch);
+        if (!pkv::mha_variant_exists(p.nw, p.ch)) { p.nw = nw; p.ch = ch; }
+        p.grid = (unsigned)((int64_t)p.n_parts * B * H_q);
+    }
+    (void)D;
+    if (p.n_parts > 1) {
+        p.ws_o = align_up((size_t)B * H_q * p.n_parts * D * sizeof(float), 256);
+        p.ws_lse = align_up((size_t)B * H_q * p.n_parts * sizeof(float), 256);
+    }
+    p.ws_total = p.ws_o + p.ws_lse;
+    return p;
+}
+
+int check_common(int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t block_size, int32_t n_blocks,
+                 int32_t bt_stride, int32_t max_ctx, int32_t partition_size) {
+    if (!elem_bytes(dtype)) return fail(PKV_ERR_UNSUPPORTED, "dtype %d is not one of PKV_F32/F16/BF16", dtype);
+    if (B < 0) return fail(PKV_ERR_INVALID_ARG, "B = %d is negative", B);
+    if (H_q <= 0 || H_kv <= 0) return fail(PKV_ERR_INVALID_ARG, "H_q = %d, H_kv = %d must be positive", H_q, H_kv);
+    if (H_q % H_kv) return fail(PKV_ERR_INVALID_ARG, "H_q = %d is not a multiple of H_kv = %d", H_q, H_kv);
+    if (D != 64 && D != 128) return fail(PKV_ERR_UNSUPPORTED, "head dim D = %d (built: 64, 128)", D);
+    if (block_size != pkv::kBlockSize)
+        return fail(PKV_ERR_UNSUPPORTED, "block_size = %d (built: %d)", block_size, pkv::kBlockSize);
+    if (n_blocks <= 0) return fail(PKV_ERR_INVALID_ARG, "n_blocks = %d must be positive", n_blocks);
+    if (bt_stride <= 0) return fail(PKV_ERR_INVALID_ARG, "bt_stride = %d must be positive", bt_stride);
+    if (max_ctx < 0 || max_ctx > kMaxContext)
+        return fail(PKV_ERR_INVALID_ARG, "max_context_len = %d outside [0, %d]", max_ctx, kMaxContext);
+    if ((int64_t)max_ctx > (int64_t)bt_stride * block_size)
+        return fail(PKV_ERR_INVALID_ARG, "max_context_len = %d exceeds bt_stride*block_size = %lld", max_ctx,
+                    (long long)bt_stride * block_size);
+    if (partition_size < 0 || partition_size % block_size)
+        return fail(PKV_ERR_INVALID_ARG, "partition_size = %d must be 0 or a positive multiple of %d",
+                    partition_size, block_size);
+    const int32_t G = H_q / H_kv;
+    if (G > 16 && dtype != PKV_F32)
+        return fail(PKV_ERR_UNSUPPORTED, "G = H_q/H_kv = %d (the grouped path takes up to 16)", G);
+    return PKV_OK;
+}
+
+int check_stride(const char* name, int64_t stride, int64_t min_elems, int eb) {
+    if (stride < min_elems)
+        return fail(PKV_ERR_INVALID_ARG, "%s = %lld is smaller than %lld", name, (long long)stride, (long long)min_elems);
+    if ((stride * eb) % 16)
+        return fail(PKV_ERR_INVALID_ARG, "%s = %lld elements is not a multiple of 16 bytes", name, (long long)stride);
+    return PKV_OK;
+}
+
+int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride, const void* k_new, const void* v_new,
+                     int64_t new_row_stride, const void* k_pool, const void* v_pool, void* k_pool_w, void* v_pool_w,
+                     const int32_t* block_tables, int32_t bt_stride, const int32_t* context_lens,
+                     const int32_t* positions, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t block_size,
+                     int32_t n_blocks, int32_t max_ctx, float scale, int32_t partition_size, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    const bool fused = positions != nullptr;
+    int st = check_common(dtype, B, H_q, H_kv, D, block_size, n_blocks, bt_stride, max_ctx, partition_size);
+    if (st) return st;
+    if (B == 0) return PKV_OK;
+    const int eb = elem_bytes(dtype);
+    if (!out || !q || !k_pool || !v_pool || !block_tables) return fail(PKV_ERR_NULL, "a required pointer is NULL");
+    if (fused ? (!k_new || !v_new) : !context_lens) return fail(PKV_ERR_NULL, "a required pointer is NULL");
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
+        (fused && (!aligned16(k_new) || !aligned16(v_new))))
+        return fail(PKV_ERR_INVALID_ARG, "q, out, k_new, v_new and the pools must be 16-byte aligned");
+    if ((st = check_stride("q_row_stride", q_row_stride, (int64_t)H_q * D, eb))) return st;
+    if (fused && (st = check_stride("new_row_stride", new_row_stride, (int64_t)H_kv * D, eb))) return st;
+    if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
+
+    const Plan p = make_plan(dtype, B, H_q, H_kv, D, max_ctx, partition_size);
+    if ((int64_t)p.n_parts * B * (p.grouped ? H_kv : H_q) > 0x7fffffff)
+        return fail(PKV_ERR_INVALID_ARG, "grid too large");
+    if (p.ws_total) {
+        if (!workspace) return fail(PKV_ERR_WORKSPACE, "split needs %zu bytes of workspace, got NULL", p.ws_total);
+        if (workspace_bytes < p.ws_total)
+            return fail(PKV_ERR_WORKSPACE, "split needs %zu bytes of workspace, got %zu", p.ws_total, workspace_bytes);
+        if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+            return fail(PKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    }
+
+    pkv::AttnArgs a{};
+    a.out = out;
+    a.part_o = p.ws_total ? reinterpret_cast<float*>(workspace) : nullptr;
+    a.part_lse = p.ws_total ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + p.ws_o) : nullptr;
+    a.q = reinterpret_cast<const char*>(q);
+    a.k_pool = reinterpret_cast<const char*>(k_pool);
+    a.v_pool = reinterpret_cast<const char*>(v_pool);
+    a.k_pool_w = reinterpret_cast<char*>(k_pool_w);
+    a.v_pool_w = reinterpret_cast<char*>(v_pool_w);
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.positions = positions;
+    a.k_new = reinterpret_cast<const char*>(k_new);
+    a.v_new = reinterpret_cast<const char*>(v_new);
+    a.q_row_stride = q_row_stride;
+    a.new_row_stride = new_row_stride;
+    a.bt_stride = bt_stride;
+    a.B = B;
+    a.H_q = H_q;
+    a.H_kv = H_kv;
+    a.G = H_q / H_kv;
+    a.n_blocks = n_blocks;
+    a.max_context_len = max_ctx;
+    a.part_tokens = p.part_tokens;
+    a.n_parts = p.n_parts;
+    a.scale_log2 = scale * pkv::kLog2e;
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = p.grouped ? pkv::launch_decode_gqa(dtype, D, p.nw, p.ch, fused, a, p.grid, s)
+                             : pkv::launch_decode_mha(dtype, D, p.nw, p.ch, fused, a, p.grid, s);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
+    if (p.n_parts > 1) {
+        pkv::MergeArgs m{};
+        m.out = out;
+        m.part_o = a.part_o;
+        m.part_lse = a.part_lse;
+        m.context_lens = fused ? nullptr : context_lens;
+        m.positions = positions;
+        m.BH = B * H_q;
+        m.H_q = H_q;
+        m.n_parts = p.n_parts;
+        m.part_tokens = p.part_tokens;
+        m.max_context_len = max_ctx;
+        e = pkv::launch_lse_merge(D, m, s);
+        if (e != hipSuccess) return fail(PKV_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
+    }
+    snprintf(g_launch, sizeof g_launch, "%s dtype=%d D=%d nw=%d ch=%d grid=%u part_tokens=%d n_parts=%d%s",
+             p.grouped ? "gqa_mfma" : "mha", dtype, D, p.nw, p.ch, p.grid, p.part_tokens, p.n_parts,
+             fused ? " fused_append" : "");
+    g_err[0] = 0;
+    return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_version(void) { return 100; }
+
+const char* pkv_status_string(int status) {
+    switch (status) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_ERR_NULL: return "PKV_ERR_NULL";
+    case PKV_ERR_INVALID_ARG: return "PKV_ERR_INVALID_ARG";
+    case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED";
+    case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE";
+    case PKV_ERR_HIP: return "PKV_ERR_HIP";
+    default: return "PKV_UNKNOWN_STATUS";
+    }
+}
+
+const char* pkv_last_error(void) { return g_err; }
+
+const char* pkv_last_launch(void) { return g_launch; }
+
+int pkv_kv_append(int dtype, const void* k_new, const void* v_new, int64_t new_row_stride, void* k_pool, void* v_pool,
+                  const int32_t* block_tables, int32_t bt_stride, const int32_t* positions, int32_t B, int32_t H_kv,
+                  int32_t D, int32_t block_size, int32_t n_blocks, void* stream) {
+    const int eb = elem_bytes(dtype);
+    if (!eb) return fail(PKV_ERR_UNSUPPORTED, "dtype %d is not one of PKV_F32/F16/BF16", dtype);
+    if (B < 0) return fail(PKV_ERR_INVALID_ARG, "B = %d is negative", B);
+    if (H_kv <= 0) return fail(PKV_ERR_INVALID_ARG, "H_kv = %d must be positive", H_kv);
+    if (D != 64 && D != 128) return fail(PKV_ERR_UNSUPPORTED, "head dim D = %d (built: 64, 128)", D);
+    if (block_size != pkv::kBlockSize)
+        return fail(PKV_ERR_UNSUPPORTED, "block_size = %d (built: %d)", block_size, pkv::kBlockSize);
+    if (n_blocks <= 0) return fail(PKV_ERR_INVALID_ARG, "n_blocks = %d must be positive", n_blocks);
+    if (bt_stride <= 0) return fail(PKV_ERR_INVALID_ARG, "bt_stride = %d must be positive", bt_stride);
+    if (B == 0) return PKV_OK;
+    if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !positions)
+        return fail(PKV_ERR_NULL, "a required pointer is NULL");
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+        return fail(PKV_ERR_INVALID_ARG, "k_new, v_new and the pools must be 16-byte aligned");
+    int st = check_stride("new_row_stride", new_row_stride, (int64_t)H_kv * D, eb);
+    if (st) return st;
+    pkv::AppendArgs a{};
+    a.k_new = reinterpret_cast<const char*>(k_new);
+    a.v_new = reinterpret_cast<const char*>(v_new);
+    a.k_pool = reinterpret_cast<char*>(k_pool);
+    a.v_pool = reinterpret_cast<char*>(v_pool);
+    a.block_tables = block_tables;
+    a.positions = positions;
+    a.new_row_stride = new_row_stride;
+    a.bt_stride = bt_stride;
+    a.B = B;
+    a.H_kv = H_kv;
+    a.D = D;
+    a.elem_bytes = eb;
+    a.n_blocks = n_blocks;
+    hipError_t e = pkv::launch_kv_append(a, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "kv_append launch: %s", hipGetErrorString(e));
+    g_err[0] = 0;
+    return PKV_OK;
+}
+
+size_t pkv_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t D, int32_t max_context_len,
+                                  int32_t partition_size) {
+    if (B <= 0 || H_q <= 0 || D <= 0 || max_context_len <= 0 || partition_size <= 0) return 0;
+    // the KV-head count and dtype do not change the workspace
+    const Plan p = make_plan(PKV_F16, B, H_q, H_q, D, max_context_len, partition_size);
+    return p.ws_total;
+}
+
+int pkv_paged_decode_attention(int dtype, float* out, const void* q, int64_t q_row_stride, const void* k_pool,
+                               const void* v_pool, const int32_t* block_tables, int32_t bt_stride,
+                               const int32_t* context_lens, int32_t B, int32_t H_q, int32_t H_kv, int32_t D,
+                               int32_t block_size, int32_t n_blocks, int32_t max_context_len, float scale,
+                               int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+    return launch_attention(dtype, out, q, q_row_stride, nullptr, nullptr, 0, k_pool, v_pool, nullptr, nullptr,
+                            block_tables, bt_stride, context_lens, nullptr, B, H_q, H_kv, D, block_size, n_blocks,
+                            max_context_len, scale, partition_size, workspace, workspace_bytes, stream);
+}
+
+int pkv_append_decode_attention(int dtype, float* out, const void* q, int64_t q_row_stride, const void* k_new,
+                                const void* v_new, int64_t new_row_stride, void* k_pool, void* v_pool,
+                                const int32_t* block_tables, int32_t bt_stride, const int32_t* positions, int32_t B,
+                                int32_t H_q, int32_t H_kv, int32_t D, int32_t block_size, int32_t n_blocks,
+                                int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    if (B > 0 && !positions) return fail(PKV_ERR_NULL, "positions is NULL");
+    return launch_attention(dtype, out, q, q_row_stride, k_new, v_new, new_row_stride, k_pool, v_pool, k_pool, v_pool,
+                            block_tables, bt_stride, nullptr, B > 0 ? positions : nullptr, B, H_q, H_kv, D,
+                            block_size, n_blocks, max_context_len, scale, partition_size, workspace,
+                            workspace_bytes, stream);
+}
+
+}  // extern "C"

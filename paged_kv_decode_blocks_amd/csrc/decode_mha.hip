@@ -1,0 +1,272 @@
+// decode_mha.hip -- paged decode attention, one query head per workgroup.
+//
+// Decode attention reads each request's whole private K/V history once per
+// step and does about one flop per byte, so it is bound by HBM bandwidth
+// ("Injecting Adrenaline into LLM Serving" review, section 2.2: the decode
+// attention kernel dominates decode time and consumes the HBM bandwidth).  The
+// kernel is therefore built around the loads:
+//
+//  * K/V rows are read with 16-byte loads; the lanes of a wave cover whole
+//    token rows, so each load instruction reads TPL consecutive rows of one
+//    block (1 KiB contiguous for D = 128 f16).
+//  * A workgroup owns one (request, query head, partition).  The physical block
+//    ids of the partition are staged in LDS once (in windows of 256 blocks),
+//    then read wave-uniformly; every block id is range-checked there.
+//  * Each wave takes chunks of CH blocks round-robin, issues all K and V loads
+//    of a chunk before using any of them, computes q.k with packed dot
+//    instructions plus a DPP row reduction, and keeps an online softmax
+//    (running max m, running sum l, output o) in the log2 domain.
+//  * Lanes that share a row position keep separate softmax states, which are
+//    merged once at the end, first across the wave with shuffles and then
+//    across the waves through LDS.  With one partition the workgroup writes the
+//    normalised output; otherwise it writes (o / l, m + log2 l) for the merge
+//    kernel.
+//
+// The fused variant (APPEND) also performs the step's kv_append: the token at
+// positions[b] is taken from k_new/v_new instead of the pool, and the lanes
+// holding it write it to its pool slot.
+#include "pkv_device.h"
+#include "pkv_launch.h"
+
+namespace pkv {
+
+constexpr int kWindowBlocks = 256;
+
+template <int DT, int D, int NW, int CH, bool APPEND>
+__global__ __launch_bounds__(NW * 64) void decode_mha_kernel(const AttnArgs a) {
+    constexpr int ES = Dt<DT>::bytes;
+    constexpr int E = 16 / ES;                // elements per 16-byte lane vector
+    constexpr int LPT = D / E;                // lanes per token row
+    constexpr int TPL = 64 / LPT;             // tokens per wave-wide load
+    constexpr int LPB = kBlockSize / TPL;     // loads per block
+    constexpr int NL = CH * LPB;              // loads (and scores) per lane per chunk
+    static_assert(TPL * LPT == 64 && LPB * TPL == kBlockSize, "unsupported shape");
+
+    __shared__ int32_t s_ids[kWindowBlocks];
+    __shared__ int s_bad;
+    __shared__ float s_m[NW];
+    __shared__ float s_l[NW];
+    __shared__ float s_o[NW][D];
+
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int r = lane / LPT;
+    const int c = lane % LPT;
+
+    const int BH = a.B * a.H_q;
+    const int part = blockIdx.x / BH;
+    const int bh = blockIdx.x - part * BH;
+    const int b = bh / a.H_q;
+    const int h = bh - b * a.H_q;
+    const int g = h / a.G;
+
+    const int n = APPEND ? a.positions[b] + 1 : a.context_lens[b];
+    const bool bad_len = APPEND ? (n < 1 || n > a.max_context_len) : (n < 0 || n > a.max_context_len);
+    float* out_row = a.out + (size_t)bh * D;
+    if (bad_len || n == 0) {
+        // unsplit: this workgroup owns the row; split: the merge kernel writes it
+        if (a.n_parts == 1 && part == 0)
+            for (int d = threadIdx.x; d < D; d += NW * 64) out_row[d] = bad_len ? __builtin_nanf("") : 0.0f;
+        return;
+    }
+    const int start = part * a.part_tokens;
+    if (start >= n) return;
+    const int end = min(start + a.part_tokens, n);
+    const int n_hist = APPEND ? n - 1 : n;   // tokens already in the pool
+    const int lim = min(end, n_hist);
+    // only the partition that ends at n holds the new token; a chunk may run past
+    // its partition's last block, so every other partition must never match it
+    const int pos_new = (APPEND && end == n) ? n - 1 : -1;
+
+    const uint4 qv = ld16_cached(a.q + ((int64_t)b * a.q_row_stride + (int64_t)h * D + c * E) * ES);
+
+    float m = kNegBig, l = 0.0f;
+    float o[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = 0.0f;
+
+    const int32_t* table = a.block_tables + (int64_t)b * a.bt_stride;
+    const int first_blk = start / kBlockSize;
+    const int nblk = (end - start + kBlockSize - 1) / kBlockSize;
+    const size_t blk_bytes = (size_t)a.H_kv * kBlockSize * D * ES;
+    const size_t head_bytes = (size_t)g * kBlockSize * D * ES;
+    // byte offset of this lane's 16 bytes for load i of a block
+    int lane_off[LPB];
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) lane_off[i] = ((i * TPL + r) * D + c * E) * ES;
+    const size_t new_off = ((size_t)b * a.new_row_stride + (size_t)g * D + c * E) * ES;
+    const bool writer = APPEND && (h % a.G) == 0;
+
+    if (threadIdx.x == 0) s_bad = 0;
+    for (int r0 = 0; r0 < nblk; r0 += kWindowBlocks) {
+        const int nr = min(kWindowBlocks, nblk - r0);
+        __syncthreads();
+        for (int t = threadIdx.x; t < nr; t += NW * 64) {
+            int id = table[first_blk + r0 + t];
+            if ((unsigned)id >= (unsigned)a.n_blocks) {
+                s_bad = 1;
+                id = 0;
+            }
+            s_ids[t] = id;
+        }
+        __syncthreads();
+        const bool any_bad = s_bad != 0;
+        const int nch = (nr + CH - 1) / CH;
+        for (int k = w; k < nch; k += NW) {
+            const int cb0 = k * CH;
+            const int tok0 = start + (r0 + cb0) * kBlockSize;
+            const char* kb[CH];
+            const char* vb[CH];
+#pragma unroll
+            for (int cb = 0; cb < CH; ++cb) {
+                const int id = __builtin_amdgcn_readfirstlane(cb0 + cb < nr ? s_ids[cb0 + cb] : 0);
+                kb[cb] = a.k_pool + (size_t)id * blk_bytes + head_bytes;
+                vb[cb] = a.v_pool + (size_t)id * blk_bytes + head_bytes;
+            }
+            uint4 kv[NL], vv[NL];
+            bool valid[NL];
+            const bool fast = tok0 + CH * kBlockSize <= lim;
+            if (fast) {
+#pragma unroll
+                for (int cb = 0; cb < CH; ++cb)
+#pragma unroll
+                    for (int i = 0; i < LPB; ++i) kv[cb * LPB + i] = ld16(kb[cb] + lane_off[i]);
+#pragma unroll
+                for (int cb = 0; cb < CH; ++cb)
+#pragma unroll
+                    for (int i = 0; i < LPB; ++i) vv[cb * LPB + i] = ld16(vb[cb] + lane_off[i]);
+#pragma unroll
+                for (int j = 0; j < NL; ++j) valid[j] = true;
+            } else {
+#pragma unroll
+                for (int cb = 0; cb < CH; ++cb)
+#pragma unroll
+                    for (int i = 0; i < LPB; ++i) {
+                        const int j = cb * LPB + i;
+                        const int t = tok0 + cb * kBlockSize + i * TPL + r;
+                        kv[j] = make_uint4(0, 0, 0, 0);
+                        vv[j] = make_uint4(0, 0, 0, 0);
+                        valid[j] = false;
+                        if (t < lim) {
+                            kv[j] = ld16(kb[cb] + lane_off[i]);
+                            vv[j] = ld16(vb[cb] + lane_off[i]);
+                            valid[j] = true;
+                        } else if (APPEND && t == pos_new) {
+                            kv[j] = ld16_cached(a.k_new + new_off);
+                            vv[j] = ld16_cached(a.v_new + new_off);
+                            valid[j] = true;
+                            if (writer && !any_bad) {
+                                st16(a.k_pool_w + (kb[cb] - a.k_pool) + lane_off[i], kv[j]);
+                                st16(a.v_pool_w + (vb[cb] - a.v_pool) + lane_off[i], vv[j]);
+                            }
+                        }
+                    }
+            }
+            float s[NL];
+#pragma unroll
+            for (int j = 0; j < NL; ++j) s[j] = mul_rn(group_sum<LPT>(dot16<DT>(qv, kv[j])), a.scale_log2);
+            float mloc = kNegBig;
+#pragma unroll
+            for (int j = 0; j < NL; ++j) mloc = valid[j] ? fmaxf(mloc, s[j]) : mloc;
+            const float m_new = fmaxf(m, mloc);
+            const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+            m = m_new;
+            l *= alpha;
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[e] *= alpha;
+#pragma unroll
+            for (int j = 0; j < NL; ++j) {
+                const float p = valid[j] ? __builtin_amdgcn_exp2f(s[j] - m) : 0.0f;
+                l += p;
+                axpy16<DT>(o, p, vv[j]);
+            }
+        }
+    }
+
+    // merge the TPL row groups of the wave
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) {
+        const float m_o = __shfl_xor(m, off, 64);
+        const float l_o = __shfl_xor(l, off, 64);
+        const float M = fmaxf(m, m_o);
+        const float fa = __builtin_amdgcn_exp2f(m - M);
+        const float fb = __builtin_amdgcn_exp2f(m_o - M);
+        l = l * fa + l_o * fb;
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = o[e] * fa + __shfl_xor(o[e], off, 64) * fb;
+        m = M;
+    }
+    if (lane < LPT) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) s_o[w][c * E + e] = o[e];
+        if (lane == 0) {
+            s_m[w] = m;
+            s_l[w] = l;
+        }
+    }
+    __syncthreads();
+    const bool bad = s_bad != 0;
+    float M = s_m[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) M = fmaxf(M, s_m[i]);
+    float L = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) L += s_l[i] * __builtin_amdgcn_exp2f(s_m[i] - M);
+    const float inv = 1.0f / L;
+    for (int d = threadIdx.x; d < D; d += NW * 64) {
+        float O = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) O += s_o[i][d] * __builtin_amdgcn_exp2f(s_m[i] - M);
+        const float val = bad ? __builtin_nanf("") : O * inv;
+        if (a.n_parts == 1) {
+            out_row[d] = val;
+        } else {
+            a.part_o[((size_t)bh * a.n_parts + part) * D + d] = val;
+        }
+    }
+    if (a.n_parts > 1 && threadIdx.x == 0)
+        a.part_lse[(size_t)bh * a.n_parts + part] = bad ? __builtin_nanf("") : M + __builtin_amdgcn_logf(L);
+}
+
+// ---------------------------------------------------------------------------
+// dispatch
+// ---------------------------------------------------------------------------
+template <int DT, int D, int NW, int CH>
+static hipError_t launch_mha_t(bool append, const AttnArgs& a, unsigned grid, hipStream_t stream) {
+    if (append)
+        hipLaunchKernelGGL((decode_mha_kernel<DT, D, NW, CH, true>), dim3(grid), dim3(NW * 64), 0, stream, a);
+    else
+        hipLaunchKernelGGL((decode_mha_kernel<DT, D, NW, CH, false>), dim3(grid), dim3(NW * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int DT, int D>
+static hipError_t launch_mha_d(int nw, int ch, bool append, const AttnArgs& a, unsigned grid, hipStream_t s) {
+    switch (nw * 10 + ch) {
+    case 42: return launch_mha_t<DT, D, 4, 2>(append, a, grid, s);
+    case 44: return launch_mha_t<DT, D, 4, 4>(append, a, grid, s);
+    case 82: return launch_mha_t<DT, D, 8, 2>(append, a, grid, s);
+    case 84: return launch_mha_t<DT, D, 8, 4>(append, a, grid, s);
+    case 162: return launch_mha_t<DT, D, 16, 2>(append, a, grid, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_decode_mha(int dtype, int D, int nw, int ch, bool append, const AttnArgs& a,
+                             unsigned grid, hipStream_t stream) {
+    switch (dtype * 1000 + D) {
+    case DT_F32 * 1000 + 64: return launch_mha_d<DT_F32, 64>(nw, ch, append, a, grid, stream);
+    case DT_F32 * 1000 + 128: return launch_mha_d<DT_F32, 128>(nw, ch, append, a, grid, stream);
+    case DT_F16 * 1000 + 64: return launch_mha_d<DT_F16, 64>(nw, ch, append, a, grid, stream);
+    case DT_F16 * 1000 + 128: return launch_mha_d<DT_F16, 128>(nw, ch, append, a, grid, stream);
+    case DT_BF16 * 1000 + 64: return launch_mha_d<DT_BF16, 64>(nw, ch, append, a, grid, stream);
+    case DT_BF16 * 1000 + 128: return launch_mha_d<DT_BF16, 128>(nw, ch, append, a, grid, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+bool mha_variant_exists(int nw, int ch) {
+    return ((nw == 4 || nw == 8) && (ch == 2 || ch == 4)) || (nw == 16 && ch == 2);
+}
+
+}  // namespace pkv

@@ -1,0 +1,41 @@
+// pkv_launch.h -- host-side launchers of the gfx950 kernels (internal to libpkv).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkv_device.h"
+
+namespace pkv {
+
+struct AppendArgs {
+    const char* k_new;
+    const char* v_new;
+    char* k_pool;
+    char* v_pool;
+    const int32_t* block_tables;
+    const int32_t* positions;
+    int64_t new_row_stride;   // elements
+    int32_t bt_stride;
+    int32_t B, H_kv, D, elem_bytes, n_blocks;
+};
+
+struct MergeArgs {
+    float* out;
+    const float* part_o;
+    const float* part_lse;
+    const int32_t* context_lens;   // plain call
+    const int32_t* positions;      // fused call (n = positions + 1); context_lens unused
+    int32_t BH, H_q, n_parts, part_tokens, max_context_len;
+};
+
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_decode_mha(int dtype, int D, int nw, int ch, bool append, const AttnArgs& a,
+                             unsigned grid, hipStream_t stream);
+hipError_t launch_decode_gqa(int dtype, int D, int nw, int ch, bool append, const AttnArgs& a,
+                             unsigned grid, hipStream_t stream);
+hipError_t launch_lse_merge(int D, const MergeArgs& a, hipStream_t stream);
+bool mha_variant_exists(int nw, int ch);
+bool gqa_variant_exists(int nw, int ch);
+
+}  // namespace pkv
