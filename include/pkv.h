@@ -187,6 +187,16 @@ int pkv_append_decode_attention(int dtype,
                                 void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/*
+ * probe_stream_read -- measurement aid, not part of the decode step: reads
+ * `bytes` bytes (rounded down to a multiple of 16) of device memory at `buf`
+ * once with 16-byte loads from `grid` workgroups of 256 threads, so that the
+ * HBM read bandwidth the device sustains can be timed next to the decode
+ * kernels.  `sink` is a device word that is written only if the loaded data
+ * fold to one particular value.  buf 16-byte aligned; 1 <= grid <= 2^20.
+ */
+int pkv_probe_stream_read(const void* buf, size_t bytes, void* sink, int32_t grid, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,7 @@ from typing import Optional
 
 __all__ = [
     "PkvError", "LIB_PATH", "load_library", "library_loaded", "kv_append", "paged_decode_attention",
-    "append_decode_attention", "decode_workspace_bytes", "last_launch", "version",
+    "append_decode_attention", "decode_workspace_bytes", "last_launch", "version", "probe_stream_read",
     "PKV_F32", "PKV_F16", "PKV_BF16", "EXPORTED_SYMBOLS",
 ]
 
@@ -33,6 +33,7 @@ BLOCK_SIZE = 16
 EXPORTED_SYMBOLS = (
     "pkv_version", "pkv_status_string", "pkv_last_error", "pkv_last_launch", "pkv_kv_append",
     "pkv_decode_workspace_bytes", "pkv_paged_decode_attention", "pkv_append_decode_attention",
+    "pkv_probe_stream_read",
 )
 
 _lib = None
@@ -76,6 +77,8 @@ def load_library(path: Optional[str] = None):
                                                 I32, I32, I32, I32, I32, I32, I32, ctypes.c_float, I32,
                                                 P, SZ, P]
     lib.pkv_append_decode_attention.restype = ctypes.c_int
+    lib.pkv_probe_stream_read.argtypes = [P, SZ, P, I32, P]
+    lib.pkv_probe_stream_read.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -97,6 +100,13 @@ def version() -> int:
 
 def last_launch() -> str:
     return load_library().pkv_last_launch().decode()
+
+
+def probe_stream_read(buf, sink, grid: int = 16384, *, stream=None):
+    """Launch the streaming-read measurement kernel over all of `buf` (a device tensor)."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(load_library().pkv_probe_stream_read(_ptr(buf), nbytes, _ptr(sink), int(grid), _stream(stream)),
+           "probe_stream_read")
 
 
 def decode_workspace_bytes(B: int, H_q: int, D: int, max_context_len: int, partition_size: int) -> int:

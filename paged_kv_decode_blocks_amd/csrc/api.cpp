@@ -72,19 +72,24 @@ Plan make_plan(int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32
     const int32_t G = H_q / H_kv;
     p.grouped = G > 1 && dtype != PKV_F32;
     const int32_t blocks = p.part_tokens / pkv::kBlockSize;
+    // Waves per workgroup and blocks per chunk, from launch-shape sweeps on MI355X:
+    // when the grid already holds several workgroups per CU (split contexts, large
+    // batches) small 4-wave workgroups let a CU overlap several workgroups' load
+    // latency; a long unsplit context per workgroup spreads over more waves.
+    const int64_t wgs = (int64_t)p.n_parts * B * (p.grouped ? H_kv : H_q);
     if (p.grouped) {
         p.nw = env_int("PKV_GQA_NW", 4);
-        p.ch = env_int("PKV_GQA_CH", 1);
-        if (!pkv::gqa_variant_exists(p.nw, p.ch)) { p.nw = 4; p.ch = 1; }
-        p.grid = (unsigned)((int64_t)p.n_parts * B * H_kv);
+        p.ch = env_int("PKV_GQA_CH", 2);
+        if (!pkv::gqa_variant_exists(p.nw, p.ch)) { p.nw = 4; p.ch = 2; }
+        p.grid = (unsigned)wgs;
     } else {
-        int ch = 2;
+        const int ch = 2;
         int nw = 4;
-        while (nw < 16 && blocks >= 2 * nw * ch) nw *= 2;   // at least two chunks per wave before widening
+        if (p.n_parts == 1 && wgs > 4 * 256 && blocks >= 64) nw = 16;
         p.nw = env_int("PKV_MHA_NW", nw);
         p.ch = env_int("PKV_MHA_CH", ch);
         if (!pkv::mha_variant_exists(p.nw, p.ch)) { p.nw = nw; p.ch = ch; }
-        p.grid = (unsigned)((int64_t)p.n_parts * B * H_q);
+        p.grid = (unsigned)wgs;
     }
     (void)D;
     if (p.n_parts > 1) {
@@ -269,6 +274,19 @@ int pkv_kv_append(int dtype, const void* k_new, const void* v_new, int64_t new_r
     a.n_blocks = n_blocks;
     hipError_t e = pkv::launch_kv_append(a, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "kv_append launch: %s", hipGetErrorString(e));
+    g_err[0] = 0;
+    return PKV_OK;
+}
+
+int pkv_probe_stream_read(const void* buf, size_t bytes, void* sink, int32_t grid, void* stream) {
+    if (!buf || !sink) return fail(PKV_ERR_NULL, "buf and sink must not be NULL");
+    if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(sink) & 3u))
+        return fail(PKV_ERR_INVALID_ARG, "buf must be 16-byte aligned and sink 4-byte aligned");
+    if (bytes < 16 || grid <= 0 || grid > (1 << 20))
+        return fail(PKV_ERR_INVALID_ARG, "bytes = %zu, grid = %d", bytes, grid);
+    hipError_t e = pkv::launch_stream_read(buf, bytes, reinterpret_cast<unsigned*>(sink), grid,
+                                           reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "probe launch: %s", hipGetErrorString(e));
     g_err[0] = 0;
     return PKV_OK;
 }

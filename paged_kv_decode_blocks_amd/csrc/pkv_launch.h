@@ -35,6 +35,7 @@ hipError_t launch_decode_mha(int dtype, int D, int nw, int ch, bool append, cons
 hipError_t launch_decode_gqa(int dtype, int D, int nw, int ch, bool append, const AttnArgs& a,
                              unsigned grid, hipStream_t stream);
 hipError_t launch_lse_merge(int D, const MergeArgs& a, hipStream_t stream);
+hipError_t launch_stream_read(const void* buf, size_t bytes, unsigned* sink, int grid, hipStream_t stream);
 bool mha_variant_exists(int nw, int ch);
 bool gqa_variant_exists(int nw, int ch);
 

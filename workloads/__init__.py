@@ -265,7 +265,7 @@ def step_bytes(cfg: Config, context_lens: np.ndarray, append: bool) -> dict:
         "q": float(B * cfg.H_q * cfg.D * e),
         "out": float(B * cfg.H_q * cfg.D * 4),
         "block_tables": float(((ctx + cfg.block_size - 1) // cfg.block_size).sum() * 4),
-        "lengths": float(B * 4 * (2 if append else 1)),
+        "lengths": float(B * 4),          # context_lens, or positions in a fused step
     }
     out["total"] = sum(out.values())
     # attention alone reads every context token from the pool
