@@ -52,7 +52,8 @@ struct Plan {
     int32_t part_tokens;
     int32_t n_parts;
     bool grouped;     // matrix-core path (one workgroup per KV head and G query heads)
-    int nw, ch;
+    int kind;         // grouped path: 0 = loads through registers, 1 = through an LDS ring
+    int nw, ch, pf;   // waves per workgroup, blocks per chunk, chunks (or ring slots) in flight per wave
     unsigned grid;
     size_t ws_o, ws_lse, ws_total;
 };
@@ -78,17 +79,22 @@ Plan make_plan(int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32
     // latency; a long unsplit context per workgroup spreads over more waves.
     const int64_t wgs = (int64_t)p.n_parts * B * (p.grouped ? H_kv : H_q);
     if (p.grouped) {
-        p.nw = env_int("PKV_GQA_NW", 4);
-        p.ch = env_int("PKV_GQA_CH", 2);
-        if (!pkv::gqa_variant_exists(p.nw, p.ch)) { p.nw = 4; p.ch = 2; }
+        // measured on c5-shaped batches: 2-wave workgroups with register-staged loads (more
+        // workgroups per CU) beat deeper register pipelines and the LDS ring
+        p.kind = env_int("PKV_GQA_KIND", 0);
+        p.nw = env_int("PKV_GQA_NW", 2);
+        p.ch = env_int("PKV_GQA_CH", 1);
+        p.pf = env_int("PKV_GQA_PF", 1);
+        if (!pkv::gqa_variant_exists(p.kind, p.nw, p.ch, p.pf)) { p.kind = 0; p.nw = 2; p.ch = 1; p.pf = 1; }
         p.grid = (unsigned)wgs;
     } else {
-        const int ch = 2;
-        int nw = 4;
-        if (p.n_parts == 1 && wgs > 4 * 256 && blocks >= 64) nw = 16;
+        // a PF-deep load pipeline pays where a workgroup walks a long unsplit context
+        int nw = 4, ch = 2, pf = 1;
+        if (p.n_parts == 1 && wgs > 4 * 256 && blocks >= 64) { nw = 8; pf = 2; }
         p.nw = env_int("PKV_MHA_NW", nw);
         p.ch = env_int("PKV_MHA_CH", ch);
-        if (!pkv::mha_variant_exists(p.nw, p.ch)) { p.nw = nw; p.ch = ch; }
+        p.pf = env_int("PKV_MHA_PF", pf);
+        if (!pkv::mha_variant_exists(p.nw, p.ch, p.pf)) { p.nw = nw; p.ch = ch; p.pf = pf; }
         p.grid = (unsigned)wgs;
     }
     (void)D;
@@ -192,8 +198,8 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
     a.scale_log2 = scale * pkv::kLog2e;
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = p.grouped ? pkv::launch_decode_gqa(dtype, D, p.nw, p.ch, fused, a, p.grid, s)
-                             : pkv::launch_decode_mha(dtype, D, p.nw, p.ch, fused, a, p.grid, s);
+    hipError_t e = p.grouped ? pkv::launch_decode_gqa(dtype, D, p.kind, p.nw, p.ch, p.pf, fused, a, p.grid, s)
+                             : pkv::launch_decode_mha(dtype, D, p.nw, p.ch, p.pf, fused, a, p.grid, s);
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
     if (p.n_parts > 1) {
         pkv::MergeArgs m{};
@@ -210,8 +216,9 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
         e = pkv::launch_lse_merge(D, m, s);
         if (e != hipSuccess) return fail(PKV_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
     }
-    snprintf(g_launch, sizeof g_launch, "%s dtype=%d D=%d nw=%d ch=%d grid=%u part_tokens=%d n_parts=%d%s",
-             p.grouped ? "gqa_mfma" : "mha", dtype, D, p.nw, p.ch, p.grid, p.part_tokens, p.n_parts,
+    snprintf(g_launch, sizeof g_launch, "%s dtype=%d D=%d nw=%d ch=%d pf=%d grid=%u part_tokens=%d n_parts=%d%s",
+             p.grouped ? (p.kind ? "gqa_mfma_lds" : "gqa_mfma") : "mha", dtype, D, p.nw, p.ch, p.pf, p.grid,
+             p.part_tokens, p.n_parts,
              fused ? " fused_append" : "");
     g_err[0] = 0;
     return PKV_OK;

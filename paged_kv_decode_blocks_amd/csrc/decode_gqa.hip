@@ -24,15 +24,26 @@
 // of tile T is element T of the lane's four V loads, packed with v_perm.
 //
 // Softmax is online per query head in the log2 domain; the per-chunk max is
-// shared by the four lane groups holding a head with two cross-row shuffles.
-// Results merge across the waves of the workgroup through LDS, as in the
-// per-head kernel, and the fused APPEND variant also writes the new token.
+// shared by the four lane groups holding a head with two cross-row shuffles,
+// and the accumulators are rescaled lazily (only when a head's running max
+// grows by more than 2^8), so the VALU rarely touches the MFMA accumulators.
+//
+// Two kernels share this arithmetic:
+//  * decode_gqa_kernel      K/V go global -> registers, PF chunks in flight per wave;
+//  * decode_gqa_lds_kernel  K/V go global -> LDS with global_load_lds_dwordx4
+//    (1 KiB fully coalesced per instruction, no registers held while in flight)
+//    into a per-wave ring of S block slots, then LDS -> registers in the MFMA
+//    layout.  K rows are stored with their 16-byte chunks XOR-swizzled by row,
+//    so the column-wise MFMA reads hit 16 different banks.
+// Both merge across the waves of the workgroup through LDS, and the fused
+// APPEND variants also write the new token.
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
 namespace pkv {
 
 constexpr int kWindowBlocksG = 256;
+constexpr float kRescaleSlack = 8.0f;   // log2 units: weights stay below 256
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -66,29 +77,29 @@ template <> struct Mfma<DT_F16> {
     }
 };
 
-// V load of VB bytes per lane (16 for D = 128, 8 for D = 64), as 32-bit words
+// V row piece of VB bytes per lane (16 for D = 128, 8 for D = 64), as 32-bit words
 template <int NWORD> struct VRow { uint32_t w[NWORD]; };
 
 template <int NWORD>
-__device__ __forceinline__ VRow<NWORD> ldv(const char* p) {
+__device__ __forceinline__ VRow<NWORD> ldv(const char* p) {   // global, streaming
     VRow<NWORD> r;
     if constexpr (NWORD == 4) {
-        uint4 v = ld16(p);
+        const uint4 v = ld16(p);
         r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
     } else {
-        uint2 v = ld8(p);
+        const uint2 v = ld8(p);
         r.w[0] = v.x; r.w[1] = v.y;
     }
     return r;
 }
 template <int NWORD>
-__device__ __forceinline__ VRow<NWORD> ldv_cached(const char* p) {
+__device__ __forceinline__ VRow<NWORD> ldv_plain(const char* p) {   // global (cached) or LDS
     VRow<NWORD> r;
     if constexpr (NWORD == 4) {
-        uint4 v = ld16_cached(p);
+        const uint4 v = *reinterpret_cast<const uint4*>(p);
         r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
     } else {
-        uint2 v = *reinterpret_cast<const uint2*>(p);
+        const uint2 v = *reinterpret_cast<const uint2*>(p);
         r.w[0] = v.x; r.w[1] = v.y;
     }
     return r;
@@ -99,273 +110,591 @@ __device__ __forceinline__ void stv(char* p, const VRow<NWORD>& r) {
     else st8(p, make_uint2(r.w[0], r.w[1]));
 }
 
-template <int DT, int D, int NW, int CH, bool APPEND>
-__global__ __launch_bounds__(NW * 64) void decode_gqa_kernel(const AttnArgs a) {
-    constexpr int ES = 2;
-    constexpr int KS = D / 32;          // score MFMA steps
-    constexpr int VT = D / 16;          // output tiles = V elements per lane per load
-    constexpr int NWORD = VT / 2;       // 32-bit words per V load
-    constexpr int DP = D + 4;           // padded LDS row
+// 16 bytes per lane from global memory straight into LDS: lane l of the wave
+// writes lds_base + 16 l (global_load_lds_dwordx4; lds_base wave-uniform).  The
+// LDS address-space cast is only meaningful in the device pass; in the host pass
+// it would silently drop the kernel's launch stub, so it is compiled there only.
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+#else
+    (void)src;
+    (void)lds_base;
+#endif
+}
+
+// s_waitcnt vmcnt(N) leaving the other counters unconstrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// ---------------------------------------------------------------------------
+// Per-lane state and arithmetic shared by both kernels.
+// ---------------------------------------------------------------------------
+template <int DT, int D, bool APPEND>
+struct GqaLane {
+    static constexpr int ES = 2;
+    static constexpr int KS = D / 32;      // score MFMA steps
+    static constexpr int VT = D / 16;      // output tiles = V elements per lane per row piece
+    static constexpr int NWORD = VT / 2;   // 32-bit words per V row piece
     static_assert(D == 64 || D == 128, "unsupported head dim");
 
-    __shared__ int32_t s_ids[kWindowBlocksG];
-    __shared__ int s_bad;
-    __shared__ float s_m[NW][16];
-    __shared__ float s_l[NW][16];
-    __shared__ float s_o[NW][16][DP];
-
-    const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
-    const int j = lane >> 4;       // lane group: MFMA k-group / output row group
-    const int col = lane & 15;     // MFMA column: query head within the group; also A-row
-
-    const int BG = a.B * a.H_kv;
-    const int part = blockIdx.x / BG;
-    const int bg = blockIdx.x - part * BG;
-    const int b = bg / a.H_kv;
-    const int g = bg - b * a.H_kv;
-    const int G = a.G;
-
-    const int n = APPEND ? a.positions[b] + 1 : a.context_lens[b];
-    const bool bad_len = APPEND ? (n < 1 || n > a.max_context_len) : (n < 0 || n > a.max_context_len);
-    if (bad_len || n == 0) {
-        if (a.n_parts == 1 && part == 0)
-            for (int x = threadIdx.x; x < G * D; x += NW * 64)
-                a.out[((size_t)b * a.H_q + (size_t)g * G) * D + x] = bad_len ? __builtin_nanf("") : 0.0f;
-        return;
-    }
-    const int start = part * a.part_tokens;
-    if (start >= n) return;
-    const int end = min(start + a.part_tokens, n);
-    const int n_hist = APPEND ? n - 1 : n;
-    const int lim = min(end, n_hist);
-    // only the partition that ends at n holds the new token; a chunk may run past
-    // its partition's last block, so every other partition must never match it
-    const int pos_new = (APPEND && end == n) ? n - 1 : -1;
-
-    // Q^T fragments: column col = query head g*G + col, k = d = 32 s + 8 j .. +7
+    int j, col, tau;
     uint4 qf[KS];
+    int koff[KS];      // byte offset of this lane's K piece of step s inside a (block, head) tile
+    int voff[4];       // byte offset of this lane's V piece of row-load i inside a tile
+    floatx4 acc[VT];
+    float m, l;
+    float scale_log2;
+
+    __device__ __forceinline__ void init(const AttnArgs& a, int lane, int b, int g) {
+        j = lane >> 4;
+        col = lane & 15;
+        tau = 4 * (col & 3) + (col >> 2);   // token (within a block) on A-row `col`
+        scale_log2 = a.scale_log2;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        qf[s] = make_uint4(0, 0, 0, 0);
-        if (col < G)
-            qf[s] = ld16_cached(a.q + ((int64_t)b * a.q_row_stride + (int64_t)(g * G + col) * D + 32 * s + 8 * j) * ES);
+        for (int s = 0; s < KS; ++s) {
+            qf[s] = make_uint4(0, 0, 0, 0);
+            if (col < a.G)
+                qf[s] = ld16_cached(a.q + ((int64_t)b * a.q_row_stride + (int64_t)(g * a.G + col) * D + 32 * s + 8 * j) * ES);
+        }
+#pragma unroll
+        for (int s = 0; s < KS; ++s) koff[s] = (tau * D + 32 * s + 8 * j) * ES;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) voff[i] = ((4 * i + j) * D + col * VT) * ES;
+#pragma unroll
+        for (int t = 0; t < VT; ++t) acc[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        m = kNegBig;
+        l = 0.0f;
     }
 
-    const int tau = 4 * (col & 3) + (col >> 2);          // token (within a block) on A-row `col`
-    int koff[KS];
+    // Online-softmax update with CH blocks: score tiles on MFMA, shared per-head
+    // max with lazy rescaling, PV tiles on MFMA.
+    template <int CH>
+    __device__ __forceinline__ void accumulate(const uint4 (&kf)[CH][KS], const VRow<NWORD> (&vf)[CH][4],
+                                               const bool (&valid)[CH][4]) {
+        // scores: lane holds S[head col][token 4 i + j of block cb], i = 0..3
+        float sc[CH][4];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) koff[s] = (tau * D + 32 * s + 8 * j) * ES;
-    int voff[4];
+        for (int cb = 0; cb < CH; ++cb) {
+            floatx4 st = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) voff[i] = ((4 * i + j) * D + col * VT) * ES;
-    const size_t knew_off = ((size_t)b * a.new_row_stride + (size_t)g * D) * ES;
-
-    floatx4 acc[VT];
+            for (int s = 0; s < KS; ++s) st = Mfma<DT>::mma(kf[cb][s], qf[s], st);
 #pragma unroll
-    for (int t = 0; t < VT; ++t) acc[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-    float m = kNegBig, l = 0.0f;
-
-    const int32_t* table = a.block_tables + (int64_t)b * a.bt_stride;
-    const int first_blk = start / kBlockSize;
-    const int nblk = (end - start + kBlockSize - 1) / kBlockSize;
-    const size_t blk_bytes = (size_t)a.H_kv * kBlockSize * D * ES;
-    const size_t head_bytes = (size_t)g * kBlockSize * D * ES;
-
-    if (threadIdx.x == 0) s_bad = 0;
-    for (int r0 = 0; r0 < nblk; r0 += kWindowBlocksG) {
-        const int nr = min(kWindowBlocksG, nblk - r0);
-        __syncthreads();
-        for (int t = threadIdx.x; t < nr; t += NW * 64) {
-            int id = table[first_blk + r0 + t];
-            if ((unsigned)id >= (unsigned)a.n_blocks) {
-                s_bad = 1;
-                id = 0;
-            }
-            s_ids[t] = id;
+            for (int i = 0; i < 4; ++i) sc[cb][i] = mul_rn(st[i], scale_log2);
         }
-        __syncthreads();
-        const bool any_bad = s_bad != 0;
-        const int nch = (nr + CH - 1) / CH;
-        for (int k = w; k < nch; k += NW) {
-            const int cb0 = k * CH;
-            const int tok0 = start + (r0 + cb0) * kBlockSize;
-            const char* kb[CH];
-            const char* vb[CH];
+        float mloc = kNegBig;
 #pragma unroll
-            for (int cb = 0; cb < CH; ++cb) {
-                const int id = __builtin_amdgcn_readfirstlane(cb0 + cb < nr ? s_ids[cb0 + cb] : 0);
-                kb[cb] = a.k_pool + (size_t)id * blk_bytes + head_bytes;
-                vb[cb] = a.v_pool + (size_t)id * blk_bytes + head_bytes;
-            }
-            uint4 kf[CH][KS];
-            VRow<NWORD> vf[CH][4];
-            bool valid[CH][4];
-            const bool fast = tok0 + CH * kBlockSize <= lim;
-            if (fast) {
+        for (int cb = 0; cb < CH; ++cb)
 #pragma unroll
-                for (int cb = 0; cb < CH; ++cb)
-#pragma unroll
-                    for (int s = 0; s < KS; ++s) kf[cb][s] = ld16(kb[cb] + koff[s]);
-#pragma unroll
-                for (int cb = 0; cb < CH; ++cb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) vf[cb][i] = ldv<NWORD>(vb[cb] + voff[i]);
-#pragma unroll
-                for (int cb = 0; cb < CH; ++cb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) valid[cb][i] = true;
-            } else {
-#pragma unroll
-                for (int cb = 0; cb < CH; ++cb) {
-                    const int tb = tok0 + cb * kBlockSize;
-                    const int tk = tb + tau;
-#pragma unroll
-                    for (int s = 0; s < KS; ++s) {
-                        kf[cb][s] = make_uint4(0, 0, 0, 0);
-                        if (tk < lim) {
-                            kf[cb][s] = ld16(kb[cb] + koff[s]);
-                        } else if (APPEND && tk == pos_new) {
-                            kf[cb][s] = ld16_cached(a.k_new + knew_off + (32 * s + 8 * j) * ES);
-                            if (!any_bad) st16(a.k_pool_w + (kb[cb] - a.k_pool) + koff[s], kf[cb][s]);
-                        }
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int tv = tb + 4 * i + j;
-#pragma unroll
-                        for (int x = 0; x < NWORD; ++x) vf[cb][i].w[x] = 0;
-                        valid[cb][i] = false;
-                        if (tv < lim) {
-                            vf[cb][i] = ldv<NWORD>(vb[cb] + voff[i]);
-                            valid[cb][i] = true;
-                        } else if (APPEND && tv == pos_new) {
-                            vf[cb][i] = ldv_cached<NWORD>(a.v_new + knew_off + col * VT * ES);
-                            valid[cb][i] = true;
-                            if (!any_bad) stv<NWORD>(a.v_pool_w + (vb[cb] - a.v_pool) + voff[i], vf[cb][i]);
-                        }
-                    }
-                }
-            }
-            // scores: lane holds S[head col][token tb + 4 i + j], i = 0..3
-            float sc[CH][4];
-#pragma unroll
-            for (int cb = 0; cb < CH; ++cb) {
-                floatx4 st = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int s = 0; s < KS; ++s) st = Mfma<DT>::mma(kf[cb][s], qf[s], st);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sc[cb][i] = mul_rn(st[i], a.scale_log2);
-            }
-            float mloc = kNegBig;
-#pragma unroll
-            for (int cb = 0; cb < CH; ++cb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) mloc = valid[cb][i] ? fmaxf(mloc, sc[cb][i]) : mloc;
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+            for (int i = 0; i < 4; ++i) mloc = valid[cb][i] ? fmaxf(mloc, sc[cb][i]) : mloc;
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+        // The reference max m only moves when some head's running max grows by
+        // more than kRescaleSlack (a rare, wave-uniform branch); with a stale m the
+        // weights exp2(s - m) stay <= 2^kRescaleSlack.
+        if (__builtin_amdgcn_ballot_w64(mloc > m + kRescaleSlack) != 0) {
             const float m_new = fmaxf(m, mloc);
             const float alpha = __builtin_amdgcn_exp2f(m - m_new);
             m = m_new;
             l *= alpha;
 #pragma unroll
             for (int t = 0; t < VT; ++t) acc[t] *= alpha;
+        }
 #pragma unroll
-            for (int cb = 0; cb < CH; ++cb) {
-                float p[4];
+        for (int cb = 0; cb < CH; ++cb) {
+            float p[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    p[i] = valid[cb][i] ? __builtin_amdgcn_exp2f(sc[cb][i] - m) : 0.0f;
-                    l += p[i];
-                }
-                // P^T operand: the k slots hold (hi of tokens 0..3, lo of tokens 0..3); the V^T
-                // operand repeats its four tokens, so one K=32 product adds V*hi + V*lo
-                uint4 pk;
-                Mfma<DT>::split(p[0], p[1], pk.x, pk.z);
-                Mfma<DT>::split(p[2], p[3], pk.y, pk.w);
+            for (int i = 0; i < 4; ++i) {
+                p[i] = valid[cb][i] ? __builtin_amdgcn_exp2f(sc[cb][i] - m) : 0.0f;
+                l += p[i];
+            }
+            // P^T operand: the k slots hold (hi of tokens 0..3, lo of tokens 0..3); the V^T
+            // operand repeats its four tokens, so one K=32 product adds V*hi + V*lo
+            uint4 pk;
+            Mfma<DT>::split(p[0], p[1], pk.x, pk.z);
+            Mfma<DT>::split(p[2], p[3], pk.y, pk.w);
 #pragma unroll
-                for (int t = 0; t < VT; ++t) {
-                    const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
-                    const int x = t >> 1;
-                    const uint32_t v01 = __builtin_amdgcn_perm(vf[cb][1].w[x], vf[cb][0].w[x], sel);
-                    const uint32_t v23 = __builtin_amdgcn_perm(vf[cb][3].w[x], vf[cb][2].w[x], sel);
-                    acc[t] = Mfma<DT>::mma(make_uint4(v01, v23, v01, v23), pk, acc[t]);
-                }
+            for (int t = 0; t < VT; ++t) {
+                const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+                const int x = t >> 1;
+                const uint32_t v01 = __builtin_amdgcn_perm(vf[cb][1].w[x], vf[cb][0].w[x], sel);
+                const uint32_t v23 = __builtin_amdgcn_perm(vf[cb][3].w[x], vf[cb][2].w[x], sel);
+                acc[t] = Mfma<DT>::mma(make_uint4(v01, v23, v01, v23), pk, acc[t]);
             }
         }
     }
 
-    // per-head sum over the four lane groups (they share m)
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    if (j == 0) {
-        s_m[w][col] = m;
-        s_l[w][col] = l;
+    // One block that is not wholly below `lim`: masked loads straight from global
+    // memory and, in the fused call, the new token from k_new/v_new (also written
+    // to its pool slot).
+    __device__ __forceinline__ void partial_block(const AttnArgs& a, const char* kb, const char* vb, int tb, int lim,
+                                                  int pos_new, size_t new_off, bool may_write) {
+        uint4 kf[1][KS];
+        VRow<NWORD> vf[1][4];
+        bool valid[1][4];
+        const int tk = tb + tau;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            kf[0][s] = make_uint4(0, 0, 0, 0);
+            if (tk < lim) {
+                kf[0][s] = ld16(kb + koff[s]);
+            } else if (APPEND && tk == pos_new) {
+                kf[0][s] = ld16_cached(a.k_new + new_off + (32 * s + 8 * j) * ES);
+                if (may_write) st16(a.k_pool_w + (kb - a.k_pool) + koff[s], kf[0][s]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tv = tb + 4 * i + j;
+#pragma unroll
+            for (int x = 0; x < NWORD; ++x) vf[0][i].w[x] = 0;
+            valid[0][i] = false;
+            if (tv < lim) {
+                vf[0][i] = ldv<NWORD>(vb + voff[i]);
+                valid[0][i] = true;
+            } else if (APPEND && tv == pos_new) {
+                vf[0][i] = ldv_plain<NWORD>(a.v_new + new_off + col * VT * ES);
+                valid[0][i] = true;
+                if (may_write) stv<NWORD>(a.v_pool_w + (vb - a.v_pool) + voff[i], vf[0][i]);
+            }
+        }
+        accumulate<1>(kf, vf, valid);
     }
-#pragma unroll
-    for (int t = 0; t < VT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s_o[w][col][(4 * j + i) * VT + t] = acc[t][i];
-    __syncthreads();
-    const bool bad = s_bad != 0;
-    for (int x = threadIdx.x; x < G * D; x += NW * 64) {
-        const int hh = x / D;
-        const int d = x - hh * D;
-        float M = s_m[0][hh];
-#pragma unroll
-        for (int i = 1; i < NW; ++i) M = fmaxf(M, s_m[i][hh]);
-        float L = 0.0f, O = 0.0f;
-#pragma unroll
-        for (int i = 0; i < NW; ++i) {
-            const float f = __builtin_amdgcn_exp2f(s_m[i][hh] - M);
-            L += s_l[i][hh] * f;
-            O += s_o[i][hh][d] * f;
+
+    // Merge the waves' states through LDS (s_o: [NW][16][DP] floats, DP >= D) and
+    // write the normalised output, or this partition's (o / l, lse) for the merge kernel.
+    template <int NW, int DP>
+    __device__ __forceinline__ void finish(const AttnArgs& a, float (*s_m)[16], float (*s_l)[16], float* s_o_raw,
+                                           int w, int b, int g, int part, bool bad) {
+        static_assert(DP >= D, "merge row");
+        float (*s_o)[16][DP] = reinterpret_cast<float (*)[16][DP]>(s_o_raw);
+        // per-head sum over the four lane groups (they share m)
+        l += __shfl_xor(l, 16, 64);
+        l += __shfl_xor(l, 32, 64);
+        if (j == 0) {
+            s_m[w][col] = m;
+            s_l[w][col] = l;
         }
-        const size_t row = (size_t)b * a.H_q + (size_t)g * G + hh;
-        const float val = bad ? __builtin_nanf("") : O / L;
-        if (a.n_parts == 1) {
-            a.out[row * D + d] = val;
-        } else {
-            a.part_o[(row * a.n_parts + part) * D + d] = val;
-            // v_log_f32 is log base 2, matching the log2-domain scores
-            if (d == 0) a.part_lse[row * a.n_parts + part] = bad ? __builtin_nanf("") : M + __builtin_amdgcn_logf(L);
+#pragma unroll
+        for (int t = 0; t < VT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s_o[w][col][(4 * j + i) * VT + t] = acc[t][i];
+        __syncthreads();
+        const int G = a.G;
+        for (int x = threadIdx.x; x < G * D; x += NW * 64) {
+            const int hh = x / D;
+            const int d = x - hh * D;
+            float M = s_m[0][hh];
+#pragma unroll
+            for (int i = 1; i < NW; ++i) M = fmaxf(M, s_m[i][hh]);
+            float L = 0.0f, O = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NW; ++i) {
+                const float f = __builtin_amdgcn_exp2f(s_m[i][hh] - M);
+                L += s_l[i][hh] * f;
+                O += s_o[i][hh][d] * f;
+            }
+            const size_t row = (size_t)b * a.H_q + (size_t)g * G + hh;
+            const float val = bad ? __builtin_nanf("") : O / L;
+            if (a.n_parts == 1) {
+                a.out[row * D + d] = val;
+            } else {
+                a.part_o[(row * a.n_parts + part) * D + d] = val;
+                // v_log_f32 is log base 2, matching the log2-domain scores
+                if (d == 0) a.part_lse[row * a.n_parts + part] = bad ? __builtin_nanf("") : M + __builtin_amdgcn_logf(L);
+            }
         }
+    }
+};
+
+// Work unit of a workgroup.  gqa_unit returns false when the workgroup has
+// nothing to stream (it has already written what it owns).
+struct GqaUnit {
+    int part, b, g, n, start, end, lim, pos_new;
+};
+
+template <int D, int NW, bool APPEND>
+__device__ __forceinline__ bool gqa_unit(const AttnArgs& a, GqaUnit& u) {
+    const int BG = a.B * a.H_kv;
+    u.part = blockIdx.x / BG;
+    const int bg = blockIdx.x - u.part * BG;
+    u.b = bg / a.H_kv;
+    u.g = bg - u.b * a.H_kv;
+    u.n = APPEND ? a.positions[u.b] + 1 : a.context_lens[u.b];
+    const bool bad_len = APPEND ? (u.n < 1 || u.n > a.max_context_len) : (u.n < 0 || u.n > a.max_context_len);
+    if (bad_len || u.n == 0) {
+        if (a.n_parts == 1 && u.part == 0)
+            for (int x = threadIdx.x; x < a.G * D; x += NW * 64)
+                a.out[((size_t)u.b * a.H_q + (size_t)u.g * a.G) * D + x] = bad_len ? __builtin_nanf("") : 0.0f;
+        return false;
+    }
+    u.start = u.part * a.part_tokens;
+    if (u.start >= u.n) return false;
+    u.end = min(u.start + a.part_tokens, u.n);
+    u.lim = min(u.end, APPEND ? u.n - 1 : u.n);
+    // only the partition that ends at n holds the new token; a chunk may run past
+    // its partition's last block, so every other partition must never match it
+    u.pos_new = (APPEND && u.end == u.n) ? u.n - 1 : -1;
+    return true;
+}
+
+// Stage one window of the partition's block ids in LDS, range-checked.
+template <int NW>
+__device__ __forceinline__ void stage_ids(const AttnArgs& a, const int32_t* table, int first, int nr, int32_t* s_ids,
+                                          int* s_bad) {
+    for (int t = threadIdx.x; t < nr; t += NW * 64) {
+        int id = table[first + t];
+        if ((unsigned)id >= (unsigned)a.n_blocks) {
+            *s_bad = 1;
+            id = 0;
+        }
+        s_ids[t] = id;
     }
 }
 
-template <int DT, int D, int NW, int CH>
+// ---------------------------------------------------------------------------
+// Kernel 1: loads through registers, PF-deep pipeline per wave.
+// ---------------------------------------------------------------------------
+template <int DT, int D, int NW, int CH, int PF, bool APPEND>
+__global__ __launch_bounds__(NW * 64) void decode_gqa_kernel(const AttnArgs a) {
+    using L = GqaLane<DT, D, APPEND>;
+    constexpr int KS = L::KS, NWORD = L::NWORD, ES = L::ES;
+    __shared__ int32_t s_ids[kWindowBlocksG];
+    __shared__ int s_bad;
+    __shared__ float s_m[NW][16];
+    __shared__ float s_l[NW][16];
+    __shared__ float s_o[NW * 16 * (D + 4)];
+
+    GqaUnit u;
+    if (!gqa_unit<D, NW, APPEND>(a, u)) return;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
+    L st;
+    st.init(a, lane, u.b, u.g);
+
+    const int32_t* table = a.block_tables + (int64_t)u.b * a.bt_stride;
+    const int first_blk = u.start / kBlockSize;
+    const int nblk = (u.end - u.start + kBlockSize - 1) / kBlockSize;
+    const size_t blk_bytes = (size_t)a.H_kv * kBlockSize * D * ES;
+    const size_t head_bytes = (size_t)u.g * kBlockSize * D * ES;
+    const size_t new_off = ((size_t)u.b * a.new_row_stride + (size_t)u.g * D) * ES;
+
+    auto load_full = [&](uint4 (&kf)[CH][KS], VRow<NWORD> (&vf)[CH][4], int cb0) {
+        const char* kb[CH];
+        const char* vb[CH];
+#pragma unroll
+        for (int cb = 0; cb < CH; ++cb) {
+            const int id = __builtin_amdgcn_readfirstlane(s_ids[cb0 + cb]);
+            kb[cb] = a.k_pool + (size_t)id * blk_bytes + head_bytes;
+            vb[cb] = a.v_pool + (size_t)id * blk_bytes + head_bytes;
+        }
+#pragma unroll
+        for (int cb = 0; cb < CH; ++cb)
+#pragma unroll
+            for (int s = 0; s < KS; ++s) kf[cb][s] = ld16(kb[cb] + st.koff[s]);
+#pragma unroll
+        for (int cb = 0; cb < CH; ++cb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vf[cb][i] = ldv<NWORD>(vb[cb] + st.voff[i]);
+    };
+    bool all_valid[CH][4];
+#pragma unroll
+    for (int cb = 0; cb < CH; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) all_valid[cb][i] = true;
+
+    if (threadIdx.x == 0) s_bad = 0;
+    for (int r0 = 0; r0 < nblk; r0 += kWindowBlocksG) {
+        const int nr = min(kWindowBlocksG, nblk - r0);
+        __syncthreads();
+        stage_ids<NW>(a, table, first_blk + r0, nr, s_ids, &s_bad);
+        __syncthreads();
+        const bool any_bad = s_bad != 0;
+        const int nch = (nr + CH - 1) / CH;
+
+        // chunks wholly below `lim`: PF-deep pipeline, unguarded steady state
+        const int tok_r = u.start + r0 * kBlockSize;
+        const int nfull_all = max(0, min(nch, (u.lim - tok_r) / (CH * kBlockSize)));
+        const int nf = w < nfull_all ? (nfull_all - w + NW - 1) / NW : 0;
+        uint4 bk[PF][CH][KS];
+        VRow<NWORD> bv[PF][CH][4];
+        auto chunk_of = [&](int i) { return (w + NW * i) * CH; };
+        if (nf >= PF) {
+#pragma unroll
+            for (int v = 0; v < PF; ++v) load_full(bk[v], bv[v], chunk_of(v));
+            int i = 0;
+            for (; i + 2 * PF <= nf; i += PF) {
+#pragma unroll
+                for (int v = 0; v < PF; ++v) {
+                    st.template accumulate<CH>(bk[v], bv[v], all_valid);
+                    load_full(bk[v], bv[v], chunk_of(i + PF + v));
+                }
+            }
+            const int rem = nf - i - PF;
+#pragma unroll
+            for (int v = 0; v < PF; ++v) {
+                st.template accumulate<CH>(bk[v], bv[v], all_valid);
+                if (v < rem) load_full(bk[v], bv[v], chunk_of(i + PF + v));
+            }
+#pragma unroll
+            for (int v = 0; v < PF; ++v)
+                if (v < rem) st.template accumulate<CH>(bk[v], bv[v], all_valid);
+        } else {
+            for (int i = 0; i < nf; ++i) {
+                load_full(bk[0], bv[0], chunk_of(i));
+                st.template accumulate<CH>(bk[0], bv[0], all_valid);
+            }
+        }
+        // the partial chunk (at most one per round), block by block
+        for (int k = nfull_all + ((w - nfull_all) % NW + NW) % NW; k < nch; k += NW) {
+#pragma unroll
+            for (int cb = 0; cb < CH; ++cb) {
+                const int blk = k * CH + cb;
+                const int id = __builtin_amdgcn_readfirstlane(blk < nr ? s_ids[blk] : 0);
+                const char* kb = a.k_pool + (size_t)id * blk_bytes + head_bytes;
+                const char* vb = a.v_pool + (size_t)id * blk_bytes + head_bytes;
+                st.partial_block(a, kb, vb, tok_r + blk * kBlockSize, u.lim, u.pos_new, new_off, !any_bad);
+            }
+        }
+    }
+    st.template finish<NW, D + 4>(a, s_m, s_l, s_o, w, u.b, u.g, u.part, s_bad != 0);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 2: loads through LDS.  Each wave owns a ring of S slots; a slot holds
+// one block's K tile (chunk-swizzled rows) followed by its V tile.
+// ---------------------------------------------------------------------------
+template <int D>
+constexpr int gqa_tile_bytes() { return kBlockSize * D * 2; }
+
+
+template <int DT, int D, int NW, int S, bool APPEND>
+__global__ __launch_bounds__(NW * 64) void decode_gqa_lds_kernel(const AttnArgs a) {
+    using L = GqaLane<DT, D, APPEND>;
+    constexpr int KS = L::KS, NWORD = L::NWORD, ES = L::ES;
+    constexpr int TILE = gqa_tile_bytes<D>();
+    constexpr int SLOT = 2 * TILE;
+    constexpr int CPR = D * ES / 16;          // 16-byte chunks per token row
+    constexpr int NDMA = TILE / 1024;         // 1 KiB DMA instructions per tile
+    constexpr int PER_BLOCK = 2 * NDMA;       // vmcnt units per block (K + V)
+    static_assert(S >= 2 && S <= 4 && (S - 1) * PER_BLOCK < 64, "ring depth");
+
+    // one LDS object per ring slot, so that the compiler's alias analysis can tell
+    // a read of slot v from the DMAs still in flight into the other slots
+    __shared__ __attribute__((aligned(16))) char s_ring0[NW * SLOT];
+    __shared__ __attribute__((aligned(16))) char s_ring1[NW * SLOT];
+    __shared__ __attribute__((aligned(16))) char s_ring2[S > 2 ? NW * SLOT : 16];
+    __shared__ __attribute__((aligned(16))) char s_ring3[S > 3 ? NW * SLOT : 16];
+    __shared__ int32_t s_ids[kWindowBlocksG];
+    __shared__ int s_bad;
+    __shared__ float s_m[NW][16];
+    __shared__ float s_l[NW][16];
+
+    GqaUnit u;
+    if (!gqa_unit<D, NW, APPEND>(a, u)) return;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    L st;
+    st.init(a, lane, u.b, u.g);
+
+    // DMA source offsets (lane l of instruction i fills LDS byte i*1024 + 16 l):
+    // K rows are chunk-swizzled (LDS chunk p of row r holds global chunk p ^ (r % CPR)),
+    // V is copied as it lies.
+    int kdma[NDMA], vdma[NDMA];
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+        const int slot16 = i * 64 + lane;
+        const int row = slot16 / CPR;
+        const int p = slot16 % CPR;
+        kdma[i] = row * D * ES + ((p ^ (row % CPR)) * 16);
+        vdma[i] = slot16 * 16;
+    }
+    // LDS read offsets of this lane's K pieces, in the MFMA layout
+    int kread[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const int c = 4 * s + st.j;
+        kread[s] = st.tau * D * ES + ((c ^ (st.tau % CPR)) * 16);
+    }
+
+    const int32_t* table = a.block_tables + (int64_t)u.b * a.bt_stride;
+    const int first_blk = u.start / kBlockSize;
+    const int nblk = (u.end - u.start + kBlockSize - 1) / kBlockSize;
+    const size_t blk_bytes = (size_t)a.H_kv * kBlockSize * D * ES;
+    const size_t head_bytes = (size_t)u.g * kBlockSize * D * ES;
+    const size_t new_off = ((size_t)u.b * a.new_row_stride + (size_t)u.g * D) * ES;
+    auto slot_of = [&](int v) -> char* {
+        char* base = v == 0 ? s_ring0 : v == 1 ? s_ring1 : v == 2 ? s_ring2 : s_ring3;
+        return base + w * SLOT;
+    };
+
+    auto issue = [&](int v, int blk) {   // DMA round-local block `blk` into ring slot v
+        const int id = __builtin_amdgcn_readfirstlane(s_ids[blk]);
+        const char* kt = a.k_pool + (size_t)id * blk_bytes + head_bytes;
+        const char* vt = a.v_pool + (size_t)id * blk_bytes + head_bytes;
+        char* slot = slot_of(v);
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) dma16(kt + kdma[i], slot + i * 1024);
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) dma16(vt + vdma[i], slot + TILE + i * 1024);
+    };
+    bool all_valid[1][4] = {{true, true, true, true}};
+    auto consume = [&](int v) {   // ring slot v -> registers -> softmax / MFMA update
+        const char* slot = slot_of(v);
+        uint4 kf[1][KS];
+        VRow<NWORD> vf[1][4];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) kf[0][s] = *reinterpret_cast<const uint4*>(slot + kread[s]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vf[0][i] = ldv_plain<NWORD>(slot + TILE + st.voff[i]);
+        st.template accumulate<1>(kf, vf, all_valid);
+    };
+    // wait until at most `after` blocks' DMAs issued after the wanted block are pending
+    auto wait_blocks = [&](int after) {
+        if (after <= 0) wait_vmcnt<0>();
+        else if (after == 1) wait_vmcnt<PER_BLOCK>();
+        else if (after == 2) wait_vmcnt<(S > 2 ? 2 : 1) * PER_BLOCK>();
+        else wait_vmcnt<(S - 1) * PER_BLOCK>();
+    };
+
+    if (threadIdx.x == 0) s_bad = 0;
+    for (int r0 = 0; r0 < nblk; r0 += kWindowBlocksG) {
+        const int nr = min(kWindowBlocksG, nblk - r0);
+        __syncthreads();
+        stage_ids<NW>(a, table, first_blk + r0, nr, s_ids, &s_bad);
+        __syncthreads();
+        const bool any_bad = s_bad != 0;
+
+        // blocks wholly below `lim`; wave w takes blk = w, w + NW, ...
+        const int tok_r = u.start + r0 * kBlockSize;
+        const int nfull_all = max(0, min(nr, (u.lim - tok_r) / kBlockSize));
+        const int nf = w < nfull_all ? (nfull_all - w + NW - 1) / NW : 0;
+        auto blk_of = [&](int i) { return w + NW * i; };
+        if (nf >= S) {
+#pragma unroll
+            for (int v = 0; v < S; ++v) issue(v, blk_of(v));
+            int i = 0;
+            for (; i + 2 * S <= nf; i += S) {
+#pragma unroll
+                for (int v = 0; v < S; ++v) {
+                    wait_vmcnt<(S - 1) * PER_BLOCK>();
+                    consume(v);
+                    issue(v, blk_of(i + S + v));
+                }
+            }
+            const int rem = nf - i - S;   // in [0, S)
+#pragma unroll
+            for (int v = 0; v < S; ++v) {
+                wait_blocks(S - 1 - v + min(v, rem));
+                consume(v);
+                if (v < rem) issue(v, blk_of(i + S + v));
+            }
+#pragma unroll
+            for (int v = 0; v < S; ++v)
+                if (v < rem) {
+                    wait_blocks(rem - 1 - v);
+                    consume(v);
+                }
+        } else {
+            for (int i = 0; i < nf; ++i) {
+                issue(0, blk_of(i));
+                wait_vmcnt<0>();
+                consume(0);
+            }
+        }
+        // remaining (partial) blocks of the round, straight from global memory
+        for (int blk = nfull_all + ((w - nfull_all) % NW + NW) % NW; blk < nr; blk += NW) {
+            const int id = __builtin_amdgcn_readfirstlane(s_ids[blk]);
+            const char* kb = a.k_pool + (size_t)id * blk_bytes + head_bytes;
+            const char* vb = a.v_pool + (size_t)id * blk_bytes + head_bytes;
+            st.partial_block(a, kb, vb, tok_r + blk * kBlockSize, u.lim, u.pos_new, new_off, !any_bad);
+        }
+    }
+    __syncthreads();   // every wave is done with its ring: the merge reuses that LDS
+    // unpadded [NW][16][D] floats are exactly NW * SLOT bytes: the merge fits in slot 0's object
+    static_assert(NW * 16 * D * 4 <= NW * SLOT, "merge area");
+    st.template finish<NW, D>(a, s_m, s_l, reinterpret_cast<float*>(s_ring0), w, u.b, u.g, u.part, s_bad != 0);
+}
+
+// ---------------------------------------------------------------------------
+// dispatch
+// ---------------------------------------------------------------------------
+template <int DT, int D, int NW, int CH, int PF>
 static hipError_t launch_gqa_t(bool append, const AttnArgs& a, unsigned grid, hipStream_t stream) {
     if (append)
-        hipLaunchKernelGGL((decode_gqa_kernel<DT, D, NW, CH, true>), dim3(grid), dim3(NW * 64), 0, stream, a);
+        hipLaunchKernelGGL((decode_gqa_kernel<DT, D, NW, CH, PF, true>), dim3(grid), dim3(NW * 64), 0, stream, a);
     else
-        hipLaunchKernelGGL((decode_gqa_kernel<DT, D, NW, CH, false>), dim3(grid), dim3(NW * 64), 0, stream, a);
+        hipLaunchKernelGGL((decode_gqa_kernel<DT, D, NW, CH, PF, false>), dim3(grid), dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
+template <int DT, int D, int NW, int S>
+static hipError_t launch_gqa_lds_t(bool append, const AttnArgs& a, unsigned grid, hipStream_t stream) {
+    if (append)
+        hipLaunchKernelGGL((decode_gqa_lds_kernel<DT, D, NW, S, true>), dim3(grid), dim3(NW * 64), 0, stream, a);
+    else
+        hipLaunchKernelGGL((decode_gqa_lds_kernel<DT, D, NW, S, false>), dim3(grid), dim3(NW * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
+// (waves, blocks per chunk, chunks in flight) of the register kernel; (waves, ring slots) of the LDS kernel
+#define PKV_GQA_VARIANTS(X) X(4, 1, 1) X(4, 1, 2) X(2, 1, 1) X(2, 1, 2) X(4, 2, 1)
+#define PKV_GQA_LDS_VARIANTS(X) X(2, 2) X(2, 3) X(2, 4) X(4, 2) X(4, 3) X(8, 2)
+
 template <int DT, int D>
-static hipError_t launch_gqa_d(int nw, int ch, bool append, const AttnArgs& a, unsigned grid, hipStream_t s) {
-    switch (nw * 10 + ch) {
-    case 21: return launch_gqa_t<DT, D, 2, 1>(append, a, grid, s);
-    case 22: return launch_gqa_t<DT, D, 2, 2>(append, a, grid, s);
-    case 41: return launch_gqa_t<DT, D, 4, 1>(append, a, grid, s);
-    case 42: return launch_gqa_t<DT, D, 4, 2>(append, a, grid, s);
+static hipError_t launch_gqa_d(int kind, int nw, int ch, int pf, bool append, const AttnArgs& a, unsigned grid,
+                               hipStream_t s) {
+    if (kind == 0) {
+        switch (nw * 100 + ch * 10 + pf) {
+#define PKV_CASE(NW_, CH_, PF_) \
+    case NW_ * 100 + CH_ * 10 + PF_: return launch_gqa_t<DT, D, NW_, CH_, PF_>(append, a, grid, s);
+            PKV_GQA_VARIANTS(PKV_CASE)
+#undef PKV_CASE
+        default: return hipErrorInvalidValue;
+        }
+    }
+    switch (nw * 10 + pf) {
+#define PKV_CASE(NW_, S_) \
+    case NW_ * 10 + S_: return launch_gqa_lds_t<DT, D, NW_, S_>(append, a, grid, s);
+        PKV_GQA_LDS_VARIANTS(PKV_CASE)
+#undef PKV_CASE
     default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_decode_gqa(int dtype, int D, int nw, int ch, bool append, const AttnArgs& a,
+hipError_t launch_decode_gqa(int dtype, int D, int kind, int nw, int ch, int pf, bool append, const AttnArgs& a,
                              unsigned grid, hipStream_t stream) {
     switch (dtype * 1000 + D) {
-    case DT_F16 * 1000 + 64: return launch_gqa_d<DT_F16, 64>(nw, ch, append, a, grid, stream);
-    case DT_F16 * 1000 + 128: return launch_gqa_d<DT_F16, 128>(nw, ch, append, a, grid, stream);
-    case DT_BF16 * 1000 + 64: return launch_gqa_d<DT_BF16, 64>(nw, ch, append, a, grid, stream);
-    case DT_BF16 * 1000 + 128: return launch_gqa_d<DT_BF16, 128>(nw, ch, append, a, grid, stream);
+    case DT_F16 * 1000 + 64: return launch_gqa_d<DT_F16, 64>(kind, nw, ch, pf, append, a, grid, stream);
+    case DT_F16 * 1000 + 128: return launch_gqa_d<DT_F16, 128>(kind, nw, ch, pf, append, a, grid, stream);
+    case DT_BF16 * 1000 + 64: return launch_gqa_d<DT_BF16, 64>(kind, nw, ch, pf, append, a, grid, stream);
+    case DT_BF16 * 1000 + 128: return launch_gqa_d<DT_BF16, 128>(kind, nw, ch, pf, append, a, grid, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
-bool gqa_variant_exists(int nw, int ch) {
-    return (nw == 2 || nw == 4) && (ch == 1 || ch == 2);
+bool gqa_variant_exists(int kind, int nw, int ch, int pf) {
+    if (kind == 0) {
+        switch (nw * 100 + ch * 10 + pf) {
+#define PKV_CASE(NW_, CH_, PF_) case NW_ * 100 + CH_ * 10 + PF_:
+            PKV_GQA_VARIANTS(PKV_CASE)
+#undef PKV_CASE
+            return true;
+        default: return false;
+        }
+    }
+    if (ch != 1) return false;
+    switch (nw * 10 + pf) {
+#define PKV_CASE(NW_, S_) case NW_ * 10 + S_:
+        PKV_GQA_LDS_VARIANTS(PKV_CASE)
+#undef PKV_CASE
+        return true;
+    default: return false;
+    }
 }
 
 }  // namespace pkv

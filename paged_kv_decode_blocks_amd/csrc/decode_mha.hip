@@ -32,7 +32,7 @@ namespace pkv {
 
 constexpr int kWindowBlocks = 256;
 
-template <int DT, int D, int NW, int CH, bool APPEND>
+template <int DT, int D, int NW, int CH, int PF, bool APPEND>
 __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(const AttnArgs a) {
     constexpr int ES = Dt<DT>::bytes;
     constexpr int E = 16 / ES;                // elements per 16-byte lane vector
@@ -49,7 +49,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(const AttnArgs a) {
     __shared__ float s_o[NW][D];
 
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
     const int r = lane / LPT;
     const int c = lane % LPT;
 
@@ -97,6 +97,50 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(const AttnArgs a) {
     const size_t new_off = ((size_t)b * a.new_row_stride + (size_t)g * D + c * E) * ES;
     const bool writer = APPEND && (h % a.G) == 0;
 
+    // Issue the K then V loads of the CH blocks starting at round-local block cb0.
+    auto load_full = [&](uint4 (&kv)[NL], uint4 (&vv)[NL], int cb0) {
+        const char* kb[CH];
+        const char* vb[CH];
+#pragma unroll
+        for (int cb = 0; cb < CH; ++cb) {
+            const int id = __builtin_amdgcn_readfirstlane(s_ids[cb0 + cb]);
+            kb[cb] = a.k_pool + (size_t)id * blk_bytes + head_bytes;
+            vb[cb] = a.v_pool + (size_t)id * blk_bytes + head_bytes;
+        }
+#pragma unroll
+        for (int cb = 0; cb < CH; ++cb)
+#pragma unroll
+            for (int i = 0; i < LPB; ++i) kv[cb * LPB + i] = ld16(kb[cb] + lane_off[i]);
+#pragma unroll
+        for (int cb = 0; cb < CH; ++cb)
+#pragma unroll
+            for (int i = 0; i < LPB; ++i) vv[cb * LPB + i] = ld16(vb[cb] + lane_off[i]);
+    };
+    // Online-softmax update with one chunk: scores, running max, rescale, weighted V.
+    auto accumulate = [&](const uint4 (&kv)[NL], const uint4 (&vv)[NL], const bool (&valid)[NL]) {
+        float s[NL];
+#pragma unroll
+        for (int j = 0; j < NL; ++j) s[j] = mul_rn(group_sum<LPT>(dot16<DT>(qv, kv[j])), a.scale_log2);
+        float mloc = kNegBig;
+#pragma unroll
+        for (int j = 0; j < NL; ++j) mloc = valid[j] ? fmaxf(mloc, s[j]) : mloc;
+        const float m_new = fmaxf(m, mloc);
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        m = m_new;
+        l *= alpha;
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] *= alpha;
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const float p = valid[j] ? __builtin_amdgcn_exp2f(s[j] - m) : 0.0f;
+            l += p;
+            axpy16<DT>(o, p, vv[j]);
+        }
+    };
+    bool all_valid[NL];
+#pragma unroll
+    for (int j = 0; j < NL; ++j) all_valid[j] = true;
+
     if (threadIdx.x == 0) s_bad = 0;
     for (int r0 = 0; r0 < nblk; r0 += kWindowBlocks) {
         const int nr = min(kWindowBlocks, nblk - r0);
@@ -112,7 +156,48 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(const AttnArgs a) {
         __syncthreads();
         const bool any_bad = s_bad != 0;
         const int nch = (nr + CH - 1) / CH;
-        for (int k = w; k < nch; k += NW) {
+
+        // Chunks that lie wholly below `lim` need no masking.  Each wave takes its
+        // share of them (k = w, w + NW, ...) through a PF-deep load pipeline: the
+        // loads of chunk i + PF are issued as soon as chunk i has been consumed, so
+        // a wave keeps PF chunks of K/V in flight while it computes.
+        const int tok_r = start + r0 * kBlockSize;
+        const int nfull_all = max(0, min(nch, (lim - tok_r) / (CH * kBlockSize)));
+        const int nf = w < nfull_all ? (nfull_all - w + NW - 1) / NW : 0;
+        uint4 bk[PF][NL], bv[PF][NL];
+        auto chunk_of = [&](int i) { return (w + NW * i) * CH; };   // round-local first block of the wave's chunk i
+        if (nf >= PF) {
+#pragma unroll
+            for (int u = 0; u < PF; ++u) load_full(bk[u], bv[u], chunk_of(u));
+            // steady state: every consumed buffer is refilled, no guards in the body
+            int i = 0;
+            for (; i + 2 * PF <= nf; i += PF) {
+#pragma unroll
+                for (int u = 0; u < PF; ++u) {
+                    accumulate(bk[u], bv[u], all_valid);
+                    load_full(bk[u], bv[u], chunk_of(i + PF + u));
+                }
+            }
+            // drain: nf - i is in [PF, 2 PF)
+            const int rem = nf - i - PF;
+#pragma unroll
+            for (int u = 0; u < PF; ++u) {
+                accumulate(bk[u], bv[u], all_valid);
+                if (u < rem) load_full(bk[u], bv[u], chunk_of(i + PF + u));
+            }
+#pragma unroll
+            for (int u = 0; u < PF; ++u)
+                if (u < rem) accumulate(bk[u], bv[u], all_valid);
+        } else {
+            for (int i = 0; i < nf; ++i) {
+                load_full(bk[0], bv[0], chunk_of(i));
+                accumulate(bk[0], bv[0], all_valid);
+            }
+        }
+
+        // The partial chunk (at most one per round): masked loads, and in the
+        // fused call the new token from k_new/v_new.
+        for (int k = nfull_all + ((w - nfull_all) % NW + NW) % NW; k < nch; k += NW) {
             const int cb0 = k * CH;
             const int tok0 = start + (r0 + cb0) * kBlockSize;
             const char* kb[CH];
@@ -125,61 +210,30 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(const AttnArgs a) {
             }
             uint4 kv[NL], vv[NL];
             bool valid[NL];
-            const bool fast = tok0 + CH * kBlockSize <= lim;
-            if (fast) {
 #pragma unroll
-                for (int cb = 0; cb < CH; ++cb)
+            for (int cb = 0; cb < CH; ++cb)
 #pragma unroll
-                    for (int i = 0; i < LPB; ++i) kv[cb * LPB + i] = ld16(kb[cb] + lane_off[i]);
-#pragma unroll
-                for (int cb = 0; cb < CH; ++cb)
-#pragma unroll
-                    for (int i = 0; i < LPB; ++i) vv[cb * LPB + i] = ld16(vb[cb] + lane_off[i]);
-#pragma unroll
-                for (int j = 0; j < NL; ++j) valid[j] = true;
-            } else {
-#pragma unroll
-                for (int cb = 0; cb < CH; ++cb)
-#pragma unroll
-                    for (int i = 0; i < LPB; ++i) {
-                        const int j = cb * LPB + i;
-                        const int t = tok0 + cb * kBlockSize + i * TPL + r;
-                        kv[j] = make_uint4(0, 0, 0, 0);
-                        vv[j] = make_uint4(0, 0, 0, 0);
-                        valid[j] = false;
-                        if (t < lim) {
-                            kv[j] = ld16(kb[cb] + lane_off[i]);
-                            vv[j] = ld16(vb[cb] + lane_off[i]);
-                            valid[j] = true;
-                        } else if (APPEND && t == pos_new) {
-                            kv[j] = ld16_cached(a.k_new + new_off);
-                            vv[j] = ld16_cached(a.v_new + new_off);
-                            valid[j] = true;
-                            if (writer && !any_bad) {
-                                st16(a.k_pool_w + (kb[cb] - a.k_pool) + lane_off[i], kv[j]);
-                                st16(a.v_pool_w + (vb[cb] - a.v_pool) + lane_off[i], vv[j]);
-                            }
+                for (int i = 0; i < LPB; ++i) {
+                    const int j = cb * LPB + i;
+                    const int t = tok0 + cb * kBlockSize + i * TPL + r;
+                    kv[j] = make_uint4(0, 0, 0, 0);
+                    vv[j] = make_uint4(0, 0, 0, 0);
+                    valid[j] = false;
+                    if (t < lim) {
+                        kv[j] = ld16(kb[cb] + lane_off[i]);
+                        vv[j] = ld16(vb[cb] + lane_off[i]);
+                        valid[j] = true;
+                    } else if (APPEND && t == pos_new) {
+                        kv[j] = ld16_cached(a.k_new + new_off);
+                        vv[j] = ld16_cached(a.v_new + new_off);
+                        valid[j] = true;
+                        if (writer && !any_bad) {
+                            st16(a.k_pool_w + (kb[cb] - a.k_pool) + lane_off[i], kv[j]);
+                            st16(a.v_pool_w + (vb[cb] - a.v_pool) + lane_off[i], vv[j]);
                         }
                     }
-            }
-            float s[NL];
-#pragma unroll
-            for (int j = 0; j < NL; ++j) s[j] = mul_rn(group_sum<LPT>(dot16<DT>(qv, kv[j])), a.scale_log2);
-            float mloc = kNegBig;
-#pragma unroll
-            for (int j = 0; j < NL; ++j) mloc = valid[j] ? fmaxf(mloc, s[j]) : mloc;
-            const float m_new = fmaxf(m, mloc);
-            const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-            m = m_new;
-            l *= alpha;
-#pragma unroll
-            for (int e = 0; e < E; ++e) o[e] *= alpha;
-#pragma unroll
-            for (int j = 0; j < NL; ++j) {
-                const float p = valid[j] ? __builtin_amdgcn_exp2f(s[j] - m) : 0.0f;
-                l += p;
-                axpy16<DT>(o, p, vv[j]);
-            }
+                }
+            accumulate(kv, vv, valid);
         }
     }
 
@@ -231,42 +285,47 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(const AttnArgs a) {
 // ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
-template <int DT, int D, int NW, int CH>
+template <int DT, int D, int NW, int CH, int PF>
 static hipError_t launch_mha_t(bool append, const AttnArgs& a, unsigned grid, hipStream_t stream) {
     if (append)
-        hipLaunchKernelGGL((decode_mha_kernel<DT, D, NW, CH, true>), dim3(grid), dim3(NW * 64), 0, stream, a);
+        hipLaunchKernelGGL((decode_mha_kernel<DT, D, NW, CH, PF, true>), dim3(grid), dim3(NW * 64), 0, stream, a);
     else
-        hipLaunchKernelGGL((decode_mha_kernel<DT, D, NW, CH, false>), dim3(grid), dim3(NW * 64), 0, stream, a);
+        hipLaunchKernelGGL((decode_mha_kernel<DT, D, NW, CH, PF, false>), dim3(grid), dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
 template <int DT, int D>
-static hipError_t launch_mha_d(int nw, int ch, bool append, const AttnArgs& a, unsigned grid, hipStream_t s) {
-    switch (nw * 10 + ch) {
-    case 42: return launch_mha_t<DT, D, 4, 2>(append, a, grid, s);
-    case 44: return launch_mha_t<DT, D, 4, 4>(append, a, grid, s);
-    case 82: return launch_mha_t<DT, D, 8, 2>(append, a, grid, s);
-    case 84: return launch_mha_t<DT, D, 8, 4>(append, a, grid, s);
-    case 162: return launch_mha_t<DT, D, 16, 2>(append, a, grid, s);
+static hipError_t launch_mha_d(int nw, int ch, int pf, bool append, const AttnArgs& a, unsigned grid, hipStream_t s) {
+    switch (nw * 100 + ch * 10 + pf) {
+    case 421: return launch_mha_t<DT, D, 4, 2, 1>(append, a, grid, s);
+    case 422: return launch_mha_t<DT, D, 4, 2, 2>(append, a, grid, s);
+    case 423: return launch_mha_t<DT, D, 4, 2, 3>(append, a, grid, s);
+    case 412: return launch_mha_t<DT, D, 4, 1, 2>(append, a, grid, s);
+    case 414: return launch_mha_t<DT, D, 4, 1, 4>(append, a, grid, s);
+    case 822: return launch_mha_t<DT, D, 8, 2, 2>(append, a, grid, s);
+    case 821: return launch_mha_t<DT, D, 8, 2, 1>(append, a, grid, s);
     default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_decode_mha(int dtype, int D, int nw, int ch, bool append, const AttnArgs& a,
+hipError_t launch_decode_mha(int dtype, int D, int nw, int ch, int pf, bool append, const AttnArgs& a,
                              unsigned grid, hipStream_t stream) {
     switch (dtype * 1000 + D) {
-    case DT_F32 * 1000 + 64: return launch_mha_d<DT_F32, 64>(nw, ch, append, a, grid, stream);
-    case DT_F32 * 1000 + 128: return launch_mha_d<DT_F32, 128>(nw, ch, append, a, grid, stream);
-    case DT_F16 * 1000 + 64: return launch_mha_d<DT_F16, 64>(nw, ch, append, a, grid, stream);
-    case DT_F16 * 1000 + 128: return launch_mha_d<DT_F16, 128>(nw, ch, append, a, grid, stream);
-    case DT_BF16 * 1000 + 64: return launch_mha_d<DT_BF16, 64>(nw, ch, append, a, grid, stream);
-    case DT_BF16 * 1000 + 128: return launch_mha_d<DT_BF16, 128>(nw, ch, append, a, grid, stream);
+    case DT_F32 * 1000 + 64: return launch_mha_d<DT_F32, 64>(nw, ch, pf, append, a, grid, stream);
+    case DT_F32 * 1000 + 128: return launch_mha_d<DT_F32, 128>(nw, ch, pf, append, a, grid, stream);
+    case DT_F16 * 1000 + 64: return launch_mha_d<DT_F16, 64>(nw, ch, pf, append, a, grid, stream);
+    case DT_F16 * 1000 + 128: return launch_mha_d<DT_F16, 128>(nw, ch, pf, append, a, grid, stream);
+    case DT_BF16 * 1000 + 64: return launch_mha_d<DT_BF16, 64>(nw, ch, pf, append, a, grid, stream);
+    case DT_BF16 * 1000 + 128: return launch_mha_d<DT_BF16, 128>(nw, ch, pf, append, a, grid, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
-bool mha_variant_exists(int nw, int ch) {
-    return ((nw == 4 || nw == 8) && (ch == 2 || ch == 4)) || (nw == 16 && ch == 2);
+bool mha_variant_exists(int nw, int ch, int pf) {
+    switch (nw * 100 + ch * 10 + pf) {
+    case 421: case 422: case 423: case 412: case 414: case 822: case 821: return true;
+    default: return false;
+    }
 }
 
 }  // namespace pkv

@@ -14,6 +14,7 @@ namespace pkv {
 template <int D>
 __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeArgs a) {
     constexpr int PER = D / 64;   // output elements per lane
+    constexpr int U = 8;          // partial rows in flight per lane
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + wave;
@@ -30,6 +31,11 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeArgs a) {
     }
     const int np = min((n + a.part_tokens - 1) / a.part_tokens, a.n_parts);
     const float* lse = a.part_lse + (size_t)row * a.n_parts;
+    const float* po = a.part_o + (size_t)row * a.n_parts * D;
+    float acc[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
+    // global max over all partitions (lane p holds partitions p, p + 64, ...)
     float M = -__builtin_inff();
     bool nan = false;
     for (int p = lane; p < np; p += 64) {
@@ -40,17 +46,31 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeArgs a) {
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
     nan = __any(nan);
-    float acc[PER];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
     float L = 0.0f;
-    const float* po = a.part_o + (size_t)row * a.n_parts * D;
-    for (int p = 0; p < np; ++p) {
-        const float wgt = __builtin_amdgcn_exp2f(lse[p] - M);
-        L += wgt;
+    for (int p0 = 0; p0 < np; p0 += 64) {
+        // lane p holds the weight of partition p0 + p; the partial rows are then read
+        // U at a time, in partition order, each weight taken from its lane
+        const int pl = p0 + lane;
+        const float wl = pl < np ? __builtin_amdgcn_exp2f(lse[pl] - M) : 0.0f;
+        L += wl;
+        const int cnt = min(64, np - p0);
+        for (int q0 = 0; q0 < cnt; q0 += U) {
+            float v[U][PER];
 #pragma unroll
-        for (int k = 0; k < PER; ++k) acc[k] = fmaf(wgt, po[(size_t)p * D + lane + 64 * k], acc[k]);
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int k = 0; k < PER; ++k)
+                    v[u][k] = q0 + u < cnt ? po[(size_t)(p0 + q0 + u) * D + lane + 64 * k] : 0.0f;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float wu = __shfl(wl, min(q0 + u, 63), 64);
+#pragma unroll
+                for (int k = 0; k < PER; ++k) acc[k] = fmaf(q0 + u < cnt ? wu : 0.0f, v[u][k], acc[k]);
+            }
+        }
     }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) L += __shfl_xor(L, off, 64);
     const float inv = 1.0f / L;
 #pragma unroll
     for (int k = 0; k < PER; ++k) o[lane + 64 * k] = nan ? __builtin_nanf("") : acc[k] * inv;

@@ -30,13 +30,15 @@ struct MergeArgs {
 };
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
-hipError_t launch_decode_mha(int dtype, int D, int nw, int ch, bool append, const AttnArgs& a,
+hipError_t launch_decode_mha(int dtype, int D, int nw, int ch, int pf, bool append, const AttnArgs& a,
                              unsigned grid, hipStream_t stream);
-hipError_t launch_decode_gqa(int dtype, int D, int nw, int ch, bool append, const AttnArgs& a,
+// kind 0: K/V through registers (nw, ch, pf = chunks in flight); kind 1: K/V through an LDS ring
+// (nw, ch = 1, pf = ring slots per wave)
+hipError_t launch_decode_gqa(int dtype, int D, int kind, int nw, int ch, int pf, bool append, const AttnArgs& a,
                              unsigned grid, hipStream_t stream);
 hipError_t launch_lse_merge(int D, const MergeArgs& a, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, size_t bytes, unsigned* sink, int grid, hipStream_t stream);
-bool mha_variant_exists(int nw, int ch);
-bool gqa_variant_exists(int nw, int ch);
+bool mha_variant_exists(int nw, int ch, int pf);
+bool gqa_variant_exists(int kind, int nw, int ch, int pf);
 
 }  // namespace pkv

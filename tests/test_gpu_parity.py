@@ -297,3 +297,70 @@ def test_bad_device_metadata_gives_nan_rows(torch_dev):
         got = out.cpu().numpy()
         assert_close(got[0], ref[0], "f16", f"good row P={P}")
         assert np.all(np.isnan(got[1])) and np.all(np.isnan(got[2])) and np.all(np.isnan(got[3]))
+
+
+# every launch-shape variant the library instantiates, forced through the plan's overrides
+GQA_VARIANTS = [(0, 4, 1, 1), (0, 4, 1, 2), (0, 2, 1, 1), (0, 2, 1, 2), (0, 4, 2, 1), (1, 2, 1, 2), (1, 2, 1, 3),
+                (1, 2, 1, 4), (1, 4, 1, 2), (1, 4, 1, 3), (1, 8, 1, 2)]
+MHA_VARIANTS = [(4, 2, 1), (4, 2, 2), (4, 2, 3), (4, 1, 2), (4, 1, 4), (8, 2, 1), (8, 2, 2)]
+
+
+def _with_env(env, fn):
+    import os
+    saved = {k: os.environ.get(k) for k in env}
+    try:
+        os.environ.update({k: str(v) for k, v in env.items()})
+        return fn()
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+@pytest.mark.parametrize("variant", GQA_VARIANTS)
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 64)])
+def test_gqa_launch_variants(torch_dev, variant, dtype, D):
+    kind, nw, ch, pf = variant
+    lens = (0, 1, 15, 16, 17, 100, 513, 1024, 3000)
+    w_attn = make_workload(get_config("c5", B=len(lens), H_q=16, H_kv=2, D=D, dtype=dtype, lengths=("fixed", lens),
+                                      pool=("factor", 1.2)), seed=32)
+    ref_attn = oracle.paged_decode_attention(dtype, w_attn.q, w_attn.k_pool, w_attn.v_pool, w_attn.block_tables,
+                                             w_attn.context_lens, w_attn.scale)
+    env = {"PKV_GQA_KIND": kind, "PKV_GQA_NW": nw, "PKV_GQA_CH": ch, "PKV_GQA_PF": pf}
+    for P in (0, 512):
+        got = _with_env(env, lambda: run_attention(torch_dev, w_attn, w_attn.k_pool, w_attn.v_pool, P))
+        launch = pkv.last_launch()
+        assert f"nw={nw} ch={ch} pf={pf}" in launch and ("lds" in launch) == bool(kind), launch
+        assert_close(got, ref_attn, dtype, f"attn {variant} P={P} [{launch}]")
+    # fused step (lengths >= 1 only)
+    wf = make_workload(get_config("c5", B=len(lens) - 1, H_q=16, H_kv=2, D=D, dtype=dtype,
+                                  lengths=("fixed", lens[1:]), pool=("factor", 1.2), append=True), seed=33)
+    ref, kp_ref, vp_ref = oracle.run_step(wf)
+    for P in (0, 512):
+        t = upload(wf)
+        out = _with_env(env, lambda: pkv.append_decode_attention(
+            t["q"], t["k_new"], t["v_new"], t["k_pool"], t["v_pool"], t["block_tables"], t["positions"],
+            float(wf.scale), max(lens), partition_size=P))
+        torch_dev.cuda.synchronize()
+        assert_close(out.cpu().numpy(), ref, dtype, f"fused {variant} P={P} [{pkv.last_launch()}]")
+        assert np.array_equal(to_numpy_bits(t["k_pool"], dtype).view(np.uint8), kp_ref.view(np.uint8))
+        assert np.array_equal(to_numpy_bits(t["v_pool"], dtype).view(np.uint8), vp_ref.view(np.uint8))
+
+
+@pytest.mark.parametrize("variant", MHA_VARIANTS)
+@pytest.mark.parametrize("dtype,D", [("f16", 128), ("bf16", 64), ("f32", 128)])
+def test_mha_launch_variants(torch_dev, variant, dtype, D):
+    nw, ch, pf = variant
+    lens = (0, 1, 15, 16, 17, 100, 513, 1024, 3000)
+    cfg = get_config("c2", B=len(lens), H_q=4, H_kv=4, D=D, dtype=dtype, lengths=("fixed", lens),
+                     pool=("factor", 1.2))
+    w = make_workload(cfg, seed=41)
+    ref = oracle.paged_decode_attention(dtype, w.q, w.k_pool, w.v_pool, w.block_tables, w.context_lens, w.scale)
+    env = {"PKV_MHA_NW": nw, "PKV_MHA_CH": ch, "PKV_MHA_PF": pf}
+    for P in (0, 512):
+        got = _with_env(env, lambda: run_attention(torch_dev, w, w.k_pool, w.v_pool, P))
+        launch = pkv.last_launch()
+        assert f"nw={nw} ch={ch} pf={pf}" in launch, launch
+        assert_close(got, ref, dtype, f"mha {variant} P={P} [{launch}]")
