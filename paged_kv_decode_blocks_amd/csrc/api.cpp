@@ -95,9 +95,10 @@ Plan make_plan(int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32
         p.ch = env_int("PKV_MHA_CH", ch);
         p.pf = env_int("PKV_MHA_PF", pf);
         if (!pkv::mha_variant_exists(p.nw, p.ch, p.pf)) { p.nw = nw; p.ch = ch; p.pf = pf; }
+        // f32 rows of 128 take 16 loads per 2-block chunk: deeper pipelines would spill
+        if (dtype == PKV_F32 && D == 128) { p.ch = 2; p.pf = 1; }
         p.grid = (unsigned)wgs;
     }
-    (void)D;
     if (p.n_parts > 1) {
         p.ws_o = align_up((size_t)B * H_q * p.n_parts * D * sizeof(float), 256);
         p.ws_lse = align_up((size_t)B * H_q * p.n_parts * sizeof(float), 256);

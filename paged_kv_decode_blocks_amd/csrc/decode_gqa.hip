@@ -311,19 +311,37 @@ struct GqaLane {
     }
 };
 
-// Work unit of a workgroup.  gqa_unit returns false when the workgroup has
-// nothing to stream (it has already written what it owns).
+// Work unit of a workgroup: (partition, request, KV head) from the block index.
 struct GqaUnit {
-    int part, b, g, n, start, end, lim, pos_new;
+    int part, b, g, n, start, end, lim, pos_new, first_blk;
 };
 
-template <int D, int NW, bool APPEND>
-__device__ __forceinline__ bool gqa_unit(const AttnArgs& a, GqaUnit& u) {
+__device__ __forceinline__ void gqa_indices(const AttnArgs& a, GqaUnit& u) {
     const int BG = a.B * a.H_kv;
     u.part = blockIdx.x / BG;
     const int bg = blockIdx.x - u.part * BG;
     u.b = bg / a.H_kv;
     u.g = bg - u.b * a.H_kv;
+    u.first_blk = u.part * (a.part_tokens / kBlockSize);
+}
+
+// The partition's first window of block ids, loaded before the length is known
+// (clamped to the table row; only entries below the real block count are used).
+template <int NW, int PRE>
+__device__ __forceinline__ void gqa_preload_ids(const AttnArgs& a, const GqaUnit& u, int (&pre)[PRE]) {
+    const int32_t* table = a.block_tables + (int64_t)u.b * a.bt_stride;
+    const int spec = min(min(a.part_tokens / kBlockSize, kWindowBlocksG), a.bt_stride - u.first_blk);
+#pragma unroll
+    for (int k = 0; k < PRE; ++k) {
+        const int t = threadIdx.x + k * NW * 64;
+        pre[k] = t < spec ? table[u.first_blk + t] : 0;
+    }
+}
+
+// Length checks; returns false when the workgroup has nothing to stream (it has
+// already written what it owns).
+template <int D, int NW, bool APPEND>
+__device__ __forceinline__ bool gqa_unit(const AttnArgs& a, GqaUnit& u) {
     u.n = APPEND ? a.positions[u.b] + 1 : a.context_lens[u.b];
     const bool bad_len = APPEND ? (u.n < 1 || u.n > a.max_context_len) : (u.n < 0 || u.n > a.max_context_len);
     if (bad_len || u.n == 0) {
@@ -342,12 +360,28 @@ __device__ __forceinline__ bool gqa_unit(const AttnArgs& a, GqaUnit& u) {
     return true;
 }
 
-// Stage one window of the partition's block ids in LDS, range-checked.
-template <int NW>
-__device__ __forceinline__ void stage_ids(const AttnArgs& a, const int32_t* table, int first, int nr, int32_t* s_ids,
-                                          int* s_bad) {
+// Stage one window of the partition's block ids in LDS, range-checked; the first
+// window comes from the preloaded registers.
+template <int NW, int PRE>
+__device__ __forceinline__ void stage_ids(const AttnArgs& a, const int32_t* table, int first, int r0, int nr,
+                                          const int (&pre)[PRE], int32_t* s_ids, int* s_bad) {
+    if (r0 == 0) {
+#pragma unroll
+        for (int k = 0; k < PRE; ++k) {
+            const int t = threadIdx.x + k * NW * 64;
+            if (t < nr) {
+                int id = pre[k];
+                if ((unsigned)id >= (unsigned)a.n_blocks) {
+                    *s_bad = 1;
+                    id = 0;
+                }
+                s_ids[t] = id;
+            }
+        }
+        return;
+    }
     for (int t = threadIdx.x; t < nr; t += NW * 64) {
-        int id = table[first + t];
+        int id = table[first + r0 + t];
         if ((unsigned)id >= (unsigned)a.n_blocks) {
             *s_bad = 1;
             id = 0;
@@ -370,14 +404,18 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_kernel(const AttnArgs a) {
     __shared__ float s_o[NW * 16 * (D + 4)];
 
     GqaUnit u;
-    if (!gqa_unit<D, NW, APPEND>(a, u)) return;
+    gqa_indices(a, u);
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
     L st;
-    st.init(a, lane, u.b, u.g);
+    st.init(a, lane, u.b, u.g);   // q loads, issued before the length is known
+    constexpr int PRE = (kWindowBlocksG + NW * 64 - 1) / (NW * 64);
+    int pre[PRE];
+    gqa_preload_ids<NW>(a, u, pre);
+    if (!gqa_unit<D, NW, APPEND>(a, u)) return;
 
     const int32_t* table = a.block_tables + (int64_t)u.b * a.bt_stride;
-    const int first_blk = u.start / kBlockSize;
+    const int first_blk = u.first_blk;
     const int nblk = (u.end - u.start + kBlockSize - 1) / kBlockSize;
     const size_t blk_bytes = (size_t)a.H_kv * kBlockSize * D * ES;
     const size_t head_bytes = (size_t)u.g * kBlockSize * D * ES;
@@ -411,7 +449,7 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_kernel(const AttnArgs a) {
     for (int r0 = 0; r0 < nblk; r0 += kWindowBlocksG) {
         const int nr = min(kWindowBlocksG, nblk - r0);
         __syncthreads();
-        stage_ids<NW>(a, table, first_blk + r0, nr, s_ids, &s_bad);
+        stage_ids<NW>(a, table, first_blk, r0, nr, pre, s_ids, &s_bad);
         __syncthreads();
         const bool any_bad = s_bad != 0;
         const int nch = (nr + CH - 1) / CH;
@@ -495,11 +533,15 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_lds_kernel(const AttnArgs 
     __shared__ float s_l[NW][16];
 
     GqaUnit u;
-    if (!gqa_unit<D, NW, APPEND>(a, u)) return;
+    gqa_indices(a, u);
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     L st;
-    st.init(a, lane, u.b, u.g);
+    st.init(a, lane, u.b, u.g);   // q loads, issued before the length is known
+    constexpr int PRE = (kWindowBlocksG + NW * 64 - 1) / (NW * 64);
+    int pre[PRE];
+    gqa_preload_ids<NW>(a, u, pre);
+    if (!gqa_unit<D, NW, APPEND>(a, u)) return;
 
     // DMA source offsets (lane l of instruction i fills LDS byte i*1024 + 16 l):
     // K rows are chunk-swizzled (LDS chunk p of row r holds global chunk p ^ (r % CPR)),
@@ -522,7 +564,7 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_lds_kernel(const AttnArgs 
     }
 
     const int32_t* table = a.block_tables + (int64_t)u.b * a.bt_stride;
-    const int first_blk = u.start / kBlockSize;
+    const int first_blk = u.first_blk;
     const int nblk = (u.end - u.start + kBlockSize - 1) / kBlockSize;
     const size_t blk_bytes = (size_t)a.H_kv * kBlockSize * D * ES;
     const size_t head_bytes = (size_t)u.g * kBlockSize * D * ES;
@@ -565,7 +607,7 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_lds_kernel(const AttnArgs 
     for (int r0 = 0; r0 < nblk; r0 += kWindowBlocksG) {
         const int nr = min(kWindowBlocksG, nblk - r0);
         __syncthreads();
-        stage_ids<NW>(a, table, first_blk + r0, nr, s_ids, &s_bad);
+        stage_ids<NW>(a, table, first_blk, r0, nr, pre, s_ids, &s_bad);
         __syncthreads();
         const bool any_bad = s_bad != 0;
 

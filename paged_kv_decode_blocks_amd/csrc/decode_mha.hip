@@ -60,7 +60,23 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(const AttnArgs a) {
     const int h = bh - b * a.H_q;
     const int g = h / a.G;
 
+    // Issued together, before the length is known: the length, this lane's q piece
+    // and the partition's first window of block ids (clamped to the table row;
+    // only the entries below the real block count are used).
     const int n = APPEND ? a.positions[b] + 1 : a.context_lens[b];
+    const uint4 qv = ld16_cached(a.q + ((int64_t)b * a.q_row_stride + (int64_t)h * D + c * E) * ES);
+    const int32_t* table = a.block_tables + (int64_t)b * a.bt_stride;
+    const int first_blk = part * (a.part_tokens / kBlockSize);
+    constexpr int PRE = (kWindowBlocks + NW * 64 - 1) / (NW * 64);
+    int pre[PRE];
+    {
+        const int spec = min(min(a.part_tokens / kBlockSize, kWindowBlocks), a.bt_stride - first_blk);
+#pragma unroll
+        for (int k = 0; k < PRE; ++k) {
+            const int t = threadIdx.x + k * NW * 64;
+            pre[k] = t < spec ? table[first_blk + t] : 0;
+        }
+    }
     const bool bad_len = APPEND ? (n < 1 || n > a.max_context_len) : (n < 0 || n > a.max_context_len);
     float* out_row = a.out + (size_t)bh * D;
     if (bad_len || n == 0) {
@@ -78,15 +94,11 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(const AttnArgs a) {
     // its partition's last block, so every other partition must never match it
     const int pos_new = (APPEND && end == n) ? n - 1 : -1;
 
-    const uint4 qv = ld16_cached(a.q + ((int64_t)b * a.q_row_stride + (int64_t)h * D + c * E) * ES);
-
     float m = kNegBig, l = 0.0f;
     float o[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) o[e] = 0.0f;
 
-    const int32_t* table = a.block_tables + (int64_t)b * a.bt_stride;
-    const int first_blk = start / kBlockSize;
     const int nblk = (end - start + kBlockSize - 1) / kBlockSize;
     const size_t blk_bytes = (size_t)a.H_kv * kBlockSize * D * ES;
     const size_t head_bytes = (size_t)g * kBlockSize * D * ES;
@@ -145,13 +157,28 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(const AttnArgs a) {
     for (int r0 = 0; r0 < nblk; r0 += kWindowBlocks) {
         const int nr = min(kWindowBlocks, nblk - r0);
         __syncthreads();
-        for (int t = threadIdx.x; t < nr; t += NW * 64) {
-            int id = table[first_blk + r0 + t];
-            if ((unsigned)id >= (unsigned)a.n_blocks) {
-                s_bad = 1;
-                id = 0;
+        if (r0 == 0) {   // the first window was loaded up front
+#pragma unroll
+            for (int k = 0; k < PRE; ++k) {
+                const int t = threadIdx.x + k * NW * 64;
+                if (t < nr) {
+                    int id = pre[k];
+                    if ((unsigned)id >= (unsigned)a.n_blocks) {
+                        s_bad = 1;
+                        id = 0;
+                    }
+                    s_ids[t] = id;
+                }
             }
-            s_ids[t] = id;
+        } else {
+            for (int t = threadIdx.x; t < nr; t += NW * 64) {
+                int id = table[first_blk + r0 + t];
+                if ((unsigned)id >= (unsigned)a.n_blocks) {
+                    s_bad = 1;
+                    id = 0;
+                }
+                s_ids[t] = id;
+            }
         }
         __syncthreads();
         const bool any_bad = s_bad != 0;
