@@ -77,13 +77,16 @@ def traffic_from_profile(workload: str, digest: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def read_ceiling(pkv, torch, dev, nbytes: int = 2 << 30, reps: int = 8) -> float:
-    """HBM read bandwidth (GB/s) of the library's plain streaming-read probe on this device."""
+def read_ceiling(pkv, torch, dev, nbytes: int = 4 << 30, reps: int = 6) -> float:
+    """HBM read bandwidth (GB/s) of the library's plain streaming-read probe on this device.
+
+    One 4 GiB read per launch (16x the Infinity Cache), best of a few grid sizes.
+    """
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
     best = 0.0
-    for grid in (8192, 16384):
+    for grid in (16384, 32768):
         times = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
