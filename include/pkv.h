@@ -78,7 +78,9 @@ typedef enum {
     PKV_ERR_INVALID_ARG = -2,   /* sizes, strides or alignment are inconsistent          */
     PKV_ERR_UNSUPPORTED = -3,   /* valid, but outside the supported set above            */
     PKV_ERR_WORKSPACE = -4,     /* workspace missing or smaller than required            */
-    PKV_ERR_HIP = -5            /* the HIP runtime reported an error when launching      */
+    PKV_ERR_HIP = -5,           /* the HIP runtime reported an error when launching      */
+    PKV_ERR_OUT_OF_BLOCKS = -6, /* block manager: too few free blocks                     */
+    PKV_ERR_SEQUENCE = -7       /* block manager: sequence id unknown, or already in use  */
 } pkv_status;
 
 /* Library version as major*10000 + minor*100 + patch. */
@@ -196,6 +198,121 @@ int pkv_append_decode_attention(int dtype,
  * fold to one particular value.  buf 16-byte aligned; 1 <= grid <= 2^20.
  */
 int pkv_probe_stream_read(const void* buf, size_t bytes, void* sink, int32_t grid, void* stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Block manager (host side): the paging lifecycle of the KV pool
+ * ---------------------------------------------------------------------------
+ * Physical blocks are handed out only when a sequence's next token needs one,
+ * and return to one global free pool as soon as no sequence maps them any more
+ * ("从 PagedAttention 到 Prefill-Decode 分离的深度解析", section 2.2, the third
+ * step: allocation on demand, reclaim at request end).  Several sequences may
+ * map the same physical blocks, e.g. a shared system prompt whose KV is
+ * computed once (same page, section 2.3); such blocks carry a reference count.
+ * A full block is never written again.  A sequence about to append into a
+ * partly filled block that another sequence also maps is first moved to a
+ * fresh private copy of that block (copy-on-write): the call reports the
+ * (source, destination) pair and the caller copies the block on the device
+ * (pkv_copy_blocks) before the append.  The tables and positions these calls
+ * return are exactly the block_tables / positions arguments of the decode
+ * calls above, prepared on the host before the step (the "Injecting Adrenaline
+ * into LLM Serving" review, section 3.2.1, on moving metadata preparation off
+ * the critical path).
+ *
+ * Allocation order is deterministic: the free block with the smallest key is
+ * handed out first, where key(i) = i for shuffle_seed == 0 and otherwise
+ * (splitmix64(shuffle_seed + (i + 1) * 0x9E3779B97F4A7C15), i) compared
+ * lexicographically (splitmix64 = the output mix of Steele, Lea and Flood's
+ * SplitMix generator).  A seeded order scatters each sequence over the pool.
+ *
+ * All block-manager calls are host-only and synchronous; a manager is not
+ * thread-safe (one per scheduler thread).  A call that fails returns a negative
+ * pkv_status, sets pkv_last_error() and leaves the manager unchanged.
+ */
+typedef struct pkv_block_manager pkv_block_manager;
+
+/* New manager over physical blocks 0 .. n_blocks-1, block_size tokens each
+ * (n_blocks >= 1, 1 <= block_size).  Returns NULL on invalid sizes. */
+pkv_block_manager* pkv_bm_create(int32_t n_blocks, int32_t block_size, uint64_t shuffle_seed);
+/* Frees the manager (NULL is allowed). */
+void pkv_bm_destroy(pkv_block_manager* bm);
+
+/* Register sequence seq_id with num_tokens >= 0 tokens (its prompt) and give it
+ * ceil(num_tokens / block_size) fresh blocks.  PKV_ERR_SEQUENCE if seq_id is in
+ * use, PKV_ERR_OUT_OF_BLOCKS if the pool is short. */
+int pkv_bm_add_sequence(pkv_block_manager* bm, int64_t seq_id, int32_t num_tokens);
+
+/* Register seq_id with num_tokens tokens whose first prefix_tokens tokens equal
+ * those of the live sequence prefix_id (prefix_tokens <= num_tokens and <= its
+ * length).  The first prefix_tokens / block_size blocks (whole blocks only) are
+ * mapped from prefix_id and shared; the rest are fresh.  *shared_tokens receives
+ * the number of tokens the new sequence gets for free (a multiple of
+ * block_size); the caller writes the KV of tokens shared_tokens .. num_tokens-1. */
+int pkv_bm_add_sequence_shared(pkv_block_manager* bm, int64_t seq_id, int32_t num_tokens, int64_t prefix_id,
+                               int32_t prefix_tokens, int32_t* shared_tokens);
+
+/* child_id starts as an exact copy of the live sequence parent_id: same length,
+ * same physical blocks, partly filled last block included (shared until one of
+ * them appends into it). */
+int pkv_bm_fork(pkv_block_manager* bm, int64_t parent_id, int64_t child_id);
+
+/* Reserve the slot of the sequence's next token: *position = its length before
+ * the call, then the length grows by one.  A token that starts a block gets a
+ * fresh block; a token that lands in a shared, partly filled block triggers the
+ * copy-on-write above, with *cow_src / *cow_dst set to the old and new block
+ * ids (both -1 when nothing must be copied).  Any out pointer may be NULL. */
+int pkv_bm_append_token(pkv_block_manager* bm, int64_t seq_id, int32_t* position, int32_t* cow_src,
+                        int32_t* cow_dst);
+
+/* One decode step's metadata: pkv_bm_append_token for seq_ids[0..B) in that
+ * order (ids must be distinct), then the batch's block tables after the append.
+ *   tables    [B][bt_stride] int32, rows padded with -1
+ *   positions [B] int32, the slot index each sequence's new token goes to
+ *             (context length of the step = positions[b] + 1)
+ *   cow_src, cow_dst  [B] int32 each; the first *n_cow entries are the block
+ *             pairs to copy before the step's append (may be NULL when the
+ *             caller knows no block is shared; then a needed copy is an error)
+ * Members are checked in batch order before anything changes: an unknown id
+ * gives PKV_ERR_SEQUENCE, a repeated id or a table that would exceed bt_stride
+ * PKV_ERR_INVALID_ARG; only then PKV_ERR_OUT_OF_BLOCKS if the pool cannot serve
+ * the whole batch. */
+int pkv_bm_append_batch(pkv_block_manager* bm, const int64_t* seq_ids, int32_t B, int32_t* tables,
+                        int32_t bt_stride, int32_t* positions, int32_t* cow_src, int32_t* cow_dst,
+                        int32_t* n_cow);
+
+/* Drop the sequence; blocks whose reference count reaches zero return to the pool. */
+int pkv_bm_free_sequence(pkv_block_manager* bm, int64_t seq_id);
+
+/* Number of free blocks, or -1 for a NULL manager. */
+int32_t pkv_bm_num_free_blocks(const pkv_block_manager* bm);
+/* Number of live sequences, or -1 for a NULL manager. */
+int32_t pkv_bm_num_sequences(const pkv_block_manager* bm);
+/* Length of the sequence in tokens, or -1 if unknown. */
+int32_t pkv_bm_sequence_length(const pkv_block_manager* bm, int64_t seq_id);
+/* Number of sequences mapping the block (0 = free), or -1 if out of range. */
+int32_t pkv_bm_block_refcount(const pkv_block_manager* bm, int32_t block);
+
+/* The sequence's block table: min(count, capacity) ids into table (may be NULL
+ * when capacity is 0), the full count into *n_blocks. */
+int pkv_bm_block_table(const pkv_block_manager* bm, int64_t seq_id, int32_t* table, int32_t capacity,
+                       int32_t* n_blocks);
+
+/* Block tables and lengths of a batch without changing anything:
+ * tables [B][bt_stride] (rows padded with -1), context_lens [B].
+ * PKV_ERR_INVALID_ARG if a sequence has more than bt_stride blocks. */
+int pkv_bm_batch_tables(const pkv_block_manager* bm, const int64_t* seq_ids, int32_t B, int32_t* tables,
+                        int32_t bt_stride, int32_t* context_lens);
+
+/*
+ * copy_blocks -- device copy of whole physical blocks, every KV head, K and V:
+ * pool[dst[i]] = pool[src[i]] for i < n, as the block manager's copy-on-write
+ * asks (pools laid out as above).  src and dst are device int32 arrays of n
+ * entries; a pair with an id outside [0, n_blocks) is skipped, and no block may
+ * be both a source and a destination in one call.  n == 0 launches nothing.
+ * Stream-ordered like the decode calls.
+ */
+int pkv_copy_blocks(int dtype, void* k_pool, void* v_pool, const int32_t* src, const int32_t* dst, int32_t n,
+                    int32_t H_kv, int32_t D, int32_t block_size, int32_t n_blocks, void* stream);
 
 #ifdef __cplusplus
 }

@@ -11,6 +11,8 @@ Entry points (same names as the C ABI without the ``pkv_`` prefix):
   paged_decode_attention    attention of one query per head over the paged history
   append_decode_attention   both, as one decode step (single attention launch)
   decode_workspace_bytes    workspace size of a split-KV call
+  copy_blocks               copy whole physical blocks (copy-on-write of shared blocks)
+  BlockManager              host-side block allocation, sharing and reclaim (pkv_bm_*)
 """
 from __future__ import annotations
 
@@ -21,19 +23,25 @@ from typing import Optional
 __all__ = [
     "PkvError", "LIB_PATH", "load_library", "library_loaded", "kv_append", "paged_decode_attention",
     "append_decode_attention", "decode_workspace_bytes", "last_launch", "version", "probe_stream_read",
-    "PKV_F32", "PKV_F16", "PKV_BF16", "EXPORTED_SYMBOLS",
+    "PKV_F32", "PKV_F16", "PKV_BF16", "EXPORTED_SYMBOLS", "copy_blocks", "BlockManager",
+    "PKV_ERR_OUT_OF_BLOCKS", "PKV_ERR_SEQUENCE",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+PKV_ERR_INVALID_ARG, PKV_ERR_OUT_OF_BLOCKS, PKV_ERR_SEQUENCE = -2, -6, -7
 BLOCK_SIZE = 16
 
 EXPORTED_SYMBOLS = (
     "pkv_version", "pkv_status_string", "pkv_last_error", "pkv_last_launch", "pkv_kv_append",
     "pkv_decode_workspace_bytes", "pkv_paged_decode_attention", "pkv_append_decode_attention",
-    "pkv_probe_stream_read",
+    "pkv_probe_stream_read", "pkv_copy_blocks",
+    "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add_sequence", "pkv_bm_add_sequence_shared", "pkv_bm_fork",
+    "pkv_bm_append_token", "pkv_bm_append_batch", "pkv_bm_free_sequence", "pkv_bm_num_free_blocks",
+    "pkv_bm_num_sequences", "pkv_bm_sequence_length", "pkv_bm_block_refcount", "pkv_bm_block_table",
+    "pkv_bm_batch_tables",
 )
 
 _lib = None
@@ -79,6 +87,30 @@ def load_library(path: Optional[str] = None):
     lib.pkv_append_decode_attention.restype = ctypes.c_int
     lib.pkv_probe_stream_read.argtypes = [P, SZ, P, I32, P]
     lib.pkv_probe_stream_read.restype = ctypes.c_int
+    lib.pkv_copy_blocks.argtypes = [ctypes.c_int, P, P, P, P, I32, I32, I32, I32, I32, P]
+    lib.pkv_copy_blocks.restype = ctypes.c_int
+    U64, C = ctypes.c_uint64, ctypes.c_int
+    lib.pkv_bm_create.argtypes = [I32, I32, U64]
+    lib.pkv_bm_create.restype = P
+    lib.pkv_bm_destroy.argtypes = [P]
+    lib.pkv_bm_destroy.restype = None
+    lib.pkv_bm_add_sequence.argtypes = [P, I64, I32]
+    lib.pkv_bm_add_sequence_shared.argtypes = [P, I64, I32, I64, I32, P]
+    lib.pkv_bm_fork.argtypes = [P, I64, I64]
+    lib.pkv_bm_append_token.argtypes = [P, I64, P, P, P]
+    lib.pkv_bm_append_batch.argtypes = [P, P, I32, P, I32, P, P, P, P]
+    lib.pkv_bm_free_sequence.argtypes = [P, I64]
+    lib.pkv_bm_num_free_blocks.argtypes = [P]
+    lib.pkv_bm_num_sequences.argtypes = [P]
+    lib.pkv_bm_sequence_length.argtypes = [P, I64]
+    lib.pkv_bm_block_refcount.argtypes = [P, I32]
+    lib.pkv_bm_block_table.argtypes = [P, I64, P, I32, P]
+    lib.pkv_bm_batch_tables.argtypes = [P, P, I32, P, I32, P]
+    for name in ("add_sequence", "add_sequence_shared", "fork", "append_token", "append_batch", "free_sequence",
+                 "block_table", "batch_tables"):
+        getattr(lib, "pkv_bm_" + name).restype = C
+    for name in ("num_free_blocks", "num_sequences", "sequence_length", "block_refcount"):
+        getattr(lib, "pkv_bm_" + name).restype = I32
     if path is None:
         _lib = lib
     return lib
@@ -254,3 +286,131 @@ def append_decode_attention(q, k_new, v_new, k_pool, v_pool, block_tables, posit
         float(scale), int(partition_size), _ptr(ws), ws_bytes, _stream(stream))
     _check(rc, "append_decode_attention")
     return out
+
+
+def copy_blocks(k_pool, v_pool, src, dst, *, stream=None):
+    """pool[dst[i]] = pool[src[i]] for both pools; src/dst are device int32 [n] tensors."""
+    torch = _torch()
+    n_blocks, H_kv, bs, D = _pool_dims(k_pool, v_pool)
+    n = src.shape[0]
+    for t, nm in ((src, "src"), (dst, "dst")):
+        _require(t.dtype == torch.int32 and t.dim() == 1 and t.shape[0] == n and (n <= 1 or t.stride(0) == 1),
+                 f"{nm} must be contiguous int32 [n]")
+    rc = load_library().pkv_copy_blocks(_dtype_code(k_pool), _ptr(k_pool), _ptr(v_pool), _ptr(src), _ptr(dst), n,
+                                        H_kv, D, bs, n_blocks, _stream(stream))
+    _check(rc, "copy_blocks")
+
+
+# ---------------------------------------------------------------------------
+# Host block manager (numpy arrays in and out; no device memory involved)
+# ---------------------------------------------------------------------------
+
+class BlockManager:
+    """Owns a ``pkv_block_manager``: which physical blocks each sequence maps.
+
+    Method names follow the C ABI (``pkv_bm_<name>``); a failing call raises
+    PkvError with the C status and changes nothing.
+    """
+
+    def __init__(self, n_blocks: int, block_size: int = BLOCK_SIZE, shuffle_seed: int = 0):
+        lib = load_library()
+        h = lib.pkv_bm_create(int(n_blocks), int(block_size), int(shuffle_seed) & ((1 << 64) - 1))
+        if not h:
+            raise PkvError(-2, "pkv_bm_create: " + lib.pkv_last_error().decode())
+        self._h = ctypes.c_void_p(h)
+        self._lib = lib
+        self.n_blocks = int(n_blocks)
+        self.block_size = int(block_size)
+
+    def close(self):
+        if getattr(self, "_h", None) is not None:
+            self._lib.pkv_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def add_sequence(self, seq_id: int, num_tokens: int) -> None:
+        _check(self._lib.pkv_bm_add_sequence(self._h, int(seq_id), int(num_tokens)), "bm_add_sequence")
+
+    def add_sequence_shared(self, seq_id: int, num_tokens: int, prefix_id: int, prefix_tokens: int) -> int:
+        """Returns the number of leading tokens mapped from prefix_id (whole blocks)."""
+        shared = ctypes.c_int32(0)
+        _check(self._lib.pkv_bm_add_sequence_shared(self._h, int(seq_id), int(num_tokens), int(prefix_id),
+                                                    int(prefix_tokens), ctypes.byref(shared)),
+               "bm_add_sequence_shared")
+        return shared.value
+
+    def fork(self, parent_id: int, child_id: int) -> None:
+        _check(self._lib.pkv_bm_fork(self._h, int(parent_id), int(child_id)), "bm_fork")
+
+    def append_token(self, seq_id: int):
+        """Returns (position, cow_src, cow_dst); (-1, -1) when no block must be copied."""
+        pos, src, dst = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(self._lib.pkv_bm_append_token(self._h, int(seq_id), ctypes.byref(pos), ctypes.byref(src),
+                                             ctypes.byref(dst)), "bm_append_token")
+        return pos.value, src.value, dst.value
+
+    def append_batch(self, seq_ids, bt_stride: int, *, out_tables=None, out_positions=None):
+        """One decode step's metadata.  Returns (tables int32 [B, bt_stride], positions int32 [B],
+        cow int32 [n_cow, 2] of (src, dst) pairs)."""
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        B = ids.shape[0]
+        tables = out_tables if out_tables is not None else np.empty((B, bt_stride), dtype=np.int32)
+        positions = out_positions if out_positions is not None else np.empty(B, dtype=np.int32)
+        _require(tables.dtype == np.int32 and tables.shape == (B, bt_stride) and tables.flags.c_contiguous,
+                 "out_tables must be C-contiguous int32 [B, bt_stride]")
+        _require(positions.dtype == np.int32 and positions.shape == (B,) and positions.flags.c_contiguous,
+                 "out_positions must be contiguous int32 [B]")
+        cow = np.empty((2, max(B, 1)), dtype=np.int32)
+        n_cow = ctypes.c_int32(0)
+        _check(self._lib.pkv_bm_append_batch(self._h, _np_ptr(ids), B, _np_ptr(tables), int(bt_stride),
+                                             _np_ptr(positions), _np_ptr(cow[0]), _np_ptr(cow[1]),
+                                             ctypes.byref(n_cow)), "bm_append_batch")
+        return tables, positions, np.ascontiguousarray(cow[:, :n_cow.value].T)
+
+    def free_sequence(self, seq_id: int) -> None:
+        _check(self._lib.pkv_bm_free_sequence(self._h, int(seq_id)), "bm_free_sequence")
+
+    def num_free_blocks(self) -> int:
+        return int(self._lib.pkv_bm_num_free_blocks(self._h))
+
+    def num_sequences(self) -> int:
+        return int(self._lib.pkv_bm_num_sequences(self._h))
+
+    def sequence_length(self, seq_id: int) -> int:
+        return int(self._lib.pkv_bm_sequence_length(self._h, int(seq_id)))
+
+    def block_refcount(self, block: int) -> int:
+        return int(self._lib.pkv_bm_block_refcount(self._h, int(block)))
+
+    def block_table(self, seq_id: int):
+        import numpy as np
+        n = ctypes.c_int32(0)
+        _check(self._lib.pkv_bm_block_table(self._h, int(seq_id), None, 0, ctypes.byref(n)), "bm_block_table")
+        table = np.empty(max(n.value, 1), dtype=np.int32)
+        _check(self._lib.pkv_bm_block_table(self._h, int(seq_id), _np_ptr(table), n.value, ctypes.byref(n)),
+               "bm_block_table")
+        return table[:n.value]
+
+    def batch_tables(self, seq_ids, bt_stride: int):
+        """Returns (tables int32 [B, bt_stride], context_lens int32 [B]) without changing anything."""
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        B = ids.shape[0]
+        tables = np.empty((B, bt_stride), dtype=np.int32)
+        lens = np.empty(B, dtype=np.int32)
+        _check(self._lib.pkv_bm_batch_tables(self._h, _np_ptr(ids), B, _np_ptr(tables), int(bt_stride),
+                                             _np_ptr(lens)), "bm_batch_tables")
+        return tables, lens
+
+
+def _np_ptr(a):
+    return ctypes.c_void_p(a.ctypes.data)

@@ -12,12 +12,15 @@
 #include <cstring>
 
 #include "pkv.h"
+#include "pkv_host.h"
 #include "pkv_launch.h"
 
 namespace {
-
 thread_local char g_err[512] = "";
 thread_local char g_launch[256] = "";
+}  // namespace
+
+namespace pkv {
 
 int fail(int status, const char* fmt, ...) {
     va_list ap;
@@ -26,6 +29,14 @@ int fail(int status, const char* fmt, ...) {
     va_end(ap);
     return status;
 }
+
+void clear_error() { g_err[0] = 0; }
+
+}  // namespace pkv
+
+namespace {
+
+using pkv::fail;
 
 int elem_bytes(int dtype) {
     switch (dtype) {
@@ -239,6 +250,8 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED";
     case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE";
     case PKV_ERR_HIP: return "PKV_ERR_HIP";
+    case PKV_ERR_OUT_OF_BLOCKS: return "PKV_ERR_OUT_OF_BLOCKS";
+    case PKV_ERR_SEQUENCE: return "PKV_ERR_SEQUENCE";
     default: return "PKV_UNKNOWN_STATUS";
     }
 }
@@ -296,6 +309,39 @@ int pkv_probe_stream_read(const void* buf, size_t bytes, void* sink, int32_t gri
                                            reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "probe launch: %s", hipGetErrorString(e));
     g_err[0] = 0;
+    return PKV_OK;
+}
+
+int pkv_copy_blocks(int dtype, void* k_pool, void* v_pool, const int32_t* src, const int32_t* dst, int32_t n,
+                    int32_t H_kv, int32_t D, int32_t block_size, int32_t n_blocks, void* stream) {
+    const int eb = elem_bytes(dtype);
+    if (!eb) return fail(PKV_ERR_UNSUPPORTED, "dtype %d is not one of PKV_F32/F16/BF16", dtype);
+    if (n < 0) return fail(PKV_ERR_INVALID_ARG, "n = %d is negative", n);
+    if (H_kv <= 0) return fail(PKV_ERR_INVALID_ARG, "H_kv = %d must be positive", H_kv);
+    if (D != 64 && D != 128) return fail(PKV_ERR_UNSUPPORTED, "head dim D = %d (built: 64, 128)", D);
+    if (block_size != pkv::kBlockSize)
+        return fail(PKV_ERR_UNSUPPORTED, "block_size = %d (built: %d)", block_size, pkv::kBlockSize);
+    if (n_blocks <= 0) return fail(PKV_ERR_INVALID_ARG, "n_blocks = %d must be positive", n_blocks);
+    if (n == 0) {
+        pkv::clear_error();
+        return PKV_OK;
+    }
+    if (!k_pool || !v_pool || !src || !dst) return fail(PKV_ERR_NULL, "a required pointer is NULL");
+    if (!aligned16(k_pool) || !aligned16(v_pool))
+        return fail(PKV_ERR_INVALID_ARG, "the pools must be 16-byte aligned");
+    pkv::CopyArgs a{};
+    a.k_pool = reinterpret_cast<char*>(k_pool);
+    a.v_pool = reinterpret_cast<char*>(v_pool);
+    a.src = src;
+    a.dst = dst;
+    a.n = n;
+    a.n_blocks = n_blocks;
+    a.block_bytes = (int64_t)H_kv * block_size * D * eb;
+    if ((int64_t)n * 2 * ((a.block_bytes + pkv::kCopyPieceBytes - 1) / pkv::kCopyPieceBytes) > 0x7fffffff)
+        return fail(PKV_ERR_INVALID_ARG, "grid too large");
+    hipError_t e = pkv::launch_copy_blocks(a, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "copy_blocks launch: %s", hipGetErrorString(e));
+    pkv::clear_error();
     return PKV_OK;
 }
 

@@ -29,6 +29,18 @@ struct MergeArgs {
     int32_t BH, H_q, n_parts, part_tokens, max_context_len;
 };
 
+// pool[dst[i]] = pool[src[i]] for both pools; a block is block_bytes contiguous bytes
+struct CopyArgs {
+    char* k_pool;
+    char* v_pool;
+    const int32_t* src;
+    const int32_t* dst;
+    int64_t block_bytes;
+    int32_t n, n_blocks;
+};
+constexpr int kCopyPieceBytes = 4096;   // bytes one 256-thread workgroup moves per piece
+
+hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_decode_mha(int dtype, int D, int nw, int ch, int pf, bool append, const AttnArgs& a,
                              unsigned grid, hipStream_t stream);

@@ -128,3 +128,26 @@ def test_fused_validation(lib):
 def test_binding_refuses_missing_library(tmp_path):
     with pytest.raises(pkv.PkvError):
         pkv.load_library(str(tmp_path / "nope.so"))
+
+
+def copy_blocks(lib, dtype=1, kp=FAKE, vp=FAKE, src=FAKE, dst=FAKE, n=4, H_kv=8, D=128, bs=16, nb=64):
+    return lib.pkv_copy_blocks(dtype, kp, vp, src, dst, n, H_kv, D, bs, nb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=9), E_UNSUP),
+    (dict(n=-1), E_ARG),
+    (dict(H_kv=0), E_ARG),
+    (dict(D=96), E_UNSUP),
+    (dict(bs=8), E_UNSUP),
+    (dict(nb=0), E_ARG),
+    (dict(src=None), E_NULL),
+    (dict(dst=None), E_NULL),
+    (dict(kp=None), E_NULL),
+    (dict(vp=FAKE + 4), E_ARG),
+    (dict(n=0, kp=None, vp=None, src=None, dst=None), OK),   # nothing to copy: nothing launched
+])
+def test_copy_blocks_validation(lib, kw, status):
+    assert copy_blocks(lib, **kw) == status
+    if status:
+        assert lib.pkv_last_error()
