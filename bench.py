@@ -132,6 +132,173 @@ def cpu_baseline(w, step_bytes_total: float, kv_tokens: int, budget_s: float = 1
     }
 
 
+def loop_bench(args, torch, pkv, dev) -> int:
+    """A decode loop driven by the library's block manager.
+
+    The workload's requests are registered with a pkv.BlockManager; every step
+    the host asks it for the step's positions, copy pairs and block tables
+    (pkv_bm_append_batch, straight into one packed pinned buffer), enqueues
+    the copy of that buffer to the device, and then either enqueues
+    copy_blocks + the fused append + attention one call at a time, or
+    (--graphs) replays the captured step graph of the smallest fitting
+    (batch, context) bucket; --native does all of that in one
+    pkv_decoder_step call.  Two metadata buffer sets alternate so the host
+    prepares step k+1 while the GPU runs step k.  Reported next to the same
+    fused step on static tables.
+    """
+    from workloads import draw_lengths, get_config, kv_bytes_per_token
+
+    cfg = get_config(args.config)
+    seed = args.seed if args.seed is not None else 1000 + int(cfg.name[1:])
+    rng = np.random.default_rng(seed)
+    hist = draw_lengths(cfg, rng).astype(np.int64) - 1          # tokens already cached
+    hist = np.maximum(hist, 0)
+    B, H_q, H_kv, D, bs = cfg.B, cfg.H_q, cfg.H_kv, cfg.D, cfg.block_size
+    total_steps = args.warmup + args.steps
+    final = hist + total_steps
+    need = int(((final + bs - 1) // bs).sum())
+    factor = cfg.pool[1] if cfg.pool[0] == "factor" else 1.0
+    n_blocks = max(int(math.ceil(factor * need)), need)
+    W = int(((final.max() + bs - 1) // bs))
+    P = cfg.partition_size if args.partition is None else args.partition
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
+
+    ids = np.arange(B, dtype=np.int64)
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    k_pool = (torch.randn((n_blocks, H_kv, bs, D), generator=g, device=dev) * cfg.kv_std).to(tdt)
+    v_pool = (torch.randn((n_blocks, H_kv, bs, D), generator=g, device=dev) * cfg.kv_std).to(tdt)
+    q = (torch.randn((B, H_q, D), generator=g, device=dev) * cfg.q_std).to(tdt)
+    k_new = (torch.randn((B, H_kv, D), generator=g, device=dev) * cfg.kv_std).to(tdt)
+    v_new = (torch.randn((B, H_kv, D), generator=g, device=dev) * cfg.kv_std).to(tdt)
+    out = torch.empty((B, H_q, D), dtype=torch.float32, device=dev)
+    bucket = 256                                      # context-capacity interval of the graph grid
+    max_ctx_bound = int(final.max()) + 1
+    ctx_caps = list(range(bucket, max_ctx_bound + bucket, bucket))
+    W = max(W, ctx_caps[-1] // bs)                    # table rows reach the top context bucket
+    ws_bytes = pkv.decode_workspace_bytes(B, H_q, D, ctx_caps[-1], P) if P else 0
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    main = torch.cuda.current_stream(dev)
+
+    dec = None
+    if args.native:
+        caps = dict(batch_caps=[B], ctx_caps=ctx_caps) if args.graphs else {}
+        dec = pkv.Decoder(q, k_new, v_new, k_pool, v_pool, out, scale, W, partition_size=P,
+                          workspace=ws if P else None, shuffle_seed=seed, **caps)
+        bm = dec.block_manager
+    else:
+        bm = pkv.BlockManager(n_blocks, bs, shuffle_seed=seed)
+    for b in range(B):
+        bm.add_sequence(b, int(hist[b]))
+
+    # packed metadata: positions [B] | cow_src [B] | cow_dst [B] | block tables [B][W]
+    meta_len = 3 * B + B * W
+    pin = [torch.empty(meta_len, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    dmeta = [torch.empty(meta_len, dtype=torch.int32, device=dev) for _ in range(2)]
+    hv = [(m.numpy(), m.numpy()[3 * B:].reshape(B, W)) for m in pin]
+    dv = [(m[:B], m[B:2 * B], m[2 * B:3 * B], m[3 * B:].view(B, W)) for m in dmeta]
+    graphs = None
+    if args.graphs and not args.native:
+        graphs = [pkv.StepGraphs(q, k_new, v_new, k_pool, v_pool, dv[s][3], dv[s][0], out, scale, [B], ctx_caps,
+                                 partition_size=P, cow_src=dv[s][1], cow_dst=dv[s][2], workspace=ws)
+                  for s in range(2)]
+    done = [torch.cuda.Event() for _ in range(2)]
+    host_bm_s, copies = 0.0, 0
+
+    def step(k):
+        nonlocal host_bm_s, copies
+        if dec is not None:
+            h0 = time.perf_counter()
+            copies += dec.step(ids, stream=main)
+            host_bm_s += time.perf_counter() - h0
+            return
+        s = k % 2
+        done[s].synchronize()          # step k-2 (which used this buffer set) has finished
+        flat, tab = hv[s]
+        h0 = time.perf_counter()
+        _, pos, cow = bm.append_batch(ids, W, out_tables=tab, out_positions=flat[:B])
+        host_bm_s += time.perf_counter() - h0
+        n = len(cow)
+        flat[B:3 * B] = -1
+        if n:
+            flat[B:B + n] = cow[:, 0]
+            flat[2 * B:2 * B + n] = cow[:, 1]
+            copies += n
+        max_ctx = int(pos.max()) + 1
+        dmeta[s].copy_(pin[s], non_blocking=True)         # in order on the compute stream
+        if graphs is not None:
+            graphs[s].launch(B, max_ctx, n, stream=main)
+        else:
+            d_pos, d_cs, d_cd, d_tab = dv[s]
+            if n:
+                pkv.copy_blocks(k_pool, v_pool, d_cs[:n], d_cd[:n], stream=main)
+            pkv.append_decode_attention(q, k_new, v_new, k_pool, v_pool, d_tab, d_pos, scale, max_ctx,
+                                        partition_size=P, out=out, workspace=ws if P else None, stream=main)
+        done[s].record(main)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    host_bm_s = 0.0
+    kv_read = 0.0
+    per_tok = kv_bytes_per_token(H_kv, D, {"f32": 4, "f16": 2, "bf16": 2}[cfg.dtype])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(main)
+    for k in range(args.warmup, total_steps):
+        kv_read += float((hist + k).sum()) * per_tok      # history the step reads (before its append)
+        step(k)
+    e1.record(main)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu = e0.elapsed_time(e1) / 1e3
+
+    # the same fused step on fixed tables, launched back to back
+    tabs, lens = bm.batch_tables(ids, W)
+    st_t = torch.from_numpy(tabs).to(dev)
+    st_p = torch.from_numpy(lens - 1).to(dev)
+    for _ in range(5):
+        pkv.append_decode_attention(q, k_new, v_new, k_pool, v_pool, st_t, st_p, scale, int(lens.max()),
+                                    partition_size=P, out=out, workspace=ws if P else None, stream=main)
+    torch.cuda.synchronize()
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record(main)
+    for _ in range(args.steps):
+        pkv.append_decode_attention(q, k_new, v_new, k_pool, v_pool, st_t, st_p, scale, int(lens.max()),
+                                    partition_size=P, out=out, workspace=ws if P else None, stream=main)
+    f1.record(main)
+    torch.cuda.synchronize()
+    static_s = f0.elapsed_time(f1) / 1e3 / args.steps
+
+    print(json.dumps({
+        "mode": "loop",
+        "metric": "decode steps driven by the host block manager" + (" (native decoder," if dec else " (python loop,")
+                  + (" step graphs)" if args.graphs else " eager)"),
+        "value": round(B * args.steps / wall, 1),
+        "unit": "tokens/s",
+        "higher_is_better": True,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "gpu_ms_per_step": round(gpu / args.steps * 1e3, 5),
+        "static_tables_eager_gpu_ms_per_step": round(static_s * 1e3, 5),
+        # python loop: time in pkv_bm_append_batch; native: time in the whole pkv_decoder_step call
+        "host_us_per_step": round(host_bm_s / args.steps * 1e6, 2),
+        "host_us_measures": "pkv_decoder_step call" if dec else "pkv_bm_append_batch call",
+        "kv_read_GBps_wall": round(kv_read / wall / 1e9, 1),
+        "cow_block_copies": copies,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded device normals; lengths drawn as the workload's)",
+        "config": {"workload": workload_label(cfg, "manager-driven fused append + attention"
+                                                   + (f" (split {P})" if P else "")),
+                   "n_blocks": n_blocks, "bt_stride": W, "partition_size": P,
+                   "graph_buckets": [[B], [ctx_caps[0], ctx_caps[-1], bucket]] if args.graphs else None},
+    }))
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,6 +314,10 @@ def main(argv=None):
     ap.add_argument("--no-graph", action="store_true", help="launch every step eagerly (for counter runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times (scales HBM byte counters)")
+    ap.add_argument("--mode", default="step", choices=["step", "loop"],
+                    help="step: the headline step over resident inputs; loop: a block-manager-driven decode loop")
+    ap.add_argument("--graphs", action="store_true", help="loop mode: replay captured step graphs")
+    ap.add_argument("--native", action="store_true", help="loop mode: one pkv_decoder_step call per step")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -175,6 +346,8 @@ def main(argv=None):
         print(json.dumps({"copy_calibration_bytes": n, "dispatches": 5}))
         return 0
     lib = pkv.load_library()
+    if args.mode == "loop":
+        return loop_bench(args, torch, pkv, dev)
 
     cfg = get_config(args.config)
     append = not args.no_append

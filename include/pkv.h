@@ -48,8 +48,9 @@
  * detail is in pkv_last_error() (thread-local).  On success the work is
  * enqueued on `stream` (a hipStream_t; NULL = the default stream) and the call
  * returns without synchronising; results are valid once the stream reaches
- * that point.  No entry point allocates device memory, and calls on different
- * streams may overlap freely as long as their outputs do not alias.
+ * that point.  No compute entry point allocates device memory (only
+ * pkv_decoder_create allocates, for its own metadata buffers), and calls on
+ * different streams may overlap freely as long as their outputs do not alias.
  *
  * Device-side metadata (block ids, lengths, positions) is read by the kernels
  * and checked there: a block id outside [0, n_blocks) or a length outside
@@ -313,6 +314,143 @@ int pkv_bm_batch_tables(const pkv_block_manager* bm, const int64_t* seq_ids, int
  */
 int pkv_copy_blocks(int dtype, void* k_pool, void* v_pool, const int32_t* src, const int32_t* dst, int32_t n,
                     int32_t H_kv, int32_t D, int32_t block_size, int32_t n_blocks, void* stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Step graphs: the decode step captured once per (batch, context) bucket
+ * ---------------------------------------------------------------------------
+ * Launching a step's kernels one by one costs host time that a small decode
+ * batch cannot hide (the "Injecting Adrenaline into LLM Serving" review,
+ * section 3.2.2: per-layer CPU time far above GPU time without graphs, fixed by
+ * capturing graphs over a two-dimensional grid of batch capacities and
+ * replaying the smallest one that fits).  A pkv_step_graphs object captures,
+ * for every pair (batch capacity Bc, context capacity Cc) of the given lists,
+ * one HIP graph of the step over fixed buffers:
+ *     pkv_append_decode_attention with B = Bc, max_context_len = Cc
+ * and, when copy buffers are given, a second one that first runs
+ *     pkv_copy_blocks over cow_src/cow_dst[0 .. Bc)
+ * pkv_step_graphs_launch(B, max_len, n_copies) replays the graph with the
+ * smallest Bc >= B and the smallest Cc >= max_len, with the copy node only if
+ * n_copies > 0, on the caller's stream.  Before each launch the
+ * caller writes the step's data into the buffers (device memory, e.g. by an
+ * async copy on the same or an earlier-synchronised stream):
+ *   positions[b] for b < B, and -1 for B <= b < Bc (such a padding row reads and
+ *   writes nothing in the pools and gets a NaN output row);
+ *   block_tables rows b < B; copy pairs, unused entries -1 (skipped).
+ * Buffers are sized for the largest capacities; workspace for the largest
+ * bucket (pkv_decode_workspace_bytes(max Bc, H_q, D, max Cc, partition_size)).
+ * The buffers must stay allocated, at the same addresses, for the object's
+ * lifetime.  Capture happens in pkv_step_graphs_create on a stream of its own;
+ * launch is asynchronous and allocation-free.  Not thread-safe per object.
+ */
+typedef struct pkv_step_desc {
+    int dtype;
+    int32_t H_q, H_kv, D, block_size, n_blocks;
+    float scale;
+    int32_t partition_size;
+    float* out;                                  /* [max Bc][H_q][D] float32           */
+    const void* q;                               /* [max Bc] rows of q_row_stride      */
+    int64_t q_row_stride;
+    const void* k_new;                           /* [max Bc] rows of new_row_stride    */
+    const void* v_new;
+    int64_t new_row_stride;
+    void* k_pool;                                /* [n_blocks][H_kv][block_size][D]    */
+    void* v_pool;
+    const int32_t* block_tables;                 /* [max Bc][bt_stride]                */
+    int32_t bt_stride;
+    const int32_t* positions;                    /* [max Bc]                           */
+    const int32_t* cow_src;                      /* [max Bc] or NULL (no copy node)    */
+    const int32_t* cow_dst;                      /* [max Bc] or NULL                   */
+    void* workspace;
+    size_t workspace_bytes;
+} pkv_step_desc;
+
+typedef struct pkv_step_graphs pkv_step_graphs;
+
+/* Capture n_batch x n_ctx graphs (capacities > 0, each list strictly
+ * increasing, max Cc <= bt_stride * block_size).  Returns NULL on an invalid
+ * description or a HIP error (detail in pkv_last_error()).  Runs on the current
+ * HIP device, which must be the one owning the buffers. */
+pkv_step_graphs* pkv_step_graphs_create(const pkv_step_desc* desc, const int32_t* batch_caps, int32_t n_batch,
+                                        const int32_t* ctx_caps, int32_t n_ctx);
+
+/* Replay the smallest fitting graph on `stream`.  PKV_ERR_INVALID_ARG if B or
+ * max_context_len exceeds the largest capacity, if n_copies exceeds the chosen
+ * batch capacity, or if n_copies > 0 without copy buffers (nothing launched). */
+int pkv_step_graphs_launch(pkv_step_graphs* g, int32_t B, int32_t max_context_len, int32_t n_copies, void* stream);
+
+/* Frees the graphs (NULL is allowed).  Work already launched is not waited for. */
+void pkv_step_graphs_destroy(pkv_step_graphs* g);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Decoder: the decode loop's per-step host work in one call
+ * ---------------------------------------------------------------------------
+ * Ties the pieces above into the loop a decode instance runs every step: the
+ * block manager reserves each sequence's next slot, the resulting positions,
+ * copy pairs and block tables are written into a pinned buffer, and the copy of
+ * that buffer to the device plus the step (copy-on-write, fused append +
+ * attention, merge) are enqueued, the step on the caller's stream -- as one
+ * step-graph replay when capacity lists are given, else call by call.  A step
+ * that reads much K/V (>= 512 MiB) copies its metadata on a stream of the
+ * decoder's own, overlapping the previous step; a short one copies in order
+ * on the caller's stream, where a cross-stream dependency would cost more
+ * than the copy.  Two
+ * metadata sets alternate, so the host prepares step k+1 while the GPU runs
+ * step k (the "Injecting Adrenaline into LLM Serving" review, section 3.2.1, on
+ * preparing metadata ahead of the step, and section 3.2.2 on graphs).
+ *
+ * The caller owns q, k_new, v_new, out, the pools and the workspace (device
+ * memory, fixed addresses for the decoder's lifetime) and, before each step,
+ * writes row b of q / k_new / v_new for seq_ids[b].  pkv_decoder_create
+ * allocates the decoder's own metadata buffers (pinned host and device memory)
+ * and captures its graphs; pkv_decoder_step allocates nothing.
+ */
+typedef struct pkv_decoder_desc {
+    int dtype;
+    int32_t H_q, H_kv, D, block_size, n_blocks;
+    float scale;
+    int32_t partition_size;
+    int32_t max_batch;                           /* rows of q, k_new, v_new and out    */
+    int32_t bt_stride;                           /* longest context = bt_stride * block_size */
+    float* out;
+    const void* q;
+    int64_t q_row_stride;
+    const void* k_new;
+    const void* v_new;
+    int64_t new_row_stride;
+    void* k_pool;
+    void* v_pool;
+    void* workspace;                             /* for max_batch rows and the longest context */
+    size_t workspace_bytes;
+    uint64_t shuffle_seed;                       /* block manager allocation order    */
+    /* Step graphs: strictly increasing capacities whose last entries are
+     * max_batch and bt_stride * block_size; n_batch_caps = 0 launches eagerly. */
+    const int32_t* batch_caps;
+    int32_t n_batch_caps;
+    const int32_t* ctx_caps;
+    int32_t n_ctx_caps;
+} pkv_decoder_desc;
+
+typedef struct pkv_decoder pkv_decoder;
+
+/* Returns NULL on an invalid description or a HIP error (pkv_last_error()).
+ * Uses the current HIP device. */
+pkv_decoder* pkv_decoder_create(const pkv_decoder_desc* desc);
+
+/* Waits for the decoder's launched work, then frees it (NULL is allowed). */
+void pkv_decoder_destroy(pkv_decoder* dec);
+
+/* The decoder's block manager (owned by the decoder): register, fork and free
+ * sequences through the pkv_bm_* calls between steps. */
+pkv_block_manager* pkv_decoder_block_manager(pkv_decoder* dec);
+
+/* One decode step for seq_ids[0 .. B), 0 <= B <= max_batch, enqueued on
+ * `stream`.  Errors from the block manager (unknown or repeated id, full pool,
+ * context beyond bt_stride * block_size) return before anything changes; a
+ * later PKV_ERR_HIP leaves the sequences already advanced.  *n_copies (may be
+ * NULL) receives the number of copy-on-write block copies the step made. */
+int pkv_decoder_step(pkv_decoder* dec, const int64_t* seq_ids, int32_t B, void* stream, int32_t* n_copies);
 
 #ifdef __cplusplus
 }

@@ -13,6 +13,8 @@ Entry points (same names as the C ABI without the ``pkv_`` prefix):
   decode_workspace_bytes    workspace size of a split-KV call
   copy_blocks               copy whole physical blocks (copy-on-write of shared blocks)
   BlockManager              host-side block allocation, sharing and reclaim (pkv_bm_*)
+  StepGraphs                the fused step captured per (batch, context) bucket (pkv_step_graphs_*)
+  Decoder                   one call per decode step: manager, staged metadata, graph or eager launch
 """
 from __future__ import annotations
 
@@ -23,7 +25,7 @@ from typing import Optional
 __all__ = [
     "PkvError", "LIB_PATH", "load_library", "library_loaded", "kv_append", "paged_decode_attention",
     "append_decode_attention", "decode_workspace_bytes", "last_launch", "version", "probe_stream_read",
-    "PKV_F32", "PKV_F16", "PKV_BF16", "EXPORTED_SYMBOLS", "copy_blocks", "BlockManager",
+    "PKV_F32", "PKV_F16", "PKV_BF16", "EXPORTED_SYMBOLS", "copy_blocks", "BlockManager", "StepGraphs", "Decoder",
     "PKV_ERR_OUT_OF_BLOCKS", "PKV_ERR_SEQUENCE",
 ]
 
@@ -41,10 +43,40 @@ EXPORTED_SYMBOLS = (
     "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add_sequence", "pkv_bm_add_sequence_shared", "pkv_bm_fork",
     "pkv_bm_append_token", "pkv_bm_append_batch", "pkv_bm_free_sequence", "pkv_bm_num_free_blocks",
     "pkv_bm_num_sequences", "pkv_bm_sequence_length", "pkv_bm_block_refcount", "pkv_bm_block_table",
-    "pkv_bm_batch_tables",
+    "pkv_bm_batch_tables", "pkv_step_graphs_create", "pkv_step_graphs_launch", "pkv_step_graphs_destroy",
+    "pkv_decoder_create", "pkv_decoder_destroy", "pkv_decoder_block_manager", "pkv_decoder_step",
 )
 
 _lib = None
+
+
+class StepDesc(ctypes.Structure):
+    """Mirror of ``pkv_step_desc`` in include/pkv.h (same field order and types)."""
+    _fields_ = [
+        ("dtype", ctypes.c_int), ("H_q", ctypes.c_int32), ("H_kv", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("block_size", ctypes.c_int32), ("n_blocks", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("partition_size", ctypes.c_int32), ("out", ctypes.c_void_p), ("q", ctypes.c_void_p),
+        ("q_row_stride", ctypes.c_int64), ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p),
+        ("new_row_stride", ctypes.c_int64), ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+        ("block_tables", ctypes.c_void_p), ("bt_stride", ctypes.c_int32), ("positions", ctypes.c_void_p),
+        ("cow_src", ctypes.c_void_p), ("cow_dst", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class DecoderDesc(ctypes.Structure):
+    """Mirror of ``pkv_decoder_desc`` in include/pkv.h (same field order and types)."""
+    _fields_ = [
+        ("dtype", ctypes.c_int), ("H_q", ctypes.c_int32), ("H_kv", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("block_size", ctypes.c_int32), ("n_blocks", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("partition_size", ctypes.c_int32), ("max_batch", ctypes.c_int32), ("bt_stride", ctypes.c_int32),
+        ("out", ctypes.c_void_p), ("q", ctypes.c_void_p), ("q_row_stride", ctypes.c_int64),
+        ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p), ("new_row_stride", ctypes.c_int64),
+        ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t), ("shuffle_seed", ctypes.c_uint64),
+        ("batch_caps", ctypes.c_void_p), ("n_batch_caps", ctypes.c_int32),
+        ("ctx_caps", ctypes.c_void_p), ("n_ctx_caps", ctypes.c_int32),
+    ]
 
 
 class PkvError(RuntimeError):
@@ -111,6 +143,20 @@ def load_library(path: Optional[str] = None):
         getattr(lib, "pkv_bm_" + name).restype = C
     for name in ("num_free_blocks", "num_sequences", "sequence_length", "block_refcount"):
         getattr(lib, "pkv_bm_" + name).restype = I32
+    lib.pkv_step_graphs_create.argtypes = [ctypes.POINTER(StepDesc), P, I32, P, I32]
+    lib.pkv_step_graphs_create.restype = P
+    lib.pkv_step_graphs_launch.argtypes = [P, I32, I32, I32, P]
+    lib.pkv_step_graphs_launch.restype = C
+    lib.pkv_step_graphs_destroy.argtypes = [P]
+    lib.pkv_step_graphs_destroy.restype = None
+    lib.pkv_decoder_create.argtypes = [ctypes.POINTER(DecoderDesc)]
+    lib.pkv_decoder_create.restype = P
+    lib.pkv_decoder_destroy.argtypes = [P]
+    lib.pkv_decoder_destroy.restype = None
+    lib.pkv_decoder_block_manager.argtypes = [P]
+    lib.pkv_decoder_block_manager.restype = P
+    lib.pkv_decoder_step.argtypes = [P, P, I32, P, P]
+    lib.pkv_decoder_step.restype = C
     if path is None:
         _lib = lib
     return lib
@@ -312,9 +358,13 @@ class BlockManager:
     PkvError with the C status and changes nothing.
     """
 
-    def __init__(self, n_blocks: int, block_size: int = BLOCK_SIZE, shuffle_seed: int = 0):
+    def __init__(self, n_blocks: int, block_size: int = BLOCK_SIZE, shuffle_seed: int = 0, *, _borrow=None):
         lib = load_library()
-        h = lib.pkv_bm_create(int(n_blocks), int(block_size), int(shuffle_seed) & ((1 << 64) - 1))
+        if _borrow is not None:            # a manager owned by a Decoder; never destroyed here
+            h, self._owner = _borrow
+        else:
+            h = lib.pkv_bm_create(int(n_blocks), int(block_size), int(shuffle_seed) & ((1 << 64) - 1))
+            self._owner = None
         if not h:
             raise PkvError(-2, "pkv_bm_create: " + lib.pkv_last_error().decode())
         self._h = ctypes.c_void_p(h)
@@ -324,7 +374,8 @@ class BlockManager:
 
     def close(self):
         if getattr(self, "_h", None) is not None:
-            self._lib.pkv_bm_destroy(self._h)
+            if self._owner is None:
+                self._lib.pkv_bm_destroy(self._h)
             self._h = None
 
     def __del__(self):
@@ -414,3 +465,151 @@ class BlockManager:
 
 def _np_ptr(a):
     return ctypes.c_void_p(a.ctypes.data)
+
+
+# ---------------------------------------------------------------------------
+# Step graphs (device tensors held for the object's lifetime)
+# ---------------------------------------------------------------------------
+
+class StepGraphs:
+    """The fused decode step captured once per (batch capacity, context capacity).
+
+    Buffers are torch device tensors sized for the largest capacities; this
+    object keeps references to them so their addresses stay valid.  Before each
+    ``launch(B, max_context_len)`` the caller writes the step's rows into them;
+    ``positions`` rows from B up to the chosen batch capacity must be -1, and
+    unused copy pairs -1.
+    """
+
+    def __init__(self, q, k_new, v_new, k_pool, v_pool, block_tables, positions, out, scale: float,
+                 batch_caps, ctx_caps, *, partition_size: int = 0, cow_src=None, cow_dst=None, workspace=None):
+        torch = _torch()
+        n_blocks, H_kv, bs, D = _pool_dims(k_pool, v_pool)
+        Bmax, H_q = q.shape[0], q.shape[1]
+        bcaps = [int(x) for x in batch_caps]
+        ccaps = [int(x) for x in ctx_caps]
+        _require(bcaps and ccaps and bcaps[-1] <= Bmax, "batch capacities must fit the buffers' rows")
+        for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new")):
+            _require(t.dtype == k_pool.dtype, f"{nm} dtype must match the pools")
+        qrs = _rows(q, "q", H_q, D)
+        nrs = _rows(k_new, "k_new", H_kv, D)
+        _require(_rows(v_new, "v_new", H_kv, D) == nrs, "k_new and v_new must share a row stride")
+        bts = _int32_2d(block_tables, "block_tables")
+        _require(block_tables.shape[0] >= bcaps[-1], "block_tables needs a row per batch slot")
+        _int32_1d(positions, "positions", positions.shape[0])
+        _require(positions.shape[0] >= bcaps[-1], "positions needs an entry per batch slot")
+        _require(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape[1:]) == (H_q, D)
+                 and out.shape[0] >= bcaps[-1], "out must be contiguous float32 [>= max batch cap, H_q, D]")
+        if (cow_src is None) != (cow_dst is None):
+            raise PkvError(-2, "cow_src and cow_dst go together")
+        if cow_src is not None:
+            for t, nm in ((cow_src, "cow_src"), (cow_dst, "cow_dst")):
+                _int32_1d(t, nm, t.shape[0])
+                _require(t.shape[0] >= bcaps[-1], f"{nm} needs an entry per batch slot")
+        need = decode_workspace_bytes(bcaps[-1], H_q, D, ccaps[-1], partition_size) if partition_size else 0
+        if need and workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        self._keep = (q, k_new, v_new, k_pool, v_pool, block_tables, positions, out, cow_src, cow_dst, workspace)
+        d = StepDesc()
+        d.dtype, d.H_q, d.H_kv, d.D, d.block_size, d.n_blocks = _dtype_code(q), H_q, H_kv, D, bs, n_blocks
+        d.scale, d.partition_size = float(scale), int(partition_size)
+        d.out, d.q, d.q_row_stride = out.data_ptr(), q.data_ptr(), qrs
+        d.k_new, d.v_new, d.new_row_stride = k_new.data_ptr(), v_new.data_ptr(), nrs
+        d.k_pool, d.v_pool = k_pool.data_ptr(), v_pool.data_ptr()
+        d.block_tables, d.bt_stride, d.positions = block_tables.data_ptr(), bts, positions.data_ptr()
+        d.cow_src = cow_src.data_ptr() if cow_src is not None else None
+        d.cow_dst = cow_dst.data_ptr() if cow_dst is not None else None
+        d.workspace = workspace.data_ptr() if workspace is not None else None
+        d.workspace_bytes = workspace.numel() if workspace is not None else 0
+        self._desc = d
+        lib = load_library()
+        bc = (ctypes.c_int32 * len(bcaps))(*bcaps)
+        cc = (ctypes.c_int32 * len(ccaps))(*ccaps)
+        h = lib.pkv_step_graphs_create(ctypes.byref(d), ctypes.cast(bc, ctypes.c_void_p), len(bcaps),
+                                       ctypes.cast(cc, ctypes.c_void_p), len(ccaps))
+        if not h:
+            raise PkvError(-5, "pkv_step_graphs_create: " + lib.pkv_last_error().decode())
+        self._lib, self._h = lib, ctypes.c_void_p(h)
+        self.batch_caps, self.ctx_caps = bcaps, ccaps
+
+    def launch(self, B: int, max_context_len: int, n_copies: int = 0, *, stream=None):
+        _check(self._lib.pkv_step_graphs_launch(self._h, int(B), int(max_context_len), int(n_copies),
+                                                _stream(stream)), "step_graphs_launch")
+
+    def close(self):
+        if getattr(self, "_h", None) is not None:
+            self._lib.pkv_step_graphs_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+
+class Decoder:
+    """One call per decode step (``pkv_decoder_*``): the library's block manager
+    reserves the batch's slots, the metadata is staged to the device on a side
+    stream, and the step runs as a graph replay (when capacity lists are given)
+    or call by call.  ``block_manager`` registers, forks and frees sequences.
+
+    q, k_new, v_new and out are device tensors with ``max_batch`` rows; before
+    each step the caller writes row b for seq_ids[b].
+    """
+
+    def __init__(self, q, k_new, v_new, k_pool, v_pool, out, scale: float, bt_stride: int, *,
+                 partition_size: int = 0, workspace=None, shuffle_seed: int = 0, batch_caps=None, ctx_caps=None):
+        torch = _torch()
+        n_blocks, H_kv, bs, D = _pool_dims(k_pool, v_pool)
+        max_batch, H_q = q.shape[0], q.shape[1]
+        for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new")):
+            _require(t.dtype == k_pool.dtype and t.shape[0] == max_batch, f"{nm}: pool dtype, max_batch rows")
+        qrs = _rows(q, "q", H_q, D)
+        nrs = _rows(k_new, "k_new", H_kv, D)
+        _require(_rows(v_new, "v_new", H_kv, D) == nrs, "k_new and v_new must share a row stride")
+        _require(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (max_batch, H_q, D),
+                 "out must be contiguous float32 [max_batch, H_q, D]")
+        if partition_size and workspace is None:
+            need = decode_workspace_bytes(max_batch, H_q, D, bt_stride * bs, partition_size)
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        self._keep = (q, k_new, v_new, k_pool, v_pool, out, workspace)
+        d = DecoderDesc()
+        d.dtype, d.H_q, d.H_kv, d.D, d.block_size, d.n_blocks = _dtype_code(q), H_q, H_kv, D, bs, n_blocks
+        d.scale, d.partition_size, d.max_batch, d.bt_stride = float(scale), int(partition_size), max_batch, bt_stride
+        d.out, d.q, d.q_row_stride = out.data_ptr(), q.data_ptr(), qrs
+        d.k_new, d.v_new, d.new_row_stride = k_new.data_ptr(), v_new.data_ptr(), nrs
+        d.k_pool, d.v_pool = k_pool.data_ptr(), v_pool.data_ptr()
+        d.workspace = workspace.data_ptr() if workspace is not None else None
+        d.workspace_bytes = workspace.numel() if workspace is not None else 0
+        d.shuffle_seed = int(shuffle_seed) & ((1 << 64) - 1)
+        self._caps = None
+        if batch_caps is not None:
+            bc = (ctypes.c_int32 * len(batch_caps))(*[int(x) for x in batch_caps])
+            cc = (ctypes.c_int32 * len(ctx_caps))(*[int(x) for x in ctx_caps])
+            self._caps = (bc, cc)
+            d.batch_caps, d.n_batch_caps = ctypes.cast(bc, ctypes.c_void_p), len(batch_caps)
+            d.ctx_caps, d.n_ctx_caps = ctypes.cast(cc, ctypes.c_void_p), len(ctx_caps)
+        lib = load_library()
+        h = lib.pkv_decoder_create(ctypes.byref(d))
+        if not h:
+            raise PkvError(-5, "pkv_decoder_create: " + lib.pkv_last_error().decode())
+        self._lib, self._h = lib, ctypes.c_void_p(h)
+        self.max_batch, self.bt_stride = max_batch, bt_stride
+        self.block_manager = BlockManager(n_blocks, bs, _borrow=(lib.pkv_decoder_block_manager(self._h), self))
+        self._ids = None
+
+    def step(self, seq_ids, *, stream=None) -> int:
+        """Enqueue one decode step for seq_ids; returns the number of copy-on-write block copies."""
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        n = ctypes.c_int32(0)
+        _check(self._lib.pkv_decoder_step(self._h, _np_ptr(ids), ids.shape[0], _stream(stream), ctypes.byref(n)),
+               "decoder_step")
+        return n.value
+
+    def close(self):
+        if getattr(self, "_h", None) is not None:
+            self.block_manager.close()
+            self._lib.pkv_decoder_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()

@@ -151,3 +151,69 @@ def test_copy_blocks_validation(lib, kw, status):
     assert copy_blocks(lib, **kw) == status
     if status:
         assert lib.pkv_last_error()
+
+
+@pytest.mark.parametrize("cname,cls", [("pkv_step_desc", pkv.StepDesc), ("pkv_decoder_desc", pkv.DecoderDesc)])
+def test_desc_layout_matches_c(tmp_path, cname, cls):
+    """The binding's ctypes mirrors of the C structs have the C compiler's size and field offsets."""
+    fields = [f[0] for f in cls._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "pkv.h"\nint main(void) {\n'
+                   f'  printf("%zu\\n", sizeof({cname}));\n'
+                   + "".join(f'  printf("%zu\\n", offsetof({cname}, {f}));\n' for f in fields) + "}\n")
+    exe = tmp_path / "layout"
+    import subprocess
+    subprocess.run(["gcc", "-I" + os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(cls)
+    assert got[1:] == [getattr(cls, f).offset for f in fields]
+
+
+def test_step_graphs_create_validation(lib):
+    """Invalid descriptions are rejected before any HIP call (NULL, with a reason)."""
+    d = pkv.StepDesc()
+    d.dtype, d.H_q, d.H_kv, d.D, d.block_size, d.n_blocks = 1, 8, 2, 128, 16, 64
+    d.positions, d.block_tables, d.bt_stride = FAKE, FAKE, 4
+    caps = (ctypes.c_int32 * 3)(1, 2, 4)
+    bad = (ctypes.c_int32 * 3)(1, 4, 2)
+    P = lambda a: ctypes.cast(a, ctypes.c_void_p)
+    assert lib.pkv_step_graphs_create(None, P(caps), 3, P(caps), 3) is None
+    assert lib.pkv_step_graphs_create(ctypes.byref(d), P(caps), 0, P(caps), 3) is None
+    assert lib.pkv_step_graphs_create(ctypes.byref(d), P(bad), 3, P(caps), 3) is None
+    assert b"increasing" in lib.pkv_last_error()
+    big = (ctypes.c_int32 * 1)(65)                       # > bt_stride * block_size = 64
+    assert lib.pkv_step_graphs_create(ctypes.byref(d), P(caps), 3, P(big), 1) is None
+    assert b"exceeds" in lib.pkv_last_error()
+    d.cow_src = FAKE                                     # cow_dst missing
+    assert lib.pkv_step_graphs_create(ctypes.byref(d), P(caps), 3, P(caps), 3) is None
+    d.cow_src = None
+    d.partition_size, d.workspace, d.workspace_bytes = 16, None, 0
+    ctx = (ctypes.c_int32 * 3)(16, 32, 64)              # split into 16-token partitions: needs a workspace
+    assert lib.pkv_step_graphs_create(ctypes.byref(d), P(caps), 3, P(ctx), 3) is None
+    assert b"workspace" in lib.pkv_last_error()
+    assert lib.pkv_step_graphs_launch(None, 1, 1, 0, None) == E_NULL
+    lib.pkv_step_graphs_destroy(None)
+
+
+def test_decoder_create_validation(lib):
+    """Invalid decoder descriptions are rejected before any HIP call."""
+    d = pkv.DecoderDesc()
+    d.dtype, d.H_q, d.H_kv, d.D, d.block_size, d.n_blocks = 1, 8, 2, 128, 16, 64
+    d.max_batch, d.bt_stride = 4, 8
+    assert lib.pkv_decoder_create(None) is None
+    d.max_batch = 0
+    assert lib.pkv_decoder_create(ctypes.byref(d)) is None
+    d.max_batch = 4
+    bc = (ctypes.c_int32 * 2)(2, 3)                      # must end at max_batch = 4
+    cc = (ctypes.c_int32 * 2)(64, 128)                   # and at bt_stride * block_size = 128
+    d.batch_caps, d.n_batch_caps = ctypes.cast(bc, ctypes.c_void_p), 2
+    d.ctx_caps, d.n_ctx_caps = ctypes.cast(cc, ctypes.c_void_p), 2
+    assert lib.pkv_decoder_create(ctypes.byref(d)) is None
+    assert b"capacity" in lib.pkv_last_error()
+    bc[1] = 4
+    d.partition_size = 32                                # split needs a workspace
+    assert lib.pkv_decoder_create(ctypes.byref(d)) is None
+    assert b"workspace" in lib.pkv_last_error()
+    assert lib.pkv_decoder_step(None, None, 1, None, None) == E_NULL
+    assert lib.pkv_decoder_block_manager(None) is None
+    lib.pkv_decoder_destroy(None)
