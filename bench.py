@@ -132,6 +132,89 @@ def cpu_baseline(w, step_bytes_total: float, kv_tokens: int, budget_s: float = 1
     }
 
 
+def resident_steps(lib, torch, pkv, dev, w, append: bool, P: int, R: int):
+    """R device-resident copies of the workload's inputs and, for each, the C-ABI
+    call (function, arguments without the trailing stream) of one decode step."""
+    from workloads.device import upload
+
+    cfg = w.cfg
+    B, H_q, H_kv, D, bs = cfg.B, cfg.H_q, cfg.H_kv, cfg.D, cfg.block_size
+    max_ctx = int(w.context_lens.max())
+    base = upload(w, dev)
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(R - 1)]
+    ws_bytes = pkv.decode_workspace_bytes(B, H_q, D, max_ctx, P)
+    calls = []
+    P_ = ctypes.c_void_p
+    dt = DTYPE_CODE[cfg.dtype]
+    for s in sets:
+        s["out"] = torch.empty((B, H_q, D), dtype=torch.float32, device=dev)
+        s["ws"] = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+        if append:
+            a = (dt, P_(s["out"].data_ptr()), P_(s["q"].data_ptr()), H_q * D, P_(s["k_new"].data_ptr()),
+                 P_(s["v_new"].data_ptr()), H_kv * D, P_(s["k_pool"].data_ptr()), P_(s["v_pool"].data_ptr()),
+                 P_(s["block_tables"].data_ptr()), w.block_tables.shape[1], P_(s["positions"].data_ptr()),
+                 B, H_q, H_kv, D, bs, w.n_blocks, max_ctx, ctypes.c_float(float(w.scale)), P,
+                 P_(s["ws"].data_ptr()), ws_bytes)
+            calls.append((lib.pkv_append_decode_attention, a))
+        else:
+            a = (dt, P_(s["out"].data_ptr()), P_(s["q"].data_ptr()), H_q * D, P_(s["k_pool"].data_ptr()),
+                 P_(s["v_pool"].data_ptr()), P_(s["block_tables"].data_ptr()), w.block_tables.shape[1],
+                 P_(s["context_lens"].data_ptr()), B, H_q, H_kv, D, bs, w.n_blocks, max_ctx,
+                 ctypes.c_float(float(w.scale)), P, P_(s["ws"].data_ptr()), ws_bytes)
+            calls.append((lib.pkv_paged_decode_attention, a))
+    return calls, sets
+
+
+def cumask_bench(args) -> int:
+    """Decode-step bandwidth on CU-limited streams, alone and beside a GEMM.
+
+    Runs the library's standalone program pkv_cumask (a child process on the
+    system ROCm runtime; PyTorch's bundled HIP runtime cannot create CU-masked
+    queues here) on the workload's shape and lengths, and prints its result as
+    one JSON line.  The parent never initialises the GPU.
+    """
+    if not os.environ.get("PKV_CUMASK_ENABLE"):
+        # Switched off: the program ended with SIGSEGV and no output when started from a
+        # Python process; it stays off until the cause is found.
+        print(json.dumps({"mode": "cumask", "error": "disabled: pkv_cumask crashed (SIGSEGV, no output) when "
+                                                     "started from Python; cause not found"}))
+        return 4
+    import subprocess
+    from workloads import draw_lengths, get_config
+
+    cfg = get_config(args.config)
+    append = not args.no_append
+    P = cfg.partition_size if args.partition is None else args.partition
+    seed = args.seed if args.seed is not None else int(cfg.name[1:])
+    lens = draw_lengths(cfg, np.random.default_rng(seed))
+    factor = cfg.pool[1] if cfg.pool[0] == "factor" else 1.0
+    prog = os.path.join(ROOT, "paged_kv_decode_blocks_amd", "pkv_cumask")
+    if not os.path.exists(prog):
+        print(json.dumps({"error": f"{prog} not built (paged_kv_decode_blocks_amd.build)"}))
+        return 3
+    cmd = [prog, "sweep", cfg.dtype, str(cfg.B), str(cfg.H_q), str(cfg.H_kv), str(cfg.D), str(P),
+           "1" if append else "0", repr(float(factor)), str(seed), str(max(args.steps // 4, 20)),
+           ",".join(str(int(x)) for x in lens)]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=900)
+    if r.returncode != 0:
+        print(json.dumps({"error": f"pkv_cumask exited with {r.returncode}"}))
+        return r.returncode
+    res = json.loads(r.stdout.strip().splitlines()[-1])
+    print(json.dumps({
+        "mode": "cumask",
+        "metric": "decode-step HBM bandwidth on CU-limited streams",
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded finite values; lengths drawn as the workload's; resident, rotated past "
+                "the Infinity Cache)",
+        "config": {"workload": workload_label(cfg, ("fused append + attention" if append else "attention")
+                                              + (f" (split {P})" if P else ""))},
+        **res,
+    }))
+    return 0
+
+
 def loop_bench(args, torch, pkv, dev) -> int:
     """A decode loop driven by the library's block manager.
 
@@ -314,7 +397,7 @@ def main(argv=None):
     ap.add_argument("--no-graph", action="store_true", help="launch every step eagerly (for counter runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times (scales HBM byte counters)")
-    ap.add_argument("--mode", default="step", choices=["step", "loop"],
+    ap.add_argument("--mode", default="step", choices=["step", "loop", "cumask"],
                     help="step: the headline step over resident inputs; loop: a block-manager-driven decode loop")
     ap.add_argument("--graphs", action="store_true", help="loop mode: replay captured step graphs")
     ap.add_argument("--native", action="store_true", help="loop mode: one pkv_decoder_step call per step")
@@ -326,10 +409,12 @@ def main(argv=None):
                           "n_gpus": args.gpus}))
         return 2
 
+    if args.mode == "cumask":
+        return cumask_bench(args)
+
     import torch
     import paged_kv_decode_blocks_amd as pkv
     from workloads import get_config, make_workload, step_bytes
-    from workloads.device import upload
 
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
@@ -361,28 +446,7 @@ def main(argv=None):
     read_per_step = sb["kv_history"]
 
     R = args.rotate or max(2, math.ceil(4 * INFINITY_CACHE_BYTES / max(read_per_step, 1)))
-    base = upload(w, dev)
-    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(R - 1)]
-    ws_bytes = pkv.decode_workspace_bytes(B, H_q, D, max_ctx, P)
-    calls = []
-    P_ = ctypes.c_void_p
-    dt = DTYPE_CODE[cfg.dtype]
-    for s in sets:
-        s["out"] = torch.empty((B, H_q, D), dtype=torch.float32, device=dev)
-        s["ws"] = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-        if append:
-            a = (dt, P_(s["out"].data_ptr()), P_(s["q"].data_ptr()), H_q * D, P_(s["k_new"].data_ptr()),
-                 P_(s["v_new"].data_ptr()), H_kv * D, P_(s["k_pool"].data_ptr()), P_(s["v_pool"].data_ptr()),
-                 P_(s["block_tables"].data_ptr()), w.block_tables.shape[1], P_(s["positions"].data_ptr()),
-                 B, H_q, H_kv, D, bs, w.n_blocks, max_ctx, ctypes.c_float(float(w.scale)), P,
-                 P_(s["ws"].data_ptr()), ws_bytes)
-            calls.append((lib.pkv_append_decode_attention, a))
-        else:
-            a = (dt, P_(s["out"].data_ptr()), P_(s["q"].data_ptr()), H_q * D, P_(s["k_pool"].data_ptr()),
-                 P_(s["v_pool"].data_ptr()), P_(s["block_tables"].data_ptr()), w.block_tables.shape[1],
-                 P_(s["context_lens"].data_ptr()), B, H_q, H_kv, D, bs, w.n_blocks, max_ctx,
-                 ctypes.c_float(float(w.scale)), P, P_(s["ws"].data_ptr()), ws_bytes)
-            calls.append((lib.pkv_paged_decode_attention, a))
+    calls, sets = resident_steps(lib, torch, pkv, dev, w, append, P, R)
 
     def step(k):
         """One decode step on input set k % R, enqueued on torch's current stream."""

@@ -452,6 +452,35 @@ pkv_block_manager* pkv_decoder_block_manager(pkv_decoder* dec);
  * NULL) receives the number of copy-on-write block copies the step made. */
 int pkv_decoder_step(pkv_decoder* dec, const int64_t* seq_ids, int32_t B, void* stream, int32_t* n_copies);
 
+/*
+ * ---------------------------------------------------------------------------
+ * CU-limited streams: decode attention on a share of the GPU
+ * ---------------------------------------------------------------------------
+ * Attention offloaded next to other work on the same GPU runs on a bounded
+ * share of the GPU's SMs, since decode attention is bandwidth-bound and needs
+ * only a fraction of them to draw most of the memory bandwidth (the
+ * "Injecting Adrenaline into LLM Serving" review, section 3.3).  On MI355X the
+ * mechanism is a stream with a compute-unit mask: kernels launched on it run
+ * only on the selected CUs.  Every entry point above takes such a stream.
+ */
+
+/* Number of compute units of the current HIP device (256 on MI355X), or a
+ * negative pkv_status. */
+int pkv_device_cu_count(void);
+
+/* Host-only helper: set in mask[0 .. n_words) the bits of `count` CUs out of
+ * n_cus (bit i of word w = CU 32*w + i, the runtime's CU numbering).
+ * layout 0 = the first `count` CUs; layout 1 = `count` CUs spread evenly over
+ * all n_cus (CU floor(j * n_cus / count) for j < count).  All other bits are
+ * cleared.  Requires 1 <= count <= n_cus <= 32 * n_words. */
+int pkv_cu_mask(int32_t n_cus, int32_t count, int layout, uint32_t* mask, int32_t n_words);
+
+/* Create a stream (default priority, non-blocking) whose kernels run only on
+ * the CUs set in mask[0 .. n_words); *stream receives the hipStream_t.  The
+ * caller destroys it with pkv_stream_destroy. */
+int pkv_stream_create_cu_masked(const uint32_t* mask, int32_t n_words, void** stream);
+int pkv_stream_destroy(void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -15,6 +15,7 @@ Entry points (same names as the C ABI without the ``pkv_`` prefix):
   BlockManager              host-side block allocation, sharing and reclaim (pkv_bm_*)
   StepGraphs                the fused step captured per (batch, context) bucket (pkv_step_graphs_*)
   Decoder                   one call per decode step: manager, staged metadata, graph or eager launch
+  cu_mask, CuMaskedStream   streams whose kernels run on a chosen subset of compute units
 """
 from __future__ import annotations
 
@@ -25,7 +26,8 @@ from typing import Optional
 __all__ = [
     "PkvError", "LIB_PATH", "load_library", "library_loaded", "kv_append", "paged_decode_attention",
     "append_decode_attention", "decode_workspace_bytes", "last_launch", "version", "probe_stream_read",
-    "PKV_F32", "PKV_F16", "PKV_BF16", "EXPORTED_SYMBOLS", "copy_blocks", "BlockManager", "StepGraphs", "Decoder",
+    "PKV_F32", "PKV_F16", "PKV_BF16", "EXPORTED_SYMBOLS", "copy_blocks", "BlockManager", "StepGraphs", "Decoder", "cu_mask", "CuMaskedStream",
+    "device_cu_count",
     "PKV_ERR_OUT_OF_BLOCKS", "PKV_ERR_SEQUENCE",
 ]
 
@@ -45,6 +47,7 @@ EXPORTED_SYMBOLS = (
     "pkv_bm_num_sequences", "pkv_bm_sequence_length", "pkv_bm_block_refcount", "pkv_bm_block_table",
     "pkv_bm_batch_tables", "pkv_step_graphs_create", "pkv_step_graphs_launch", "pkv_step_graphs_destroy",
     "pkv_decoder_create", "pkv_decoder_destroy", "pkv_decoder_block_manager", "pkv_decoder_step",
+    "pkv_device_cu_count", "pkv_cu_mask", "pkv_stream_create_cu_masked", "pkv_stream_destroy",
 )
 
 _lib = None
@@ -157,6 +160,14 @@ def load_library(path: Optional[str] = None):
     lib.pkv_decoder_block_manager.restype = P
     lib.pkv_decoder_step.argtypes = [P, P, I32, P, P]
     lib.pkv_decoder_step.restype = C
+    lib.pkv_device_cu_count.argtypes = []
+    lib.pkv_device_cu_count.restype = C
+    lib.pkv_cu_mask.argtypes = [I32, I32, C, P, I32]
+    lib.pkv_cu_mask.restype = C
+    lib.pkv_stream_create_cu_masked.argtypes = [P, I32, ctypes.POINTER(ctypes.c_void_p)]
+    lib.pkv_stream_create_cu_masked.restype = C
+    lib.pkv_stream_destroy.argtypes = [P]
+    lib.pkv_stream_destroy.restype = C
     if path is None:
         _lib = lib
     return lib
@@ -613,3 +624,55 @@ class Decoder:
 
     def __del__(self):
         self.close()
+
+
+# ---------------------------------------------------------------------------
+# CU-limited streams
+# ---------------------------------------------------------------------------
+
+def device_cu_count() -> int:
+    n = int(load_library().pkv_device_cu_count())
+    if n < 0:
+        _check(n, "device_cu_count")
+    return n
+
+
+def cu_mask(n_cus: int, count: int, layout: str = "spread"):
+    """uint32 words selecting `count` of `n_cus` CUs: 'first' = CUs 0..count-1, 'spread' = evenly strided."""
+    import numpy as np
+    words = (n_cus + 31) // 32
+    mask = np.zeros(words, dtype=np.uint32)
+    _check(load_library().pkv_cu_mask(int(n_cus), int(count), {"first": 0, "spread": 1}[layout], _np_ptr(mask),
+                                      words), "cu_mask")
+    return mask
+
+
+class CuMaskedStream:
+    """A HIP stream restricted to the CUs of ``mask``; ``.torch`` is the same stream as a torch.cuda.ExternalStream
+    (for torch work on it), ``.ptr`` the raw hipStream_t for the library's ``stream=`` arguments."""
+
+    def __init__(self, mask):
+        import numpy as np
+        m = np.ascontiguousarray(np.asarray(mask, dtype=np.uint32))
+        out = ctypes.c_void_p()
+        lib = load_library()
+        _check(lib.pkv_stream_create_cu_masked(_np_ptr(m), m.shape[0], ctypes.byref(out)), "stream_create_cu_masked")
+        self._lib, self.ptr = lib, out.value
+        self.mask = m
+        self.torch = _torch().cuda.ExternalStream(self.ptr)
+
+    @property
+    def cuda_stream(self):
+        return self.ptr
+
+    def close(self):
+        if getattr(self, "ptr", None):
+            _torch().cuda.synchronize()
+            self._lib.pkv_stream_destroy(ctypes.c_void_p(self.ptr))
+            self.ptr = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

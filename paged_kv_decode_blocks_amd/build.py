@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libpkv.so")
 
-SOURCES = ["api.cpp", "block_manager.cpp", "step_graphs.cpp", "decoder.cpp", "kv_append.hip", "block_copy.hip", "decode_mha.hip", "decode_gqa.hip", "lse_merge.hip", "probe.hip"]
+SOURCES = ["api.cpp", "block_manager.cpp", "step_graphs.cpp", "decoder.cpp", "cu_streams.cpp", "kv_append.hip", "block_copy.hip", "decode_mha.hip", "decode_gqa.hip", "lse_merge.hip", "probe.hip"]
 
 # Packed-fp32 instructions are switched off for all device code.
 HIPCC_FLAGS = [
@@ -57,7 +57,24 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
     tmp = LIB_PATH + ".tmp%d" % os.getpid()
     subprocess.run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], check=True)
     os.replace(tmp, LIB_PATH)
+    _build_programs(hipcc, obj_dir)
     return LIB_PATH
+
+
+# Standalone programs linked against libpkv.so (found next to them at run time).
+PROGRAMS = {"pkv_cumask": ("pkv_cumask.cpp", ["-lrocblas"])}
+
+
+def _build_programs(hipcc: str, obj_dir: str):
+    for name, (src, libs) in PROGRAMS.items():
+        obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
+        subprocess.run([hipcc, "-x", "hip", *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], check=True,
+                       stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+        out = os.path.join(HERE, name)
+        tmp = out + ".tmp%d" % os.getpid()
+        subprocess.run([hipcc, "--offload-arch=gfx950", "-o", tmp, obj, "-L" + HERE, "-lpkv", *libs,
+                        "-Wl,-rpath,$ORIGIN", "-Wl,-rpath,/opt/rocm/lib"], check=True)
+        os.replace(tmp, out)
 
 
 if __name__ == "__main__":

