@@ -51,6 +51,14 @@ def _load():
         lib.oracle_paged_decode_attention.restype = ctypes.c_int
         lib.oracle_threads.argtypes = [I32]
         lib.oracle_threads.restype = ctypes.c_int
+        lib.oracle_e4m3_decode.argtypes = [P, P, I64]
+        lib.oracle_e4m3_decode.restype = ctypes.c_int
+        lib.oracle_e4m3_quantize_row.argtypes = [ctypes.c_int, P, I32, P, P]
+        lib.oracle_e4m3_quantize_row.restype = ctypes.c_int
+        lib.oracle_kv_append_fp8.argtypes = [ctypes.c_int, P, P, I64, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32]
+        lib.oracle_kv_append_fp8.restype = ctypes.c_int
+        lib.oracle_e4m3_dequantize_rows.argtypes = [P, P, I64, I32, P]
+        lib.oracle_e4m3_dequantize_rows.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -126,3 +134,60 @@ def run_step(w, nthreads: int = 0):
     out = paged_decode_attention(w.cfg.dtype, w.q, k_pool, v_pool, w.block_tables, w.context_lens,
                                  w.scale, nthreads=nthreads)
     return out, k_pool, v_pool
+
+
+# ---------------------------------------------------------------------------
+# FP8 (OCP E4M3) K/V cache with one power-of-two scale per token row and head
+# ---------------------------------------------------------------------------
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """uint8 E4M3 codes -> float64 values (NaN for S.1111.111)."""
+    src = np.ascontiguousarray(codes, dtype=np.uint8)
+    dst = np.empty(src.size, dtype=np.float64)
+    _check(_load().oracle_e4m3_decode(_ptr(src), _ptr(dst), src.size), "e4m3_decode")
+    return dst.reshape(src.shape)
+
+
+def e4m3_quantize_row(dtype: str, row: np.ndarray):
+    """One row of source-dtype storage elements -> (uint8 codes, float32 power-of-two scale)."""
+    src = np.ascontiguousarray(row)
+    codes = np.empty(src.size, dtype=np.uint8)
+    scale = np.zeros(1, dtype=np.float32)
+    _check(_load().oracle_e4m3_quantize_row(_DTYPE_CODE[dtype], _ptr(src), src.size, _ptr(codes), _ptr(scale)),
+           "e4m3_quantize_row")
+    return codes, np.float32(scale[0])
+
+
+def kv_append_fp8(dtype: str, k_new, v_new, k_pool, v_pool, k_scale, v_scale, block_tables, positions,
+                  block_size: int):
+    """Quantize the new K/V rows (source dtype) into their slots, in place on the code and scale pools."""
+    B, H_kv, D = k_new.shape
+    for a in (k_new, v_new, k_pool, v_pool, k_scale, v_scale, block_tables, positions):
+        assert a.flags.c_contiguous
+    assert k_pool.dtype == np.uint8 and k_scale.dtype == np.float32
+    rc = _load().oracle_kv_append_fp8(_DTYPE_CODE[dtype], _ptr(k_new), _ptr(v_new), H_kv * D, _ptr(k_pool),
+                                      _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
+                                      block_tables.shape[1], _ptr(positions), B, H_kv, D, block_size,
+                                      k_pool.shape[0])
+    _check(rc, "oracle_kv_append_fp8")
+
+
+def e4m3_dequantize(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """Pools of codes [..., D] and scales [...] -> float32 values (exact)."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    s = np.ascontiguousarray(scale, dtype=np.float32)
+    assert c.shape[:-1] == s.shape
+    D = c.shape[-1]
+    out = np.empty(c.shape, dtype=np.float32)
+    _check(_load().oracle_e4m3_dequantize_rows(_ptr(c), _ptr(s), s.size, D, _ptr(out)), "e4m3_dequantize")
+    return out
+
+
+def paged_decode_attention_fp8(q_dtype: str, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens,
+                               scale, *, with_lse: bool = False, nthreads: int = 0):
+    """fp64 attention over FP8 pools: the float32 attention on the exactly dequantized pools, q exactly widened."""
+    qf = decode(q_dtype, q).astype(np.float32) if q_dtype != "f32" else np.ascontiguousarray(q)
+    kf = e4m3_dequantize(k_pool, k_scale)
+    vf = e4m3_dequantize(v_pool, v_scale)
+    return paged_decode_attention("f32", qf, kf, vf, block_tables, context_lens, scale, with_lse=with_lse,
+                                  nthreads=nthreads)

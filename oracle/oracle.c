@@ -253,3 +253,136 @@ int oracle_threads(int32_t nthreads) {
     return 1;
 #endif
 }
+
+/*
+ * ---------------------------------------------------------------------------
+ * FP8 K/V cache
+ * ---------------------------------------------------------------------------
+ * "从 PagedAttention 到 Prefill-Decode 分离的深度解析", section 6.2: a
+ * low-precision KV cache stores K/V in a few bits with fine-grained block
+ * scales and dequantizes them before attention.  Reading taken here (the page
+ * gives no layout): 8-bit OCP E4M3 codes (sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits, no infinities, S.1111.111 = NaN, largest finite 448; the
+ * format gfx950 decodes in hardware), with one power-of-two scale per token row
+ * and KV head, so that each appended row is quantized on its own:
+ *   amax  = max_d |x_d|                       (x the row in its source dtype)
+ *   E     = max(floor(log2 amax) - 8, -126)   (E = 0 when amax = 0)
+ *   scale = 2^E                               (so amax / scale lies in [256, 512))
+ *   code  = the E4M3 value nearest to x_d / scale, magnitudes above 448 taken
+ *           as 448, ties to the even code; the sign bit is the sign of x_d
+ * and the dequantized value is value(code) * scale (exact in double and f32).
+ * Dividing by a power of two is exact, so the only rounding is the one to the
+ * E4M3 grid, done here by searching the grid.
+ */
+
+/* OCP E4M3 code -> double, from the format's definition. */
+static double e4m3_value(uint8_t c) {
+    int sign = (c >> 7) & 1;
+    int ex = (c >> 3) & 15;
+    int man = c & 7;
+    double v;
+    if (ex == 15 && man == 7) return NAN;
+    if (ex == 0) v = ldexp((double)man, -9);              /* zero or subnormal: man/8 * 2^-6 */
+    else v = ldexp(1.0 + man / 8.0, ex - 7);
+    return sign ? -v : v;
+}
+
+int oracle_e4m3_decode(const uint8_t* codes, double* dst, int64_t n) {
+    if (n < 0 || (n && (!codes || !dst))) return ORC_ERR_ARG;
+    for (int64_t i = 0; i < n; ++i) dst[i] = e4m3_value(codes[i]);
+    return ORC_OK;
+}
+
+/* The non-negative code (0x00 .. 0x7E) whose value is nearest to a, 0 <= a; ties to the even code. */
+static uint8_t e4m3_nearest_magnitude(double a) {
+    if (a > 448.0) a = 448.0;
+    int best = 0;
+    double best_err = fabs(a - e4m3_value(0));
+    for (int c = 1; c <= 0x7E; ++c) {
+        double err = fabs(a - e4m3_value((uint8_t)c));
+        if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    return (uint8_t)best;
+}
+
+/* Quantize one row of D source elements: codes[0 .. D) and its scale. */
+int oracle_e4m3_quantize_row(int src_dtype, const void* src, int32_t D, uint8_t* codes, float* scale) {
+    if (!elem_size(src_dtype) || D <= 0 || !src || !codes || !scale) return ORC_ERR_ARG;
+    double amax = 0.0;
+    for (int32_t d = 0; d < D; ++d) {
+        double x = load_elem(src_dtype, src, d);
+        if (!isfinite(x)) return ORC_ERR_RANGE;
+        if (fabs(x) > amax) amax = fabs(x);
+    }
+    int E = 0;
+    if (amax > 0.0) {
+        int e2;
+        frexp(amax, &e2);               /* amax = f * 2^e2, f in [0.5, 1): floor(log2 amax) = e2 - 1 */
+        E = e2 - 1 - 8;
+        if (E < -126) E = -126;
+    }
+    const double s = ldexp(1.0, E);
+    for (int32_t d = 0; d < D; ++d) {
+        double v = load_elem(src_dtype, src, d) / s;
+        uint8_t mag = e4m3_nearest_magnitude(fabs(v));
+        codes[d] = (uint8_t)(signbit(v) ? (mag | 0x80) : mag);
+    }
+    *scale = (float)s;
+    return ORC_OK;
+}
+
+/*
+ * FP8 append: quantize k_new[b][g][:] and v_new[b][g][:] (source dtype) and
+ * write the codes to slot positions[b] % block_size of block
+ * block_tables[b][positions[b] / block_size], the scales to the same
+ * (block, head, slot) of k_scale / v_scale ([n_blocks][H_kv][block_size] f32).
+ */
+int oracle_kv_append_fp8(int src_dtype, const void* k_new, const void* v_new, int64_t new_row_stride,
+                         uint8_t* k_pool, uint8_t* v_pool, float* k_scale, float* v_scale,
+                         const int32_t* block_tables, int32_t bt_stride, const int32_t* positions,
+                         int32_t B, int32_t H_kv, int32_t D, int32_t block_size, int32_t n_blocks) {
+    int e = elem_size(src_dtype);
+    if (!e || B < 0 || H_kv <= 0 || D <= 0 || block_size <= 0 || n_blocks <= 0 || bt_stride <= 0)
+        return ORC_ERR_ARG;
+    if (B == 0) return ORC_OK;
+    if (!k_new || !v_new || !k_pool || !v_pool || !k_scale || !v_scale || !block_tables || !positions)
+        return ORC_ERR_ARG;
+    if (new_row_stride < (int64_t)H_kv * D) return ORC_ERR_ARG;
+    for (int32_t b = 0; b < B; ++b) {
+        int32_t p = positions[b];
+        if (p < 0 || p / block_size >= bt_stride) return ORC_ERR_RANGE;
+        int32_t blk = block_tables[(int64_t)b * bt_stride + p / block_size];
+        if (blk < 0 || blk >= n_blocks) return ORC_ERR_RANGE;
+    }
+    for (int32_t b = 0; b < B; ++b) {
+        int32_t p = positions[b];
+        int32_t blk = block_tables[(int64_t)b * bt_stride + p / block_size];
+        int32_t slot = p % block_size;
+        for (int32_t g = 0; g < H_kv; ++g) {
+            int64_t row = ((int64_t)blk * H_kv + g) * block_size + slot;
+            const char* ks = (const char*)k_new + ((int64_t)b * new_row_stride + (int64_t)g * D) * e;
+            const char* vs = (const char*)v_new + ((int64_t)b * new_row_stride + (int64_t)g * D) * e;
+            int st = oracle_e4m3_quantize_row(src_dtype, ks, D, k_pool + row * D, k_scale + row);
+            if (st == ORC_OK) st = oracle_e4m3_quantize_row(src_dtype, vs, D, v_pool + row * D, v_scale + row);
+            if (st != ORC_OK) return st;
+        }
+    }
+    return ORC_OK;
+}
+
+/*
+ * Dequantize n_rows rows of D codes with one scale per row into float32:
+ * dst[r][d] = value(codes[r][d]) * scale[r] (exact for every finite code and
+ * power-of-two scale >= 2^-126).  The FP8 attention is the float32 attention
+ * above on pools dequantized this way.
+ */
+int oracle_e4m3_dequantize_rows(const uint8_t* codes, const float* scale, int64_t n_rows, int32_t D, float* dst) {
+    if (n_rows < 0 || D <= 0 || (n_rows && (!codes || !scale || !dst))) return ORC_ERR_ARG;
+    for (int64_t r = 0; r < n_rows; ++r)
+        for (int32_t d = 0; d < D; ++d)
+            dst[r * D + d] = (float)(e4m3_value(codes[r * D + d]) * (double)scale[r]);
+    return ORC_OK;
+}
