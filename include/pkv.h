@@ -202,6 +202,68 @@ int pkv_probe_stream_read(const void* buf, size_t bytes, void* sink, int32_t gri
 
 /*
  * ---------------------------------------------------------------------------
+ * FP8 K/V cache
+ * ---------------------------------------------------------------------------
+ * A low-precision KV cache stores K/V in a few bits with fine-grained scales
+ * and dequantizes them before attention ("从 PagedAttention 到 Prefill-Decode
+ * 分离的深度解析", section 6.2); decode attention reads the whole history every
+ * step, so one-byte codes halve its HBM traffic against f16/bf16.  Format:
+ * OCP E4M3 codes (bias 7, no infinities, S.1111.111 = NaN, largest 448) with one
+ * power-of-two float scale per token row and KV head:
+ *   k_pool, v_pool   : [n_blocks][H_kv][block_size][D] uint8 codes
+ *   k_scale, v_scale : [n_blocks][H_kv][block_size] float32
+ * Quantizing a row x: E = max(floor(log2 max|x|) - 8, -126) (0 for a zero row),
+ * scale = 2^E, code = nearest E4M3 value to x / scale (ties to even, magnitudes
+ * above 448 clamped, sign kept); its value is code * scale.  Each row is
+ * quantized on its own when it is appended.  Non-finite new K/V values are
+ * outside the contract.  q, k_new and v_new keep their own dtype (q_dtype /
+ * src_dtype: PKV_F32, PKV_F16 or PKV_BF16); out is float32.  Pools 16-byte
+ * aligned, scale arrays 4-byte aligned; other rules as the calls above.  Any
+ * H_q / H_kv grouping runs per query head.
+ */
+
+/* Quantize each request's new K/V rows into slot positions[b] of its block. */
+int pkv_kv_append_fp8(int src_dtype,
+                      const void* k_new, const void* v_new, int64_t new_row_stride,
+                      uint8_t* k_pool, uint8_t* v_pool, float* k_scale, float* v_scale,
+                      const int32_t* block_tables, int32_t bt_stride,
+                      const int32_t* positions,
+                      int32_t B, int32_t H_kv, int32_t D,
+                      int32_t block_size, int32_t n_blocks,
+                      void* stream);
+
+/* pkv_paged_decode_attention over FP8 pools (same arguments and workspace rule). */
+int pkv_paged_decode_attention_fp8(int q_dtype,
+                                   float* out,
+                                   const void* q, int64_t q_row_stride,
+                                   const uint8_t* k_pool, const uint8_t* v_pool,
+                                   const float* k_scale, const float* v_scale,
+                                   const int32_t* block_tables, int32_t bt_stride,
+                                   const int32_t* context_lens,
+                                   int32_t B, int32_t H_q, int32_t H_kv, int32_t D,
+                                   int32_t block_size, int32_t n_blocks,
+                                   int32_t max_context_len, float scale, int32_t partition_size,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/* pkv_append_decode_attention over FP8 pools: the new rows (q_dtype) are
+ * quantized in the attention launch, written with their scales, and attended
+ * to as stored. */
+int pkv_append_decode_attention_fp8(int q_dtype,
+                                    float* out,
+                                    const void* q, int64_t q_row_stride,
+                                    const void* k_new, const void* v_new, int64_t new_row_stride,
+                                    uint8_t* k_pool, uint8_t* v_pool, float* k_scale, float* v_scale,
+                                    const int32_t* block_tables, int32_t bt_stride,
+                                    const int32_t* positions,
+                                    int32_t B, int32_t H_q, int32_t H_kv, int32_t D,
+                                    int32_t block_size, int32_t n_blocks,
+                                    int32_t max_context_len, float scale, int32_t partition_size,
+                                    void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/*
+ * ---------------------------------------------------------------------------
  * Block manager (host side): the paging lifecycle of the KV pool
  * ---------------------------------------------------------------------------
  * Physical blocks are handed out only when a sequence's next token needs one,

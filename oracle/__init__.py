@@ -124,10 +124,19 @@ def threads(nthreads: int = 0) -> int:
 def run_step(w, nthreads: int = 0):
     """One whole decode step on a ``workloads.Workload``: append (if any), then attention.
 
-    Returns (out fp64 [B,H_q,D], k_pool_after, v_pool_after); the workload's
-    own pools are left untouched.
+    Returns (out fp64 [B,H_q,D], k_pool_after, v_pool_after) -- for an FP8
+    workload each pool is a (codes, scales) pair; the workload's own pools are
+    left untouched.
     """
     k_pool, v_pool = w.k_pool.copy(), w.v_pool.copy()
+    if getattr(w.cfg, "fp8", False):
+        k_scale, v_scale = w.k_scale.copy(), w.v_scale.copy()
+        if w.positions is not None:
+            kv_append_fp8(w.cfg.dtype, w.k_new, w.v_new, k_pool, v_pool, k_scale, v_scale, w.block_tables,
+                          w.positions, w.cfg.block_size)
+        out = paged_decode_attention_fp8(w.cfg.dtype, w.q, k_pool, v_pool, k_scale, v_scale, w.block_tables,
+                                         w.context_lens, w.scale, nthreads=nthreads)
+        return out, (k_pool, k_scale), (v_pool, v_scale)
     if w.positions is not None:
         kv_append(w.cfg.dtype, w.k_new, w.v_new, k_pool, v_pool, w.block_tables, w.positions,
                   w.cfg.block_size)

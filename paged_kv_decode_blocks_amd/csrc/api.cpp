@@ -70,7 +70,8 @@ struct Plan {
 };
 
 // Launch geometry.  Unsplit: one partition spanning the padded context.
-Plan make_plan(int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t max_ctx, int32_t partition_size) {
+Plan make_plan(int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t max_ctx, int32_t partition_size,
+               bool fp8 = false) {
     Plan p{};
     const int32_t padded = max_ctx <= 0 ? pkv::kBlockSize
                                         : (max_ctx + pkv::kBlockSize - 1) / pkv::kBlockSize * pkv::kBlockSize;
@@ -82,14 +83,23 @@ Plan make_plan(int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32
         p.n_parts = (max_ctx + partition_size - 1) / partition_size;
     }
     const int32_t G = H_q / H_kv;
-    p.grouped = G > 1 && dtype != PKV_F32;
+    p.grouped = G > 1 && dtype != PKV_F32 && !fp8;
     const int32_t blocks = p.part_tokens / pkv::kBlockSize;
     // Waves per workgroup and blocks per chunk, from launch-shape sweeps on MI355X:
     // when the grid already holds several workgroups per CU (split contexts, large
     // batches) small 4-wave workgroups let a CU overlap several workgroups' load
     // latency; a long unsplit context per workgroup spreads over more waves.
     const int64_t wgs = (int64_t)p.n_parts * B * (p.grouped ? H_kv : H_q);
-    if (p.grouped) {
+    if (fp8) {
+        // one-byte codes: twice the blocks per chunk keeps the bytes in flight of the f16 path
+        int nw = 4, ch = 4, pf = 1;
+        if (p.n_parts == 1 && wgs > 4 * 256 && blocks >= 64) { nw = 8; ch = 2; pf = 2; }
+        p.nw = env_int("PKV_FP8_NW", nw);
+        p.ch = env_int("PKV_FP8_CH", ch);
+        p.pf = env_int("PKV_FP8_PF", pf);
+        if (!pkv::fp8_variant_exists(p.nw, p.ch, p.pf)) { p.nw = nw; p.ch = ch; p.pf = pf; }
+        p.grid = (unsigned)wgs;
+    } else if (p.grouped) {
         // measured on c5-shaped batches: 2-wave workgroups with register-staged loads (more
         // workgroups per CU) beat deeper register pipelines and the LDS ring
         p.kind = env_int("PKV_GQA_KIND", 0);
@@ -151,12 +161,19 @@ int check_stride(const char* name, int64_t stride, int64_t min_elems, int eb) {
     return PKV_OK;
 }
 
+struct Fp8Scales {
+    const float* k;
+    const float* v;
+    float* k_w;
+    float* v_w;
+};
+
 int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride, const void* k_new, const void* v_new,
                      int64_t new_row_stride, const void* k_pool, const void* v_pool, void* k_pool_w, void* v_pool_w,
                      const int32_t* block_tables, int32_t bt_stride, const int32_t* context_lens,
                      const int32_t* positions, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t block_size,
                      int32_t n_blocks, int32_t max_ctx, float scale, int32_t partition_size, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+                     size_t workspace_bytes, void* stream, const Fp8Scales* fp8 = nullptr) {
     const bool fused = positions != nullptr;
     int st = check_common(dtype, B, H_q, H_kv, D, block_size, n_blocks, bt_stride, max_ctx, partition_size);
     if (st) return st;
@@ -170,8 +187,13 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
     if ((st = check_stride("q_row_stride", q_row_stride, (int64_t)H_q * D, eb))) return st;
     if (fused && (st = check_stride("new_row_stride", new_row_stride, (int64_t)H_kv * D, eb))) return st;
     if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
+    if (fp8) {
+        if (!fp8->k || !fp8->v) return fail(PKV_ERR_NULL, "k_scale and v_scale must not be NULL");
+        if ((reinterpret_cast<uintptr_t>(fp8->k) | reinterpret_cast<uintptr_t>(fp8->v)) & 3u)
+            return fail(PKV_ERR_INVALID_ARG, "k_scale and v_scale must be 4-byte aligned");
+    }
 
-    const Plan p = make_plan(dtype, B, H_q, H_kv, D, max_ctx, partition_size);
+    const Plan p = make_plan(dtype, B, H_q, H_kv, D, max_ctx, partition_size, fp8 != nullptr);
     if ((int64_t)p.n_parts * B * (p.grouped ? H_kv : H_q) > 0x7fffffff)
         return fail(PKV_ERR_INVALID_ARG, "grid too large");
     if (p.ws_total) {
@@ -208,10 +230,17 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
     a.part_tokens = p.part_tokens;
     a.n_parts = p.n_parts;
     a.scale_log2 = scale * pkv::kLog2e;
+    if (fp8) {
+        a.k_scale = fp8->k;
+        a.v_scale = fp8->v;
+        a.k_scale_w = fp8->k_w;
+        a.v_scale_w = fp8->v_w;
+    }
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = p.grouped ? pkv::launch_decode_gqa(dtype, D, p.kind, p.nw, p.ch, p.pf, fused, a, p.grid, s)
-                             : pkv::launch_decode_mha(dtype, D, p.nw, p.ch, p.pf, fused, a, p.grid, s);
+    hipError_t e = fp8         ? pkv::launch_decode_fp8(dtype, D, p.nw, p.ch, p.pf, fused, a, p.grid, s)
+                   : p.grouped ? pkv::launch_decode_gqa(dtype, D, p.kind, p.nw, p.ch, p.pf, fused, a, p.grid, s)
+                               : pkv::launch_decode_mha(dtype, D, p.nw, p.ch, p.pf, fused, a, p.grid, s);
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
     if (p.n_parts > 1) {
         pkv::MergeArgs m{};
@@ -229,7 +258,8 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
         if (e != hipSuccess) return fail(PKV_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
     }
     snprintf(g_launch, sizeof g_launch, "%s dtype=%d D=%d nw=%d ch=%d pf=%d grid=%u part_tokens=%d n_parts=%d%s",
-             p.grouped ? (p.kind ? "gqa_mfma_lds" : "gqa_mfma") : "mha", dtype, D, p.nw, p.ch, p.pf, p.grid,
+             fp8 ? "fp8" : p.grouped ? (p.kind ? "gqa_mfma_lds" : "gqa_mfma") : "mha", dtype, D, p.nw, p.ch, p.pf,
+             p.grid,
              p.part_tokens, p.n_parts,
              fused ? " fused_append" : "");
     g_err[0] = 0;
@@ -297,6 +327,76 @@ int pkv_kv_append(int dtype, const void* k_new, const void* v_new, int64_t new_r
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "kv_append launch: %s", hipGetErrorString(e));
     g_err[0] = 0;
     return PKV_OK;
+}
+
+int pkv_kv_append_fp8(int src_dtype, const void* k_new, const void* v_new, int64_t new_row_stride, uint8_t* k_pool,
+                      uint8_t* v_pool, float* k_scale, float* v_scale, const int32_t* block_tables, int32_t bt_stride,
+                      const int32_t* positions, int32_t B, int32_t H_kv, int32_t D, int32_t block_size,
+                      int32_t n_blocks, void* stream) {
+    const int eb = elem_bytes(src_dtype);
+    if (!eb) return fail(PKV_ERR_UNSUPPORTED, "src_dtype %d is not one of PKV_F32/F16/BF16", src_dtype);
+    if (B < 0) return fail(PKV_ERR_INVALID_ARG, "B = %d is negative", B);
+    if (H_kv <= 0) return fail(PKV_ERR_INVALID_ARG, "H_kv = %d must be positive", H_kv);
+    if (D != 64 && D != 128) return fail(PKV_ERR_UNSUPPORTED, "head dim D = %d (built: 64, 128)", D);
+    if (block_size != pkv::kBlockSize)
+        return fail(PKV_ERR_UNSUPPORTED, "block_size = %d (built: %d)", block_size, pkv::kBlockSize);
+    if (n_blocks <= 0) return fail(PKV_ERR_INVALID_ARG, "n_blocks = %d must be positive", n_blocks);
+    if (bt_stride <= 0) return fail(PKV_ERR_INVALID_ARG, "bt_stride = %d must be positive", bt_stride);
+    if (B == 0) {
+        pkv::clear_error();
+        return PKV_OK;
+    }
+    if (!k_new || !v_new || !k_pool || !v_pool || !k_scale || !v_scale || !block_tables || !positions)
+        return fail(PKV_ERR_NULL, "a required pointer is NULL");
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool) ||
+        ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 3u))
+        return fail(PKV_ERR_INVALID_ARG, "rows and pools must be 16-byte aligned, scales 4-byte aligned");
+    int st = check_stride("new_row_stride", new_row_stride, (int64_t)H_kv * D, eb);
+    if (st) return st;
+    pkv::AppendFp8Args a{};
+    a.k_new = reinterpret_cast<const char*>(k_new);
+    a.v_new = reinterpret_cast<const char*>(v_new);
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.block_tables = block_tables;
+    a.positions = positions;
+    a.new_row_stride = new_row_stride;
+    a.bt_stride = bt_stride;
+    a.B = B;
+    a.H_kv = H_kv;
+    a.n_blocks = n_blocks;
+    hipError_t e = pkv::launch_kv_append_fp8(src_dtype, D, a, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "kv_append_fp8 launch: %s", hipGetErrorString(e));
+    pkv::clear_error();
+    return PKV_OK;
+}
+
+int pkv_paged_decode_attention_fp8(int q_dtype, float* out, const void* q, int64_t q_row_stride,
+                                   const uint8_t* k_pool, const uint8_t* v_pool, const float* k_scale,
+                                   const float* v_scale, const int32_t* block_tables, int32_t bt_stride,
+                                   const int32_t* context_lens, int32_t B, int32_t H_q, int32_t H_kv, int32_t D,
+                                   int32_t block_size, int32_t n_blocks, int32_t max_context_len, float scale,
+                                   int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+    const Fp8Scales sc{k_scale, v_scale, nullptr, nullptr};
+    return launch_attention(q_dtype, out, q, q_row_stride, nullptr, nullptr, 0, k_pool, v_pool, nullptr, nullptr,
+                            block_tables, bt_stride, context_lens, nullptr, B, H_q, H_kv, D, block_size, n_blocks,
+                            max_context_len, scale, partition_size, workspace, workspace_bytes, stream, &sc);
+}
+
+int pkv_append_decode_attention_fp8(int q_dtype, float* out, const void* q, int64_t q_row_stride, const void* k_new,
+                                    const void* v_new, int64_t new_row_stride, uint8_t* k_pool, uint8_t* v_pool,
+                                    float* k_scale, float* v_scale, const int32_t* block_tables, int32_t bt_stride,
+                                    const int32_t* positions, int32_t B, int32_t H_q, int32_t H_kv, int32_t D,
+                                    int32_t block_size, int32_t n_blocks, int32_t max_context_len, float scale,
+                                    int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+    if (B > 0 && !positions) return fail(PKV_ERR_NULL, "positions is NULL");
+    const Fp8Scales sc{k_scale, v_scale, k_scale, v_scale};
+    return launch_attention(q_dtype, out, q, q_row_stride, k_new, v_new, new_row_stride, k_pool, v_pool, k_pool,
+                            v_pool, block_tables, bt_stride, nullptr, B > 0 ? positions : nullptr, B, H_q, H_kv, D,
+                            block_size, n_blocks, max_context_len, scale, partition_size, workspace,
+                            workspace_bytes, stream, &sc);
 }
 
 int pkv_probe_stream_read(const void* buf, size_t bytes, void* sink, int32_t grid, void* stream) {

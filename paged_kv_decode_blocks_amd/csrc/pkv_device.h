@@ -10,7 +10,7 @@
 
 namespace pkv {
 
-enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };   // storage dtypes of q, K/V and new rows
 
 constexpr int kBlockSize = 16;   // tokens per physical KV block (the only size built)
 constexpr float kLog2e = 1.4426950408889634f;
@@ -175,6 +175,10 @@ struct AttnArgs {
     const int32_t* positions;      // appended slot (fused call); n = positions + 1
     const char* k_new;             // [B][H_kv][D] (fused call)
     const char* v_new;
+    const float* k_scale;          // FP8 pools only: [n_blocks][H_kv][16] per-row scales
+    const float* v_scale;
+    float* k_scale_w;              // same, written by the fused FP8 append
+    float* v_scale_w;
     int64_t q_row_stride;          // elements
     int64_t new_row_stride;        // elements
     int32_t bt_stride;

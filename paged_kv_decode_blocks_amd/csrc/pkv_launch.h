@@ -41,6 +41,26 @@ struct CopyArgs {
 constexpr int kCopyPieceBytes = 4096;   // bytes one 256-thread workgroup moves per piece
 
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
+
+// FP8 (OCP E4M3) K/V cache: one power-of-two scale per (block, KV head, slot).
+struct AppendFp8Args {
+    const char* k_new;          // source rows, src dtype
+    const char* v_new;
+    uint8_t* k_pool;
+    uint8_t* v_pool;
+    float* k_scale;
+    float* v_scale;
+    const int32_t* block_tables;
+    const int32_t* positions;
+    int64_t new_row_stride;     // elements
+    int32_t bt_stride;
+    int32_t B, H_kv, n_blocks;
+};
+hipError_t launch_kv_append_fp8(int src_dtype, int D, const AppendFp8Args& a, hipStream_t stream);
+// per query head; q (and new rows) in q_dtype, K/V codes + scales in the AttnArgs pools
+hipError_t launch_decode_fp8(int q_dtype, int D, int nw, int ch, int pf, bool append, const AttnArgs& a,
+                             unsigned grid, hipStream_t stream);
+bool fp8_variant_exists(int nw, int ch, int pf);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_decode_mha(int dtype, int D, int nw, int ch, int pf, bool append, const AttnArgs& a,
                              unsigned grid, hipStream_t stream);

@@ -246,3 +246,33 @@ def test_cu_mask_and_stream_validation(lib):
     assert lib.pkv_stream_create_cu_masked(ctypes.cast(zero, ctypes.c_void_p), 8, ctypes.byref(out)) == E_ARG
     assert lib.pkv_stream_create_cu_masked(None, 8, ctypes.byref(out)) == E_NULL
     assert lib.pkv_stream_destroy(None) == E_NULL
+
+
+def test_fp8_entry_point_validation(lib):
+    P = ctypes.c_void_p
+    # (q_dtype, out, q, qrs, kp, vp, ks, vs, bt, bts, ctx, B, H_q, H_kv, D, bs, nb, maxc, scale, P, ws, wsb, stream)
+    base = [1, FAKE, FAKE, 8 * 128, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 2, 8, 8, 128, 16, 64, 100, 0.1, 0,
+            None, 0, None]
+    def call(kw):
+        a = list(base)
+        for k, v in kw.items():
+            a[k] = v
+        return lib.pkv_paged_decode_attention_fp8(*a)
+    assert call({0: 9}) == E_UNSUP                 # q dtype
+    assert call({6: None}) == E_NULL               # k_scale
+    assert call({7: FAKE + 2}) == E_ARG            # v_scale not 4-byte aligned
+    assert call({4: FAKE + 8}) == E_ARG            # pool not 16-byte aligned
+    assert call({14: 96}) == E_UNSUP               # D
+    assert call({11: 0}) == OK                     # B == 0: nothing to do
+    # append: (src_dtype, k_new, v_new, rs, kp, vp, ks, vs, bt, bts, pos, B, H_kv, D, bs, nb, stream)
+    app = [1, FAKE, FAKE, 8 * 128, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 2, 8, 128, 16, 64, None]
+    def append(kw):
+        a = list(app)
+        for k, v in kw.items():
+            a[k] = v
+        return lib.pkv_kv_append_fp8(*a)
+    assert append({0: 5}) == E_UNSUP
+    assert append({7: None}) == E_NULL
+    assert append({3: 100}) == E_ARG               # row stride below H_kv * D
+    assert append({11: 0}) == OK
+    assert lib.pkv_status_string(E_UNSUP) == b"PKV_ERR_UNSUPPORTED"

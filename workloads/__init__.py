@@ -17,6 +17,14 @@ Storage dtypes on the host:
 Every slot of the pool that holds no valid token (unassigned blocks, slots at
 or past a request's history length, the slot the step's append will fill) is a
 quiet NaN, so any stray read shows up in the output.
+
+FP8 K/V workloads (``kv_dtype="fp8"``) hold OCP E4M3 codes (uint8) and one
+float32 scale per (block, KV head, slot).  The generator draws codes and scales
+directly -- codes with exponent fields concentrated around 12.5 (spread 1.6),
+uniform mantissas and signs, so a row looks like a quantized Gaussian whose
+largest values sit near the top of the E4M3 range; scales 2^k with k uniform in
+[-12, -8] -- and never quantizes anything.  Their poison is the NaN code 0x7F
+with a NaN scale.  q, k_new and v_new keep ``dtype``.
 """
 from __future__ import annotations
 
@@ -29,7 +37,7 @@ import numpy as np
 __all__ = [
     "Config", "Workload", "CONFIGS", "get_config", "make_workload", "draw_lengths",
     "DTYPE_BYTES", "NAN_BITS", "to_storage", "storage_dtype",
-    "kv_bytes_per_token", "step_bytes",
+    "kv_bytes_per_token", "step_bytes", "draw_e4m3_codes",
 ]
 
 DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
@@ -86,10 +94,15 @@ class Config:
     kv_std: float = 1.0
     append: bool = False      # the step appends one new token per request before attention
     partition_size: int = 0   # split-KV partition length in tokens (0 = whole context per workgroup)
+    kv_dtype: str = ""        # "" = same as dtype; "fp8" = OCP E4M3 codes with per-row scales
 
     @property
     def G(self) -> int:
         return self.H_q // self.H_kv
+
+    @property
+    def fp8(self) -> bool:
+        return self.kv_dtype == "fp8"
 
 
 # The five workloads.  Shapes, dtypes, length mixes and pool sizes follow the
@@ -113,6 +126,22 @@ CONFIGS = {
                  B=32, H_q=64, H_kv=8, D=128, dtype="bf16", block_size=16,
                  lengths=("uniform", 4096, 16384), pool=("factor", 1.2), partition_size=1024),
 }
+# the same decode batches with an FP8 K/V cache (q, new rows and output keep their dtype)
+CONFIGS["c3f8"] = replace(CONFIGS["c3"], name="c3f8", kv_dtype="fp8",
+                          title="large decode batch, FP8 E4M3 K/V (B80, 32 heads MHA, D128, f16 q, ctx U[128,2048], "
+                                "append)")
+CONFIGS["c5f8"] = replace(CONFIGS["c5"], name="c5f8", kv_dtype="fp8",
+                          title="GQA long context, FP8 E4M3 K/V (B32, 64 q / 8 kv heads, D128, bf16 q, "
+                                "ctx U[4096,16384], split 1024)")
+
+
+def draw_e4m3_codes(rng: np.random.Generator, shape) -> np.ndarray:
+    """E4M3 codes shaped like a quantized Gaussian row (never the NaN code)."""
+    ex = np.clip(np.rint(rng.normal(12.5, 1.6, shape)), 0, 15).astype(np.uint8)
+    man = rng.integers(0, 8, shape).astype(np.uint8)
+    man = np.where((ex == 15) & (man == 7), 6, man).astype(np.uint8)
+    sign = rng.integers(0, 2, shape).astype(np.uint8)
+    return ((sign << 7) | (ex << 3) | man).astype(np.uint8)
 
 
 def get_config(name: str, **overrides) -> Config:
@@ -135,6 +164,8 @@ class Workload:
     v_new: Optional[np.ndarray]
     scale: np.float32
     meta: dict = field(default_factory=dict)
+    k_scale: Optional[np.ndarray] = None   # FP8 pools only: [n_blocks, H_kv, bs] float32
+    v_scale: Optional[np.ndarray] = None
 
     @property
     def max_context_len(self) -> int:
@@ -207,23 +238,39 @@ def make_workload(cfg: Config, seed: Optional[int] = None, *, append: Optional[b
     q = to_storage(cfg.q_std * rng.standard_normal((B, cfg.H_q, D), dtype=np.float32), cfg.dtype)
 
     poison = _poison(cfg.dtype)
-    pools = []
-    for _ in range(2):  # K then V
-        pool = np.full((n_blocks, H_kv, bs, D), poison, dtype=sdt)
+    pools, scales = [], []
+    for _ in range(2):  # K then V (FP8: codes then scales for each)
+        if cfg.fp8:
+            pool = np.full((n_blocks, H_kv, bs, D), 0x7F, dtype=np.uint8)
+            sc = np.full((n_blocks, H_kv, bs), np.nan, dtype=np.float32)
+        else:
+            pool = np.full((n_blocks, H_kv, bs, D), poison, dtype=sdt)
         for b in range(B):
             h = int(hist[b])
             full, rem = divmod(h, bs)
             nfill = full + (1 if rem else 0)
             if nfill == 0:
                 continue
-            vals = cfg.kv_std * rng.standard_normal((nfill, H_kv, bs, D), dtype=np.float32)
-            vals = to_storage(vals, cfg.dtype)
             ids = bt[b, :nfill]
-            if rem:
-                vals[-1, :, rem:, :] = poison
-            pool[ids] = vals
+            if cfg.fp8:
+                vals = draw_e4m3_codes(rng, (nfill, H_kv, bs, D))
+                svals = (2.0 ** rng.integers(-12, -7, (nfill, H_kv, bs))).astype(np.float32)
+                if rem:
+                    vals[-1, :, rem:, :] = 0x7F
+                    svals[-1, :, rem:] = np.nan
+                pool[ids] = vals
+                sc[ids] = svals
+            else:
+                vals = cfg.kv_std * rng.standard_normal((nfill, H_kv, bs, D), dtype=np.float32)
+                vals = to_storage(vals, cfg.dtype)
+                if rem:
+                    vals[-1, :, rem:, :] = poison
+                pool[ids] = vals
         pools.append(pool)
+        if cfg.fp8:
+            scales.append(sc)
     k_pool, v_pool = pools
+    k_scale, v_scale = scales if cfg.fp8 else (None, None)
 
     k_new = v_new = positions = None
     if append:
@@ -234,7 +281,7 @@ def make_workload(cfg: Config, seed: Optional[int] = None, *, append: Optional[b
     scale = np.float32(1.0 / math.sqrt(D))
     return Workload(cfg=cfg, seed=seed, context_lens=ctx, positions=positions, block_tables=bt,
                     n_blocks=n_blocks, q=q, k_pool=k_pool, v_pool=v_pool, k_new=k_new, v_new=v_new,
-                    scale=scale, meta={"required_blocks": required})
+                    scale=scale, meta={"required_blocks": required}, k_scale=k_scale, v_scale=v_scale)
 
 
 # ---------------------------------------------------------------------------
@@ -255,13 +302,15 @@ def step_bytes(cfg: Config, context_lens: np.ndarray, append: bool) -> dict:
     not algorithmic bytes.
     """
     e = DTYPE_BYTES[cfg.dtype]
-    row = kv_bytes_per_token(cfg.H_kv, cfg.D, e)
+    # an FP8 row is D one-byte codes plus its 4-byte scale
+    row = 2.0 * cfg.H_kv * (cfg.D + 4) if cfg.fp8 else kv_bytes_per_token(cfg.H_kv, cfg.D, e)
     ctx = np.asarray(context_lens, dtype=np.int64)
     B = ctx.size
     hist = ctx - 1 if append else ctx
     out = {
         "kv_history": float(hist.sum() * row),
-        "append": float(2 * B * row) if append else 0.0,
+        # the new rows are read in q's dtype and written as stored
+        "append": float(B * (2.0 * cfg.H_kv * cfg.D * e + row)) if append else 0.0,
         "q": float(B * cfg.H_q * cfg.D * e),
         "out": float(B * cfg.H_q * cfg.D * 4),
         "block_tables": float(((ctx + cfg.block_size - 1) // cfg.block_size).sum() * 4),

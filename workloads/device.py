@@ -33,10 +33,16 @@ def upload(w, device="cuda"):
     """All buffers of a Workload as device tensors, in a dict."""
     import torch
     d = w.cfg.dtype
+    if w.cfg.fp8:
+        pools = {"k_pool": torch.from_numpy(np.ascontiguousarray(w.k_pool)).to(device),
+                 "v_pool": torch.from_numpy(np.ascontiguousarray(w.v_pool)).to(device),
+                 "k_scale": torch.from_numpy(np.ascontiguousarray(w.k_scale)).to(device),
+                 "v_scale": torch.from_numpy(np.ascontiguousarray(w.v_scale)).to(device)}
+    else:
+        pools = {"k_pool": to_tensor(w.k_pool, d, device), "v_pool": to_tensor(w.v_pool, d, device)}
     out = {
         "q": to_tensor(w.q, d, device),
-        "k_pool": to_tensor(w.k_pool, d, device),
-        "v_pool": to_tensor(w.v_pool, d, device),
+        **pools,
         "block_tables": torch.from_numpy(np.ascontiguousarray(w.block_tables)).to(device),
         "context_lens": torch.from_numpy(np.ascontiguousarray(w.context_lens)).to(device),
     }
