@@ -218,8 +218,11 @@ int pkv_probe_stream_read(const void* buf, size_t bytes, void* sink, int32_t gri
  * quantized on its own when it is appended.  Non-finite new K/V values are
  * outside the contract.  q, k_new and v_new keep their own dtype (q_dtype /
  * src_dtype: PKV_F32, PKV_F16 or PKV_BF16); out is float32.  Pools 16-byte
- * aligned, scale arrays 4-byte aligned; other rules as the calls above.  Any
- * H_q / H_kv grouping runs per query head.
+ * aligned, scale arrays 4-byte aligned; other rules as the calls above.  With
+ * grouped heads (H_q > H_kv) and f16/bf16 q the products run on the matrix
+ * cores over codes widened to q's type, and the fused call quantizes the new
+ * rows in a launch of its own before attention; otherwise attention runs per
+ * query head with the new rows quantized in the attention launch.
  */
 
 /* Quantize each request's new K/V rows into slot positions[b] of its block. */

@@ -65,6 +65,7 @@ struct Plan {
     bool grouped;     // matrix-core path (one workgroup per KV head and G query heads)
     int kind;         // grouped path: 0 = loads through registers, 1 = through an LDS ring
     int nw, ch, pf;   // waves per workgroup, blocks per chunk, chunks (or ring slots) in flight per wave
+    int wpe;          // grouped FP8 kernel: waves per SIMD its registers are sized for
     unsigned grid;
     size_t ws_o, ws_lse, ws_total;
 };
@@ -83,17 +84,25 @@ Plan make_plan(int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32
         p.n_parts = (max_ctx + partition_size - 1) / partition_size;
     }
     const int32_t G = H_q / H_kv;
-    p.grouped = G > 1 && dtype != PKV_F32 && !fp8;
+    p.grouped = G > 1 && dtype != PKV_F32;
     const int32_t blocks = p.part_tokens / pkv::kBlockSize;
     // Waves per workgroup and blocks per chunk, from launch-shape sweeps on MI355X:
     // when the grid already holds several workgroups per CU (split contexts, large
     // batches) small 4-wave workgroups let a CU overlap several workgroups' load
     // latency; a long unsplit context per workgroup spreads over more waves.
     const int64_t wgs = (int64_t)p.n_parts * B * (p.grouped ? H_kv : H_q);
-    if (fp8) {
-        // one-byte codes: twice the blocks per chunk keeps the bytes in flight of the f16 path
-        int nw = 4, ch = 4, pf = 1;
-        if (p.n_parts == 1 && wgs > 4 * 256 && blocks >= 64) { nw = 8; ch = 2; pf = 2; }
+    if (fp8 && p.grouped) {
+        p.kind = 2;   // grouped heads on MFMA over FP8 codes
+        p.nw = env_int("PKV_GQA8_NW", 2);
+        p.ch = env_int("PKV_GQA8_CH", 1);
+        p.pf = env_int("PKV_GQA8_PF", 1);
+        p.wpe = env_int("PKV_GQA8_WPE", 2);
+        if (!pkv::gqa_fp8_variant_exists(p.nw, p.ch, p.pf, p.wpe)) { p.nw = 2; p.ch = 1; p.pf = 1; p.wpe = 2; }
+        p.grid = (unsigned)wgs;
+    } else if (fp8) {
+        // launch-shape sweep on MI355X (c3-shaped FP8 batch): 4-wave workgroups with 2-block
+        // chunks beat 8 waves (the decode work per byte keeps register use high) and deeper pipelines
+        const int nw = 4, ch = 2, pf = 1;
         p.nw = env_int("PKV_FP8_NW", nw);
         p.ch = env_int("PKV_FP8_CH", ch);
         p.pf = env_int("PKV_FP8_PF", pf);
@@ -238,9 +247,35 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
     }
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = fp8         ? pkv::launch_decode_fp8(dtype, D, p.nw, p.ch, p.pf, fused, a, p.grid, s)
-                   : p.grouped ? pkv::launch_decode_gqa(dtype, D, p.kind, p.nw, p.ch, p.pf, fused, a, p.grid, s)
-                               : pkv::launch_decode_mha(dtype, D, p.nw, p.ch, p.pf, fused, a, p.grid, s);
+    hipError_t e = hipSuccess;
+    if (fp8 && p.grouped) {
+        // the grouped FP8 kernel reads the new row from the pool: quantize it there first
+        if (fused) {
+            pkv::AppendFp8Args ap{};
+            ap.k_new = a.k_new;
+            ap.v_new = a.v_new;
+            ap.k_pool = reinterpret_cast<uint8_t*>(k_pool_w);
+            ap.v_pool = reinterpret_cast<uint8_t*>(v_pool_w);
+            ap.k_scale = fp8->k_w;
+            ap.v_scale = fp8->v_w;
+            ap.block_tables = block_tables;
+            ap.positions = positions;
+            ap.new_row_stride = new_row_stride;
+            ap.bt_stride = bt_stride;
+            ap.B = B;
+            ap.H_kv = H_kv;
+            ap.n_blocks = n_blocks;
+            e = pkv::launch_kv_append_fp8(dtype, D, ap, s);
+            if (e != hipSuccess) return fail(PKV_ERR_HIP, "kv_append_fp8 launch: %s", hipGetErrorString(e));
+        }
+        e = pkv::launch_decode_gqa_fp8(dtype, D, p.nw, p.ch, p.pf, p.wpe, a, p.grid, s);
+    } else if (fp8) {
+        e = pkv::launch_decode_fp8(dtype, D, p.nw, p.ch, p.pf, fused, a, p.grid, s);
+    } else if (p.grouped) {
+        e = pkv::launch_decode_gqa(dtype, D, p.kind, p.nw, p.ch, p.pf, fused, a, p.grid, s);
+    } else {
+        e = pkv::launch_decode_mha(dtype, D, p.nw, p.ch, p.pf, fused, a, p.grid, s);
+    }
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
     if (p.n_parts > 1) {
         pkv::MergeArgs m{};
@@ -257,8 +292,9 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
         e = pkv::launch_lse_merge(D, m, s);
         if (e != hipSuccess) return fail(PKV_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
     }
-    snprintf(g_launch, sizeof g_launch, "%s dtype=%d D=%d nw=%d ch=%d pf=%d grid=%u part_tokens=%d n_parts=%d%s",
-             fp8 ? "fp8" : p.grouped ? (p.kind ? "gqa_mfma_lds" : "gqa_mfma") : "mha", dtype, D, p.nw, p.ch, p.pf,
+    snprintf(g_launch, sizeof g_launch, "%s dtype=%d D=%d nw=%d ch=%d pf=%d%s grid=%u part_tokens=%d n_parts=%d%s",
+             fp8 ? (p.grouped ? "gqa_mfma_fp8" : "fp8") : p.grouped ? (p.kind ? "gqa_mfma_lds" : "gqa_mfma") : "mha",
+             dtype, D, p.nw, p.ch, p.pf, (fp8 && p.grouped) ? (p.wpe == 3 ? " wpe=3" : " wpe=2") : "",
              p.grid,
              p.part_tokens, p.n_parts,
              fused ? " fused_append" : "");

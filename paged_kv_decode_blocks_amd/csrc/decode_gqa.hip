@@ -739,4 +739,327 @@ bool gqa_variant_exists(int kind, int nw, int ch, int pf) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Kernel 3: grouped heads over an FP8 (OCP E4M3) K/V cache.
+//
+// The same MFMA tiles in q's type (f16 or bf16): each lane loads its K piece
+// as 8 one-byte codes and its V piece as D/16 codes and widens them with
+// v_cvt_scalef32_pk_{bf16,f16}_fp8 at scale 1 (every E4M3 value is exact in
+// both types), so the product sees code values.  The row scales (one power of
+// two per token row and KV head) enter where the tokens are separate: the
+// score of token t is multiplied by k_scale[t] before the softmax, and its
+// weight by v_scale[t] before the P V product -- exact multiplications.  A lane
+// holds scores and V rows of the same four tokens per block (4 i + j), so it
+// loads those four scales of each pool.
+//
+// Lengths are context_lens[b], or positions[b] + 1 when context_lens is NULL:
+// the fused FP8 step appends with the quantizing append kernel first and then
+// runs this kernel over the updated pools.
+// ---------------------------------------------------------------------------
+template <int DT>
+__device__ __forceinline__ uint32_t fp8x2_widen(uint32_t w, bool hi) {
+    if constexpr (DT == DT_BF16) {
+        return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, true))
+                  : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, false));
+    } else {
+        return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, true))
+                  : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, false));
+    }
+}
+
+__device__ __forceinline__ uint32_t ld4(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+
+template <int DT, int D>
+struct GqaLaneF8 : GqaLane<DT, D, false> {
+    using Base = GqaLane<DT, D, false>;
+    static constexpr int KS = Base::KS, VT = Base::VT, NWORD = Base::NWORD;
+    static constexpr int VW = NWORD / 2 > 0 ? NWORD / 2 : 1;   // 32-bit words of V codes per row piece
+    int koff8[KS];     // byte offset of this lane's 8 K codes of step s inside a (block, head) tile
+    int voff8[4];      // byte offset of this lane's VT V codes of row-load i inside a tile
+    int soff[4];       // row (within the block) of this lane's token 4 i + j
+
+    __device__ __forceinline__ void init8(const AttnArgs& a, int lane, int b, int g) {
+        Base::init(a, lane, b, g);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) koff8[s] = this->tau * D + 32 * s + 8 * this->j;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            voff8[i] = (4 * i + this->j) * D + this->col * VT;
+            soff[i] = 4 * i + this->j;
+        }
+    }
+
+    __device__ __forceinline__ void load_v(const uint8_t* vb, int i, uint32_t (&vc)[VW]) const {
+        if constexpr (VT == 8) {
+            const uint2 v = ld8(vb + voff8[i]);
+            vc[0] = v.x;
+            vc[1] = v.y;
+        } else {
+            vc[0] = ld4(vb + voff8[i]);
+        }
+    }
+
+    // loads of one whole block: K codes (8 per step), V codes (VT per row), the four scales of each pool
+    __device__ __forceinline__ void load(const uint8_t* kb, const uint8_t* vb, const float* ksb, const float* vsb,
+                                         uint2 (&kc)[KS], uint32_t (&vc)[4][VW], float (&ks)[4], float (&vs)[4]) const {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) kc[s] = ld8(kb + koff8[s]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) load_v(vb, i, vc[i]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ks[i] = ksb[soff[i]];
+            vs[i] = vsb[soff[i]];
+        }
+    }
+
+    // Online-softmax update with CH blocks of codes.
+    template <int CH>
+    __device__ __forceinline__ void accumulate8(const uint2 (&kc)[CH][KS], const uint32_t (&vc)[CH][4][VW],
+                                                const float (&ks)[CH][4], const float (&vs)[CH][4],
+                                                const bool (&valid)[CH][4]) {
+        float sc[CH][4];
+#pragma unroll
+        for (int cb = 0; cb < CH; ++cb) {
+            floatx4 st = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const uint4 kw = make_uint4(fp8x2_widen<DT>(kc[cb][s].x, false), fp8x2_widen<DT>(kc[cb][s].x, true),
+                                            fp8x2_widen<DT>(kc[cb][s].y, false), fp8x2_widen<DT>(kc[cb][s].y, true));
+                st = Mfma<DT>::mma(kw, this->qf[s], st);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[cb][i] = mul_rn(st[i] * ks[cb][i], this->scale_log2);
+        }
+        float mloc = kNegBig;
+#pragma unroll
+        for (int cb = 0; cb < CH; ++cb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mloc = valid[cb][i] ? fmaxf(mloc, sc[cb][i]) : mloc;
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+        if (__builtin_amdgcn_ballot_w64(mloc > this->m + kRescaleSlack) != 0) {   // lazy rescale, as in GqaLane
+            const float m_new = fmaxf(this->m, mloc);
+            const float alpha = __builtin_amdgcn_exp2f(this->m - m_new);
+            this->m = m_new;
+            this->l *= alpha;
+#pragma unroll
+            for (int t = 0; t < VT; ++t) this->acc[t] *= alpha;
+        }
+#pragma unroll
+        for (int cb = 0; cb < CH; ++cb) {
+            float p[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float e = valid[cb][i] ? __builtin_amdgcn_exp2f(sc[cb][i] - this->m) : 0.0f;
+                this->l += e;
+                p[i] = e * vs[cb][i];
+            }
+            uint4 pk;
+            Mfma<DT>::split(p[0], p[1], pk.x, pk.z);
+            Mfma<DT>::split(p[2], p[3], pk.y, pk.w);
+            // widen the four V rows: word x of row i holds elements 2x, 2x+1 of the lane's piece
+            uint32_t vw[4][NWORD];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int x = 0; x < NWORD; ++x) vw[i][x] = fp8x2_widen<DT>(vc[cb][i][x >> 1], (x & 1) != 0);
+#pragma unroll
+            for (int t = 0; t < VT; ++t) {
+                const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+                const int x = t >> 1;
+                const uint32_t v01 = __builtin_amdgcn_perm(vw[1][x], vw[0][x], sel);
+                const uint32_t v23 = __builtin_amdgcn_perm(vw[3][x], vw[2][x], sel);
+                this->acc[t] = Mfma<DT>::mma(make_uint4(v01, v23, v01, v23), pk, this->acc[t]);
+            }
+        }
+    }
+
+    // One block not wholly below `lim`: masked loads.
+    __device__ __forceinline__ void partial_block8(const uint8_t* kb, const uint8_t* vb, const float* ksb,
+                                                   const float* vsb, int tb, int lim) {
+        uint2 kc[1][KS];
+        uint32_t vc[1][4][VW];
+        float ks[1][4], vs[1][4];
+        bool valid[1][4];
+        const int tk = tb + this->tau;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) kc[0][s] = tk < lim ? ld8(kb + koff8[s]) : make_uint2(0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tv = tb + soff[i];
+            valid[0][i] = tv < lim;
+#pragma unroll
+            for (int x = 0; x < VW; ++x) vc[0][i][x] = 0;
+            ks[0][i] = 0.0f;
+            vs[0][i] = 0.0f;
+            if (tv < lim) {
+                load_v(vb, i, vc[0][i]);
+                ks[0][i] = ksb[soff[i]];
+                vs[0][i] = vsb[soff[i]];
+            }
+        }
+        accumulate8<1>(kc, vc, ks, vs, valid);
+    }
+};
+
+// WPE: waves per SIMD the register allocation must leave room for (2 = as many
+// registers as the code wants; 3 trades a few spills for occupancy)
+template <int DT, int D, int NW, int CH, int PF, int WPE>
+__global__ __launch_bounds__(NW * 64, WPE) void decode_gqa_fp8_kernel(const AttnArgs a) {
+    using L = GqaLaneF8<DT, D>;
+    constexpr int KS = L::KS, VW = L::VW;
+    __shared__ int32_t s_ids[kWindowBlocksG];
+    __shared__ int s_bad;
+    __shared__ float s_m[NW][16];
+    __shared__ float s_l[NW][16];
+    __shared__ float s_o[NW * 16 * (D + 4)];
+
+    GqaUnit u;
+    gqa_indices(a, u);
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    L st;
+    st.init8(a, lane, u.b, u.g);
+    constexpr int PRE = (kWindowBlocksG + NW * 64 - 1) / (NW * 64);
+    int pre[PRE];
+    gqa_preload_ids<NW>(a, u, pre);
+    // lengths: context_lens, or positions + 1 after the fused call's append
+    {
+        const bool from_pos = a.context_lens == nullptr;
+        u.n = from_pos ? a.positions[u.b] + 1 : a.context_lens[u.b];
+        const bool bad_len = from_pos ? (u.n < 1 || u.n > a.max_context_len) : (u.n < 0 || u.n > a.max_context_len);
+        if (bad_len || u.n == 0) {
+            if (a.n_parts == 1 && u.part == 0)
+                for (int x = threadIdx.x; x < a.G * D; x += NW * 64)
+                    a.out[((size_t)u.b * a.H_q + (size_t)u.g * a.G) * D + x] = bad_len ? __builtin_nanf("") : 0.0f;
+            return;
+        }
+        u.start = u.part * a.part_tokens;
+        if (u.start >= u.n) return;
+        u.end = min(u.start + a.part_tokens, u.n);
+        u.lim = u.end;
+    }
+
+    const int32_t* table = a.block_tables + (int64_t)u.b * a.bt_stride;
+    const int nblk = (u.end - u.start + kBlockSize - 1) / kBlockSize;
+    const size_t blk_codes = (size_t)a.H_kv * kBlockSize * D;
+    const size_t head_codes = (size_t)u.g * kBlockSize * D;
+    const size_t blk_rows = (size_t)a.H_kv * kBlockSize;
+    const size_t head_rows = (size_t)u.g * kBlockSize;
+    const uint8_t* kpool = reinterpret_cast<const uint8_t*>(a.k_pool);
+    const uint8_t* vpool = reinterpret_cast<const uint8_t*>(a.v_pool);
+
+    auto load_full = [&](uint2 (&kc)[CH][KS], uint32_t (&vc)[CH][4][VW], float (&ks)[CH][4], float (&vs)[CH][4],
+                         int cb0) {
+#pragma unroll
+        for (int cb = 0; cb < CH; ++cb) {
+            const int id = __builtin_amdgcn_readfirstlane(s_ids[cb0 + cb]);
+            st.load(kpool + (size_t)id * blk_codes + head_codes, vpool + (size_t)id * blk_codes + head_codes,
+                    a.k_scale + (size_t)id * blk_rows + head_rows, a.v_scale + (size_t)id * blk_rows + head_rows,
+                    kc[cb], vc[cb], ks[cb], vs[cb]);
+        }
+    };
+    bool all_valid[CH][4];
+#pragma unroll
+    for (int cb = 0; cb < CH; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) all_valid[cb][i] = true;
+
+    if (threadIdx.x == 0) s_bad = 0;
+    for (int r0 = 0; r0 < nblk; r0 += kWindowBlocksG) {
+        const int nr = min(kWindowBlocksG, nblk - r0);
+        __syncthreads();
+        stage_ids<NW>(a, table, u.first_blk, r0, nr, pre, s_ids, &s_bad);
+        __syncthreads();
+        const int nch = (nr + CH - 1) / CH;
+        const int tok_r = u.start + r0 * kBlockSize;
+        const int nfull_all = max(0, min(nch, (u.lim - tok_r) / (CH * kBlockSize)));
+        const int nf = w < nfull_all ? (nfull_all - w + NW - 1) / NW : 0;
+        uint2 bk[PF][CH][KS];
+        uint32_t bv[PF][CH][4][VW];
+        float bks[PF][CH][4], bvs[PF][CH][4];
+        auto chunk_of = [&](int i) { return (w + NW * i) * CH; };
+        if (nf >= PF) {
+#pragma unroll
+            for (int v = 0; v < PF; ++v) load_full(bk[v], bv[v], bks[v], bvs[v], chunk_of(v));
+            int i = 0;
+            for (; i + 2 * PF <= nf; i += PF) {
+#pragma unroll
+                for (int v = 0; v < PF; ++v) {
+                    st.template accumulate8<CH>(bk[v], bv[v], bks[v], bvs[v], all_valid);
+                    load_full(bk[v], bv[v], bks[v], bvs[v], chunk_of(i + PF + v));
+                }
+            }
+            const int rem = nf - i - PF;
+#pragma unroll
+            for (int v = 0; v < PF; ++v) {
+                st.template accumulate8<CH>(bk[v], bv[v], bks[v], bvs[v], all_valid);
+                if (v < rem) load_full(bk[v], bv[v], bks[v], bvs[v], chunk_of(i + PF + v));
+            }
+#pragma unroll
+            for (int v = 0; v < PF; ++v)
+                if (v < rem) st.template accumulate8<CH>(bk[v], bv[v], bks[v], bvs[v], all_valid);
+        } else {
+            for (int i = 0; i < nf; ++i) {
+                load_full(bk[0], bv[0], bks[0], bvs[0], chunk_of(i));
+                st.template accumulate8<CH>(bk[0], bv[0], bks[0], bvs[0], all_valid);
+            }
+        }
+        for (int k = nfull_all + ((w - nfull_all) % NW + NW) % NW; k < nch; k += NW) {
+#pragma unroll
+            for (int cb = 0; cb < CH; ++cb) {
+                const int blk = k * CH + cb;
+                const int id = __builtin_amdgcn_readfirstlane(blk < nr ? s_ids[blk] : 0);
+                st.partial_block8(kpool + (size_t)id * blk_codes + head_codes,
+                                  vpool + (size_t)id * blk_codes + head_codes,
+                                  a.k_scale + (size_t)id * blk_rows + head_rows,
+                                  a.v_scale + (size_t)id * blk_rows + head_rows, tok_r + blk * kBlockSize, u.lim);
+            }
+        }
+    }
+    st.template finish<NW, D + 4>(a, s_m, s_l, s_o, w, u.b, u.g, u.part, s_bad != 0);
+}
+
+#define PKV_GQA_FP8_VARIANTS(X) \
+    X(2, 1, 1, 2) X(2, 1, 2, 2) X(4, 1, 1, 2) X(2, 2, 1, 2) X(4, 2, 1, 2) X(2, 1, 1, 3) X(4, 1, 1, 3)
+
+template <int DT, int D>
+static hipError_t launch_gqa_fp8_d(int nw, int ch, int pf, int wpe, const AttnArgs& a, unsigned grid,
+                                   hipStream_t s) {
+    switch (wpe * 1000 + nw * 100 + ch * 10 + pf) {
+#define PKV_CASE(NW_, CH_, PF_, W_)                                                                             \
+    case W_ * 1000 + NW_ * 100 + CH_ * 10 + PF_:                                                                \
+        hipLaunchKernelGGL((decode_gqa_fp8_kernel<DT, D, NW_, CH_, PF_, W_>), dim3(grid), dim3(NW_ * 64), 0, s, \
+                           a);                                                                                  \
+        return hipGetLastError();
+        PKV_GQA_FP8_VARIANTS(PKV_CASE)
+#undef PKV_CASE
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_decode_gqa_fp8(int dtype, int D, int nw, int ch, int pf, int wpe, const AttnArgs& a, unsigned grid,
+                                 hipStream_t stream) {
+    switch (dtype * 1000 + D) {
+    case DT_F16 * 1000 + 64: return launch_gqa_fp8_d<DT_F16, 64>(nw, ch, pf, wpe, a, grid, stream);
+    case DT_F16 * 1000 + 128: return launch_gqa_fp8_d<DT_F16, 128>(nw, ch, pf, wpe, a, grid, stream);
+    case DT_BF16 * 1000 + 64: return launch_gqa_fp8_d<DT_BF16, 64>(nw, ch, pf, wpe, a, grid, stream);
+    case DT_BF16 * 1000 + 128: return launch_gqa_fp8_d<DT_BF16, 128>(nw, ch, pf, wpe, a, grid, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+bool gqa_fp8_variant_exists(int nw, int ch, int pf, int wpe) {
+    switch (wpe * 1000 + nw * 100 + ch * 10 + pf) {
+#define PKV_CASE(NW_, CH_, PF_, W_) case W_ * 1000 + NW_ * 100 + CH_ * 10 + PF_:
+        PKV_GQA_FP8_VARIANTS(PKV_CASE)
+#undef PKV_CASE
+        return true;
+    default: return false;
+    }
+}
+
 }  // namespace pkv

@@ -61,6 +61,12 @@ hipError_t launch_kv_append_fp8(int src_dtype, int D, const AppendFp8Args& a, hi
 hipError_t launch_decode_fp8(int q_dtype, int D, int nw, int ch, int pf, bool append, const AttnArgs& a,
                              unsigned grid, hipStream_t stream);
 bool fp8_variant_exists(int nw, int ch, int pf);
+// grouped heads on MFMA over FP8 pools (no append inside; lengths from context_lens, or positions + 1 when
+// context_lens is NULL)
+// wpe: waves per SIMD the kernel's register allocation targets (2 or 3)
+hipError_t launch_decode_gqa_fp8(int q_dtype, int D, int nw, int ch, int pf, int wpe, const AttnArgs& a,
+                                 unsigned grid, hipStream_t stream);
+bool gqa_fp8_variant_exists(int nw, int ch, int pf, int wpe);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_decode_mha(int dtype, int D, int nw, int ch, int pf, bool append, const AttnArgs& a,
                              unsigned grid, hipStream_t stream);

@@ -119,14 +119,34 @@ def test_fp8_every_launch_variant(torch_dev, monkeypatch, variant):
     monkeypatch.setenv("PKV_FP8_NW", nw)
     monkeypatch.setenv("PKV_FP8_CH", ch)
     monkeypatch.setenv("PKV_FP8_PF", pf)
-    for dtype, D, P in (("bf16", 128, 0), ("f16", 64, 64)):
-        cfg = cfg_for(dtype, D, 4, 2, (1, 17, 200, 1000, 2049), P=P)
+    for dtype, D, P, G in (("bf16", 128, 0, 1), ("f16", 64, 64, 1), ("f32", 128, 0, 2)):
+        cfg = cfg_for(dtype, D, 4, 4 // G, (1, 17, 200, 1000, 2049), P=P)
         w = make_workload(cfg, 41)
         ref, _, _ = oracle.run_step(w)
         got, _ = run(torch_dev, w, P, True)
         launch = pkv.last_launch()
-        assert launch.startswith("fp8") and f"nw={nw} ch={ch} pf={pf}" in launch, launch
+        assert launch.startswith("fp8 ") and f"nw={nw} ch={ch} pf={pf}" in launch, launch
         assert_close(got, ref, dtype, f"variant {variant} {dtype} D{D} P{P}")
+
+
+@pytest.mark.parametrize("variant", ["2,1,1", "2,1,2", "4,1,1", "2,2,1", "4,2,1"])
+def test_fp8_grouped_every_launch_variant(torch_dev, monkeypatch, variant):
+    nw, ch, pf = variant.split(",")
+    monkeypatch.setenv("PKV_GQA8_NW", nw)
+    monkeypatch.setenv("PKV_GQA8_CH", ch)
+    monkeypatch.setenv("PKV_GQA8_PF", pf)
+    for dtype, D, P, H_q, H_kv, append in (("bf16", 128, 0, 8, 1, True), ("f16", 64, 64, 16, 2, True),
+                                           ("bf16", 128, 256, 12, 4, False)):
+        cfg = cfg_for(dtype, D, H_q, H_kv, (1, 17, 200, 1000, 2049), P=P, append=append)
+        w = make_workload(cfg, 43)
+        ref, pk, pv = oracle.run_step(w)
+        got, d = run(torch_dev, w, P, append)
+        launch = pkv.last_launch()
+        assert launch.startswith("gqa_mfma_fp8") and f"nw={nw} ch={ch} pf={pf}" in launch, launch
+        assert_close(got, ref, dtype, f"grouped variant {variant} {dtype} D{D} P{P}")
+        if append:
+            assert bits_equal(d["k_pool"].cpu().numpy(), pk[0]) and bits_equal(d["k_scale"].cpu().numpy(), pk[1])
+            assert bits_equal(d["v_pool"].cpu().numpy(), pv[0]) and bits_equal(d["v_scale"].cpu().numpy(), pv[1])
 
 
 def test_fp8_single_token_is_exact(torch_dev):
