@@ -380,6 +380,12 @@ int pkv_bm_batch_tables(const pkv_block_manager* bm, const int64_t* seq_ids, int
 int pkv_copy_blocks(int dtype, void* k_pool, void* v_pool, const int32_t* src, const int32_t* dst, int32_t n,
                     int32_t H_kv, int32_t D, int32_t block_size, int32_t n_blocks, void* stream);
 
+/* copy_blocks for an FP8 cache: the blocks' codes and their row scales (pools
+ * and scale arrays 16-byte aligned). */
+int pkv_copy_blocks_fp8(uint8_t* k_pool, uint8_t* v_pool, float* k_scale, float* v_scale, const int32_t* src,
+                        const int32_t* dst, int32_t n, int32_t H_kv, int32_t D, int32_t block_size, int32_t n_blocks,
+                        void* stream);
+
 /*
  * ---------------------------------------------------------------------------
  * Step graphs: the decode step captured once per (batch, context) bucket
@@ -404,6 +410,8 @@ int pkv_copy_blocks(int dtype, void* k_pool, void* v_pool, const int32_t* src, c
  *   block_tables rows b < B; copy pairs, unused entries -1 (skipped).
  * Buffers are sized for the largest capacities; workspace for the largest
  * bucket (pkv_decode_workspace_bytes(max Bc, H_q, D, max Cc, partition_size)).
+ * With k_scale / v_scale set the pools are an FP8 cache (uint8 codes, as in the
+ * FP8 calls above; dtype is then q's) and the graphs run the FP8 step.
  * The buffers must stay allocated, at the same addresses, for the object's
  * lifetime.  Capture happens in pkv_step_graphs_create on a stream of its own;
  * launch is asynchronous and allocation-free.  Not thread-safe per object.
@@ -428,6 +436,8 @@ typedef struct pkv_step_desc {
     const int32_t* cow_dst;                      /* [max Bc] or NULL                   */
     void* workspace;
     size_t workspace_bytes;
+    float* k_scale;                              /* FP8 pools: row scales (else NULL)  */
+    float* v_scale;
 } pkv_step_desc;
 
 typedef struct pkv_step_graphs pkv_step_graphs;
@@ -495,6 +505,8 @@ typedef struct pkv_decoder_desc {
     int32_t n_batch_caps;
     const int32_t* ctx_caps;
     int32_t n_ctx_caps;
+    float* k_scale;                              /* FP8 pools: row scales (else NULL); dtype is q's */
+    float* v_scale;
 } pkv_decoder_desc;
 
 typedef struct pkv_decoder pkv_decoder;

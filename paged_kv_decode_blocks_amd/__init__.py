@@ -29,7 +29,7 @@ __all__ = [
     "PkvError", "LIB_PATH", "load_library", "library_loaded", "kv_append", "paged_decode_attention",
     "append_decode_attention", "decode_workspace_bytes", "last_launch", "version", "probe_stream_read",
     "PKV_F32", "PKV_F16", "PKV_BF16", "EXPORTED_SYMBOLS", "copy_blocks", "BlockManager", "StepGraphs", "Decoder", "cu_mask", "CuMaskedStream",
-    "kv_append_fp8", "paged_decode_attention_fp8", "append_decode_attention_fp8",
+    "kv_append_fp8", "paged_decode_attention_fp8", "append_decode_attention_fp8", "copy_blocks_fp8",
     "device_cu_count",
     "PKV_ERR_OUT_OF_BLOCKS", "PKV_ERR_SEQUENCE",
 ]
@@ -44,7 +44,7 @@ BLOCK_SIZE = 16
 EXPORTED_SYMBOLS = (
     "pkv_version", "pkv_status_string", "pkv_last_error", "pkv_last_launch", "pkv_kv_append",
     "pkv_decode_workspace_bytes", "pkv_paged_decode_attention", "pkv_append_decode_attention",
-    "pkv_probe_stream_read", "pkv_copy_blocks", "pkv_kv_append_fp8", "pkv_paged_decode_attention_fp8",
+    "pkv_probe_stream_read", "pkv_copy_blocks", "pkv_copy_blocks_fp8", "pkv_kv_append_fp8", "pkv_paged_decode_attention_fp8",
     "pkv_append_decode_attention_fp8",
     "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add_sequence", "pkv_bm_add_sequence_shared", "pkv_bm_fork",
     "pkv_bm_append_token", "pkv_bm_append_batch", "pkv_bm_free_sequence", "pkv_bm_num_free_blocks",
@@ -67,7 +67,7 @@ class StepDesc(ctypes.Structure):
         ("new_row_stride", ctypes.c_int64), ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
         ("block_tables", ctypes.c_void_p), ("bt_stride", ctypes.c_int32), ("positions", ctypes.c_void_p),
         ("cow_src", ctypes.c_void_p), ("cow_dst", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
-        ("workspace_bytes", ctypes.c_size_t),
+        ("workspace_bytes", ctypes.c_size_t), ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
     ]
 
 
@@ -83,6 +83,7 @@ class DecoderDesc(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t), ("shuffle_seed", ctypes.c_uint64),
         ("batch_caps", ctypes.c_void_p), ("n_batch_caps", ctypes.c_int32),
         ("ctx_caps", ctypes.c_void_p), ("n_ctx_caps", ctypes.c_int32),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
     ]
 
 
@@ -136,6 +137,8 @@ def load_library(path: Optional[str] = None):
                                                     I32, I32, I32, I32, I32, I32, I32, ctypes.c_float, I32,
                                                     P, SZ, P]
     lib.pkv_append_decode_attention_fp8.restype = ctypes.c_int
+    lib.pkv_copy_blocks_fp8.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, P]
+    lib.pkv_copy_blocks_fp8.restype = ctypes.c_int
     lib.pkv_copy_blocks.argtypes = [ctypes.c_int, P, P, P, P, I32, I32, I32, I32, I32, P]
     lib.pkv_copy_blocks.restype = ctypes.c_int
     U64, C = ctypes.c_uint64, ctypes.c_int
@@ -507,15 +510,18 @@ class StepGraphs:
     """
 
     def __init__(self, q, k_new, v_new, k_pool, v_pool, block_tables, positions, out, scale: float,
-                 batch_caps, ctx_caps, *, partition_size: int = 0, cow_src=None, cow_dst=None, workspace=None):
+                 batch_caps, ctx_caps, *, partition_size: int = 0, cow_src=None, cow_dst=None, workspace=None,
+                 k_scale=None, v_scale=None):
         torch = _torch()
-        n_blocks, H_kv, bs, D = _pool_dims(k_pool, v_pool)
+        fp8 = k_scale is not None
+        n_blocks, H_kv, bs, D = (_fp8_pools(k_pool, v_pool, k_scale, v_scale) if fp8
+                                 else _pool_dims(k_pool, v_pool))
         Bmax, H_q = q.shape[0], q.shape[1]
         bcaps = [int(x) for x in batch_caps]
         ccaps = [int(x) for x in ctx_caps]
         _require(bcaps and ccaps and bcaps[-1] <= Bmax, "batch capacities must fit the buffers' rows")
         for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new")):
-            _require(t.dtype == k_pool.dtype, f"{nm} dtype must match the pools")
+            _require(t.dtype == (q.dtype if fp8 else k_pool.dtype), f"{nm} dtype must match the pools (q's for FP8)")
         qrs = _rows(q, "q", H_q, D)
         nrs = _rows(k_new, "k_new", H_kv, D)
         _require(_rows(v_new, "v_new", H_kv, D) == nrs, "k_new and v_new must share a row stride")
@@ -534,7 +540,8 @@ class StepGraphs:
         need = decode_workspace_bytes(bcaps[-1], H_q, D, ccaps[-1], partition_size) if partition_size else 0
         if need and workspace is None:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-        self._keep = (q, k_new, v_new, k_pool, v_pool, block_tables, positions, out, cow_src, cow_dst, workspace)
+        self._keep = (q, k_new, v_new, k_pool, v_pool, block_tables, positions, out, cow_src, cow_dst, workspace,
+                      k_scale, v_scale)
         d = StepDesc()
         d.dtype, d.H_q, d.H_kv, d.D, d.block_size, d.n_blocks = _dtype_code(q), H_q, H_kv, D, bs, n_blocks
         d.scale, d.partition_size = float(scale), int(partition_size)
@@ -546,6 +553,8 @@ class StepGraphs:
         d.cow_dst = cow_dst.data_ptr() if cow_dst is not None else None
         d.workspace = workspace.data_ptr() if workspace is not None else None
         d.workspace_bytes = workspace.numel() if workspace is not None else 0
+        d.k_scale = k_scale.data_ptr() if fp8 else None
+        d.v_scale = v_scale.data_ptr() if fp8 else None
         self._desc = d
         lib = load_library()
         bc = (ctypes.c_int32 * len(bcaps))(*bcaps)
@@ -581,12 +590,16 @@ class Decoder:
     """
 
     def __init__(self, q, k_new, v_new, k_pool, v_pool, out, scale: float, bt_stride: int, *,
-                 partition_size: int = 0, workspace=None, shuffle_seed: int = 0, batch_caps=None, ctx_caps=None):
+                 partition_size: int = 0, workspace=None, shuffle_seed: int = 0, batch_caps=None, ctx_caps=None,
+                 k_scale=None, v_scale=None):
         torch = _torch()
-        n_blocks, H_kv, bs, D = _pool_dims(k_pool, v_pool)
+        fp8 = k_scale is not None
+        n_blocks, H_kv, bs, D = (_fp8_pools(k_pool, v_pool, k_scale, v_scale) if fp8
+                                 else _pool_dims(k_pool, v_pool))
         max_batch, H_q = q.shape[0], q.shape[1]
         for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new")):
-            _require(t.dtype == k_pool.dtype and t.shape[0] == max_batch, f"{nm}: pool dtype, max_batch rows")
+            _require(t.dtype == (q.dtype if fp8 else k_pool.dtype) and t.shape[0] == max_batch,
+                     f"{nm}: pool dtype (q's for FP8), max_batch rows")
         qrs = _rows(q, "q", H_q, D)
         nrs = _rows(k_new, "k_new", H_kv, D)
         _require(_rows(v_new, "v_new", H_kv, D) == nrs, "k_new and v_new must share a row stride")
@@ -595,7 +608,7 @@ class Decoder:
         if partition_size and workspace is None:
             need = decode_workspace_bytes(max_batch, H_q, D, bt_stride * bs, partition_size)
             workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-        self._keep = (q, k_new, v_new, k_pool, v_pool, out, workspace)
+        self._keep = (q, k_new, v_new, k_pool, v_pool, out, workspace, k_scale, v_scale)
         d = DecoderDesc()
         d.dtype, d.H_q, d.H_kv, d.D, d.block_size, d.n_blocks = _dtype_code(q), H_q, H_kv, D, bs, n_blocks
         d.scale, d.partition_size, d.max_batch, d.bt_stride = float(scale), int(partition_size), max_batch, bt_stride
@@ -605,6 +618,8 @@ class Decoder:
         d.workspace = workspace.data_ptr() if workspace is not None else None
         d.workspace_bytes = workspace.numel() if workspace is not None else 0
         d.shuffle_seed = int(shuffle_seed) & ((1 << 64) - 1)
+        d.k_scale = k_scale.data_ptr() if fp8 else None
+        d.v_scale = v_scale.data_ptr() if fp8 else None
         self._caps = None
         if batch_caps is not None:
             bc = (ctypes.c_int32 * len(batch_caps))(*[int(x) for x in batch_caps])
@@ -768,3 +783,16 @@ def append_decode_attention_fp8(q, k_new, v_new, k_pool, v_pool, k_scale, v_scal
         int(max_context_len), float(scale), int(partition_size), _ptr(ws), ws_bytes, _stream(stream))
     _check(rc, "append_decode_attention_fp8")
     return out
+
+
+def copy_blocks_fp8(k_pool, v_pool, k_scale, v_scale, src, dst, *, stream=None):
+    """copy_blocks for an FP8 cache: codes and row scales of blocks src[i] -> dst[i]."""
+    torch = _torch()
+    n_blocks, H_kv, bs, D = _fp8_pools(k_pool, v_pool, k_scale, v_scale)
+    n = src.shape[0]
+    for t, nm in ((src, "src"), (dst, "dst")):
+        _require(t.dtype == torch.int32 and t.dim() == 1 and t.shape[0] == n and (n <= 1 or t.stride(0) == 1),
+                 f"{nm} must be contiguous int32 [n]")
+    rc = load_library().pkv_copy_blocks_fp8(_ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(src),
+                                            _ptr(dst), n, H_kv, D, bs, n_blocks, _stream(stream))
+    _check(rc, "copy_blocks_fp8")

@@ -246,3 +246,25 @@ def test_copy_blocks_bit_exact(torch_dev, dtype, H_kv, D):
     oracle_copy_blocks(kp, vp, pairs)
     assert bits_equal(to_numpy_bits(k, dtype), kp)
     assert bits_equal(to_numpy_bits(v, dtype), vp)
+
+
+@pytest.mark.parametrize("H_kv,D", [(8, 128), (2, 64)])
+def test_copy_blocks_fp8_bit_exact(torch_dev, H_kv, D):
+    t = torch_dev
+    rng = np.random.default_rng(9)
+    n_blocks = 30
+    kp = rng.integers(0, 256, (n_blocks, H_kv, BS, D), dtype=np.uint8)
+    vp = rng.integers(0, 256, (n_blocks, H_kv, BS, D), dtype=np.uint8)
+    ks = rng.standard_normal((n_blocks, H_kv, BS)).astype(np.float32)
+    vs = rng.standard_normal((n_blocks, H_kv, BS)).astype(np.float32)
+    perm = rng.permutation(n_blocks)
+    src, dst = perm[:9].astype(np.int32), perm[9:18].astype(np.int32)
+    src[2] = -1
+    dev = [t.from_numpy(a.copy()).cuda() for a in (kp, vp, ks, vs)]
+    pkv.copy_blocks_fp8(*dev, t.from_numpy(src).cuda(), t.from_numpy(dst).cuda())
+    t.cuda.synchronize()
+    pairs = [(int(a), int(b)) for a, b in zip(src, dst) if a >= 0]
+    oracle_copy_blocks(kp, vp, pairs)
+    oracle_copy_blocks(ks, vs, pairs)
+    for d, r in zip(dev, (kp, vp, ks, vs)):
+        assert bits_equal(d.cpu().numpy(), r)

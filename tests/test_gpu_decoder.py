@@ -26,27 +26,38 @@ def torch_dev():
     return torch
 
 
-@pytest.mark.parametrize("dtype,H_q,H_kv,D,P,graphs,seed", [
-    ("f16", 8, 2, 128, 32, True, 301),
-    ("bf16", 8, 8, 128, 0, True, 302),
-    ("f32", 4, 4, 64, 0, False, 303),
-    ("bf16", 16, 2, 128, 64, False, 304),
+@pytest.mark.parametrize("dtype,H_q,H_kv,D,P,graphs,seed,fp8", [
+    ("f16", 8, 2, 128, 32, True, 301, False),
+    ("bf16", 8, 8, 128, 0, True, 302, False),
+    ("f32", 4, 4, 64, 0, False, 303, False),
+    ("bf16", 16, 2, 128, 64, False, 304, False),
+    ("bf16", 8, 2, 128, 32, False, 305, True),
+    ("f16", 4, 4, 64, 0, True, 306, True),
 ])
-def test_decoder_matches_oracle(torch_dev, dtype, H_q, H_kv, D, P, graphs, seed):
+def test_decoder_matches_oracle(torch_dev, dtype, H_q, H_kv, D, P, graphs, seed, fp8):
     t = torch_dev
-    print(f"decoder {dtype} H_q={H_q} H_kv={H_kv} D={D} P={P} graphs={graphs} seed={seed}", flush=True)
+    print(f"decoder {dtype} H_q={H_q} H_kv={H_kv} D={D} P={P} graphs={graphs} seed={seed} fp8={fp8}", flush=True)
     rng = np.random.default_rng(seed)
     Bmax, W, n_blocks = 8, 12, 120
     scale = 1.0 / math.sqrt(D)
-    kp = poisoned_pool(dtype, n_blocks, H_kv, D)
+    tdt = {"f32": t.float32, "f16": t.float16, "bf16": t.bfloat16}[dtype]
+    if fp8:
+        kp = np.full((n_blocks, H_kv, BS, D), 0x7F, np.uint8)
+        ksc = np.full((n_blocks, H_kv, BS), np.nan, np.float32)
+        vsc = ksc.copy()
+        k, v = t.from_numpy(kp.copy()).cuda(), t.from_numpy(kp.copy()).cuda()
+        ks_d, vs_d = t.from_numpy(ksc.copy()).cuda(), t.from_numpy(vsc.copy()).cuda()
+    else:
+        kp = poisoned_pool(dtype, n_blocks, H_kv, D)
+        k, v = to_tensor(kp, dtype, "cuda"), to_tensor(kp, dtype, "cuda")
     vp = kp.copy()
-    k, v = to_tensor(kp, dtype, "cuda"), to_tensor(vp, dtype, "cuda")
-    tdt = k.dtype
     q_buf = t.zeros((Bmax, H_q, D), dtype=tdt, device="cuda")
     kn_buf = t.zeros((Bmax, H_kv, D), dtype=tdt, device="cuda")
     vn_buf = t.zeros((Bmax, H_kv, D), dtype=tdt, device="cuda")
     out_buf = t.zeros((Bmax, H_q, D), dtype=t.float32, device="cuda")
     caps = dict(batch_caps=[2, 4, 8], ctx_caps=[64, 128, W * BS]) if graphs else {}
+    if fp8:
+        caps.update(k_scale=ks_d, v_scale=vs_d)
     dec = pkv.Decoder(q_buf, kn_buf, vn_buf, k, v, out_buf, scale, W, partition_size=P, shuffle_seed=seed, **caps)
     bm, ora = dec.block_manager, OracleBM(n_blocks, BS, seed)
     live, next_id = [], [0]
@@ -60,9 +71,14 @@ def test_decoder_matches_oracle(torch_dev, dtype, H_q, H_kv, D, P, graphs, seed)
         bt = np.full((n, W), -1, dtype=np.int32)
         bt[:, :table.size] = table
         pos = np.arange(n, dtype=np.int32)
-        oracle.kv_append(dtype, kn, vn, kp, vp, bt, pos, BS)
-        pkv.kv_append(to_tensor(kn, dtype, "cuda"), to_tensor(vn, dtype, "cuda"), k, v,
-                      t.from_numpy(bt).cuda(), t.from_numpy(pos).cuda())
+        if fp8:
+            oracle.kv_append_fp8(dtype, kn, vn, kp, vp, ksc, vsc, bt, pos, BS)
+            pkv.kv_append_fp8(to_tensor(kn, dtype, "cuda"), to_tensor(vn, dtype, "cuda"), k, v, ks_d, vs_d,
+                              t.from_numpy(bt).cuda(), t.from_numpy(pos).cuda())
+        else:
+            oracle.kv_append(dtype, kn, vn, kp, vp, bt, pos, BS)
+            pkv.kv_append(to_tensor(kn, dtype, "cuda"), to_tensor(vn, dtype, "cuda"), k, v,
+                          t.from_numpy(bt).cuda(), t.from_numpy(pos).cuda())
 
     atol, rtol = TOL[dtype]
     total_copies = 0
@@ -100,8 +116,13 @@ def test_decoder_matches_oracle(torch_dev, dtype, H_q, H_kv, D, P, graphs, seed)
         oracle_copy_blocks(kp, vp, copies)
         tables = np.asarray(tables, dtype=np.int32)
         positions = np.asarray(positions, dtype=np.int32)
-        oracle.kv_append(dtype, kn, vn, kp, vp, tables, positions, BS)
-        ref = oracle.paged_decode_attention(dtype, q, kp, vp, tables, positions + 1, scale)
+        if fp8:
+            oracle_copy_blocks(ksc, vsc, copies)
+            oracle.kv_append_fp8(dtype, kn, vn, kp, vp, ksc, vsc, tables, positions, BS)
+            ref = oracle.paged_decode_attention_fp8(dtype, q, kp, vp, ksc, vsc, tables, positions + 1, scale)
+        else:
+            oracle.kv_append(dtype, kn, vn, kp, vp, tables, positions, BS)
+            ref = oracle.paged_decode_attention(dtype, q, kp, vp, tables, positions + 1, scale)
         t.cuda.synchronize()
         got = out_buf[:B].cpu().numpy().astype(np.float64)
         assert np.all(np.isfinite(got)), step
@@ -111,7 +132,11 @@ def test_decoder_matches_oracle(torch_dev, dtype, H_q, H_kv, D, P, graphs, seed)
         for sid in ids:
             assert list(bm.block_table(sid)) == ora.block_table(sid)
     assert total_copies > 0, "the stream never exercised copy-on-write"
-    assert bits_equal(to_numpy_bits(k, dtype), kp) and bits_equal(to_numpy_bits(v, dtype), vp)
+    if fp8:
+        assert bits_equal(k.cpu().numpy(), kp) and bits_equal(v.cpu().numpy(), vp)
+        assert bits_equal(ks_d.cpu().numpy(), ksc) and bits_equal(vs_d.cpu().numpy(), vsc)
+    else:
+        assert bits_equal(to_numpy_bits(k, dtype), kp) and bits_equal(to_numpy_bits(v, dtype), vp)
 
     # errors leave the manager as it was and launch nothing
     before = [(s, bm.sequence_length(s)) for s in live]
