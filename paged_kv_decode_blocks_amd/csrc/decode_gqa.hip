@@ -742,15 +742,25 @@ bool gqa_variant_exists(int kind, int nw, int ch, int pf) {
 // ---------------------------------------------------------------------------
 // Kernel 3: grouped heads over an FP8 (OCP E4M3) K/V cache.
 //
-// The same MFMA tiles in q's type (f16 or bf16): each lane loads its K piece
-// as 8 one-byte codes and its V piece as D/16 codes and widens them with
+// The same MFMA tiles in q's type (f16 or bf16), with the codes widened by
 // v_cvt_scalef32_pk_{bf16,f16}_fp8 at scale 1 (every E4M3 value is exact in
-// both types), so the product sees code values.  The row scales (one power of
+// both types), so the products see code values.  The row scales (one power of
 // two per token row and KV head) enter where the tokens are separate: the
 // score of token t is multiplied by k_scale[t] before the softmax, and its
-// weight by v_scale[t] before the P V product -- exact multiplications.  A lane
-// holds scores and V rows of the same four tokens per block (4 i + j), so it
-// loads those four scales of each pool.
+// weight by v_scale[t] before the P V product -- exact multiplications.
+//
+// Layout differences from the 16-bit kernels, all to cut load instructions per
+// block (a code block is half as many bytes, so the per-block instruction and
+// latency cost, not the bytes, sets the rate):
+//  * tile row r is token r of the block, so the lane holding head `col` in
+//    lane group j gets the scores of tokens 4 j .. 4 j + 3; its V rows and its
+//    eight scales are those four tokens (one 16-byte load per scale pool);
+//  * the head dimension is renumbered inside each 64-wide slice: MFMA step
+//    2 u + e, k slot kk of lane group j is d = 64 u + 16 j + 8 e + kk, applied to
+//    q and K alike (the dot product does not depend on the order of d), so one
+//    16-byte K load feeds two steps;
+//  * loads of the chunk PF ahead are issued before the current chunk's
+//    arithmetic, and a lane's offsets are 32-bit from a per-block scalar base.
 //
 // Lengths are context_lens[b], or positions[b] + 1 when context_lens is NULL:
 // the fused FP8 step appends with the quantizing append kernel first and then
@@ -771,67 +781,91 @@ __device__ __forceinline__ uint32_t ld4(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
 }
 
+// One block's loads for one lane.
+template <int D>
+struct F8Codes {
+    static constexpr int KL = D / 64;   // 16-byte K loads (two MFMA steps each)
+    static constexpr int VW = D / 64;   // 32-bit words of V codes per row piece
+    uint4 k[KL];
+    uint32_t v[4][VW];
+    float4 ks, vs;                      // scales of tokens 4 j .. 4 j + 3
+};
+
 template <int DT, int D>
 struct GqaLaneF8 : GqaLane<DT, D, false> {
     using Base = GqaLane<DT, D, false>;
-    static constexpr int KS = Base::KS, VT = Base::VT, NWORD = Base::NWORD;
-    static constexpr int VW = NWORD / 2 > 0 ? NWORD / 2 : 1;   // 32-bit words of V codes per row piece
-    int koff8[KS];     // byte offset of this lane's 8 K codes of step s inside a (block, head) tile
-    int voff8[4];      // byte offset of this lane's VT V codes of row-load i inside a tile
-    int soff[4];       // row (within the block) of this lane's token 4 i + j
+    using Codes = F8Codes<D>;
+    static constexpr int KS = Base::KS, VT = Base::VT, NWORD = Base::NWORD, ES = Base::ES;
+    static constexpr int KL = Codes::KL, VW = Codes::VW;
+    uint32_t kofs;   // byte offset of this lane's first K piece in a (block, head) tile
+    uint32_t vofs;   // byte offset of this lane's V piece of token 4 j
+    uint32_t sofs;   // byte offset of this lane's four scales in a (block, head) scale row
 
     __device__ __forceinline__ void init8(const AttnArgs& a, int lane, int b, int g) {
-        Base::init(a, lane, b, g);
+        this->j = lane >> 4;
+        this->col = lane & 15;
+        this->tau = this->col;
+        this->scale_log2 = a.scale_log2;
+        const int j = this->j, col = this->col;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) koff8[s] = this->tau * D + 32 * s + 8 * this->j;
+        for (int u = 0; u < KL; ++u)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            voff8[i] = (4 * i + this->j) * D + this->col * VT;
-            soff[i] = 4 * i + this->j;
-        }
+            for (int e = 0; e < 2; ++e) {
+                this->qf[2 * u + e] = make_uint4(0, 0, 0, 0);
+                if (col < a.G)
+                    this->qf[2 * u + e] = ld16_cached(
+                        a.q + ((int64_t)b * a.q_row_stride + (int64_t)(g * a.G + col) * D + 64 * u + 16 * j + 8 * e) * ES);
+            }
+        kofs = (uint32_t)(col * D + 16 * j);
+        vofs = (uint32_t)(4 * j * D + col * VT);
+        sofs = (uint32_t)(16 * j);
+#pragma unroll
+        for (int t = 0; t < VT; ++t) this->acc[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        this->m = kNegBig;
+        this->l = 0.0f;
     }
 
     __device__ __forceinline__ void load_v(const uint8_t* vb, int i, uint32_t (&vc)[VW]) const {
-        if constexpr (VT == 8) {
-            const uint2 v = ld8(vb + voff8[i]);
+        if constexpr (VW == 2) {
+            const uint2 v = ld8(vb + vofs + i * D);
             vc[0] = v.x;
             vc[1] = v.y;
         } else {
-            vc[0] = ld4(vb + voff8[i]);
+            vc[0] = ld4(vb + vofs + i * D);
         }
     }
 
-    // loads of one whole block: K codes (8 per step), V codes (VT per row), the four scales of each pool
-    __device__ __forceinline__ void load(const uint8_t* kb, const uint8_t* vb, const float* ksb, const float* vsb,
-                                         uint2 (&kc)[KS], uint32_t (&vc)[4][VW], float (&ks)[4], float (&vs)[4]) const {
+    // kb, vb: the (block, head) code tiles; ksb, vsb: its scale rows
+    __device__ __forceinline__ void load(const uint8_t* kb, const uint8_t* vb, const uint8_t* ksb, const uint8_t* vsb,
+                                         Codes& c) const {
 #pragma unroll
-        for (int s = 0; s < KS; ++s) kc[s] = ld8(kb + koff8[s]);
+        for (int u = 0; u < KL; ++u) c.k[u] = ld16(kb + kofs + 64 * u);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) load_v(vb, i, vc[i]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            ks[i] = ksb[soff[i]];
-            vs[i] = vsb[soff[i]];
-        }
+        for (int i = 0; i < 4; ++i) load_v(vb, i, c.v[i]);
+        c.ks = *reinterpret_cast<const float4*>(ksb + sofs);
+        c.vs = *reinterpret_cast<const float4*>(vsb + sofs);
     }
 
     // Online-softmax update with CH blocks of codes.
     template <int CH>
-    __device__ __forceinline__ void accumulate8(const uint2 (&kc)[CH][KS], const uint32_t (&vc)[CH][4][VW],
-                                                const float (&ks)[CH][4], const float (&vs)[CH][4],
-                                                const bool (&valid)[CH][4]) {
+    __device__ __forceinline__ void accumulate8(const Codes (&c)[CH], const bool (&valid)[CH][4]) {
         float sc[CH][4];
 #pragma unroll
         for (int cb = 0; cb < CH; ++cb) {
             floatx4 st = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const uint4 kw = make_uint4(fp8x2_widen<DT>(kc[cb][s].x, false), fp8x2_widen<DT>(kc[cb][s].x, true),
-                                            fp8x2_widen<DT>(kc[cb][s].y, false), fp8x2_widen<DT>(kc[cb][s].y, true));
-                st = Mfma<DT>::mma(kw, this->qf[s], st);
+            for (int u = 0; u < KL; ++u) {
+                const uint4 kw = c[cb].k[u];
+                const uint4 k0 = make_uint4(fp8x2_widen<DT>(kw.x, false), fp8x2_widen<DT>(kw.x, true),
+                                            fp8x2_widen<DT>(kw.y, false), fp8x2_widen<DT>(kw.y, true));
+                const uint4 k1 = make_uint4(fp8x2_widen<DT>(kw.z, false), fp8x2_widen<DT>(kw.z, true),
+                                            fp8x2_widen<DT>(kw.w, false), fp8x2_widen<DT>(kw.w, true));
+                st = Mfma<DT>::mma(k0, this->qf[2 * u], st);
+                st = Mfma<DT>::mma(k1, this->qf[2 * u + 1], st);
             }
+            const float ks[4] = {c[cb].ks.x, c[cb].ks.y, c[cb].ks.z, c[cb].ks.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sc[cb][i] = mul_rn(st[i] * ks[cb][i], this->scale_log2);
+            for (int i = 0; i < 4; ++i) sc[cb][i] = mul_rn(st[i] * ks[i], this->scale_log2);
         }
         float mloc = kNegBig;
 #pragma unroll
@@ -850,12 +884,13 @@ struct GqaLaneF8 : GqaLane<DT, D, false> {
         }
 #pragma unroll
         for (int cb = 0; cb < CH; ++cb) {
+            const float vs[4] = {c[cb].vs.x, c[cb].vs.y, c[cb].vs.z, c[cb].vs.w};
             float p[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float e = valid[cb][i] ? __builtin_amdgcn_exp2f(sc[cb][i] - this->m) : 0.0f;
                 this->l += e;
-                p[i] = e * vs[cb][i];
+                p[i] = e * vs[i];
             }
             uint4 pk;
             Mfma<DT>::split(p[0], p[1], pk.x, pk.z);
@@ -865,7 +900,7 @@ struct GqaLaneF8 : GqaLane<DT, D, false> {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int x = 0; x < NWORD; ++x) vw[i][x] = fp8x2_widen<DT>(vc[cb][i][x >> 1], (x & 1) != 0);
+                for (int x = 0; x < NWORD; ++x) vw[i][x] = fp8x2_widen<DT>(c[cb].v[i][x >> 1], (x & 1) != 0);
 #pragma unroll
             for (int t = 0; t < VT; ++t) {
                 const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
@@ -877,40 +912,44 @@ struct GqaLaneF8 : GqaLane<DT, D, false> {
         }
     }
 
-    // One block not wholly below `lim`: masked loads.
-    __device__ __forceinline__ void partial_block8(const uint8_t* kb, const uint8_t* vb, const float* ksb,
-                                                   const float* vsb, int tb, int lim) {
-        uint2 kc[1][KS];
-        uint32_t vc[1][4][VW];
-        float ks[1][4], vs[1][4];
+    // One block not wholly below `lim`: masked loads; the scales of tokens at or
+    // past `lim` are taken as zero (their slots may hold anything).
+    __device__ __forceinline__ void partial_block8(const uint8_t* kb, const uint8_t* vb, const uint8_t* ksb,
+                                                   const uint8_t* vsb, int tb, int lim) {
+        Codes c[1];
         bool valid[1][4];
-        const int tk = tb + this->tau;
+        const int tk = tb + this->col;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) kc[0][s] = tk < lim ? ld8(kb + koff8[s]) : make_uint2(0, 0);
+        for (int u = 0; u < KL; ++u) c[0].k[u] = tk < lim ? ld16(kb + kofs + 64 * u) : make_uint4(0, 0, 0, 0);
+        const int t0 = tb + 4 * this->j;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int tv = tb + soff[i];
-            valid[0][i] = tv < lim;
+            valid[0][i] = t0 + i < lim;
 #pragma unroll
-            for (int x = 0; x < VW; ++x) vc[0][i][x] = 0;
-            ks[0][i] = 0.0f;
-            vs[0][i] = 0.0f;
-            if (tv < lim) {
-                load_v(vb, i, vc[0][i]);
-                ks[0][i] = ksb[soff[i]];
-                vs[0][i] = vsb[soff[i]];
-            }
+            for (int x = 0; x < VW; ++x) c[0].v[i][x] = 0;
+            if (valid[0][i]) load_v(vb, i, c[0].v[i]);
         }
-        accumulate8<1>(kc, vc, ks, vs, valid);
+        float4 ks = make_float4(0.0f, 0.0f, 0.0f, 0.0f), vs = ks;
+        if (t0 < lim) {
+            ks = *reinterpret_cast<const float4*>(ksb + sofs);
+            vs = *reinterpret_cast<const float4*>(vsb + sofs);
+        }
+        c[0].ks = make_float4(valid[0][0] ? ks.x : 0.0f, valid[0][1] ? ks.y : 0.0f, valid[0][2] ? ks.z : 0.0f,
+                              valid[0][3] ? ks.w : 0.0f);
+        c[0].vs = make_float4(valid[0][0] ? vs.x : 0.0f, valid[0][1] ? vs.y : 0.0f, valid[0][2] ? vs.z : 0.0f,
+                              valid[0][3] ? vs.w : 0.0f);
+        accumulate8<1>(c, valid);
     }
 };
 
 // WPE: waves per SIMD the register allocation must leave room for (2 = as many
-// registers as the code wants; 3 trades a few spills for occupancy)
+// registers as the code wants; 3 trades a few spills for occupancy).  PF: chunks
+// whose loads are in flight while a chunk is being computed.
 template <int DT, int D, int NW, int CH, int PF, int WPE>
 __global__ __launch_bounds__(NW * 64, WPE) void decode_gqa_fp8_kernel(const AttnArgs a) {
     using L = GqaLaneF8<DT, D>;
-    constexpr int KS = L::KS, VW = L::VW;
+    using Codes = typename L::Codes;
+    constexpr int R = PF + 1;   // chunk buffers
     __shared__ int32_t s_ids[kWindowBlocksG];
     __shared__ int s_bad;
     __shared__ float s_m[NW][16];
@@ -947,19 +986,19 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_gqa_fp8_kernel(const Attn
     const int nblk = (u.end - u.start + kBlockSize - 1) / kBlockSize;
     const size_t blk_codes = (size_t)a.H_kv * kBlockSize * D;
     const size_t head_codes = (size_t)u.g * kBlockSize * D;
-    const size_t blk_rows = (size_t)a.H_kv * kBlockSize;
-    const size_t head_rows = (size_t)u.g * kBlockSize;
-    const uint8_t* kpool = reinterpret_cast<const uint8_t*>(a.k_pool);
-    const uint8_t* vpool = reinterpret_cast<const uint8_t*>(a.v_pool);
+    const size_t blk_sbytes = (size_t)a.H_kv * kBlockSize * 4;
+    const size_t head_sbytes = (size_t)u.g * kBlockSize * 4;
+    const uint8_t* kpool = reinterpret_cast<const uint8_t*>(a.k_pool) + head_codes;
+    const uint8_t* vpool = reinterpret_cast<const uint8_t*>(a.v_pool) + head_codes;
+    const uint8_t* kspool = reinterpret_cast<const uint8_t*>(a.k_scale) + head_sbytes;
+    const uint8_t* vspool = reinterpret_cast<const uint8_t*>(a.v_scale) + head_sbytes;
 
-    auto load_full = [&](uint2 (&kc)[CH][KS], uint32_t (&vc)[CH][4][VW], float (&ks)[CH][4], float (&vs)[CH][4],
-                         int cb0) {
+    auto load_chunk = [&](Codes (&c)[CH], int cb0) {
 #pragma unroll
         for (int cb = 0; cb < CH; ++cb) {
-            const int id = __builtin_amdgcn_readfirstlane(s_ids[cb0 + cb]);
-            st.load(kpool + (size_t)id * blk_codes + head_codes, vpool + (size_t)id * blk_codes + head_codes,
-                    a.k_scale + (size_t)id * blk_rows + head_rows, a.v_scale + (size_t)id * blk_rows + head_rows,
-                    kc[cb], vc[cb], ks[cb], vs[cb]);
+            const size_t id = (size_t)__builtin_amdgcn_readfirstlane(s_ids[cb0 + cb]);
+            st.load(kpool + id * blk_codes, vpool + id * blk_codes, kspool + id * blk_sbytes, vspool + id * blk_sbytes,
+                    c[cb]);
         }
     };
     bool all_valid[CH][4];
@@ -977,46 +1016,37 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_gqa_fp8_kernel(const Attn
         const int nch = (nr + CH - 1) / CH;
         const int tok_r = u.start + r0 * kBlockSize;
         const int nfull_all = max(0, min(nch, (u.lim - tok_r) / (CH * kBlockSize)));
-        const int nf = w < nfull_all ? (nfull_all - w + NW - 1) / NW : 0;
-        uint2 bk[PF][CH][KS];
-        uint32_t bv[PF][CH][4][VW];
-        float bks[PF][CH][4], bvs[PF][CH][4];
+        const int nf = w < nfull_all ? (nfull_all - w + NW - 1) / NW : 0;   // this wave's full chunks
         auto chunk_of = [&](int i) { return (w + NW * i) * CH; };
-        if (nf >= PF) {
+        // chunk i lives in buf[i % R]; the loads of chunk i + PF go out before chunk i is used
+        Codes buf[R][CH];
 #pragma unroll
-            for (int v = 0; v < PF; ++v) load_full(bk[v], bv[v], bks[v], bvs[v], chunk_of(v));
-            int i = 0;
-            for (; i + 2 * PF <= nf; i += PF) {
+        for (int v = 0; v < PF; ++v)
+            if (v < nf) load_chunk(buf[v], chunk_of(v));
+        int i = 0;
+        for (; i + R + PF <= nf; i += R) {   // steady state: every load in range
 #pragma unroll
-                for (int v = 0; v < PF; ++v) {
-                    st.template accumulate8<CH>(bk[v], bv[v], bks[v], bvs[v], all_valid);
-                    load_full(bk[v], bv[v], bks[v], bvs[v], chunk_of(i + PF + v));
+            for (int v = 0; v < R; ++v) {
+                load_chunk(buf[(v + PF) % R], chunk_of(i + v + PF));
+                st.template accumulate8<CH>(buf[v], all_valid);
+            }
+        }
+        for (; i < nf; i += R) {   // at most two rounds left
+#pragma unroll
+            for (int v = 0; v < R; ++v) {
+                if (i + v < nf) {
+                    if (i + v + PF < nf) load_chunk(buf[(v + PF) % R], chunk_of(i + v + PF));
+                    st.template accumulate8<CH>(buf[v], all_valid);
                 }
-            }
-            const int rem = nf - i - PF;
-#pragma unroll
-            for (int v = 0; v < PF; ++v) {
-                st.template accumulate8<CH>(bk[v], bv[v], bks[v], bvs[v], all_valid);
-                if (v < rem) load_full(bk[v], bv[v], bks[v], bvs[v], chunk_of(i + PF + v));
-            }
-#pragma unroll
-            for (int v = 0; v < PF; ++v)
-                if (v < rem) st.template accumulate8<CH>(bk[v], bv[v], bks[v], bvs[v], all_valid);
-        } else {
-            for (int i = 0; i < nf; ++i) {
-                load_full(bk[0], bv[0], bks[0], bvs[0], chunk_of(i));
-                st.template accumulate8<CH>(bk[0], bv[0], bks[0], bvs[0], all_valid);
             }
         }
         for (int k = nfull_all + ((w - nfull_all) % NW + NW) % NW; k < nch; k += NW) {
 #pragma unroll
             for (int cb = 0; cb < CH; ++cb) {
                 const int blk = k * CH + cb;
-                const int id = __builtin_amdgcn_readfirstlane(blk < nr ? s_ids[blk] : 0);
-                st.partial_block8(kpool + (size_t)id * blk_codes + head_codes,
-                                  vpool + (size_t)id * blk_codes + head_codes,
-                                  a.k_scale + (size_t)id * blk_rows + head_rows,
-                                  a.v_scale + (size_t)id * blk_rows + head_rows, tok_r + blk * kBlockSize, u.lim);
+                const size_t id = (size_t)__builtin_amdgcn_readfirstlane(blk < nr ? s_ids[blk] : 0);
+                st.partial_block8(kpool + id * blk_codes, vpool + id * blk_codes, kspool + id * blk_sbytes,
+                                  vspool + id * blk_sbytes, tok_r + blk * kBlockSize, u.lim);
             }
         }
     }
@@ -1024,7 +1054,8 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_gqa_fp8_kernel(const Attn
 }
 
 #define PKV_GQA_FP8_VARIANTS(X) \
-    X(2, 1, 1, 2) X(2, 1, 2, 2) X(4, 1, 1, 2) X(2, 2, 1, 2) X(4, 2, 1, 2) X(2, 1, 1, 3) X(4, 1, 1, 3)
+    X(2, 1, 1, 2) X(2, 1, 2, 2) X(4, 1, 1, 2) X(2, 2, 1, 2) X(4, 2, 1, 2) X(2, 1, 1, 3) X(4, 1, 1, 3) \
+    X(2, 1, 2, 3) X(4, 1, 2, 3) X(2, 1, 3, 2)
 
 template <int DT, int D>
 static hipError_t launch_gqa_fp8_d(int nw, int ch, int pf, int wpe, const AttnArgs& a, unsigned grid,
