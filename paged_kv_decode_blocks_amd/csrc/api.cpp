@@ -66,6 +66,7 @@ struct Plan {
     int kind;         // grouped path: 0 = loads through registers, 1 = through an LDS ring
     int nw, ch, pf;   // waves per workgroup, blocks per chunk, chunks (or ring slots) in flight per wave
     int wpe;          // grouped FP8 kernel: waves per SIMD its registers are sized for
+    int kd;           // grouped FP8 kernel: K tiles staged through LDS (1) or loaded into registers (0)
     unsigned grid;
     size_t ws_o, ws_lse, ws_total;
 };
@@ -97,7 +98,10 @@ Plan make_plan(int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32
         p.ch = env_int("PKV_GQA8_CH", 1);
         p.pf = env_int("PKV_GQA8_PF", 1);
         p.wpe = env_int("PKV_GQA8_WPE", 2);
-        if (!pkv::gqa_fp8_variant_exists(p.nw, p.ch, p.pf, p.wpe)) { p.nw = 2; p.ch = 1; p.pf = 1; p.wpe = 2; }
+        p.kd = env_int("PKV_GQA8_KDMA", 1);
+        if (!pkv::gqa_fp8_variant_exists(p.nw, p.ch, p.pf, p.wpe, p.kd)) {
+            p.nw = 2; p.ch = 1; p.pf = 1; p.wpe = 2; p.kd = 1;
+        }
         p.grid = (unsigned)wgs;
     } else if (fp8) {
         // launch-shape sweep on MI355X (c3-shaped FP8 batch): 4-wave workgroups with 2-block
@@ -109,13 +113,14 @@ Plan make_plan(int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32
         if (!pkv::fp8_variant_exists(p.nw, p.ch, p.pf)) { p.nw = nw; p.ch = ch; p.pf = pf; }
         p.grid = (unsigned)wgs;
     } else if (p.grouped) {
-        // measured on c5-shaped batches: 2-wave workgroups with register-staged loads (more
-        // workgroups per CU) beat deeper register pipelines and the LDS ring
-        p.kind = env_int("PKV_GQA_KIND", 0);
-        p.nw = env_int("PKV_GQA_NW", 2);
+        // measured on c5-shaped batches: K tiles staged through LDS by DMA (whole cache
+        // lines) with V in registers beat K loaded into registers (half lines) by ~7 %;
+        // 4-wave workgroups, one block per chunk, one chunk in flight
+        p.kind = env_int("PKV_GQA_KIND", 2);
+        p.nw = env_int("PKV_GQA_NW", 4);
         p.ch = env_int("PKV_GQA_CH", 1);
         p.pf = env_int("PKV_GQA_PF", 1);
-        if (!pkv::gqa_variant_exists(p.kind, p.nw, p.ch, p.pf)) { p.kind = 0; p.nw = 2; p.ch = 1; p.pf = 1; }
+        if (!pkv::gqa_variant_exists(p.kind, p.nw, p.ch, p.pf)) { p.kind = 2; p.nw = 4; p.ch = 1; p.pf = 1; }
         p.grid = (unsigned)wgs;
     } else {
         // a PF-deep load pipeline pays where a workgroup walks a long unsplit context
@@ -268,7 +273,7 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
             e = pkv::launch_kv_append_fp8(dtype, D, ap, s);
             if (e != hipSuccess) return fail(PKV_ERR_HIP, "kv_append_fp8 launch: %s", hipGetErrorString(e));
         }
-        e = pkv::launch_decode_gqa_fp8(dtype, D, p.nw, p.ch, p.pf, p.wpe, a, p.grid, s);
+        e = pkv::launch_decode_gqa_fp8(dtype, D, p.nw, p.ch, p.pf, p.wpe, p.kd, a, p.grid, s);
     } else if (fp8) {
         e = pkv::launch_decode_fp8(dtype, D, p.nw, p.ch, p.pf, fused, a, p.grid, s);
     } else if (p.grouped) {
@@ -293,8 +298,8 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
         if (e != hipSuccess) return fail(PKV_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
     }
     snprintf(g_launch, sizeof g_launch, "%s dtype=%d D=%d nw=%d ch=%d pf=%d%s grid=%u part_tokens=%d n_parts=%d%s",
-             fp8 ? (p.grouped ? "gqa_mfma_fp8" : "fp8") : p.grouped ? (p.kind ? "gqa_mfma_lds" : "gqa_mfma") : "mha",
-             dtype, D, p.nw, p.ch, p.pf, (fp8 && p.grouped) ? (p.wpe == 3 ? " wpe=3" : " wpe=2") : "",
+             fp8 ? (p.grouped ? "gqa_mfma_fp8" : "fp8") : p.grouped ? (p.kind == 1 ? "gqa_mfma_lds" : p.kind == 2 ? "gqa_mfma_kdma" : "gqa_mfma") : "mha",
+             dtype, D, p.nw, p.ch, p.pf, (fp8 && p.grouped) ? (p.kd ? (p.wpe == 3 ? " wpe=3 kdma" : " wpe=2 kdma") : (p.wpe == 3 ? " wpe=3" : " wpe=2")) : "",
              p.grid,
              p.part_tokens, p.n_parts,
              fused ? " fused_append" : "");

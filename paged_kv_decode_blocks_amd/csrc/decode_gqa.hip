@@ -123,6 +123,37 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
 #endif
 }
 
+// KL 16-byte reads from LDS, completed before return.  Issued as inline asm: the
+// compiler cannot tell a ring slot from the LDS DMAs still in flight into the
+// other slots and would drain every load before a plain LDS read; the caller's
+// own vmcnt wait orders the read after the DMA that filled the slot.
+template <int KL>
+__device__ __forceinline__ void lds_read16x(const char* base, const int (&off)[KL], uint4 (&r)[KL]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint32_t a0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)base;
+    if constexpr (KL == 1) {
+        asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r[0]) : "v"(a0 + off[0]) : "memory");
+    } else if constexpr (KL == 2) {
+        asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                     : "=v"(r[0]), "=v"(r[1])
+                     : "v"(a0 + off[0]), "v"(a0 + off[1])
+                     : "memory");
+    } else {
+        static_assert(KL == 4, "one, two or four reads");
+        asm volatile(
+            "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3])
+            : "v"(a0 + off[0]), "v"(a0 + off[1]), "v"(a0 + off[2]), "v"(a0 + off[3])
+            : "memory");
+    }
+#else
+    (void)base;
+    (void)off;
+    for (int q = 0; q < KL; ++q) r[q] = make_uint4(0, 0, 0, 0);
+#endif
+}
+
 // s_waitcnt vmcnt(N) leaving the other counters unconstrained (gfx9 encoding:
 // vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
 template <int N>
@@ -391,12 +422,31 @@ __device__ __forceinline__ void stage_ids(const AttnArgs& a, const int32_t* tabl
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 1: loads through registers, PF-deep pipeline per wave.
+// Kernel 1: V through registers; K through registers (KDMA = false) or staged
+// in LDS (KDMA = true).  Each wave keeps the loads of PF chunks in flight while
+// it computes one: the loads of chunk i + PF go out before chunk i is used.
+// A register load in the MFMA layout takes 64 bytes of each of 16 K rows (half
+// cache lines); with KDMA the K tile instead goes global -> LDS with
+// global_load_lds_dwordx4 (1 KiB contiguous per instruction) into a per-wave
+// ring of R = PF + 1 chunk slots, rows stored with an XOR chunk swizzle so the
+// MFMA-layout reads are conflict-free.  V rows are whole lines either way.
 // ---------------------------------------------------------------------------
-template <int DT, int D, int NW, int CH, int PF, bool APPEND>
+template <int DT, int D, int NW, int CH, int PF, bool KDMA, bool APPEND>
 __global__ __launch_bounds__(NW * 64) void decode_gqa_kernel(const AttnArgs a) {
     using L = GqaLane<DT, D, APPEND>;
     constexpr int KS = L::KS, NWORD = L::NWORD, ES = L::ES;
+    constexpr int R = PF + 1;                  // chunk buffers
+    constexpr int TILE = kBlockSize * D * ES;  // bytes of one (block, head) K tile
+    constexpr int CPR = D * ES / 16;           // 16-byte chunks per K row
+    constexpr int NDMA = TILE / 1024;          // DMA instructions per tile
+    constexpr int SLOT = CH * TILE;            // one chunk's K tiles
+    constexpr int LPC = CH * (NDMA + 4);       // vmcnt units per chunk: K DMAs, then 4 V rows
+    static_assert(R <= 4, "ring depth");
+    static_assert(!KDMA || PF * LPC < 64, "vmcnt range");
+    __shared__ __attribute__((aligned(16))) char s_k0[KDMA ? NW * SLOT : 16];
+    __shared__ __attribute__((aligned(16))) char s_k1[KDMA ? NW * SLOT : 16];
+    __shared__ __attribute__((aligned(16))) char s_k2[KDMA && R > 2 ? NW * SLOT : 16];
+    __shared__ __attribute__((aligned(16))) char s_k3[KDMA && R > 3 ? NW * SLOT : 16];
     __shared__ int32_t s_ids[kWindowBlocksG];
     __shared__ int s_bad;
     __shared__ float s_m[NW][16];
@@ -420,30 +470,68 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_kernel(const AttnArgs a) {
     const size_t blk_bytes = (size_t)a.H_kv * kBlockSize * D * ES;
     const size_t head_bytes = (size_t)u.g * kBlockSize * D * ES;
     const size_t new_off = ((size_t)u.b * a.new_row_stride + (size_t)u.g * D) * ES;
+    const char* kpool = a.k_pool + head_bytes;
+    const char* vpool = a.v_pool + head_bytes;
 
-    auto load_full = [&](uint4 (&kf)[CH][KS], VRow<NWORD> (&vf)[CH][4], int cb0) {
-        const char* kb[CH];
-        const char* vb[CH];
+    // DMA sources: lane l of instruction i fills LDS byte 16 (64 i + l) of the tile,
+    // i.e. row r = (64 i + l) / CPR, position p = (64 i + l) % CPR, with global chunk
+    // p ^ (r % CPR) of row r; the lane's piece of step s (chunk 4 s + j of row tau)
+    // is then at position (4 s + j) ^ (tau % CPR).
+    int kdma[NDMA], kread[KS];
 #pragma unroll
-        for (int cb = 0; cb < CH; ++cb) {
-            const int id = __builtin_amdgcn_readfirstlane(s_ids[cb0 + cb]);
-            kb[cb] = a.k_pool + (size_t)id * blk_bytes + head_bytes;
-            vb[cb] = a.v_pool + (size_t)id * blk_bytes + head_bytes;
+    for (int i = 0; i < NDMA; ++i) {
+        const int slot16 = i * 64 + lane;
+        const int row = slot16 / CPR, p = slot16 % CPR;
+        kdma[i] = row * D * ES + ((p ^ (row % CPR)) * 16);
+    }
+#pragma unroll
+    for (int q = 0; q < KS; ++q) kread[q] = st.tau * D * ES + (((4 * q + st.j) ^ (st.tau % CPR)) * 16);
+    auto slot_of = [&](int v) -> char* {
+        char* base = v == 0 ? s_k0 : v == 1 ? s_k1 : v == 2 ? s_k2 : s_k3;
+        return base + w * SLOT;
+    };
+
+    struct Buf {
+        uint4 k[CH][KS];
+        VRow<NWORD> v[CH][4];
+    };
+    auto load_chunk = [&](int v, Buf& bf, int cb0) {
+        size_t id[CH];
+#pragma unroll
+        for (int cb = 0; cb < CH; ++cb) id[cb] = (size_t)__builtin_amdgcn_readfirstlane(s_ids[cb0 + cb]);
+        if constexpr (KDMA) {   // the chunk's DMAs first: a wait that leaves later loads pending covers them
+#pragma unroll
+            for (int cb = 0; cb < CH; ++cb)
+#pragma unroll
+                for (int i = 0; i < NDMA; ++i)
+                    dma16(kpool + id[cb] * blk_bytes + kdma[i], slot_of(v) + cb * TILE + i * 1024);
+        } else {
+#pragma unroll
+            for (int cb = 0; cb < CH; ++cb)
+#pragma unroll
+                for (int s = 0; s < KS; ++s) bf.k[cb][s] = ld16(kpool + id[cb] * blk_bytes + st.koff[s]);
         }
 #pragma unroll
         for (int cb = 0; cb < CH; ++cb)
 #pragma unroll
-            for (int s = 0; s < KS; ++s) kf[cb][s] = ld16(kb[cb] + st.koff[s]);
-#pragma unroll
-        for (int cb = 0; cb < CH; ++cb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) vf[cb][i] = ldv<NWORD>(vb[cb] + st.voff[i]);
+            for (int i = 0; i < 4; ++i) bf.v[cb][i] = ldv<NWORD>(vpool + id[cb] * blk_bytes + st.voff[i]);
     };
     bool all_valid[CH][4];
 #pragma unroll
     for (int cb = 0; cb < CH; ++cb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) all_valid[cb][i] = true;
+    // steady: exactly PF later chunks' loads were issued after this chunk's
+    auto consume = [&](int v, Buf& bf, bool steady) {
+        if constexpr (KDMA) {
+            if (steady) wait_vmcnt<KDMA ? PF * LPC : 0>();
+            else wait_vmcnt<0>();
+            const char* sl = slot_of(v);
+#pragma unroll
+            for (int cb = 0; cb < CH; ++cb) lds_read16x<KS>(sl + cb * TILE, kread, bf.k[cb]);
+        }
+        st.template accumulate<CH>(bf.k, bf.v, all_valid);
+    };
 
     if (threadIdx.x == 0) s_bad = 0;
     for (int r0 = 0; r0 < nblk; r0 += kWindowBlocksG) {
@@ -454,37 +542,38 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_kernel(const AttnArgs a) {
         const bool any_bad = s_bad != 0;
         const int nch = (nr + CH - 1) / CH;
 
-        // chunks wholly below `lim`: PF-deep pipeline, unguarded steady state
+        // chunks wholly below `lim`: no masking; wave w takes chunks w, w + NW, ...
         const int tok_r = u.start + r0 * kBlockSize;
         const int nfull_all = max(0, min(nch, (u.lim - tok_r) / (CH * kBlockSize)));
         const int nf = w < nfull_all ? (nfull_all - w + NW - 1) / NW : 0;
-        uint4 bk[PF][CH][KS];
-        VRow<NWORD> bv[PF][CH][4];
         auto chunk_of = [&](int i) { return (w + NW * i) * CH; };
-        if (nf >= PF) {
+        // chunk i lives in buffer (and ring slot) i % R
+        Buf buf[R];
+        int i = 0;
+        if (nf >= R + PF) {
+            // unconditional prologue, so the loop is entered with the same loads in
+            // flight as it loops back with (keeps the compiler's waits exact)
 #pragma unroll
-            for (int v = 0; v < PF; ++v) load_full(bk[v], bv[v], chunk_of(v));
-            int i = 0;
-            for (; i + 2 * PF <= nf; i += PF) {
+            for (int v = 0; v < PF; ++v) load_chunk(v, buf[v], chunk_of(v));
+            for (; i + R + PF <= nf; i += R) {   // steady state: every load in range
 #pragma unroll
-                for (int v = 0; v < PF; ++v) {
-                    st.template accumulate<CH>(bk[v], bv[v], all_valid);
-                    load_full(bk[v], bv[v], chunk_of(i + PF + v));
+                for (int v = 0; v < R; ++v) {
+                    load_chunk((v + PF) % R, buf[(v + PF) % R], chunk_of(i + v + PF));
+                    consume(v, buf[v], true);
                 }
             }
-            const int rem = nf - i - PF;
-#pragma unroll
-            for (int v = 0; v < PF; ++v) {
-                st.template accumulate<CH>(bk[v], bv[v], all_valid);
-                if (v < rem) load_full(bk[v], bv[v], chunk_of(i + PF + v));
-            }
+        } else {
 #pragma unroll
             for (int v = 0; v < PF; ++v)
-                if (v < rem) st.template accumulate<CH>(bk[v], bv[v], all_valid);
-        } else {
-            for (int i = 0; i < nf; ++i) {
-                load_full(bk[0], bv[0], chunk_of(i));
-                st.template accumulate<CH>(bk[0], bv[0], all_valid);
+                if (v < nf) load_chunk(v, buf[v], chunk_of(v));
+        }
+        for (; i < nf; i += R) {   // at most two rounds left
+#pragma unroll
+            for (int v = 0; v < R; ++v) {
+                if (i + v < nf) {
+                    if (i + v + PF < nf) load_chunk((v + PF) % R, buf[(v + PF) % R], chunk_of(i + v + PF));
+                    consume(v, buf[v], false);
+                }
             }
         }
         // the partial chunk (at most one per round), block by block
@@ -665,12 +754,14 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_lds_kernel(const AttnArgs 
 // ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
-template <int DT, int D, int NW, int CH, int PF>
+template <int DT, int D, int NW, int CH, int PF, bool KDMA>
 static hipError_t launch_gqa_t(bool append, const AttnArgs& a, unsigned grid, hipStream_t stream) {
     if (append)
-        hipLaunchKernelGGL((decode_gqa_kernel<DT, D, NW, CH, PF, true>), dim3(grid), dim3(NW * 64), 0, stream, a);
+        hipLaunchKernelGGL((decode_gqa_kernel<DT, D, NW, CH, PF, KDMA, true>), dim3(grid), dim3(NW * 64), 0, stream,
+                           a);
     else
-        hipLaunchKernelGGL((decode_gqa_kernel<DT, D, NW, CH, PF, false>), dim3(grid), dim3(NW * 64), 0, stream, a);
+        hipLaunchKernelGGL((decode_gqa_kernel<DT, D, NW, CH, PF, KDMA, false>), dim3(grid), dim3(NW * 64), 0, stream,
+                           a);
     return hipGetLastError();
 }
 
@@ -683,8 +774,10 @@ static hipError_t launch_gqa_lds_t(bool append, const AttnArgs& a, unsigned grid
     return hipGetLastError();
 }
 
-// (waves, blocks per chunk, chunks in flight) of the register kernel; (waves, ring slots) of the LDS kernel
+// (waves, blocks per chunk, chunks in flight) of kernel 1 with K in registers (kind 0) and with
+// K staged in LDS (kind 2); (waves, ring slots) of the LDS kernel (kind 1)
 #define PKV_GQA_VARIANTS(X) X(4, 1, 1) X(4, 1, 2) X(2, 1, 1) X(2, 1, 2) X(4, 2, 1)
+#define PKV_GQA_KDMA_VARIANTS(X) X(2, 1, 1) X(2, 1, 2) X(4, 1, 1) X(2, 2, 1)
 #define PKV_GQA_LDS_VARIANTS(X) X(2, 2) X(2, 3) X(2, 4) X(4, 2) X(4, 3) X(8, 2)
 
 template <int DT, int D>
@@ -693,8 +786,17 @@ static hipError_t launch_gqa_d(int kind, int nw, int ch, int pf, bool append, co
     if (kind == 0) {
         switch (nw * 100 + ch * 10 + pf) {
 #define PKV_CASE(NW_, CH_, PF_) \
-    case NW_ * 100 + CH_ * 10 + PF_: return launch_gqa_t<DT, D, NW_, CH_, PF_>(append, a, grid, s);
+    case NW_ * 100 + CH_ * 10 + PF_: return launch_gqa_t<DT, D, NW_, CH_, PF_, false>(append, a, grid, s);
             PKV_GQA_VARIANTS(PKV_CASE)
+#undef PKV_CASE
+        default: return hipErrorInvalidValue;
+        }
+    }
+    if (kind == 2) {
+        switch (nw * 100 + ch * 10 + pf) {
+#define PKV_CASE(NW_, CH_, PF_) \
+    case NW_ * 100 + CH_ * 10 + PF_: return launch_gqa_t<DT, D, NW_, CH_, PF_, true>(append, a, grid, s);
+            PKV_GQA_KDMA_VARIANTS(PKV_CASE)
 #undef PKV_CASE
         default: return hipErrorInvalidValue;
         }
@@ -729,6 +831,16 @@ bool gqa_variant_exists(int kind, int nw, int ch, int pf) {
         default: return false;
         }
     }
+    if (kind == 2) {
+        switch (nw * 100 + ch * 10 + pf) {
+#define PKV_CASE(NW_, CH_, PF_) case NW_ * 100 + CH_ * 10 + PF_:
+            PKV_GQA_KDMA_VARIANTS(PKV_CASE)
+#undef PKV_CASE
+            return true;
+        default: return false;
+        }
+    }
+    if (kind != 1) return false;
     if (ch != 1) return false;
     switch (nw * 10 + pf) {
 #define PKV_CASE(NW_, S_) case NW_ * 10 + S_:
@@ -836,10 +948,12 @@ struct GqaLaneF8 : GqaLane<DT, D, false> {
     }
 
     // kb, vb: the (block, head) code tiles; ksb, vsb: its scale rows
-    __device__ __forceinline__ void load(const uint8_t* kb, const uint8_t* vb, const uint8_t* ksb, const uint8_t* vsb,
-                                         Codes& c) const {
+    __device__ __forceinline__ void load_k(const uint8_t* kb, Codes& c) const {
 #pragma unroll
         for (int u = 0; u < KL; ++u) c.k[u] = ld16(kb + kofs + 64 * u);
+    }
+    __device__ __forceinline__ void load_vs(const uint8_t* vb, const uint8_t* ksb, const uint8_t* vsb,
+                                            Codes& c) const {
 #pragma unroll
         for (int i = 0; i < 4; ++i) load_v(vb, i, c.v[i]);
         c.ks = *reinterpret_cast<const float4*>(ksb + sofs);
@@ -848,14 +962,15 @@ struct GqaLaneF8 : GqaLane<DT, D, false> {
 
     // Online-softmax update with CH blocks of codes.
     template <int CH>
-    __device__ __forceinline__ void accumulate8(const Codes (&c)[CH], const bool (&valid)[CH][4]) {
+    __device__ __forceinline__ void accumulate8(const uint4 (&kc)[CH][KL], const Codes (&c)[CH],
+                                                const bool (&valid)[CH][4]) {
         float sc[CH][4];
 #pragma unroll
         for (int cb = 0; cb < CH; ++cb) {
             floatx4 st = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int u = 0; u < KL; ++u) {
-                const uint4 kw = c[cb].k[u];
+                const uint4 kw = kc[cb][u];
                 const uint4 k0 = make_uint4(fp8x2_widen<DT>(kw.x, false), fp8x2_widen<DT>(kw.x, true),
                                             fp8x2_widen<DT>(kw.y, false), fp8x2_widen<DT>(kw.y, true));
                 const uint4 k1 = make_uint4(fp8x2_widen<DT>(kw.z, false), fp8x2_widen<DT>(kw.z, true),
@@ -938,18 +1053,40 @@ struct GqaLaneF8 : GqaLane<DT, D, false> {
                               valid[0][3] ? ks.w : 0.0f);
         c[0].vs = make_float4(valid[0][0] ? vs.x : 0.0f, valid[0][1] ? vs.y : 0.0f, valid[0][2] ? vs.z : 0.0f,
                               valid[0][3] ? vs.w : 0.0f);
-        accumulate8<1>(c, valid);
+        uint4 kc[1][KL];
+#pragma unroll
+        for (int u = 0; u < KL; ++u) kc[0][u] = c[0].k[u];
+        accumulate8<1>(kc, c, valid);
     }
 };
 
 // WPE: waves per SIMD the register allocation must leave room for (2 = as many
 // registers as the code wants; 3 trades a few spills for occupancy).  PF: chunks
-// whose loads are in flight while a chunk is being computed.
-template <int DT, int D, int NW, int CH, int PF, int WPE>
+// whose loads are in flight while a chunk is being computed.  KDMA: K tiles go
+// global -> LDS with global_load_lds_dwordx4 (1 KiB contiguous per instruction,
+// whole cache lines; a register load of the MFMA layout takes 64 bytes of each
+// of 16 rows) into a per-wave ring of R chunk slots, rows stored with an XOR
+// chunk swizzle so the MFMA-layout reads (16 rows, one chunk each) are
+// conflict-free; V and the scales stay register loads (already whole lines).
+template <int DT, int D, int NW, int CH, int PF, int WPE, bool KDMA>
 __global__ __launch_bounds__(NW * 64, WPE) void decode_gqa_fp8_kernel(const AttnArgs a) {
     using L = GqaLaneF8<DT, D>;
     using Codes = typename L::Codes;
-    constexpr int R = PF + 1;   // chunk buffers
+    constexpr int KL = L::KL;
+    constexpr int R = PF + 1;                 // chunk buffers
+    constexpr int TILE = kBlockSize * D;      // bytes of one (block, head) code tile
+    constexpr int CPR = D / 16;               // 16-byte chunks per code row
+    constexpr int NDMA = TILE / 1024;         // DMA instructions per tile
+    constexpr int SLOT = CH * TILE;           // one chunk's K tiles
+    constexpr int LPC = CH * (NDMA + 6);      // vmcnt units per chunk: K DMAs, 4 V rows, 2 scale loads
+    static_assert(R <= 4, "ring depth");
+    static_assert(!KDMA || PF * LPC < 64, "vmcnt range");
+    // one LDS object per ring slot, so that alias analysis can tell a read of one
+    // slot from the DMAs still in flight into the others
+    __shared__ __attribute__((aligned(16))) char s_k0[KDMA ? NW * SLOT : 16];
+    __shared__ __attribute__((aligned(16))) char s_k1[KDMA ? NW * SLOT : 16];
+    __shared__ __attribute__((aligned(16))) char s_k2[KDMA && R > 2 ? NW * SLOT : 16];
+    __shared__ __attribute__((aligned(16))) char s_k3[KDMA && R > 3 ? NW * SLOT : 16];
     __shared__ int32_t s_ids[kWindowBlocksG];
     __shared__ int s_bad;
     __shared__ float s_m[NW][16];
@@ -993,19 +1130,64 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_gqa_fp8_kernel(const Attn
     const uint8_t* kspool = reinterpret_cast<const uint8_t*>(a.k_scale) + head_sbytes;
     const uint8_t* vspool = reinterpret_cast<const uint8_t*>(a.v_scale) + head_sbytes;
 
-    auto load_chunk = [&](Codes (&c)[CH], int cb0) {
+    // DMA sources: lane l of instruction i fills LDS byte 16 (64 i + l) of the tile,
+    // i.e. row r = (64 i + l) / CPR, position p = (64 i + l) % CPR, with global chunk
+    // p ^ (r % CPR) of row r; the lane's MFMA piece (chunk 4 u + j of row col) is
+    // then at position (4 u + j) ^ (col % CPR).
+    int kdma[NDMA], kread[KL];
 #pragma unroll
-        for (int cb = 0; cb < CH; ++cb) {
-            const size_t id = (size_t)__builtin_amdgcn_readfirstlane(s_ids[cb0 + cb]);
-            st.load(kpool + id * blk_codes, vpool + id * blk_codes, kspool + id * blk_sbytes, vspool + id * blk_sbytes,
-                    c[cb]);
-        }
+    for (int i = 0; i < NDMA; ++i) {
+        const int slot16 = i * 64 + lane;
+        const int row = slot16 / CPR, p = slot16 % CPR;
+        kdma[i] = row * D + ((p ^ (row % CPR)) * 16);
+    }
+#pragma unroll
+    for (int q = 0; q < KL; ++q) kread[q] = st.col * D + (((4 * q + st.j) ^ (st.col % CPR)) * 16);
+    auto slot_of = [&](int v) -> char* {
+        char* base = v == 0 ? s_k0 : v == 1 ? s_k1 : v == 2 ? s_k2 : s_k3;
+        return base + w * SLOT;
     };
-    bool all_valid[CH][4];
+
+    auto load_chunk = [&](int v, Codes (&c)[CH], int cb0) {
+        size_t id[CH];
 #pragma unroll
-    for (int cb = 0; cb < CH; ++cb)
+        for (int cb = 0; cb < CH; ++cb) id[cb] = (size_t)__builtin_amdgcn_readfirstlane(s_ids[cb0 + cb]);
+        if constexpr (KDMA) {   // the chunk's DMAs first: a wait that leaves later loads pending covers them
 #pragma unroll
-        for (int i = 0; i < 4; ++i) all_valid[cb][i] = true;
+            for (int cb = 0; cb < CH; ++cb)
+#pragma unroll
+                for (int i = 0; i < NDMA; ++i)
+                    dma16(kpool + id[cb] * blk_codes + kdma[i], slot_of(v) + cb * TILE + i * 1024);
+        } else {
+#pragma unroll
+            for (int cb = 0; cb < CH; ++cb) st.load_k(kpool + id[cb] * blk_codes, c[cb]);
+        }
+#pragma unroll
+        for (int cb = 0; cb < CH; ++cb)
+            st.load_vs(vpool + id[cb] * blk_codes, kspool + id[cb] * blk_sbytes, vspool + id[cb] * blk_sbytes, c[cb]);
+    };
+    // steady: exactly PF later chunks' loads were issued after this chunk's
+    auto consume = [&](int v, const Codes (&c)[CH], bool steady) {
+        uint4 kc[CH][KL];
+        if constexpr (KDMA) {
+            if (steady) wait_vmcnt<KDMA ? PF * LPC : 0>();
+            else wait_vmcnt<0>();
+            const char* sl = slot_of(v);
+#pragma unroll
+            for (int cb = 0; cb < CH; ++cb) lds_read16x<KL>(sl + cb * TILE, kread, kc[cb]);
+        } else {
+#pragma unroll
+            for (int cb = 0; cb < CH; ++cb)
+#pragma unroll
+                for (int q = 0; q < KL; ++q) kc[cb][q] = c[cb].k[q];
+        }
+        bool all_valid[CH][4];
+#pragma unroll
+        for (int cb = 0; cb < CH; ++cb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) all_valid[cb][i] = true;
+        st.template accumulate8<CH>(kc, c, all_valid);
+    };
 
     if (threadIdx.x == 0) s_bad = 0;
     for (int r0 = 0; r0 < nblk; r0 += kWindowBlocksG) {
@@ -1018,25 +1200,33 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_gqa_fp8_kernel(const Attn
         const int nfull_all = max(0, min(nch, (u.lim - tok_r) / (CH * kBlockSize)));
         const int nf = w < nfull_all ? (nfull_all - w + NW - 1) / NW : 0;   // this wave's full chunks
         auto chunk_of = [&](int i) { return (w + NW * i) * CH; };
-        // chunk i lives in buf[i % R]; the loads of chunk i + PF go out before chunk i is used
+        // chunk i lives in buffer (and ring slot) i % R; the loads of chunk i + PF
+        // go out before chunk i is used
         Codes buf[R][CH];
-#pragma unroll
-        for (int v = 0; v < PF; ++v)
-            if (v < nf) load_chunk(buf[v], chunk_of(v));
         int i = 0;
-        for (; i + R + PF <= nf; i += R) {   // steady state: every load in range
+        if (nf >= R + PF) {
+            // unconditional prologue, so the loop is entered with the same loads in
+            // flight as it loops back with (keeps the compiler's waits exact)
 #pragma unroll
-            for (int v = 0; v < R; ++v) {
-                load_chunk(buf[(v + PF) % R], chunk_of(i + v + PF));
-                st.template accumulate8<CH>(buf[v], all_valid);
+            for (int v = 0; v < PF; ++v) load_chunk(v, buf[v], chunk_of(v));
+            for (; i + R + PF <= nf; i += R) {   // steady state: every load in range
+#pragma unroll
+                for (int v = 0; v < R; ++v) {
+                    load_chunk((v + PF) % R, buf[(v + PF) % R], chunk_of(i + v + PF));
+                    consume(v, buf[v], true);
+                }
             }
+        } else {
+#pragma unroll
+            for (int v = 0; v < PF; ++v)
+                if (v < nf) load_chunk(v, buf[v], chunk_of(v));
         }
         for (; i < nf; i += R) {   // at most two rounds left
 #pragma unroll
             for (int v = 0; v < R; ++v) {
                 if (i + v < nf) {
-                    if (i + v + PF < nf) load_chunk(buf[(v + PF) % R], chunk_of(i + v + PF));
-                    st.template accumulate8<CH>(buf[v], all_valid);
+                    if (i + v + PF < nf) load_chunk((v + PF) % R, buf[(v + PF) % R], chunk_of(i + v + PF));
+                    consume(v, buf[v], false);
                 }
             }
         }
@@ -1053,18 +1243,21 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_gqa_fp8_kernel(const Attn
     st.template finish<NW, D + 4>(a, s_m, s_l, s_o, w, u.b, u.g, u.part, s_bad != 0);
 }
 
-#define PKV_GQA_FP8_VARIANTS(X) \
-    X(2, 1, 1, 2) X(2, 1, 2, 2) X(4, 1, 1, 2) X(2, 2, 1, 2) X(4, 2, 1, 2) X(2, 1, 1, 3) X(4, 1, 1, 3) \
-    X(2, 1, 2, 3) X(4, 1, 2, 3) X(2, 1, 3, 2)
+#define PKV_GQA_FP8_VARIANTS(X)                                                                       \
+    X(2, 1, 1, 2, 0) X(2, 1, 2, 2, 0) X(4, 1, 1, 2, 0) X(2, 2, 1, 2, 0) X(4, 2, 1, 2, 0) X(2, 1, 1, 3, 0) \
+    X(4, 1, 1, 3, 0) X(4, 1, 2, 3, 0) X(2, 1, 1, 2, 1) X(2, 1, 2, 2, 1) X(2, 1, 3, 2, 1) X(4, 1, 1, 2, 1) \
+    X(4, 1, 2, 2, 1) X(2, 2, 1, 2, 1) X(2, 1, 1, 3, 1) X(4, 1, 2, 3, 1)
+
+#define PKV_GQA_FP8_KEY(NW_, CH_, PF_, W_, KD_) ((KD_) * 10000 + (W_) * 1000 + (NW_) * 100 + (CH_) * 10 + (PF_))
 
 template <int DT, int D>
-static hipError_t launch_gqa_fp8_d(int nw, int ch, int pf, int wpe, const AttnArgs& a, unsigned grid,
+static hipError_t launch_gqa_fp8_d(int nw, int ch, int pf, int wpe, int kd, const AttnArgs& a, unsigned grid,
                                    hipStream_t s) {
-    switch (wpe * 1000 + nw * 100 + ch * 10 + pf) {
-#define PKV_CASE(NW_, CH_, PF_, W_)                                                                             \
-    case W_ * 1000 + NW_ * 100 + CH_ * 10 + PF_:                                                                \
-        hipLaunchKernelGGL((decode_gqa_fp8_kernel<DT, D, NW_, CH_, PF_, W_>), dim3(grid), dim3(NW_ * 64), 0, s, \
-                           a);                                                                                  \
+    switch (PKV_GQA_FP8_KEY(nw, ch, pf, wpe, kd)) {
+#define PKV_CASE(NW_, CH_, PF_, W_, KD_)                                                                     \
+    case PKV_GQA_FP8_KEY(NW_, CH_, PF_, W_, KD_):                                                            \
+        hipLaunchKernelGGL((decode_gqa_fp8_kernel<DT, D, NW_, CH_, PF_, W_, KD_ != 0>), dim3(grid),          \
+                           dim3(NW_ * 64), 0, s, a);                                                         \
         return hipGetLastError();
         PKV_GQA_FP8_VARIANTS(PKV_CASE)
 #undef PKV_CASE
@@ -1072,20 +1265,20 @@ static hipError_t launch_gqa_fp8_d(int nw, int ch, int pf, int wpe, const AttnAr
     }
 }
 
-hipError_t launch_decode_gqa_fp8(int dtype, int D, int nw, int ch, int pf, int wpe, const AttnArgs& a, unsigned grid,
-                                 hipStream_t stream) {
+hipError_t launch_decode_gqa_fp8(int dtype, int D, int nw, int ch, int pf, int wpe, int kd, const AttnArgs& a,
+                                 unsigned grid, hipStream_t stream) {
     switch (dtype * 1000 + D) {
-    case DT_F16 * 1000 + 64: return launch_gqa_fp8_d<DT_F16, 64>(nw, ch, pf, wpe, a, grid, stream);
-    case DT_F16 * 1000 + 128: return launch_gqa_fp8_d<DT_F16, 128>(nw, ch, pf, wpe, a, grid, stream);
-    case DT_BF16 * 1000 + 64: return launch_gqa_fp8_d<DT_BF16, 64>(nw, ch, pf, wpe, a, grid, stream);
-    case DT_BF16 * 1000 + 128: return launch_gqa_fp8_d<DT_BF16, 128>(nw, ch, pf, wpe, a, grid, stream);
+    case DT_F16 * 1000 + 64: return launch_gqa_fp8_d<DT_F16, 64>(nw, ch, pf, wpe, kd, a, grid, stream);
+    case DT_F16 * 1000 + 128: return launch_gqa_fp8_d<DT_F16, 128>(nw, ch, pf, wpe, kd, a, grid, stream);
+    case DT_BF16 * 1000 + 64: return launch_gqa_fp8_d<DT_BF16, 64>(nw, ch, pf, wpe, kd, a, grid, stream);
+    case DT_BF16 * 1000 + 128: return launch_gqa_fp8_d<DT_BF16, 128>(nw, ch, pf, wpe, kd, a, grid, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
-bool gqa_fp8_variant_exists(int nw, int ch, int pf, int wpe) {
-    switch (wpe * 1000 + nw * 100 + ch * 10 + pf) {
-#define PKV_CASE(NW_, CH_, PF_, W_) case W_ * 1000 + NW_ * 100 + CH_ * 10 + PF_:
+bool gqa_fp8_variant_exists(int nw, int ch, int pf, int wpe, int kd) {
+    switch (PKV_GQA_FP8_KEY(nw, ch, pf, wpe, kd)) {
+#define PKV_CASE(NW_, CH_, PF_, W_, KD_) case PKV_GQA_FP8_KEY(NW_, CH_, PF_, W_, KD_):
         PKV_GQA_FP8_VARIANTS(PKV_CASE)
 #undef PKV_CASE
         return true;

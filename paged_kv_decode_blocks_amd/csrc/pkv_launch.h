@@ -63,10 +63,11 @@ hipError_t launch_decode_fp8(int q_dtype, int D, int nw, int ch, int pf, bool ap
 bool fp8_variant_exists(int nw, int ch, int pf);
 // grouped heads on MFMA over FP8 pools (no append inside; lengths from context_lens, or positions + 1 when
 // context_lens is NULL)
-// wpe: waves per SIMD the kernel's register allocation targets (2 or 3)
-hipError_t launch_decode_gqa_fp8(int q_dtype, int D, int nw, int ch, int pf, int wpe, const AttnArgs& a,
+// wpe: waves per SIMD the kernel's register allocation targets (2 or 3);
+// kd: 1 = K tiles staged through LDS by DMA, 0 = K loaded straight into registers
+hipError_t launch_decode_gqa_fp8(int q_dtype, int D, int nw, int ch, int pf, int wpe, int kd, const AttnArgs& a,
                                  unsigned grid, hipStream_t stream);
-bool gqa_fp8_variant_exists(int nw, int ch, int pf, int wpe);
+bool gqa_fp8_variant_exists(int nw, int ch, int pf, int wpe, int kd);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_decode_mha(int dtype, int D, int nw, int ch, int pf, bool append, const AttnArgs& a,
                              unsigned grid, hipStream_t stream);

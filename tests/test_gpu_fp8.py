@@ -129,20 +129,31 @@ def test_fp8_every_launch_variant(torch_dev, monkeypatch, variant):
         assert_close(got, ref, dtype, f"variant {variant} {dtype} D{D} P{P}")
 
 
-@pytest.mark.parametrize("variant", ["2,1,1", "2,1,2", "4,1,1", "2,2,1", "4,2,1"])
+# (waves, blocks per chunk, chunks in flight, waves per SIMD, K staged through LDS): every
+# variant the library instantiates for the grouped FP8 kernel
+GQA8_VARIANTS = ["2,1,1,2,0", "2,1,2,2,0", "4,1,1,2,0", "2,2,1,2,0", "4,2,1,2,0", "2,1,1,3,0", "4,1,1,3,0",
+                 "4,1,2,3,0", "2,1,1,2,1", "2,1,2,2,1", "2,1,3,2,1", "4,1,1,2,1", "4,1,2,2,1", "2,2,1,2,1",
+                 "2,1,1,3,1", "4,1,2,3,1"]
+
+
+@pytest.mark.parametrize("variant", GQA8_VARIANTS)
 def test_fp8_grouped_every_launch_variant(torch_dev, monkeypatch, variant):
-    nw, ch, pf = variant.split(",")
+    nw, ch, pf, wpe, kd = variant.split(",")
     monkeypatch.setenv("PKV_GQA8_NW", nw)
     monkeypatch.setenv("PKV_GQA8_CH", ch)
     monkeypatch.setenv("PKV_GQA8_PF", pf)
+    monkeypatch.setenv("PKV_GQA8_WPE", wpe)
+    monkeypatch.setenv("PKV_GQA8_KDMA", kd)
+    tag = f"nw={nw} ch={ch} pf={pf} wpe={wpe}" + (" kdma" if kd == "1" else "")
+    # 4500 tokens unsplit: more than one 256-block window of ids per workgroup
     for dtype, D, P, H_q, H_kv, append in (("bf16", 128, 0, 8, 1, True), ("f16", 64, 64, 16, 2, True),
                                            ("bf16", 128, 256, 12, 4, False)):
-        cfg = cfg_for(dtype, D, H_q, H_kv, (1, 17, 200, 1000, 2049), P=P, append=append)
+        cfg = cfg_for(dtype, D, H_q, H_kv, (1, 17, 200, 1000, 2049, 4500), P=P, append=append)
         w = make_workload(cfg, 43)
         ref, pk, pv = oracle.run_step(w)
         got, d = run(torch_dev, w, P, append)
         launch = pkv.last_launch()
-        assert launch.startswith("gqa_mfma_fp8") and f"nw={nw} ch={ch} pf={pf}" in launch, launch
+        assert launch.startswith("gqa_mfma_fp8") and tag + " " in launch, launch
         assert_close(got, ref, dtype, f"grouped variant {variant} {dtype} D{D} P{P}")
         if append:
             assert bits_equal(d["k_pool"].cpu().numpy(), pk[0]) and bits_equal(d["k_scale"].cpu().numpy(), pk[1])

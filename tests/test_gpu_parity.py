@@ -300,8 +300,10 @@ def test_bad_device_metadata_gives_nan_rows(torch_dev):
 
 
 # every launch-shape variant the library instantiates, forced through the plan's overrides
+# (kind, waves, blocks per chunk, chunks in flight or ring slots): every grouped variant the library instantiates
 GQA_VARIANTS = [(0, 4, 1, 1), (0, 4, 1, 2), (0, 2, 1, 1), (0, 2, 1, 2), (0, 4, 2, 1), (1, 2, 1, 2), (1, 2, 1, 3),
-                (1, 2, 1, 4), (1, 4, 1, 2), (1, 4, 1, 3), (1, 8, 1, 2)]
+                (1, 2, 1, 4), (1, 4, 1, 2), (1, 4, 1, 3), (1, 8, 1, 2), (2, 2, 1, 1), (2, 2, 1, 2), (2, 4, 1, 1),
+                (2, 2, 2, 1)]
 MHA_VARIANTS = [(4, 2, 1), (4, 2, 2), (4, 2, 3), (4, 1, 2), (4, 1, 4), (8, 2, 1), (8, 2, 2)]
 
 
@@ -323,7 +325,7 @@ def _with_env(env, fn):
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f16", 64)])
 def test_gqa_launch_variants(torch_dev, variant, dtype, D):
     kind, nw, ch, pf = variant
-    lens = (0, 1, 15, 16, 17, 100, 513, 1024, 3000)
+    lens = (0, 1, 15, 16, 17, 100, 513, 1024, 3000, 4500)   # 4500 unsplit: two windows of block ids
     w_attn = make_workload(get_config("c5", B=len(lens), H_q=16, H_kv=2, D=D, dtype=dtype, lengths=("fixed", lens),
                                       pool=("factor", 1.2)), seed=32)
     ref_attn = oracle.paged_decode_attention(dtype, w_attn.q, w_attn.k_pool, w_attn.v_pool, w_attn.block_tables,
@@ -332,7 +334,8 @@ def test_gqa_launch_variants(torch_dev, variant, dtype, D):
     for P in (0, 512):
         got = _with_env(env, lambda: run_attention(torch_dev, w_attn, w_attn.k_pool, w_attn.v_pool, P))
         launch = pkv.last_launch()
-        assert f"nw={nw} ch={ch} pf={pf}" in launch and ("lds" in launch) == bool(kind), launch
+        assert f"nw={nw} ch={ch} pf={pf}" in launch, launch
+        assert ("_lds" in launch) == (kind == 1) and ("_kdma" in launch) == (kind == 2), launch
         assert_close(got, ref_attn, dtype, f"attn {variant} P={P} [{launch}]")
     # fused step (lengths >= 1 only)
     wf = make_workload(get_config("c5", B=len(lens) - 1, H_q=16, H_kv=2, D=D, dtype=dtype,
