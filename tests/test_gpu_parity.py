@@ -304,6 +304,7 @@ def test_bad_device_metadata_gives_nan_rows(torch_dev):
 GQA_VARIANTS = [(0, 4, 1, 1), (0, 4, 1, 2), (0, 2, 1, 1), (0, 2, 1, 2), (0, 4, 2, 1), (1, 2, 1, 2), (1, 2, 1, 3),
                 (1, 2, 1, 4), (1, 4, 1, 2), (1, 4, 1, 3), (1, 8, 1, 2), (2, 2, 1, 1), (2, 2, 1, 2), (2, 4, 1, 1),
                 (2, 2, 2, 1)]
+# (waves, blocks per chunk, chunks in flight): every per-head variant the library instantiates
 MHA_VARIANTS = [(4, 2, 1), (4, 2, 2), (4, 2, 3), (4, 1, 2), (4, 1, 4), (8, 2, 1), (8, 2, 2)]
 
 
@@ -356,7 +357,7 @@ def test_gqa_launch_variants(torch_dev, variant, dtype, D):
 @pytest.mark.parametrize("dtype,D", [("f16", 128), ("bf16", 64), ("f32", 128)])
 def test_mha_launch_variants(torch_dev, variant, dtype, D):
     nw, ch, pf = variant
-    lens = (0, 1, 15, 16, 17, 100, 513, 1024, 3000)
+    lens = (0, 1, 15, 16, 17, 100, 513, 1024, 3000, 4500)   # 4500 unsplit: two windows of block ids
     cfg = get_config("c2", B=len(lens), H_q=4, H_kv=4, D=D, dtype=dtype, lengths=("fixed", lens),
                      pool=("factor", 1.2))
     w = make_workload(cfg, seed=41)
