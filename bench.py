@@ -243,6 +243,131 @@ def cumask_bench(args) -> int:
     return 0
 
 
+def cufrac_bench(args, torch, pkv, dev, lib) -> int:
+    """The decode step on a share of the CUs ([P2] section 3.3.1: a fraction of the
+    GPU already draws most of the HBM bandwidth for decode attention), alone and
+    beside a compute-bound neighbour on the other CUs.
+
+    The step runs as n persistent 16-wave workgroups (pkv_append_decode_attention_persistent),
+    each filling one CU's register file, so it occupies n CUs; the neighbour is the
+    library's MFMA-bound probe (pkv_probe_mfma_burn), one 100 KiB-LDS workgroup per
+    CU, launched first on N - n CUs so that exactly n stay free for the step.  This
+    bounds the step's share of the GPU by occupancy instead of a CU-masked queue."""
+    from workloads import get_config, make_workload, step_bytes
+
+    cfg = get_config(args.config)
+    if cfg.fp8 or cfg.H_q != cfg.H_kv or cfg.dtype == "f32":
+        print(json.dumps({"mode": "cufrac", "error": f"{args.config}: the persistent step takes f16/bf16 with "
+                                                     "one query head per KV head (c2, c3, c4)"}))
+        return 2
+    P = cfg.partition_size if args.partition is None else args.partition
+    w = make_workload(cfg, args.seed, append=True)
+    sb = step_bytes(cfg, w.context_lens, True)
+    bytes_per_step = sb["total"]
+    R = args.rotate or max(2, math.ceil(4 * INFINITY_CACHE_BYTES / max(sb["kv_history"], 1)))
+    calls, sets = resident_steps(lib, torch, pkv, dev, w, True, P, R)
+    n_cus = int(lib.pkv_device_cu_count())
+    P_ = ctypes.c_void_p
+    sa = torch.cuda.Stream(device=dev)
+    sg = torch.cuda.Stream(device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    K = max(args.steps // 10, 2 * R)
+
+    def step(k, n_wg, stream):
+        fn, a = calls[k % R]
+        sp = P_(stream.cuda_stream)
+        rc = lib.pkv_append_decode_attention_persistent(*a, n_wg, sp) if n_wg else fn(*a, sp)
+        if rc:
+            raise RuntimeError(f"step failed: {lib.pkv_status_string(rc).decode()}: {lib.pkv_last_error().decode()}")
+
+    def burn(n_wg, iters, stream):
+        rc = lib.pkv_probe_mfma_burn(n_wg, iters, P_(sink.data_ptr()), P_(stream.cuda_stream))
+        if rc:
+            raise RuntimeError(f"burn failed: {lib.pkv_status_string(rc).decode()}: {lib.pkv_last_error().decode()}")
+
+    def time_steps(n_wg):
+        for k in range(R):
+            step(k, n_wg, sa)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(sa)
+        for k in range(K):
+            step(k, n_wg, sa)
+        e1.record(sa)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / K
+
+    def burn_flops(n_wg, iters):
+        return n_wg * 16.0 * iters * 8 * 16384
+
+    def time_burn(n_wg, iters):
+        burn(n_wg, max(1, iters // 10), sg)
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(sg)
+        burn(n_wg, iters, sg)
+        g1.record(sg)
+        torch.cuda.synchronize()
+        return g0.elapsed_time(g1) * 1e-3
+
+    t_full = time_steps(0)
+    sweep = []
+    for n in (8, 16, 32, 52, 64, 96, 128, 192, 256):
+        if n > n_cus:
+            continue
+        t = time_steps(n)
+        sweep.append({"cus": n, "cu_fraction": round(n / n_cus, 3), "us_per_step": round(t * 1e6, 2),
+                      "GBps": round(bytes_per_step / t / 1e9, 1)})
+    ref = max(r["GBps"] for r in sweep)
+    for r in sweep:
+        r["frac_of_best"] = round(r["GBps"] / ref, 3)
+    print(json.dumps({"sweep_done": len(sweep)}), file=sys.stderr, flush=True)
+
+    # neighbour shares in multiples of 32 CUs: workgroups are dealt over the shader engines,
+    # so an uneven neighbour grid leaves some engines one free CU short and a step
+    # workgroup waits for one (a 204-CU neighbour cut the 52-CU step to the 32-CU rate)
+    corun = []
+    iters0 = 20000
+    for n in (32, 64, 96, 128, 192):
+        if n >= n_cus:
+            continue
+        ta = time_steps(n)
+        tb = time_burn(n_cus - n, iters0)
+        iters = max(1000, int(iters0 * (K * ta * 1.3) / tb))   # the neighbour outlasts the K steps
+        tb_alone = time_burn(n_cus - n, iters)
+        for k in range(R):
+            step(k, n, sa)
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(sg)
+        burn(n_cus - n, iters, sg)          # first: it takes N - n CUs, the step gets the rest
+        g1.record(sg)
+        e0.record(sa)
+        for k in range(K):
+            step(k, n, sa)
+        e1.record(sa)
+        torch.cuda.synchronize()
+        ta2 = e0.elapsed_time(e1) * 1e-3 / K
+        tb2 = g0.elapsed_time(g1) * 1e-3
+        corun.append({"attention_cus": n, "neighbour_cus": n_cus - n,
+                      "attention_alone_GBps": round(bytes_per_step / ta / 1e9, 1),
+                      "attention_beside_neighbour_GBps": round(bytes_per_step / ta2 / 1e9, 1),
+                      "neighbour_alone_TFLOPs": round(burn_flops(n_cus - n, iters) / tb_alone / 1e12, 1),
+                      "neighbour_beside_attention_TFLOPs": round(burn_flops(n_cus - n, iters) / tb2 / 1e12, 1),
+                      "neighbour_outlasts_steps": bool(tb2 >= K * ta2)})
+    print(json.dumps({
+        "mode": "cufrac", "metric": "decode step HBM GB/s on a share of the CUs", "unit": "GB/s",
+        "config": {"workload": workload_label(cfg, "kv_append + paged decode attention (fused), persistent "
+                                                   "16-wave workgroups"), "partition_size": P,
+                   "algorithmic_bytes_per_step": int(bytes_per_step), "input_rotation_sets": R,
+                   "steps_per_point": K, "n_cus": n_cus},
+        "full_step_default_launch_GBps": round(bytes_per_step / t_full / 1e9, 1),
+        "sweep": sweep, "corun_mfma_neighbour": corun,
+        "note": "share bounded by occupancy (one 16-wave workgroup per CU), not by a CU-masked queue"}))
+    return 0
+
+
 def loop_bench(args, torch, pkv, dev) -> int:
     """A decode loop driven by the library's block manager.
 
@@ -425,7 +550,7 @@ def main(argv=None):
     ap.add_argument("--no-graph", action="store_true", help="launch every step eagerly (for counter runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times (scales HBM byte counters)")
-    ap.add_argument("--mode", default="step", choices=["step", "loop", "cumask"],
+    ap.add_argument("--mode", default="step", choices=["step", "loop", "cumask", "cufrac"],
                     help="step: the headline step over resident inputs; loop: a block-manager-driven decode loop")
     ap.add_argument("--graphs", action="store_true", help="loop mode: replay captured step graphs")
     ap.add_argument("--native", action="store_true", help="loop mode: one pkv_decoder_step call per step")
@@ -461,6 +586,8 @@ def main(argv=None):
     lib = pkv.load_library()
     if args.mode == "loop":
         return loop_bench(args, torch, pkv, dev)
+    if args.mode == "cufrac":
+        return cufrac_bench(args, torch, pkv, dev, lib)
 
     cfg = get_config(args.config)
     append = not args.no_append

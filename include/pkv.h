@@ -191,6 +191,36 @@ int pkv_append_decode_attention(int dtype,
                                 void* stream);
 
 /*
+ * append_decode_attention_persistent -- the same fused step on a bounded share
+ * of the GPU ("Injecting Adrenaline into LLM Serving" review, section 3.3.1:
+ * decode attention is memory-bound, so a fraction of the compute units already
+ * draws most of the HBM bandwidth and the rest can serve other work).  The step
+ * runs as `n_workgroups` persistent workgroups of 16 waves that walk the
+ * (request, head, partition) units round-robin; one such workgroup fills the
+ * register file of its compute unit, so the step occupies n_workgroups CUs (all
+ * of them when n_workgroups >= the CU count) and leaves the others to work on
+ * other streams.  Results agree with pkv_append_decode_attention to the same
+ * tolerance (the wave count per unit differs, so the summation order does).
+ *
+ *   n_workgroups     in [1, 65536]; more than the number of units is clamped
+ *   dtype            PKV_F16 or PKV_BF16, and H_q == H_kv (else PKV_ERR_UNSUPPORTED)
+ *   other arguments  as in pkv_append_decode_attention
+ */
+int pkv_append_decode_attention_persistent(int dtype,
+                                           float* out,
+                                           const void* q, int64_t q_row_stride,
+                                           const void* k_new, const void* v_new, int64_t new_row_stride,
+                                           void* k_pool, void* v_pool,
+                                           const int32_t* block_tables, int32_t bt_stride,
+                                           const int32_t* positions,
+                                           int32_t B, int32_t H_q, int32_t H_kv, int32_t D,
+                                           int32_t block_size, int32_t n_blocks,
+                                           int32_t max_context_len, float scale, int32_t partition_size,
+                                           void* workspace, size_t workspace_bytes,
+                                           int32_t n_workgroups,
+                                           void* stream);
+
+/*
  * probe_stream_read -- measurement aid, not part of the decode step: reads
  * `bytes` bytes (rounded down to a multiple of 16) of device memory at `buf`
  * once with 16-byte loads from `grid` workgroups of 256 threads, so that the
@@ -199,6 +229,19 @@ int pkv_append_decode_attention(int dtype,
  * fold to one particular value.  buf 16-byte aligned; 1 <= grid <= 2^20.
  */
 int pkv_probe_stream_read(const void* buf, size_t bytes, void* sink, int32_t grid, void* stream);
+
+/*
+ * probe_mfma_burn -- measurement aid, not part of the decode step: a compute-
+ * bound neighbour for the step on a share of the CUs ("Injecting Adrenaline
+ * into LLM Serving" review, section 3.3.1: decode attention beside compute-bound
+ * work).  Launches `n_workgroups` workgroups of 16 waves, each holding 100 KiB
+ * of LDS so that nothing else of this library fits on its CU; every wave runs
+ * bf16 MFMA chains (v_mfma_f32_16x16x32_bf16, 8 chains) for `iterations` rounds,
+ * i.e. n_workgroups * 16 * iterations * 8 * 16384 flops.  Touches no memory but
+ * `sink` (a device word, written only if the result hits one value).
+ *   n_workgroups in [1, 65536], iterations in [1, 2^30], sink 4-byte aligned.
+ */
+int pkv_probe_mfma_burn(int32_t n_workgroups, int32_t iterations, void* sink, void* stream);
 
 /*
  * ---------------------------------------------------------------------------

@@ -5,6 +5,7 @@
 // or allocates; every kernel is enqueued on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -187,7 +188,8 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
                      const int32_t* block_tables, int32_t bt_stride, const int32_t* context_lens,
                      const int32_t* positions, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t block_size,
                      int32_t n_blocks, int32_t max_ctx, float scale, int32_t partition_size, void* workspace,
-                     size_t workspace_bytes, void* stream, const Fp8Scales* fp8 = nullptr) {
+                     size_t workspace_bytes, void* stream, const Fp8Scales* fp8 = nullptr,
+                     int32_t persistent_wgs = 0) {
     const bool fused = positions != nullptr;
     int st = check_common(dtype, B, H_q, H_kv, D, block_size, n_blocks, bt_stride, max_ctx, partition_size);
     if (st) return st;
@@ -210,6 +212,8 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
     const Plan p = make_plan(dtype, B, H_q, H_kv, D, max_ctx, partition_size, fp8 != nullptr);
     if ((int64_t)p.n_parts * B * (p.grouped ? H_kv : H_q) > 0x7fffffff)
         return fail(PKV_ERR_INVALID_ARG, "grid too large");
+    if (persistent_wgs && (fp8 || p.grouped || (dtype != PKV_F16 && dtype != PKV_BF16)))
+        return fail(PKV_ERR_UNSUPPORTED, "the persistent step takes f16/bf16 K/V with one query head per KV head");
     if (p.ws_total) {
         if (!workspace) return fail(PKV_ERR_WORKSPACE, "split needs %zu bytes of workspace, got NULL", p.ws_total);
         if (workspace_bytes < p.ws_total)
@@ -278,6 +282,9 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
         e = pkv::launch_decode_fp8(dtype, D, p.nw, p.ch, p.pf, fused, a, p.grid, s);
     } else if (p.grouped) {
         e = pkv::launch_decode_gqa(dtype, D, p.kind, p.nw, p.ch, p.pf, fused, a, p.grid, s);
+    } else if (persistent_wgs) {
+        e = pkv::launch_decode_mha_persistent(dtype, D, fused, a, std::min<unsigned>(p.grid, (unsigned)persistent_wgs),
+                                              s);
     } else {
         e = pkv::launch_decode_mha(dtype, D, p.nw, p.ch, p.pf, fused, a, p.grid, s);
     }
@@ -297,12 +304,22 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
         e = pkv::launch_lse_merge(D, m, s);
         if (e != hipSuccess) return fail(PKV_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
     }
-    snprintf(g_launch, sizeof g_launch, "%s dtype=%d D=%d nw=%d ch=%d pf=%d%s grid=%u part_tokens=%d n_parts=%d%s",
-             fp8 ? (p.grouped ? "gqa_mfma_fp8" : "fp8") : p.grouped ? (p.kind == 1 ? "gqa_mfma_lds" : p.kind == 2 ? "gqa_mfma_kdma" : "gqa_mfma") : "mha",
-             dtype, D, p.nw, p.ch, p.pf, (fp8 && p.grouped) ? (p.kd ? (p.wpe == 3 ? " wpe=3 kdma" : " wpe=2 kdma") : (p.wpe == 3 ? " wpe=3" : " wpe=2")) : "",
-             p.grid,
-             p.part_tokens, p.n_parts,
-             fused ? " fused_append" : "");
+    if (persistent_wgs) {
+        snprintf(g_launch, sizeof g_launch,
+                 "mha_persistent dtype=%d D=%d nw=16 ch=%d pf=1 grid=%u units=%u part_tokens=%d n_parts=%d%s", dtype, D,
+                 (dtype == PKV_BF16 && D == 128) ? 1 : 2, std::min<unsigned>(p.grid, (unsigned)persistent_wgs), p.grid,
+                 p.part_tokens, p.n_parts, fused ? " fused_append" : "");
+    } else {
+        snprintf(g_launch, sizeof g_launch, "%s dtype=%d D=%d nw=%d ch=%d pf=%d%s grid=%u part_tokens=%d n_parts=%d%s",
+                 fp8 ? (p.grouped ? "gqa_mfma_fp8" : "fp8")
+                     : p.grouped ? (p.kind == 1 ? "gqa_mfma_lds" : p.kind == 2 ? "gqa_mfma_kdma" : "gqa_mfma")
+                                 : "mha",
+                 dtype, D, p.nw, p.ch, p.pf,
+                 (fp8 && p.grouped)
+                     ? (p.kd ? (p.wpe == 3 ? " wpe=3 kdma" : " wpe=2 kdma") : (p.wpe == 3 ? " wpe=3" : " wpe=2"))
+                     : "",
+                 p.grid, p.part_tokens, p.n_parts, fused ? " fused_append" : "");
+    }
     g_err[0] = 0;
     return PKV_OK;
 }
@@ -440,6 +457,18 @@ int pkv_append_decode_attention_fp8(int q_dtype, float* out, const void* q, int6
                             workspace_bytes, stream, &sc);
 }
 
+int pkv_probe_mfma_burn(int32_t n_workgroups, int32_t iterations, void* sink, void* stream) {
+    if (!sink) return fail(PKV_ERR_NULL, "sink must not be NULL");
+    if (reinterpret_cast<uintptr_t>(sink) & 3u) return fail(PKV_ERR_INVALID_ARG, "sink must be 4-byte aligned");
+    if (n_workgroups < 1 || n_workgroups > 65536 || iterations < 1 || iterations > (1 << 30))
+        return fail(PKV_ERR_INVALID_ARG, "n_workgroups = %d, iterations = %d", n_workgroups, iterations);
+    hipError_t e = pkv::launch_mfma_burn(n_workgroups, iterations, reinterpret_cast<unsigned*>(sink),
+                                         reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "probe launch: %s", hipGetErrorString(e));
+    g_err[0] = 0;
+    return PKV_OK;
+}
+
 int pkv_probe_stream_read(const void* buf, size_t bytes, void* sink, int32_t grid, void* stream) {
     if (!buf || !sink) return fail(PKV_ERR_NULL, "buf and sink must not be NULL");
     if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(sink) & 3u))
@@ -553,6 +582,22 @@ int pkv_append_decode_attention(int dtype, float* out, const void* q, int64_t q_
                             block_tables, bt_stride, nullptr, B > 0 ? positions : nullptr, B, H_q, H_kv, D,
                             block_size, n_blocks, max_context_len, scale, partition_size, workspace,
                             workspace_bytes, stream);
+}
+
+int pkv_append_decode_attention_persistent(int dtype, float* out, const void* q, int64_t q_row_stride,
+                                           const void* k_new, const void* v_new, int64_t new_row_stride, void* k_pool,
+                                           void* v_pool, const int32_t* block_tables, int32_t bt_stride,
+                                           const int32_t* positions, int32_t B, int32_t H_q, int32_t H_kv, int32_t D,
+                                           int32_t block_size, int32_t n_blocks, int32_t max_context_len, float scale,
+                                           int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                           int32_t n_workgroups, void* stream) {
+    if (n_workgroups < 1 || n_workgroups > 65536)
+        return fail(PKV_ERR_INVALID_ARG, "n_workgroups = %d is outside [1, 65536]", n_workgroups);
+    if (B > 0 && !positions) return fail(PKV_ERR_NULL, "positions is NULL");
+    return launch_attention(dtype, out, q, q_row_stride, k_new, v_new, new_row_stride, k_pool, v_pool, k_pool, v_pool,
+                            block_tables, bt_stride, nullptr, B > 0 ? positions : nullptr, B, H_q, H_kv, D,
+                            block_size, n_blocks, max_context_len, scale, partition_size, workspace,
+                            workspace_bytes, stream, nullptr, n_workgroups);
 }
 
 }  // extern "C"

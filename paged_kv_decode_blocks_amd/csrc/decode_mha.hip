@@ -32,8 +32,9 @@ namespace pkv {
 
 constexpr int kWindowBlocks = 256;
 
+// One work unit: (request, query head, partition) number `unit`, partition-major.
 template <int DT, int D, int NW, int CH, int PF, bool APPEND>
-__global__ __launch_bounds__(NW * 64) void decode_mha_kernel(const AttnArgs a) {
+__device__ __forceinline__ void mha_unit(const AttnArgs& a, const int unit) {
     constexpr int ES = Dt<DT>::bytes;
     constexpr int E = 16 / ES;                // elements per 16-byte lane vector
     constexpr int LPT = D / E;                // lanes per token row
@@ -54,8 +55,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(const AttnArgs a) {
     const int c = lane % LPT;
 
     const int BH = a.B * a.H_q;
-    const int part = blockIdx.x / BH;
-    const int bh = blockIdx.x - part * BH;
+    const int part = unit / BH;
+    const int bh = unit - part * BH;
     const int b = bh / a.H_q;
     const int h = bh - b * a.H_q;
     const int g = h / a.G;
@@ -309,6 +310,26 @@ __global__ __launch_bounds__(NW * 64) void decode_mha_kernel(const AttnArgs a) {
         a.part_lse[(size_t)bh * a.n_parts + part] = bad ? __builtin_nanf("") : M + __builtin_amdgcn_logf(L);
 }
 
+template <int DT, int D, int NW, int CH, int PF, bool APPEND>
+__global__ __launch_bounds__(NW * 64) void decode_mha_kernel(const AttnArgs a) {
+    mha_unit<DT, D, NW, CH, PF, APPEND>(a, blockIdx.x);
+}
+
+// Persistent form: gridDim.x workgroups walk the units round-robin.  With 16
+// waves per workgroup and the register budget the body needs, a workgroup fills
+// its CU's register file, so a grid of n workgroups runs on n CUs: the step on a
+// bounded share of the GPU, next to whatever else runs on the other CUs ("Injecting
+// Adrenaline into LLM Serving" review, section 3.3: a fraction of the GPU already
+// draws most of the HBM bandwidth for decode attention).
+template <int DT, int D, int CH, bool APPEND>
+__global__ __launch_bounds__(1024) void decode_mha_persistent_kernel(const AttnArgs a) {
+    const int units = a.n_parts * a.B * a.H_q;
+    for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
+        __syncthreads();   // the previous unit's readers of the shared arrays are done
+        mha_unit<DT, D, 16, CH, 1, APPEND>(a, unit);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
@@ -344,6 +365,28 @@ hipError_t launch_decode_mha(int dtype, int D, int nw, int ch, int pf, bool appe
     case DT_F16 * 1000 + 128: return launch_mha_d<DT_F16, 128>(nw, ch, pf, append, a, grid, stream);
     case DT_BF16 * 1000 + 64: return launch_mha_d<DT_BF16, 64>(nw, ch, pf, append, a, grid, stream);
     case DT_BF16 * 1000 + 128: return launch_mha_d<DT_BF16, 128>(nw, ch, pf, append, a, grid, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int DT, int D, int CH>
+static hipError_t launch_mha_p(bool append, const AttnArgs& a, unsigned grid, hipStream_t stream) {
+    if (append)
+        hipLaunchKernelGGL((decode_mha_persistent_kernel<DT, D, CH, true>), dim3(grid), dim3(1024), 0, stream, a);
+    else
+        hipLaunchKernelGGL((decode_mha_persistent_kernel<DT, D, CH, false>), dim3(grid), dim3(1024), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_mha_persistent(int dtype, int D, bool append, const AttnArgs& a, unsigned grid,
+                                        hipStream_t stream) {
+    // 16 waves per workgroup leave 128 VGPRs per lane: bf16 D=128 takes one block per
+    // chunk to stay inside them without spilling (f16 packs its PV products tighter)
+    switch (dtype * 1000 + D) {
+    case DT_F16 * 1000 + 64: return launch_mha_p<DT_F16, 64, 2>(append, a, grid, stream);
+    case DT_F16 * 1000 + 128: return launch_mha_p<DT_F16, 128, 2>(append, a, grid, stream);
+    case DT_BF16 * 1000 + 64: return launch_mha_p<DT_BF16, 64, 2>(append, a, grid, stream);
+    case DT_BF16 * 1000 + 128: return launch_mha_p<DT_BF16, 128, 1>(append, a, grid, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -71,12 +71,17 @@ bool gqa_fp8_variant_exists(int nw, int ch, int pf, int wpe, int kd);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_decode_mha(int dtype, int D, int nw, int ch, int pf, bool append, const AttnArgs& a,
                              unsigned grid, hipStream_t stream);
+// persistent per-head kernel: `grid` workgroups of 16 waves walk all units (one CU each)
+hipError_t launch_decode_mha_persistent(int dtype, int D, bool append, const AttnArgs& a, unsigned grid,
+                                        hipStream_t stream);
 // kind 0: K/V through registers (nw, ch, pf = chunks in flight); kind 1: K/V through an LDS ring
 // (nw, ch = 1, pf = ring slots per wave)
 hipError_t launch_decode_gqa(int dtype, int D, int kind, int nw, int ch, int pf, bool append, const AttnArgs& a,
                              unsigned grid, hipStream_t stream);
 hipError_t launch_lse_merge(int D, const MergeArgs& a, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, size_t bytes, unsigned* sink, int grid, hipStream_t stream);
+// `grid` 16-wave workgroups, one per CU, each running bf16 MFMA chains for `iterations` rounds
+hipError_t launch_mfma_burn(int grid, int iterations, unsigned* sink, hipStream_t stream);
 bool mha_variant_exists(int nw, int ch, int pf);
 bool gqa_variant_exists(int kind, int nw, int ch, int pf);
 

@@ -1,6 +1,7 @@
-// probe.hip -- a plain streaming-read kernel, used only to measure the HBM read
-// bandwidth the device actually sustains (the practical ceiling next to the
-// nameplate peak).  Not part of the decode step.
+// probe.hip -- measurement aids, not part of the decode step: a plain
+// streaming-read kernel (the HBM read bandwidth the device actually sustains,
+// the practical ceiling next to the nameplate peak) and an MFMA-bound kernel
+// that occupies a chosen number of CUs.
 //
 // Every lane reads 16 bytes per access with a grid-stride loop, four accesses
 // in flight per iteration, and folds them into one word so the loads cannot be
@@ -31,6 +32,45 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4_t* __restr
 hipError_t launch_stream_read(const void* buf, size_t bytes, unsigned* sink, int grid, hipStream_t stream) {
     hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(256), 0, stream, reinterpret_cast<const u32x4_t*>(buf),
                        bytes / 16, sink);
+    return hipGetLastError();
+}
+
+// A compute-bound neighbour for measurements of the decode step on a share of
+// the CUs.  Each workgroup is 16 waves and holds 100 KiB of LDS, so neither a
+// second workgroup of this kernel nor one of the persistent decode step fits
+// beside it: a grid of n workgroups occupies n CUs for as long as it runs.  Every
+// wave runs 8 independent chains of v_mfma_f32_16x16x32_bf16 on register operands
+// for `iterations` rounds; nothing touches global memory but one word of `sink`,
+// written only if the result hits one particular value.
+constexpr int kBurnLdsBytes = 100 * 1024;
+
+typedef __bf16 bf16x8_burn_t __attribute__((ext_vector_type(8)));
+
+__global__ __launch_bounds__(1024) void mfma_burn_kernel(int iterations, unsigned* sink) {
+    __shared__ char pad[kBurnLdsBytes];
+    pad[threadIdx.x * 100] = (char)threadIdx.x;   // in use, so the allocation stays
+    const unsigned lane = threadIdx.x & 63;
+    // operands near 2^-10 (bf16 0x3A80): the accumulators stay finite for any run length here
+    const uint4 ra = make_uint4(0x3A803A80u ^ (lane & 7), 0x3A803A81u, 0x3A813A80u, 0x3A803A80u);
+    const uint4 rb = make_uint4(0x3A803A80u, 0x3A803A80u ^ (lane & 3), 0x3A803A80u, 0x3A823A80u);
+    const bf16x8_burn_t a = __builtin_bit_cast(bf16x8_burn_t, ra);
+    const bf16x8_burn_t b = __builtin_bit_cast(bf16x8_burn_t, rb);
+    floatx4 acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int it = 0; it < iterations; ++it) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
+    }
+    __syncthreads();
+    float sum = (float)pad[(threadIdx.x * 100 + 100) % kBurnLdsBytes];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) sum += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+    if (sum == 1234.5f) sink[0] = 1u;
+}
+
+hipError_t launch_mfma_burn(int grid, int iterations, unsigned* sink, hipStream_t stream) {
+    hipLaunchKernelGGL(mfma_burn_kernel, dim3(grid), dim3(1024), 0, stream, iterations, sink);
     return hipGetLastError();
 }
 

@@ -126,6 +126,36 @@ def test_fused_validation(lib):
     assert f(*bad) == OK
 
 
+def test_persistent_validation(lib):
+    f = lib.pkv_append_decode_attention_persistent
+    args = [1, FAKE, FAKE, 32 * 128, FAKE, FAKE, 32 * 128, FAKE, FAKE, FAKE, 64, FAKE, 8, 32, 32, 128, 16, 1024,
+            1024, 0.088, 0, None, 0, 64, None]
+    for n_wg in (0, -3, 65537):
+        bad = list(args)
+        bad[23] = n_wg
+        assert f(*bad) == E_ARG
+    bad = list(args)
+    bad[0] = 0                          # f32: not taken by the persistent step
+    assert f(*bad) == E_UNSUP
+    bad = list(args)
+    bad[14] = 8                         # H_kv = 8 < H_q: grouped, not taken
+    assert f(*bad) == E_UNSUP
+    bad = list(args)
+    bad[11] = None                      # positions
+    assert f(*bad) == E_NULL
+    bad = list(args)
+    bad[12] = 0                         # B = 0
+    assert f(*bad) == OK
+
+
+def test_mfma_burn_validation(lib):
+    f = lib.pkv_probe_mfma_burn
+    assert f(8, 100, None, None) == E_NULL
+    assert f(8, 100, FAKE + 2, None) == E_ARG
+    for n_wg, iters in ((0, 100), (65537, 100), (8, 0), (8, (1 << 30) + 1)):
+        assert f(n_wg, iters, FAKE, None) == E_ARG
+
+
 def test_binding_refuses_missing_library(tmp_path):
     with pytest.raises(pkv.PkvError):
         pkv.load_library(str(tmp_path / "nope.so"))
