@@ -52,8 +52,9 @@ __global__ __launch_bounds__(NW * 64) void decode_fp8_kernel(const AttnArgs a) {
     const int c = lane % LPT;
 
     const int BH = a.B * a.H_q;
-    const int part = blockIdx.x / BH;
-    const int bh = blockIdx.x - part * BH;
+    const int unit = xcd_pair_unit(blockIdx.x, a.n_parts * BH);
+    const int part = unit / BH;
+    const int bh = unit - part * BH;
     const int b = bh / a.H_q;
     const int h = bh - b * a.H_q;
     const int g = h / a.G;

@@ -33,6 +33,21 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
+// Work unit of workgroup `x` out of `units` (units numbered head-fastest), for
+// the per-head FP8 kernel.  Workgroups are dealt to the 8 XCDs round-robin by
+// index, so units 2k and 2k+1 -- KV heads 2k' and 2k'+1, whose 64-byte row-scale
+// pieces share one 128-byte line -- would land on two XCDs and each fetch that
+// line from HBM.  Within every full group of 16 indices, index 8m + j takes unit
+// 2 (8 i + j) + m (i the group): a head pair shares an XCD and starts together.
+// A bijection on [0, units); the last partial group keeps its order.  (Measured
+// on the 16-bit kernels, which have no scale lines, it helped one workload and
+// hurt another, so they keep the plain order.)
+__device__ __forceinline__ int xcd_pair_unit(int x, int units) {
+    if (x >= (units & ~15)) return x;
+    const int r = x & 15;
+    return ((x >> 4) * 8 + (r & 7)) * 2 + (r >> 3);
+}
+
 __device__ __forceinline__ uint4 ld16(const void* p) {
     const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
     return make_uint4(v.x, v.y, v.z, v.w);
