@@ -94,7 +94,15 @@ const char* pkv_status_string(int status);
 const char* pkv_last_error(void);
 
 /* Launch geometry of the last successful attention call on this thread
- * (kernel family, waves per workgroup, blocks per chunk, grid, partitions). */
+ * (kernel family, waves per workgroup, blocks per chunk, grid, partitions).
+ *
+ * The launch shapes are the library's measured defaults.  For tuning only, they
+ * can be overridden per process with environment variables read at each call:
+ * PKV_MHA_{NW,CH,PF} (per-head 16-bit), PKV_GQA_{KIND,NW,CH,PF} (grouped 16-bit;
+ * KIND 0 = K in registers, 1 = K and V through LDS, 2 = K through LDS),
+ * PKV_FP8_{NW,CH,PF} (per-head FP8) and PKV_GQA8_{NW,CH,PF,WPE,KDMA} (grouped
+ * FP8).  A combination the library does not instantiate falls back to the
+ * default; results agree to the same tolerance for every instantiated shape. */
 const char* pkv_last_launch(void);
 
 /*

@@ -28,15 +28,19 @@
 // and the accumulators are rescaled lazily (only when a head's running max
 // grows by more than 2^8), so the VALU rarely touches the MFMA accumulators.
 //
-// Two kernels share this arithmetic:
-//  * decode_gqa_kernel      K/V go global -> registers, PF chunks in flight per wave;
-//  * decode_gqa_lds_kernel  K/V go global -> LDS with global_load_lds_dwordx4
-//    (1 KiB fully coalesced per instruction, no registers held while in flight)
-//    into a per-wave ring of S block slots, then LDS -> registers in the MFMA
-//    layout.  K rows are stored with their 16-byte chunks XOR-swizzled by row,
-//    so the column-wise MFMA reads hit 16 different banks.
-// Both merge across the waves of the workgroup through LDS, and the fused
-// APPEND variants also write the new token.
+// Three kernels:
+//  * decode_gqa_kernel      V global -> registers; K global -> registers
+//    (KDMA = false) or global -> LDS with global_load_lds_dwordx4 (KDMA = true,
+//    the default: a register load in the MFMA layout takes half cache lines,
+//    a DMA takes 1 KiB contiguous); the loads of the chunk PF ahead go out
+//    before the current chunk is computed;
+//  * decode_gqa_lds_kernel  K and V both go global -> LDS into a per-wave ring
+//    of S block slots, then LDS -> registers in the MFMA layout;
+//  * decode_gqa_fp8_kernel  the same tiles over an FP8 (E4M3) cache, codes
+//    widened to q's type, row scales on scores and weights.
+// K rows in LDS are stored with their 16-byte chunks XOR-swizzled by row, so the
+// column-wise MFMA reads hit different banks.  All merge across the waves of the
+// workgroup through LDS, and the fused APPEND variants also write the new token.
 #include "pkv_device.h"
 #include "pkv_launch.h"
 
