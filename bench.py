@@ -40,14 +40,24 @@ INFINITY_CACHE_BYTES = 256 << 20
 DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source with comments removed and whitespace runs collapsed (the digest ignores
+    edits that cannot change the build; the sources hold no string with a comment marker)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_digest() -> str:
-    """sha256 over the HIP sources and headers: ties committed counter data to this kernel build."""
+    """sha256 over the HIP sources and headers, comments excluded: ties committed counter
+    data to this kernel build."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_decode_blocks_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".h", ".cpp")):
             h.update(name.encode())
-            h.update(open(os.path.join(csrc, name), "rb").read())
+            h.update(_code_only(open(os.path.join(csrc, name), encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 
