@@ -59,6 +59,15 @@ def _load():
         lib.oracle_kv_append_fp8.restype = ctypes.c_int
         lib.oracle_e4m3_dequantize_rows.argtypes = [P, P, I64, I32, P]
         lib.oracle_e4m3_dequantize_rows.restype = ctypes.c_int
+        lib.oracle_e2m1_decode.argtypes = [P, P, I64]
+        lib.oracle_e2m1_decode.restype = ctypes.c_int
+        lib.oracle_mxfp4_quantize_row.argtypes = [ctypes.c_int, P, I32, P, P]
+        lib.oracle_mxfp4_quantize_row.restype = ctypes.c_int
+        lib.oracle_kv_append_mxfp4.argtypes = [ctypes.c_int, P, P, I64, P, P, P, P, P, I32, P, I32, I32, I32, I32,
+                                               I32]
+        lib.oracle_kv_append_mxfp4.restype = ctypes.c_int
+        lib.oracle_mxfp4_dequantize_rows.argtypes = [P, P, I64, I32, P]
+        lib.oracle_mxfp4_dequantize_rows.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -124,11 +133,19 @@ def threads(nthreads: int = 0) -> int:
 def run_step(w, nthreads: int = 0):
     """One whole decode step on a ``workloads.Workload``: append (if any), then attention.
 
-    Returns (out fp64 [B,H_q,D], k_pool_after, v_pool_after) -- for an FP8
-    workload each pool is a (codes, scales) pair; the workload's own pools are
-    left untouched.
+    Returns (out fp64 [B,H_q,D], k_pool_after, v_pool_after) -- for an FP8 or
+    MXFP4 workload each pool is a (codes, scales) pair; the workload's own pools
+    are left untouched.
     """
     k_pool, v_pool = w.k_pool.copy(), w.v_pool.copy()
+    if getattr(w.cfg, "kv_dtype", "") == "mxfp4":
+        k_scale, v_scale = w.k_scale.copy(), w.v_scale.copy()
+        if w.positions is not None:
+            kv_append_mxfp4(w.cfg.dtype, w.k_new, w.v_new, k_pool, v_pool, k_scale, v_scale, w.block_tables,
+                            w.positions, w.cfg.block_size)
+        out = paged_decode_attention_mxfp4(w.cfg.dtype, w.q, k_pool, v_pool, k_scale, v_scale, w.block_tables,
+                                           w.context_lens, w.scale, nthreads=nthreads)
+        return out, (k_pool, k_scale), (v_pool, v_scale)
     if getattr(w.cfg, "fp8", False):
         k_scale, v_scale = w.k_scale.copy(), w.v_scale.copy()
         if w.positions is not None:
@@ -198,5 +215,64 @@ def paged_decode_attention_fp8(q_dtype: str, q, k_pool, v_pool, k_scale, v_scale
     qf = decode(q_dtype, q).astype(np.float32) if q_dtype != "f32" else np.ascontiguousarray(q)
     kf = e4m3_dequantize(k_pool, k_scale)
     vf = e4m3_dequantize(v_pool, v_scale)
+    return paged_decode_attention("f32", qf, kf, vf, block_tables, context_lens, scale, with_lse=with_lse,
+                                  nthreads=nthreads)
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 K/V cache: E2M1 codes two per byte, one E8M0 scale per 32 elements
+# ---------------------------------------------------------------------------
+
+def e2m1_decode(packed: np.ndarray) -> np.ndarray:
+    """Packed E2M1 codes (uint8, two per byte, element 2k in the low nibble) -> float64 values, unscaled."""
+    src = np.ascontiguousarray(packed, dtype=np.uint8)
+    dst = np.empty(src.size * 2, dtype=np.float64)
+    _check(_load().oracle_e2m1_decode(_ptr(src), _ptr(dst), dst.size), "e2m1_decode")
+    return dst.reshape(src.shape[:-1] + (src.shape[-1] * 2,)) if src.ndim else dst
+
+
+def mxfp4_quantize_row(dtype: str, row: np.ndarray):
+    """One row of D source-dtype storage elements -> (uint8 codes [D/2], uint8 E8M0 scales [D/32])."""
+    src = np.ascontiguousarray(row)
+    D = src.size
+    codes = np.zeros(D // 2, dtype=np.uint8)
+    scales = np.zeros(D // 32, dtype=np.uint8)
+    _check(_load().oracle_mxfp4_quantize_row(_DTYPE_CODE[dtype], _ptr(src), D, _ptr(codes), _ptr(scales)),
+           "mxfp4_quantize_row")
+    return codes, scales
+
+
+def kv_append_mxfp4(dtype: str, k_new, v_new, k_pool, v_pool, k_scale, v_scale, block_tables, positions,
+                    block_size: int):
+    """Quantize the new K/V rows (source dtype) into their slots, in place on the code and scale pools."""
+    B, H_kv, D = k_new.shape
+    for a in (k_new, v_new, k_pool, v_pool, k_scale, v_scale, block_tables, positions):
+        assert a.flags.c_contiguous
+    assert k_pool.dtype == np.uint8 and k_scale.dtype == np.uint8
+    rc = _load().oracle_kv_append_mxfp4(_DTYPE_CODE[dtype], _ptr(k_new), _ptr(v_new), H_kv * D, _ptr(k_pool),
+                                        _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
+                                        block_tables.shape[1], _ptr(positions), B, H_kv, D, block_size,
+                                        k_pool.shape[0])
+    _check(rc, "oracle_kv_append_mxfp4")
+
+
+def mxfp4_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Pools of codes [..., D/2] and scales [..., D/32] -> float32 values [..., D] (exact)."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    s = np.ascontiguousarray(scales, dtype=np.uint8)
+    D = c.shape[-1] * 2
+    assert c.shape[:-1] == s.shape[:-1] and s.shape[-1] * 32 == D
+    n_rows = int(np.prod(c.shape[:-1]))
+    out = np.empty(c.shape[:-1] + (D,), dtype=np.float32)
+    _check(_load().oracle_mxfp4_dequantize_rows(_ptr(c), _ptr(s), n_rows, D, _ptr(out)), "mxfp4_dequantize")
+    return out
+
+
+def paged_decode_attention_mxfp4(q_dtype: str, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens,
+                                 scale, *, with_lse: bool = False, nthreads: int = 0):
+    """fp64 attention over MXFP4 pools: the float32 attention on the exactly dequantized pools, q exactly widened."""
+    qf = decode(q_dtype, q).astype(np.float32) if q_dtype != "f32" else np.ascontiguousarray(q)
+    kf = mxfp4_dequantize(k_pool, k_scale)
+    vf = mxfp4_dequantize(v_pool, v_scale)
     return paged_decode_attention("f32", qf, kf, vf, block_tables, context_lens, scale, with_lse=with_lse,
                                   nthreads=nthreads)

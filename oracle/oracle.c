@@ -386,3 +386,148 @@ int oracle_e4m3_dequantize_rows(const uint8_t* codes, const float* scale, int64_
             dst[r * D + d] = (float)(e4m3_value(codes[r * D + d]) * (double)scale[r]);
     return ORC_OK;
 }
+
+/*
+ * ---------------------------------------------------------------------------
+ * MXFP4 K/V cache
+ * ---------------------------------------------------------------------------
+ * The same page, section 6.2, names a 4-bit KV cache with fine-grained block
+ * scales.  Reading taken here: the OCP microscaling format MXFP4 (OCP
+ * Microscaling Formats (MX) Specification v1.0, section 5: a block of 32
+ * elements shares one scale).  Elements are E2M1 codes (sign, 2 exponent bits
+ * with bias 1, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; no
+ * infinity or NaN); the shared scale is E8M0 (an 8-bit biased exponent, value
+ * 2^(s - 127), s = 255 is NaN).  Per block of 32 consecutive elements of a row:
+ *   amax = max_i |x_i|                    (x in its source dtype)
+ *   E    = floor(log2 amax) - 2           (2: the exponent of E2M1's largest
+ *          value 6 = 1.5 * 2^2), clamped to [-127, 127]; E = -127 when amax = 0
+ *   code = the E2M1 value nearest to x_i / 2^E, magnitudes above 6 taken as 6,
+ *          ties to the even code; the sign bit is the sign of x_i
+ *   s    = E + 127
+ * and the dequantized value is value(code) * 2^E (exact in double and in f32
+ * for every E a finite f32 input produces).  Dividing by 2^E is exact for the
+ * E range used here, so the only rounding is the one to the E2M1 grid, done
+ * here by searching the grid.  Storage: codes two per byte, element 2k in the
+ * low nibble of byte k; one scale byte per block of 32.
+ */
+
+static double e2m1_value(uint8_t c) {
+    int sign = (c >> 3) & 1;
+    int ex = (c >> 1) & 3;
+    int man = c & 1;
+    double v = ex == 0 ? 0.5 * man : ldexp(1.0 + 0.5 * man, ex - 1);
+    return sign ? -v : v;
+}
+
+static double e8m0_value(uint8_t s) { return s == 255 ? NAN : ldexp(1.0, (int)s - 127); }
+
+/* packed MXFP4 codes (n elements, two per byte) -> doubles, unscaled */
+int oracle_e2m1_decode(const uint8_t* packed, double* dst, int64_t n) {
+    if (n < 0 || (n & 1) || (n && (!packed || !dst))) return ORC_ERR_ARG;
+    for (int64_t i = 0; i < n; ++i) dst[i] = e2m1_value((uint8_t)((packed[i >> 1] >> (4 * (i & 1))) & 15));
+    return ORC_OK;
+}
+
+/* The non-negative code (0 .. 7) whose value is nearest to a, 0 <= a; ties to the even code. */
+static uint8_t e2m1_nearest_magnitude(double a) {
+    if (a > 6.0) a = 6.0;
+    int best = 0;
+    double best_err = fabs(a - e2m1_value(0));
+    for (int c = 1; c <= 7; ++c) {
+        double err = fabs(a - e2m1_value((uint8_t)c));
+        if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    return (uint8_t)best;
+}
+
+/* Quantize one row of D source elements (D a multiple of 32): codes[0 .. D/2), scales[0 .. D/32). */
+int oracle_mxfp4_quantize_row(int src_dtype, const void* src, int32_t D, uint8_t* codes, uint8_t* scales) {
+    if (!elem_size(src_dtype) || D <= 0 || D % 32 || !src || !codes || !scales) return ORC_ERR_ARG;
+    for (int32_t d = 0; d < D; ++d)
+        if (!isfinite(load_elem(src_dtype, src, d))) return ORC_ERR_RANGE;
+    for (int32_t blk = 0; blk < D / 32; ++blk) {
+        double amax = 0.0;
+        for (int32_t i = 0; i < 32; ++i) {
+            double x = fabs(load_elem(src_dtype, src, blk * 32 + i));
+            if (x > amax) amax = x;
+        }
+        int E = -127;
+        if (amax > 0.0) {
+            int e2;
+            frexp(amax, &e2);               /* amax = f * 2^e2, f in [0.5, 1): floor(log2 amax) = e2 - 1 */
+            E = e2 - 1 - 2;
+            if (E < -127) E = -127;
+            if (E > 127) E = 127;
+        }
+        for (int32_t i = 0; i < 32; ++i) {
+            const int32_t d = blk * 32 + i;
+            double v = ldexp(load_elem(src_dtype, src, d), -E);
+            uint8_t c = e2m1_nearest_magnitude(fabs(v));
+            if (signbit(v)) c |= 8;
+            if (i & 1) codes[d >> 1] = (uint8_t)((codes[d >> 1] & 0x0F) | (c << 4));
+            else codes[d >> 1] = c;
+        }
+        scales[blk] = (uint8_t)(E + 127);
+    }
+    return ORC_OK;
+}
+
+/*
+ * MXFP4 append: quantize k_new[b][g][:] and v_new[b][g][:] into slot
+ * positions[b] % block_size of block block_tables[b][positions[b] / block_size]:
+ * codes into k_pool / v_pool ([n_blocks][H_kv][block_size][D/2] bytes), scales
+ * into k_scale / v_scale ([n_blocks][H_kv][block_size][D/32] bytes).
+ */
+int oracle_kv_append_mxfp4(int src_dtype, const void* k_new, const void* v_new, int64_t new_row_stride,
+                           uint8_t* k_pool, uint8_t* v_pool, uint8_t* k_scale, uint8_t* v_scale,
+                           const int32_t* block_tables, int32_t bt_stride, const int32_t* positions,
+                           int32_t B, int32_t H_kv, int32_t D, int32_t block_size, int32_t n_blocks) {
+    int e = elem_size(src_dtype);
+    if (!e || B < 0 || H_kv <= 0 || D <= 0 || D % 32 || block_size <= 0 || n_blocks <= 0 || bt_stride <= 0)
+        return ORC_ERR_ARG;
+    if (B == 0) return ORC_OK;
+    if (!k_new || !v_new || !k_pool || !v_pool || !k_scale || !v_scale || !block_tables || !positions)
+        return ORC_ERR_ARG;
+    if (new_row_stride < (int64_t)H_kv * D) return ORC_ERR_ARG;
+    for (int32_t b = 0; b < B; ++b) {
+        int32_t p = positions[b];
+        if (p < 0 || p / block_size >= bt_stride) return ORC_ERR_RANGE;
+        int32_t blk = block_tables[(int64_t)b * bt_stride + p / block_size];
+        if (blk < 0 || blk >= n_blocks) return ORC_ERR_RANGE;
+    }
+    for (int32_t b = 0; b < B; ++b) {
+        int32_t p = positions[b];
+        int32_t blk = block_tables[(int64_t)b * bt_stride + p / block_size];
+        int32_t slot = p % block_size;
+        for (int32_t g = 0; g < H_kv; ++g) {
+            int64_t row = ((int64_t)blk * H_kv + g) * block_size + slot;
+            const char* ks = (const char*)k_new + ((int64_t)b * new_row_stride + (int64_t)g * D) * e;
+            const char* vs = (const char*)v_new + ((int64_t)b * new_row_stride + (int64_t)g * D) * e;
+            int st = oracle_mxfp4_quantize_row(src_dtype, ks, D, k_pool + row * (D / 2), k_scale + row * (D / 32));
+            if (st == ORC_OK)
+                st = oracle_mxfp4_quantize_row(src_dtype, vs, D, v_pool + row * (D / 2), v_scale + row * (D / 32));
+            if (st != ORC_OK) return st;
+        }
+    }
+    return ORC_OK;
+}
+
+/*
+ * Dequantize n_rows rows of D elements into float32: dst[r][d] =
+ * value(code of element d of row r) * 2^(scale byte of its block - 127) (exact;
+ * NaN where the scale byte is 255).  The MXFP4 attention is the float32
+ * attention above on pools dequantized this way.
+ */
+int oracle_mxfp4_dequantize_rows(const uint8_t* codes, const uint8_t* scales, int64_t n_rows, int32_t D,
+                                 float* dst) {
+    if (n_rows < 0 || D <= 0 || D % 32 || (n_rows && (!codes || !scales || !dst))) return ORC_ERR_ARG;
+    for (int64_t r = 0; r < n_rows; ++r)
+        for (int32_t d = 0; d < D; ++d) {
+            const uint8_t c = (uint8_t)((codes[r * (D / 2) + (d >> 1)] >> (4 * (d & 1))) & 15);
+            dst[r * D + d] = (float)(e2m1_value(c) * e8m0_value(scales[r * (D / 32) + d / 32]));
+        }
+    return ORC_OK;
+}

@@ -25,6 +25,13 @@ uniform mantissas and signs, so a row looks like a quantized Gaussian whose
 largest values sit near the top of the E4M3 range; scales 2^k with k uniform in
 [-12, -8] -- and never quantizes anything.  Their poison is the NaN code 0x7F
 with a NaN scale.  q, k_new and v_new keep ``dtype``.
+
+MXFP4 K/V workloads (``kv_dtype="mxfp4"``) hold E2M1 codes two per byte
+(element 2k in the low nibble of byte k) and one E8M0 scale byte per 32
+elements of a row ([n_blocks][H_kv][slot][D/2] and [n_blocks][H_kv][slot][D/32]
+uint8).  The generator draws code bytes uniformly (every 4-bit code is finite)
+and scale bytes 2^k with k uniform in [-5, -1], and never quantizes anything.
+Their poison is a NaN scale byte (0xFF) over code bytes 0x77.
 """
 from __future__ import annotations
 
@@ -94,7 +101,8 @@ class Config:
     kv_std: float = 1.0
     append: bool = False      # the step appends one new token per request before attention
     partition_size: int = 0   # split-KV partition length in tokens (0 = whole context per workgroup)
-    kv_dtype: str = ""        # "" = same as dtype; "fp8" = OCP E4M3 codes with per-row scales
+    kv_dtype: str = ""        # "" = same as dtype; "fp8" = OCP E4M3 codes with per-row scales;
+                              # "mxfp4" = E2M1 codes with an E8M0 scale per 32 elements
 
     @property
     def G(self) -> int:
@@ -103,6 +111,10 @@ class Config:
     @property
     def fp8(self) -> bool:
         return self.kv_dtype == "fp8"
+
+    @property
+    def mxfp4(self) -> bool:
+        return self.kv_dtype == "mxfp4"
 
 
 # The five workloads.  Shapes, dtypes, length mixes and pool sizes follow the
@@ -133,6 +145,10 @@ CONFIGS["c3f8"] = replace(CONFIGS["c3"], name="c3f8", kv_dtype="fp8",
 CONFIGS["c5f8"] = replace(CONFIGS["c5"], name="c5f8", kv_dtype="fp8",
                           title="GQA long context, FP8 E4M3 K/V (B32, 64 q / 8 kv heads, D128, bf16 q, "
                                 "ctx U[4096,16384], split 1024)")
+# and with an MXFP4 K/V cache
+CONFIGS["c3f4"] = replace(CONFIGS["c3"], name="c3f4", kv_dtype="mxfp4",
+                          title="large decode batch, MXFP4 K/V (B80, 32 heads MHA, D128, f16 q, ctx U[128,2048], "
+                                "append)")
 
 
 def draw_e4m3_codes(rng: np.random.Generator, shape) -> np.ndarray:
@@ -239,10 +255,13 @@ def make_workload(cfg: Config, seed: Optional[int] = None, *, append: Optional[b
 
     poison = _poison(cfg.dtype)
     pools, scales = [], []
-    for _ in range(2):  # K then V (FP8: codes then scales for each)
+    for _ in range(2):  # K then V (FP8, MXFP4: codes then scales for each)
         if cfg.fp8:
             pool = np.full((n_blocks, H_kv, bs, D), 0x7F, dtype=np.uint8)
             sc = np.full((n_blocks, H_kv, bs), np.nan, dtype=np.float32)
+        elif cfg.mxfp4:
+            pool = np.full((n_blocks, H_kv, bs, D // 2), 0x77, dtype=np.uint8)
+            sc = np.full((n_blocks, H_kv, bs, D // 32), 0xFF, dtype=np.uint8)
         else:
             pool = np.full((n_blocks, H_kv, bs, D), poison, dtype=sdt)
         for b in range(B):
@@ -260,6 +279,14 @@ def make_workload(cfg: Config, seed: Optional[int] = None, *, append: Optional[b
                     svals[-1, :, rem:] = np.nan
                 pool[ids] = vals
                 sc[ids] = svals
+            elif cfg.mxfp4:
+                vals = rng.integers(0, 256, (nfill, H_kv, bs, D // 2), dtype=np.uint8)
+                svals = rng.integers(127 - 5, 127, (nfill, H_kv, bs, D // 32), dtype=np.uint8)
+                if rem:
+                    vals[-1, :, rem:, :] = 0x77
+                    svals[-1, :, rem:, :] = 0xFF
+                pool[ids] = vals
+                sc[ids] = svals
             else:
                 vals = cfg.kv_std * rng.standard_normal((nfill, H_kv, bs, D), dtype=np.float32)
                 vals = to_storage(vals, cfg.dtype)
@@ -267,10 +294,10 @@ def make_workload(cfg: Config, seed: Optional[int] = None, *, append: Optional[b
                     vals[-1, :, rem:, :] = poison
                 pool[ids] = vals
         pools.append(pool)
-        if cfg.fp8:
+        if cfg.fp8 or cfg.mxfp4:
             scales.append(sc)
     k_pool, v_pool = pools
-    k_scale, v_scale = scales if cfg.fp8 else (None, None)
+    k_scale, v_scale = scales if (cfg.fp8 or cfg.mxfp4) else (None, None)
 
     k_new = v_new = positions = None
     if append:
@@ -302,8 +329,13 @@ def step_bytes(cfg: Config, context_lens: np.ndarray, append: bool) -> dict:
     not algorithmic bytes.
     """
     e = DTYPE_BYTES[cfg.dtype]
-    # an FP8 row is D one-byte codes plus its 4-byte scale
-    row = 2.0 * cfg.H_kv * (cfg.D + 4) if cfg.fp8 else kv_bytes_per_token(cfg.H_kv, cfg.D, e)
+    # an FP8 row is D one-byte codes plus its 4-byte scale; an MXFP4 row D/2 code bytes plus D/32 scale bytes
+    if cfg.fp8:
+        row = 2.0 * cfg.H_kv * (cfg.D + 4)
+    elif cfg.mxfp4:
+        row = 2.0 * cfg.H_kv * (cfg.D // 2 + cfg.D // 32)
+    else:
+        row = kv_bytes_per_token(cfg.H_kv, cfg.D, e)
     ctx = np.asarray(context_lens, dtype=np.int64)
     B = ctx.size
     hist = ctx - 1 if append else ctx

@@ -33,7 +33,7 @@ def upload(w, device="cuda"):
     """All buffers of a Workload as device tensors, in a dict."""
     import torch
     d = w.cfg.dtype
-    if w.cfg.fp8:
+    if w.cfg.fp8 or getattr(w.cfg, "mxfp4", False):
         pools = {"k_pool": torch.from_numpy(np.ascontiguousarray(w.k_pool)).to(device),
                  "v_pool": torch.from_numpy(np.ascontiguousarray(w.v_pool)).to(device),
                  "k_scale": torch.from_numpy(np.ascontiguousarray(w.k_scale)).to(device),
