@@ -69,7 +69,12 @@ def workload_label(cfg, step_desc):
         ctx = "ctx {" + ",".join(map(str, lens[1])) + "}"
     else:
         ctx = f"ctx {lens[0]}[{lens[1]},{lens[2]}]"
-    kv = f"{cfg.dtype} q, fp8 e4m3 K/V (per-row scales)" if getattr(cfg, "fp8", False) else cfg.dtype
+    if getattr(cfg, "fp8", False):
+        kv = f"{cfg.dtype} q, fp8 e4m3 K/V (per-row scales)"
+    elif getattr(cfg, "mxfp4", False):
+        kv = f"{cfg.dtype} q, mxfp4 e2m1 K/V (e8m0 scale per 32)"
+    else:
+        kv = cfg.dtype
     return (f"{cfg.name}: B{cfg.B} Hq{cfg.H_q}/Hkv{cfg.H_kv} D{cfg.D} {kv} bs{cfg.block_size} {ctx}, "
             f"{step_desc}")
 
@@ -120,13 +125,20 @@ def cpu_baseline(w, step_bytes_total: float, kv_tokens: int, budget_s: float = 1
     used = oracle.threads(threads)
     kp, vp = w.k_pool.copy(), w.v_pool.copy()
     fp8 = getattr(w.cfg, "fp8", False)
-    if fp8:
+    mx4 = getattr(w.cfg, "mxfp4", False)
+    if fp8 or mx4:
         ks, vs = w.k_scale.copy(), w.v_scale.copy()
     times = []
     t_end = time.perf_counter() + budget_s
     while True:
         t0 = time.perf_counter()
-        if fp8:
+        if mx4:
+            if w.positions is not None:
+                oracle.kv_append_mxfp4(w.cfg.dtype, w.k_new, w.v_new, kp, vp, ks, vs, w.block_tables, w.positions,
+                                       w.cfg.block_size)
+            oracle.paged_decode_attention_mxfp4(w.cfg.dtype, w.q, kp, vp, ks, vs, w.block_tables, w.context_lens,
+                                                w.scale, nthreads=used)
+        elif fp8:
             if w.positions is not None:
                 oracle.kv_append_fp8(w.cfg.dtype, w.k_new, w.v_new, kp, vp, ks, vs, w.block_tables, w.positions,
                                      w.cfg.block_size)
@@ -171,21 +183,23 @@ def resident_steps(lib, torch, pkv, dev, w, append: bool, P: int, R: int):
     for s in sets:
         s["out"] = torch.empty((B, H_q, D), dtype=torch.float32, device=dev)
         s["ws"] = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-        if cfg.fp8:
+        if cfg.fp8 or cfg.mxfp4:
             scales = (P_(s["k_scale"].data_ptr()), P_(s["v_scale"].data_ptr()))
+            fa = lib.pkv_append_decode_attention_mxfp4 if cfg.mxfp4 else lib.pkv_append_decode_attention_fp8
+            fd = lib.pkv_paged_decode_attention_mxfp4 if cfg.mxfp4 else lib.pkv_paged_decode_attention_fp8
             if append:
                 a = (dt, P_(s["out"].data_ptr()), P_(s["q"].data_ptr()), H_q * D, P_(s["k_new"].data_ptr()),
                      P_(s["v_new"].data_ptr()), H_kv * D, P_(s["k_pool"].data_ptr()), P_(s["v_pool"].data_ptr()),
                      *scales, P_(s["block_tables"].data_ptr()), w.block_tables.shape[1],
                      P_(s["positions"].data_ptr()), B, H_q, H_kv, D, bs, w.n_blocks, max_ctx,
                      ctypes.c_float(float(w.scale)), P, P_(s["ws"].data_ptr()), ws_bytes)
-                calls.append((lib.pkv_append_decode_attention_fp8, a))
+                calls.append((fa, a))
             else:
                 a = (dt, P_(s["out"].data_ptr()), P_(s["q"].data_ptr()), H_q * D, P_(s["k_pool"].data_ptr()),
                      P_(s["v_pool"].data_ptr()), *scales, P_(s["block_tables"].data_ptr()),
                      w.block_tables.shape[1], P_(s["context_lens"].data_ptr()), B, H_q, H_kv, D, bs, w.n_blocks,
                      max_ctx, ctypes.c_float(float(w.scale)), P, P_(s["ws"].data_ptr()), ws_bytes)
-                calls.append((lib.pkv_paged_decode_attention_fp8, a))
+                calls.append((fd, a))
             continue
         if append:
             a = (dt, P_(s["out"].data_ptr()), P_(s["q"].data_ptr()), H_q * D, P_(s["k_new"].data_ptr()),
@@ -266,7 +280,7 @@ def cufrac_bench(args, torch, pkv, dev, lib) -> int:
     from workloads import get_config, make_workload, step_bytes
 
     cfg = get_config(args.config)
-    if cfg.fp8 or cfg.H_q != cfg.H_kv or cfg.dtype == "f32":
+    if cfg.fp8 or cfg.mxfp4 or cfg.H_q != cfg.H_kv or cfg.dtype == "f32":
         print(json.dumps({"mode": "cufrac", "error": f"{args.config}: the persistent step takes f16/bf16 with "
                                                      "one query head per KV head (c2, c3, c4)"}))
         return 2
@@ -550,7 +564,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "c3f8", "c5f8"])
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "c3f8", "c5f8", "c3f4"])
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--partition", type=int, default=None, help="split-KV partition size (default: the workload's)")
     ap.add_argument("--no-append", action="store_true", help="attention only (no kv_append in the step)")
@@ -687,7 +701,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3" if cfg.fp8 else cfg.dtype,
+        "dtype": "fp8_e4m3" if cfg.fp8 else ("mxfp4_e2m1" if cfg.mxfp4 else cfg.dtype),
         "data": "synthetic",
         "config": {
             "workload": workload_label(cfg, "kv_append + paged decode attention (fused)" if append

@@ -100,8 +100,8 @@ const char* pkv_last_error(void);
  * can be overridden per process with environment variables read at each call:
  * PKV_MHA_{NW,CH,PF} (per-head 16-bit), PKV_GQA_{KIND,NW,CH,PF} (grouped 16-bit;
  * KIND 0 = K in registers, 1 = K and V through LDS, 2 = K through LDS),
- * PKV_FP8_{NW,CH,PF} (per-head FP8) and PKV_GQA8_{NW,CH,PF,WPE,KDMA} (grouped
- * FP8).  A combination the library does not instantiate falls back to the
+ * PKV_FP8_{NW,CH,PF} (per-head FP8), PKV_GQA8_{NW,CH,PF,WPE,KDMA} (grouped
+ * FP8) and PKV_MX4_{NW,CH} (MXFP4).  A combination the library does not instantiate falls back to the
  * default; results agree to the same tolerance for every instantiated shape. */
 const char* pkv_last_launch(void);
 
@@ -315,6 +315,71 @@ int pkv_append_decode_attention_fp8(int q_dtype,
                                     int32_t max_context_len, float scale, int32_t partition_size,
                                     void* workspace, size_t workspace_bytes,
                                     void* stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * MXFP4 K/V cache
+ * ---------------------------------------------------------------------------
+ * The same page's 4-bit cache with fine-grained block scales, in the OCP
+ * microscaling format MXFP4 (OCP MX specification v1.0: blocks of 32 elements
+ * share one E8M0 scale): a quarter of the f16/bf16 bytes plus one scale byte per
+ * 32 elements.
+ *   k_pool, v_pool   : [n_blocks][H_kv][block_size][D/2] uint8, E2M1 codes two
+ *                      per byte (element 2k in the low nibble of byte k;
+ *                      magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6, sign in bit 3)
+ *   k_scale, v_scale : [n_blocks][H_kv][block_size][D/32] uint8, E8M0 scale of
+ *                      each 32-element block of a row (value 2^(s - 127),
+ *                      s = 255 is NaN)
+ * Quantizing a block of 32 values x: E = floor(log2 max|x|) - 2 clamped to
+ * [-127, 127] (-127 for an all-zero block), s = E + 127, code = nearest E2M1
+ * value to x / 2^E (ties to the even code, magnitudes above 6 saturating, sign
+ * kept); its value is code * 2^E (exact in float32).  Each row is quantized on
+ * its own when it is appended.  Non-finite new K/V values are outside the
+ * contract.  q, k_new and v_new keep their own dtype (PKV_F32, PKV_F16 or
+ * PKV_BF16); out is float32.  Pools 16-byte aligned; D in {64, 128}; other
+ * rules as the calls above.  Attention runs per query head (with grouped heads
+ * each KV head is read once per query head); the fused call quantizes the new
+ * rows in a launch of its own before attention.
+ */
+
+/* Quantize each request's new K/V rows into slot positions[b] of its block. */
+int pkv_kv_append_mxfp4(int src_dtype,
+                        const void* k_new, const void* v_new, int64_t new_row_stride,
+                        uint8_t* k_pool, uint8_t* v_pool, uint8_t* k_scale, uint8_t* v_scale,
+                        const int32_t* block_tables, int32_t bt_stride,
+                        const int32_t* positions,
+                        int32_t B, int32_t H_kv, int32_t D,
+                        int32_t block_size, int32_t n_blocks,
+                        void* stream);
+
+/* pkv_paged_decode_attention over MXFP4 pools (same arguments and workspace rule). */
+int pkv_paged_decode_attention_mxfp4(int q_dtype,
+                                     float* out,
+                                     const void* q, int64_t q_row_stride,
+                                     const uint8_t* k_pool, const uint8_t* v_pool,
+                                     const uint8_t* k_scale, const uint8_t* v_scale,
+                                     const int32_t* block_tables, int32_t bt_stride,
+                                     const int32_t* context_lens,
+                                     int32_t B, int32_t H_q, int32_t H_kv, int32_t D,
+                                     int32_t block_size, int32_t n_blocks,
+                                     int32_t max_context_len, float scale, int32_t partition_size,
+                                     void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
+/* pkv_append_decode_attention over MXFP4 pools: the new rows (q_dtype) are
+ * quantized and written with their scales, then attended to as stored. */
+int pkv_append_decode_attention_mxfp4(int q_dtype,
+                                      float* out,
+                                      const void* q, int64_t q_row_stride,
+                                      const void* k_new, const void* v_new, int64_t new_row_stride,
+                                      uint8_t* k_pool, uint8_t* v_pool, uint8_t* k_scale, uint8_t* v_scale,
+                                      const int32_t* block_tables, int32_t bt_stride,
+                                      const int32_t* positions,
+                                      int32_t B, int32_t H_q, int32_t H_kv, int32_t D,
+                                      int32_t block_size, int32_t n_blocks,
+                                      int32_t max_context_len, float scale, int32_t partition_size,
+                                      void* workspace, size_t workspace_bytes,
+                                      void* stream);
 
 /*
  * ---------------------------------------------------------------------------

@@ -31,6 +31,7 @@ __all__ = [
     "PKV_F32", "PKV_F16", "PKV_BF16", "EXPORTED_SYMBOLS", "copy_blocks", "BlockManager", "StepGraphs", "Decoder", "cu_mask", "CuMaskedStream",
     "kv_append_fp8", "paged_decode_attention_fp8", "append_decode_attention_fp8", "copy_blocks_fp8",
     "device_cu_count", "append_decode_attention_persistent",
+    "kv_append_mxfp4", "paged_decode_attention_mxfp4", "append_decode_attention_mxfp4",
     "PKV_ERR_OUT_OF_BLOCKS", "PKV_ERR_SEQUENCE",
 ]
 
@@ -46,7 +47,8 @@ EXPORTED_SYMBOLS = (
     "pkv_decode_workspace_bytes", "pkv_paged_decode_attention", "pkv_append_decode_attention",
     "pkv_append_decode_attention_persistent", "pkv_probe_mfma_burn",
     "pkv_probe_stream_read", "pkv_copy_blocks", "pkv_copy_blocks_fp8", "pkv_kv_append_fp8", "pkv_paged_decode_attention_fp8",
-    "pkv_append_decode_attention_fp8",
+    "pkv_append_decode_attention_fp8", "pkv_kv_append_mxfp4", "pkv_paged_decode_attention_mxfp4",
+    "pkv_append_decode_attention_mxfp4",
     "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add_sequence", "pkv_bm_add_sequence_shared", "pkv_bm_fork",
     "pkv_bm_append_token", "pkv_bm_append_batch", "pkv_bm_free_sequence", "pkv_bm_num_free_blocks",
     "pkv_bm_num_sequences", "pkv_bm_sequence_length", "pkv_bm_block_refcount", "pkv_bm_block_table",
@@ -144,6 +146,16 @@ def load_library(path: Optional[str] = None):
                                                     I32, I32, I32, I32, I32, I32, I32, ctypes.c_float, I32,
                                                     P, SZ, P]
     lib.pkv_append_decode_attention_fp8.restype = ctypes.c_int
+    lib.pkv_kv_append_mxfp4.argtypes = [ctypes.c_int, P, P, I64, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, P]
+    lib.pkv_kv_append_mxfp4.restype = ctypes.c_int
+    lib.pkv_paged_decode_attention_mxfp4.argtypes = [ctypes.c_int, P, P, I64, P, P, P, P, P, I32, P,
+                                                     I32, I32, I32, I32, I32, I32, I32, ctypes.c_float, I32,
+                                                     P, SZ, P]
+    lib.pkv_paged_decode_attention_mxfp4.restype = ctypes.c_int
+    lib.pkv_append_decode_attention_mxfp4.argtypes = [ctypes.c_int, P, P, I64, P, P, I64, P, P, P, P, P, I32, P,
+                                                      I32, I32, I32, I32, I32, I32, I32, ctypes.c_float, I32,
+                                                      P, SZ, P]
+    lib.pkv_append_decode_attention_mxfp4.restype = ctypes.c_int
     lib.pkv_copy_blocks_fp8.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, P]
     lib.pkv_copy_blocks_fp8.restype = ctypes.c_int
     lib.pkv_copy_blocks.argtypes = [ctypes.c_int, P, P, P, P, I32, I32, I32, I32, I32, P]
@@ -830,3 +842,83 @@ def copy_blocks_fp8(k_pool, v_pool, k_scale, v_scale, src, dst, *, stream=None):
     rc = load_library().pkv_copy_blocks_fp8(_ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(src),
                                             _ptr(dst), n, H_kv, D, bs, n_blocks, _stream(stream))
     _check(rc, "copy_blocks_fp8")
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 K/V cache: E2M1 codes two per byte plus one E8M0 scale byte per 32 elements
+# ---------------------------------------------------------------------------
+
+def _mx4_pools(k_pool, v_pool, k_scale, v_scale):
+    """(n_blocks, H_kv, block_size, D) of MXFP4 pools: codes [.., D/2] and scales [.., D/32], all uint8."""
+    torch = _torch()
+    _require(k_pool.dtype == torch.uint8 and v_pool.dtype == torch.uint8, "MXFP4 pools are uint8 code bytes")
+    n_blocks, H_kv, bs, half = _pool_dims(k_pool, v_pool)
+    D = 2 * half
+    for t, nm in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        _require(t.dtype == torch.uint8 and t.is_contiguous() and tuple(t.shape) == (n_blocks, H_kv, bs, D // 32),
+                 f"{nm} must be contiguous uint8 [n_blocks, H_kv, block_size, D/32]")
+    return n_blocks, H_kv, bs, D
+
+
+def kv_append_mxfp4(k_new, v_new, k_pool, v_pool, k_scale, v_scale, block_tables, positions, *, stream=None):
+    """Quantize k_new/v_new [B, H_kv, D] (f32/f16/bf16) to MXFP4 into slot positions[b] of each request's block."""
+    n_blocks, H_kv, bs, D = _mx4_pools(k_pool, v_pool, k_scale, v_scale)
+    B = k_new.shape[0]
+    _require(v_new.dtype == k_new.dtype, "k_new and v_new dtypes differ")
+    rs = _rows(k_new, "k_new", H_kv, D)
+    _require(_rows(v_new, "v_new", H_kv, D) == rs, "k_new and v_new must share a row stride")
+    bts = _int32_2d(block_tables, "block_tables")
+    _int32_1d(positions, "positions", B)
+    rc = load_library().pkv_kv_append_mxfp4(_dtype_code(k_new), _ptr(k_new), _ptr(v_new), rs, _ptr(k_pool),
+                                            _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), bts,
+                                            _ptr(positions), B, H_kv, D, bs, n_blocks, _stream(stream))
+    _check(rc, "kv_append_mxfp4")
+
+
+def paged_decode_attention_mxfp4(q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens, scale: float,
+                                 max_context_len: int, *, partition_size: int = 0, out=None, workspace=None,
+                                 stream=None):
+    """paged_decode_attention over MXFP4 pools; q in f32/f16/bf16, output float32."""
+    torch = _torch()
+    n_blocks, H_kv, bs, D = _mx4_pools(k_pool, v_pool, k_scale, v_scale)
+    B, H_q = q.shape[0], q.shape[1]
+    qrs = _rows(q, "q", H_q, D)
+    bts = _int32_2d(block_tables, "block_tables")
+    _int32_1d(context_lens, "context_lens", B)
+    if out is None:
+        out = torch.empty((B, H_q, D), dtype=torch.float32, device=q.device)
+    _require(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, H_q, D),
+             "out must be contiguous float32 [B, H_q, D]")
+    ws, ws_bytes = _workspace(B, H_q, D, max_context_len, partition_size, workspace, q.device)
+    rc = load_library().pkv_paged_decode_attention_mxfp4(
+        _dtype_code(q), _ptr(out), _ptr(q), qrs, _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_tables), bts, _ptr(context_lens), B, H_q, H_kv, D, bs, n_blocks, int(max_context_len),
+        float(scale), int(partition_size), _ptr(ws), ws_bytes, _stream(stream))
+    _check(rc, "paged_decode_attention_mxfp4")
+    return out
+
+
+def append_decode_attention_mxfp4(q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, block_tables, positions,
+                                  scale: float, max_context_len: int, *, partition_size: int = 0, out=None,
+                                  workspace=None, stream=None):
+    """One decode step over MXFP4 pools: quantize and write the new rows, attend over positions[b] + 1 tokens."""
+    torch = _torch()
+    n_blocks, H_kv, bs, D = _mx4_pools(k_pool, v_pool, k_scale, v_scale)
+    B, H_q = q.shape[0], q.shape[1]
+    _require(k_new.dtype == q.dtype and v_new.dtype == q.dtype, "k_new/v_new dtype must match q")
+    qrs = _rows(q, "q", H_q, D)
+    nrs = _rows(k_new, "k_new", H_kv, D)
+    _require(_rows(v_new, "v_new", H_kv, D) == nrs, "k_new and v_new must share a row stride")
+    bts = _int32_2d(block_tables, "block_tables")
+    _int32_1d(positions, "positions", B)
+    if out is None:
+        out = torch.empty((B, H_q, D), dtype=torch.float32, device=q.device)
+    _require(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, H_q, D),
+             "out must be contiguous float32 [B, H_q, D]")
+    ws, ws_bytes = _workspace(B, H_q, D, max_context_len, partition_size, workspace, q.device)
+    rc = load_library().pkv_append_decode_attention_mxfp4(
+        _dtype_code(q), _ptr(out), _ptr(q), qrs, _ptr(k_new), _ptr(v_new), nrs, _ptr(k_pool), _ptr(v_pool),
+        _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), bts, _ptr(positions), B, H_q, H_kv, D, bs, n_blocks,
+        int(max_context_len), float(scale), int(partition_size), _ptr(ws), ws_bytes, _stream(stream))
+    _check(rc, "append_decode_attention_mxfp4")
+    return out

@@ -183,13 +183,20 @@ struct Fp8Scales {
     float* v_w;
 };
 
+struct Mx4Scales {   // E8M0 scale bytes of MXFP4 pools
+    const uint8_t* k;
+    const uint8_t* v;
+    uint8_t* k_w;
+    uint8_t* v_w;
+};
+
 int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride, const void* k_new, const void* v_new,
                      int64_t new_row_stride, const void* k_pool, const void* v_pool, void* k_pool_w, void* v_pool_w,
                      const int32_t* block_tables, int32_t bt_stride, const int32_t* context_lens,
                      const int32_t* positions, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t block_size,
                      int32_t n_blocks, int32_t max_ctx, float scale, int32_t partition_size, void* workspace,
                      size_t workspace_bytes, void* stream, const Fp8Scales* fp8 = nullptr,
-                     int32_t persistent_wgs = 0) {
+                     int32_t persistent_wgs = 0, const Mx4Scales* mx4 = nullptr) {
     const bool fused = positions != nullptr;
     int st = check_common(dtype, B, H_q, H_kv, D, block_size, n_blocks, bt_stride, max_ctx, partition_size);
     if (st) return st;
@@ -208,8 +215,17 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
         if ((reinterpret_cast<uintptr_t>(fp8->k) | reinterpret_cast<uintptr_t>(fp8->v)) & 3u)
             return fail(PKV_ERR_INVALID_ARG, "k_scale and v_scale must be 4-byte aligned");
     }
+    if (mx4 && (!mx4->k || !mx4->v)) return fail(PKV_ERR_NULL, "k_scale and v_scale must not be NULL");
 
-    const Plan p = make_plan(dtype, B, H_q, H_kv, D, max_ctx, partition_size, fp8 != nullptr);
+    Plan p = make_plan(dtype, B, H_q, H_kv, D, max_ctx, partition_size, fp8 != nullptr);
+    if (mx4) {   // per query head (a KV head read once per query head when grouped)
+        p.grouped = false;
+        p.nw = env_int("PKV_MX4_NW", 4);
+        p.ch = env_int("PKV_MX4_CH", 2);
+        p.pf = 1;
+        if (!pkv::mxfp4_variant_exists(p.nw, p.ch)) { p.nw = 4; p.ch = 2; }
+        p.grid = (unsigned)((int64_t)p.n_parts * B * H_q);
+    }
     if ((int64_t)p.n_parts * B * (p.grouped ? H_kv : H_q) > 0x7fffffff)
         return fail(PKV_ERR_INVALID_ARG, "grid too large");
     if (persistent_wgs && (fp8 || p.grouped || (dtype != PKV_F16 && dtype != PKV_BF16)))
@@ -254,10 +270,35 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
         a.k_scale_w = fp8->k_w;
         a.v_scale_w = fp8->v_w;
     }
+    if (mx4) {
+        a.k_mx_scale = mx4->k;
+        a.v_mx_scale = mx4->v;
+    }
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
-    if (fp8 && p.grouped) {
+    if (mx4) {
+        // the attention kernel reads the new row from the pool: quantize it there first
+        if (fused) {
+            pkv::AppendMx4Args ap{};
+            ap.k_new = a.k_new;
+            ap.v_new = a.v_new;
+            ap.k_pool = reinterpret_cast<uint8_t*>(k_pool_w);
+            ap.v_pool = reinterpret_cast<uint8_t*>(v_pool_w);
+            ap.k_scale = mx4->k_w;
+            ap.v_scale = mx4->v_w;
+            ap.block_tables = block_tables;
+            ap.positions = positions;
+            ap.new_row_stride = new_row_stride;
+            ap.bt_stride = bt_stride;
+            ap.B = B;
+            ap.H_kv = H_kv;
+            ap.n_blocks = n_blocks;
+            e = pkv::launch_kv_append_mxfp4(dtype, D, ap, s);
+            if (e != hipSuccess) return fail(PKV_ERR_HIP, "kv_append_mxfp4 launch: %s", hipGetErrorString(e));
+        }
+        e = pkv::launch_decode_mxfp4(dtype, D, p.nw, p.ch, a, p.grid, s);
+    } else if (fp8 && p.grouped) {
         // the grouped FP8 kernel reads the new row from the pool: quantize it there first
         if (fused) {
             pkv::AppendFp8Args ap{};
@@ -304,7 +345,10 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
         e = pkv::launch_lse_merge(D, m, s);
         if (e != hipSuccess) return fail(PKV_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
     }
-    if (persistent_wgs) {
+    if (mx4) {
+        snprintf(g_launch, sizeof g_launch, "mxfp4 dtype=%d D=%d nw=%d ch=%d pf=1 grid=%u part_tokens=%d n_parts=%d%s",
+                 dtype, D, p.nw, p.ch, p.grid, p.part_tokens, p.n_parts, fused ? " fused_append" : "");
+    } else if (persistent_wgs) {
         snprintf(g_launch, sizeof g_launch,
                  "mha_persistent dtype=%d D=%d nw=16 ch=%d pf=1 grid=%u units=%u part_tokens=%d n_parts=%d%s", dtype, D,
                  (dtype == PKV_BF16 && D == 128) ? 1 : 2, std::min<unsigned>(p.grid, (unsigned)persistent_wgs), p.grid,
@@ -455,6 +499,78 @@ int pkv_append_decode_attention_fp8(int q_dtype, float* out, const void* q, int6
                             v_pool, block_tables, bt_stride, nullptr, B > 0 ? positions : nullptr, B, H_q, H_kv, D,
                             block_size, n_blocks, max_context_len, scale, partition_size, workspace,
                             workspace_bytes, stream, &sc);
+}
+
+int pkv_kv_append_mxfp4(int src_dtype, const void* k_new, const void* v_new, int64_t new_row_stride,
+                        uint8_t* k_pool, uint8_t* v_pool, uint8_t* k_scale, uint8_t* v_scale,
+                        const int32_t* block_tables, int32_t bt_stride, const int32_t* positions, int32_t B,
+                        int32_t H_kv, int32_t D, int32_t block_size, int32_t n_blocks, void* stream) {
+    const int eb = elem_bytes(src_dtype);
+    if (!eb) return fail(PKV_ERR_UNSUPPORTED, "src_dtype %d is not one of PKV_F32/F16/BF16", src_dtype);
+    if (B < 0) return fail(PKV_ERR_INVALID_ARG, "B = %d is negative", B);
+    if (H_kv <= 0) return fail(PKV_ERR_INVALID_ARG, "H_kv = %d must be positive", H_kv);
+    if (D != 64 && D != 128) return fail(PKV_ERR_UNSUPPORTED, "head dim D = %d (built: 64, 128)", D);
+    if (block_size != pkv::kBlockSize)
+        return fail(PKV_ERR_UNSUPPORTED, "block_size = %d (built: %d)", block_size, pkv::kBlockSize);
+    if (n_blocks <= 0) return fail(PKV_ERR_INVALID_ARG, "n_blocks = %d must be positive", n_blocks);
+    if (bt_stride <= 0) return fail(PKV_ERR_INVALID_ARG, "bt_stride = %d must be positive", bt_stride);
+    if (B == 0) {
+        pkv::clear_error();
+        return PKV_OK;
+    }
+    if (!k_new || !v_new || !k_pool || !v_pool || !k_scale || !v_scale || !block_tables || !positions)
+        return fail(PKV_ERR_NULL, "a required pointer is NULL");
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+        return fail(PKV_ERR_INVALID_ARG, "rows and pools must be 16-byte aligned");
+    int st = check_stride("new_row_stride", new_row_stride, (int64_t)H_kv * D, eb);
+    if (st) return st;
+    pkv::AppendMx4Args a{};
+    a.k_new = reinterpret_cast<const char*>(k_new);
+    a.v_new = reinterpret_cast<const char*>(v_new);
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.block_tables = block_tables;
+    a.positions = positions;
+    a.new_row_stride = new_row_stride;
+    a.bt_stride = bt_stride;
+    a.B = B;
+    a.H_kv = H_kv;
+    a.n_blocks = n_blocks;
+    hipError_t e = pkv::launch_kv_append_mxfp4(src_dtype, D, a, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "kv_append_mxfp4 launch: %s", hipGetErrorString(e));
+    pkv::clear_error();
+    return PKV_OK;
+}
+
+int pkv_paged_decode_attention_mxfp4(int q_dtype, float* out, const void* q, int64_t q_row_stride,
+                                     const uint8_t* k_pool, const uint8_t* v_pool, const uint8_t* k_scale,
+                                     const uint8_t* v_scale, const int32_t* block_tables, int32_t bt_stride,
+                                     const int32_t* context_lens, int32_t B, int32_t H_q, int32_t H_kv, int32_t D,
+                                     int32_t block_size, int32_t n_blocks, int32_t max_context_len, float scale,
+                                     int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+    const Mx4Scales sc{k_scale, v_scale, nullptr, nullptr};
+    return launch_attention(q_dtype, out, q, q_row_stride, nullptr, nullptr, 0, k_pool, v_pool, nullptr, nullptr,
+                            block_tables, bt_stride, context_lens, nullptr, B, H_q, H_kv, D, block_size, n_blocks,
+                            max_context_len, scale, partition_size, workspace, workspace_bytes, stream, nullptr, 0,
+                            &sc);
+}
+
+int pkv_append_decode_attention_mxfp4(int q_dtype, float* out, const void* q, int64_t q_row_stride,
+                                      const void* k_new, const void* v_new, int64_t new_row_stride, uint8_t* k_pool,
+                                      uint8_t* v_pool, uint8_t* k_scale, uint8_t* v_scale,
+                                      const int32_t* block_tables, int32_t bt_stride, const int32_t* positions,
+                                      int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t block_size,
+                                      int32_t n_blocks, int32_t max_context_len, float scale,
+                                      int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+    if (B > 0 && !positions) return fail(PKV_ERR_NULL, "positions is NULL");
+    const Mx4Scales sc{k_scale, v_scale, k_scale, v_scale};
+    return launch_attention(q_dtype, out, q, q_row_stride, k_new, v_new, new_row_stride, k_pool, v_pool, k_pool,
+                            v_pool, block_tables, bt_stride, nullptr, B > 0 ? positions : nullptr, B, H_q, H_kv, D,
+                            block_size, n_blocks, max_context_len, scale, partition_size, workspace,
+                            workspace_bytes, stream, nullptr, 0, &sc);
 }
 
 int pkv_probe_mfma_burn(int32_t n_workgroups, int32_t iterations, void* sink, void* stream) {

@@ -194,6 +194,8 @@ struct AttnArgs {
     const float* v_scale;
     float* k_scale_w;              // same, written by the fused FP8 append
     float* v_scale_w;
+    const uint8_t* k_mx_scale;     // MXFP4 pools only: [n_blocks][H_kv][16][D/32] E8M0 scale bytes
+    const uint8_t* v_mx_scale;
     int64_t q_row_stride;          // elements
     int64_t new_row_stride;        // elements
     int32_t bt_stride;

@@ -57,6 +57,26 @@ struct AppendFp8Args {
     int32_t B, H_kv, n_blocks;
 };
 hipError_t launch_kv_append_fp8(int src_dtype, int D, const AppendFp8Args& a, hipStream_t stream);
+// MXFP4 pools: codes [n_blocks][H_kv][16][D/2] bytes, E8M0 scales [n_blocks][H_kv][16][D/32] bytes
+struct AppendMx4Args {
+    const char* k_new;          // source rows, src dtype
+    const char* v_new;
+    uint8_t* k_pool;
+    uint8_t* v_pool;
+    uint8_t* k_scale;
+    uint8_t* v_scale;
+    const int32_t* block_tables;
+    const int32_t* positions;
+    int64_t new_row_stride;     // elements
+    int32_t bt_stride;
+    int32_t B, H_kv, n_blocks;
+};
+hipError_t launch_kv_append_mxfp4(int src_dtype, int D, const AppendMx4Args& a, hipStream_t stream);
+// per query head over MXFP4 pools (no append inside: lengths from context_lens, or
+// positions + 1 when context_lens is NULL, after the append kernel has run)
+hipError_t launch_decode_mxfp4(int q_dtype, int D, int nw, int ch, const AttnArgs& a, unsigned grid,
+                               hipStream_t stream);
+bool mxfp4_variant_exists(int nw, int ch);
 // per query head; q (and new rows) in q_dtype, K/V codes + scales in the AttnArgs pools
 hipError_t launch_decode_fp8(int q_dtype, int D, int nw, int ch, int pf, bool append, const AttnArgs& a,
                              unsigned grid, hipStream_t stream);

@@ -156,6 +156,41 @@ def test_mfma_burn_validation(lib):
         assert f(n_wg, iters, FAKE, None) == E_ARG
 
 
+def test_mxfp4_validation(lib):
+    ap = lib.pkv_kv_append_mxfp4
+    args = [1, FAKE, FAKE, 8 * 128, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 4, 8, 128, 16, 1024, None]
+    bad = list(args)
+    bad[13] = 96                        # D
+    assert ap(*bad) == E_UNSUP
+    bad = list(args)
+    bad[6] = None                       # k_scale
+    assert ap(*bad) == E_NULL
+    bad = list(args)
+    bad[4] = FAKE + 8                   # k_pool not 16-byte aligned
+    assert ap(*bad) == E_ARG
+    bad = list(args)
+    bad[11] = 0                         # B = 0
+    assert ap(*bad) == OK
+    at = lib.pkv_paged_decode_attention_mxfp4
+    args = [1, FAKE, FAKE, 32 * 128, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 8, 32, 32, 128, 16, 1024, 1024,
+            0.088, 0, None, 0, None]
+    bad = list(args)
+    bad[7] = None                       # v_scale
+    assert at(*bad) == E_NULL
+    bad = list(args)
+    bad[11] = 0                         # B = 0
+    assert at(*bad) == OK
+    f = lib.pkv_append_decode_attention_mxfp4
+    args = [1, FAKE, FAKE, 32 * 128, FAKE, FAKE, 32 * 128, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 8, 32, 32, 128,
+            16, 1024, 1024, 0.088, 0, None, 0, None]
+    bad = list(args)
+    bad[13] = None                      # positions
+    assert f(*bad) == E_NULL
+    bad = list(args)
+    bad[14] = 0                         # B = 0
+    assert f(*bad) == OK
+
+
 def test_binding_refuses_missing_library(tmp_path):
     with pytest.raises(pkv.PkvError):
         pkv.load_library(str(tmp_path / "nope.so"))

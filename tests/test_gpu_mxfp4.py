@@ -1,0 +1,213 @@
+"""GPU parity of the MXFP4 (OCP E2M1 codes, E8M0 block scales) K/V cache through the C ABI.
+
+The quantizing append is compared bit for bit (code and scale bytes, whole
+pools); attention outputs must satisfy the same (atol, rtol) as the f16/bf16
+path ((1e-5, 1e-5) for f32 q): the kernel decodes codes exactly, so only the
+float32 accumulation order separates it from the oracle.  Unwritten slots hold
+code 7 (6.0) under scale byte 255 (NaN in E8M0), so a stray read shows up as a
+non-finite output."""
+import numpy as np
+import pytest
+
+import oracle
+import paged_kv_decode_blocks_amd as pkv
+from tests.test_gpu_decode_loop import bits_equal
+from workloads import get_config, make_workload
+from workloads.device import upload
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-5, 1e-5), "f16": (2e-3, 1e-2), "bf16": (2e-3, 1e-2)}
+EDGE_LENS = (1, 2, 15, 16, 17, 31, 33, 64, 255, 257, 700)
+MX4_VARIANTS = ["4,2", "4,4", "8,2"]
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available()
+    pkv.load_library()
+    return torch
+
+
+def assert_close(got, ref, dtype, what=""):
+    atol, rtol = TOL[dtype]
+    got = np.asarray(got, dtype=np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    rel = err / np.maximum(np.abs(ref), atol / rtol)
+    assert err.max() <= atol and rel.max() <= rtol, f"{what}: max_abs={err.max():.3e} max_rel={rel.max():.3e}"
+
+
+def cfg_for(dtype, D, H_q, H_kv, lens, P=0, append=True):
+    return get_config("c3f4", dtype=dtype, D=D, H_q=H_q, H_kv=H_kv, B=len(lens), lengths=("fixed", tuple(lens)),
+                      pool=("factor", 1.3), append=append, partition_size=P)
+
+
+def run(torch, w, P, append):
+    d = upload(w, "cuda")
+    if append:
+        out = pkv.append_decode_attention_mxfp4(d["q"], d["k_new"], d["v_new"], d["k_pool"], d["v_pool"],
+                                                d["k_scale"], d["v_scale"], d["block_tables"], d["positions"],
+                                                float(w.scale), w.max_context_len, partition_size=P)
+    else:
+        out = pkv.paged_decode_attention_mxfp4(d["q"], d["k_pool"], d["v_pool"], d["k_scale"], d["v_scale"],
+                                               d["block_tables"], d["context_lens"], float(w.scale),
+                                               w.max_context_len, partition_size=P)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), d
+
+
+def pools_equal(d, pk, pv):
+    return (bits_equal(d["k_pool"].cpu().numpy(), pk[0]) and bits_equal(d["k_scale"].cpu().numpy(), pk[1])
+            and bits_equal(d["v_pool"].cpu().numpy(), pv[0]) and bits_equal(d["v_scale"].cpu().numpy(), pv[1]))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_kv_append_mxfp4_bit_exact(torch_dev, dtype, D):
+    t = torch_dev
+    cfg = cfg_for(dtype, D, 8, 4, [5, 16, 17, 40, 1, 33])
+    w = make_workload(cfg, 21)
+    ref = [w.k_pool.copy(), w.v_pool.copy(), w.k_scale.copy(), w.v_scale.copy()]
+    oracle.kv_append_mxfp4(dtype, w.k_new, w.v_new, *ref, w.block_tables, w.positions, 16)
+    d = upload(w, "cuda")
+    pkv.kv_append_mxfp4(d["k_new"], d["v_new"], d["k_pool"], d["v_pool"], d["k_scale"], d["v_scale"],
+                        d["block_tables"], d["positions"])
+    t.cuda.synchronize()
+    for name, r in zip(("k_pool", "v_pool", "k_scale", "v_scale"), ref):
+        assert bits_equal(d[name].cpu().numpy(), r), name
+
+
+def test_kv_append_mxfp4_rounding_cases(torch_dev):
+    """Rows built to land on every E2M1 midpoint (ties to the even code), on the
+    saturation above 6, on an all-zero block, on subnormal and huge maxima and
+    on negative zero, compared bit for bit (f32 source, so no rounding on load)."""
+    t = torch_dev
+    H_kv, D, nb = 4, 64, 8
+    rows = np.zeros((4, H_kv, D), np.float32)
+    # block with amax 4 (E = 0): every midpoint of the grid, both signs, and values that saturate
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    rows[0, 0, :7] = mids
+    rows[0, 0, 7:14] = [-x for x in mids]
+    rows[0, 0, 14:18] = [4.0, 0.2499, 0.7501, -0.0]
+    rows[0, 0, 32:36] = [7.9, 6.5, 5.5, -7.0]                        # amax 7.9: E = 0, 6.5 and 7.9 saturate
+    rows[0, 1, :32] = np.linspace(-3, 3, 32, dtype=np.float32)       # E = -1
+    rows[0, 1, 32:] = 0.0                                            # all-zero block: scale byte 0
+    rows[0, 2, :4] = [2.0 ** -140, -(2.0 ** -145), 2.0 ** -149, 0.0]  # subnormal maximum: E = -127
+    rows[0, 2, 32:35] = [3.0e38, -1.0e38, 2.0e37]                    # E = 125
+    rows[0, 3, :32] = 2.0 ** -126 * np.arange(1, 33, dtype=np.float32)  # smallest normal exponents: clamp at -127
+    rows[1] = np.linspace(-7, 7, H_kv * D, dtype=np.float32).reshape(H_kv, D)
+    rows[2] = (np.arange(H_kv * D, dtype=np.float32).reshape(H_kv, D) % 13 - 6) * 0.125
+    # rows[3] stays zero
+    bt = np.arange(nb, dtype=np.int32).reshape(4, 2)
+    pos = np.array([0, 3, 17, 9], np.int32)
+    kp = np.full((nb, H_kv, 16, D // 2), 0x77, np.uint8)
+    ks = np.full((nb, H_kv, 16, D // 32), 0xFF, np.uint8)
+    ref = [kp.copy(), kp.copy(), ks.copy(), ks.copy()]
+    oracle.kv_append_mxfp4("f32", rows, -rows, *ref, bt, pos, 16)
+    dev = [t.from_numpy(a.copy()).cuda() for a in (kp, kp, ks, ks)]
+    pkv.kv_append_mxfp4(t.from_numpy(rows).cuda(), t.from_numpy(-rows).cuda(), *dev, t.from_numpy(bt).cuda(),
+                        t.from_numpy(pos).cuda())
+    t.cuda.synchronize()
+    for g, r in zip(dev, ref):
+        assert bits_equal(g.cpu().numpy(), r)
+
+
+def test_mxfp4_decode_every_code_and_extreme_scales(torch_dev):
+    """A one-token context returns its dequantized V row bit for bit: rows
+    covering all 16 codes under scale bytes 0 (2^-127), 1, 127, 200 and 254."""
+    t = torch_dev
+    H_kv, D = 2, 64
+    nb = 5
+    kp = np.full((nb, H_kv, 16, D // 2), 0x77, np.uint8)
+    ks = np.full((nb, H_kv, 16, D // 32), 0xFF, np.uint8)
+    vp, vs = kp.copy(), ks.copy()
+    sc_bytes = [0, 1, 127, 200, 254]
+    for b in range(nb):
+        for g in range(H_kv):
+            kp[b, g, 0] = 0                                          # all-zero K: every score equal
+            ks[b, g, 0] = 127
+            codes = np.arange(D // 2, dtype=np.uint8)
+            vp[b, g, 0] = ((codes % 16) | (((codes + 7 * g) % 16) << 4)).astype(np.uint8)
+            vs[b, g, 0] = [sc_bytes[b], sc_bytes[(b + 2 + g) % len(sc_bytes)]]
+    q = np.ones((nb, H_kv, D), np.float32)
+    bt = np.arange(nb, dtype=np.int32).reshape(nb, 1)
+    ctx = np.ones(nb, np.int32)
+    dev = {k: t.from_numpy(v).cuda() for k, v in (("q", q), ("kp", kp), ("vp", vp), ("ks", ks), ("vs", vs),
+                                                    ("bt", bt), ("ctx", ctx))}
+    out = pkv.paged_decode_attention_mxfp4(dev["q"], dev["kp"], dev["vp"], dev["ks"], dev["vs"], dev["bt"],
+                                           dev["ctx"], 0.125, 16)
+    t.cuda.synchronize()
+    got = out.cpu().numpy()
+    want = oracle.mxfp4_dequantize(vp[:, :, 0], vs[:, :, 0])
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("dtype,D,H_q,H_kv", [("f16", 128, 8, 8), ("bf16", 128, 16, 2), ("bf16", 64, 8, 1),
+                                              ("f32", 64, 4, 4), ("f16", 64, 4, 2), ("f32", 128, 2, 1)])
+@pytest.mark.parametrize("P", [0, 32, 256])
+@pytest.mark.parametrize("append", [False, True])
+def test_mxfp4_attention_parity(torch_dev, dtype, D, H_q, H_kv, P, append):
+    cfg = cfg_for(dtype, D, H_q, H_kv, EDGE_LENS, P=P, append=append)
+    w = make_workload(cfg, 31)
+    ref, pk, pv = oracle.run_step(w)
+    got, d = run(torch_dev, w, P, append)
+    assert_close(got, ref, dtype, f"{dtype} D{D} G{H_q // H_kv} P{P} append={append}")
+    if append:
+        assert pools_equal(d, pk, pv)
+
+
+@pytest.mark.parametrize("variant", MX4_VARIANTS)
+def test_mxfp4_every_launch_variant(torch_dev, monkeypatch, variant):
+    nw, ch = variant.split(",")
+    monkeypatch.setenv("PKV_MX4_NW", nw)
+    monkeypatch.setenv("PKV_MX4_CH", ch)
+    # 4500 tokens unsplit: more than one 256-block window of ids per workgroup
+    for dtype, D, P, H_q, H_kv, append in (("f16", 128, 0, 4, 4, True), ("bf16", 64, 64, 8, 2, True),
+                                           ("f32", 128, 256, 4, 2, False)):
+        cfg = cfg_for(dtype, D, H_q, H_kv, (1, 17, 200, 1000, 2049, 4500), P=P, append=append)
+        w = make_workload(cfg, 41)
+        ref, pk, pv = oracle.run_step(w)
+        got, d = run(torch_dev, w, P, append)
+        launch = pkv.last_launch()
+        assert launch.startswith("mxfp4 ") and f"nw={nw} ch={ch} " in launch, launch
+        assert_close(got, ref, dtype, f"variant {variant} {dtype} D{D} P{P}")
+        if append:
+            assert pools_equal(d, pk, pv)
+
+
+def test_mxfp4_bad_metadata_gives_nan_rows(torch_dev):
+    t = torch_dev
+    cfg = cfg_for("f16", 128, 4, 4, (40, 40, 40), append=False)
+    w = make_workload(cfg, 61)
+    w.block_tables[1, 1] = w.n_blocks + 5          # out of range: request 1 gets NaN rows
+    ctx = w.context_lens.copy()
+    ctx[2] = 10 ** 6                                # longer than max_context_len: NaN rows
+    d = upload(w, "cuda")
+    out = pkv.paged_decode_attention_mxfp4(d["q"], d["k_pool"], d["v_pool"], d["k_scale"], d["v_scale"],
+                                           d["block_tables"], t.from_numpy(ctx).cuda(), float(w.scale), 40)
+    t.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(np.isfinite(o[0])) and np.all(np.isnan(o[1])) and np.all(np.isnan(o[2]))
+
+
+def test_mxfp4_full_size_sampled(torch_dev):
+    """The full-size workload in the launch configuration the bench times; a sample of requests
+    is recomputed by the oracle over the pools after the step (their own rows of the batch)."""
+    cfg = get_config("c3f4", append=True)
+    w = make_workload(cfg)
+    got, d = run(torch_dev, w, cfg.partition_size, True)
+    kp, vp = d["k_pool"].cpu().numpy(), d["v_pool"].cpu().numpy()
+    ks, vs = d["k_scale"].cpu().numpy(), d["v_scale"].cpu().numpy()
+    ok, ov, oks, ovs = w.k_pool.copy(), w.v_pool.copy(), w.k_scale.copy(), w.v_scale.copy()
+    oracle.kv_append_mxfp4(cfg.dtype, w.k_new, w.v_new, ok, ov, oks, ovs, w.block_tables, w.positions, 16)
+    assert bits_equal(kp, ok) and bits_equal(vp, ov) and bits_equal(ks, oks) and bits_equal(vs, ovs)
+    rng = np.random.default_rng(3)
+    sample = np.sort(rng.choice(cfg.B, size=4, replace=False))
+    used = np.unique(np.concatenate([w.block_tables[b][w.block_tables[b] >= 0] for b in sample]))
+    remap = {int(x): i for i, x in enumerate(used)}
+    bt = np.array([[remap.get(int(x), -1) for x in w.block_tables[b]] for b in sample], dtype=np.int32)
+    ref = oracle.paged_decode_attention_mxfp4(cfg.dtype, np.ascontiguousarray(w.q[sample]), ok[used], ov[used],
+                                              oks[used], ovs[used], bt, w.context_lens[sample], w.scale)
+    assert_close(got[sample], ref, cfg.dtype, "c3f4")
