@@ -564,7 +564,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "c3f8", "c5f8", "c3f4"])
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "c3f8", "c5f8", "c3f4", "c5f4"])
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--partition", type=int, default=None, help="split-KV partition size (default: the workload's)")
     ap.add_argument("--no-append", action="store_true", help="attention only (no kv_append in the step)")

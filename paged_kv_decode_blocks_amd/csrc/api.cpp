@@ -218,13 +218,27 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
     if (mx4 && (!mx4->k || !mx4->v)) return fail(PKV_ERR_NULL, "k_scale and v_scale must not be NULL");
 
     Plan p = make_plan(dtype, B, H_q, H_kv, D, max_ctx, partition_size, fp8 != nullptr);
-    if (mx4) {   // per query head (a KV head read once per query head when grouped)
-        p.grouped = false;
-        p.nw = env_int("PKV_MX4_NW", 4);
-        p.ch = env_int("PKV_MX4_CH", 2);
+    if (mx4) {
+        // kind 1: one workgroup per KV head and its G <= 16 query heads on MFMA (f16/bf16 q),
+        // reading each K/V block once for the group; kind 0: one workgroup per query head on the
+        // vector units (any q dtype).  With one query head per KV head the MFMA tiles are 1/16
+        // used and kind 0 is faster, so it is the default there.
+        const bool mfma_ok = (dtype == PKV_F16 || dtype == PKV_BF16) && H_q / H_kv <= 16;
+        p.kind = mfma_ok ? env_int("PKV_MX4_KIND", H_q > H_kv ? 1 : 0) : 0;
+        if (p.kind != 0 && p.kind != 1) p.kind = 1;
+        p.grouped = p.kind == 1;
         p.pf = 1;
-        if (!pkv::mxfp4_variant_exists(p.nw, p.ch)) { p.nw = 4; p.ch = 2; }
-        p.grid = (unsigned)((int64_t)p.n_parts * B * H_q);
+        if (p.kind == 1) {
+            p.nw = env_int("PKV_MX4_NW", 4);
+            p.ch = env_int("PKV_MX4_CH", 2);
+            if (!pkv::mxfp4_mfma_variant_exists(p.nw, p.ch)) { p.nw = 4; p.ch = 2; }
+            p.grid = (unsigned)((int64_t)p.n_parts * B * H_kv);
+        } else {
+            p.nw = env_int("PKV_MX4_NW", 4);
+            p.ch = env_int("PKV_MX4_CH", 2);
+            if (!pkv::mxfp4_variant_exists(p.nw, p.ch)) { p.nw = 4; p.ch = 2; }
+            p.grid = (unsigned)((int64_t)p.n_parts * B * H_q);
+        }
     }
     if ((int64_t)p.n_parts * B * (p.grouped ? H_kv : H_q) > 0x7fffffff)
         return fail(PKV_ERR_INVALID_ARG, "grid too large");
@@ -297,7 +311,8 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
             e = pkv::launch_kv_append_mxfp4(dtype, D, ap, s);
             if (e != hipSuccess) return fail(PKV_ERR_HIP, "kv_append_mxfp4 launch: %s", hipGetErrorString(e));
         }
-        e = pkv::launch_decode_mxfp4(dtype, D, p.nw, p.ch, a, p.grid, s);
+        e = p.kind == 1 ? pkv::launch_decode_mxfp4_mfma(dtype, D, p.nw, p.ch, a, p.grid, s)
+                        : pkv::launch_decode_mxfp4(dtype, D, p.nw, p.ch, a, p.grid, s);
     } else if (fp8 && p.grouped) {
         // the grouped FP8 kernel reads the new row from the pool: quantize it there first
         if (fused) {
@@ -346,8 +361,9 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
         if (e != hipSuccess) return fail(PKV_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
     }
     if (mx4) {
-        snprintf(g_launch, sizeof g_launch, "mxfp4 dtype=%d D=%d nw=%d ch=%d pf=1 grid=%u part_tokens=%d n_parts=%d%s",
-                 dtype, D, p.nw, p.ch, p.grid, p.part_tokens, p.n_parts, fused ? " fused_append" : "");
+        snprintf(g_launch, sizeof g_launch, "%s dtype=%d D=%d nw=%d ch=%d pf=1 grid=%u part_tokens=%d n_parts=%d%s",
+                 p.kind == 1 ? "mxfp4_mfma" : "mxfp4", dtype, D, p.nw, p.ch, p.grid, p.part_tokens, p.n_parts,
+                 fused ? " fused_append" : "");
     } else if (persistent_wgs) {
         snprintf(g_launch, sizeof g_launch,
                  "mha_persistent dtype=%d D=%d nw=16 ch=%d pf=1 grid=%u units=%u part_tokens=%d n_parts=%d%s", dtype, D,

@@ -12,14 +12,16 @@ import pytest
 import oracle
 import paged_kv_decode_blocks_amd as pkv
 from tests.test_gpu_decode_loop import bits_equal
-from workloads import get_config, make_workload
-from workloads.device import upload
+from workloads import get_config, make_workload, to_storage
+from workloads.device import to_tensor, upload
 
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": (1e-5, 1e-5), "f16": (2e-3, 1e-2), "bf16": (2e-3, 1e-2)}
 EDGE_LENS = (1, 2, 15, 16, 17, 31, 33, 64, 255, 257, 700)
-MX4_VARIANTS = ["4,2", "4,4", "8,2"]
+# (kernel kind, waves, blocks per chunk): kind 1 = grouped MFMA kernel (f16/bf16 q, G <= 16),
+# kind 0 = per-head vector-unit kernel
+MX4_VARIANTS = ["0,4,2", "0,4,4", "0,8,2", "1,2,1", "1,2,2", "1,4,1", "1,4,2"]
 
 
 @pytest.fixture(scope="module")
@@ -114,38 +116,47 @@ def test_kv_append_mxfp4_rounding_cases(torch_dev):
         assert bits_equal(g.cpu().numpy(), r)
 
 
-def test_mxfp4_decode_every_code_and_extreme_scales(torch_dev):
+@pytest.mark.parametrize("qdt,D", [("f32", 64), ("bf16", 64), ("f16", 128)])
+def test_mxfp4_decode_every_code_and_extreme_scales(torch_dev, monkeypatch, qdt, D):
     """A one-token context returns its dequantized V row bit for bit: rows
-    covering all 16 codes under scale bytes 0 (2^-127), 1, 127, 200 and 254."""
+    covering all 16 codes under scale bytes 0 (2^-127), 1, 127, 200 and 252 (254
+    for the vector-unit kernel, whose products overflow to inf as f32 does; the
+    MFMA kernel's p = hi + lo form turns an infinite V element into NaN, and the
+    quantizing append never writes a scale above 252).  f32 q takes the per-head
+    kernel, f16/bf16 q the grouped MFMA kernel."""
     t = torch_dev
-    H_kv, D = 2, 64
+    monkeypatch.setenv("PKV_MX4_KIND", "0" if qdt == "f32" else "1")
+    H_kv = 2
     nb = 5
     kp = np.full((nb, H_kv, 16, D // 2), 0x77, np.uint8)
     ks = np.full((nb, H_kv, 16, D // 32), 0xFF, np.uint8)
     vp, vs = kp.copy(), ks.copy()
-    sc_bytes = [0, 1, 127, 200, 254]
+    sc_bytes = [0, 1, 127, 200, 254 if qdt == "f32" else 252]
     for b in range(nb):
         for g in range(H_kv):
             kp[b, g, 0] = 0                                          # all-zero K: every score equal
             ks[b, g, 0] = 127
             codes = np.arange(D // 2, dtype=np.uint8)
             vp[b, g, 0] = ((codes % 16) | (((codes + 7 * g) % 16) << 4)).astype(np.uint8)
-            vs[b, g, 0] = [sc_bytes[b], sc_bytes[(b + 2 + g) % len(sc_bytes)]]
-    q = np.ones((nb, H_kv, D), np.float32)
+            vs[b, g, 0] = [sc_bytes[(b + k * (2 + g)) % len(sc_bytes)] for k in range(D // 32)]
+    q = to_storage(np.ones((nb, H_kv, D), np.float32), qdt)
     bt = np.arange(nb, dtype=np.int32).reshape(nb, 1)
     ctx = np.ones(nb, np.int32)
-    dev = {k: t.from_numpy(v).cuda() for k, v in (("q", q), ("kp", kp), ("vp", vp), ("ks", ks), ("vs", vs),
-                                                    ("bt", bt), ("ctx", ctx))}
+    dev = {k: t.from_numpy(v).cuda() for k, v in (("kp", kp), ("vp", vp), ("ks", ks), ("vs", vs), ("bt", bt),
+                                                    ("ctx", ctx))}
+    dev["q"] = to_tensor(q, qdt, "cuda")
     out = pkv.paged_decode_attention_mxfp4(dev["q"], dev["kp"], dev["vp"], dev["ks"], dev["vs"], dev["bt"],
                                            dev["ctx"], 0.125, 16)
     t.cuda.synchronize()
     got = out.cpu().numpy()
     want = oracle.mxfp4_dequantize(vp[:, :, 0], vs[:, :, 0])
+    assert pkv.last_launch().startswith("mxfp4 " if qdt == "f32" else "mxfp4_mfma "), pkv.last_launch()
     assert np.array_equal(got, want)
 
 
 @pytest.mark.parametrize("dtype,D,H_q,H_kv", [("f16", 128, 8, 8), ("bf16", 128, 16, 2), ("bf16", 64, 8, 1),
-                                              ("f32", 64, 4, 4), ("f16", 64, 4, 2), ("f32", 128, 2, 1)])
+                                              ("f32", 64, 4, 4), ("f16", 64, 4, 2), ("f32", 128, 2, 1),
+                                              ("f16", 128, 16, 1), ("f16", 64, 12, 4)])
 @pytest.mark.parametrize("P", [0, 32, 256])
 @pytest.mark.parametrize("append", [False, True])
 def test_mxfp4_attention_parity(torch_dev, dtype, D, H_q, H_kv, P, append):
@@ -156,22 +167,30 @@ def test_mxfp4_attention_parity(torch_dev, dtype, D, H_q, H_kv, P, append):
     assert_close(got, ref, dtype, f"{dtype} D{D} G{H_q // H_kv} P{P} append={append}")
     if append:
         assert pools_equal(d, pk, pv)
+    # f16/bf16 q with grouped heads takes the MFMA kernel, f32 q and one head per KV head the per-head one
+    mfma = dtype != "f32" and H_q // H_kv > 1
+    assert pkv.last_launch().startswith("mxfp4_mfma " if mfma else "mxfp4 "), pkv.last_launch()
 
 
 @pytest.mark.parametrize("variant", MX4_VARIANTS)
 def test_mxfp4_every_launch_variant(torch_dev, monkeypatch, variant):
-    nw, ch = variant.split(",")
+    kind, nw, ch = variant.split(",")
+    monkeypatch.setenv("PKV_MX4_KIND", kind)
     monkeypatch.setenv("PKV_MX4_NW", nw)
     monkeypatch.setenv("PKV_MX4_CH", ch)
+    name = "mxfp4_mfma " if kind == "1" else "mxfp4 "
     # 4500 tokens unsplit: more than one 256-block window of ids per workgroup
-    for dtype, D, P, H_q, H_kv, append in (("f16", 128, 0, 4, 4, True), ("bf16", 64, 64, 8, 2, True),
-                                           ("f32", 128, 256, 4, 2, False)):
+    cases = [("f16", 128, 0, 4, 4, True), ("bf16", 64, 64, 8, 2, True), ("bf16", 128, 256, 16, 1, False),
+             ("f16", 64, 0, 6, 2, False)]
+    if kind == "0":
+        cases.append(("f32", 128, 256, 4, 2, False))
+    for dtype, D, P, H_q, H_kv, append in cases:
         cfg = cfg_for(dtype, D, H_q, H_kv, (1, 17, 200, 1000, 2049, 4500), P=P, append=append)
         w = make_workload(cfg, 41)
         ref, pk, pv = oracle.run_step(w)
         got, d = run(torch_dev, w, P, append)
         launch = pkv.last_launch()
-        assert launch.startswith("mxfp4 ") and f"nw={nw} ch={ch} " in launch, launch
+        assert launch.startswith(name) and f"nw={nw} ch={ch} " in launch, launch
         assert_close(got, ref, dtype, f"variant {variant} {dtype} D{D} P{P}")
         if append:
             assert pools_equal(d, pk, pv)
@@ -192,10 +211,11 @@ def test_mxfp4_bad_metadata_gives_nan_rows(torch_dev):
     assert np.all(np.isfinite(o[0])) and np.all(np.isnan(o[1])) and np.all(np.isnan(o[2]))
 
 
-def test_mxfp4_full_size_sampled(torch_dev):
+@pytest.mark.parametrize("name", ["c3f4", "c5f4"])
+def test_mxfp4_full_size_sampled(torch_dev, name):
     """The full-size workload in the launch configuration the bench times; a sample of requests
     is recomputed by the oracle over the pools after the step (their own rows of the batch)."""
-    cfg = get_config("c3f4", append=True)
+    cfg = get_config(name, append=True)
     w = make_workload(cfg)
     got, d = run(torch_dev, w, cfg.partition_size, True)
     kp, vp = d["k_pool"].cpu().numpy(), d["v_pool"].cpu().numpy()
@@ -210,4 +230,4 @@ def test_mxfp4_full_size_sampled(torch_dev):
     bt = np.array([[remap.get(int(x), -1) for x in w.block_tables[b]] for b in sample], dtype=np.int32)
     ref = oracle.paged_decode_attention_mxfp4(cfg.dtype, np.ascontiguousarray(w.q[sample]), ok[used], ov[used],
                                               oks[used], ovs[used], bt, w.context_lens[sample], w.scale)
-    assert_close(got[sample], ref, cfg.dtype, "c3f4")
+    assert_close(got[sample], ref, cfg.dtype, name)

@@ -149,6 +149,9 @@ CONFIGS["c5f8"] = replace(CONFIGS["c5"], name="c5f8", kv_dtype="fp8",
 CONFIGS["c3f4"] = replace(CONFIGS["c3"], name="c3f4", kv_dtype="mxfp4",
                           title="large decode batch, MXFP4 K/V (B80, 32 heads MHA, D128, f16 q, ctx U[128,2048], "
                                 "append)")
+CONFIGS["c5f4"] = replace(CONFIGS["c5"], name="c5f4", kv_dtype="mxfp4",
+                          title="GQA long context, MXFP4 K/V (B32, 64 q / 8 kv heads, D128, bf16 q, "
+                                "ctx U[4096,16384], split 1024)")
 
 
 def draw_e4m3_codes(rng: np.random.Generator, shape) -> np.ndarray:
