@@ -228,10 +228,11 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
         if (p.kind != 0 && p.kind != 1) p.kind = 1;
         p.grouped = p.kind == 1;
         p.pf = 1;
-        if (p.kind == 1) {
+        if (p.kind == 1) {   // blocks stream through an LDS ring, pf blocks ahead per wave
             p.nw = env_int("PKV_MX4_NW", 4);
-            p.ch = env_int("PKV_MX4_CH", 2);
-            if (!pkv::mxfp4_mfma_variant_exists(p.nw, p.ch)) { p.nw = 4; p.ch = 2; }
+            p.ch = 1;
+            p.pf = env_int("PKV_MX4_PF", 2);
+            if (!pkv::mxfp4_mfma_variant_exists(p.nw, p.pf)) { p.nw = 4; p.pf = 2; }
             p.grid = (unsigned)((int64_t)p.n_parts * B * H_kv);
         } else {
             p.nw = env_int("PKV_MX4_NW", 4);
@@ -311,7 +312,7 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
             e = pkv::launch_kv_append_mxfp4(dtype, D, ap, s);
             if (e != hipSuccess) return fail(PKV_ERR_HIP, "kv_append_mxfp4 launch: %s", hipGetErrorString(e));
         }
-        e = p.kind == 1 ? pkv::launch_decode_mxfp4_mfma(dtype, D, p.nw, p.ch, a, p.grid, s)
+        e = p.kind == 1 ? pkv::launch_decode_mxfp4_mfma(dtype, D, p.nw, p.pf, a, p.grid, s)
                         : pkv::launch_decode_mxfp4(dtype, D, p.nw, p.ch, a, p.grid, s);
     } else if (fp8 && p.grouped) {
         // the grouped FP8 kernel reads the new row from the pool: quantize it there first
@@ -361,8 +362,8 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
         if (e != hipSuccess) return fail(PKV_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
     }
     if (mx4) {
-        snprintf(g_launch, sizeof g_launch, "%s dtype=%d D=%d nw=%d ch=%d pf=1 grid=%u part_tokens=%d n_parts=%d%s",
-                 p.kind == 1 ? "mxfp4_mfma" : "mxfp4", dtype, D, p.nw, p.ch, p.grid, p.part_tokens, p.n_parts,
+        snprintf(g_launch, sizeof g_launch, "%s dtype=%d D=%d nw=%d ch=%d pf=%d grid=%u part_tokens=%d n_parts=%d%s",
+                 p.kind == 1 ? "mxfp4_mfma" : "mxfp4", dtype, D, p.nw, p.ch, p.pf, p.grid, p.part_tokens, p.n_parts,
                  fused ? " fused_append" : "");
     } else if (persistent_wgs) {
         snprintf(g_launch, sizeof g_launch,

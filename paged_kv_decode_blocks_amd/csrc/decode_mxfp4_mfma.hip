@@ -60,6 +60,21 @@ __device__ __forceinline__ void split_bf16(float p0, float p1, uint32_t& hi, uin
     lo = __builtin_bit_cast(uint32_t, r);
 }
 
+// Max / sum over the four lane groups (lanes 16 apart) with the gfx950 lane swaps:
+// v_permlane16_swap pairs rows 0-1 and 2-3, v_permlane32_swap pairs the halves.
+__device__ __forceinline__ float max_groups(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_groups(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // E8M0 byte -> scale operand.  The conversion reads only the exponent field of
 // its f32 scale, and an exponent field of 0 means 2^-127, so the byte shifted
 // into place is the operand for every scale.
@@ -71,6 +86,11 @@ __device__ __forceinline__ void e2m1x8_to_bf16(uint32_t w, float sc, uint32_t (&
     o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
     o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
     o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
+}
+// byte X of a word of codes -> one packed bf16 pair (elements 2X, 2X + 1), scaled
+template <int X>
+__device__ __forceinline__ uint32_t e2m1x2_to_bf16(uint32_t w, float sc) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, X));
 }
 // two codes of the low byte -> one packed pair (D = 64 V pieces are 2 bytes)
 __device__ __forceinline__ void e2m1x4_to_bf16(uint32_t w, float sc, uint32_t (&o)[2]) {
@@ -88,8 +108,8 @@ struct Mx4Geo {
     static constexpr int SB = D / 32;          // scale bytes per row
 };
 
-// One chunk of CH blocks as loaded: K codes of the lane's row, its scale byte,
-// and the codes and scale bytes of its four V rows.
+// CH blocks as read from LDS: K codes of the lane's row, its scale byte, and the
+// codes and scale bytes of its four V rows.
 template <int D, int CH>
 struct Mx4Chunk {
     uint32_t k[CH][Mx4Geo<D>::KW];
@@ -98,27 +118,17 @@ struct Mx4Chunk {
     uint32_t vs[CH][4];
 };
 
-template <int D>
-__device__ __forceinline__ void ld_kcodes(const uint8_t* p, uint32_t (&w)[Mx4Geo<D>::KW]) {
-    if constexpr (D == 128) {
-        const uint4 x = ld16(p);
-        w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
-    } else {
-        const uint2 x = ld8(p);
-        w[0] = x.x; w[1] = x.y;
-    }
-}
-template <int D>
-__device__ __forceinline__ uint32_t ld_vcodes(const uint8_t* p) {
-    if constexpr (D == 128) return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
-    else return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
-}
-
-template <int QDT, int D>
+// LO: G <= 8, and columns [G, 2G) of both products repeat heads [0, G): their
+// scores, maxima and weights are the same numbers, and they carry the lo half of
+// P while columns [0, G) carry the hi half, so one K=32 output product takes 32
+// distinct tokens (two blocks) and the halves are added once at the end.
+// Otherwise (G <= 16) hi and lo share a product's k-slots, one block at a time.
+template <int QDT, int D, bool LO>
 struct Mx4Lane {
     using Geo = Mx4Geo<D>;
     static constexpr int KS = Geo::KS, VT = Geo::VT, NQ = QDT == DT_F16 ? 2 : 1;
     int j, c;
+    bool lo_lane;              // this lane's column carries the lo half of P
     uint4 qf[NQ][KS];          // B operand of step s (bf16; [1] = lo part of an f16 q)
     floatx4 acc[VT];
     float m, l, scale_log2;
@@ -132,8 +142,10 @@ struct Mx4Lane {
             qf[0][s] = make_uint4(0, 0, 0, 0);
             if constexpr (NQ == 2) qf[1][s] = make_uint4(0, 0, 0, 0);
         }
-        if (c < a.G) {
-            const char* qp = a.q + ((int64_t)b * a.q_row_stride + (int64_t)(g * a.G + c) * D + 8 * KS * j) * 2;
+        lo_lane = LO && c >= a.G;
+        if (c < (LO ? 2 : 1) * a.G) {
+            const int h = c < a.G ? c : c - a.G;
+            const char* qp = a.q + ((int64_t)b * a.q_row_stride + (int64_t)(g * a.G + h) * D + 8 * KS * j) * 2;
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 const uint4 x = ld16_cached(qp + 16 * s);
@@ -158,32 +170,53 @@ struct Mx4Lane {
         l = 0.0f;
     }
 
-    // Online-softmax update with CH blocks; valid[cb][i] masks token 4 i + j.
+    // Score tile of block cb (lane holds tokens 4 i + j of its column), log2 domain.
     template <int CH>
-    __device__ __forceinline__ void accumulate(const Mx4Chunk<D, CH>& ck, const bool (&valid)[CH][4]) {
-        float sc[CH][4];
+    __device__ __forceinline__ void scores(const Mx4Chunk<D, CH>& ck, int cb, float (&sc)[4]) {
+        const float ksc = mx_operand(ck.ks[cb]);
+        floatx4 st = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int cb = 0; cb < CH; ++cb) {
-            const float ksc = mx_operand(ck.ks[cb]);
-            floatx4 st = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                uint32_t kd[4];
-                e2m1x8_to_bf16(ck.k[cb][s], ksc, kd);
-                const uint4 ka = make_uint4(kd[0], kd[1], kd[2], kd[3]);
-                st = mma_bf16(ka, qf[0][s], st);
-                if constexpr (NQ == 2) st = mma_bf16(ka, qf[1][s], st);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sc[cb][i] = mul_rn(st[i], scale_log2);
+        for (int s = 0; s < KS; ++s) {
+            uint32_t kd[4];
+            e2m1x8_to_bf16(ck.k[cb][s], ksc, kd);
+            const uint4 ka = make_uint4(kd[0], kd[1], kd[2], kd[3]);
+            st = mma_bf16(ka, qf[0][s], st);
+            if constexpr (NQ == 2) st = mma_bf16(ka, qf[1][s], st);
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[i] = mul_rn(st[i], scale_log2);
+    }
+
+    // V rows of the lane's four tokens of block cb, decoded with their scales: word
+    // x of row i holds elements (2x, 2x + 1) of the lane's piece.
+    template <int CH>
+    __device__ __forceinline__ void vrows(const Mx4Chunk<D, CH>& ck, int cb, uint32_t (&vd)[4][VT / 2]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float vsc = mx_operand(ck.vs[cb][i]);
+            if constexpr (D == 128) {
+                uint32_t o[4];
+                e2m1x8_to_bf16(ck.v[cb][i], vsc, o);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) vd[i][x] = o[x];
+            } else {
+                uint32_t o[2];
+                e2m1x4_to_bf16(ck.v[cb][i], vsc, o);
+                vd[i][0] = o[0];
+                vd[i][1] = o[1];
+            }
+        }
+    }
+
+    // Shared max of the chunk and the lazy rescale; returns nothing, updates m, l, acc.
+    template <int CH, bool MASK>
+    __device__ __forceinline__ void rescale(const float (&sc)[CH][4], const bool (&valid)[CH][4]) {
         float mloc = kNegBig;
 #pragma unroll
         for (int cb = 0; cb < CH; ++cb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) mloc = valid[cb][i] ? fmaxf(mloc, sc[cb][i]) : mloc;
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+            for (int i = 0; i < 4; ++i) mloc = (!MASK || valid[cb][i]) ? fmaxf(mloc, sc[cb][i]) : mloc;
+        mloc = max_groups(mloc);
         // the reference max moves only when some head's running max grows by more
         // than kSlack (a rare, wave-uniform branch)
         if (__builtin_amdgcn_ballot_w64(mloc > m + kSlack) != 0) {
@@ -194,59 +227,212 @@ struct Mx4Lane {
 #pragma unroll
             for (int t = 0; t < VT; ++t) acc[t] *= alpha;
         }
+    }
+
+    // LO: two blocks, 32 tokens in one K=32 output product per tile.
+    template <bool MASK>
+    __device__ __forceinline__ void accumulate_pair(const Mx4Chunk<D, 2>& ck, const bool (&valid)[2][4]) {
+        float sc[2][4];
+        scores<2>(ck, 0, sc[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        scores<2>(ck, 1, sc[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        rescale<2, MASK>(sc, valid);
+        uint32_t pw[2][2];     // per block: packed weights of tokens (0, 1) and (2, 3), hi or lo half
 #pragma unroll
-        for (int cb = 0; cb < CH; ++cb) {
+        for (int cb = 0; cb < 2; ++cb) {
             float p[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                p[i] = valid[cb][i] ? __builtin_amdgcn_exp2f(sc[cb][i] - m) : 0.0f;
+                p[i] = (!MASK || valid[cb][i]) ? __builtin_amdgcn_exp2f(sc[cb][i] - m) : 0.0f;
                 l += p[i];
             }
-            uint4 pk;
-            split_bf16(p[0], p[1], pk.x, pk.z);
-            split_bf16(p[2], p[3], pk.y, pk.w);
-            // V rows of the lane's four tokens, decoded with their scales: word x of
-            // row i holds elements (2x, 2x + 1) of the lane's piece
-            uint32_t vd[4][VT / 2];
+            uint32_t h01, l01, h23, l23;
+            split_bf16(p[0], p[1], h01, l01);
+            split_bf16(p[2], p[3], h23, l23);
+            pw[cb][0] = lo_lane ? l01 : h01;
+            pw[cb][1] = lo_lane ? l23 : h23;
+        }
+        const uint4 pk = make_uint4(pw[0][0], pw[0][1], pw[1][0], pw[1][1]);
+        float vsc[2][4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float vsc = mx_operand(ck.vs[cb][i]);
-                if constexpr (D == 128) {
-                    uint32_t o[4];
-                    e2m1x8_to_bf16(ck.v[cb][i], vsc, o);
+        for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-                    for (int x = 0; x < 4; ++x) vd[i][x] = o[x];
-                } else {
-                    uint32_t o[2];
-                    e2m1x4_to_bf16(ck.v[cb][i], vsc, o);
-                    vd[i][0] = o[0];
-                    vd[i][1] = o[1];
-                }
-            }
+            for (int i = 0; i < 4; ++i) vsc[cb][i] = mx_operand(ck.vs[cb][i]);
+        // two output tiles per byte of the V pieces, decoded as they are used (keeps
+        // the live registers down; the barriers stop the scheduler from hoisting
+        // every conversion to the top)
+        pv_pair<0>(ck, vsc, pk);
+        if constexpr (VT / 2 > 1) pv_pair<1>(ck, vsc, pk);
+        if constexpr (VT / 2 > 2) pv_pair<2>(ck, vsc, pk);
+        if constexpr (VT / 2 > 3) pv_pair<3>(ck, vsc, pk);
+    }
+
+    // Output tiles 2X and 2X + 1 of a two-block chunk: byte X of each V piece.
+    template <int X>
+    __device__ __forceinline__ void pv_pair(const Mx4Chunk<D, 2>& ck, const float (&vsc)[2][4], const uint4& pk) {
+        uint32_t d0[4], d1[4];
 #pragma unroll
-            for (int t = 0; t < VT; ++t) {
-                const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
-                const int x = t >> 1;
-                const uint32_t v01 = __builtin_amdgcn_perm(vd[1][x], vd[0][x], sel);
-                const uint32_t v23 = __builtin_amdgcn_perm(vd[3][x], vd[2][x], sel);
-                acc[t] = mma_bf16(make_uint4(v01, v23, v01, v23), pk, acc[t]);
-            }
+        for (int i = 0; i < 4; ++i) {
+            d0[i] = e2m1x2_to_bf16<X>(ck.v[0][i], vsc[0][i]);
+            d1[i] = e2m1x2_to_bf16<X>(ck.v[1][i], vsc[1][i]);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t sel = h ? 0x07060302u : 0x05040100u;
+            const uint32_t a01 = __builtin_amdgcn_perm(d0[1], d0[0], sel);
+            const uint32_t a23 = __builtin_amdgcn_perm(d0[3], d0[2], sel);
+            const uint32_t b01 = __builtin_amdgcn_perm(d1[1], d1[0], sel);
+            const uint32_t b23 = __builtin_amdgcn_perm(d1[3], d1[2], sel);
+            acc[2 * X + h] = mma_bf16(make_uint4(a01, a23, b01, b23), pk, acc[2 * X + h]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Not LO: one block at a time, hi and lo halves of P in the k-slots of one product.
+    template <bool MASK>
+    __device__ __forceinline__ void accumulate(const Mx4Chunk<D, 1>& ck, const bool (&valid)[1][4]) {
+        float sc[1][4];
+        scores<1>(ck, 0, sc[0]);
+        rescale<1, MASK>(sc, valid);
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[i] = (!MASK || valid[0][i]) ? __builtin_amdgcn_exp2f(sc[0][i] - m) : 0.0f;
+            l += p[i];
+        }
+        uint4 pk;
+        split_bf16(p[0], p[1], pk.x, pk.z);
+        split_bf16(p[2], p[3], pk.y, pk.w);
+        uint32_t vd[4][VT / 2];
+        vrows<1>(ck, 0, vd);
+#pragma unroll
+        for (int t = 0; t < VT; ++t) {
+            const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+            const int x = t >> 1;
+            const uint32_t v01 = __builtin_amdgcn_perm(vd[1][x], vd[0][x], sel);
+            const uint32_t v23 = __builtin_amdgcn_perm(vd[3][x], vd[2][x], sel);
+            acc[t] = mma_bf16(make_uint4(v01, v23, v01, v23), pk, acc[t]);
         }
     }
 };
 
 }  // namespace
 
-template <int QDT, int D, int NW, int CH>
-__global__ __launch_bounds__(NW * 64) void decode_mxfp4_mfma_kernel(const AttnArgs a) {
+// global -> LDS, 4 or 16 bytes per active lane: lane l writes lds_base + 4 l or
+// 16 l (lds_base wave-uniform).  The LDS address-space cast only means something
+// in the device pass; in the host pass it would drop the kernel's launch stub.
+__device__ __forceinline__ void dma4(const void* src, void* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
+#else
+    (void)src;
+    (void)lds_base;
+#endif
+}
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+#else
+    (void)src;
+    (void)lds_base;
+#endif
+}
+
+// s_waitcnt vmcnt(N), other counters unconstrained (gfx9: vmcnt in bits [3:0] and [15:14])
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// One block of the ring -> registers in the MFMA layout, completed before return.
+// Issued as inline asm: the compiler cannot tell this slot from the DMAs still in
+// flight into the other slots and would drain every load before a plain LDS read;
+// the caller's vmcnt wait orders these reads after the DMAs that filled the slot.
+// Offsets: K codes at ka (16 bytes; for D = 64 two words at ka and ka + 256), K scale byte at ksa, V pieces at va +
+// i * VSTEP (4 or 2 bytes), V scale bytes at vsa + i * SSTEP.
+template <int D>
+__device__ __forceinline__ void lds_block(uint32_t ka, uint32_t ksa, uint32_t va, uint32_t vsa,
+                                          uint32_t (&k)[Mx4Geo<D>::KW], uint32_t& ks, uint32_t (&v)[4],
+                                          uint32_t (&vs)[4]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    constexpr int VSTEP = 4 * Mx4Geo<D>::RB, SSTEP = 4 * Mx4Geo<D>::SB;
+    if constexpr (D == 128) {
+        u32x4_t kk;
+        asm volatile(
+            "ds_read_b128 %0, %10\n\t"
+            "ds_read_u8 %1, %11\n\t"
+            "ds_read_b32 %2, %12\n\t"
+            "ds_read_b32 %3, %12 offset:%14\n\t"
+            "ds_read_b32 %4, %12 offset:%15\n\t"
+            "ds_read_b32 %5, %12 offset:%16\n\t"
+            "ds_read_u8 %6, %13\n\t"
+            "ds_read_u8 %7, %13 offset:%17\n\t"
+            "ds_read_u8 %8, %13 offset:%18\n\t"
+            "ds_read_u8 %9, %13 offset:%19\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=v"(kk), "=v"(ks), "=v"(v[0]), "=v"(v[1]), "=v"(v[2]), "=v"(v[3]), "=v"(vs[0]), "=v"(vs[1]),
+              "=v"(vs[2]), "=v"(vs[3])
+            : "v"(ka), "v"(ksa), "v"(va), "v"(vsa), "i"(VSTEP), "i"(2 * VSTEP), "i"(3 * VSTEP), "i"(SSTEP),
+              "i"(2 * SSTEP), "i"(3 * SSTEP)
+            : "memory");
+        k[0] = kk.x; k[1] = kk.y; k[2] = kk.z; k[3] = kk.w;
+    } else {   // the lane's two K words are at ka and ka + 256 (two dword DMAs)
+        asm volatile(
+            "ds_read_b32 %0, %11\n\t"
+            "ds_read_b32 %1, %11 offset:256\n\t"
+            "ds_read_u8 %2, %12\n\t"
+            "ds_read_u16 %3, %13\n\t"
+            "ds_read_u16 %4, %13 offset:%15\n\t"
+            "ds_read_u16 %5, %13 offset:%16\n\t"
+            "ds_read_u16 %6, %13 offset:%17\n\t"
+            "ds_read_u8 %7, %14\n\t"
+            "ds_read_u8 %8, %14 offset:%18\n\t"
+            "ds_read_u8 %9, %14 offset:%19\n\t"
+            "ds_read_u8 %10, %14 offset:%20\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=v"(k[0]), "=v"(k[1]), "=v"(ks), "=v"(v[0]), "=v"(v[1]), "=v"(v[2]), "=v"(v[3]), "=v"(vs[0]),
+              "=v"(vs[1]), "=v"(vs[2]), "=v"(vs[3])
+            : "v"(ka), "v"(ksa), "v"(va), "v"(vsa), "i"(VSTEP), "i"(2 * VSTEP), "i"(3 * VSTEP), "i"(SSTEP),
+              "i"(2 * SSTEP), "i"(3 * SSTEP)
+            : "memory");
+    }
+#else
+    (void)ka; (void)ksa; (void)va; (void)vsa;
+    for (int x = 0; x < Mx4Geo<D>::KW; ++x) k[x] = 0;
+    ks = 0;
+    for (int i = 0; i < 4; ++i) v[i] = vs[i] = 0;
+#endif
+}
+
+// Each wave streams its blocks (w, w + NW, ...) through a ring of R = PF + 1 LDS
+// slots, PF blocks ahead of the one it computes.  A slot holds one block of the
+// KV head: K codes placed so that lane l's 16 bytes sit at 16 l (for D = 64 its
+// two words at 4 l and 256 + 4 l) -- the DMA lane that fetches them is lane l, so
+// the read is conflict-free -- then V codes, K scales and V scales in pool order.  Every DMA stays inside the block's rows of this KV head; rows at
+// or past the length are masked after the read, so the last, partial block
+// needs no other path.
+template <int QDT, int D, int NW, int PF, bool LO>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_mxfp4_mfma_kernel(const AttnArgs a) {
     using Geo = Mx4Geo<D>;
-    using L = Mx4Lane<QDT, D>;
+    using L = Mx4Lane<QDT, D, LO>;
     constexpr int RB = Geo::RB, SB = Geo::SB, VT = Geo::VT;
+    constexpr int CH = LO ? 2 : 1;                         // blocks per chunk (one output product)
+    constexpr int R = PF + 1;                              // chunk slots per wave
+    constexpr int CODES = kBlockSize * RB;                 // bytes of one tile of codes
+    constexpr int SLOT = 2 * CODES + 2 * kBlockSize * SB;  // K codes, V codes, K scales, V scales
+    constexpr int LPB = D == 128 ? 3 : 5;                  // DMA instructions per block
+    constexpr int LPC = CH * LPB;
+    static_assert(PF * LPC < 64, "vmcnt range");
+    constexpr int RING = NW * R * CH * SLOT;
+    constexpr int MERGE = NW * 16 * (D + 4) * 4;
+    __shared__ __attribute__((aligned(16))) char s_ring[RING > MERGE ? RING : MERGE];
     __shared__ int32_t s_ids[kWin];
     __shared__ int s_bad;
     __shared__ float s_m[NW][16];
     __shared__ float s_l[NW][16];
-    __shared__ float s_o[NW][16][D + 4];
 
     const int BG = a.B * a.H_kv;
     const int unit = xcd_pair_unit(blockIdx.x, a.n_parts * BG);
@@ -285,46 +471,106 @@ __global__ __launch_bounds__(NW * 64) void decode_mxfp4_mfma_kernel(const AttnAr
     const int lim = min(start + a.part_tokens, n);
     const int nblk = (lim - start + kBlockSize - 1) / kBlockSize;
 
-    // per-lane byte offsets inside one (block, KV head) tile of codes / of scales
-    const int tau = 4 * (st.c & 3) + (st.c >> 2);
-    const int koff = tau * RB + (D / 8) * st.j;
-    const int ksoff = tau * SB + (Geo::KS * st.j) / 4;
-    int voff[4], vsoff[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        voff[i] = (4 * i + st.j) * RB + st.c * Geo::VB;
-        vsoff[i] = (4 * i + st.j) * SB + (st.c * VT) / 32;
-    }
+    const int j = st.j, c = st.c;
+    const int tau = 4 * (c & 3) + (c >> 2);
+    // DMA sources inside one (block, KV head) tile
+    const int kdma = D == 128 ? tau * RB + 16 * j : tau * RB + 8 * j;   // + 4 h for D = 64
+    const bool sc_lane = lane < 8 * SB;                                  // 4 SB lanes per scale tile
+    const int sdma = lane < 4 * SB ? 4 * lane : 4 * (lane - 4 * SB);
     const size_t blk_codes = (size_t)a.H_kv * kBlockSize * RB;
     const size_t blk_sc = (size_t)a.H_kv * kBlockSize * SB;
     const uint8_t* kp = reinterpret_cast<const uint8_t*>(a.k_pool) + (size_t)g * kBlockSize * RB;
     const uint8_t* vp = reinterpret_cast<const uint8_t*>(a.v_pool) + (size_t)g * kBlockSize * RB;
-    const uint8_t* ksp = a.k_mx_scale + (size_t)g * kBlockSize * SB;
-    const uint8_t* vsp = a.v_mx_scale + (size_t)g * kBlockSize * SB;
+    const uint8_t* sp = (lane < 4 * SB ? a.k_mx_scale : a.v_mx_scale) + (size_t)g * kBlockSize * SB + sdma;
+    // LDS read offsets inside a slot
+    const uint32_t ring0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)s_ring;
+    const uint32_t k_rd = (D == 128 ? 16 : 4) * lane;
+    const uint32_t ks_rd = 2 * CODES + tau * SB + (Geo::KS * j) / 4;
+    const uint32_t v_rd = CODES + j * RB + c * Geo::VB;
+    const uint32_t vs_rd = 2 * CODES + kBlockSize * SB + j * SB + (c * VT) / 32;
+    char* my_ring = s_ring + w * R * CH * SLOT;
+    const uint32_t my_ring_a = ring0 + w * R * CH * SLOT;
 
-    using Chunk = Mx4Chunk<D, CH>;
-    auto load_chunk = [&](Chunk& ck, int cb0) {
+    auto issue_block = [&](int slot, int blk) {
+        const size_t id = (size_t)__builtin_amdgcn_readfirstlane(s_ids[blk]);
+        char* dst = my_ring + slot * SLOT;
+        if constexpr (D == 128) {
+            dma16(kp + id * blk_codes + kdma, dst);
+            dma16(vp + id * blk_codes + 16 * lane, dst + CODES);
+        } else {
+            dma4(kp + id * blk_codes + kdma, dst);
+            dma4(kp + id * blk_codes + kdma + 4, dst + 256);
+            dma4(vp + id * blk_codes + 4 * lane, dst + CODES);
+            dma4(vp + id * blk_codes + 256 + 4 * lane, dst + CODES + 256);
+        }
+        if (sc_lane) dma4(sp + id * blk_sc, dst + 2 * CODES);
+    };
+    // chunk i of the wave: blocks w + NW (CH i + cb); a block past the window's
+    // end (the last chunk's second block) is fetched as a copy of the first and
+    // masked, so every chunk issues the same number of DMAs
+    int nr = 0;
+    auto blk_of = [&](int i, int cb) { return w + NW * (CH * i + cb); };
+    auto issue = [&](int slot, int i) {
 #pragma unroll
         for (int cb = 0; cb < CH; ++cb) {
-            const size_t id = (size_t)__builtin_amdgcn_readfirstlane(s_ids[cb0 + cb]);
-            ld_kcodes<D>(kp + id * blk_codes + koff, ck.k[cb]);
-            ck.ks[cb] = ksp[id * blk_sc + ksoff];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                ck.v[cb][i] = ld_vcodes<D>(vp + id * blk_codes + voff[i]);
-                ck.vs[cb][i] = vsp[id * blk_sc + vsoff[i]];
-            }
+            const int blk = blk_of(i, cb);
+            issue_block(CH * slot + cb, blk < nr ? blk : blk_of(i, 0));
         }
     };
-    bool all_valid[CH][4];
+    // one chunk from its slots: read, mask rows at or past lim, accumulate
+    auto consume = [&](int slot, int i, int tok_r) {
+        Mx4Chunk<D, CH> ck;
+        bool valid[CH][4];
+        int tbs[CH];
+        int nfull = 0;
 #pragma unroll
-    for (int cb = 0; cb < CH; ++cb)
+        for (int cb = 0; cb < CH; ++cb) {
+            const int blk = blk_of(i, cb);
+            tbs[cb] = blk < nr ? tok_r + blk * kBlockSize : lim;   // a copied block is wholly masked
+            nfull += tbs[cb] + kBlockSize <= lim;
+        }
+        const bool full = __builtin_amdgcn_readfirstlane(nfull) == CH;   // wave-uniform
 #pragma unroll
-        for (int i = 0; i < 4; ++i) all_valid[cb][i] = true;
+        for (int cb = 0; cb < CH; ++cb) {
+            const uint32_t base = my_ring_a + (CH * slot + cb) * SLOT;
+            lds_block<D>(base + k_rd, base + ks_rd, base + v_rd, base + vs_rd, ck.k[cb], ck.ks[cb], ck.v[cb],
+                         ck.vs[cb]);
+        }
+        if (!full) {   // only a window's last chunk
+#pragma unroll
+            for (int cb = 0; cb < CH; ++cb) {
+                if (tbs[cb] + tau >= lim) {
+#pragma unroll
+                    for (int x = 0; x < Geo::KW; ++x) ck.k[cb][x] = 0;
+                    ck.ks[cb] = 127;
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    valid[cb][q] = tbs[cb] + 4 * q + j < lim;
+                    if (!valid[cb][q]) {
+                        ck.v[cb][q] = 0;
+                        ck.vs[cb][q] = 127;
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int cb = 0; cb < CH; ++cb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) valid[cb][q] = true;
+        }
+        if constexpr (LO) {
+            if (full) st.template accumulate_pair<false>(ck, valid);
+            else st.template accumulate_pair<true>(ck, valid);
+        } else {
+            if (full) st.template accumulate<false>(ck, valid);
+            else st.template accumulate<true>(ck, valid);
+        }
+    };
 
     if (threadIdx.x == 0) s_bad = 0;
     for (int r0 = 0; r0 < nblk; r0 += kWin) {
-        const int nr = min(kWin, nblk - r0);
+        nr = min(kWin, nblk - r0);
         __syncthreads();
         if (r0 == 0) {
 #pragma unroll
@@ -350,77 +596,52 @@ __global__ __launch_bounds__(NW * 64) void decode_mxfp4_mfma_kernel(const AttnAr
             }
         }
         __syncthreads();
-        const int nch = (nr + CH - 1) / CH;
         const int tok_r = start + r0 * kBlockSize;
-        const int nfull_all = max(0, min(nch, (lim - tok_r) / (CH * kBlockSize)));
-        const int nf = w < nfull_all ? (nfull_all - w + NW - 1) / NW : 0;
-        auto chunk_of = [&](int i) { return (w + NW * i) * CH; };
-        // chunk i lives in buf[i % 2]; the loads of chunk i + 1 go out before chunk i is used
-        Chunk buf[2];
+        const int nbw = w < nr ? (nr - w + NW - 1) / NW : 0;   // this wave's blocks: w + NW i
+        const int nb = (nbw + CH - 1) / CH;                      // ... in chunks of CH
         int i = 0;
-        if (nf >= 3) {
-            load_chunk(buf[0], chunk_of(0));   // unconditional, so the loop's waits stay exact
-            for (; i + 3 <= nf; i += 2) {
-                load_chunk(buf[1], chunk_of(i + 1));
-                st.template accumulate<CH>(buf[0], all_valid);
-                load_chunk(buf[0], chunk_of(i + 2));
-                st.template accumulate<CH>(buf[1], all_valid);
-            }
-        } else if (nf > 0) {
-            load_chunk(buf[0], chunk_of(0));
-        }
-        for (; i < nf; i += 2) {   // at most two chunks left; chunk i is loaded
-            if (i + 1 < nf) load_chunk(buf[1], chunk_of(i + 1));
-            st.template accumulate<CH>(buf[0], all_valid);
-            if (i + 1 < nf) {
-                if (i + 2 < nf) load_chunk(buf[0], chunk_of(i + 2));
-                st.template accumulate<CH>(buf[1], all_valid);
-            }
-        }
-        // the partial chunk: rows at or past lim are never read and enter as zeros
-        for (int k = nfull_all + ((w - nfull_all) % NW + NW) % NW; k < nch; k += NW) {
-            const int cb0 = k * CH;
-            Chunk ck;
-            bool valid[CH][4];
+        if (nb >= R + PF) {
+            // unconditional prologue, so the loop is entered with the same DMAs in
+            // flight as it loops back with (keeps the waits exact)
 #pragma unroll
-            for (int cb = 0; cb < CH; ++cb) {
-                const bool in = cb0 + cb < nr;
-                const size_t id = (size_t)__builtin_amdgcn_readfirstlane(in ? s_ids[cb0 + cb] : 0);
-                const int tb = tok_r + (cb0 + cb) * kBlockSize;
+            for (int v = 0; v < PF; ++v) issue(v, v);
+            for (; i + R + PF <= nb; i += R) {
 #pragma unroll
-                for (int x = 0; x < Geo::KW; ++x) ck.k[cb][x] = 0;
-                ck.ks[cb] = 127;
-                if (in && tb + tau < lim) {
-                    ld_kcodes<D>(kp + id * blk_codes + koff, ck.k[cb]);
-                    ck.ks[cb] = ksp[id * blk_sc + ksoff];
-                }
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    valid[cb][q] = in && tb + 4 * q + st.j < lim;
-                    ck.v[cb][q] = 0;
-                    ck.vs[cb][q] = 127;
-                    if (valid[cb][q]) {
-                        ck.v[cb][q] = ld_vcodes<D>(vp + id * blk_codes + voff[q]);
-                        ck.vs[cb][q] = vsp[id * blk_sc + vsoff[q]];
-                    }
+                for (int v = 0; v < R; ++v) {
+                    issue((v + PF) % R, i + v + PF);
+                    wait_vm<PF * LPC>();
+                    consume(v, i + v, tok_r);
                 }
             }
-            st.template accumulate<CH>(ck, valid);
+        } else {
+#pragma unroll
+            for (int v = 0; v < PF; ++v)
+                if (v < nb) issue(v, v);
+        }
+        for (; i < nb; i += R) {   // at most two rounds left
+#pragma unroll
+            for (int v = 0; v < R; ++v) {
+                if (i + v < nb) {
+                    if (i + v + PF < nb) issue((v + PF) % R, i + v + PF);
+                    wait_vm<0>();
+                    consume(v, i + v, tok_r);
+                }
+            }
         }
     }
 
-    // merge the waves through LDS and write the partition's result
-    float l = st.l;
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    if (st.j == 0) {
-        s_m[w][st.c] = st.m;
-        s_l[w][st.c] = l;
+    // merge the waves through LDS (the ring is free once every wave is past here)
+    const float l = sum_groups(st.l);
+    __syncthreads();
+    float (*s_o)[16][D + 4] = reinterpret_cast<float (*)[16][D + 4]>(s_ring);
+    if (j == 0) {
+        s_m[w][c] = st.m;
+        s_l[w][c] = l;
     }
 #pragma unroll
     for (int t = 0; t < VT; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s_o[w][st.c][(4 * st.j + i) * VT + t] = st.acc[t][i];
+        for (int q = 0; q < 4; ++q) s_o[w][c][(4 * j + q) * VT + t] = st.acc[t][q];
     __syncthreads();
     const bool bad = s_bad != 0;
     const int G = a.G;
@@ -435,7 +656,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mxfp4_mfma_kernel(const AttnAr
         for (int q = 0; q < NW; ++q) {
             const float f = __builtin_amdgcn_exp2f(s_m[q][hh] - M);
             Ls += s_l[q][hh] * f;
-            O += s_o[q][hh][d] * f;
+            O += (LO ? s_o[q][hh][d] + s_o[q][hh + G][d] : s_o[q][hh][d]) * f;   // hi + lo columns
         }
         const size_t row = (size_t)b * a.H_q + (size_t)g * G + hh;
         const float val = bad ? __builtin_nanf("") : O / Ls;
@@ -448,37 +669,44 @@ __global__ __launch_bounds__(NW * 64) void decode_mxfp4_mfma_kernel(const AttnAr
     }
 }
 
-template <int QDT, int D, int NW, int CH>
+template <int QDT, int D, int NW, int PF>
 static hipError_t launch_t(const AttnArgs& a, unsigned grid, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_mxfp4_mfma_kernel<QDT, D, NW, CH>), dim3(grid), dim3(NW * 64), 0, stream, a);
+    if (a.G <= 8)
+        hipLaunchKernelGGL((decode_mxfp4_mfma_kernel<QDT, D, NW, PF, true>), dim3(grid), dim3(NW * 64), 0, stream, a);
+    else
+        hipLaunchKernelGGL((decode_mxfp4_mfma_kernel<QDT, D, NW, PF, false>), dim3(grid), dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
+// (waves, chunks in flight per wave; a chunk is two blocks when G <= 8, else one)
+#define PKV_MX4_MFMA_VARIANTS(X) X(4, 1) X(4, 2) X(4, 3) X(2, 2) X(2, 4)
+
 template <int QDT, int D>
-static hipError_t launch_d(int nw, int ch, const AttnArgs& a, unsigned grid, hipStream_t s) {
-    switch (nw * 10 + ch) {
-    case 21: return launch_t<QDT, D, 2, 1>(a, grid, s);
-    case 22: return launch_t<QDT, D, 2, 2>(a, grid, s);
-    case 41: return launch_t<QDT, D, 4, 1>(a, grid, s);
-    case 42: return launch_t<QDT, D, 4, 2>(a, grid, s);
-    default: return hipErrorInvalidValue;
-    }
+static hipError_t launch_d(int nw, int pf, const AttnArgs& a, unsigned grid, hipStream_t s) {
+#define X(NW_, PF_) \
+    if (nw == NW_ && pf == PF_) return launch_t<QDT, D, NW_, PF_>(a, grid, s);
+    PKV_MX4_MFMA_VARIANTS(X)
+#undef X
+    return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode_mxfp4_mfma(int q_dtype, int D, int nw, int ch, const AttnArgs& a, unsigned grid,
+hipError_t launch_decode_mxfp4_mfma(int q_dtype, int D, int nw, int pf, const AttnArgs& a, unsigned grid,
                                     hipStream_t stream) {
     switch (q_dtype * 1000 + D) {
-    case DT_F16 * 1000 + 64: return launch_d<DT_F16, 64>(nw, ch, a, grid, stream);
-    case DT_F16 * 1000 + 128: return launch_d<DT_F16, 128>(nw, ch, a, grid, stream);
-    case DT_BF16 * 1000 + 64: return launch_d<DT_BF16, 64>(nw, ch, a, grid, stream);
-    case DT_BF16 * 1000 + 128: return launch_d<DT_BF16, 128>(nw, ch, a, grid, stream);
+    case DT_F16 * 1000 + 64: return launch_d<DT_F16, 64>(nw, pf, a, grid, stream);
+    case DT_F16 * 1000 + 128: return launch_d<DT_F16, 128>(nw, pf, a, grid, stream);
+    case DT_BF16 * 1000 + 64: return launch_d<DT_BF16, 64>(nw, pf, a, grid, stream);
+    case DT_BF16 * 1000 + 128: return launch_d<DT_BF16, 128>(nw, pf, a, grid, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
-bool mxfp4_mfma_variant_exists(int nw, int ch) {
-    const int v = nw * 10 + ch;
-    return v == 21 || v == 22 || v == 41 || v == 42;
+bool mxfp4_mfma_variant_exists(int nw, int pf) {
+#define X(NW_, PF_) \
+    if (nw == NW_ && pf == PF_) return true;
+    PKV_MX4_MFMA_VARIANTS(X)
+#undef X
+    return false;
 }
 
 }  // namespace pkv

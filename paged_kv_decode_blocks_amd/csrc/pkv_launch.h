@@ -77,10 +77,11 @@ hipError_t launch_kv_append_mxfp4(int src_dtype, int D, const AppendMx4Args& a, 
 hipError_t launch_decode_mxfp4(int q_dtype, int D, int nw, int ch, const AttnArgs& a, unsigned grid,
                                hipStream_t stream);
 bool mxfp4_variant_exists(int nw, int ch);
-// grouped MXFP4 attention on MFMA (f16/bf16 q, G <= 16): grid = n_parts * B * H_kv
-hipError_t launch_decode_mxfp4_mfma(int q_dtype, int D, int nw, int ch, const AttnArgs& a, unsigned grid,
+// grouped MXFP4 attention on MFMA (f16/bf16 q, G <= 16): grid = n_parts * B * H_kv;
+// nw waves per workgroup, pf blocks in flight per wave
+hipError_t launch_decode_mxfp4_mfma(int q_dtype, int D, int nw, int pf, const AttnArgs& a, unsigned grid,
                                     hipStream_t stream);
-bool mxfp4_mfma_variant_exists(int nw, int ch);
+bool mxfp4_mfma_variant_exists(int nw, int pf);
 // per query head; q (and new rows) in q_dtype, K/V codes + scales in the AttnArgs pools
 hipError_t launch_decode_fp8(int q_dtype, int D, int nw, int ch, int pf, bool append, const AttnArgs& a,
                              unsigned grid, hipStream_t stream);

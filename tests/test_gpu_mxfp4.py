@@ -19,9 +19,10 @@ pytestmark = pytest.mark.gpu
 
 TOL = {"f32": (1e-5, 1e-5), "f16": (2e-3, 1e-2), "bf16": (2e-3, 1e-2)}
 EDGE_LENS = (1, 2, 15, 16, 17, 31, 33, 64, 255, 257, 700)
-# (kernel kind, waves, blocks per chunk): kind 1 = grouped MFMA kernel (f16/bf16 q, G <= 16),
-# kind 0 = per-head vector-unit kernel
-MX4_VARIANTS = ["0,4,2", "0,4,4", "0,8,2", "1,2,1", "1,2,2", "1,4,1", "1,4,2"]
+# (kernel kind, waves, blocks per chunk or in flight): kind 0 = per-head vector-unit kernel
+# (blocks per chunk), kind 1 = grouped MFMA kernel over an LDS ring (f16/bf16 q, G <= 16;
+# chunks in flight per wave)
+MX4_VARIANTS = ["0,4,2", "0,4,4", "0,8,2", "1,4,1", "1,4,2", "1,4,3", "1,2,2", "1,2,4"]
 
 
 @pytest.fixture(scope="module")
@@ -174,11 +175,12 @@ def test_mxfp4_attention_parity(torch_dev, dtype, D, H_q, H_kv, P, append):
 
 @pytest.mark.parametrize("variant", MX4_VARIANTS)
 def test_mxfp4_every_launch_variant(torch_dev, monkeypatch, variant):
-    kind, nw, ch = variant.split(",")
+    kind, nw, x = variant.split(",")
     monkeypatch.setenv("PKV_MX4_KIND", kind)
     monkeypatch.setenv("PKV_MX4_NW", nw)
-    monkeypatch.setenv("PKV_MX4_CH", ch)
+    monkeypatch.setenv("PKV_MX4_PF" if kind == "1" else "PKV_MX4_CH", x)
     name = "mxfp4_mfma " if kind == "1" else "mxfp4 "
+    tag = f"nw={nw} ch=1 pf={x} " if kind == "1" else f"nw={nw} ch={x} "
     # 4500 tokens unsplit: more than one 256-block window of ids per workgroup
     cases = [("f16", 128, 0, 4, 4, True), ("bf16", 64, 64, 8, 2, True), ("bf16", 128, 256, 16, 1, False),
              ("f16", 64, 0, 6, 2, False)]
@@ -190,7 +192,7 @@ def test_mxfp4_every_launch_variant(torch_dev, monkeypatch, variant):
         ref, pk, pv = oracle.run_step(w)
         got, d = run(torch_dev, w, P, append)
         launch = pkv.last_launch()
-        assert launch.startswith(name) and f"nw={nw} ch={ch} " in launch, launch
+        assert launch.startswith(name) and tag in launch, launch
         assert_close(got, ref, dtype, f"variant {variant} {dtype} D{D} P{P}")
         if append:
             assert pools_equal(d, pk, pv)
