@@ -101,8 +101,10 @@ const char* pkv_last_error(void);
  * PKV_MHA_{NW,CH,PF} (per-head 16-bit), PKV_GQA_{KIND,NW,CH,PF} (grouped 16-bit;
  * KIND 0 = K in registers, 1 = K and V through LDS, 2 = K through LDS),
  * PKV_FP8_{NW,CH,PF} (per-head FP8), PKV_GQA8_{NW,CH,PF,WPE,KDMA} (grouped
- * FP8) and PKV_MX4_{NW,CH} (MXFP4).  A combination the library does not instantiate falls back to the
- * default; results agree to the same tolerance for every instantiated shape. */
+ * FP8) and PKV_MX4_{KIND,NW,CH,PF} (MXFP4; KIND 0 = per query head on the
+ * vector units, 1 = grouped heads on MFMA; CH for kind 0, PF for kind 1).  A
+ * combination the library does not instantiate falls back to the default;
+ * results agree to the same tolerance for every instantiated shape. */
 const char* pkv_last_launch(void);
 
 /*

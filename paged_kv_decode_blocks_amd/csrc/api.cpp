@@ -293,7 +293,7 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
     if (mx4) {
-        // the attention kernel reads the new row from the pool: quantize it there first
+        // both attention kernels read the new row from the pool: quantize it there first
         if (fused) {
             pkv::AppendMx4Args ap{};
             ap.k_new = a.k_new;

@@ -15,18 +15,42 @@
 //    lanes of a row add their partial dot products with DPP.
 //  * Block ids are staged in LDS per window; each wave takes chunks of CH
 //    blocks and issues the next chunk's loads before computing the current one;
-//    the online softmax runs in the log2 domain, merged across the wave's row
-//    groups with shuffles and across waves through LDS.
+//    the online softmax runs in the log2 domain with one running max per wave,
+//    moved lazily, so the wave's row groups merge by plain sums (DPP row
+//    rotations and lane swaps) and the waves through LDS.
 //
 // The fused step runs the quantizing append kernel first; this kernel then
 // reads every row, the new one included, from the pools (lengths from
-// context_lens, or positions + 1 when context_lens is NULL).
+// context_lens, or positions + 1 when context_lens is NULL).  Quantizing the new
+// row in this kernel instead measured slower: its registers cost a wave per SIMD.
 #include "pkv_mxfp4.h"
 #include "pkv_launch.h"
 
 namespace pkv {
 
 constexpr int kMx4WindowBlocks = 256;
+constexpr float kMx4Slack = 8.0f;   // log2 units: weights stay below 256
+constexpr int kDppRowRor4 = 0x124;  // rotate each row of 16 lanes right by 4
+constexpr int kDppRowRor8 = 0x128;  // ... by 8
+
+// Sum / max over the 16 row groups of a wave (lanes 4 apart): row rotations by 4
+// and 8 within each row of 16, then the gfx950 row and half swaps.
+__device__ __forceinline__ float rows_sum(float v) {
+    v += dpp_f<kDppRowRor4>(v);
+    v += dpp_f<kDppRowRor8>(v);
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float rows_max(float v) {
+    v = fmaxf(v, dpp_f<kDppRowRor4>(v));
+    v = fmaxf(v, dpp_f<kDppRowRor8>(v));
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
 template <int D>
 struct Mx4Row {
@@ -114,7 +138,6 @@ __global__ __launch_bounds__(NW * 64) void decode_mxfp4_kernel(const AttnArgs a)
     if (start >= n) return;
     const int end = min(start + a.part_tokens, n);
     const int lim = end;
-
     float m = kNegBig, l = 0.0f;
     float o[CPL];
 #pragma unroll
@@ -158,15 +181,20 @@ __global__ __launch_bounds__(NW * 64) void decode_mxfp4_kernel(const AttnArgs a)
             }
             s[cb] = mul_rn(group_sum<4>(acc), a.scale_log2);
         }
+        // one running max per wave, moved only when the chunk's max exceeds it by
+        // more than kMx4Slack (a rare, wave-uniform branch)
         float mloc = kNegBig;
 #pragma unroll
         for (int cb = 0; cb < CH; ++cb) mloc = valid[cb] ? fmaxf(mloc, s[cb]) : mloc;
-        const float m_new = fmaxf(m, mloc);
-        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-        m = m_new;
-        l *= alpha;
+        mloc = rows_max(mloc);
+        if (__builtin_amdgcn_ballot_w64(mloc > m + kMx4Slack) != 0) {
+            const float m_new = fmaxf(m, mloc);
+            const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+            m = m_new;
+            l *= alpha;
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) o[e] *= alpha;
+            for (int e = 0; e < CPL; ++e) o[e] *= alpha;
+        }
 #pragma unroll
         for (int cb = 0; cb < CH; ++cb) {
             const float p = valid[cb] ? __builtin_amdgcn_exp2f(s[cb] - m) : 0.0f;
@@ -264,19 +292,11 @@ __global__ __launch_bounds__(NW * 64) void decode_mxfp4_kernel(const AttnArgs a)
         }
     }
 
-    // merge the 16 row groups of the wave (lanes 4 apart hold the same columns)
+    // merge the 16 row groups of the wave (lanes 4 apart hold the same columns):
+    // they share m, so the merge is a sum
+    l = rows_sum(l);
 #pragma unroll
-    for (int off = 4; off < 64; off <<= 1) {
-        const float m_o = __shfl_xor(m, off, 64);
-        const float l_o = __shfl_xor(l, off, 64);
-        const float M = fmaxf(m, m_o);
-        const float fa = __builtin_amdgcn_exp2f(m - M);
-        const float fb = __builtin_amdgcn_exp2f(m_o - M);
-        l = l * fa + l_o * fb;
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) o[e] = o[e] * fa + __shfl_xor(o[e], off, 64) * fb;
-        m = M;
-    }
+    for (int e = 0; e < CPL; ++e) o[e] = rows_sum(o[e]);
     if (lane < 4) {
 #pragma unroll
         for (int e = 0; e < CPL; ++e) s_o[w][c * CPL + e] = o[e];
@@ -316,7 +336,6 @@ template <int QDT, int D>
 static hipError_t launch_d(int nw, int ch, const AttnArgs& a, unsigned grid, hipStream_t s) {
     switch (nw * 10 + ch) {
     case 42: return launch_t<QDT, D, 4, 2>(a, grid, s);
-    case 44: return launch_t<QDT, D, 4, 4>(a, grid, s);
     case 82: return launch_t<QDT, D, 8, 2>(a, grid, s);
     default: return hipErrorInvalidValue;
     }
@@ -335,6 +354,6 @@ hipError_t launch_decode_mxfp4(int q_dtype, int D, int nw, int ch, const AttnArg
     }
 }
 
-bool mxfp4_variant_exists(int nw, int ch) { return nw * 10 + ch == 42 || nw * 10 + ch == 44 || nw * 10 + ch == 82; }
+bool mxfp4_variant_exists(int nw, int ch) { return nw * 10 + ch == 42 || nw * 10 + ch == 82; }
 
 }  // namespace pkv

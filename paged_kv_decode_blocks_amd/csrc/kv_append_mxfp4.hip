@@ -44,11 +44,8 @@ __global__ __launch_bounds__(256) void kv_append_mxfp4_kernel(const AppendMx4Arg
             }
         }
     }
-    const float amax = group_max<16>(fmaxf(fabsf(x[0]), fabsf(x[1])));
-    const int E = mx_block_exponent(amax);
-    // 2^-E as a float: -E in [-125, 127]
-    const float inv = __uint_as_float((uint32_t)(127 - E) << 23);
-    const uint32_t byte = e2m1_encode(x[0] * inv) | (e2m1_encode(x[1] * inv) << 4);
+    int E;
+    const uint32_t byte = mx4_quantize_pair(x[0], x[1], E);
     const size_t row = ((size_t)blk * a.H_kv + g) * kBlockSize + p % kBlockSize;
     if (on) {
         (which ? a.v_pool : a.k_pool)[row * (D / 2) + lane] = (uint8_t)byte;

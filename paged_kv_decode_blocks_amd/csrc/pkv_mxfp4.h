@@ -54,4 +54,15 @@ __device__ __forceinline__ uint32_t e2m1_encode(float v) {
     return c | ((__float_as_uint(v) >> 28) & 8u);
 }
 
+// One row quantized by one wave: lane l holds elements 2l and 2l + 1 (zeros for
+// lanes >= D/2); returns the lane's code byte and, in E, its 32-element block's
+// scale exponent (the block's max from a 16-lane reduction).
+__device__ __forceinline__ uint32_t mx4_quantize_pair(float x0, float x1, int& E) {
+    const float amax = group_max<16>(fmaxf(fabsf(x0), fabsf(x1)));
+    E = mx_block_exponent(amax);
+    // 2^-E as a float: -E in [-125, 127]
+    const float inv = __uint_as_float((uint32_t)(127 - E) << 23);
+    return e2m1_encode(x0 * inv) | (e2m1_encode(x1 * inv) << 4);
+}
+
 }  // namespace pkv

@@ -22,7 +22,7 @@ EDGE_LENS = (1, 2, 15, 16, 17, 31, 33, 64, 255, 257, 700)
 # (kernel kind, waves, blocks per chunk or in flight): kind 0 = per-head vector-unit kernel
 # (blocks per chunk), kind 1 = grouped MFMA kernel over an LDS ring (f16/bf16 q, G <= 16;
 # chunks in flight per wave)
-MX4_VARIANTS = ["0,4,2", "0,4,4", "0,8,2", "1,4,1", "1,4,2", "1,4,3", "1,2,2", "1,2,4"]
+MX4_VARIANTS = ["0,4,2", "0,8,2", "1,4,1", "1,4,2", "1,4,3", "1,2,2", "1,2,4"]
 
 
 @pytest.fixture(scope="module")
