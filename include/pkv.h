@@ -504,6 +504,13 @@ int pkv_copy_blocks_fp8(uint8_t* k_pool, uint8_t* v_pool, float* k_scale, float*
                         const int32_t* dst, int32_t n, int32_t H_kv, int32_t D, int32_t block_size, int32_t n_blocks,
                         void* stream);
 
+/* copy_blocks for an MXFP4 cache: the blocks' code bytes ([n_blocks][H_kv][16][D/2])
+ * and their E8M0 scale bytes ([n_blocks][H_kv][16][D/32]); pools and scale arrays
+ * 16-byte aligned.  Same pair rules as pkv_copy_blocks. */
+int pkv_copy_blocks_mxfp4(uint8_t* k_pool, uint8_t* v_pool, uint8_t* k_scale, uint8_t* v_scale, const int32_t* src,
+                          const int32_t* dst, int32_t n, int32_t H_kv, int32_t D, int32_t block_size, int32_t n_blocks,
+                          void* stream);
+
 /*
  * ---------------------------------------------------------------------------
  * Step graphs: the decode step captured once per (batch, context) bucket
@@ -529,7 +536,9 @@ int pkv_copy_blocks_fp8(uint8_t* k_pool, uint8_t* v_pool, float* k_scale, float*
  * Buffers are sized for the largest capacities; workspace for the largest
  * bucket (pkv_decode_workspace_bytes(max Bc, H_q, D, max Cc, partition_size)).
  * With k_scale / v_scale set the pools are an FP8 cache (uint8 codes, as in the
- * FP8 calls above; dtype is then q's) and the graphs run the FP8 step.
+ * FP8 calls above; dtype is then q's) and the graphs run the FP8 step; with
+ * k_mx_scale / v_mx_scale set they are an MXFP4 cache and the graphs run the
+ * MXFP4 step (at most one of the two pairs).
  * The buffers must stay allocated, at the same addresses, for the object's
  * lifetime.  Capture happens in pkv_step_graphs_create on a stream of its own;
  * launch is asynchronous and allocation-free.  Not thread-safe per object.
@@ -556,6 +565,8 @@ typedef struct pkv_step_desc {
     size_t workspace_bytes;
     float* k_scale;                              /* FP8 pools: row scales (else NULL)  */
     float* v_scale;
+    uint8_t* k_mx_scale;                         /* MXFP4 pools: E8M0 scale bytes (else NULL) */
+    uint8_t* v_mx_scale;
 } pkv_step_desc;
 
 typedef struct pkv_step_graphs pkv_step_graphs;
@@ -625,6 +636,8 @@ typedef struct pkv_decoder_desc {
     int32_t n_ctx_caps;
     float* k_scale;                              /* FP8 pools: row scales (else NULL); dtype is q's */
     float* v_scale;
+    uint8_t* k_mx_scale;                         /* MXFP4 pools: E8M0 scale bytes (else NULL); dtype is q's */
+    uint8_t* v_mx_scale;
 } pkv_decoder_desc;
 
 typedef struct pkv_decoder pkv_decoder;

@@ -31,7 +31,7 @@ __all__ = [
     "PKV_F32", "PKV_F16", "PKV_BF16", "EXPORTED_SYMBOLS", "copy_blocks", "BlockManager", "StepGraphs", "Decoder", "cu_mask", "CuMaskedStream",
     "kv_append_fp8", "paged_decode_attention_fp8", "append_decode_attention_fp8", "copy_blocks_fp8",
     "device_cu_count", "append_decode_attention_persistent",
-    "kv_append_mxfp4", "paged_decode_attention_mxfp4", "append_decode_attention_mxfp4",
+    "kv_append_mxfp4", "paged_decode_attention_mxfp4", "append_decode_attention_mxfp4", "copy_blocks_mxfp4",
     "PKV_ERR_OUT_OF_BLOCKS", "PKV_ERR_SEQUENCE",
 ]
 
@@ -48,7 +48,7 @@ EXPORTED_SYMBOLS = (
     "pkv_append_decode_attention_persistent", "pkv_probe_mfma_burn",
     "pkv_probe_stream_read", "pkv_copy_blocks", "pkv_copy_blocks_fp8", "pkv_kv_append_fp8", "pkv_paged_decode_attention_fp8",
     "pkv_append_decode_attention_fp8", "pkv_kv_append_mxfp4", "pkv_paged_decode_attention_mxfp4",
-    "pkv_append_decode_attention_mxfp4",
+    "pkv_append_decode_attention_mxfp4", "pkv_copy_blocks_mxfp4",
     "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add_sequence", "pkv_bm_add_sequence_shared", "pkv_bm_fork",
     "pkv_bm_append_token", "pkv_bm_append_batch", "pkv_bm_free_sequence", "pkv_bm_num_free_blocks",
     "pkv_bm_num_sequences", "pkv_bm_sequence_length", "pkv_bm_block_refcount", "pkv_bm_block_table",
@@ -71,6 +71,7 @@ class StepDesc(ctypes.Structure):
         ("block_tables", ctypes.c_void_p), ("bt_stride", ctypes.c_int32), ("positions", ctypes.c_void_p),
         ("cow_src", ctypes.c_void_p), ("cow_dst", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t), ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("k_mx_scale", ctypes.c_void_p), ("v_mx_scale", ctypes.c_void_p),
     ]
 
 
@@ -87,6 +88,7 @@ class DecoderDesc(ctypes.Structure):
         ("batch_caps", ctypes.c_void_p), ("n_batch_caps", ctypes.c_int32),
         ("ctx_caps", ctypes.c_void_p), ("n_ctx_caps", ctypes.c_int32),
         ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("k_mx_scale", ctypes.c_void_p), ("v_mx_scale", ctypes.c_void_p),
     ]
 
 
@@ -158,6 +160,8 @@ def load_library(path: Optional[str] = None):
     lib.pkv_append_decode_attention_mxfp4.restype = ctypes.c_int
     lib.pkv_copy_blocks_fp8.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, P]
     lib.pkv_copy_blocks_fp8.restype = ctypes.c_int
+    lib.pkv_copy_blocks_mxfp4.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, P]
+    lib.pkv_copy_blocks_mxfp4.restype = ctypes.c_int
     lib.pkv_copy_blocks.argtypes = [ctypes.c_int, P, P, P, P, I32, I32, I32, I32, I32, P]
     lib.pkv_copy_blocks.restype = ctypes.c_int
     U64, C = ctypes.c_uint64, ctypes.c_int
@@ -559,15 +563,19 @@ class StepGraphs:
                  batch_caps, ctx_caps, *, partition_size: int = 0, cow_src=None, cow_dst=None, workspace=None,
                  k_scale=None, v_scale=None):
         torch = _torch()
-        fp8 = k_scale is not None
-        n_blocks, H_kv, bs, D = (_fp8_pools(k_pool, v_pool, k_scale, v_scale) if fp8
+        lowp = k_scale is not None                  # FP8 (float32 scales) or MXFP4 (uint8 scales)
+        mx4 = lowp and k_scale.dtype == torch.uint8
+        fp8 = lowp and not mx4
+        n_blocks, H_kv, bs, D = (_mx4_pools(k_pool, v_pool, k_scale, v_scale) if mx4
+                                 else _fp8_pools(k_pool, v_pool, k_scale, v_scale) if fp8
                                  else _pool_dims(k_pool, v_pool))
         Bmax, H_q = q.shape[0], q.shape[1]
         bcaps = [int(x) for x in batch_caps]
         ccaps = [int(x) for x in ctx_caps]
         _require(bcaps and ccaps and bcaps[-1] <= Bmax, "batch capacities must fit the buffers' rows")
         for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new")):
-            _require(t.dtype == (q.dtype if fp8 else k_pool.dtype), f"{nm} dtype must match the pools (q's for FP8)")
+            _require(t.dtype == (q.dtype if lowp else k_pool.dtype),
+                     f"{nm} dtype must match the pools (q's for FP8 / MXFP4)")
         qrs = _rows(q, "q", H_q, D)
         nrs = _rows(k_new, "k_new", H_kv, D)
         _require(_rows(v_new, "v_new", H_kv, D) == nrs, "k_new and v_new must share a row stride")
@@ -601,6 +609,8 @@ class StepGraphs:
         d.workspace_bytes = workspace.numel() if workspace is not None else 0
         d.k_scale = k_scale.data_ptr() if fp8 else None
         d.v_scale = v_scale.data_ptr() if fp8 else None
+        d.k_mx_scale = k_scale.data_ptr() if mx4 else None
+        d.v_mx_scale = v_scale.data_ptr() if mx4 else None
         self._desc = d
         lib = load_library()
         bc = (ctypes.c_int32 * len(bcaps))(*bcaps)
@@ -639,13 +649,16 @@ class Decoder:
                  partition_size: int = 0, workspace=None, shuffle_seed: int = 0, batch_caps=None, ctx_caps=None,
                  k_scale=None, v_scale=None):
         torch = _torch()
-        fp8 = k_scale is not None
-        n_blocks, H_kv, bs, D = (_fp8_pools(k_pool, v_pool, k_scale, v_scale) if fp8
+        lowp = k_scale is not None                  # FP8 (float32 scales) or MXFP4 (uint8 scales)
+        mx4 = lowp and k_scale.dtype == torch.uint8
+        fp8 = lowp and not mx4
+        n_blocks, H_kv, bs, D = (_mx4_pools(k_pool, v_pool, k_scale, v_scale) if mx4
+                                 else _fp8_pools(k_pool, v_pool, k_scale, v_scale) if fp8
                                  else _pool_dims(k_pool, v_pool))
         max_batch, H_q = q.shape[0], q.shape[1]
         for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new")):
-            _require(t.dtype == (q.dtype if fp8 else k_pool.dtype) and t.shape[0] == max_batch,
-                     f"{nm}: pool dtype (q's for FP8), max_batch rows")
+            _require(t.dtype == (q.dtype if lowp else k_pool.dtype) and t.shape[0] == max_batch,
+                     f"{nm}: pool dtype (q's for FP8 / MXFP4), max_batch rows")
         qrs = _rows(q, "q", H_q, D)
         nrs = _rows(k_new, "k_new", H_kv, D)
         _require(_rows(v_new, "v_new", H_kv, D) == nrs, "k_new and v_new must share a row stride")
@@ -666,6 +679,8 @@ class Decoder:
         d.shuffle_seed = int(shuffle_seed) & ((1 << 64) - 1)
         d.k_scale = k_scale.data_ptr() if fp8 else None
         d.v_scale = v_scale.data_ptr() if fp8 else None
+        d.k_mx_scale = k_scale.data_ptr() if mx4 else None
+        d.v_mx_scale = v_scale.data_ptr() if mx4 else None
         self._caps = None
         if batch_caps is not None:
             bc = (ctypes.c_int32 * len(batch_caps))(*[int(x) for x in batch_caps])
@@ -858,6 +873,19 @@ def _mx4_pools(k_pool, v_pool, k_scale, v_scale):
         _require(t.dtype == torch.uint8 and t.is_contiguous() and tuple(t.shape) == (n_blocks, H_kv, bs, D // 32),
                  f"{nm} must be contiguous uint8 [n_blocks, H_kv, block_size, D/32]")
     return n_blocks, H_kv, bs, D
+
+
+def copy_blocks_mxfp4(k_pool, v_pool, k_scale, v_scale, src, dst, *, stream=None):
+    """copy_blocks for an MXFP4 cache: code and scale bytes of blocks src[i] -> dst[i]."""
+    torch = _torch()
+    n_blocks, H_kv, bs, D = _mx4_pools(k_pool, v_pool, k_scale, v_scale)
+    n = src.shape[0]
+    for t, nm in ((src, "src"), (dst, "dst")):
+        _require(t.dtype == torch.int32 and t.dim() == 1 and t.shape[0] == n and (n <= 1 or t.stride(0) == 1),
+                 f"{nm} must be contiguous int32 [n]")
+    rc = load_library().pkv_copy_blocks_mxfp4(_ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(src),
+                                              _ptr(dst), n, H_kv, D, bs, n_blocks, _stream(stream))
+    _check(rc, "copy_blocks_mxfp4")
 
 
 def kv_append_mxfp4(k_new, v_new, k_pool, v_pool, k_scale, v_scale, block_tables, positions, *, stream=None):

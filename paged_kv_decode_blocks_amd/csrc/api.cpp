@@ -686,6 +686,45 @@ int pkv_copy_blocks_fp8(uint8_t* k_pool, uint8_t* v_pool, float* k_scale, float*
     return PKV_OK;
 }
 
+int pkv_copy_blocks_mxfp4(uint8_t* k_pool, uint8_t* v_pool, uint8_t* k_scale, uint8_t* v_scale, const int32_t* src,
+                          const int32_t* dst, int32_t n, int32_t H_kv, int32_t D, int32_t block_size, int32_t n_blocks,
+                          void* stream) {
+    if (n < 0) return fail(PKV_ERR_INVALID_ARG, "n = %d is negative", n);
+    if (H_kv <= 0) return fail(PKV_ERR_INVALID_ARG, "H_kv = %d must be positive", H_kv);
+    if (D != 64 && D != 128) return fail(PKV_ERR_UNSUPPORTED, "head dim D = %d (built: 64, 128)", D);
+    if (block_size != pkv::kBlockSize)
+        return fail(PKV_ERR_UNSUPPORTED, "block_size = %d (built: %d)", block_size, pkv::kBlockSize);
+    if (n_blocks <= 0) return fail(PKV_ERR_INVALID_ARG, "n_blocks = %d must be positive", n_blocks);
+    if (n == 0) {
+        pkv::clear_error();
+        return PKV_OK;
+    }
+    if (!k_pool || !v_pool || !k_scale || !v_scale || !src || !dst) return fail(PKV_ERR_NULL, "a required pointer is NULL");
+    if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_scale) || !aligned16(v_scale))
+        return fail(PKV_ERR_INVALID_ARG, "pools and scale arrays must be 16-byte aligned");
+    pkv::CopyArgs a{};
+    a.src = src;
+    a.dst = dst;
+    a.n = n;
+    a.n_blocks = n_blocks;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // codes: H_kv * block_size * D/2 bytes per block; scales: H_kv * block_size * D/32 bytes per
+    // block (both multiples of the copy's 16-byte grain)
+    a.k_pool = reinterpret_cast<char*>(k_pool);
+    a.v_pool = reinterpret_cast<char*>(v_pool);
+    a.block_bytes = (int64_t)H_kv * block_size * (D / 2);
+    hipError_t e = pkv::launch_copy_blocks(a, s);
+    if (e == hipSuccess) {
+        a.k_pool = reinterpret_cast<char*>(k_scale);
+        a.v_pool = reinterpret_cast<char*>(v_scale);
+        a.block_bytes = (int64_t)H_kv * block_size * (D / 32);
+        e = pkv::launch_copy_blocks(a, s);
+    }
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "copy_blocks_mxfp4 launch: %s", hipGetErrorString(e));
+    pkv::clear_error();
+    return PKV_OK;
+}
+
 size_t pkv_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t D, int32_t max_context_len,
                                   int32_t partition_size) {
     if (B <= 0 || H_q <= 0 || D <= 0 || max_context_len <= 0 || partition_size <= 0) return 0;

@@ -109,8 +109,9 @@ pkv_decoder* pkv_decoder_create(const pkv_decoder_desc* desc) {
             return nullptr;
         }
     }
-    if (!d.k_scale != !d.v_scale) {
-        fail(PKV_ERR_INVALID_ARG, "k_scale and v_scale must both be set (FP8 pools) or both be NULL");
+    if (!d.k_scale != !d.v_scale || !d.k_mx_scale != !d.v_mx_scale || (d.k_scale && d.k_mx_scale)) {
+        fail(PKV_ERR_INVALID_ARG, "set k_scale and v_scale (FP8 pools) or k_mx_scale and v_mx_scale (MXFP4 pools), "
+             "both of a pair or neither");
         return nullptr;
     }
     if (d.partition_size > 0) {
@@ -135,7 +136,9 @@ pkv_decoder* pkv_decoder_create(const pkv_decoder_desc* desc) {
     dec->meta_len = d.max_batch * (3 + d.bt_stride);
     const size_t bytes = (size_t)dec->meta_len * sizeof(int32_t);
     const int eb = d.dtype == PKV_F32 ? 4 : 2;
-    dec->kv_bytes_per_token = d.k_scale ? 2.0 * d.H_kv * (d.D + 4) : 2.0 * d.H_kv * d.D * eb;
+    dec->kv_bytes_per_token = d.k_scale      ? 2.0 * d.H_kv * (d.D + 4)
+                              : d.k_mx_scale ? 2.0 * d.H_kv * (d.D / 2 + d.D / 32)
+                                             : 2.0 * d.H_kv * d.D * eb;
     hipError_t e = hipStreamCreateWithFlags(&dec->side, hipStreamNonBlocking);
     for (int s = 0; s < 2 && e == hipSuccess; ++s) {
         e = hipHostMalloc(reinterpret_cast<void**>(&dec->host[s]), bytes, hipHostMallocDefault);
@@ -194,6 +197,8 @@ pkv_decoder* pkv_decoder_create(const pkv_decoder_desc* desc) {
             g.workspace_bytes = d.workspace_bytes;
             g.k_scale = d.k_scale;
             g.v_scale = d.v_scale;
+            g.k_mx_scale = d.k_mx_scale;
+            g.v_mx_scale = d.v_mx_scale;
             dec->graphs[s] = pkv_step_graphs_create(&g, dec->bcaps, d.n_batch_caps, dec->ccaps, d.n_ctx_caps);
             if (!dec->graphs[s]) {
                 delete dec;   // pkv_last_error() holds the reason
@@ -257,6 +262,18 @@ int pkv_decoder_step(pkv_decoder* dec, const int64_t* seq_ids, int32_t B, void* 
     const MetaView m = view(dec->dev[s], d.max_batch);
     if (dec->graphs[s]) {
         st = pkv_step_graphs_launch(dec->graphs[s], B, max_len, nc, stream);
+    } else if (d.k_mx_scale) {
+        uint8_t* kp = static_cast<uint8_t*>(d.k_pool);
+        uint8_t* vp = static_cast<uint8_t*>(d.v_pool);
+        st = nc ? pkv_copy_blocks_mxfp4(kp, vp, d.k_mx_scale, d.v_mx_scale, m.cow_src, m.cow_dst, nc, d.H_kv, d.D,
+                                        d.block_size, d.n_blocks, stream)
+                : PKV_OK;
+        if (st == PKV_OK)
+            st = pkv_append_decode_attention_mxfp4(d.dtype, d.out, d.q, d.q_row_stride, d.k_new, d.v_new,
+                                                   d.new_row_stride, kp, vp, d.k_mx_scale, d.v_mx_scale, m.tables,
+                                                   d.bt_stride, m.positions, B, d.H_q, d.H_kv, d.D, d.block_size,
+                                                   d.n_blocks, max_len, d.scale, d.partition_size, d.workspace,
+                                                   d.workspace_bytes, stream);
     } else if (d.k_scale) {
         uint8_t* kp = static_cast<uint8_t*>(d.k_pool);
         uint8_t* vp = static_cast<uint8_t*>(d.v_pool);

@@ -47,14 +47,24 @@ bool strictly_increasing_positive(const int32_t* v, int32_t n) {
 // Enqueue one bucket's step on `s` (capturing).  Returns a pkv_status.
 int enqueue_step(const pkv_step_desc& d, int32_t Bc, int32_t Cc, bool with_copy, hipStream_t s) {
     const bool fp8 = d.k_scale != nullptr;
+    const bool mx4 = d.k_mx_scale != nullptr;
+    uint8_t* kp = static_cast<uint8_t*>(d.k_pool);
+    uint8_t* vp = static_cast<uint8_t*>(d.v_pool);
     if (with_copy) {
-        const int st = fp8 ? pkv_copy_blocks_fp8(static_cast<uint8_t*>(d.k_pool), static_cast<uint8_t*>(d.v_pool),
-                                                 d.k_scale, d.v_scale, d.cow_src, d.cow_dst, Bc, d.H_kv, d.D,
-                                                 d.block_size, d.n_blocks, s)
-                           : pkv_copy_blocks(d.dtype, d.k_pool, d.v_pool, d.cow_src, d.cow_dst, Bc, d.H_kv, d.D,
-                                             d.block_size, d.n_blocks, s);
+        const int st = fp8   ? pkv_copy_blocks_fp8(kp, vp, d.k_scale, d.v_scale, d.cow_src, d.cow_dst, Bc, d.H_kv,
+                                                   d.D, d.block_size, d.n_blocks, s)
+                       : mx4 ? pkv_copy_blocks_mxfp4(kp, vp, d.k_mx_scale, d.v_mx_scale, d.cow_src, d.cow_dst, Bc,
+                                                     d.H_kv, d.D, d.block_size, d.n_blocks, s)
+                             : pkv_copy_blocks(d.dtype, d.k_pool, d.v_pool, d.cow_src, d.cow_dst, Bc, d.H_kv, d.D,
+                                               d.block_size, d.n_blocks, s);
         if (st) return st;
     }
+    if (mx4)
+        return pkv_append_decode_attention_mxfp4(d.dtype, d.out, d.q, d.q_row_stride, d.k_new, d.v_new,
+                                                 d.new_row_stride, kp, vp, d.k_mx_scale, d.v_mx_scale,
+                                                 d.block_tables, d.bt_stride, d.positions, Bc, d.H_q, d.H_kv, d.D,
+                                                 d.block_size, d.n_blocks, Cc, d.scale, d.partition_size,
+                                                 d.workspace, d.workspace_bytes, s);
     if (fp8)
         return pkv_append_decode_attention_fp8(d.dtype, d.out, d.q, d.q_row_stride, d.k_new, d.v_new,
                                                d.new_row_stride, static_cast<uint8_t*>(d.k_pool),
@@ -94,8 +104,10 @@ pkv_step_graphs* pkv_step_graphs_create(const pkv_step_desc* desc, const int32_t
         fail(PKV_ERR_INVALID_ARG, "cow_src and cow_dst must both be set or both be NULL");
         return nullptr;
     }
-    if (!desc->k_scale != !desc->v_scale) {
-        fail(PKV_ERR_INVALID_ARG, "k_scale and v_scale must both be set (FP8 pools) or both be NULL");
+    if (!desc->k_scale != !desc->v_scale || !desc->k_mx_scale != !desc->v_mx_scale ||
+        (desc->k_scale && desc->k_mx_scale)) {
+        fail(PKV_ERR_INVALID_ARG, "set k_scale and v_scale (FP8 pools) or k_mx_scale and v_mx_scale (MXFP4 pools), "
+             "both of a pair or neither");
         return nullptr;
     }
     const int32_t maxB = batch_caps[n_batch - 1], maxC = ctx_caps[n_ctx - 1];

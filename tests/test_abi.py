@@ -191,6 +191,26 @@ def test_mxfp4_validation(lib):
     assert f(*bad) == OK
 
 
+def test_copy_blocks_mxfp4_validation(lib):
+    f = lib.pkv_copy_blocks_mxfp4
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 8, 128, 16, 64, None]
+    bad = list(args)
+    bad[8] = 96                         # D
+    assert f(*bad) == E_UNSUP
+    bad = list(args)
+    bad[3] = None                       # v_scale
+    assert f(*bad) == E_NULL
+    bad = list(args)
+    bad[2] = FAKE + 4                   # k_scale not 16-byte aligned
+    assert f(*bad) == E_ARG
+    bad = list(args)
+    bad[6] = 0                          # n = 0: nothing to do
+    assert f(*bad) == OK
+    bad = list(args)
+    bad[6] = -1
+    assert f(*bad) == E_ARG
+
+
 def test_binding_refuses_missing_library(tmp_path):
     with pytest.raises(pkv.PkvError):
         pkv.load_library(str(tmp_path / "nope.so"))

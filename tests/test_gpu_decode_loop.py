@@ -248,6 +248,31 @@ def test_copy_blocks_bit_exact(torch_dev, dtype, H_kv, D):
     assert bits_equal(to_numpy_bits(v, dtype), vp)
 
 
+@pytest.mark.parametrize("H_kv,D", [(8, 128), (2, 64), (1, 64)])
+def test_copy_blocks_mxfp4_bit_exact(torch_dev, H_kv, D):
+    """Code and scale bytes of whole blocks move unchanged; the neighbours of every
+    destination block (the scale tiles are only 32 or 64 bytes per head) stay as they were."""
+    t = torch_dev
+    rng = np.random.default_rng(11)
+    n_blocks = 30
+    kp = rng.integers(0, 256, (n_blocks, H_kv, BS, D // 2), dtype=np.uint8)
+    vp = rng.integers(0, 256, (n_blocks, H_kv, BS, D // 2), dtype=np.uint8)
+    ks = rng.integers(0, 256, (n_blocks, H_kv, BS, D // 32), dtype=np.uint8)
+    vs = rng.integers(0, 256, (n_blocks, H_kv, BS, D // 32), dtype=np.uint8)
+    perm = rng.permutation(n_blocks)
+    src, dst = perm[:9].astype(np.int32), perm[9:18].astype(np.int32)
+    src[2] = -1
+    dst[6] = n_blocks                       # out of range: skipped
+    dev = [t.from_numpy(a.copy()).cuda() for a in (kp, vp, ks, vs)]
+    pkv.copy_blocks_mxfp4(*dev, t.from_numpy(src).cuda(), t.from_numpy(dst).cuda())
+    t.cuda.synchronize()
+    pairs = [(int(a), int(b)) for a, b in zip(src, dst) if 0 <= a < n_blocks and 0 <= b < n_blocks]
+    oracle_copy_blocks(kp, vp, pairs)
+    oracle_copy_blocks(ks, vs, pairs)
+    for d, r in zip(dev, (kp, vp, ks, vs)):
+        assert bits_equal(d.cpu().numpy(), r)
+
+
 @pytest.mark.parametrize("H_kv,D", [(8, 128), (2, 64)])
 def test_copy_blocks_fp8_bit_exact(torch_dev, H_kv, D):
     t = torch_dev

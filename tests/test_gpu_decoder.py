@@ -26,17 +26,21 @@ def torch_dev():
     return torch
 
 
-@pytest.mark.parametrize("dtype,H_q,H_kv,D,P,graphs,seed,fp8", [
-    ("f16", 8, 2, 128, 32, True, 301, False),
-    ("bf16", 8, 8, 128, 0, True, 302, False),
-    ("f32", 4, 4, 64, 0, False, 303, False),
-    ("bf16", 16, 2, 128, 64, False, 304, False),
-    ("bf16", 8, 2, 128, 32, False, 305, True),
-    ("f16", 4, 4, 64, 0, True, 306, True),
+@pytest.mark.parametrize("dtype,H_q,H_kv,D,P,graphs,seed,kv", [
+    ("f16", 8, 2, 128, 32, True, 301, "16"),
+    ("bf16", 8, 8, 128, 0, True, 302, "16"),
+    ("f32", 4, 4, 64, 0, False, 303, "16"),
+    ("bf16", 16, 2, 128, 64, False, 304, "16"),
+    ("bf16", 8, 2, 128, 32, False, 305, "fp8"),
+    ("f16", 4, 4, 64, 0, True, 306, "fp8"),
+    ("bf16", 8, 2, 128, 32, True, 307, "mx4"),     # grouped MFMA kernel, split, graphs
+    ("f16", 4, 4, 128, 0, False, 308, "mx4"),      # per-head kernel, eager
+    ("f32", 4, 2, 64, 64, True, 309, "mx4"),       # per-head kernel (f32 q), split, graphs
 ])
-def test_decoder_matches_oracle(torch_dev, dtype, H_q, H_kv, D, P, graphs, seed, fp8):
+def test_decoder_matches_oracle(torch_dev, dtype, H_q, H_kv, D, P, graphs, seed, kv):
     t = torch_dev
-    print(f"decoder {dtype} H_q={H_q} H_kv={H_kv} D={D} P={P} graphs={graphs} seed={seed} fp8={fp8}", flush=True)
+    fp8, mx4 = kv == "fp8", kv == "mx4"
+    print(f"decoder {dtype} H_q={H_q} H_kv={H_kv} D={D} P={P} graphs={graphs} seed={seed} kv={kv}", flush=True)
     rng = np.random.default_rng(seed)
     Bmax, W, n_blocks = 8, 12, 120
     scale = 1.0 / math.sqrt(D)
@@ -44,6 +48,12 @@ def test_decoder_matches_oracle(torch_dev, dtype, H_q, H_kv, D, P, graphs, seed,
     if fp8:
         kp = np.full((n_blocks, H_kv, BS, D), 0x7F, np.uint8)
         ksc = np.full((n_blocks, H_kv, BS), np.nan, np.float32)
+        vsc = ksc.copy()
+        k, v = t.from_numpy(kp.copy()).cuda(), t.from_numpy(kp.copy()).cuda()
+        ks_d, vs_d = t.from_numpy(ksc.copy()).cuda(), t.from_numpy(vsc.copy()).cuda()
+    elif mx4:   # unwritten slots: code 7 (6.0) under scale byte 255 (NaN)
+        kp = np.full((n_blocks, H_kv, BS, D // 2), 0x77, np.uint8)
+        ksc = np.full((n_blocks, H_kv, BS, D // 32), 0xFF, np.uint8)
         vsc = ksc.copy()
         k, v = t.from_numpy(kp.copy()).cuda(), t.from_numpy(kp.copy()).cuda()
         ks_d, vs_d = t.from_numpy(ksc.copy()).cuda(), t.from_numpy(vsc.copy()).cuda()
@@ -56,7 +66,7 @@ def test_decoder_matches_oracle(torch_dev, dtype, H_q, H_kv, D, P, graphs, seed,
     vn_buf = t.zeros((Bmax, H_kv, D), dtype=tdt, device="cuda")
     out_buf = t.zeros((Bmax, H_q, D), dtype=t.float32, device="cuda")
     caps = dict(batch_caps=[2, 4, 8], ctx_caps=[64, 128, W * BS]) if graphs else {}
-    if fp8:
+    if fp8 or mx4:
         caps.update(k_scale=ks_d, v_scale=vs_d)
     dec = pkv.Decoder(q_buf, kn_buf, vn_buf, k, v, out_buf, scale, W, partition_size=P, shuffle_seed=seed, **caps)
     bm, ora = dec.block_manager, OracleBM(n_blocks, BS, seed)
@@ -75,6 +85,10 @@ def test_decoder_matches_oracle(torch_dev, dtype, H_q, H_kv, D, P, graphs, seed,
             oracle.kv_append_fp8(dtype, kn, vn, kp, vp, ksc, vsc, bt, pos, BS)
             pkv.kv_append_fp8(to_tensor(kn, dtype, "cuda"), to_tensor(vn, dtype, "cuda"), k, v, ks_d, vs_d,
                               t.from_numpy(bt).cuda(), t.from_numpy(pos).cuda())
+        elif mx4:
+            oracle.kv_append_mxfp4(dtype, kn, vn, kp, vp, ksc, vsc, bt, pos, BS)
+            pkv.kv_append_mxfp4(to_tensor(kn, dtype, "cuda"), to_tensor(vn, dtype, "cuda"), k, v, ks_d, vs_d,
+                                t.from_numpy(bt).cuda(), t.from_numpy(pos).cuda())
         else:
             oracle.kv_append(dtype, kn, vn, kp, vp, bt, pos, BS)
             pkv.kv_append(to_tensor(kn, dtype, "cuda"), to_tensor(vn, dtype, "cuda"), k, v,
@@ -120,6 +134,10 @@ def test_decoder_matches_oracle(torch_dev, dtype, H_q, H_kv, D, P, graphs, seed,
             oracle_copy_blocks(ksc, vsc, copies)
             oracle.kv_append_fp8(dtype, kn, vn, kp, vp, ksc, vsc, tables, positions, BS)
             ref = oracle.paged_decode_attention_fp8(dtype, q, kp, vp, ksc, vsc, tables, positions + 1, scale)
+        elif mx4:
+            oracle_copy_blocks(ksc, vsc, copies)
+            oracle.kv_append_mxfp4(dtype, kn, vn, kp, vp, ksc, vsc, tables, positions, BS)
+            ref = oracle.paged_decode_attention_mxfp4(dtype, q, kp, vp, ksc, vsc, tables, positions + 1, scale)
         else:
             oracle.kv_append(dtype, kn, vn, kp, vp, tables, positions, BS)
             ref = oracle.paged_decode_attention(dtype, q, kp, vp, tables, positions + 1, scale)
@@ -132,7 +150,7 @@ def test_decoder_matches_oracle(torch_dev, dtype, H_q, H_kv, D, P, graphs, seed,
         for sid in ids:
             assert list(bm.block_table(sid)) == ora.block_table(sid)
     assert total_copies > 0, "the stream never exercised copy-on-write"
-    if fp8:
+    if fp8 or mx4:
         assert bits_equal(k.cpu().numpy(), kp) and bits_equal(v.cpu().numpy(), vp)
         assert bits_equal(ks_d.cpu().numpy(), ksc) and bits_equal(vs_d.cpu().numpy(), vsc)
     else:
