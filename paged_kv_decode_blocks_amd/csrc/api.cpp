@@ -231,8 +231,8 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
         if (p.kind == 1) {   // blocks stream through an LDS ring, pf blocks ahead per wave
             p.nw = env_int("PKV_MX4_NW", 4);
             p.ch = 1;
-            p.pf = env_int("PKV_MX4_PF", 2);
-            if (!pkv::mxfp4_mfma_variant_exists(p.nw, p.pf)) { p.nw = 4; p.pf = 2; }
+            p.pf = env_int("PKV_MX4_PF", 1);
+            if (!pkv::mxfp4_mfma_variant_exists(p.nw, p.pf)) { p.nw = 4; p.pf = 1; }
             p.grid = (unsigned)((int64_t)p.n_parts * B * H_kv);
         } else {
             p.nw = env_int("PKV_MX4_NW", 4);

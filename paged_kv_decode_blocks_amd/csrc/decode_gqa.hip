@@ -130,16 +130,18 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
 // KL 16-byte reads from LDS, completed before return.  Issued as inline asm: the
 // compiler cannot tell a ring slot from the LDS DMAs still in flight into the
 // other slots and would drain every load before a plain LDS read; the caller's
-// own vmcnt wait orders the read after the DMA that filled the slot.
+// own vmcnt wait orders the read after the DMA that filled the slot.  The outputs
+// are early-clobber: a read's destination must not share a register with an
+// address that a later read of the same statement still uses.
 template <int KL>
 __device__ __forceinline__ void lds_read16x(const char* base, const int (&off)[KL], uint4 (&r)[KL]) {
 #if defined(__HIP_DEVICE_COMPILE__)
     const uint32_t a0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)base;
     if constexpr (KL == 1) {
-        asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r[0]) : "v"(a0 + off[0]) : "memory");
+        asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r[0]) : "v"(a0 + off[0]) : "memory");
     } else if constexpr (KL == 2) {
         asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
-                     : "=v"(r[0]), "=v"(r[1])
+                     : "=&v"(r[0]), "=&v"(r[1])
                      : "v"(a0 + off[0]), "v"(a0 + off[1])
                      : "memory");
     } else {
@@ -147,7 +149,7 @@ __device__ __forceinline__ void lds_read16x(const char* base, const int (&off)[K
         asm volatile(
             "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
             "s_waitcnt lgkmcnt(0)"
-            : "=v"(r[0]), "=v"(r[1]), "=v"(r[2]), "=v"(r[3])
+            : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
             : "v"(a0 + off[0]), "v"(a0 + off[1]), "v"(a0 + off[2]), "v"(a0 + off[3])
             : "memory");
     }

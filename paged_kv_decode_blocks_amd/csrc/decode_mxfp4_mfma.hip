@@ -229,22 +229,35 @@ struct Mx4Lane {
         }
     }
 
-    // LO: two blocks, 32 tokens in one K=32 output product per tile.
-    template <bool MASK>
-    __device__ __forceinline__ void accumulate_pair(const Mx4Chunk<D, 2>& ck, const bool (&valid)[2][4]) {
-        float sc[2][4];
-        scores<2>(ck, 0, sc[0]);
-        __builtin_amdgcn_sched_barrier(0);
-        scores<2>(ck, 1, sc[1]);
-        __builtin_amdgcn_sched_barrier(0);
-        rescale<2, MASK>(sc, valid);
+    // LO: two blocks, 32 tokens in one K=32 output product per tile, in two stages
+    // so that a wave overlaps one chunk's score products with the previous
+    // chunk's softmax and output products (the caller runs scores(i) and
+    // finish(i - 1) back to back, in one basic block).
+    struct PairStage {
+        uint32_t v[2][4];      // V code words of the lane's four tokens, per block
+        uint32_t vs[2][4];     // their scale bytes; 0 (2^-127, finite) for masked tokens
+        float sc[2][4];        // scores, log2 domain
+        bool valid[2][4];      // token 4 i + j of block cb lies below the length
+    };
+
+    __device__ __forceinline__ void pair_scores(const Mx4Chunk<D, 2>& ck, PairStage& ps) {
+        scores<2>(ck, 0, ps.sc[0]);
+        scores<2>(ck, 1, ps.sc[1]);
+    }
+
+    // Softmax update and output products of a chunk whose scores are in ps.  Masked
+    // tokens get weight 0 and their V rows decode to finite values (scale byte 0),
+    // so their K and V bytes (unwritten slots hold NaN scale bytes) never reach the
+    // accumulators.
+    __device__ __forceinline__ void pair_finish(const PairStage& ps) {
+        rescale<2, true>(ps.sc, ps.valid);
         uint32_t pw[2][2];     // per block: packed weights of tokens (0, 1) and (2, 3), hi or lo half
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
             float p[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                p[i] = (!MASK || valid[cb][i]) ? __builtin_amdgcn_exp2f(sc[cb][i] - m) : 0.0f;
+                p[i] = ps.valid[cb][i] ? __builtin_amdgcn_exp2f(ps.sc[cb][i] - m) : 0.0f;
                 l += p[i];
             }
             uint32_t h01, l01, h23, l23;
@@ -258,24 +271,21 @@ struct Mx4Lane {
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) vsc[cb][i] = mx_operand(ck.vs[cb][i]);
-        // two output tiles per byte of the V pieces, decoded as they are used (keeps
-        // the live registers down; the barriers stop the scheduler from hoisting
-        // every conversion to the top)
-        pv_pair<0>(ck, vsc, pk);
-        if constexpr (VT / 2 > 1) pv_pair<1>(ck, vsc, pk);
-        if constexpr (VT / 2 > 2) pv_pair<2>(ck, vsc, pk);
-        if constexpr (VT / 2 > 3) pv_pair<3>(ck, vsc, pk);
+            for (int i = 0; i < 4; ++i) vsc[cb][i] = mx_operand(ps.vs[cb][i]);
+        pv_pair<0>(ps, vsc, pk);
+        if constexpr (VT / 2 > 1) pv_pair<1>(ps, vsc, pk);
+        if constexpr (VT / 2 > 2) pv_pair<2>(ps, vsc, pk);
+        if constexpr (VT / 2 > 3) pv_pair<3>(ps, vsc, pk);
     }
 
     // Output tiles 2X and 2X + 1 of a two-block chunk: byte X of each V piece.
     template <int X>
-    __device__ __forceinline__ void pv_pair(const Mx4Chunk<D, 2>& ck, const float (&vsc)[2][4], const uint4& pk) {
+    __device__ __forceinline__ void pv_pair(const PairStage& ps, const float (&vsc)[2][4], const uint4& pk) {
         uint32_t d0[4], d1[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            d0[i] = e2m1x2_to_bf16<X>(ck.v[0][i], vsc[0][i]);
-            d1[i] = e2m1x2_to_bf16<X>(ck.v[1][i], vsc[1][i]);
+            d0[i] = e2m1x2_to_bf16<X>(ps.v[0][i], vsc[0][i]);
+            d1[i] = e2m1x2_to_bf16<X>(ps.v[1][i], vsc[1][i]);
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -286,7 +296,6 @@ struct Mx4Lane {
             const uint32_t b23 = __builtin_amdgcn_perm(d1[3], d1[2], sel);
             acc[2 * X + h] = mma_bf16(make_uint4(a01, a23, b01, b23), pk, acc[2 * X + h]);
         }
-        __builtin_amdgcn_sched_barrier(0);
     }
 
     // Not LO: one block at a time, hi and lo halves of P in the k-slots of one product.
@@ -350,6 +359,8 @@ __device__ __forceinline__ void wait_vm() {
 // Issued as inline asm: the compiler cannot tell this slot from the DMAs still in
 // flight into the other slots and would drain every load before a plain LDS read;
 // the caller's vmcnt wait orders these reads after the DMAs that filled the slot.
+// The outputs are early-clobber: a read's destination must not share a register
+// with an address that a later read of the same statement still uses.
 // Offsets: K codes at ka (16 bytes; for D = 64 two words at ka and ka + 256), K scale byte at ksa, V pieces at va +
 // i * VSTEP (4 or 2 bytes), V scale bytes at vsa + i * SSTEP.
 template <int D>
@@ -372,8 +383,8 @@ __device__ __forceinline__ void lds_block(uint32_t ka, uint32_t ksa, uint32_t va
             "ds_read_u8 %8, %13 offset:%18\n\t"
             "ds_read_u8 %9, %13 offset:%19\n\t"
             "s_waitcnt lgkmcnt(0)"
-            : "=v"(kk), "=v"(ks), "=v"(v[0]), "=v"(v[1]), "=v"(v[2]), "=v"(v[3]), "=v"(vs[0]), "=v"(vs[1]),
-              "=v"(vs[2]), "=v"(vs[3])
+            : "=&v"(kk), "=&v"(ks), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(vs[0]), "=&v"(vs[1]),
+              "=&v"(vs[2]), "=&v"(vs[3])
             : "v"(ka), "v"(ksa), "v"(va), "v"(vsa), "i"(VSTEP), "i"(2 * VSTEP), "i"(3 * VSTEP), "i"(SSTEP),
               "i"(2 * SSTEP), "i"(3 * SSTEP)
             : "memory");
@@ -392,8 +403,8 @@ __device__ __forceinline__ void lds_block(uint32_t ka, uint32_t ksa, uint32_t va
             "ds_read_u8 %9, %14 offset:%19\n\t"
             "ds_read_u8 %10, %14 offset:%20\n\t"
             "s_waitcnt lgkmcnt(0)"
-            : "=v"(k[0]), "=v"(k[1]), "=v"(ks), "=v"(v[0]), "=v"(v[1]), "=v"(v[2]), "=v"(v[3]), "=v"(vs[0]),
-              "=v"(vs[1]), "=v"(vs[2]), "=v"(vs[3])
+            : "=&v"(k[0]), "=&v"(k[1]), "=&v"(ks), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(vs[0]),
+              "=&v"(vs[1]), "=&v"(vs[2]), "=&v"(vs[3])
             : "v"(ka), "v"(ksa), "v"(va), "v"(vsa), "i"(VSTEP), "i"(2 * VSTEP), "i"(3 * VSTEP), "i"(SSTEP),
               "i"(2 * SSTEP), "i"(3 * SSTEP)
             : "memory");
@@ -559,13 +570,30 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) valid[cb][q] = true;
         }
-        if constexpr (LO) {
-            if (full) st.template accumulate_pair<false>(ck, valid);
-            else st.template accumulate_pair<true>(ck, valid);
-        } else {
+        if constexpr (!LO) {
             if (full) st.template accumulate<false>(ck, valid);
             else st.template accumulate<true>(ck, valid);
         }
+    };
+    // LO, stage A of chunk i from its slots: read, mark the tokens below lim, scores.
+    // Branch-free, so that it shares a basic block with the previous chunk's stage B.
+    auto stage_scores = [&](int slot, int i, int tok_r, typename L::PairStage& ps) {
+        Mx4Chunk<D, 2> ck;
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            const uint32_t base = my_ring_a + (2 * slot + cb) * SLOT;
+            lds_block<D>(base + k_rd, base + ks_rd, base + v_rd, base + vs_rd, ck.k[cb], ck.ks[cb], ck.v[cb],
+                         ck.vs[cb]);
+            const int blk = blk_of(i, cb);
+            const int tb = blk < nr ? tok_r + blk * kBlockSize : lim;   // a copied block is wholly masked
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                ps.valid[cb][q] = tb + 4 * q + j < lim;
+                ps.v[cb][q] = ck.v[cb][q];
+                ps.vs[cb][q] = ps.valid[cb][q] ? ck.vs[cb][q] : 0u;
+            }
+        }
+        st.pair_scores(ck, ps);
     };
 
     if (threadIdx.x == 0) s_bad = 0;
@@ -599,6 +627,44 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
         const int tok_r = start + r0 * kBlockSize;
         const int nbw = w < nr ? (nr - w + NW - 1) / NW : 0;   // this wave's blocks: w + NW i
         const int nb = (nbw + CH - 1) / CH;                      // ... in chunks of CH
+        if constexpr (LO) {
+            // chunk i is read from slot i % R; the DMAs of chunk i + PF go into the slot
+            // chunk i - 1 was read from.  Iteration i runs scores(i), then finish(i - 1).
+            typename L::PairStage prev, cur;
+            int i = 1;
+            if (nb >= R + PF + 1) {
+                // unconditional prologue (keeps the loop's waits exact): chunks 0 .. PF
+#pragma unroll
+                for (int v = 0; v <= PF; ++v) issue(v, v);
+                wait_vm<PF * LPC>();
+                stage_scores(0, 0, tok_r, prev);
+                for (; i + R + PF <= nb; i += R) {   // i = 1 mod R: read slot (1 + v) % R, refill slot v
+#pragma unroll
+                    for (int v = 0; v < R; ++v) {
+                        issue(v, i + v + PF);
+                        wait_vm<PF * LPC>();
+                        stage_scores((1 + v) % R, i + v, tok_r, cur);
+                        st.pair_finish(prev);
+                        prev = cur;
+                    }
+                }
+            } else if (nb > 0) {
+#pragma unroll
+                for (int v = 0; v <= PF; ++v)
+                    if (v < nb) issue(v, v);
+                wait_vm<0>();
+                stage_scores(0, 0, tok_r, prev);
+            }
+            for (; i < nb; ++i) {   // the last chunks
+                if (i + PF < nb) issue((i + PF) % R, i + PF);
+                wait_vm<0>();
+                stage_scores(i % R, i, tok_r, cur);
+                st.pair_finish(prev);
+                prev = cur;
+            }
+            if (nb > 0) st.pair_finish(prev);
+            continue;
+        }
         int i = 0;
         if (nb >= R + PF) {
             // unconditional prologue, so the loop is entered with the same DMAs in
