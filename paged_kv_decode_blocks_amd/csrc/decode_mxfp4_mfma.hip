@@ -355,6 +355,23 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
+// Wait until at most n chunks' DMAs (LPC instructions each) are outstanding, for a
+// runtime n in [0, MAXN]: DMAs complete in issue order, so this is the exact wait
+// for the oldest chunk when n later chunks have been issued after it.
+template <int LPC, int MAXN>
+__device__ __forceinline__ void wait_chunks(int n) {
+    if constexpr (MAXN >= 3) {
+        if (n >= 3) { wait_vm<3 * LPC>(); return; }
+    }
+    if constexpr (MAXN >= 2) {
+        if (n == 2) { wait_vm<2 * LPC>(); return; }
+    }
+    if constexpr (MAXN >= 1) {
+        if (n == 1) { wait_vm<LPC>(); return; }
+    }
+    wait_vm<0>();
+}
+
 // One block of the ring -> registers in the MFMA layout, completed before return.
 // Issued as inline asm: the compiler cannot tell this slot from the DMAs still in
 // flight into the other slots and would drain every load before a plain LDS read;
@@ -652,12 +669,12 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
 #pragma unroll
                 for (int v = 0; v <= PF; ++v)
                     if (v < nb) issue(v, v);
-                wait_vm<0>();
+                wait_chunks<LPC, PF>(min(nb - 1, PF));
                 stage_scores(0, 0, tok_r, prev);
             }
-            for (; i < nb; ++i) {   // the last chunks
+            for (; i < nb; ++i) {   // the last chunks: wait for chunk i only
                 if (i + PF < nb) issue((i + PF) % R, i + PF);
-                wait_vm<0>();
+                wait_chunks<LPC, PF>(min(nb - 1 - i, PF));
                 stage_scores(i % R, i, tok_r, cur);
                 st.pair_finish(prev);
                 prev = cur;
