@@ -348,15 +348,19 @@ struct GqaLane {
     }
 };
 
-// Work unit of a workgroup: (partition, request, KV head) from the block index.
+// Work unit of a workgroup: (partition, request, KV head) from the block index,
+// KV head fastest.  PAIR deals neighbouring KV heads to one XCD (xcd_pair_unit),
+// for the FP8 kernel whose per-(block, head) scale pieces share lines in pairs.
 struct GqaUnit {
     int part, b, g, n, start, end, lim, pos_new, first_blk;
 };
 
+template <bool PAIR = false>
 __device__ __forceinline__ void gqa_indices(const AttnArgs& a, GqaUnit& u) {
     const int BG = a.B * a.H_kv;
-    u.part = blockIdx.x / BG;
-    const int bg = blockIdx.x - u.part * BG;
+    const int x = PAIR ? xcd_pair_unit(blockIdx.x, a.n_parts * BG) : (int)blockIdx.x;
+    u.part = x / BG;
+    const int bg = x - u.part * BG;
     u.b = bg / a.H_kv;
     u.g = bg - u.b * a.H_kv;
     u.first_blk = u.part * (a.part_tokens / kBlockSize);
@@ -1100,7 +1104,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_gqa_fp8_kernel(const Attn
     __shared__ float s_o[NW * 16 * (D + 4)];
 
     GqaUnit u;
-    gqa_indices(a, u);
+    gqa_indices<true>(a, u);
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     L st;
