@@ -52,12 +52,25 @@ __device__ __forceinline__ floatx4 mma_bf16(const uint4& a, const uint4& b, floa
                                                    0, 0, 0);
 }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// (p0, p1) -> packed bf16, round to nearest even (one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16(float p0, float p1) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){p0, p1}, bf162_t));
+}
+
 // p0, p1 -> packed bf16 (hi0, hi1) and (lo0, lo1) with p ~= hi + lo (to ~2^-17)
 __device__ __forceinline__ void split_bf16(float p0, float p1, uint32_t& hi, uint32_t& lo) {
-    const bf162_t h = {(__bf16)p0, (__bf16)p1};
-    const bf162_t r = {(__bf16)(p0 - (float)h.x), (__bf16)(p1 - (float)h.y)};
-    hi = __builtin_bit_cast(uint32_t, h);
-    lo = __builtin_bit_cast(uint32_t, r);
+    hi = pack_bf16(p0, p1);
+    lo = pack_bf16(p0 - __uint_as_float(hi << 16), p1 - __uint_as_float(hi & 0xffff0000u));
+}
+
+// One half of split_bf16 per lane: the hi pair when lo_mul = 0, the lo pair when
+// lo_mul = 1 (p - 1 * hi is exact, p - 0 * hi is p).
+__device__ __forceinline__ uint32_t split_half_bf16(float p0, float p1, float lo_mul) {
+    const uint32_t hi = pack_bf16(p0, p1);
+    return pack_bf16(fmaf(-lo_mul, __uint_as_float(hi << 16), p0),
+                     fmaf(-lo_mul, __uint_as_float(hi & 0xffff0000u), p1));
 }
 
 // Max / sum over the four lane groups (lanes 16 apart) with the gfx950 lane swaps:
@@ -128,7 +141,7 @@ struct Mx4Lane {
     using Geo = Mx4Geo<D>;
     static constexpr int KS = Geo::KS, VT = Geo::VT, NQ = QDT == DT_F16 ? 2 : 1;
     int j, c;
-    bool lo_lane;              // this lane's column carries the lo half of P
+    float lo_mul;              // 1 if this lane's column carries the lo half of P, else 0
     uint4 qf[NQ][KS];          // B operand of step s (bf16; [1] = lo part of an f16 q)
     floatx4 acc[VT];
     float m, l, scale_log2;
@@ -142,7 +155,7 @@ struct Mx4Lane {
             qf[0][s] = make_uint4(0, 0, 0, 0);
             if constexpr (NQ == 2) qf[1][s] = make_uint4(0, 0, 0, 0);
         }
-        lo_lane = LO && c >= a.G;
+        lo_mul = (LO && c >= a.G) ? 1.0f : 0.0f;
         if (c < (LO ? 2 : 1) * a.G) {
             const int h = c < a.G ? c : c - a.G;
             const char* qp = a.q + ((int64_t)b * a.q_row_stride + (int64_t)(g * a.G + h) * D + 8 * KS * j) * 2;
@@ -236,8 +249,7 @@ struct Mx4Lane {
     struct PairStage {
         uint32_t v[2][4];      // V code words of the lane's four tokens, per block
         uint32_t vs[2][4];     // their scale bytes; 0 (2^-127, finite) for masked tokens
-        float sc[2][4];        // scores, log2 domain
-        bool valid[2][4];      // token 4 i + j of block cb lies below the length
+        float sc[2][4];        // scores, log2 domain; -inf for masked tokens
     };
 
     __device__ __forceinline__ void pair_scores(const Mx4Chunk<D, 2>& ck, PairStage& ps) {
@@ -246,25 +258,24 @@ struct Mx4Lane {
     }
 
     // Softmax update and output products of a chunk whose scores are in ps.  Masked
-    // tokens get weight 0 and their V rows decode to finite values (scale byte 0),
-    // so their K and V bytes (unwritten slots hold NaN scale bytes) never reach the
-    // accumulators.
+    // tokens carry a score of -inf, so they take no part in the max and get weight
+    // exp2(-inf) = 0 (m is always finite), and their V rows decode to finite values
+    // (scale byte 0), so their K and V bytes (unwritten slots hold NaN scale bytes)
+    // never reach the accumulators.
     __device__ __forceinline__ void pair_finish(const PairStage& ps) {
-        rescale<2, true>(ps.sc, ps.valid);
+        const bool unused[2][4] = {};   // no mask: masked scores are -inf
+        rescale<2, false>(ps.sc, unused);
         uint32_t pw[2][2];     // per block: packed weights of tokens (0, 1) and (2, 3), hi or lo half
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
             float p[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                p[i] = ps.valid[cb][i] ? __builtin_amdgcn_exp2f(ps.sc[cb][i] - m) : 0.0f;
+                p[i] = __builtin_amdgcn_exp2f(ps.sc[cb][i] - m);
                 l += p[i];
             }
-            uint32_t h01, l01, h23, l23;
-            split_bf16(p[0], p[1], h01, l01);
-            split_bf16(p[2], p[3], h23, l23);
-            pw[cb][0] = lo_lane ? l01 : h01;
-            pw[cb][1] = lo_lane ? l23 : h23;
+            pw[cb][0] = split_half_bf16(p[0], p[1], lo_mul);
+            pw[cb][1] = split_half_bf16(p[2], p[3], lo_mul);
         }
         const uint4 pk = make_uint4(pw[0][0], pw[0][1], pw[1][0], pw[1][1]);
         float vsc[2][4];
@@ -601,16 +612,22 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
             const uint32_t base = my_ring_a + (2 * slot + cb) * SLOT;
             lds_block<D>(base + k_rd, base + ks_rd, base + v_rd, base + vs_rd, ck.k[cb], ck.ks[cb], ck.v[cb],
                          ck.vs[cb]);
-            const int blk = blk_of(i, cb);
-            const int tb = blk < nr ? tok_r + blk * kBlockSize : lim;   // a copied block is wholly masked
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                ps.valid[cb][q] = tb + 4 * q + j < lim;
-                ps.v[cb][q] = ck.v[cb][q];
-                ps.vs[cb][q] = ps.valid[cb][q] ? ck.vs[cb][q] : 0u;
-            }
+            for (int q = 0; q < 4; ++q) ps.v[cb][q] = ck.v[cb][q];
         }
         st.pair_scores(ck, ps);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            const int blk = blk_of(i, cb);
+            // token 4 q + j of the block is valid iff 4 q < rem (a copied block is wholly masked)
+            const int rem = blk < nr ? lim - (tok_r + blk * kBlockSize) - j : 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const bool valid = 4 * q < rem;
+                ps.sc[cb][q] = valid ? ps.sc[cb][q] : -__builtin_inff();
+                ps.vs[cb][q] = valid ? ck.vs[cb][q] : 0u;
+            }
+        }
     };
 
     if (threadIdx.x == 0) s_bad = 0;
