@@ -45,6 +45,9 @@ namespace {
 constexpr int kWin = 256;                 // block ids staged per window
 constexpr float kSlack = 8.0f;            // log2 units: weights stay below 256
 
+template <bool B>
+struct Flag { static constexpr bool value = B; };
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ floatx4 mma_bf16(const uint4& a, const uint4& b, floatx4 c) {
@@ -516,8 +519,10 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
     const int kdma = D == 128 ? tau * RB + 16 * j : tau * RB + 8 * j;   // + 4 h for D = 64
     const bool sc_lane = lane < 8 * SB;                                  // 4 SB lanes per scale tile
     const int sdma = lane < 4 * SB ? 4 * lane : 4 * (lane - 4 * SB);
-    const size_t blk_codes = (size_t)a.H_kv * kBlockSize * RB;
-    const size_t blk_sc = (size_t)a.H_kv * kBlockSize * SB;
+    // per-block strides fit 32 bits (H_kv * 16 * D / 2); block id x stride is formed
+    // as a 32 x 32 -> 64-bit product of wave-uniform values, on the scalar unit
+    const uint32_t blk_codes = (uint32_t)a.H_kv * kBlockSize * RB;
+    const uint32_t blk_sc = (uint32_t)a.H_kv * kBlockSize * SB;
     const uint8_t* kp = reinterpret_cast<const uint8_t*>(a.k_pool) + (size_t)g * kBlockSize * RB;
     const uint8_t* vp = reinterpret_cast<const uint8_t*>(a.v_pool) + (size_t)g * kBlockSize * RB;
     const uint8_t* sp = (lane < 4 * SB ? a.k_mx_scale : a.v_mx_scale) + (size_t)g * kBlockSize * SB + sdma;
@@ -531,18 +536,19 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
     const uint32_t my_ring_a = ring0 + w * R * CH * SLOT;
 
     auto issue_block = [&](int slot, int blk) {
-        const size_t id = (size_t)__builtin_amdgcn_readfirstlane(s_ids[blk]);
+        const uint32_t id = (uint32_t)__builtin_amdgcn_readfirstlane(s_ids[blk]);
+        const uint64_t co = (uint64_t)id * blk_codes, so = (uint64_t)id * blk_sc;
         char* dst = my_ring + slot * SLOT;
         if constexpr (D == 128) {
-            dma16(kp + id * blk_codes + kdma, dst);
-            dma16(vp + id * blk_codes + 16 * lane, dst + CODES);
+            dma16(kp + co + kdma, dst);
+            dma16(vp + co + 16 * lane, dst + CODES);
         } else {
-            dma4(kp + id * blk_codes + kdma, dst);
-            dma4(kp + id * blk_codes + kdma + 4, dst + 256);
-            dma4(vp + id * blk_codes + 4 * lane, dst + CODES);
-            dma4(vp + id * blk_codes + 256 + 4 * lane, dst + CODES + 256);
+            dma4(kp + co + kdma, dst);
+            dma4(kp + co + kdma + 4, dst + 256);
+            dma4(vp + co + 4 * lane, dst + CODES);
+            dma4(vp + co + 256 + 4 * lane, dst + CODES + 256);
         }
-        if (sc_lane) dma4(sp + id * blk_sc, dst + 2 * CODES);
+        if (sc_lane) dma4(sp + so, dst + 2 * CODES);
     };
     // chunk i of the wave: blocks w + NW (CH i + cb); a block past the window's
     // end (the last chunk's second block) is fetched as a copy of the first and
@@ -603,9 +609,13 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
             else st.template accumulate<true>(ck, valid);
         }
     };
-    // LO, stage A of chunk i from its slots: read, mark the tokens below lim, scores.
-    // Branch-free, so that it shares a basic block with the previous chunk's stage B.
-    auto stage_scores = [&](int slot, int i, int tok_r, typename L::PairStage& ps) {
+    // LO, stage A of chunk i from its slots: read, scores, and (MASK) mark the tokens
+    // at or past lim.  Branch-free, so that it shares a basic block with the previous
+    // chunk's stage B.  Only a wave's last chunk of a window can hold such tokens (the
+    // partition's ragged last block, or a copied block past the window's end), and
+    // the steady loop never stages it, so the steady loop stages without the mask.
+    auto stage_scores = [&](int slot, int i, int tok_r, typename L::PairStage& ps, auto mask) {
+        constexpr bool MASK = decltype(mask)::value;
         Mx4Chunk<D, 2> ck;
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
@@ -616,6 +626,13 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
             for (int q = 0; q < 4; ++q) ps.v[cb][q] = ck.v[cb][q];
         }
         st.pair_scores(ck, ps);
+        if constexpr (!MASK) {
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) ps.vs[cb][q] = ck.vs[cb][q];
+            return;
+        }
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
             const int blk = blk_of(i, cb);
@@ -664,22 +681,29 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
         if constexpr (LO) {
             // chunk i is read from slot i % R; the DMAs of chunk i + PF go into the slot
             // chunk i - 1 was read from.  Iteration i runs scores(i), then finish(i - 1).
-            typename L::PairStage prev, cur;
+            // ps[0] holds the staged chunk awaiting stage B between iterations; with an
+            // even R the unrolled steady loop alternates the two buffers instead of copying
+            typename L::PairStage ps[2];
             int i = 1;
             if (nb >= R + PF + 1) {
                 // unconditional prologue (keeps the loop's waits exact): chunks 0 .. PF
 #pragma unroll
                 for (int v = 0; v <= PF; ++v) issue(v, v);
                 wait_vm<PF * LPC>();
-                stage_scores(0, 0, tok_r, prev);
+                stage_scores(0, 0, tok_r, ps[0], Flag<false>{});
                 for (; i + R + PF <= nb; i += R) {   // i = 1 mod R: read slot (1 + v) % R, refill slot v
 #pragma unroll
                     for (int v = 0; v < R; ++v) {
                         issue(v, i + v + PF);
                         wait_vm<PF * LPC>();
-                        stage_scores((1 + v) % R, i + v, tok_r, cur);
-                        st.pair_finish(prev);
-                        prev = cur;
+                        if constexpr (R % 2 == 0) {
+                            stage_scores((1 + v) % R, i + v, tok_r, ps[(v + 1) & 1], Flag<false>{});
+                            st.pair_finish(ps[v & 1]);
+                        } else {
+                            stage_scores((1 + v) % R, i + v, tok_r, ps[1], Flag<false>{});
+                            st.pair_finish(ps[0]);
+                            ps[0] = ps[1];
+                        }
                     }
                 }
             } else if (nb > 0) {
@@ -687,16 +711,16 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
                 for (int v = 0; v <= PF; ++v)
                     if (v < nb) issue(v, v);
                 wait_chunks<LPC, PF>(min(nb - 1, PF));
-                stage_scores(0, 0, tok_r, prev);
+                stage_scores(0, 0, tok_r, ps[0], Flag<true>{});
             }
             for (; i < nb; ++i) {   // the last chunks: wait for chunk i only
                 if (i + PF < nb) issue((i + PF) % R, i + PF);
                 wait_chunks<LPC, PF>(min(nb - 1 - i, PF));
-                stage_scores(i % R, i, tok_r, cur);
-                st.pair_finish(prev);
-                prev = cur;
+                stage_scores(i % R, i, tok_r, ps[1], Flag<true>{});
+                st.pair_finish(ps[0]);
+                ps[0] = ps[1];
             }
-            if (nb > 0) st.pair_finish(prev);
+            if (nb > 0) st.pair_finish(ps[0]);
             continue;
         }
         int i = 0;
