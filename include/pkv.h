@@ -338,10 +338,12 @@ int pkv_append_decode_attention_fp8(int q_dtype,
  * kept); its value is code * 2^E (exact in float32).  Each row is quantized on
  * its own when it is appended.  Non-finite new K/V values are outside the
  * contract.  q, k_new and v_new keep their own dtype (PKV_F32, PKV_F16 or
- * PKV_BF16); out is float32.  Pools 16-byte aligned; D in {64, 128}; other
- * rules as the calls above.  Attention runs per query head (with grouped heads
- * each KV head is read once per query head); the fused call quantizes the new
- * rows in a launch of its own before attention.
+ * PKV_BF16); out is float32.  Pools 16-byte aligned; D in {64, 128}; code
+ * pools of 1 TiB or more return PKV_ERR_UNSUPPORTED; other rules as the calls
+ * above.  With grouped heads (H_q / H_kv in 2..16) and an f16/bf16 q, one
+ * workgroup serves a KV head's query heads on MFMA tiles, reading each block
+ * once; otherwise attention runs per query head on the vector units.  The fused
+ * call quantizes the new rows in a launch of its own before attention.
  */
 
 /* Quantize each request's new K/V rows into slot positions[b] of its block. */

@@ -216,6 +216,9 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
             return fail(PKV_ERR_INVALID_ARG, "k_scale and v_scale must be 4-byte aligned");
     }
     if (mx4 && (!mx4->k || !mx4->v)) return fail(PKV_ERR_NULL, "k_scale and v_scale must not be NULL");
+    // the grouped MXFP4 kernel addresses blocks in 256-byte units held in 32 bits
+    if (mx4 && (uint64_t)n_blocks * H_kv * block_size * (D / 2) >= (1ull << 40))
+        return fail(PKV_ERR_UNSUPPORTED, "MXFP4 code pools of 1 TiB or more are not supported");
 
     Plan p = make_plan(dtype, B, H_q, H_kv, D, max_ctx, partition_size, fp8 != nullptr);
     if (mx4) {

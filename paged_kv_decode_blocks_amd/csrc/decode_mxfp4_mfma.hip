@@ -471,7 +471,7 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
     constexpr int RING = NW * R * CH * SLOT;
     constexpr int MERGE = NW * 16 * (D + 4) * 4;
     __shared__ __attribute__((aligned(16))) char s_ring[RING > MERGE ? RING : MERGE];
-    __shared__ int32_t s_ids[kWin];
+    __shared__ uint32_t s_ids[kWin];   // block offsets in 256-byte units of the code pools
     __shared__ int s_bad;
     __shared__ float s_m[NW][16];
     __shared__ float s_l[NW][16];
@@ -519,10 +519,10 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
     const int kdma = D == 128 ? tau * RB + 16 * j : tau * RB + 8 * j;   // + 4 h for D = 64
     const bool sc_lane = lane < 8 * SB;                                  // 4 SB lanes per scale tile
     const int sdma = lane < 4 * SB ? 4 * lane : 4 * (lane - 4 * SB);
-    // per-block strides fit 32 bits (H_kv * 16 * D / 2); block id x stride is formed
-    // as a 32 x 32 -> 64-bit product of wave-uniform values, on the scalar unit
-    const uint32_t blk_codes = (uint32_t)a.H_kv * kBlockSize * RB;
-    const uint32_t blk_sc = (uint32_t)a.H_kv * kBlockSize * SB;
+    // A block of a code pool is H_kv * 16 * D / 2 bytes, a multiple of 256, and its
+    // scales 1/16 of that: the window stages id * blk_units (exact; below 2^32 for
+    // pools under 1 TiB), and a DMA address is one shift-add of it.
+    const uint32_t blk_units = (uint32_t)a.H_kv * kBlockSize * RB / 256;
     const uint8_t* kp = reinterpret_cast<const uint8_t*>(a.k_pool) + (size_t)g * kBlockSize * RB;
     const uint8_t* vp = reinterpret_cast<const uint8_t*>(a.v_pool) + (size_t)g * kBlockSize * RB;
     const uint8_t* sp = (lane < 4 * SB ? a.k_mx_scale : a.v_mx_scale) + (size_t)g * kBlockSize * SB + sdma;
@@ -536,8 +536,8 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
     const uint32_t my_ring_a = ring0 + w * R * CH * SLOT;
 
     auto issue_block = [&](int slot, int blk) {
-        const uint32_t id = (uint32_t)__builtin_amdgcn_readfirstlane(s_ids[blk]);
-        const uint64_t co = (uint64_t)id * blk_codes, so = (uint64_t)id * blk_sc;
+        const uint64_t u = (uint32_t)__builtin_amdgcn_readfirstlane(s_ids[blk]);
+        const uint64_t co = u << 8, so = u << 4;
         char* dst = my_ring + slot * SLOT;
         if constexpr (D == 128) {
             dma16(kp + co + kdma, dst);
@@ -661,7 +661,7 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
                         s_bad = 1;
                         id = 0;
                     }
-                    s_ids[t] = id;
+                    s_ids[t] = (uint32_t)id * blk_units;
                 }
             }
         } else {
@@ -671,7 +671,7 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
                     s_bad = 1;
                     id = 0;
                 }
-                s_ids[t] = id;
+                s_ids[t] = (uint32_t)id * blk_units;
             }
         }
         __syncthreads();

@@ -178,6 +178,9 @@ def test_mxfp4_validation(lib):
     bad[7] = None                       # v_scale
     assert at(*bad) == E_NULL
     bad = list(args)
+    bad[16] = 1 << 25                   # n_blocks: code pools of 2^25 * 32 KiB = 1 TiB
+    assert at(*bad) == E_UNSUP and b"1 TiB" in lib.pkv_last_error()
+    bad = list(args)
     bad[11] = 0                         # B = 0
     assert at(*bad) == OK
     f = lib.pkv_append_decode_attention_mxfp4
