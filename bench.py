@@ -37,6 +37,7 @@ import numpy as np
 METRIC = "paged decode attention HBM GB/s (% of MI355X peak) and KV-tokens/s"
 PEAK_HBM_GBPS = 8000.0           # MI355X HBM3E, decimal GB/s
 INFINITY_CACHE_BYTES = 256 << 20
+GRAPH_MIN_STEPS = 32      # steps per replayed graph (cycling over the input sets): fewer graph launches
 DTYPE_CODE = {"f32": 0, "f16": 1, "bf16": 2}
 
 
@@ -641,27 +642,40 @@ def main(argv=None):
     torch.cuda.synchronize()
 
     # The step is launch-bound on the host for small batches, so the throughput
-    # region replays a HIP graph holding one step per input set (the library
-    # makes no allocation, memset or synchronisation, so it captures as is).
-    graph = None
-    if not args.no_graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for k in range(R):
+    # region replays HIP graphs of steps (the library makes no allocation, memset
+    # or synchronisation, so it captures as is): one of G >= GRAPH_MIN_STEPS steps
+    # cycling over the R input sets (each replay also pays a fixed cost), and one
+    # of the remaining steps.
+    graph = tail = None
+    G = R * max(1, math.ceil(GRAPH_MIN_STEPS / R))
+    reps, rem = divmod(args.steps, G) if not args.no_graph else (0, args.steps)
+
+    def capture(n):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for k in range(n):
                 step(k)
         torch.cuda.synchronize()
-        graph.replay()
+        gr.replay()
         torch.cuda.synchronize()
+        return gr
+
+    if not args.no_graph:
+        graph = capture(G)
+        if rem:
+            tail = capture(rem)
     stream = torch.cuda.current_stream(dev)
-    reps, rem = divmod(args.steps, R) if graph is not None else (0, args.steps)
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     g0.record(stream)
     for _ in range(reps):
         graph.replay()
-    for k in range(rem):
-        step(k)
+    if tail is not None:
+        tail.replay()
+    else:
+        for k in range(rem):
+            step(k)
     g1.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -710,7 +724,8 @@ def main(argv=None):
             "kv_tokens_per_step": kv_tokens, "max_context_len": max_ctx, "partition_size": P,
             "accumulate": "f32", "output": "f32", "seed": w.seed, "input_rotation_sets": R,
             "algorithmic_bytes_per_step": int(bytes_per_step), "launch": launch,
-            "timed_loop": (f"{reps} replays of a HIP graph of {R} steps + {rem} eager steps" if graph is not None
+            "timed_loop": (f"{reps} replays of a HIP graph of {G} steps (input sets cycled)"
+                           + (f" + one graph of {rem} steps" if rem else "") if graph is not None
                            else f"{rem} eager steps"),
         },
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBPS, 2),
