@@ -10,8 +10,12 @@
 //    row r (16 bytes for D = 128, 8 for D = 64), so one load instruction reads a
 //    whole 16-row block of one pool; each lane also loads the one scale byte of
 //    its 32-element block(s).
-//  * Codes are decoded by the hardware conversion with the block scale folded
-//    in (v_cvt_scalef32_pk_f32_fp4: exact), against q held in float32; the four
+//  * Codes are decoded by the hardware conversions, exact: for q . k, code pairs
+//    go to q's type and meet q's pairs in packed dot products accumulated in
+//    float32 (bf16: v_cvt_scalef32_pk_bf16_fp4 with the block scale; f16:
+//    v_cvt_scalef32_pk_f16_fp4 at unit scale, the lane's sum then times the
+//    scale; an f32 q takes float32 codes and FMAs); V codes go to float32 with
+//    their scale (v_cvt_scalef32_pk_f32_fp4) for the weighted sum.  The four
 //    lanes of a row add their partial dot products with DPP.
 //  * Block ids are staged in LDS per window; each wave takes chunks of CH
 //    blocks and issues the next chunk's loads before computing the current one;
@@ -50,6 +54,20 @@ __device__ __forceinline__ float rows_max(float v) {
     v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// acc + q . (codes of byte X of w), as one packed dot product: the code pair is
+// decoded with the block scale to bf16 (exact), or at unit scale to f16 (the code
+// values are exact there; the caller applies the scale)
+template <int X>
+__device__ __forceinline__ float dot_codes_bf16(uint32_t q, uint32_t w, float sc, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, q),
+                                           __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, X), acc, false);
+}
+template <int X>
+__device__ __forceinline__ float dot_codes_f16(uint32_t q, uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, q), __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, X),
+                                  acc, false);
 }
 
 template <int D>
@@ -113,8 +131,21 @@ __global__ __launch_bounds__(NW * 64) void decode_mxfp4_kernel(const AttnArgs a)
 
     const bool from_pos = a.context_lens == nullptr;
     const int n = from_pos ? a.positions[b] + 1 : a.context_lens[b];
-    float qf[CPL];
-    load_q<QDT, CPL>(a.q + ((int64_t)b * a.q_row_stride + (int64_t)h * D + c * CPL) * QES, qf);
+    // q: float32 for an f32 q; otherwise the storage pairs as they are, for the
+    // packed dot products (element pair j of the lane's piece in word j)
+    constexpr bool PACKED = QDT != DT_F32;
+    float qf[PACKED ? 1 : CPL];
+    uint32_t qp[PACKED ? CPL / 2 : 1];
+    if constexpr (PACKED) {
+        const char* qs = a.q + ((int64_t)b * a.q_row_stride + (int64_t)h * D + c * CPL) * QES;
+#pragma unroll
+        for (int i = 0; i < CPL / 8; ++i) {
+            const uint4 v = ld16_cached(qs + 16 * i);
+            qp[4 * i] = v.x; qp[4 * i + 1] = v.y; qp[4 * i + 2] = v.z; qp[4 * i + 3] = v.w;
+        }
+    } else {
+        load_q<QDT, CPL>(a.q + ((int64_t)b * a.q_row_stride + (int64_t)h * D + c * CPL) * QES, qf);
+    }
     const int32_t* table = a.block_tables + (int64_t)b * a.bt_stride;
     const int first_blk = part * (a.part_tokens / kBlockSize);
     constexpr int PRE = (kMx4WindowBlocks + NW * 64 - 1) / (NW * 64);
@@ -172,12 +203,38 @@ __global__ __launch_bounds__(NW * 64) void decode_mxfp4_kernel(const AttnArgs a)
         for (int cb = 0; cb < CH; ++cb) {
             const float sc = mx_scale_operand(bf.ks[cb]);
             float acc = 0.0f;
+            if constexpr (QDT == DT_BF16) {
+                // code pairs decoded with their scale to bf16 (exact for every scale),
+                // one packed dot product with q per pair, accumulated in float32
 #pragma unroll
-            for (int x = 0; x < Mx4Row<D>::NWD; ++x) {
-                float f[8];
-                e2m1x8_to_f32(bf.k[cb].w[x], sc, f);
+                for (int x = 0; x < Mx4Row<D>::NWD; ++x) {
+                    const uint32_t w = bf.k[cb].w[x];
+                    acc = dot_codes_bf16<0>(qp[4 * x], w, sc, acc);
+                    acc = dot_codes_bf16<1>(qp[4 * x + 1], w, sc, acc);
+                    acc = dot_codes_bf16<2>(qp[4 * x + 2], w, sc, acc);
+                    acc = dot_codes_bf16<3>(qp[4 * x + 3], w, sc, acc);
+                }
+            } else if constexpr (QDT == DT_F16) {
+                // code pairs decoded at unit scale to f16 (the code values are exact
+                // there), one packed dot product with q per pair; the block scale, a
+                // power of two, multiplies the lane's sum
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc = fmaf(qf[8 * x + e], f[e], acc);
+                for (int x = 0; x < Mx4Row<D>::NWD; ++x) {
+                    const uint32_t w = bf.k[cb].w[x];
+                    acc = dot_codes_f16<0>(qp[4 * x], w, acc);
+                    acc = dot_codes_f16<1>(qp[4 * x + 1], w, acc);
+                    acc = dot_codes_f16<2>(qp[4 * x + 2], w, acc);
+                    acc = dot_codes_f16<3>(qp[4 * x + 3], w, acc);
+                }
+                acc *= bf.ks[cb] == 255u ? __builtin_nanf("") : sc;   // 255: a NaN scale
+            } else {
+#pragma unroll
+                for (int x = 0; x < Mx4Row<D>::NWD; ++x) {
+                    float f[8];
+                    e2m1x8_to_f32(bf.k[cb].w[x], sc, f);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc = fmaf(qf[8 * x + e], f[e], acc);
+                }
             }
             s[cb] = mul_rn(group_sum<4>(acc), a.scale_log2);
         }
