@@ -155,6 +155,24 @@ def test_mxfp4_decode_every_code_and_extreme_scales(torch_dev, monkeypatch, qdt,
     assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("qdt,D", [("f16", 128), ("bf16", 128), ("f16", 64), ("bf16", 64)])
+def test_mxfp4_per_head_scores_over_k_scales(torch_dev, monkeypatch, qdt, D):
+    """The per-head kernel's packed q . k (f16 codes at unit scale times the block
+    scale; bf16 codes with the scale folded in) against the oracle, with K scale
+    bytes drawn from 0 (2^-127), 1, 40, 90, 120, 127 and 132 instead of the
+    workload's narrow range: every exponent from the subnormal end to 2^5."""
+    monkeypatch.setenv("PKV_MX4_KIND", "0")
+    cfg = cfg_for(qdt, D, 4, 4, (1, 17, 200, 700), append=False)
+    w = make_workload(cfg, 71)
+    rng = np.random.default_rng(72)
+    written = w.k_scale != 0xFF
+    w.k_scale[written] = rng.choice(np.array([0, 1, 40, 90, 120, 127, 132], np.uint8), size=int(written.sum()))
+    ref, _, _ = oracle.run_step(w)
+    got, _ = run(torch_dev, w, 0, False)
+    assert pkv.last_launch().startswith("mxfp4 "), pkv.last_launch()
+    assert_close(got, ref, qdt, f"{qdt} D{D}")
+
+
 @pytest.mark.parametrize("dtype,D,H_q,H_kv", [("f16", 128, 8, 8), ("bf16", 128, 16, 2), ("bf16", 64, 8, 1),
                                               ("f32", 64, 4, 4), ("f16", 64, 4, 2), ("f32", 128, 2, 1),
                                               ("f16", 128, 16, 1), ("f16", 64, 12, 4)])
