@@ -291,13 +291,16 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
     if (mx4) {
         a.k_mx_scale = mx4->k;
         a.v_mx_scale = mx4->v;
+        a.k_mx_scale_w = mx4->k_w;
+        a.v_mx_scale_w = mx4->v_w;
     }
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
     if (mx4) {
-        // both attention kernels read the new row from the pool: quantize it there first
-        if (fused) {
+        // the per-head kernel reads the new row from the pool: quantize it there first (the
+        // grouped kernel quantizes it itself)
+        if (fused && p.kind == 0) {
             pkv::AppendMx4Args ap{};
             ap.k_new = a.k_new;
             ap.v_new = a.v_new;

@@ -33,8 +33,9 @@
 //
 // Softmax is online per query head in the log2 domain with the lazy rescale of
 // the 16-bit grouped kernel; waves merge through LDS; the partition's result
-// goes to the output or, when split, to the log-sum-exp merge.  The quantizing
-// append runs before this kernel, which reads every row from the pools.
+// goes to the output or, when split, to the log-sum-exp merge.  In the fused
+// step the new token is quantized inside the kernel, in the wave whose ring slot
+// holds its block (see APPEND below), so the step is one launch plus the merge.
 #include "pkv_mxfp4.h"
 #include "pkv_launch.h"
 
@@ -455,7 +456,7 @@ __device__ __forceinline__ void lds_block(uint32_t ka, uint32_t ksa, uint32_t va
 // the read is conflict-free -- then V codes, K scales and V scales in pool order.  Every DMA stays inside the block's rows of this KV head; rows at
 // or past the length are masked after the read, so the last, partial block
 // needs no other path.
-template <int QDT, int D, int NW, int PF, bool LO>
+template <int QDT, int D, int NW, int PF, bool LO, bool APPEND>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_mxfp4_mfma_kernel(const AttnArgs a) {
     using Geo = Mx4Geo<D>;
@@ -475,6 +476,8 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
     __shared__ int s_bad;
     __shared__ float s_m[NW][16];
     __shared__ float s_l[NW][16];
+    __shared__ uint8_t s_new[2][APPEND ? D / 2 : 1];    // APPEND: the new K and V rows' codes ...
+    __shared__ uint8_t s_nsc[2][APPEND ? D / 32 : 1];   // ... and scale bytes
 
     const int BG = a.B * a.H_kv;
     const int unit = xcd_pair_unit(blockIdx.x, a.n_parts * BG);
@@ -499,9 +502,8 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
             pre[k] = t < spec ? table[first_blk + t] : 0;
         }
     }
-    const bool from_pos = a.context_lens == nullptr;
-    const int n = from_pos ? a.positions[b] + 1 : a.context_lens[b];
-    const bool bad_len = from_pos ? (n < 1 || n > a.max_context_len) : (n < 0 || n > a.max_context_len);
+    const int n = APPEND ? a.positions[b] + 1 : a.context_lens[b];
+    const bool bad_len = APPEND ? (n < 1 || n > a.max_context_len) : (n < 0 || n > a.max_context_len);
     if (bad_len || n == 0) {
         if (a.n_parts == 1 && part == 0)
             for (int x = threadIdx.x; x < a.G * D; x += NW * 64)
@@ -512,6 +514,45 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
     if (start >= n) return;
     const int lim = min(start + a.part_tokens, n);
     const int nblk = (lim - start + kBlockSize - 1) / kBlockSize;
+    // APPEND: when this partition ends at n, the new token (position n - 1, row
+    // t_new of the partition's last block) is quantized here from k_new / v_new by
+    // the wave that owns that block (blocks go round-robin and a window holds a
+    // multiple of NW blocks), exactly as the append kernel would: it writes the
+    // codes into the block's ring slot before the slot is read, and to the pools
+    // (this workgroup is the only one holding that position of its KV head).
+    const bool holds_new = APPEND && lim == n;
+    const int t_new = (n - 1) % kBlockSize;
+    const bool new_wave = holds_new && w == (nblk - 1) % NW;
+    if constexpr (APPEND) {
+        // quantized now into a small LDS area of the owner wave (lane l: elements 2l
+        // and 2l + 1, one row per pass), copied into the ring slot once the block's
+        // DMAs have landed there
+        if (new_wave) {
+            const bool on = lane < D / 2;
+#pragma unroll
+            for (int which = 0; which < 2; ++which) {
+                float x0 = 0.0f, x1 = 0.0f;
+                if (on) {
+                    const uint32_t u = *reinterpret_cast<const uint32_t*>(
+                        (which ? a.v_new : a.k_new) + ((size_t)b * a.new_row_stride + (size_t)g * D + 2 * lane) * 2);
+                    if constexpr (QDT == DT_F16) {
+                        const half2_t h = __builtin_bit_cast(half2_t, u);
+                        x0 = (float)h.x;
+                        x1 = (float)h.y;
+                    } else {
+                        x0 = __uint_as_float(u << 16);
+                        x1 = __uint_as_float(u & 0xffff0000u);
+                    }
+                }
+                int E;
+                const uint32_t code = mx4_quantize_pair(x0, x1, E);
+                if (on) {
+                    s_new[which][lane] = (uint8_t)code;
+                    if ((lane & 15) == 0) s_nsc[which][lane / 16] = (uint8_t)(E + 127);
+                }
+            }
+        }
+    }
 
     const int j = st.j, c = st.c;
     const int tau = 4 * (c & 3) + (c >> 2);
@@ -535,6 +576,28 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
     char* my_ring = s_ring + w * R * CH * SLOT;
     const uint32_t my_ring_a = ring0 + w * R * CH * SLOT;
 
+    // APPEND: put the new rows in row t_new of ring slot sl, at the places the
+    // block's DMAs fill (after they have landed there); the pools get them after
+    // the loop
+    auto put_new = [&](int sl) {
+        if (lane < D / 2) {
+            char* dst = my_ring + sl * SLOT;
+            const int cn = 4 * (t_new & 3) + (t_new >> 2);   // the lane column whose K row is t_new
+            const int kpos = D == 128 ? 256 * (lane / 16) + 16 * cn + (lane % 16)
+                                      : 256 * ((lane % 8) / 4) + 4 * (16 * (lane / 8) + cn) + (lane % 4);
+            dst[kpos] = (char)s_new[0][lane];
+            dst[CODES + t_new * RB + lane] = (char)s_new[1][lane];
+            if ((lane & 15) == 0) {
+                dst[2 * CODES + t_new * SB + lane / 16] = (char)s_nsc[0][lane / 16];
+                dst[2 * CODES + kBlockSize * SB + t_new * SB + lane / 16] = (char)s_nsc[1][lane / 16];
+            }
+        }
+        // this wave's LDS writes land before its reads of the slot (in order per wave)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
     auto issue_block = [&](int slot, int blk) {
         const uint64_t u = (uint32_t)__builtin_amdgcn_readfirstlane(s_ids[blk]);
         const uint64_t co = u << 8, so = u << 4;
@@ -553,7 +616,7 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
     // chunk i of the wave: blocks w + NW (CH i + cb); a block past the window's
     // end (the last chunk's second block) is fetched as a copy of the first and
     // masked, so every chunk issues the same number of DMAs
-    int nr = 0;
+    int nr = 0, r0_cur = 0;   // the current window: its block count and first block
     auto blk_of = [&](int i, int cb) { return w + NW * (CH * i + cb); };
     auto issue = [&](int slot, int i) {
 #pragma unroll
@@ -578,6 +641,9 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
 #pragma unroll
         for (int cb = 0; cb < CH; ++cb) {
             const uint32_t base = my_ring_a + (CH * slot + cb) * SLOT;
+            if constexpr (APPEND) {
+                if (new_wave && r0_cur + blk_of(i, cb) == nblk - 1) put_new(CH * slot + cb);   // full or not
+            }
             lds_block<D>(base + k_rd, base + ks_rd, base + v_rd, base + vs_rd, ck.k[cb], ck.ks[cb], ck.v[cb],
                          ck.vs[cb]);
         }
@@ -620,6 +686,9 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
             const uint32_t base = my_ring_a + (2 * slot + cb) * SLOT;
+            if constexpr (APPEND && MASK) {
+                if (new_wave && r0_cur + blk_of(i, cb) == nblk - 1) put_new(2 * slot + cb);
+            }
             lds_block<D>(base + k_rd, base + ks_rd, base + v_rd, base + vs_rd, ck.k[cb], ck.ks[cb], ck.v[cb],
                          ck.vs[cb]);
 #pragma unroll
@@ -650,6 +719,7 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
     if (threadIdx.x == 0) s_bad = 0;
     for (int r0 = 0; r0 < nblk; r0 += kWin) {
         nr = min(kWin, nblk - r0);
+        r0_cur = r0;
         __syncthreads();
         if (r0 == 0) {
 #pragma unroll
@@ -754,6 +824,22 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
         }
     }
 
+    if constexpr (APPEND) {
+        // the new rows to the pools, from the owner wave (s_ids still holds the last
+        // window, which has the new token's block; an out-of-range id writes nothing)
+        if (new_wave && lane < D / 2 && s_bad == 0) {
+            const size_t u = s_ids[(nblk - 1) % kWin];
+            const size_t row = (size_t)g * kBlockSize * RB + (u << 8) + (size_t)t_new * RB + lane;
+            reinterpret_cast<uint8_t*>(a.k_pool_w)[row] = s_new[0][lane];
+            reinterpret_cast<uint8_t*>(a.v_pool_w)[row] = s_new[1][lane];
+            if ((lane & 15) == 0) {
+                const size_t srow = (size_t)g * kBlockSize * SB + (u << 4) + (size_t)t_new * SB + lane / 16;
+                a.k_mx_scale_w[srow] = s_nsc[0][lane / 16];
+                a.v_mx_scale_w[srow] = s_nsc[1][lane / 16];
+            }
+        }
+    }
+
     // merge the waves through LDS (the ring is free once every wave is past here)
     const float l = sum_groups(st.l);
     __syncthreads();
@@ -795,10 +881,23 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
 
 template <int QDT, int D, int NW, int PF>
 static hipError_t launch_t(const AttnArgs& a, unsigned grid, hipStream_t stream) {
-    if (a.G <= 8)
-        hipLaunchKernelGGL((decode_mxfp4_mfma_kernel<QDT, D, NW, PF, true>), dim3(grid), dim3(NW * 64), 0, stream, a);
-    else
-        hipLaunchKernelGGL((decode_mxfp4_mfma_kernel<QDT, D, NW, PF, false>), dim3(grid), dim3(NW * 64), 0, stream, a);
+    // the fused step passes positions instead of context_lens
+    const bool append = a.context_lens == nullptr;
+    if (a.G <= 8) {
+        if (append)
+            hipLaunchKernelGGL((decode_mxfp4_mfma_kernel<QDT, D, NW, PF, true, true>), dim3(grid), dim3(NW * 64), 0,
+                               stream, a);
+        else
+            hipLaunchKernelGGL((decode_mxfp4_mfma_kernel<QDT, D, NW, PF, true, false>), dim3(grid), dim3(NW * 64), 0,
+                               stream, a);
+    } else {
+        if (append)
+            hipLaunchKernelGGL((decode_mxfp4_mfma_kernel<QDT, D, NW, PF, false, true>), dim3(grid), dim3(NW * 64), 0,
+                               stream, a);
+        else
+            hipLaunchKernelGGL((decode_mxfp4_mfma_kernel<QDT, D, NW, PF, false, false>), dim3(grid), dim3(NW * 64),
+                               0, stream, a);
+    }
     return hipGetLastError();
 }
 

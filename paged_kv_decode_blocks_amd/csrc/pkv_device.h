@@ -196,6 +196,8 @@ struct AttnArgs {
     float* v_scale_w;
     const uint8_t* k_mx_scale;     // MXFP4 pools only: [n_blocks][H_kv][16][D/32] E8M0 scale bytes
     const uint8_t* v_mx_scale;
+    uint8_t* k_mx_scale_w;         // same, written by the fused MXFP4 append
+    uint8_t* v_mx_scale_w;
     int64_t q_row_stride;          // elements
     int64_t new_row_stride;        // elements
     int32_t bt_stride;
