@@ -321,25 +321,7 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
         e = p.kind == 1 ? pkv::launch_decode_mxfp4_mfma(dtype, D, p.nw, p.pf, a, p.grid, s)
                         : pkv::launch_decode_mxfp4(dtype, D, p.nw, p.ch, a, p.grid, s);
     } else if (fp8 && p.grouped) {
-        // the grouped FP8 kernel reads the new row from the pool: quantize it there first
-        if (fused) {
-            pkv::AppendFp8Args ap{};
-            ap.k_new = a.k_new;
-            ap.v_new = a.v_new;
-            ap.k_pool = reinterpret_cast<uint8_t*>(k_pool_w);
-            ap.v_pool = reinterpret_cast<uint8_t*>(v_pool_w);
-            ap.k_scale = fp8->k_w;
-            ap.v_scale = fp8->v_w;
-            ap.block_tables = block_tables;
-            ap.positions = positions;
-            ap.new_row_stride = new_row_stride;
-            ap.bt_stride = bt_stride;
-            ap.B = B;
-            ap.H_kv = H_kv;
-            ap.n_blocks = n_blocks;
-            e = pkv::launch_kv_append_fp8(dtype, D, ap, s);
-            if (e != hipSuccess) return fail(PKV_ERR_HIP, "kv_append_fp8 launch: %s", hipGetErrorString(e));
-        }
+        // in the fused step the kernel quantizes and writes the new rows itself
         e = pkv::launch_decode_gqa_fp8(dtype, D, p.nw, p.ch, p.pf, p.wpe, p.kd, a, p.grid, s);
     } else if (fp8) {
         e = pkv::launch_decode_fp8(dtype, D, p.nw, p.ch, p.pf, fused, a, p.grid, s);

@@ -41,7 +41,7 @@
 // K rows in LDS are stored with their 16-byte chunks XOR-swizzled by row, so the
 // column-wise MFMA reads hit different banks.  All merge across the waves of the
 // workgroup through LDS, and the fused APPEND variants also write the new token.
-#include "pkv_device.h"
+#include "pkv_fp8.h"
 #include "pkv_launch.h"
 
 namespace pkv {
@@ -1126,7 +1126,28 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_gqa_fp8_kernel(const Attn
         u.start = u.part * a.part_tokens;
         if (u.start >= u.n) return;
         u.end = min(u.start + a.part_tokens, u.n);
-        u.lim = u.end;
+        // the fused step: the pools hold the rows below n - 1; the new token is
+        // quantized here, by wave 0 of the partition that ends at n (below)
+        u.lim = from_pos ? min(u.end, u.n - 1) : u.end;
+    }
+    const bool holds_new = a.context_lens == nullptr && u.end == u.n;
+    const int t_new = (u.n - 1) % kBlockSize;
+    constexpr int PER = D / 64;   // elements of a new row per lane
+    float xnew[2][PER];           // wave 0 of that partition: the new K and V rows, loaded now
+#pragma unroll
+    for (int which = 0; which < 2; ++which)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) xnew[which][i] = 0.0f;
+    if (holds_new && w == 0) {
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+            const char* src = (which ? a.v_new : a.k_new) + ((size_t)u.b * a.new_row_stride + (size_t)u.g * D + lane * PER) * L::ES;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const uint16_t v16 = reinterpret_cast<const uint16_t*>(src)[i];
+                xnew[which][i] = DT == DT_F16 ? (float)__builtin_bit_cast(_Float16, v16) : __uint_as_float((uint32_t)v16 << 16);
+            }
+        }
     }
 
     const int32_t* table = a.block_tables + (int64_t)u.b * a.bt_stride;
@@ -1249,6 +1270,63 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_gqa_fp8_kernel(const Attn
                                   vspool + id * blk_sbytes, tok_r + blk * kBlockSize, u.lim);
             }
         }
+    }
+    if (holds_new && w == 0) {
+        // Quantize the new K and V rows as the append kernel does (lane l holds
+        // elements PER l .. PER l + PER - 1; the row max from a wave reduction), write
+        // them to the pools (this workgroup is the only one holding position n - 1 of
+        // its KV head; an out-of-range block id writes nothing), and add the token
+        // as one more masked row, its codes reaching the MFMA layout through LDS.
+        __shared__ __attribute__((aligned(16))) uint8_t s_new[2][D];
+        __shared__ float s_nsc[2];
+        const int blk = (int)s_ids[(nblk - 1) % kWindowBlocksG];   // the last window is still staged
+        const size_t row = ((size_t)blk * a.H_kv + u.g) * kBlockSize + t_new;
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+            float amax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) amax = fmaxf(amax, fabsf(xnew[which][i]));
+            amax = group_max<64>(amax);
+            const int E = fp8_row_exponent(amax);
+            const float inv = pow2f(-E);
+            uint8_t* pool = reinterpret_cast<uint8_t*>(which ? a.v_pool_w : a.k_pool_w);
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const uint8_t code = (uint8_t)fp8_encode(xnew[which][i] * inv);
+                s_new[which][lane * PER + i] = code;
+                if (s_bad == 0) pool[row * D + lane * PER + i] = code;
+            }
+            if (lane == 0) {
+                s_nsc[which] = pow2f(E);
+                if (s_bad == 0) (which ? a.v_scale_w : a.k_scale_w)[row] = pow2f(E);
+            }
+        }
+        // this wave's LDS writes land before its reads (in order per wave)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        typename L::Codes c[1];
+        bool valid[1][4];
+        const int j = st.j, col = st.col;
+#pragma unroll
+        for (int q = 0; q < KL; ++q)
+            c[0].k[q] = col == t_new ? *reinterpret_cast<const uint4*>(&s_new[0][64 * q + 16 * j]) : make_uint4(0, 0, 0, 0);
+        float ks[4], vs[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            valid[0][i] = 4 * j + i == t_new;
+#pragma unroll
+            for (int x = 0; x < L::VW; ++x)
+                c[0].v[i][x] = valid[0][i] ? *reinterpret_cast<const uint32_t*>(&s_new[1][col * L::VT + 4 * x]) : 0u;
+            ks[i] = valid[0][i] ? s_nsc[0] : 0.0f;
+            vs[i] = valid[0][i] ? s_nsc[1] : 0.0f;
+        }
+        c[0].ks = make_float4(ks[0], ks[1], ks[2], ks[3]);
+        c[0].vs = make_float4(vs[0], vs[1], vs[2], vs[3]);
+        uint4 kc[1][KL];
+#pragma unroll
+        for (int q = 0; q < KL; ++q) kc[0][q] = c[0].k[q];
+        st.template accumulate8<1>(kc, c, valid);
     }
     st.template finish<NW, D + 4>(a, s_m, s_l, s_o, w, u.b, u.g, u.part, s_bad != 0);
 }
