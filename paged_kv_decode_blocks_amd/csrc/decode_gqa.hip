@@ -37,7 +37,8 @@
 //  * decode_gqa_lds_kernel  K and V both go global -> LDS into a per-wave ring
 //    of S block slots, then LDS -> registers in the MFMA layout;
 //  * decode_gqa_fp8_kernel  the same tiles over an FP8 (E4M3) cache, codes
-//    widened to q's type, row scales on scores and weights.
+//    widened to q's type, row scales on scores and weights; in the fused step it
+//    quantizes the new token itself (after its loop) as the append kernel would.
 // K rows in LDS are stored with their 16-byte chunks XOR-swizzled by row, so the
 // column-wise MFMA reads hit different banks.  All merge across the waves of the
 // workgroup through LDS, and the fused APPEND variants also write the new token.
@@ -1112,7 +1113,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_gqa_fp8_kernel(const Attn
     constexpr int PRE = (kWindowBlocksG + NW * 64 - 1) / (NW * 64);
     int pre[PRE];
     gqa_preload_ids<NW>(a, u, pre);
-    // lengths: context_lens, or positions + 1 after the fused call's append
+    // lengths: context_lens, or positions + 1 in the fused step
     {
         const bool from_pos = a.context_lens == nullptr;
         u.n = from_pos ? a.positions[u.b] + 1 : a.context_lens[u.b];
