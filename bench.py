@@ -582,8 +582,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the step has no cross-GPU exchange; "
-                                   "run with --gpus 1 (sharding is described in DESIGN.md)",
+        print(json.dumps({"error": "one GPU only: the step has no cross-GPU exchange (each GPU would run its own "
+                                   "shard of requests or KV heads); run with --gpus 1",
                           "n_gpus": args.gpus}))
         return 2
 
