@@ -273,9 +273,10 @@ int pkv_probe_mfma_burn(int32_t n_workgroups, int32_t iterations, void* sink, vo
  * src_dtype: PKV_F32, PKV_F16 or PKV_BF16); out is float32.  Pools 16-byte
  * aligned, scale arrays 4-byte aligned; other rules as the calls above.  With
  * grouped heads (H_q > H_kv) and f16/bf16 q the products run on the matrix
- * cores over codes widened to q's type, and the fused call quantizes the new
- * rows in a launch of its own before attention; otherwise attention runs per
- * query head with the new rows quantized in the attention launch.
+ * cores over codes widened to q's type; otherwise attention runs per query
+ * head.  Either way the fused call quantizes the new rows inside the attention
+ * launch (the workgroup holding the new position writes them to the pools), so
+ * the step is one launch (plus the merge when split).
  */
 
 /* Quantize each request's new K/V rows into slot positions[b] of its block. */
@@ -343,7 +344,9 @@ int pkv_append_decode_attention_fp8(int q_dtype,
  * above.  With grouped heads (H_q / H_kv in 2..16) and an f16/bf16 q, one
  * workgroup serves a KV head's query heads on MFMA tiles, reading each block
  * once; otherwise attention runs per query head on the vector units.  The fused
- * call quantizes the new rows in a launch of its own before attention.
+ * call quantizes the new rows inside the grouped attention launch (the
+ * workgroup holding the new position writes them to the pools), and in a launch
+ * of its own before the per-head one.
  */
 
 /* Quantize each request's new K/V rows into slot positions[b] of its block. */
