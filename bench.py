@@ -52,7 +52,7 @@ def _code_only(text: str) -> str:
 
 def kernel_source_digest() -> str:
     """sha256 over the HIP sources and headers, comments excluded: ties committed counter
-    data to this kernel build."""
+    data to the kernel sources it was taken with."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_decode_blocks_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
