@@ -187,30 +187,3 @@ def test_fp8_bad_metadata_gives_nan_rows(torch_dev):
     t.cuda.synchronize()
     o = out.cpu().numpy()
     assert np.all(np.isfinite(o[0])) and np.all(np.isnan(o[1])) and np.all(np.isnan(o[2]))
-
-
-@pytest.mark.parametrize("name", ["c3f8", "c5f8"])
-def test_fp8_full_size_sampled(torch_dev, name):
-    """The full-size workload in the launch configuration the bench times; a sample of requests
-    is recomputed by the oracle over the pools after the step (their own rows of the batch)."""
-    cfg = get_config(name, append=True)       # the bench times the fused step
-    w = make_workload(cfg)
-    got, d = run(torch_dev, w, cfg.partition_size, True)
-    kp, vp = d["k_pool"].cpu().numpy(), d["v_pool"].cpu().numpy()
-    ks, vs = d["k_scale"].cpu().numpy(), d["v_scale"].cpu().numpy()
-    rng = np.random.default_rng(3)
-    sample = np.sort(rng.choice(cfg.B, size=4, replace=False))
-    # the oracle's own append of the sampled requests' rows, onto the workload's pools
-    ok, ov, oks, ovs = w.k_pool.copy(), w.v_pool.copy(), w.k_scale.copy(), w.v_scale.copy()
-    oracle.kv_append_fp8(cfg.dtype, w.k_new, w.v_new, ok, ov, oks, ovs, w.block_tables, w.positions, 16)
-    for b in sample:
-        blocks = w.block_tables[b][w.block_tables[b] >= 0]
-        assert bits_equal(kp[blocks], ok[blocks]) and bits_equal(vp[blocks], ov[blocks])
-        assert bits_equal(ks[blocks], oks[blocks]) and bits_equal(vs[blocks], ovs[blocks])
-    # the sampled requests' blocks only, tables renumbered into that sub-pool
-    used = np.unique(np.concatenate([w.block_tables[b][w.block_tables[b] >= 0] for b in sample]))
-    remap = {int(x): i for i, x in enumerate(used)}
-    bt = np.array([[remap.get(int(x), -1) for x in w.block_tables[b]] for b in sample], dtype=np.int32)
-    ref = oracle.paged_decode_attention_fp8(cfg.dtype, np.ascontiguousarray(w.q[sample]), ok[used], ov[used],
-                                            oks[used], ovs[used], bt, w.context_lens[sample], w.scale)
-    assert_close(got[sample], ref, cfg.dtype, name)

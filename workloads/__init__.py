@@ -44,7 +44,7 @@ import numpy as np
 __all__ = [
     "Config", "Workload", "CONFIGS", "get_config", "make_workload", "draw_lengths",
     "DTYPE_BYTES", "NAN_BITS", "to_storage", "storage_dtype",
-    "kv_bytes_per_token", "step_bytes", "draw_e4m3_codes",
+    "kv_bytes_per_token", "step_bytes", "draw_e4m3_codes", "make_peaked_workload",
 ]
 
 DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
@@ -312,6 +312,82 @@ def make_workload(cfg: Config, seed: Optional[int] = None, *, append: Optional[b
     return Workload(cfg=cfg, seed=seed, context_lens=ctx, positions=positions, block_tables=bt,
                     n_blocks=n_blocks, q=q, k_pool=k_pool, v_pool=v_pool, k_new=k_new, v_new=v_new,
                     scale=scale, meta={"required_blocks": required}, k_scale=k_scale, v_scale=v_scale)
+
+
+def make_peaked_workload(cfg: Config, seed: int, *, period: int = 512, rise_log2: float = 64.0,
+                         dominant_first=(), dominant_last=(), dominant_log2: float = 96.0) -> Workload:
+    """Decode-step inputs whose scores climb steeply along each context.
+
+    Built for the online softmax's rescaling: where the running maximum of a
+    head's scores grows by many binary orders within a pass, every weight and
+    partial sum already accumulated must be scaled down.  The layout (lengths,
+    tables, poison, draw of the first values) is ``make_workload``'s; then, from
+    a second generator seeded with (seed, 0x5EA4), per request b and KV head g:
+
+      u ~ N(0, 1)^D                                a direction
+      q_h = u + 0.3 n_h  for even h in the group   "climbing" heads
+      q_h = n_h          for odd h                  heads that see only noise
+      k_t = z_t + a(t) u / |u|,   z_t ~ N(0, 1)^D
+      a(t) = ln2 * rise_log2 * ((t mod period) / period) / (scale |u|)
+
+    so a climbing head's score of token t is about ln2 * rise_log2 * (t mod
+    period) / period plus unit noise: in binary orders, a sawtooth that rises by
+    ``rise_log2`` over each ``period`` tokens.  Token 0 of each request in
+    ``dominant_first`` and the last token (the appended one, with append) of
+    each in ``dominant_last`` instead get a(t) for rise_log2 + dominant_log2
+    orders: they outweigh every other token of a climbing head by about
+    2^dominant_log2.  V rows (and v_new) ~ N(0, 1)^D.  Values are drawn in
+    float32 and rounded once to ``cfg.dtype``.
+
+    FP8 or MXFP4 configs get the same rows in ``cfg.dtype`` storage (this module
+    never quantizes): the returned workload's config has ``kv_dtype=""``.
+    """
+    base = replace(cfg, kv_dtype="")
+    w = make_workload(base, seed)
+    rng = np.random.default_rng([seed, 0x5EA4])
+    bs, H_kv, D, G = cfg.block_size, cfg.H_kv, cfg.D, cfg.G
+    B = w.context_lens.size
+    scale = float(w.scale)
+    ln2 = math.log(2.0)
+    q = np.empty((B, cfg.H_q, D), dtype=np.float32)
+    kp = w.k_pool.copy()
+    vp = w.v_pool.copy()
+    k_new = np.empty((B, H_kv, D), dtype=np.float32)
+    v_new = np.empty((B, H_kv, D), dtype=np.float32)
+    first, last = set(int(b) for b in dominant_first), set(int(b) for b in dominant_last)
+    for b in range(B):
+        n = int(w.context_lens[b])
+        hist = n - 1 if w.positions is not None else n
+        t = np.arange(n)
+        for g in range(H_kv):
+            u = rng.standard_normal(D).astype(np.float64)
+            un = float(np.sqrt(u @ u))
+            for hh in range(G):
+                nh = rng.standard_normal(D)
+                q[b, g * G + hh] = (u + 0.3 * nh) if hh % 2 == 0 else nh
+            orders = rise_log2 * (t % period) / period
+            if b in first and n > 0:
+                orders[0] = rise_log2 + dominant_log2
+            if b in last and n > 0:
+                orders[n - 1] = rise_log2 + dominant_log2
+            a = ln2 * orders / (scale * un)
+            krows = rng.standard_normal((n, D)) + a[:, None] * (u / un)[None, :]
+            vrows = rng.standard_normal((n, D))
+            if hist > 0:
+                x = np.arange(hist)
+                blk, slot = w.block_tables[b, x // bs], x % bs
+                kp[blk, g, slot] = to_storage(krows[:hist], cfg.dtype)
+                vp[blk, g, slot] = to_storage(vrows[:hist], cfg.dtype)
+            if w.positions is not None:
+                k_new[b, g] = krows[n - 1]
+                v_new[b, g] = vrows[n - 1]
+    w.q = to_storage(q, cfg.dtype)
+    w.k_pool, w.v_pool = kp, vp
+    if w.positions is not None:
+        w.k_new, w.v_new = to_storage(k_new, cfg.dtype), to_storage(v_new, cfg.dtype)
+    w.meta.update(peaked=dict(period=period, rise_log2=rise_log2, dominant_first=sorted(first),
+                              dominant_last=sorted(last), dominant_log2=dominant_log2))
+    return w
 
 
 # ---------------------------------------------------------------------------
