@@ -201,6 +201,42 @@ int pkv_append_decode_attention(int dtype,
                                 void* stream);
 
 /*
+ * append_decode_attention_noalloc -- pkv_append_decode_attention for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  The split-KV partials go to
+ * a fixed array the library holds in device memory (one copy per GPU, kept
+ * until the process ends) instead of a caller's workspace; the call allocates
+ * nothing and otherwise behaves exactly as pkv_append_decode_attention (same
+ * kernels, same launch, same results bit for bit).
+ *
+ *   arguments        as in pkv_append_decode_attention, without the workspace
+ *   limit            pkv_decode_workspace_bytes(B, H_q, D, max_context_len,
+ *                    partition_size) must not exceed PKV_NOALLOC_SCRATCH_BYTES
+ *                    (32 MiB; e.g. B 32 x 64 heads x 16 partitions of D 128 takes
+ *                    17 MB), else PKV_ERR_WORKSPACE and nothing is launched
+ *   device           the GPU current on the calling thread, which must be the
+ *                    device of `stream`
+ *   concurrency      every call on one GPU shares that GPU's array: two calls
+ *                    whose work overlaps on the device (different streams, or
+ *                    graphs replayed concurrently) race on it; order them on
+ *                    one stream.  Nothing in the array needs clearing between
+ *                    calls (the merge reads only the partitions the same call
+ *                    wrote).
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int pkv_append_decode_attention_noalloc(int dtype,
+                                        float* out,
+                                        const void* q, int64_t q_row_stride,
+                                        const void* k_new, const void* v_new, int64_t new_row_stride,
+                                        void* k_pool, void* v_pool,
+                                        const int32_t* block_tables, int32_t bt_stride,
+                                        const int32_t* positions,
+                                        int32_t B, int32_t H_q, int32_t H_kv, int32_t D,
+                                        int32_t block_size, int32_t n_blocks,
+                                        int32_t max_context_len, float scale, int32_t partition_size,
+                                        void* stream);
+
+/*
  * append_decode_attention_persistent -- the same fused step on a bounded share
  * of the GPU ("Injecting Adrenaline into LLM Serving" review, section 3.3.1:
  * decode attention is memory-bound, so a fraction of the compute units already

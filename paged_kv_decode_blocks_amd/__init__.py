@@ -30,7 +30,8 @@ __all__ = [
     "append_decode_attention", "decode_workspace_bytes", "last_launch", "version", "probe_stream_read",
     "PKV_F32", "PKV_F16", "PKV_BF16", "EXPORTED_SYMBOLS", "copy_blocks", "BlockManager", "StepGraphs", "Decoder", "cu_mask", "CuMaskedStream",
     "kv_append_fp8", "paged_decode_attention_fp8", "append_decode_attention_fp8", "copy_blocks_fp8",
-    "device_cu_count", "append_decode_attention_persistent",
+    "device_cu_count", "append_decode_attention_persistent", "append_decode_attention_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
     "kv_append_mxfp4", "paged_decode_attention_mxfp4", "append_decode_attention_mxfp4", "copy_blocks_mxfp4",
     "PKV_ERR_OUT_OF_BLOCKS", "PKV_ERR_SEQUENCE",
 ]
@@ -45,7 +46,7 @@ BLOCK_SIZE = 16
 EXPORTED_SYMBOLS = (
     "pkv_version", "pkv_status_string", "pkv_last_error", "pkv_last_launch", "pkv_kv_append",
     "pkv_decode_workspace_bytes", "pkv_paged_decode_attention", "pkv_append_decode_attention",
-    "pkv_append_decode_attention_persistent", "pkv_probe_mfma_burn",
+    "pkv_append_decode_attention_persistent", "pkv_append_decode_attention_noalloc", "pkv_probe_mfma_burn",
     "pkv_probe_stream_read", "pkv_copy_blocks", "pkv_copy_blocks_fp8", "pkv_kv_append_fp8", "pkv_paged_decode_attention_fp8",
     "pkv_append_decode_attention_fp8", "pkv_kv_append_mxfp4", "pkv_paged_decode_attention_mxfp4",
     "pkv_append_decode_attention_mxfp4", "pkv_copy_blocks_mxfp4",
@@ -130,6 +131,9 @@ def load_library(path: Optional[str] = None):
                                                 I32, I32, I32, I32, I32, I32, I32, ctypes.c_float, I32,
                                                 P, SZ, P]
     lib.pkv_append_decode_attention.restype = ctypes.c_int
+    lib.pkv_append_decode_attention_noalloc.argtypes = [ctypes.c_int, P, P, I64, P, P, I64, P, P, P, I32, P,
+                                                        I32, I32, I32, I32, I32, I32, I32, ctypes.c_float, I32, P]
+    lib.pkv_append_decode_attention_noalloc.restype = ctypes.c_int
     lib.pkv_append_decode_attention_persistent.argtypes = [ctypes.c_int, P, P, I64, P, P, I64, P, P, P, I32, P,
                                                            I32, I32, I32, I32, I32, I32, I32, ctypes.c_float, I32,
                                                            P, SZ, I32, P]
@@ -382,6 +386,36 @@ def append_decode_attention(q, k_new, v_new, k_pool, v_pool, block_tables, posit
         _ptr(block_tables), bts, _ptr(positions), B, H_q, H_kv, D, bs, n_blocks, int(max_context_len),
         float(scale), int(partition_size), _ptr(ws), ws_bytes, _stream(stream))
     _check(rc, "append_decode_attention")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20     # PKV_NOALLOC_SCRATCH_BYTES
+
+
+def append_decode_attention_noalloc(q, k_new, v_new, k_pool, v_pool, block_tables, positions, scale: float,
+                                    max_context_len: int, *, partition_size: int = 0, out=None, stream=None):
+    """append_decode_attention whose split partials live in the library's own device array
+    (at most NOALLOC_SCRATCH_BYTES): the C call allocates nothing.  Pass ``out`` to keep the
+    Python call allocation-free too.  Calls that overlap on one GPU race on that array."""
+    torch = _torch()
+    n_blocks, H_kv, bs, D = _pool_dims(k_pool, v_pool)
+    B, H_q = q.shape[0], q.shape[1]
+    for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new")):
+        _require(t.dtype == k_pool.dtype, f"{nm} dtype must match the pools")
+    qrs = _rows(q, "q", H_q, D)
+    nrs = _rows(k_new, "k_new", H_kv, D)
+    _require(_rows(v_new, "v_new", H_kv, D) == nrs, "k_new and v_new must share a row stride")
+    bts = _int32_2d(block_tables, "block_tables")
+    _int32_1d(positions, "positions", B)
+    if out is None:
+        out = torch.empty((B, H_q, D), dtype=torch.float32, device=q.device)
+    _require(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, H_q, D),
+             "out must be contiguous float32 [B, H_q, D]")
+    rc = load_library().pkv_append_decode_attention_noalloc(
+        _dtype_code(q), _ptr(out), _ptr(q), qrs, _ptr(k_new), _ptr(v_new), nrs, _ptr(k_pool), _ptr(v_pool),
+        _ptr(block_tables), bts, _ptr(positions), B, H_q, H_kv, D, bs, n_blocks, int(max_context_len),
+        float(scale), int(partition_size), _stream(stream))
+    _check(rc, "append_decode_attention_noalloc")
     return out
 
 

@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "pkv.h"
 #include "pkv_host.h"
@@ -373,6 +374,41 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
     return PKV_OK;
 }
 
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Scratch for the allocation-free fused step: the split-KV partials of
+// pkv_append_decode_attention_noalloc live in this fixed device array.  Each GPU
+// the library runs on holds its own copy, at its own address, until the process
+// ends.  In host code the array's name is only a host-side stand-in: the device
+// address comes from hipGetSymbolAddress, once per device, and only that address
+// is ever handed to a kernel.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr size_t kScratchBytes = PKV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current GPU's copy of `scratch`, looked up on the first
+// call on that device with the device current.
+int scratch_for_current_device(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(PKV_ERR_UNSUPPORTED, "device %d (at most %d)", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(PKV_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return PKV_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -758,6 +794,28 @@ int pkv_append_decode_attention_persistent(int dtype, float* out, const void* q,
                             block_tables, bt_stride, nullptr, B > 0 ? positions : nullptr, B, H_q, H_kv, D,
                             block_size, n_blocks, max_context_len, scale, partition_size, workspace,
                             workspace_bytes, stream, nullptr, n_workgroups);
+}
+
+int pkv_append_decode_attention_noalloc(int dtype, float* out, const void* q, int64_t q_row_stride,
+                                        const void* k_new, const void* v_new, int64_t new_row_stride, void* k_pool,
+                                        void* v_pool, const int32_t* block_tables, int32_t bt_stride,
+                                        const int32_t* positions, int32_t B, int32_t H_q, int32_t H_kv, int32_t D,
+                                        int32_t block_size, int32_t n_blocks, int32_t max_context_len, float scale,
+                                        int32_t partition_size, void* stream) {
+    const size_t need = pkv_decode_workspace_bytes(B, H_q, D, max_context_len, partition_size);
+    if (need > kScratchBytes)
+        return fail(PKV_ERR_WORKSPACE,
+                    "the split needs %zu bytes of partials; the allocation-free step holds at most %zu "
+                    "(use pkv_append_decode_attention with a workspace, or a larger partition_size)",
+                    need, kScratchBytes);
+    void* ws = nullptr;
+    if (need) {
+        const int st = scratch_for_current_device(&ws);
+        if (st) return st;
+    }
+    return pkv_append_decode_attention(dtype, out, q, q_row_stride, k_new, v_new, new_row_stride, k_pool, v_pool,
+                                       block_tables, bt_stride, positions, B, H_q, H_kv, D, block_size, n_blocks,
+                                       max_context_len, scale, partition_size, ws, need ? kScratchBytes : 0, stream);
 }
 
 }  // extern "C"
