@@ -117,9 +117,25 @@ def read_ceiling(pkv, torch, dev, nbytes: int = 4 << 30, reps: int = 6) -> float
     return best
 
 
+def host_cpu_model() -> str:
+    """The host CPU's model string (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(w, step_bytes_total: float, kv_tokens: int, budget_s: float = 10.0):
-    """Time the fp64 oracle (as it stands) on the host cores on the same step; bounded to ~budget_s."""
+    """Time the fp64 oracle (as it stands) on the host's cores on the same step, bounded to about
+    budget_s, and on one thread on the batch's first requests (a sample of about 2 s)."""
     import oracle
+    from workloads import step_bytes
+
     threads = len(os.sched_getaffinity(0))
     if os.environ.get("OMP_NUM_THREADS", "").isdigit():
         threads = min(threads, int(os.environ["OMP_NUM_THREADS"]))
@@ -127,34 +143,46 @@ def cpu_baseline(w, step_bytes_total: float, kv_tokens: int, budget_s: float = 1
     kp, vp = w.k_pool.copy(), w.v_pool.copy()
     fp8 = getattr(w.cfg, "fp8", False)
     mx4 = getattr(w.cfg, "mxfp4", False)
+    ks = vs = None
     if fp8 or mx4:
         ks, vs = w.k_scale.copy(), w.v_scale.copy()
+    append = w.positions is not None
+
+    def step(nthreads, k):
+        """The oracle's append + attention for requests 0 .. k-1."""
+        q, bt, cl = w.q[:k], w.block_tables[:k], w.context_lens[:k]
+        if append:
+            args = (w.cfg.dtype, w.k_new[:k], w.v_new[:k], kp, vp) + ((ks, vs) if ks is not None else ()) + \
+                   (bt, w.positions[:k], w.cfg.block_size)
+            (oracle.kv_append_mxfp4 if mx4 else oracle.kv_append_fp8 if fp8 else oracle.kv_append)(*args)
+        if mx4:
+            oracle.paged_decode_attention_mxfp4(w.cfg.dtype, q, kp, vp, ks, vs, bt, cl, w.scale, nthreads=nthreads)
+        elif fp8:
+            oracle.paged_decode_attention_fp8(w.cfg.dtype, q, kp, vp, ks, vs, bt, cl, w.scale, nthreads=nthreads)
+        else:
+            oracle.paged_decode_attention(w.cfg.dtype, q, kp, vp, bt, cl, w.scale, nthreads=nthreads)
+
+    B = int(w.context_lens.size)
     times = []
     t_end = time.perf_counter() + budget_s
     while True:
         t0 = time.perf_counter()
-        if mx4:
-            if w.positions is not None:
-                oracle.kv_append_mxfp4(w.cfg.dtype, w.k_new, w.v_new, kp, vp, ks, vs, w.block_tables, w.positions,
-                                       w.cfg.block_size)
-            oracle.paged_decode_attention_mxfp4(w.cfg.dtype, w.q, kp, vp, ks, vs, w.block_tables, w.context_lens,
-                                                w.scale, nthreads=used)
-        elif fp8:
-            if w.positions is not None:
-                oracle.kv_append_fp8(w.cfg.dtype, w.k_new, w.v_new, kp, vp, ks, vs, w.block_tables, w.positions,
-                                     w.cfg.block_size)
-            oracle.paged_decode_attention_fp8(w.cfg.dtype, w.q, kp, vp, ks, vs, w.block_tables, w.context_lens,
-                                              w.scale, nthreads=used)
-        else:
-            if w.positions is not None:
-                oracle.kv_append(w.cfg.dtype, w.k_new, w.v_new, kp, vp, w.block_tables, w.positions,
-                                 w.cfg.block_size)
-            oracle.paged_decode_attention(w.cfg.dtype, w.q, kp, vp, w.block_tables, w.context_lens, w.scale,
-                                          nthreads=used)
+        step(used, B)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() >= t_end or len(times) >= 1000:
             break
     med = float(np.median(times))
+    # one thread: the first k requests, covering about 2 s of one-thread work (median of 3)
+    frac = min(1.0, 2.0 / max(med * used, 1e-9))
+    cum = np.cumsum(w.context_lens.astype(np.int64))
+    k = int(min(max(int(np.searchsorted(cum, frac * cum[-1])) + 1, 1), B))
+    t1 = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        step(1, k)
+        t1.append(time.perf_counter() - t0)
+    med1 = float(np.median(t1))
+    sb1 = step_bytes(w.cfg, w.context_lens[:k], append)["total"]
     return {
         "value": round(step_bytes_total / med / 1e9, 3),
         "unit": "GB/s",
@@ -162,8 +190,18 @@ def cpu_baseline(w, step_bytes_total: float, kv_tokens: int, budget_s: float = 1
         "s_per_step": med,
         "cores": used,
         "kind": "oracle",
+        "cpu_model": host_cpu_model(),
+        "host_logical_cpus": os.cpu_count(),
         "sample": f"the whole step of the same workload (seed {w.seed}), repeated {len(times)}x within "
-                  f"~{budget_s:.0f} s; median per step; fp64 C + OpenMP over (request, head)",
+                  f"~{budget_s:.0f} s on {used} threads; median per step; fp64 C + OpenMP over (request, head)",
+        "one_thread": {
+            "value": round(sb1 / med1 / 1e9, 4),
+            "unit": "GB/s",
+            "kv_tokens_per_s": round(float(cum[k - 1]) / med1, 1),
+            "s_per_sample": med1,
+            "sample": f"requests 0..{k - 1} of the batch ({int(cum[k - 1])} of {int(cum[-1])} context tokens, "
+                      f"{int(sb1)} algorithmic bytes), append + attention on one thread, median of 3",
+        },
     }
 
 
@@ -565,7 +603,11 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "c3f8", "c5f8", "c3f4", "c5f4"])
+    ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4", "c5", "c3f8", "c5f8", "c3f4", "c5f4"],
+                    help="the headline workload (default c4, the largest that fits one GPU)")
+    ap.add_argument("--also", default="c2,c3,c5",
+                    help="more workloads timed the same way in the same run, reported under other_workloads "
+                         "(comma-separated; 'none' for only --config)")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--partition", type=int, default=None, help="split-KV partition size (default: the workload's)")
     ap.add_argument("--no-append", action="store_true", help="attention only (no kv_append in the step)")
@@ -614,7 +656,78 @@ def main(argv=None):
     if args.mode == "cufrac":
         return cufrac_bench(args, torch, pkv, dev, lib)
 
-    cfg = get_config(args.config)
+    names = [args.config] + [c for c in (args.also.split(",") if args.also not in ("", "none") else [])
+                             if c and c != args.config]
+    result = None
+    others = {}
+    ceiling = read_ceiling(pkv, torch, dev)
+    for i, name in enumerate(names):
+        r = measure_step(name, args, torch, pkv, dev, lib, cpu=(i == 0 and not args.no_cpu_baseline), ceiling=ceiling)
+        print(json.dumps({"measured": name, "pct_of_peak": r["pct_of_peak"], "frac": r["roofline"]["frac"]}),
+              file=sys.stderr, flush=True)
+        if i == 0:
+            result = r
+        else:
+            others[name] = {k: r[k] for k in ("value", "unit", "pct_of_peak", "ms_per_step", "kv_tokens_per_s",
+                                              "dtype")}
+            others[name]["workload"] = r["config"]["workload"]
+            others[name]["launch"] = r["config"]["launch"]
+            others[name]["algorithmic_bytes_per_step"] = r["config"]["algorithmic_bytes_per_step"]
+            others[name]["roofline"] = {k: r["roofline"][k] for k in ("achieved", "frac", "traffic", "gpu_us_per_step",
+                                                                      "size_matched_read_probe")}
+    if others:
+        result["other_workloads"] = others
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def size_matched_read_probe(pkv, torch, dev, nbytes: int, kernel_grid: int, reps: int = 32):
+    """Best HBM read rate (GB/s) of the plain streaming-read probe over reads of the step's own
+    size, at the attention launch's grid and at other grid sizes: a ceiling for one launch that
+    moves that many bytes.  Successive launches read different slices of a buffer of at least
+    1 GiB + 4x the Infinity Cache, so no slice is cached; launches are replayed from a graph."""
+    nbytes = max(nbytes // 4096 * 4096, 4096)
+    n_slices = max(2, math.ceil((4 * INFINITY_CACHE_BYTES + (1 << 30)) / nbytes))
+    buf = torch.empty(n_slices * nbytes // 4, dtype=torch.int32, device=dev)
+    buf.fill_(1)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for grid in sorted({int(kernel_grid), 256, 1024, 2048, 4096, 8192, 16384}):
+        if grid < 1:
+            continue
+
+        def launch(k):
+            pkv.probe_stream_read(buf[(k % n_slices) * nbytes // 4:], sink, grid, nbytes=nbytes)
+
+        for k in range(2):
+            launch(k)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for k in range(reps):
+                launch(k)
+        gr.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        gr.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[grid] = round(nbytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9, 1)
+        del gr
+    del buf
+    best = max(res, key=res.get)
+    return {"bytes": nbytes, "best_GBps": res[best], "best_grid": best, "kernel_grid": int(kernel_grid),
+            "GBps_by_grid": {str(k): v for k, v in sorted(res.items())}}
+
+
+def measure_step(name, args, torch, pkv, dev, lib, cpu: bool, ceiling: float):
+    """Time K decode steps of workload `name` (fused append + attention, + merge when split)
+    over device-resident inputs; returns the bench's JSON record for it."""
+    from workloads import get_config, make_workload, step_bytes
+
+    cfg = get_config(name)
     append = not args.no_append
     P = cfg.partition_size if args.partition is None else args.partition
     w = make_workload(cfg, args.seed, append=append)
@@ -700,7 +813,8 @@ def main(argv=None):
     # pair around a single eager launch also catches.
     gpu_step_s = gpu_region_s / args.steps
     achieved = bytes_per_step / gpu_step_s / 1e9
-    ceiling = read_ceiling(pkv, torch, dev)
+    kernel_grid = int(launch.split("grid=")[1].split()[0]) if "grid=" in launch else 1024
+    probe = size_matched_read_probe(pkv, torch, dev, int(read_per_step), kernel_grid)
     digest = kernel_source_digest()
     traffic = traffic_from_profile(cfg.name + ("" if append else "_attn"), digest)
 
@@ -741,6 +855,8 @@ def main(argv=None):
             "gpu_us_per_step": round(gpu_step_s * 1e6, 2),
             "stream_read_probe_GBps": round(ceiling, 1),
             "frac_of_stream_read_probe": round(achieved / ceiling, 4),
+            "size_matched_read_probe": probe,
+            "frac_of_size_matched_read_probe": round(achieved / probe["best_GBps"], 4),
             "eager_launch_us": {"mean": round(float(launch_ms.mean()) * 1e3, 2),
                           "p10": round(float(np.percentile(launch_ms, 10)) * 1e3, 2),
                           "p50": round(float(np.median(launch_ms)) * 1e3, 2),
@@ -748,10 +864,12 @@ def main(argv=None):
             "kernel_src_digest": digest,
         },
     }
-    if not args.no_cpu_baseline:
+    if cpu:
         result["cpu_baseline"] = cpu_baseline(w, bytes_per_step, kv_tokens, args.cpu_budget)
-    print(json.dumps(result), flush=True)
-    return 0
+    del calls, sets
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return result
 
 
 if __name__ == "__main__":

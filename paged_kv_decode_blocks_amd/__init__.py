@@ -235,9 +235,12 @@ def last_launch() -> str:
     return load_library().pkv_last_launch().decode()
 
 
-def probe_stream_read(buf, sink, grid: int = 16384, *, stream=None):
-    """Launch the streaming-read measurement kernel over all of `buf` (a device tensor)."""
-    nbytes = buf.numel() * buf.element_size()
+def probe_stream_read(buf, sink, grid: int = 16384, *, nbytes: Optional[int] = None, stream=None):
+    """Launch the streaming-read measurement kernel over the first `nbytes` bytes of `buf`
+    (a device tensor; all of it by default)."""
+    total = buf.numel() * buf.element_size()
+    nbytes = total if nbytes is None else int(nbytes)
+    _require(0 <= nbytes <= total, "nbytes exceeds the buffer")
     _check(load_library().pkv_probe_stream_read(_ptr(buf), nbytes, _ptr(sink), int(grid), _stream(stream)),
            "probe_stream_read")
 
