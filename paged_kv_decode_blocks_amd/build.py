@@ -77,5 +77,40 @@ def _build_programs(hipcc: str, obj_dir: str):
         os.replace(tmp, out)
 
 
+def kernel_resource_usage(sources=None) -> dict:
+    """Per-kernel register, scratch and LDS use of the device code, from the compiler's
+    kernel-resource-usage remarks (device pass only; nothing is linked).
+
+    Returns {demangled kernel name: {"VGPRs", "AGPRs", "ScratchSize", "Occupancy", "LDS", ...}}.
+    """
+    import re
+    srcs = sources or [s for s in SOURCES if s.endswith(".hip")]
+    hipcc = _hipcc()
+    procs = []
+    for src in srcs:
+        cmd = [hipcc, *HIPCC_FLAGS, "--offload-device-only", "-c", os.path.join(CSRC, src), "-o", os.devnull,
+               "-Rpass-analysis=kernel-resource-usage"]
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+    raw = {}
+    for src, p in procs:
+        out, _ = p.communicate()
+        if p.returncode:
+            raise RuntimeError(f"hipcc failed for {src}:\n{out}")
+        name = None
+        for line in out.splitlines():
+            m = re.search(r"remark: Function Name: (\S+)", line)
+            if m:
+                name = m.group(1)
+                raw[name] = {"source": src}
+                continue
+            m = re.search(r"remark:\s+([A-Za-z ]+?)(?: \[[^\]]*\])?: (\d+) \[-Rpass", line)
+            if m and name:
+                key = {"LDS Size": "LDS", "ScratchSize": "ScratchSize"}.get(m.group(1).strip(), m.group(1).strip())
+                raw[name][key] = int(m.group(2))
+    names = list(raw)
+    dem = subprocess.run(["c++filt"], input="\n".join(names), stdout=subprocess.PIPE, text=True).stdout.splitlines()
+    return {d: raw[n] for n, d in zip(names, dem)}
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -67,6 +67,7 @@ struct Plan {
     bool grouped;     // matrix-core path (one workgroup per KV head and G query heads)
     int kind;         // grouped path: 0 = loads through registers, 1 = through an LDS ring
     int nw, ch, pf;   // waves per workgroup, blocks per chunk, chunks (or ring slots) in flight per wave
+    int32_t wave_tokens;  // grouped kernel: > 0 = each wave streams one partition of this many tokens
     int wpe;          // grouped FP8 kernel: waves per SIMD its registers are sized for
     int kd;           // grouped FP8 kernel: K tiles staged through LDS (1) or loaded into registers (0)
     unsigned grid;
@@ -123,7 +124,21 @@ Plan make_plan(int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32
         p.ch = env_int("PKV_GQA_CH", 1);
         p.pf = env_int("PKV_GQA_PF", 1);
         if (!pkv::gqa_variant_exists(p.kind, p.nw, p.ch, p.pf)) { p.kind = 2; p.nw = 4; p.ch = 1; p.pf = 1; }
-        p.grid = (unsigned)wgs;
+        // A split context: one workgroup spans nw consecutive partitions and wave w streams
+        // partition w alone, so each wave's softmax state is its partition's and the
+        // workgroup's closing merge of the waves is the log-sum-exp merge of those
+        // partitions; the merge kernel then combines spans.  Long per-wave streams and
+        // nw times fewer partial rows (measured on c5-shaped batches: as fast as 4x larger
+        // partitions shared round-robin).  Kernel 1 only, a span within one window of
+        // block ids, whole chunks per partition.
+        const int32_t span = p.nw * partition_size;
+        if (p.n_parts > 1 && p.kind != 1 && env_int("PKV_GQA_BLOCKED", 1) &&
+            span <= pkv::kGqaWindowTokens && (partition_size / pkv::kBlockSize) % p.ch == 0) {
+            p.wave_tokens = partition_size;
+            p.part_tokens = span;
+            p.n_parts = (max_ctx + span - 1) / span;
+        }
+        p.grid = (unsigned)((int64_t)p.n_parts * B * H_kv);
     } else {
         // a PF-deep load pipeline pays where a workgroup walks a long unsplit context
         int nw = 4, ch = 2, pf = 1;
@@ -282,6 +297,7 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
     a.max_context_len = max_ctx;
     a.part_tokens = p.part_tokens;
     a.n_parts = p.n_parts;
+    a.wave_tokens = p.wave_tokens;
     a.scale_log2 = scale * pkv::kLog2e;
     if (fp8) {
         a.k_scale = fp8->k;
@@ -360,7 +376,9 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
                  (dtype == PKV_BF16 && D == 128) ? 1 : 2, std::min<unsigned>(p.grid, (unsigned)persistent_wgs), p.grid,
                  p.part_tokens, p.n_parts, fused ? " fused_append" : "");
     } else {
-        snprintf(g_launch, sizeof g_launch, "%s dtype=%d D=%d nw=%d ch=%d pf=%d%s grid=%u part_tokens=%d n_parts=%d%s",
+        char wt[32] = "";
+        if (p.wave_tokens) snprintf(wt, sizeof wt, " wave_tokens=%d", p.wave_tokens);
+        snprintf(g_launch, sizeof g_launch, "%s dtype=%d D=%d nw=%d ch=%d pf=%d%s grid=%u part_tokens=%d n_parts=%d%s%s",
                  fp8 ? (p.grouped ? "gqa_mfma_fp8" : "fp8")
                      : p.grouped ? (p.kind == 1 ? "gqa_mfma_lds" : p.kind == 2 ? "gqa_mfma_kdma" : "gqa_mfma")
                                  : "mha",
@@ -368,7 +386,7 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
                  (fp8 && p.grouped)
                      ? (p.kd ? (p.wpe == 3 ? " wpe=3 kdma" : " wpe=2 kdma") : (p.wpe == 3 ? " wpe=3" : " wpe=2"))
                      : "",
-                 p.grid, p.part_tokens, p.n_parts, fused ? " fused_append" : "");
+                 p.grid, p.part_tokens, p.n_parts, wt, fused ? " fused_append" : "");
     }
     g_err[0] = 0;
     return PKV_OK;

@@ -47,7 +47,7 @@
 
 namespace pkv {
 
-constexpr int kWindowBlocksG = 256;
+constexpr int kWindowBlocksG = kGqaWindowTokens / kBlockSize;
 constexpr float kRescaleSlack = 8.0f;   // log2 units: weights stay below 256
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -303,13 +303,18 @@ struct GqaLane {
         accumulate<1>(kf, vf, valid);
     }
 
-    // Merge the waves' states through LDS (s_o: [NW][16][DP] floats, DP >= D) and
-    // write the normalised output, or this partition's (o / l, lse) for the merge kernel.
+    // Merge the waves' states through LDS and write the normalised output, or this
+    // partition's (o / l, lse) for the merge kernel.  Wave w's [16][DP] floats (DP >= D)
+    // are at s_o_lo + w * 16 DP for the first (NW + 1) / 2 waves and at s_o_hi + (w -
+    // (NW + 1) / 2) * 16 DP for the others, so the area may be two separate LDS objects.
     template <int NW, int DP>
-    __device__ __forceinline__ void finish(const AttnArgs& a, float (*s_m)[16], float (*s_l)[16], float* s_o_raw,
-                                           int w, int b, int g, int part, bool bad) {
+    __device__ __forceinline__ void finish(const AttnArgs& a, float (*s_m)[16], float (*s_l)[16], float* s_o_lo,
+                                           float* s_o_hi, int w, int b, int g, int part, bool bad) {
         static_assert(DP >= D, "merge row");
-        float (*s_o)[16][DP] = reinterpret_cast<float (*)[16][DP]>(s_o_raw);
+        constexpr int HALF = (NW + 1) / 2;
+        auto s_o = [&](int wv) -> float (*)[DP] {
+            return reinterpret_cast<float (*)[DP]>((wv < HALF ? s_o_lo : s_o_hi) + (wv % HALF) * 16 * DP);
+        };
         // per-head sum over the four lane groups (they share m)
         l += __shfl_xor(l, 16, 64);
         l += __shfl_xor(l, 32, 64);
@@ -320,7 +325,7 @@ struct GqaLane {
 #pragma unroll
         for (int t = 0; t < VT; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s_o[w][col][(4 * j + i) * VT + t] = acc[t][i];
+            for (int i = 0; i < 4; ++i) s_o(w)[col][(4 * j + i) * VT + t] = acc[t][i];
         __syncthreads();
         const int G = a.G;
         for (int x = threadIdx.x; x < G * D; x += NW * 64) {
@@ -334,7 +339,7 @@ struct GqaLane {
             for (int i = 0; i < NW; ++i) {
                 const float f = __builtin_amdgcn_exp2f(s_m[i][hh] - M);
                 L += s_l[i][hh] * f;
-                O += s_o[i][hh][d] * f;
+                O += s_o(i)[hh][d] * f;
             }
             const size_t row = (size_t)b * a.H_q + (size_t)g * G + hh;
             const float val = bad ? __builtin_nanf("") : O / L;
@@ -454,15 +459,19 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_kernel(const AttnArgs a) {
     constexpr int LPC = CH * (NDMA + 4);       // vmcnt units per chunk: K DMAs, then 4 V rows
     static_assert(R <= 4, "ring depth");
     static_assert(!KDMA || PF * LPC < 64, "vmcnt range");
-    __shared__ __attribute__((aligned(16))) char s_k0[KDMA ? NW * SLOT : 16];
-    __shared__ __attribute__((aligned(16))) char s_k1[KDMA ? NW * SLOT : 16];
+    // With KDMA the waves' merge rows ([16][D + 4] floats each, half of the waves in
+    // each of the first two ring slots) reuse the ring once every wave is past its loop.
+    constexpr int OROWS = 16 * (D + 4) * 4;                 // one wave's merge rows, bytes
+    constexpr int RING = KDMA ? (NW * SLOT > (NW + 1) / 2 * OROWS ? NW * SLOT : (NW + 1) / 2 * OROWS) : 16;
+    __shared__ __attribute__((aligned(16))) char s_k0[RING];
+    __shared__ __attribute__((aligned(16))) char s_k1[RING];
     __shared__ __attribute__((aligned(16))) char s_k2[KDMA && R > 2 ? NW * SLOT : 16];
     __shared__ __attribute__((aligned(16))) char s_k3[KDMA && R > 3 ? NW * SLOT : 16];
     __shared__ int32_t s_ids[kWindowBlocksG];
     __shared__ int s_bad;
     __shared__ float s_m[NW][16];
     __shared__ float s_l[NW][16];
-    __shared__ float s_o[NW * 16 * (D + 4)];
+    __shared__ float s_o[KDMA ? 4 : NW * 16 * (D + 4)];
 
     GqaUnit u;
     gqa_indices(a, u);
@@ -553,11 +562,18 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_kernel(const AttnArgs a) {
         const bool any_bad = s_bad != 0;
         const int nch = (nr + CH - 1) / CH;
 
-        // chunks wholly below `lim`: no masking; wave w takes chunks w, w + NW, ...
+        // Chunks wholly below `lim` need no masking.  Round-robin: wave w takes chunks w,
+        // w + NW, ... of the window.  Partition per wave (a.wave_tokens > 0; the span is
+        // one window): wave w takes the chunks of its own partition, blocks [wb0, wb1).
         const int tok_r = u.start + r0 * kBlockSize;
-        const int nfull_all = max(0, min(nch, (u.lim - tok_r) / (CH * kBlockSize)));
-        const int nf = w < nfull_all ? (nfull_all - w + NW - 1) / NW : 0;
-        auto chunk_of = [&](int i) { return (w + NW * i) * CH; };
+        const bool blocked = a.wave_tokens > 0;
+        const int wb0 = blocked ? w * (a.wave_tokens / kBlockSize) : 0;
+        const int wb1 = blocked ? min(wb0 + a.wave_tokens / kBlockSize, nr) : nr;
+        const int nch_w = blocked ? max(0, (wb1 - wb0 + CH - 1) / CH) : nch;
+        const int nfull_all = blocked ? max(0, min(nch_w, (u.lim - tok_r - wb0 * kBlockSize) / (CH * kBlockSize)))
+                                      : max(0, min(nch, (u.lim - tok_r) / (CH * kBlockSize)));
+        const int nf = blocked ? nfull_all : (w < nfull_all ? (nfull_all - w + NW - 1) / NW : 0);
+        auto chunk_of = [&](int i) { return blocked ? wb0 + i * CH : (w + NW * i) * CH; };
         // chunk i lives in buffer (and ring slot) i % R
         Buf buf[R];
         int i = 0;
@@ -587,19 +603,27 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_kernel(const AttnArgs a) {
                 }
             }
         }
-        // the partial chunk (at most one per round), block by block
-        for (int k = nfull_all + ((w - nfull_all) % NW + NW) % NW; k < nch; k += NW) {
+        // the partial chunk (at most one per round, or per partition), block by block
+        const int k0 = blocked ? nfull_all : nfull_all + ((w - nfull_all) % NW + NW) % NW;
+        for (int k = k0; k < nch_w; k += blocked ? 1 : NW) {
 #pragma unroll
             for (int cb = 0; cb < CH; ++cb) {
-                const int blk = k * CH + cb;
-                const int id = __builtin_amdgcn_readfirstlane(blk < nr ? s_ids[blk] : 0);
+                const int blk = (blocked ? wb0 : 0) + k * CH + cb;
+                const int id = __builtin_amdgcn_readfirstlane(blk < wb1 ? s_ids[blk] : 0);
                 const char* kb = a.k_pool + (size_t)id * blk_bytes + head_bytes;
                 const char* vb = a.v_pool + (size_t)id * blk_bytes + head_bytes;
                 st.partial_block(a, kb, vb, tok_r + blk * kBlockSize, u.lim, u.pos_new, new_off, !any_bad);
             }
         }
     }
-    st.template finish<NW, D + 4>(a, s_m, s_l, s_o, w, u.b, u.g, u.part, s_bad != 0);
+    if constexpr (KDMA) {
+        __syncthreads();   // every wave is done with its ring slots: the merge reuses them
+        st.template finish<NW, D + 4>(a, s_m, s_l, reinterpret_cast<float*>(s_k0), reinterpret_cast<float*>(s_k1),
+                                      w, u.b, u.g, u.part, s_bad != 0);
+    } else {
+        st.template finish<NW, D + 4>(a, s_m, s_l, s_o, s_o + (NW + 1) / 2 * 16 * (D + 4), w, u.b, u.g, u.part,
+                                      s_bad != 0);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -759,7 +783,9 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_lds_kernel(const AttnArgs 
     __syncthreads();   // every wave is done with its ring: the merge reuses that LDS
     // unpadded [NW][16][D] floats are exactly NW * SLOT bytes: the merge fits in slot 0's object
     static_assert(NW * 16 * D * 4 <= NW * SLOT, "merge area");
-    st.template finish<NW, D>(a, s_m, s_l, reinterpret_cast<float*>(s_ring0), w, u.b, u.g, u.part, s_bad != 0);
+    st.template finish<NW, D>(a, s_m, s_l, reinterpret_cast<float*>(s_ring0),
+                              reinterpret_cast<float*>(s_ring0) + (NW + 1) / 2 * 16 * D, w, u.b, u.g, u.part,
+                              s_bad != 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -788,7 +814,8 @@ static hipError_t launch_gqa_lds_t(bool append, const AttnArgs& a, unsigned grid
 // (waves, blocks per chunk, chunks in flight) of kernel 1 with K in registers (kind 0) and with
 // K staged in LDS (kind 2); (waves, ring slots) of the LDS kernel (kind 1)
 #define PKV_GQA_VARIANTS(X) X(4, 1, 1) X(4, 1, 2) X(2, 1, 1) X(2, 1, 2) X(4, 2, 1)
-#define PKV_GQA_KDMA_VARIANTS(X) X(2, 1, 1) X(2, 1, 2) X(4, 1, 1) X(2, 2, 1)
+#define PKV_GQA_KDMA_VARIANTS(X) X(2, 1, 1) X(2, 1, 2) X(4, 1, 1) X(2, 2, 1) X(4, 1, 2) X(8, 1, 1) X(1, 1, 1) \
+    X(1, 1, 2)
 #define PKV_GQA_LDS_VARIANTS(X) X(2, 2) X(2, 3) X(2, 4) X(4, 2) X(4, 3) X(8, 2)
 
 template <int DT, int D>
@@ -1329,13 +1356,14 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_gqa_fp8_kernel(const Attn
         for (int q = 0; q < KL; ++q) kc[0][q] = c[0].k[q];
         st.template accumulate8<1>(kc, c, valid);
     }
-    st.template finish<NW, D + 4>(a, s_m, s_l, s_o, w, u.b, u.g, u.part, s_bad != 0);
+    st.template finish<NW, D + 4>(a, s_m, s_l, s_o, s_o + (NW + 1) / 2 * 16 * (D + 4), w, u.b, u.g, u.part,
+                                  s_bad != 0);
 }
 
 #define PKV_GQA_FP8_VARIANTS(X)                                                                       \
     X(2, 1, 1, 2, 0) X(2, 1, 2, 2, 0) X(4, 1, 1, 2, 0) X(2, 2, 1, 2, 0) X(4, 2, 1, 2, 0) X(2, 1, 1, 3, 0) \
-    X(4, 1, 1, 3, 0) X(4, 1, 2, 3, 0) X(2, 1, 1, 2, 1) X(2, 1, 2, 2, 1) X(2, 1, 3, 2, 1) X(4, 1, 1, 2, 1) \
-    X(4, 1, 2, 2, 1) X(2, 2, 1, 2, 1) X(2, 1, 1, 3, 1) X(4, 1, 2, 3, 1)
+    X(4, 1, 1, 3, 0) X(2, 1, 1, 2, 1) X(2, 1, 2, 2, 1) X(2, 1, 3, 2, 1) X(4, 1, 1, 2, 1) X(4, 1, 2, 2, 1) \
+    X(2, 2, 1, 2, 1) X(2, 1, 1, 3, 1) X(4, 1, 2, 3, 1)
 
 #define PKV_GQA_FP8_KEY(NW_, CH_, PF_, W_, KD_) ((KD_) * 10000 + (W_) * 1000 + (NW_) * 100 + (CH_) * 10 + (PF_))
 

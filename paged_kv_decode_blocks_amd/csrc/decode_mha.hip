@@ -155,24 +155,32 @@ __device__ __forceinline__ void mha_unit(const AttnArgs& a, const int unit) {
     for (int j = 0; j < NL; ++j) all_valid[j] = true;
 
     if (threadIdx.x == 0) s_bad = 0;
+    __syncthreads();
+    // The first window comes from the ids loaded up front; staging it before the
+    // window loop ends their live range here, so nothing of it is held (or
+    // spilled) across the loads of the loop.
+#pragma unroll
+    for (int k = 0; k < PRE; ++k) {
+        const int t = threadIdx.x + k * NW * 64;
+        if (t < min(kWindowBlocks, nblk)) {
+            int id = pre[k];
+            if ((unsigned)id >= (unsigned)a.n_blocks) {
+                s_bad = 1;
+                id = 0;
+            }
+            s_ids[t] = id;
+        }
+    }
     for (int r0 = 0; r0 < nblk; r0 += kWindowBlocks) {
         const int nr = min(kWindowBlocks, nblk - r0);
-        __syncthreads();
-        if (r0 == 0) {   // the first window was loaded up front
-#pragma unroll
-            for (int k = 0; k < PRE; ++k) {
-                const int t = threadIdx.x + k * NW * 64;
-                if (t < nr) {
-                    int id = pre[k];
-                    if ((unsigned)id >= (unsigned)a.n_blocks) {
-                        s_bad = 1;
-                        id = 0;
-                    }
-                    s_ids[t] = id;
-                }
-            }
-        } else {
-            for (int t = threadIdx.x; t < nr; t += NW * 64) {
+        if (r0 > 0) {
+            __syncthreads();   // every wave is done with the previous window
+            // the thread index is re-read here so that the per-thread staging
+            // addresses are formed inside this rare branch instead of being
+            // hoisted out of the loop and kept live across it
+            int tid = threadIdx.x;
+            asm volatile("" : "+v"(tid));
+            for (int t = tid; t < nr; t += NW * 64) {
                 int id = table[first_blk + r0 + t];
                 if ((unsigned)id >= (unsigned)a.n_blocks) {
                     s_bad = 1;
@@ -344,15 +352,28 @@ static hipError_t launch_mha_t(bool append, const AttnArgs& a, unsigned grid, hi
 
 template <int DT, int D>
 static hipError_t launch_mha_d(int nw, int ch, int pf, bool append, const AttnArgs& a, unsigned grid, hipStream_t s) {
-    switch (nw * 100 + ch * 10 + pf) {
-    case 421: return launch_mha_t<DT, D, 4, 2, 1>(append, a, grid, s);
-    case 422: return launch_mha_t<DT, D, 4, 2, 2>(append, a, grid, s);
-    case 423: return launch_mha_t<DT, D, 4, 2, 3>(append, a, grid, s);
-    case 412: return launch_mha_t<DT, D, 4, 1, 2>(append, a, grid, s);
-    case 414: return launch_mha_t<DT, D, 4, 1, 4>(append, a, grid, s);
-    case 822: return launch_mha_t<DT, D, 8, 2, 2>(append, a, grid, s);
-    case 821: return launch_mha_t<DT, D, 8, 2, 1>(append, a, grid, s);
-    default: return hipErrorInvalidValue;
+    if constexpr (DT == DT_F32 && D == 128) {
+        // f32 rows of 128 take 16 loads per 2-block chunk: the planner runs them with one
+        // 2-block chunk in flight (deeper pipelines would spill), the only ones built
+        if (ch != 2 || pf != 1) return hipErrorInvalidValue;
+        if (nw == 4) return launch_mha_t<DT, D, 4, 2, 1>(append, a, grid, s);
+        if (nw == 8) return launch_mha_t<DT, D, 8, 2, 1>(append, a, grid, s);
+        return hipErrorInvalidValue;
+    } else {
+        switch (nw * 100 + ch * 10 + pf) {
+        case 421: return launch_mha_t<DT, D, 4, 2, 1>(append, a, grid, s);
+        case 422: return launch_mha_t<DT, D, 4, 2, 2>(append, a, grid, s);
+        case 423: return launch_mha_t<DT, D, 4, 2, 3>(append, a, grid, s);
+        case 412: return launch_mha_t<DT, D, 4, 1, 2>(append, a, grid, s);
+        case 414: return launch_mha_t<DT, D, 4, 1, 4>(append, a, grid, s);
+        case 822: return launch_mha_t<DT, D, 8, 2, 2>(append, a, grid, s);
+        case 821: return launch_mha_t<DT, D, 8, 2, 1>(append, a, grid, s);
+        case 121: return launch_mha_t<DT, D, 1, 2, 1>(append, a, grid, s);
+        case 122: return launch_mha_t<DT, D, 1, 2, 2>(append, a, grid, s);
+        case 221: return launch_mha_t<DT, D, 2, 2, 1>(append, a, grid, s);
+        case 222: return launch_mha_t<DT, D, 2, 2, 2>(append, a, grid, s);
+        default: return hipErrorInvalidValue;
+        }
     }
 }
 
@@ -393,7 +414,8 @@ hipError_t launch_decode_mha_persistent(int dtype, int D, bool append, const Att
 
 bool mha_variant_exists(int nw, int ch, int pf) {
     switch (nw * 100 + ch * 10 + pf) {
-    case 421: case 422: case 423: case 412: case 414: case 822: case 821: return true;
+    case 421: case 422: case 423: case 412: case 414: case 822: case 821: case 121: case 122: case 221: case 222:
+        return true;
     default: return false;
     }
 }

@@ -13,6 +13,7 @@ namespace pkv {
 enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };   // storage dtypes of q, K/V and new rows
 
 constexpr int kBlockSize = 16;   // tokens per physical KV block (the only size built)
+constexpr int kGqaWindowTokens = 256 * kBlockSize;   // block ids a grouped workgroup stages in LDS at a time
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -3.0e38f;   // "no score yet": exp2(kNegBig - m) == 0 for any real m
 
@@ -204,8 +205,11 @@ struct AttnArgs {
     int32_t B, H_q, H_kv, G;
     int32_t n_blocks;
     int32_t max_context_len;
-    int32_t part_tokens;           // tokens per partition (whole padded context when not split)
-    int32_t n_parts;               // partitions per (request, head); 1 = no split
+    int32_t part_tokens;           // tokens per workgroup span (whole padded context when not split)
+    int32_t n_parts;               // spans per (request, head); 1 = no split
+    int32_t wave_tokens;           // grouped kernel: 0 = the waves share the span's chunks round-robin;
+                                   // > 0 = the span is part_tokens / wave_tokens partitions of this many
+                                   // tokens and wave w streams partition w alone
     float scale_log2;              // scale * log2(e)
 };
 

@@ -132,8 +132,8 @@ def test_fp8_every_launch_variant(torch_dev, monkeypatch, variant):
 # (waves, blocks per chunk, chunks in flight, waves per SIMD, K staged through LDS): every
 # variant the library instantiates for the grouped FP8 kernel
 GQA8_VARIANTS = ["2,1,1,2,0", "2,1,2,2,0", "4,1,1,2,0", "2,2,1,2,0", "4,2,1,2,0", "2,1,1,3,0", "4,1,1,3,0",
-                 "4,1,2,3,0", "2,1,1,2,1", "2,1,2,2,1", "2,1,3,2,1", "4,1,1,2,1", "4,1,2,2,1", "2,2,1,2,1",
-                 "2,1,1,3,1", "4,1,2,3,1"]
+                 "2,1,1,2,1", "2,1,2,2,1", "2,1,3,2,1", "4,1,1,2,1", "4,1,2,2,1", "2,2,1,2,1", "2,1,1,3,1",
+                 "4,1,2,3,1"]
 
 
 @pytest.mark.parametrize("variant", GQA8_VARIANTS)
