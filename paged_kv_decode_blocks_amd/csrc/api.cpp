@@ -75,8 +75,10 @@ struct Plan {
 };
 
 // Launch geometry.  Unsplit: one partition spanning the padded context.
+// `spans`: the kernel the plan is for implements one partition per wave (the 16-bit
+// per-head and grouped kernels, not the persistent, FP8 or MXFP4 ones).
 Plan make_plan(int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t max_ctx, int32_t partition_size,
-               bool fp8 = false) {
+               bool fp8 = false, bool spans = false) {
     Plan p{};
     const int32_t padded = max_ctx <= 0 ? pkv::kBlockSize
                                         : (max_ctx + pkv::kBlockSize - 1) / pkv::kBlockSize * pkv::kBlockSize;
@@ -132,8 +134,8 @@ Plan make_plan(int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32
         // partitions shared round-robin).  Kernel 1 only, a span within one window of
         // block ids, whole chunks per partition.
         const int32_t span = p.nw * partition_size;
-        if (p.n_parts > 1 && p.kind != 1 && env_int("PKV_GQA_BLOCKED", 1) &&
-            span <= pkv::kGqaWindowTokens && (partition_size / pkv::kBlockSize) % p.ch == 0) {
+        if (spans && p.n_parts > 1 && p.kind != 1 && env_int("PKV_GQA_BLOCKED", 1) &&
+            span <= pkv::kGqaSpanTokens && (partition_size / pkv::kBlockSize) % p.ch == 0) {
             p.wave_tokens = partition_size;
             p.part_tokens = span;
             p.n_parts = (max_ctx + span - 1) / span;
@@ -143,13 +145,28 @@ Plan make_plan(int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32
         // a PF-deep load pipeline pays where a workgroup walks a long unsplit context
         int nw = 4, ch = 2, pf = 1;
         if (p.n_parts == 1 && wgs > 4 * 256 && blocks >= 64) { nw = 8; pf = 2; }
+        // a split context takes one partition per wave below (8 waves while a span of
+        // 8 partitions fits one window of block ids: c4 at P = 512 then needs no merge
+        // kernel, 397 vs 426 us per step with 4 waves sharing each partition)
+        const bool want_spans = spans && p.n_parts > 1 && env_int("PKV_MHA_BLOCKED", 1);
+        if (want_spans && 8 * partition_size <= pkv::kMhaWindowTokens) nw = 8;
         p.nw = env_int("PKV_MHA_NW", nw);
         p.ch = env_int("PKV_MHA_CH", ch);
         p.pf = env_int("PKV_MHA_PF", pf);
         if (!pkv::mha_variant_exists(p.nw, p.ch, p.pf)) { p.nw = nw; p.ch = ch; p.pf = pf; }
         // f32 rows of 128 take 16 loads per 2-block chunk: deeper pipelines would spill
         if (dtype == PKV_F32 && D == 128) { p.ch = 2; p.pf = 1; }
-        p.grid = (unsigned)wgs;
+        // A split context may also take one partition per wave, as on the grouped path
+        // (the workgroup's closing merge of its waves is the log-sum-exp merge of nw
+        // consecutive partitions); per-head kernels only while a span fits one window
+        // of block ids and holds whole chunks.
+        const int32_t span = p.nw * partition_size;
+        if (want_spans && span <= pkv::kMhaWindowTokens && (partition_size / pkv::kBlockSize) % p.ch == 0) {
+            p.wave_tokens = partition_size;
+            p.part_tokens = span;
+            p.n_parts = (max_ctx + span - 1) / span;
+        }
+        p.grid = (unsigned)((int64_t)p.n_parts * B * H_q);
     }
     if (p.n_parts > 1) {
         p.ws_o = align_up((size_t)B * H_q * p.n_parts * D * sizeof(float), 256);
@@ -236,7 +253,8 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
     if (mx4 && (uint64_t)n_blocks * H_kv * block_size * (D / 2) >= (1ull << 40))
         return fail(PKV_ERR_UNSUPPORTED, "MXFP4 code pools of 1 TiB or more are not supported");
 
-    Plan p = make_plan(dtype, B, H_q, H_kv, D, max_ctx, partition_size, fp8 != nullptr);
+    Plan p = make_plan(dtype, B, H_q, H_kv, D, max_ctx, partition_size, fp8 != nullptr,
+                       !fp8 && !mx4 && !persistent_wgs);
     if (mx4) {
         // kind 1: one workgroup per KV head and its G <= 16 query heads on MFMA (f16/bf16 q),
         // reading each K/V block once for the group; kind 0: one workgroup per query head on the

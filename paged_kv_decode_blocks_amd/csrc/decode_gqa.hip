@@ -374,10 +374,10 @@ __device__ __forceinline__ void gqa_indices(const AttnArgs& a, GqaUnit& u) {
 
 // The partition's first window of block ids, loaded before the length is known
 // (clamped to the table row; only entries below the real block count are used).
-template <int NW, int PRE>
+template <int NW, int PRE, int WIN = kWindowBlocksG>
 __device__ __forceinline__ void gqa_preload_ids(const AttnArgs& a, const GqaUnit& u, int (&pre)[PRE]) {
     const int32_t* table = a.block_tables + (int64_t)u.b * a.bt_stride;
-    const int spec = min(min(a.part_tokens / kBlockSize, kWindowBlocksG), a.bt_stride - u.first_blk);
+    const int spec = min(min(a.part_tokens / kBlockSize, WIN), a.bt_stride - u.first_blk);
 #pragma unroll
     for (int k = 0; k < PRE; ++k) {
         const int t = threadIdx.x + k * NW * 64;
@@ -427,7 +427,11 @@ __device__ __forceinline__ void stage_ids(const AttnArgs& a, const int32_t* tabl
         }
         return;
     }
-    for (int t = threadIdx.x; t < nr; t += NW * 64) {
+    // the thread index is re-read here so that the staging addresses of a later window are
+    // formed where they are used instead of being hoisted out of the caller's loop
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    for (int t = tid; t < nr; t += NW * 64) {
         int id = table[first + r0 + t];
         if ((unsigned)id >= (unsigned)a.n_blocks) {
             *s_bad = 1;
@@ -467,7 +471,8 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_kernel(const AttnArgs a) {
     __shared__ __attribute__((aligned(16))) char s_k1[RING];
     __shared__ __attribute__((aligned(16))) char s_k2[KDMA && R > 2 ? NW * SLOT : 16];
     __shared__ __attribute__((aligned(16))) char s_k3[KDMA && R > 3 ? NW * SLOT : 16];
-    __shared__ int32_t s_ids[kWindowBlocksG];
+    constexpr int WIN = kGqaSpanTokens / kBlockSize;   // block ids staged in LDS at a time
+    __shared__ int32_t s_ids[WIN];
     __shared__ int s_bad;
     __shared__ float s_m[NW][16];
     __shared__ float s_l[NW][16];
@@ -479,9 +484,9 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_kernel(const AttnArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar)
     L st;
     st.init(a, lane, u.b, u.g);   // q loads, issued before the length is known
-    constexpr int PRE = (kWindowBlocksG + NW * 64 - 1) / (NW * 64);
+    constexpr int PRE = (WIN + NW * 64 - 1) / (NW * 64);
     int pre[PRE];
-    gqa_preload_ids<NW>(a, u, pre);
+    gqa_preload_ids<NW, PRE, WIN>(a, u, pre);
     if (!gqa_unit<D, NW, APPEND>(a, u)) return;
 
     const int32_t* table = a.block_tables + (int64_t)u.b * a.bt_stride;
@@ -554,10 +559,15 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_kernel(const AttnArgs a) {
     };
 
     if (threadIdx.x == 0) s_bad = 0;
-    for (int r0 = 0; r0 < nblk; r0 += kWindowBlocksG) {
-        const int nr = min(kWindowBlocksG, nblk - r0);
-        __syncthreads();
-        stage_ids<NW>(a, table, first_blk, r0, nr, pre, s_ids, &s_bad);
+    __syncthreads();
+    // the first window from the preloaded ids, before the loop: their live range ends here
+    stage_ids<NW>(a, table, first_blk, 0, min(WIN, nblk), pre, s_ids, &s_bad);
+    for (int r0 = 0; r0 < nblk; r0 += WIN) {
+        const int nr = min(WIN, nblk - r0);
+        if (r0 > 0) {
+            __syncthreads();   // every wave is done with the previous window
+            stage_ids<NW>(a, table, first_blk, r0, nr, pre, s_ids, &s_bad);
+        }
         __syncthreads();
         const bool any_bad = s_bad != 0;
         const int nch = (nr + CH - 1) / CH;
@@ -814,8 +824,7 @@ static hipError_t launch_gqa_lds_t(bool append, const AttnArgs& a, unsigned grid
 // (waves, blocks per chunk, chunks in flight) of kernel 1 with K in registers (kind 0) and with
 // K staged in LDS (kind 2); (waves, ring slots) of the LDS kernel (kind 1)
 #define PKV_GQA_VARIANTS(X) X(4, 1, 1) X(4, 1, 2) X(2, 1, 1) X(2, 1, 2) X(4, 2, 1)
-#define PKV_GQA_KDMA_VARIANTS(X) X(2, 1, 1) X(2, 1, 2) X(4, 1, 1) X(2, 2, 1) X(4, 1, 2) X(8, 1, 1) X(1, 1, 1) \
-    X(1, 1, 2)
+#define PKV_GQA_KDMA_VARIANTS(X) X(2, 1, 1) X(2, 1, 2) X(4, 1, 1) X(2, 2, 1) X(4, 1, 2) X(8, 1, 1)
 #define PKV_GQA_LDS_VARIANTS(X) X(2, 2) X(2, 3) X(2, 4) X(4, 2) X(4, 3) X(8, 2)
 
 template <int DT, int D>

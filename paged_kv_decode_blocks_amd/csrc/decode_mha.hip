@@ -30,7 +30,7 @@
 
 namespace pkv {
 
-constexpr int kWindowBlocks = 256;
+constexpr int kWindowBlocks = kMhaWindowTokens / kBlockSize;
 
 // One work unit: (request, query head, partition) number `unit`, partition-major.
 template <int DT, int D, int NW, int CH, int PF, bool APPEND>
@@ -194,14 +194,22 @@ __device__ __forceinline__ void mha_unit(const AttnArgs& a, const int unit) {
         const int nch = (nr + CH - 1) / CH;
 
         // Chunks that lie wholly below `lim` need no masking.  Each wave takes its
-        // share of them (k = w, w + NW, ...) through a PF-deep load pipeline: the
-        // loads of chunk i + PF are issued as soon as chunk i has been consumed, so
-        // a wave keeps PF chunks of K/V in flight while it computes.
+        // share of them through a PF-deep load pipeline: the loads of chunk i + PF are
+        // issued as soon as chunk i has been consumed, so a wave keeps PF chunks of K/V
+        // in flight while it computes.  Round-robin: wave w takes chunks w, w + NW, ...
+        // of the window.  Partition per wave (a.wave_tokens > 0; the span is one
+        // window): wave w takes the chunks of its own partition, blocks [wb0, wb1).
         const int tok_r = start + r0 * kBlockSize;
-        const int nfull_all = max(0, min(nch, (lim - tok_r) / (CH * kBlockSize)));
-        const int nf = w < nfull_all ? (nfull_all - w + NW - 1) / NW : 0;
+        const bool blocked = a.wave_tokens > 0;
+        const int wb0 = blocked ? w * (a.wave_tokens / kBlockSize) : 0;
+        const int wb1 = blocked ? min(wb0 + a.wave_tokens / kBlockSize, nr) : nr;
+        const int nch_w = blocked ? max(0, (wb1 - wb0 + CH - 1) / CH) : nch;
+        const int nfull_all = blocked ? max(0, min(nch_w, (lim - tok_r - wb0 * kBlockSize) / (CH * kBlockSize)))
+                                      : max(0, min(nch, (lim - tok_r) / (CH * kBlockSize)));
+        const int nf = blocked ? nfull_all : (w < nfull_all ? (nfull_all - w + NW - 1) / NW : 0);
         uint4 bk[PF][NL], bv[PF][NL];
-        auto chunk_of = [&](int i) { return (w + NW * i) * CH; };   // round-local first block of the wave's chunk i
+        // round-local first block of the wave's chunk i
+        auto chunk_of = [&](int i) { return blocked ? wb0 + i * CH : (w + NW * i) * CH; };
         if (nf >= PF) {
 #pragma unroll
             for (int u = 0; u < PF; ++u) load_full(bk[u], bv[u], chunk_of(u));
@@ -231,16 +239,17 @@ __device__ __forceinline__ void mha_unit(const AttnArgs& a, const int unit) {
             }
         }
 
-        // The partial chunk (at most one per round): masked loads, and in the
-        // fused call the new token from k_new/v_new.
-        for (int k = nfull_all + ((w - nfull_all) % NW + NW) % NW; k < nch; k += NW) {
-            const int cb0 = k * CH;
+        // The partial chunk (at most one per round, or per partition): masked loads,
+        // and in the fused call the new token from k_new/v_new.
+        const int k0 = blocked ? nfull_all : nfull_all + ((w - nfull_all) % NW + NW) % NW;
+        for (int k = k0; k < nch_w; k += blocked ? 1 : NW) {
+            const int cb0 = (blocked ? wb0 : 0) + k * CH;
             const int tok0 = start + (r0 + cb0) * kBlockSize;
             const char* kb[CH];
             const char* vb[CH];
 #pragma unroll
             for (int cb = 0; cb < CH; ++cb) {
-                const int id = __builtin_amdgcn_readfirstlane(cb0 + cb < nr ? s_ids[cb0 + cb] : 0);
+                const int id = __builtin_amdgcn_readfirstlane(cb0 + cb < wb1 ? s_ids[cb0 + cb] : 0);
                 kb[cb] = a.k_pool + (size_t)id * blk_bytes + head_bytes;
                 vb[cb] = a.v_pool + (size_t)id * blk_bytes + head_bytes;
             }
@@ -318,8 +327,11 @@ __device__ __forceinline__ void mha_unit(const AttnArgs& a, const int unit) {
         a.part_lse[(size_t)bh * a.n_parts + part] = bad ? __builtin_nanf("") : M + __builtin_amdgcn_logf(L);
 }
 
+// Two chunks of two blocks (or four of one) in flight need about 190 VGPRs; left
+// unbounded the compiler takes all 256 of a lone wave plus one AGPR, and the
+// kernel runs at one wave per SIMD.  Those variants are held to two.
 template <int DT, int D, int NW, int CH, int PF, bool APPEND>
-__global__ __launch_bounds__(NW * 64) void decode_mha_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(NW * 64, CH * PF == 4 ? 2 : 1) void decode_mha_kernel(const AttnArgs a) {
     mha_unit<DT, D, NW, CH, PF, APPEND>(a, blockIdx.x);
 }
 
@@ -368,10 +380,6 @@ static hipError_t launch_mha_d(int nw, int ch, int pf, bool append, const AttnAr
         case 414: return launch_mha_t<DT, D, 4, 1, 4>(append, a, grid, s);
         case 822: return launch_mha_t<DT, D, 8, 2, 2>(append, a, grid, s);
         case 821: return launch_mha_t<DT, D, 8, 2, 1>(append, a, grid, s);
-        case 121: return launch_mha_t<DT, D, 1, 2, 1>(append, a, grid, s);
-        case 122: return launch_mha_t<DT, D, 1, 2, 2>(append, a, grid, s);
-        case 221: return launch_mha_t<DT, D, 2, 2, 1>(append, a, grid, s);
-        case 222: return launch_mha_t<DT, D, 2, 2, 2>(append, a, grid, s);
         default: return hipErrorInvalidValue;
         }
     }
@@ -414,8 +422,7 @@ hipError_t launch_decode_mha_persistent(int dtype, int D, bool append, const Att
 
 bool mha_variant_exists(int nw, int ch, int pf) {
     switch (nw * 100 + ch * 10 + pf) {
-    case 421: case 422: case 423: case 412: case 414: case 822: case 821: case 121: case 122: case 221: case 222:
-        return true;
+    case 421: case 422: case 423: case 412: case 414: case 822: case 821: return true;
     default: return false;
     }
 }

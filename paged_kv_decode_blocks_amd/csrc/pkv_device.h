@@ -14,6 +14,8 @@ enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };   // storage dtypes of q, K/
 
 constexpr int kBlockSize = 16;   // tokens per physical KV block (the only size built)
 constexpr int kGqaWindowTokens = 256 * kBlockSize;   // block ids a grouped workgroup stages in LDS at a time
+constexpr int kGqaSpanTokens = 512 * kBlockSize;     // the same for the 16-bit grouped kernel with K in LDS
+constexpr int kMhaWindowTokens = 256 * kBlockSize;   // the same for the per-head kernel
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -3.0e38f;   // "no score yet": exp2(kNegBig - m) == 0 for any real m
 

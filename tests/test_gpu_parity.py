@@ -303,7 +303,7 @@ def test_bad_device_metadata_gives_nan_rows(torch_dev):
 # (kind, waves, blocks per chunk, chunks in flight or ring slots): every grouped variant the library instantiates
 GQA_VARIANTS = [(0, 4, 1, 1), (0, 4, 1, 2), (0, 2, 1, 1), (0, 2, 1, 2), (0, 4, 2, 1), (1, 2, 1, 2), (1, 2, 1, 3),
                 (1, 2, 1, 4), (1, 4, 1, 2), (1, 4, 1, 3), (1, 8, 1, 2), (2, 2, 1, 1), (2, 2, 1, 2), (2, 4, 1, 1),
-                (2, 2, 2, 1)]
+                (2, 2, 2, 1), (2, 4, 1, 2), (2, 8, 1, 1)]
 # (waves, blocks per chunk, chunks in flight): every per-head variant the library instantiates
 MHA_VARIANTS = [(4, 2, 1), (4, 2, 2), (4, 2, 3), (4, 1, 2), (4, 1, 4), (8, 2, 1), (8, 2, 2)]
 
