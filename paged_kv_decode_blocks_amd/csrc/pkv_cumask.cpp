@@ -160,8 +160,10 @@ void upload(void* dst, const std::string& path, size_t expect) {
 hipStream_t masked_stream(int n_cus, int count, int layout) {
     std::vector<uint32_t> mask((n_cus + 31) / 32);
     CHECK_PKV(pkv_cu_mask(n_cus, count, layout, mask.data(), (int32_t)mask.size()));
+    fprintf(stderr, "pkv_cumask: creating a stream on %d of %d CUs (%s)\n", count, n_cus, layout ? "spread" : "first");
     void* s = nullptr;
     CHECK_PKV(pkv_stream_create_cu_masked(mask.data(), (int32_t)mask.size(), &s));
+    fprintf(stderr, "pkv_cumask: stream created\n");
     return (hipStream_t)s;
 }
 
@@ -178,9 +180,11 @@ int run_check(const std::string& dir) {
         fclose(f);
         st.append = app != 0;
     }
+    fprintf(stderr, "pkv_cumask: allocating\n");
     st.alloc();
     const int e = elem_bytes(st.dtype);
     const int n_cus = pkv_device_cu_count();
+    fprintf(stderr, "pkv_cumask: %d CUs\n", n_cus);
     struct Run { const char* tag; int count, layout; };
     const Run runs[] = {{"full", 0, 0}, {"m8_spread", 8, 1}, {"m32_first", 32, 0}, {"m128_spread", 128, 1}};
     for (const Run& r : runs) {
@@ -196,8 +200,10 @@ int run_check(const std::string& dir) {
             upload(st.ctx, dir + "/context_lens.bin", (size_t)st.B * 4);
         }
         hipStream_t s = r.count ? masked_stream(n_cus, r.count, r.layout) : nullptr;
+        fprintf(stderr, "pkv_cumask: step %s\n", r.tag);
         CHECK_PKV(st.launch(s));
         CHECK_HIP(hipDeviceSynchronize());
+        fprintf(stderr, "pkv_cumask: step %s done\n", r.tag);
         std::vector<char> host((size_t)st.B * st.H_q * st.D * 4);
         CHECK_HIP(hipMemcpy(host.data(), st.out, host.size(), hipMemcpyDeviceToHost));
         write_file(dir + "/out_" + r.tag + ".bin", host.data(), host.size());
@@ -438,6 +444,10 @@ int run_sweep(int argc, char** argv) {
 }  // namespace
 
 int main(int argc, char** argv) {
+    // unbuffered: a run that dies part-way leaves every line it got to in the parent's pipes
+    setvbuf(stdout, nullptr, _IONBF, 0);
+    setvbuf(stderr, nullptr, _IONBF, 0);
+    fprintf(stderr, "pkv_cumask: start\n");
     if (argc >= 3 && std::string(argv[1]) == "check") return run_check(argv[2]);
     if (argc >= 2 && std::string(argv[1]) == "sweep") return run_sweep(argc, argv);
     fprintf(stderr, "usage: pkv_cumask check DIR | pkv_cumask sweep dtype B H_q H_kv D P append pool_factor seed steps lens\n");
