@@ -79,9 +79,12 @@ typedef enum {
     PKV_ERR_INVALID_ARG = -2,   /* sizes, strides or alignment are inconsistent          */
     PKV_ERR_UNSUPPORTED = -3,   /* valid, but outside the supported set above            */
     PKV_ERR_WORKSPACE = -4,     /* workspace missing or smaller than required            */
-    PKV_ERR_HIP = -5,           /* the HIP runtime reported an error when launching      */
-    PKV_ERR_OUT_OF_BLOCKS = -6, /* block manager: too few free blocks                     */
-    PKV_ERR_SEQUENCE = -7       /* block manager: sequence id unknown, or already in use  */
+    PKV_ERR_ALIASED_APPEND = -5,/* two appends of one step target the same (block, slot)
+                                   (pkv_check_step_metadata, or any append entry point
+                                   with PKV_DEBUG_CHECKS=1 in the environment)           */
+    PKV_ERR_HIP = -6,           /* the HIP runtime reported an error when launching      */
+    PKV_ERR_OUT_OF_BLOCKS = -7, /* block manager: too few free blocks                     */
+    PKV_ERR_SEQUENCE = -8       /* block manager: sequence id unknown, or already in use  */
 } pkv_status;
 
 /* Library version as major*10000 + minor*100 + patch. */
@@ -123,8 +126,10 @@ const char* pkv_last_launch(void);
  *   positions       [B]; a request with positions[b] outside [0, bt_stride*block_size)
  *                   or whose target block id is outside [0, n_blocks) is skipped
  *   B               number of requests (0 is a no-op)
- * Two requests must not target the same (block, slot); if they do, which one
- * lands is unspecified.
+ * Two requests must not target the same (block, slot): each new token has a
+ * slot of its own (same section).  The kernels do not detect it (which write
+ * lands is then unspecified); pkv_check_step_metadata does, and so does every
+ * append entry point when PKV_DEBUG_CHECKS=1 is set in the environment.
  */
 int pkv_kv_append(int dtype,
                   const void* k_new, const void* v_new, int64_t new_row_stride,
@@ -152,13 +157,22 @@ size_t pkv_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t D,
  *                    no device-to-host copy is made).  Must be <= bt_stride*block_size.
  *   partition_size   0: each (request, KV head) is handled by one workgroup over
  *                    its whole context.  > 0: the context is cut into partitions
- *                    of this many tokens (a multiple of block_size), each
- *                    workgroup handles one partition and a log-sum-exp merge
- *                    kernel combines them in partition order (deterministic).
+ *                    of this many tokens (a multiple of block_size); each
+ *                    partition's softmax state (maximum, sum, weighted V) is
+ *                    computed on its own and the states are combined by a
+ *                    log-sum-exp merge in partition order (deterministic).  The
+ *                    16-bit kernels give a workgroup several consecutive
+ *                    partitions, one per wave, and merge those themselves; a merge
+ *                    kernel combines the workgroups' results when a context needs
+ *                    more than one workgroup.
  *   workspace        device buffer of at least
  *                    pkv_decode_workspace_bytes(B, H_q, D, max_context_len,
- *                    partition_size) bytes, 256-byte aligned; may be NULL when
- *                    that is 0.  Its contents on entry do not matter.
+ *                    partition_size) bytes, 256-byte aligned (a size that always
+ *                    suffices); may be NULL when that is 0, or when the call's
+ *                    workgroups each span every partition of their contexts and
+ *                    merge them themselves (a call that needs partials and gets
+ *                    no or too small a workspace returns PKV_ERR_WORKSPACE).  Its
+ *                    contents on entry do not matter.
  */
 int pkv_paged_decode_attention(int dtype,
                                float* out,
@@ -199,6 +213,31 @@ int pkv_append_decode_attention(int dtype,
                                 int32_t max_context_len, float scale, int32_t partition_size,
                                 void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/*
+ * check_step_metadata -- debugging aid, not for the hot path: checks a step's
+ * device-side metadata against the contract the kernels assume, and returns the
+ * first violation ("从 PagedAttention 到 Prefill-Decode 分离的深度解析",
+ * section 2.2: a request's logical block j lives in physical block
+ * block_tables[b][j], and every new token is given a slot of its own).
+ *
+ *   context_lens / positions  exactly one is non-NULL: lengths of an attention
+ *                    call, or append positions (kv_append, or the fused step
+ *                    with n_b = positions[b] + 1)
+ *   max_context_len  the bound the call passes (0 with positions: a plain
+ *                    kv_append, whose lengths are not checked)
+ * Returns PKV_ERR_INVALID_ARG if a length lies outside [0, max_context_len]
+ * ([1, ...] for a fused step) or beyond bt_stride*block_size, or a block id the
+ * step reads or writes lies outside [0, n_blocks); else PKV_ERR_ALIASED_APPEND
+ * if two appends target the same (block, slot); else PKV_OK.  Runs on `stream`
+ * and waits for it (synchronous); allocates nothing (the verdict word is a
+ * device variable of the library).  Calls on one GPU that overlap race on that
+ * word.  O(B^2) comparisons.
+ */
+int pkv_check_step_metadata(const int32_t* block_tables, int32_t bt_stride,
+                            const int32_t* context_lens, const int32_t* positions,
+                            int32_t B, int32_t block_size, int32_t n_blocks,
+                            int32_t max_context_len, void* stream);
 
 /*
  * append_decode_attention_noalloc -- pkv_append_decode_attention for callers

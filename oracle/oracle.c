@@ -49,7 +49,7 @@
 #endif
 
 enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
-enum { ORC_OK = 0, ORC_ERR_ARG = -1, ORC_ERR_RANGE = -2, ORC_ERR_NOMEM = -3 };
+enum { ORC_OK = 0, ORC_ERR_ARG = -1, ORC_ERR_RANGE = -2, ORC_ERR_NOMEM = -3, ORC_ERR_ALIAS = -4 };
 
 static int elem_size(int dtype) {
     switch (dtype) {
@@ -99,6 +99,34 @@ int oracle_decode(int dtype, const void* src, double* dst, int64_t n) {
     return ORC_OK;
 }
 
+static int cmp_i64(const void* a, const void* b) {
+    int64_t x = *(const int64_t*)a, y = *(const int64_t*)b;
+    return (x > y) - (x < y);
+}
+
+/*
+ * The requests of one append step write distinct slots: each new token is given a
+ * slot of its own ("从 PagedAttention 到 Prefill-Decode 分离的深度解析", section
+ * 2.2, step three), so two requests naming the same (block, slot) is an error and
+ * nothing is written.  Targets are range-checked before this is called.
+ */
+static int check_distinct_targets(const int32_t* block_tables, int32_t bt_stride, const int32_t* positions,
+                                  int32_t B, int32_t block_size) {
+    int64_t* key = (int64_t*)malloc((size_t)B * sizeof(int64_t));
+    if (!key) return ORC_ERR_NOMEM;
+    for (int32_t b = 0; b < B; ++b) {
+        int32_t p = positions[b];
+        int32_t blk = block_tables[(int64_t)b * bt_stride + p / block_size];
+        key[b] = (int64_t)blk * block_size + p % block_size;
+    }
+    qsort(key, (size_t)B, sizeof(int64_t), cmp_i64);
+    int rc = ORC_OK;
+    for (int32_t b = 1; b < B; ++b)
+        if (key[b] == key[b - 1]) rc = ORC_ERR_ALIAS;
+    free(key);
+    return rc;
+}
+
 /*
  * Append: for every request b, copy the bits of k_new[b][g][:] and
  * v_new[b][g][:] (all KV heads g) into slot positions[b] % block_size of
@@ -121,6 +149,8 @@ int oracle_kv_append(int dtype, const void* k_new, const void* v_new, int64_t ne
         int32_t blk = block_tables[(int64_t)b * bt_stride + p / block_size];
         if (blk < 0 || blk >= n_blocks) return ORC_ERR_RANGE;
     }
+    int rc_alias = check_distinct_targets(block_tables, bt_stride, positions, B, block_size);
+    if (rc_alias != ORC_OK) return rc_alias;
     size_t row_bytes = (size_t)D * (size_t)e;
     for (int32_t b = 0; b < B; ++b) {
         int32_t p = positions[b];
@@ -357,6 +387,8 @@ int oracle_kv_append_fp8(int src_dtype, const void* k_new, const void* v_new, in
         int32_t blk = block_tables[(int64_t)b * bt_stride + p / block_size];
         if (blk < 0 || blk >= n_blocks) return ORC_ERR_RANGE;
     }
+    int rc_alias = check_distinct_targets(block_tables, bt_stride, positions, B, block_size);
+    if (rc_alias != ORC_OK) return rc_alias;
     for (int32_t b = 0; b < B; ++b) {
         int32_t p = positions[b];
         int32_t blk = block_tables[(int64_t)b * bt_stride + p / block_size];
@@ -498,6 +530,8 @@ int oracle_kv_append_mxfp4(int src_dtype, const void* k_new, const void* v_new, 
         int32_t blk = block_tables[(int64_t)b * bt_stride + p / block_size];
         if (blk < 0 || blk >= n_blocks) return ORC_ERR_RANGE;
     }
+    int rc_alias = check_distinct_targets(block_tables, bt_stride, positions, B, block_size);
+    if (rc_alias != ORC_OK) return rc_alias;
     for (int32_t b = 0; b < B; ++b) {
         int32_t p = positions[b];
         int32_t blk = block_tables[(int64_t)b * bt_stride + p / block_size];

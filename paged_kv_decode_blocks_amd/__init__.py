@@ -33,20 +33,21 @@ __all__ = [
     "device_cu_count", "append_decode_attention_persistent", "append_decode_attention_noalloc",
     "NOALLOC_SCRATCH_BYTES",
     "kv_append_mxfp4", "paged_decode_attention_mxfp4", "append_decode_attention_mxfp4", "copy_blocks_mxfp4",
-    "PKV_ERR_OUT_OF_BLOCKS", "PKV_ERR_SEQUENCE",
+    "PKV_ERR_OUT_OF_BLOCKS", "PKV_ERR_SEQUENCE", "PKV_ERR_ALIASED_APPEND", "PKV_ERR_HIP", "check_step_metadata",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
-PKV_ERR_INVALID_ARG, PKV_ERR_OUT_OF_BLOCKS, PKV_ERR_SEQUENCE = -2, -6, -7
+PKV_ERR_INVALID_ARG, PKV_ERR_ALIASED_APPEND, PKV_ERR_HIP, PKV_ERR_OUT_OF_BLOCKS, PKV_ERR_SEQUENCE = -2, -5, -6, -7, -8
 BLOCK_SIZE = 16
 
 EXPORTED_SYMBOLS = (
     "pkv_version", "pkv_status_string", "pkv_last_error", "pkv_last_launch", "pkv_kv_append",
     "pkv_decode_workspace_bytes", "pkv_paged_decode_attention", "pkv_append_decode_attention",
-    "pkv_append_decode_attention_persistent", "pkv_append_decode_attention_noalloc", "pkv_probe_mfma_burn",
+    "pkv_append_decode_attention_persistent", "pkv_append_decode_attention_noalloc", "pkv_check_step_metadata",
+    "pkv_probe_mfma_burn",
     "pkv_probe_stream_read", "pkv_copy_blocks", "pkv_copy_blocks_fp8", "pkv_kv_append_fp8", "pkv_paged_decode_attention_fp8",
     "pkv_append_decode_attention_fp8", "pkv_kv_append_mxfp4", "pkv_paged_decode_attention_mxfp4",
     "pkv_append_decode_attention_mxfp4", "pkv_copy_blocks_mxfp4",
@@ -131,6 +132,8 @@ def load_library(path: Optional[str] = None):
                                                 I32, I32, I32, I32, I32, I32, I32, ctypes.c_float, I32,
                                                 P, SZ, P]
     lib.pkv_append_decode_attention.restype = ctypes.c_int
+    lib.pkv_check_step_metadata.argtypes = [P, I32, P, P, I32, I32, I32, I32, P]
+    lib.pkv_check_step_metadata.restype = ctypes.c_int
     lib.pkv_append_decode_attention_noalloc.argtypes = [ctypes.c_int, P, P, I64, P, P, I64, P, P, P, I32, P,
                                                         I32, I32, I32, I32, I32, I32, I32, ctypes.c_float, I32, P]
     lib.pkv_append_decode_attention_noalloc.restype = ctypes.c_int
@@ -390,6 +393,28 @@ def append_decode_attention(q, k_new, v_new, k_pool, v_pool, block_tables, posit
         float(scale), int(partition_size), _ptr(ws), ws_bytes, _stream(stream))
     _check(rc, "append_decode_attention")
     return out
+
+
+def check_step_metadata(block_tables, *, context_lens=None, positions=None, n_blocks: int,
+                        max_context_len: int = 0, block_size: int = BLOCK_SIZE, stream=None) -> int:
+    """The step's device metadata against the kernels' contract (synchronous debugging aid).
+
+    Returns PKV_OK (0), PKV_ERR_INVALID_ARG (a length or block id out of range) or
+    PKV_ERR_ALIASED_APPEND (two appends of the step target one (block, slot)); the
+    detail of a violation is in last_error()."""
+    _require((context_lens is None) != (positions is None), "pass exactly one of context_lens and positions")
+    lens = positions if positions is not None else context_lens
+    B = int(lens.shape[0])
+    bts = _int32_2d(block_tables, "block_tables")
+    _int32_1d(lens, "positions" if positions is not None else "context_lens", B)
+    return int(load_library().pkv_check_step_metadata(
+        _ptr(block_tables), bts, _ptr(context_lens), _ptr(positions), B, int(block_size), int(n_blocks),
+        int(max_context_len), _stream(stream)))
+
+
+def last_error() -> str:
+    """Detail of the calling thread's last non-OK status."""
+    return load_library().pkv_last_error().decode()
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20     # PKV_NOALLOC_SCRATCH_BYTES
@@ -655,7 +680,7 @@ class StepGraphs:
         h = lib.pkv_step_graphs_create(ctypes.byref(d), ctypes.cast(bc, ctypes.c_void_p), len(bcaps),
                                        ctypes.cast(cc, ctypes.c_void_p), len(ccaps))
         if not h:
-            raise PkvError(-5, "pkv_step_graphs_create: " + lib.pkv_last_error().decode())
+            raise PkvError(PKV_ERR_HIP, "pkv_step_graphs_create: " + lib.pkv_last_error().decode())
         self._lib, self._h = lib, ctypes.c_void_p(h)
         self.batch_caps, self.ctx_caps = bcaps, ccaps
 
@@ -728,7 +753,7 @@ class Decoder:
         lib = load_library()
         h = lib.pkv_decoder_create(ctypes.byref(d))
         if not h:
-            raise PkvError(-5, "pkv_decoder_create: " + lib.pkv_last_error().decode())
+            raise PkvError(PKV_ERR_HIP, "pkv_decoder_create: " + lib.pkv_last_error().decode())
         self._lib, self._h = lib, ctypes.c_void_p(h)
         self.max_batch, self.bt_stride = max_batch, bt_stride
         self.block_manager = BlockManager(n_blocks, bs, _borrow=(lib.pkv_decoder_block_manager(self._h), self))

@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libpkv.so")
 
-SOURCES = ["api.cpp", "block_manager.cpp", "step_graphs.cpp", "decoder.cpp", "cu_streams.cpp", "kv_append.hip", "kv_append_fp8.hip", "decode_fp8.hip", "kv_append_mxfp4.hip", "decode_mxfp4.hip", "decode_mxfp4_mfma.hip", "block_copy.hip", "decode_mha.hip", "decode_gqa.hip", "lse_merge.hip", "probe.hip"]
+SOURCES = ["api.cpp", "block_manager.cpp", "step_graphs.cpp", "decoder.cpp", "cu_streams.cpp", "kv_append.hip", "kv_append_fp8.hip", "decode_fp8.hip", "kv_append_mxfp4.hip", "decode_mxfp4.hip", "decode_mxfp4_mfma.hip", "block_copy.hip", "decode_mha.hip", "decode_gqa.hip", "lse_merge.hip", "probe.hip", "debug_checks.hip"]
 
 # Packed-fp32 instructions are switched off for all device code.
 HIPCC_FLAGS = [

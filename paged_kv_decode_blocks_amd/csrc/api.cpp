@@ -332,6 +332,10 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
         a.v_mx_scale_w = mx4->v_w;
     }
 
+    if (fused) {
+        st = pkv::debug_check_appends(block_tables, bt_stride, positions, B, block_size, n_blocks, max_ctx, stream);
+        if (st) return st;
+    }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
     if (mx4) {
@@ -460,6 +464,7 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_INVALID_ARG: return "PKV_ERR_INVALID_ARG";
     case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED";
     case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE";
+    case PKV_ERR_ALIASED_APPEND: return "PKV_ERR_ALIASED_APPEND";
     case PKV_ERR_HIP: return "PKV_ERR_HIP";
     case PKV_ERR_OUT_OF_BLOCKS: return "PKV_ERR_OUT_OF_BLOCKS";
     case PKV_ERR_SEQUENCE: return "PKV_ERR_SEQUENCE";
@@ -504,6 +509,8 @@ int pkv_kv_append(int dtype, const void* k_new, const void* v_new, int64_t new_r
     a.D = D;
     a.elem_bytes = eb;
     a.n_blocks = n_blocks;
+    if ((st = pkv::debug_check_appends(block_tables, bt_stride, positions, B, block_size, n_blocks, 0, stream)))
+        return st;
     hipError_t e = pkv::launch_kv_append(a, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "kv_append launch: %s", hipGetErrorString(e));
     g_err[0] = 0;
@@ -548,6 +555,8 @@ int pkv_kv_append_fp8(int src_dtype, const void* k_new, const void* v_new, int64
     a.B = B;
     a.H_kv = H_kv;
     a.n_blocks = n_blocks;
+    if (int dc = pkv::debug_check_appends(block_tables, bt_stride, positions, B, block_size, n_blocks, 0, stream))
+        return dc;
     hipError_t e = pkv::launch_kv_append_fp8(src_dtype, D, a, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "kv_append_fp8 launch: %s", hipGetErrorString(e));
     pkv::clear_error();
@@ -617,6 +626,8 @@ int pkv_kv_append_mxfp4(int src_dtype, const void* k_new, const void* v_new, int
     a.B = B;
     a.H_kv = H_kv;
     a.n_blocks = n_blocks;
+    if (int dc = pkv::debug_check_appends(block_tables, bt_stride, positions, B, block_size, n_blocks, 0, stream))
+        return dc;
     hipError_t e = pkv::launch_kv_append_mxfp4(src_dtype, D, a, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "kv_append_mxfp4 launch: %s", hipGetErrorString(e));
     pkv::clear_error();

@@ -77,9 +77,10 @@ def attn(lib, dtype=1, out=FAKE, q=FAKE, qrs=32 * 128, kp=FAKE, vp=FAKE, bt=FAKE
     (dict(qrs=32 * 128 + 4), E_ARG),                # row stride not a multiple of 16 bytes
     (dict(scale=float("inf")), E_ARG),
     (dict(H_q=64, H_kv=2, dtype=2, qrs=64 * 128), E_UNSUP),   # G = 32 on the grouped path
-    (dict(P=256), E_WS),                            # split without workspace
-    (dict(P=256, ws=FAKE, wsb=100), E_WS),          # too small
-    (dict(P=256, ws=FAKE + 16, wsb=1 << 30), E_WS), # misaligned workspace
+    # a context of 4096 tokens split every 256 spans two 8-wave workgroups: partials needed
+    (dict(P=256, maxc=4096, bts=256), E_WS),                            # split without workspace
+    (dict(P=256, maxc=4096, bts=256, ws=FAKE, wsb=100), E_WS),          # too small
+    (dict(P=256, maxc=4096, bts=256, ws=FAKE + 16, wsb=1 << 30), E_WS), # misaligned workspace
     (dict(B=0), OK),                                # nothing to do, nothing launched
     (dict(B=0, q=None, out=None), OK),
 ])
@@ -364,3 +365,25 @@ def test_fp8_entry_point_validation(lib):
     assert append({3: 100}) == E_ARG               # row stride below H_kv * D
     assert append({11: 0}) == OK
     assert lib.pkv_status_string(E_UNSUP) == b"PKV_ERR_UNSUPPORTED"
+
+
+def test_status_codes_of_the_contract(lib):
+    """The boundary's status values: aliased appends -5, HIP errors -6, then the block manager's."""
+    names = {-5: b"PKV_ERR_ALIASED_APPEND", -6: b"PKV_ERR_HIP", -7: b"PKV_ERR_OUT_OF_BLOCKS", -8: b"PKV_ERR_SEQUENCE"}
+    for code, name in names.items():
+        assert lib.pkv_status_string(code) == name
+    assert (pkv.PKV_ERR_ALIASED_APPEND, pkv.PKV_ERR_HIP, pkv.PKV_ERR_OUT_OF_BLOCKS, pkv.PKV_ERR_SEQUENCE) == (-5, -6, -7, -8)
+
+
+def test_check_step_metadata_host_validation(lib):
+    """Argument errors are reported before anything touches the GPU."""
+    E_ARG = -2
+    # exactly one of context_lens and positions
+    assert lib.pkv_check_step_metadata(FAKE, 4, None, None, 2, 16, 8, 0, None) == E_ARG
+    assert lib.pkv_check_step_metadata(FAKE, 4, FAKE, FAKE, 2, 16, 8, 0, None) == E_ARG
+    assert b"exactly one" in lib.pkv_last_error()
+    for bt_stride, bs, nb, mx, B in ((0, 16, 8, 0, 2), (4, 0, 8, 0, 2), (4, 16, 0, 0, 2), (4, 16, 8, -1, 2),
+                                     (4, 16, 8, 0, -1)):
+        assert lib.pkv_check_step_metadata(FAKE, bt_stride, None, FAKE, B, bs, nb, mx, None) == E_ARG
+    assert lib.pkv_check_step_metadata(None, 4, None, FAKE, 2, 16, 8, 0, None) == -1     # PKV_ERR_NULL
+    assert lib.pkv_check_step_metadata(FAKE, 4, None, FAKE, 0, 16, 8, 0, None) == 0      # B = 0: nothing to check

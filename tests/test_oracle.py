@@ -452,3 +452,55 @@ def test_planted_mistakes_are_caught(oracle_lib):
             assert not _pin_suite(so), f"planted mistake '{name}' was not caught"
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
+
+
+# ---------------------------------------------------------------------------
+# Appends of one step write distinct slots ("从 PagedAttention 到 Prefill-Decode
+# 分离的深度解析", section 2.2, step three: each new token is given its own slot)
+# ---------------------------------------------------------------------------
+
+def _two_appends(dtype, same_slot):
+    """Two requests whose tables share physical block 3: positions 5 and 5 (the same
+    slot) or 5 and 6 (neighbouring slots of the shared block)."""
+    H_kv, D, nb = 2, 64, 6
+    rng = np.random.default_rng(5)
+    k_new = to_storage(rng.standard_normal((2, H_kv, D)), dtype)
+    v_new = to_storage(rng.standard_normal((2, H_kv, D)), dtype)
+    bt = np.array([[3, 1], [3, 0]], np.int32)
+    pos = np.array([5, 5 if same_slot else 6], np.int32)
+    return k_new, v_new, bt, pos, nb, H_kv, D
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_aliased_append_is_rejected_and_writes_nothing(oracle_lib, dtype):
+    k_new, v_new, bt, pos, nb, H_kv, D = _two_appends(dtype, True)
+    sdt = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[dtype]
+    kp = np.zeros((nb, H_kv, 16, D), sdt)
+    vp = np.zeros((nb, H_kv, 16, D), sdt)
+    with pytest.raises(oracle.OracleError):
+        oracle.kv_append(dtype, k_new, v_new, kp, vp, bt, pos, 16)
+    assert not kp.view(np.uint8).any() and not vp.view(np.uint8).any()
+    # neighbouring slots of one shared block are two distinct targets
+    k_new, v_new, bt, pos, nb, H_kv, D = _two_appends(dtype, False)
+    oracle.kv_append(dtype, k_new, v_new, kp, vp, bt, pos, 16)
+    assert np.array_equal(kp[3, :, 5].view(np.uint8), k_new[0].view(np.uint8))
+    assert np.array_equal(kp[3, :, 6].view(np.uint8), k_new[1].view(np.uint8))
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_aliased_quantizing_append_is_rejected(oracle_lib, fmt):
+    k_new, v_new, bt, pos, nb, H_kv, D = _two_appends("bf16", True)
+    if fmt == "fp8":
+        kp = np.full((nb, H_kv, 16, D), 0x7F, np.uint8)
+        ks = np.full((nb, H_kv, 16), np.nan, np.float32)
+        fn = oracle.kv_append_fp8
+    else:
+        kp = np.full((nb, H_kv, 16, D // 2), 0x77, np.uint8)
+        ks = np.full((nb, H_kv, 16, D // 32), 0xFF, np.uint8)
+        fn = oracle.kv_append_mxfp4
+    vp, vs = kp.copy(), ks.copy()
+    before = [a.copy() for a in (kp, vp, ks, vs)]
+    with pytest.raises(oracle.OracleError):
+        fn("bf16", k_new, v_new, kp, vp, ks, vs, bt, pos, 16)
+    for a, b in zip((kp, vp, ks, vs), before):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
