@@ -327,11 +327,12 @@ __device__ __forceinline__ void mha_unit(const AttnArgs& a, const int unit) {
         a.part_lse[(size_t)bh * a.n_parts + part] = bad ? __builtin_nanf("") : M + __builtin_amdgcn_logf(L);
 }
 
-// Two chunks of two blocks (or four of one) in flight need about 190 VGPRs; left
-// unbounded the compiler takes all 256 of a lone wave plus one AGPR, and the
-// kernel runs at one wave per SIMD.  Those variants are held to two.
+// Two chunks of two blocks in flight need about 190 VGPRs; left unbounded the
+// compiler takes all 256 of a lone wave plus one AGPR, and the kernel runs at one
+// wave per SIMD.  That variant is held to two (four chunks of one block would
+// spill there, so they keep the whole register file).
 template <int DT, int D, int NW, int CH, int PF, bool APPEND>
-__global__ __launch_bounds__(NW * 64, CH * PF == 4 ? 2 : 1) void decode_mha_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(NW * 64, CH == 2 && PF == 2 ? 2 : 1) void decode_mha_kernel(const AttnArgs a) {
     mha_unit<DT, D, NW, CH, PF, APPEND>(a, blockIdx.x);
 }
 
