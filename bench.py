@@ -343,8 +343,25 @@ def cufrac_bench(args, torch, pkv, dev, lib) -> int:
         if rc:
             raise RuntimeError(f"step failed: {lib.pkv_status_string(rc).decode()}: {lib.pkv_last_error().decode()}")
 
+    gemm = args.neighbour == "gemm"
+    GM = GN = GK = 8192                        # the GEMM neighbour: 2 x 8192^3 flops per launch
+    if gemm:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(11)
+        ga = (torch.rand((GM, GK), generator=gen, device=dev) - 0.5).to(torch.bfloat16)
+        gb = (torch.rand((GN, GK), generator=gen, device=dev) - 0.5).to(torch.bfloat16)
+        gc = torch.empty((GM, GN), dtype=torch.float32, device=dev)
+
     def burn(n_wg, iters, stream):
-        rc = lib.pkv_probe_mfma_burn(n_wg, iters, P_(sink.data_ptr()), P_(stream.cuda_stream))
+        """The neighbour on n_wg CUs: `iters` GEMM launches, or an MFMA chain of `iters` rounds."""
+        if gemm:
+            for _ in range(iters):
+                rc = lib.pkv_probe_gemm_bf16(n_wg, P_(ga.data_ptr()), P_(gb.data_ptr()), P_(gc.data_ptr()), GM, GN, GK,
+                                             P_(stream.cuda_stream))
+                if rc:
+                    break
+        else:
+            rc = lib.pkv_probe_mfma_burn(n_wg, iters, P_(sink.data_ptr()), P_(stream.cuda_stream))
         if rc:
             raise RuntimeError(f"burn failed: {lib.pkv_status_string(rc).decode()}: {lib.pkv_last_error().decode()}")
 
@@ -361,10 +378,10 @@ def cufrac_bench(args, torch, pkv, dev, lib) -> int:
         return e0.elapsed_time(e1) * 1e-3 / K
 
     def burn_flops(n_wg, iters):
-        return n_wg * 16.0 * iters * 8 * 16384
+        return iters * 2.0 * GM * GN * GK if gemm else n_wg * 16.0 * iters * 8 * 16384
 
     def time_burn(n_wg, iters):
-        burn(n_wg, max(1, iters // 10), sg)
+        burn(n_wg, 1 if gemm else max(1, iters // 10), sg)
         torch.cuda.synchronize()
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         g0.record(sg)
@@ -390,13 +407,14 @@ def cufrac_bench(args, torch, pkv, dev, lib) -> int:
     # so an uneven neighbour grid leaves some engines one free CU short and a step
     # workgroup waits for one (a 204-CU neighbour cut the 52-CU step to the 32-CU rate)
     corun = []
-    iters0 = 20000
+    iters0 = 2 if gemm else 20000
     for n in (32, 64, 96, 128, 192):
         if n >= n_cus:
             continue
         ta = time_steps(n)
         tb = time_burn(n_cus - n, iters0)
-        iters = max(1000, int(iters0 * (K * ta * 1.3) / tb))   # the neighbour outlasts the K steps
+        # the neighbour outlasts the K steps
+        iters = max(2 if gemm else 1000, math.ceil(iters0 * (K * ta * 1.3) / tb))
         tb_alone = time_burn(n_cus - n, iters)
         for k in range(R):
             step(k, n, sa)
@@ -426,7 +444,10 @@ def cufrac_bench(args, torch, pkv, dev, lib) -> int:
                    "algorithmic_bytes_per_step": int(bytes_per_step), "input_rotation_sets": R,
                    "steps_per_point": K, "n_cus": n_cus},
         "full_step_default_launch_GBps": round(bytes_per_step / t_full / 1e9, 1),
-        "sweep": sweep, "corun_mfma_neighbour": corun,
+        "sweep": sweep, ("corun_gemm_neighbour" if gemm else "corun_mfma_neighbour"): corun,
+        "neighbour": ("bf16 GEMM c[8192][8192] = a[8192][8192] b_t[8192][8192]^T streaming its operands through "
+                      "LDS (pkv_probe_gemm_bf16), one 8-wave workgroup per CU" if gemm else
+                      "bf16 MFMA chains on register operands (pkv_probe_mfma_burn), touching no memory"),
         "note": "share bounded by occupancy (one 16-wave workgroup per CU), not by a CU-masked queue"}))
     return 0
 
@@ -621,6 +642,10 @@ def main(argv=None):
                     help="step: the headline step over resident inputs; loop: a block-manager-driven decode loop")
     ap.add_argument("--graphs", action="store_true", help="loop mode: replay captured step graphs")
     ap.add_argument("--native", action="store_true", help="loop mode: one pkv_decoder_step call per step")
+    ap.add_argument("--neighbour", default="gemm", choices=["gemm", "mfma"],
+                    help="cufrac mode: the work on the other CUs (an HBM-streaming GEMM or MFMA chains)")
+    ap.add_argument("--gemm-only", type=int, default=0, metavar="N_WG",
+                    help="only run the GEMM neighbour 3 times on N_WG workgroups (for its counter runs)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -651,6 +676,15 @@ def main(argv=None):
         print(json.dumps({"copy_calibration_bytes": n, "dispatches": 5}))
         return 0
     lib = pkv.load_library()
+    if args.gemm_only:
+        g = 8192
+        ga = torch.zeros((g, g), dtype=torch.bfloat16, device=dev)
+        gc = torch.empty((g, g), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            pkv.probe_gemm_bf16(ga, ga, gc, args.gemm_only)
+        torch.cuda.synchronize()
+        print(json.dumps({"gemm_only": args.gemm_only, "M": g, "N": g, "K": g, "dispatches": 3}))
+        return 0
     if args.mode == "loop":
         return loop_bench(args, torch, pkv, dev)
     if args.mode == "cufrac":

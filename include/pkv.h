@@ -329,6 +329,21 @@ int pkv_probe_stream_read(const void* buf, size_t bytes, void* sink, int32_t gri
 int pkv_probe_mfma_burn(int32_t n_workgroups, int32_t iterations, void* sink, void* stream);
 
 /*
+ * probe_gemm_bf16 -- measurement aid, not part of the decode step: a neighbour
+ * that streams its operands from HBM, standing in for the prefill GEMMs that
+ * share the GPU with decode attention ("Injecting Adrenaline into LLM Serving"
+ * review, section 3.3.1).  c[M][N] = a[M][K] . b_t[N][K]^T in bf16 with float32
+ * accumulation on the matrix cores; `n_workgroups` persistent workgroups of 8
+ * waves walk the 256 x 256 output tiles round-robin, each workgroup holding
+ * 128 KiB of LDS and most of its CU's registers, so that the grid occupies
+ * n_workgroups CUs and nothing of the persistent decode step fits beside it.
+ * 2 M N K flops.  M, N multiples of 256, K a multiple of 64, all 16-byte aligned;
+ * n_workgroups in [1, 65536].
+ */
+int pkv_probe_gemm_bf16(int32_t n_workgroups, const void* a, const void* b_t, float* c,
+                        int32_t M, int32_t N, int32_t K, void* stream);
+
+/*
  * ---------------------------------------------------------------------------
  * FP8 K/V cache
  * ---------------------------------------------------------------------------

@@ -47,7 +47,7 @@ EXPORTED_SYMBOLS = (
     "pkv_version", "pkv_status_string", "pkv_last_error", "pkv_last_launch", "pkv_kv_append",
     "pkv_decode_workspace_bytes", "pkv_paged_decode_attention", "pkv_append_decode_attention",
     "pkv_append_decode_attention_persistent", "pkv_append_decode_attention_noalloc", "pkv_check_step_metadata",
-    "pkv_probe_mfma_burn",
+    "pkv_probe_mfma_burn", "pkv_probe_gemm_bf16",
     "pkv_probe_stream_read", "pkv_copy_blocks", "pkv_copy_blocks_fp8", "pkv_kv_append_fp8", "pkv_paged_decode_attention_fp8",
     "pkv_append_decode_attention_fp8", "pkv_kv_append_mxfp4", "pkv_paged_decode_attention_mxfp4",
     "pkv_append_decode_attention_mxfp4", "pkv_copy_blocks_mxfp4",
@@ -143,6 +143,8 @@ def load_library(path: Optional[str] = None):
     lib.pkv_append_decode_attention_persistent.restype = ctypes.c_int
     lib.pkv_probe_mfma_burn.argtypes = [I32, I32, P, P]
     lib.pkv_probe_mfma_burn.restype = ctypes.c_int
+    lib.pkv_probe_gemm_bf16.argtypes = [I32, P, P, P, I32, I32, I32, P]
+    lib.pkv_probe_gemm_bf16.restype = ctypes.c_int
     lib.pkv_probe_stream_read.argtypes = [P, SZ, P, I32, P]
     lib.pkv_probe_stream_read.restype = ctypes.c_int
     lib.pkv_kv_append_fp8.argtypes = [ctypes.c_int, P, P, I64, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, P]
@@ -246,6 +248,19 @@ def probe_stream_read(buf, sink, grid: int = 16384, *, nbytes: Optional[int] = N
     _require(0 <= nbytes <= total, "nbytes exceeds the buffer")
     _check(load_library().pkv_probe_stream_read(_ptr(buf), nbytes, _ptr(sink), int(grid), _stream(stream)),
            "probe_stream_read")
+
+
+def probe_gemm_bf16(a, b_t, c, n_workgroups: int, *, stream=None):
+    """Launch the GEMM neighbour: c[M][N] (float32) = a[M][K] . b_t[N][K]^T (bf16) on n_workgroups CUs."""
+    torch = _torch()
+    M, K = a.shape
+    N = b_t.shape[0]
+    _require(a.dtype == torch.bfloat16 and b_t.dtype == torch.bfloat16 and c.dtype == torch.float32,
+             "a, b_t bf16 and c float32")
+    _require(a.is_contiguous() and b_t.is_contiguous() and c.is_contiguous(), "contiguous operands")
+    _require(tuple(b_t.shape) == (N, K) and tuple(c.shape) == (M, N), "shapes a [M][K], b_t [N][K], c [M][N]")
+    _check(load_library().pkv_probe_gemm_bf16(int(n_workgroups), _ptr(a), _ptr(b_t), _ptr(c), M, N, K,
+                                              _stream(stream)), "probe_gemm_bf16")
 
 
 def decode_workspace_bytes(B: int, H_q: int, D: int, max_context_len: int, partition_size: int) -> int:

@@ -675,6 +675,24 @@ int pkv_probe_mfma_burn(int32_t n_workgroups, int32_t iterations, void* sink, vo
     return PKV_OK;
 }
 
+int pkv_probe_gemm_bf16(int32_t n_workgroups, const void* a, const void* b_t, float* c, int32_t M, int32_t N,
+                        int32_t K, void* stream) {
+    if (!a || !b_t || !c) return fail(PKV_ERR_NULL, "a, b_t and c must not be NULL");
+    if (!aligned16(a) || !aligned16(b_t) || !aligned16(c))
+        return fail(PKV_ERR_INVALID_ARG, "a, b_t and c must be 16-byte aligned");
+    if (M < 256 || N < 256 || K < 64 || M % 256 || N % 256 || K % 64)
+        return fail(PKV_ERR_INVALID_ARG, "M = %d, N = %d (multiples of 256), K = %d (a multiple of 64)", M, N, K);
+    if ((int64_t)(M / 256) * (N / 256) > 0x7fffffff || (int64_t)M * K > (1ll << 40) || (int64_t)N * K > (1ll << 40))
+        return fail(PKV_ERR_INVALID_ARG, "problem too large");
+    if (n_workgroups < 1 || n_workgroups > 65536)
+        return fail(PKV_ERR_INVALID_ARG, "n_workgroups = %d is outside [1, 65536]", n_workgroups);
+    pkv::GemmArgs g{reinterpret_cast<const char*>(a), reinterpret_cast<const char*>(b_t), c, M, N, K};
+    hipError_t e = pkv::launch_gemm_nt_bf16(n_workgroups, g, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "probe launch: %s", hipGetErrorString(e));
+    g_err[0] = 0;
+    return PKV_OK;
+}
+
 int pkv_probe_stream_read(const void* buf, size_t bytes, void* sink, int32_t grid, void* stream) {
     if (!buf || !sink) return fail(PKV_ERR_NULL, "buf and sink must not be NULL");
     if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(sink) & 3u))

@@ -107,6 +107,13 @@ hipError_t launch_lse_merge(int D, const MergeArgs& a, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, size_t bytes, unsigned* sink, int grid, hipStream_t stream);
 // `grid` 16-wave workgroups, one per CU, each running bf16 MFMA chains for `iterations` rounds
 hipError_t launch_mfma_burn(int grid, int iterations, unsigned* sink, hipStream_t stream);
+struct GemmArgs {
+    const char* a;   // [M][K] bf16
+    const char* b;   // [N][K] bf16 (B transposed)
+    float* c;        // [M][N]
+    int32_t M, N, K;
+};
+hipError_t launch_gemm_nt_bf16(int grid, const GemmArgs& g, hipStream_t stream);
 bool mha_variant_exists(int nw, int ch, int pf);
 bool gqa_variant_exists(int kind, int nw, int ch, int pf);
 

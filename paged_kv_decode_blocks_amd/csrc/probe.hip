@@ -74,4 +74,110 @@ hipError_t launch_mfma_burn(int grid, int iterations, unsigned* sink, hipStream_
     return hipGetLastError();
 }
 
+// A neighbour that streams from HBM: C = A B^T in bf16 with float32 accumulation
+// on MFMA, A [M][K] and B [N][K] row-major, C [M][N] float32, standing in for the
+// prefill-sized GEMMs that share the GPU with decode attention.  Persistent: the
+// grid's workgroups walk the 256 x 256 output tiles round-robin.  A workgroup is
+// 8 waves of about 230 registers (accumulators in AGPRs) with 128 KiB of LDS: one
+// per CU, and no workgroup of the persistent decode step fits beside it, so a grid
+// of n workgroups occupies n CUs.  Per 64-wide K step the two 256 x 64 operand
+// tiles go global -> registers -> LDS (16-byte chunks XOR-swizzled by row, so the
+// MFMA-layout reads of 16 rows spread over the banks), double-buffered: the next
+// step's loads are in flight while the current step's 32 MFMAs per wave run.
+constexpr int kGemmTile = 256;
+constexpr int kGemmK = 64;
+
+typedef __bf16 bf16x8_gemm_t __attribute__((ext_vector_type(8)));
+
+__global__ __launch_bounds__(512) void gemm_nt_bf16_kernel(const GemmArgs g) {
+    __shared__ uint4 s_a[2][kGemmTile * 8];   // [row][8 chunks of 8 bf16]
+    __shared__ uint4 s_b[2][kGemmTile * 8];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1;        // 4 x 2 waves, each 64 rows x 128 columns of the tile
+    const int tiles_n = g.N / kGemmTile;
+    const int n_tiles = (g.M / kGemmTile) * tiles_n;
+    const int nk = g.K / kGemmK;
+    uint4 ra[4], rb[4];
+    for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+        const int tm = tile / tiles_n, tn = tile - (tile / tiles_n) * tiles_n;
+        const char* A = g.a + (size_t)tm * kGemmTile * g.K * 2;
+        const char* Bt = g.b + (size_t)tn * kGemmTile * g.K * 2;
+        // thread t moves chunks t + 512 j (j < 4) of each 256 x 64 tile: row q / 8, chunk q % 8
+        auto gload = [&](int kt) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int q = tid + 512 * j;
+                const size_t off = ((size_t)(q >> 3) * g.K + (size_t)kt * kGemmK + (q & 7) * 8) * 2;
+                ra[j] = ld16(A + off);
+                rb[j] = ld16(Bt + off);
+            }
+        };
+        auto lstore = [&](int buf) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int q = tid + 512 * j;
+                const int row = q >> 3;
+                s_a[buf][row * 8 + ((q & 7) ^ (row & 7))] = ra[j];
+                s_b[buf][row * 8 + ((q & 7) ^ (row & 7))] = rb[j];
+            }
+        };
+        floatx4 acc[4][8];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 8; ++ni) acc[mi][ni] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        __syncthreads();   // the previous tile's last LDS reads are done
+        gload(0);
+        lstore(0);
+        __syncthreads();
+        for (int kt = 0; kt < nk; ++kt) {
+            const int buf = kt & 1;
+            if (kt + 1 < nk) gload(kt + 1);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                // MFMA operands: lane l holds row l % 16 of a 16-row block, k = 8 (l / 16) .. + 7 of the step
+                const int c = ks * 4 + (lane >> 4);
+                uint4 fa[4], fb[8];
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi) {
+                    const int row = wm * 64 + mi * 16 + (lane & 15);
+                    fa[mi] = s_a[buf][row * 8 + (c ^ (row & 7))];
+                }
+#pragma unroll
+                for (int ni = 0; ni < 8; ++ni) {
+                    const int row = wn * 128 + ni * 16 + (lane & 15);
+                    fb[ni] = s_b[buf][row * 8 + (c ^ (row & 7))];
+                }
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < 8; ++ni)
+                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_gemm_t, fa[mi]), __builtin_bit_cast(bf16x8_gemm_t, fb[ni]),
+                            acc[mi][ni], 0, 0, 0);
+            }
+            if (kt + 1 < nk) lstore(buf ^ 1);   // read in step kt - 1, released by its closing barrier
+            __syncthreads();
+        }
+        // output tile (16 x 16 per MFMA): lane l holds column l % 16, rows 4 (l / 16) + i
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 8; ++ni)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const size_t row = (size_t)tm * kGemmTile + wm * 64 + mi * 16 + 4 * (lane >> 4) + i;
+                    const size_t col = (size_t)tn * kGemmTile + wn * 128 + ni * 16 + (lane & 15);
+                    g.c[row * g.N + col] = acc[mi][ni][i];
+                }
+    }
+}
+
+hipError_t launch_gemm_nt_bf16(int grid, const GemmArgs& g, hipStream_t stream) {
+    hipLaunchKernelGGL(gemm_nt_bf16_kernel, dim3(grid), dim3(512), 0, stream, g);
+    return hipGetLastError();
+}
+
 }  // namespace pkv

@@ -93,3 +93,77 @@ def test_persistent_step_beside_mfma_neighbour(torch_dev):
     assert_close(out.cpu().numpy(), ref, "bf16", f"persistent beside neighbour [{pkv.last_launch()}]")
     assert np.array_equal(to_numpy_bits(t["k_pool"], "bf16").view(np.uint8), kp_ref.view(np.uint8))
     assert np.array_equal(to_numpy_bits(t["v_pool"], "bf16").view(np.uint8), vp_ref.view(np.uint8))
+
+
+def _gemm_bound(a, b_t):
+    """|g - r| bound for a float32 accumulation of K bf16 products (exact in float32):
+    K * 2^-24 * sum_k |a_ik b_jk| per element, plus the float32 rounding of r itself."""
+    A, Bt = np.abs(a.astype(np.float64)), np.abs(b_t.astype(np.float64))
+    return a.shape[1] * 2.0 ** -24 * (A @ Bt.T) + 1e-30
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 64), (512, 768, 320), (768, 256, 1024)])
+def test_gemm_neighbour_matches_torch(torch_dev, M, N, K):
+    """The HBM-streaming GEMM neighbour against a plain PyTorch reference on the CPU, on 1, 3
+    and more workgroups than tiles."""
+    torch = torch_dev
+    g = torch.Generator().manual_seed(M + N + K)
+    a = (torch.rand((M, K), generator=g) * 2 - 1).to(torch.bfloat16)
+    b_t = (torch.rand((N, K), generator=g) * 2 - 1).to(torch.bfloat16)
+    ref = (a.double() @ b_t.double().T).numpy()                  # bf16 values are exact in float64
+    bound = _gemm_bound(a.float().numpy(), b_t.float().numpy())
+    da, db = a.cuda(), b_t.cuda()
+    for n_wg in (1, 3, 64):
+        c = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        pkv.probe_gemm_bf16(da, db, c, n_wg)
+        torch.cuda.synchronize()
+        got = c.cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(got)), n_wg
+        err = np.abs(got - ref)
+        assert np.all(err <= bound), f"n_wg={n_wg}: max err {err.max():.3e}, worst ratio {(err / bound).max():.3f}"
+
+
+def test_gemm_neighbour_refuses_bad_shapes(torch_dev):
+    torch = torch_dev
+    a = torch.zeros((256, 64), dtype=torch.bfloat16, device="cuda")
+    c = torch.zeros((256, 256), dtype=torch.float32, device="cuda")
+    lib = pkv.load_library()
+    import ctypes
+    V = ctypes.c_void_p
+    for M, N, K in ((250, 256, 64), (256, 100, 64), (256, 256, 48), (256, 256, 0)):
+        assert lib.pkv_probe_gemm_bf16(4, V(a.data_ptr()), V(a.data_ptr()), V(c.data_ptr()), M, N, K, None) == -2
+    assert lib.pkv_probe_gemm_bf16(0, V(a.data_ptr()), V(a.data_ptr()), V(c.data_ptr()), 256, 256, 64, None) == -2
+
+
+def test_persistent_step_beside_gemm_neighbour(torch_dev):
+    """The step on 8 CUs while the GEMM neighbour streams its operands on all the others:
+    both results hold (the step against the oracle, sampled GEMM rows against float64)."""
+    torch = torch_dev
+    lib = pkv.load_library()
+    lens = (1, 17, 100, 257, 1000, 2049)
+    cfg = get_config("c3", B=len(lens), H_q=8, H_kv=8, dtype="bf16", lengths=("fixed", lens), append=True)
+    w = make_workload(cfg, seed=72)
+    ref, kp_ref, vp_ref = oracle.run_step(w)
+    n_cus = lib.pkv_device_cu_count()
+    M = N = K = 2048
+    g = torch.Generator().manual_seed(9)
+    a = (torch.rand((M, K), generator=g) * 2 - 1).to(torch.bfloat16)
+    b_t = (torch.rand((N, K), generator=g) * 2 - 1).to(torch.bfloat16)
+    da, db = a.cuda(), b_t.cuda()
+    c = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    sg, sa = torch.cuda.Stream(), torch.cuda.Stream()
+    t = upload(w)
+    torch.cuda.synchronize()
+    pkv.probe_gemm_bf16(da, db, c, n_cus - 8, stream=sg)
+    with torch.cuda.stream(sa):
+        out = pkv.append_decode_attention_persistent(t["q"], t["k_new"], t["v_new"], t["k_pool"], t["v_pool"],
+                                                     t["block_tables"], t["positions"], float(w.scale), max(lens), 8,
+                                                     stream=sa)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), ref, "bf16", f"persistent beside the GEMM [{pkv.last_launch()}]")
+    assert np.array_equal(to_numpy_bits(t["k_pool"], "bf16").view(np.uint8), kp_ref.view(np.uint8))
+    assert np.array_equal(to_numpy_bits(t["v_pool"], "bf16").view(np.uint8), vp_ref.view(np.uint8))
+    rows = np.random.default_rng(1).choice(M, 6, replace=False)
+    got = c.cpu().numpy()[rows].astype(np.float64)
+    want = (a[rows].double() @ b_t.double().T).numpy()
+    assert np.all(np.abs(got - want) <= _gemm_bound(a[rows].float().numpy(), b_t.float().numpy()))
