@@ -682,6 +682,40 @@ int pkv_step_graphs_launch(pkv_step_graphs* g, int32_t B, int32_t max_context_le
 void pkv_step_graphs_destroy(pkv_step_graphs* g);
 
 /*
+ * Dual step graphs: a local and an offloaded attention batch in one step.  The
+ * Adrenaline review (section 3.2.1) runs the decode instance's own attention
+ * and the attention it offloaded at the same time, and (section 3.2.2) captures
+ * graphs bucketed over both batch sizes.  A pkv_dual_step_graphs object takes two
+ * step descriptions (each with its own q/new rows/pools/tables/positions/out and,
+ * when split, its own workspace; no copy buffers) and captures, for every pair
+ * (local capacity Lc, offloaded capacity Oc) of the lists, one graph running
+ *     the local step with B = Lc and the offloaded step with B = Oc,
+ * both with max_context_len = ctx_cap: as two parallel branches (parallel != 0)
+ * or one after the other (parallel == 0, to measure what the overlap buys).  A
+ * capacity of 0 (allowed as the first entry of a list) leaves that branch out.
+ * pkv_dual_step_graphs_launch(B_local, B_off) replays the smallest fitting pair
+ * (nothing, if both are 0); padding rows as for pkv_step_graphs.  Buffers stay
+ * allocated for the object's lifetime; launch is asynchronous and
+ * allocation-free; not thread-safe per object.
+ */
+typedef struct pkv_dual_step_graphs pkv_dual_step_graphs;
+
+/* Capture n_local x n_off graphs (capacity lists >= 0 and strictly increasing,
+ * ctx_cap <= bt_stride * block_size of both).  NULL on an invalid description or
+ * a HIP error (detail in pkv_last_error()). */
+pkv_dual_step_graphs* pkv_dual_step_graphs_create(const pkv_step_desc* local, const pkv_step_desc* offloaded,
+                                                  const int32_t* local_caps, int32_t n_local,
+                                                  const int32_t* off_caps, int32_t n_off, int32_t ctx_cap,
+                                                  int parallel);
+
+/* Replay the smallest fitting graph on `stream`.  PKV_ERR_INVALID_ARG if a batch
+ * exceeds its largest capacity (nothing launched). */
+int pkv_dual_step_graphs_launch(pkv_dual_step_graphs* g, int32_t B_local, int32_t B_off, void* stream);
+
+/* Frees the graphs (NULL is allowed).  Work already launched is not waited for. */
+void pkv_dual_step_graphs_destroy(pkv_dual_step_graphs* g);
+
+/*
  * ---------------------------------------------------------------------------
  * Decoder: the decode loop's per-step host work in one call
  * ---------------------------------------------------------------------------

@@ -28,7 +28,7 @@ from typing import Optional
 __all__ = [
     "PkvError", "LIB_PATH", "load_library", "library_loaded", "kv_append", "paged_decode_attention",
     "append_decode_attention", "decode_workspace_bytes", "last_launch", "version", "probe_stream_read",
-    "PKV_F32", "PKV_F16", "PKV_BF16", "EXPORTED_SYMBOLS", "copy_blocks", "BlockManager", "StepGraphs", "Decoder", "cu_mask", "CuMaskedStream",
+    "PKV_F32", "PKV_F16", "PKV_BF16", "EXPORTED_SYMBOLS", "copy_blocks", "BlockManager", "StepGraphs", "DualStepGraphs", "Decoder", "cu_mask", "CuMaskedStream",
     "kv_append_fp8", "paged_decode_attention_fp8", "append_decode_attention_fp8", "copy_blocks_fp8",
     "device_cu_count", "append_decode_attention_persistent", "append_decode_attention_noalloc",
     "NOALLOC_SCRATCH_BYTES",
@@ -47,7 +47,8 @@ EXPORTED_SYMBOLS = (
     "pkv_version", "pkv_status_string", "pkv_last_error", "pkv_last_launch", "pkv_kv_append",
     "pkv_decode_workspace_bytes", "pkv_paged_decode_attention", "pkv_append_decode_attention",
     "pkv_append_decode_attention_persistent", "pkv_append_decode_attention_noalloc", "pkv_check_step_metadata",
-    "pkv_probe_mfma_burn", "pkv_probe_gemm_bf16",
+    "pkv_probe_mfma_burn", "pkv_probe_gemm_bf16", "pkv_dual_step_graphs_create", "pkv_dual_step_graphs_launch",
+    "pkv_dual_step_graphs_destroy",
     "pkv_probe_stream_read", "pkv_copy_blocks", "pkv_copy_blocks_fp8", "pkv_kv_append_fp8", "pkv_paged_decode_attention_fp8",
     "pkv_append_decode_attention_fp8", "pkv_kv_append_mxfp4", "pkv_paged_decode_attention_mxfp4",
     "pkv_append_decode_attention_mxfp4", "pkv_copy_blocks_mxfp4",
@@ -201,6 +202,13 @@ def load_library(path: Optional[str] = None):
     lib.pkv_step_graphs_launch.restype = C
     lib.pkv_step_graphs_destroy.argtypes = [P]
     lib.pkv_step_graphs_destroy.restype = None
+    lib.pkv_dual_step_graphs_create.argtypes = [ctypes.POINTER(StepDesc), ctypes.POINTER(StepDesc), P, I32, P, I32,
+                                                I32, ctypes.c_int]
+    lib.pkv_dual_step_graphs_create.restype = P
+    lib.pkv_dual_step_graphs_launch.argtypes = [P, I32, I32, P]
+    lib.pkv_dual_step_graphs_launch.restype = ctypes.c_int
+    lib.pkv_dual_step_graphs_destroy.argtypes = [P]
+    lib.pkv_dual_step_graphs_destroy.restype = None
     lib.pkv_decoder_create.argtypes = [ctypes.POINTER(DecoderDesc)]
     lib.pkv_decoder_create.restype = P
     lib.pkv_decoder_destroy.argtypes = [P]
@@ -626,6 +634,59 @@ def _np_ptr(a):
 # Step graphs (device tensors held for the object's lifetime)
 # ---------------------------------------------------------------------------
 
+def _step_desc(q, k_new, v_new, k_pool, v_pool, block_tables, positions, out, scale, max_batch, max_ctx,
+               partition_size, cow_src, cow_dst, workspace, k_scale, v_scale):
+    """A ``StepDesc`` over torch buffers sized for max_batch rows (checked), and the tensors it points into."""
+    torch = _torch()
+    lowp = k_scale is not None                  # FP8 (float32 scales) or MXFP4 (uint8 scales)
+    mx4 = lowp and k_scale.dtype == torch.uint8
+    fp8 = lowp and not mx4
+    n_blocks, H_kv, bs, D = (_mx4_pools(k_pool, v_pool, k_scale, v_scale) if mx4
+                             else _fp8_pools(k_pool, v_pool, k_scale, v_scale) if fp8
+                             else _pool_dims(k_pool, v_pool))
+    Bmax, H_q = q.shape[0], q.shape[1]
+    _require(max_batch <= Bmax, "batch capacities must fit the buffers' rows")
+    for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new")):
+        _require(t.dtype == (q.dtype if lowp else k_pool.dtype),
+                 f"{nm} dtype must match the pools (q's for FP8 / MXFP4)")
+    qrs = _rows(q, "q", H_q, D)
+    nrs = _rows(k_new, "k_new", H_kv, D)
+    _require(_rows(v_new, "v_new", H_kv, D) == nrs, "k_new and v_new must share a row stride")
+    bts = _int32_2d(block_tables, "block_tables")
+    _require(block_tables.shape[0] >= max_batch, "block_tables needs a row per batch slot")
+    _int32_1d(positions, "positions", positions.shape[0])
+    _require(positions.shape[0] >= max_batch, "positions needs an entry per batch slot")
+    _require(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape[1:]) == (H_q, D)
+             and out.shape[0] >= max_batch, "out must be contiguous float32 [>= max batch cap, H_q, D]")
+    if (cow_src is None) != (cow_dst is None):
+        raise PkvError(-2, "cow_src and cow_dst go together")
+    if cow_src is not None:
+        for t, nm in ((cow_src, "cow_src"), (cow_dst, "cow_dst")):
+            _int32_1d(t, nm, t.shape[0])
+            _require(t.shape[0] >= max_batch, f"{nm} needs an entry per batch slot")
+    need = decode_workspace_bytes(max_batch, H_q, D, max_ctx, partition_size) if partition_size and max_batch else 0
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    keep = (q, k_new, v_new, k_pool, v_pool, block_tables, positions, out, cow_src, cow_dst, workspace, k_scale,
+            v_scale)
+    d = StepDesc()
+    d.dtype, d.H_q, d.H_kv, d.D, d.block_size, d.n_blocks = _dtype_code(q), H_q, H_kv, D, bs, n_blocks
+    d.scale, d.partition_size = float(scale), int(partition_size)
+    d.out, d.q, d.q_row_stride = out.data_ptr(), q.data_ptr(), qrs
+    d.k_new, d.v_new, d.new_row_stride = k_new.data_ptr(), v_new.data_ptr(), nrs
+    d.k_pool, d.v_pool = k_pool.data_ptr(), v_pool.data_ptr()
+    d.block_tables, d.bt_stride, d.positions = block_tables.data_ptr(), bts, positions.data_ptr()
+    d.cow_src = cow_src.data_ptr() if cow_src is not None else None
+    d.cow_dst = cow_dst.data_ptr() if cow_dst is not None else None
+    d.workspace = workspace.data_ptr() if workspace is not None else None
+    d.workspace_bytes = workspace.numel() if workspace is not None else 0
+    d.k_scale = k_scale.data_ptr() if fp8 else None
+    d.v_scale = v_scale.data_ptr() if fp8 else None
+    d.k_mx_scale = k_scale.data_ptr() if mx4 else None
+    d.v_mx_scale = v_scale.data_ptr() if mx4 else None
+    return d, keep
+
+
 class StepGraphs:
     """The fused decode step captured once per (batch capacity, context capacity).
 
@@ -639,56 +700,12 @@ class StepGraphs:
     def __init__(self, q, k_new, v_new, k_pool, v_pool, block_tables, positions, out, scale: float,
                  batch_caps, ctx_caps, *, partition_size: int = 0, cow_src=None, cow_dst=None, workspace=None,
                  k_scale=None, v_scale=None):
-        torch = _torch()
-        lowp = k_scale is not None                  # FP8 (float32 scales) or MXFP4 (uint8 scales)
-        mx4 = lowp and k_scale.dtype == torch.uint8
-        fp8 = lowp and not mx4
-        n_blocks, H_kv, bs, D = (_mx4_pools(k_pool, v_pool, k_scale, v_scale) if mx4
-                                 else _fp8_pools(k_pool, v_pool, k_scale, v_scale) if fp8
-                                 else _pool_dims(k_pool, v_pool))
-        Bmax, H_q = q.shape[0], q.shape[1]
         bcaps = [int(x) for x in batch_caps]
         ccaps = [int(x) for x in ctx_caps]
-        _require(bcaps and ccaps and bcaps[-1] <= Bmax, "batch capacities must fit the buffers' rows")
-        for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new")):
-            _require(t.dtype == (q.dtype if lowp else k_pool.dtype),
-                     f"{nm} dtype must match the pools (q's for FP8 / MXFP4)")
-        qrs = _rows(q, "q", H_q, D)
-        nrs = _rows(k_new, "k_new", H_kv, D)
-        _require(_rows(v_new, "v_new", H_kv, D) == nrs, "k_new and v_new must share a row stride")
-        bts = _int32_2d(block_tables, "block_tables")
-        _require(block_tables.shape[0] >= bcaps[-1], "block_tables needs a row per batch slot")
-        _int32_1d(positions, "positions", positions.shape[0])
-        _require(positions.shape[0] >= bcaps[-1], "positions needs an entry per batch slot")
-        _require(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape[1:]) == (H_q, D)
-                 and out.shape[0] >= bcaps[-1], "out must be contiguous float32 [>= max batch cap, H_q, D]")
-        if (cow_src is None) != (cow_dst is None):
-            raise PkvError(-2, "cow_src and cow_dst go together")
-        if cow_src is not None:
-            for t, nm in ((cow_src, "cow_src"), (cow_dst, "cow_dst")):
-                _int32_1d(t, nm, t.shape[0])
-                _require(t.shape[0] >= bcaps[-1], f"{nm} needs an entry per batch slot")
-        need = decode_workspace_bytes(bcaps[-1], H_q, D, ccaps[-1], partition_size) if partition_size else 0
-        if need and workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-        self._keep = (q, k_new, v_new, k_pool, v_pool, block_tables, positions, out, cow_src, cow_dst, workspace,
-                      k_scale, v_scale)
-        d = StepDesc()
-        d.dtype, d.H_q, d.H_kv, d.D, d.block_size, d.n_blocks = _dtype_code(q), H_q, H_kv, D, bs, n_blocks
-        d.scale, d.partition_size = float(scale), int(partition_size)
-        d.out, d.q, d.q_row_stride = out.data_ptr(), q.data_ptr(), qrs
-        d.k_new, d.v_new, d.new_row_stride = k_new.data_ptr(), v_new.data_ptr(), nrs
-        d.k_pool, d.v_pool = k_pool.data_ptr(), v_pool.data_ptr()
-        d.block_tables, d.bt_stride, d.positions = block_tables.data_ptr(), bts, positions.data_ptr()
-        d.cow_src = cow_src.data_ptr() if cow_src is not None else None
-        d.cow_dst = cow_dst.data_ptr() if cow_dst is not None else None
-        d.workspace = workspace.data_ptr() if workspace is not None else None
-        d.workspace_bytes = workspace.numel() if workspace is not None else 0
-        d.k_scale = k_scale.data_ptr() if fp8 else None
-        d.v_scale = v_scale.data_ptr() if fp8 else None
-        d.k_mx_scale = k_scale.data_ptr() if mx4 else None
-        d.v_mx_scale = v_scale.data_ptr() if mx4 else None
-        self._desc = d
+        _require(bcaps and ccaps, "capacity lists must not be empty")
+        d, keep = _step_desc(q, k_new, v_new, k_pool, v_pool, block_tables, positions, out, scale, bcaps[-1],
+                             ccaps[-1], partition_size, cow_src, cow_dst, workspace, k_scale, v_scale)
+        self._keep, self._desc = keep, d
         lib = load_library()
         bc = (ctypes.c_int32 * len(bcaps))(*bcaps)
         cc = (ctypes.c_int32 * len(ccaps))(*ccaps)
@@ -706,6 +723,53 @@ class StepGraphs:
     def close(self):
         if getattr(self, "_h", None) is not None:
             self._lib.pkv_step_graphs_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+
+class DualStepGraphs:
+    """A local and an offloaded attention batch per step, captured once per (local capacity,
+    offloaded capacity) pair as two parallel graph branches (``parallel=False``: one after the
+    other).  Each batch is a dict of the buffers ``StepGraphs`` takes (q, k_new, v_new, k_pool,
+    v_pool, block_tables, positions, out, optional workspace / k_scale / v_scale), sized for
+    its largest capacity, and optionally its own ``partition_size`` (else the keyword's); a
+    capacity of 0 leaves that branch out."""
+
+    def __init__(self, local: dict, offloaded: dict, scale: float, local_caps, off_caps, ctx_cap: int, *,
+                 partition_size: int = 0, parallel: bool = True):
+        lcaps = [int(x) for x in local_caps]
+        ocaps = [int(x) for x in off_caps]
+        _require(lcaps and ocaps, "capacity lists must not be empty")
+        descs, keeps = [], []
+        for bufs, caps in ((local, lcaps), (offloaded, ocaps)):
+            d, keep = _step_desc(bufs["q"], bufs["k_new"], bufs["v_new"], bufs["k_pool"], bufs["v_pool"],
+                                 bufs["block_tables"], bufs["positions"], bufs["out"], scale, caps[-1], ctx_cap,
+                                 int(bufs.get("partition_size", partition_size)), None, None, bufs.get("workspace"),
+                                 bufs.get("k_scale"), bufs.get("v_scale"))
+            descs.append(d)
+            keeps.append(keep)
+        self._keep, self._descs = keeps, descs
+        lib = load_library()
+        lc = (ctypes.c_int32 * len(lcaps))(*lcaps)
+        oc = (ctypes.c_int32 * len(ocaps))(*ocaps)
+        h = lib.pkv_dual_step_graphs_create(ctypes.byref(descs[0]), ctypes.byref(descs[1]),
+                                            ctypes.cast(lc, ctypes.c_void_p), len(lcaps),
+                                            ctypes.cast(oc, ctypes.c_void_p), len(ocaps), int(ctx_cap),
+                                            1 if parallel else 0)
+        if not h:
+            raise PkvError(PKV_ERR_HIP, "pkv_dual_step_graphs_create: " + lib.pkv_last_error().decode())
+        self._lib, self._h = lib, ctypes.c_void_p(h)
+        self.local_caps, self.off_caps, self.ctx_cap = lcaps, ocaps, int(ctx_cap)
+
+    def launch(self, B_local: int, B_off: int, *, stream=None):
+        _check(self._lib.pkv_dual_step_graphs_launch(self._h, int(B_local), int(B_off), _stream(stream)),
+               "dual_step_graphs_launch")
+
+    def close(self):
+        if getattr(self, "_h", None) is not None:
+            self._lib.pkv_dual_step_graphs_destroy(self._h)
             self._h = None
 
     def __del__(self):

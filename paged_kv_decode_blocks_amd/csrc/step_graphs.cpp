@@ -211,3 +211,171 @@ int pkv_step_graphs_launch(pkv_step_graphs* g, int32_t B, int32_t max_context_le
 void pkv_step_graphs_destroy(pkv_step_graphs* g) { delete g; }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Two attention batches per step, captured over a (local capacity, offloaded
+// capacity) grid.  The Adrenaline review (section 3.2.1) runs the decode
+// instance's own attention and the attention it offloaded to another GPU at the
+// same time, and (section 3.2.2) captures graphs over both batch sizes; on one
+// GPU the two batches are two step descriptions with their own tables, pools and
+// workspaces, captured as two parallel branches of one graph (or one after the
+// other, to measure what the overlap buys).
+// ---------------------------------------------------------------------------
+struct pkv_dual_step_graphs {
+    pkv_step_desc desc[2];
+    std::vector<int32_t> caps[2];
+    int32_t ctx_cap = 0;
+    std::vector<hipGraph_t> graphs;          // [i_local * n_off + i_off]; the (0, 0) bucket has none
+    std::vector<hipGraphExec_t> execs;
+
+    ~pkv_dual_step_graphs() {
+        for (hipGraphExec_t e : execs)
+            if (e) (void)hipGraphExecDestroy(e);
+        for (hipGraph_t g : graphs)
+            if (g) (void)hipGraphDestroy(g);
+    }
+};
+
+namespace {
+
+bool increasing_from_zero(const int32_t* v, int32_t n) {
+    for (int32_t i = 0; i < n; ++i)
+        if (v[i] < 0 || (i && v[i] <= v[i - 1])) return false;
+    return true;
+}
+
+int check_branch(const pkv_step_desc* d, const char* name, int32_t max_cap, int32_t ctx_cap) {
+    if (!d->positions || !d->block_tables) return fail(PKV_ERR_NULL, "%s: positions and block_tables must be set", name);
+    if (d->cow_src || d->cow_dst) return fail(PKV_ERR_UNSUPPORTED, "%s: no copy-on-write node in a dual step", name);
+    if (!d->k_scale != !d->v_scale || !d->k_mx_scale != !d->v_mx_scale || (d->k_scale && d->k_mx_scale))
+        return fail(PKV_ERR_INVALID_ARG, "%s: set one pair of scale pools at most, both of a pair", name);
+    if ((int64_t)ctx_cap > (int64_t)d->bt_stride * d->block_size)
+        return fail(PKV_ERR_INVALID_ARG, "%s: context capacity %d exceeds bt_stride * block_size", name, ctx_cap);
+    if (d->partition_size > 0 && max_cap > 0) {
+        const size_t need = pkv_decode_workspace_bytes(max_cap, d->H_q, d->D, ctx_cap, d->partition_size);
+        if (d->workspace_bytes < need || (need && !d->workspace))
+            return fail(PKV_ERR_WORKSPACE, "%s: needs %zu bytes of workspace, got %zu", name, need, d->workspace_bytes);
+    }
+    return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_dual_step_graphs* pkv_dual_step_graphs_create(const pkv_step_desc* local, const pkv_step_desc* offloaded,
+                                                  const int32_t* local_caps, int32_t n_local,
+                                                  const int32_t* off_caps, int32_t n_off, int32_t ctx_cap,
+                                                  int parallel) {
+    if (!local || !offloaded || !local_caps || !off_caps) {
+        fail(PKV_ERR_NULL, "descriptions and capacity lists must not be NULL");
+        return nullptr;
+    }
+    if (n_local <= 0 || n_off <= 0 || n_local > 1024 || n_off > 1024 || ctx_cap <= 0) {
+        fail(PKV_ERR_INVALID_ARG, "n_local = %d, n_off = %d in [1, 1024]; ctx_cap = %d > 0", n_local, n_off, ctx_cap);
+        return nullptr;
+    }
+    if (!increasing_from_zero(local_caps, n_local) || !increasing_from_zero(off_caps, n_off)) {
+        fail(PKV_ERR_INVALID_ARG, "capacity lists must be non-negative and strictly increasing");
+        return nullptr;
+    }
+    if (check_branch(local, "local", local_caps[n_local - 1], ctx_cap) ||
+        check_branch(offloaded, "offloaded", off_caps[n_off - 1], ctx_cap))
+        return nullptr;
+    if (local->partition_size > 0 && offloaded->partition_size > 0 && local->workspace &&
+        local->workspace == offloaded->workspace) {
+        fail(PKV_ERR_WORKSPACE, "the two branches run at the same time: give each its own workspace");
+        return nullptr;
+    }
+    pkv_dual_step_graphs* g = new (std::nothrow) pkv_dual_step_graphs();
+    if (!g) {
+        fail(PKV_ERR_INVALID_ARG, "out of host memory");
+        return nullptr;
+    }
+    g->desc[0] = *local;
+    g->desc[1] = *offloaded;
+    g->caps[0].assign(local_caps, local_caps + n_local);
+    g->caps[1].assign(off_caps, off_caps + n_off);
+    g->ctx_cap = ctx_cap;
+    const size_t n = (size_t)n_local * n_off;
+    g->graphs.assign(n, nullptr);
+    g->execs.assign(n, nullptr);
+
+    hipStream_t s0 = nullptr, s1 = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    hipError_t e = hipStreamCreateWithFlags(&s0, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&s1, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&join, hipEventDisableTiming);
+    int status = e == hipSuccess ? PKV_OK : fail(PKV_ERR_HIP, "capture streams: %s", hipGetErrorString(e));
+    for (size_t k = 0; k < n && status == PKV_OK; ++k) {
+        const int32_t c0 = g->caps[0][k / n_off], c1 = g->caps[1][k % n_off];
+        if (c0 == 0 && c1 == 0) continue;   // nothing to run
+        e = hipStreamBeginCapture(s0, hipStreamCaptureModeThreadLocal);
+        if (e != hipSuccess) {
+            status = fail(PKV_ERR_HIP, "begin capture: %s", hipGetErrorString(e));
+            break;
+        }
+        int st = PKV_OK;
+        const bool both = c0 > 0 && c1 > 0;
+        hipStream_t s_off = both && parallel ? s1 : s0;
+        if (both && parallel) {   // fork: s1 joins the capture after this point of s0
+            e = hipEventRecord(fork, s0);
+            if (e == hipSuccess) e = hipStreamWaitEvent(s1, fork, 0);
+            if (e != hipSuccess) st = fail(PKV_ERR_HIP, "fork: %s", hipGetErrorString(e));
+        }
+        if (st == PKV_OK && c0 > 0) st = enqueue_step(g->desc[0], c0, ctx_cap, false, s0);
+        if (st == PKV_OK && c1 > 0) st = enqueue_step(g->desc[1], c1, ctx_cap, false, s_off);
+        if (st == PKV_OK && both && parallel) {   // join the offloaded branch back into s0
+            e = hipEventRecord(join, s1);
+            if (e == hipSuccess) e = hipStreamWaitEvent(s0, join, 0);
+            if (e != hipSuccess) st = fail(PKV_ERR_HIP, "join: %s", hipGetErrorString(e));
+        }
+        hipGraph_t graph = nullptr;
+        e = hipStreamEndCapture(s0, &graph);
+        if (st != PKV_OK || e != hipSuccess || !graph) {
+            if (graph) (void)hipGraphDestroy(graph);
+            status = st != PKV_OK ? st : fail(PKV_ERR_HIP, "end capture: %s", hipGetErrorString(e));
+            break;
+        }
+        g->graphs[k] = graph;
+        e = hipGraphInstantiate(&g->execs[k], graph, nullptr, nullptr, 0);
+        if (e != hipSuccess) {
+            g->execs[k] = nullptr;
+            status = fail(PKV_ERR_HIP, "instantiate: %s", hipGetErrorString(e));
+        }
+    }
+    if (join) (void)hipEventDestroy(join);
+    if (fork) (void)hipEventDestroy(fork);
+    if (s1) (void)hipStreamDestroy(s1);
+    if (s0) (void)hipStreamDestroy(s0);
+    if (status != PKV_OK) {
+        delete g;
+        return nullptr;
+    }
+    pkv::clear_error();
+    return g;
+}
+
+int pkv_dual_step_graphs_launch(pkv_dual_step_graphs* g, int32_t B_local, int32_t B_off, void* stream) {
+    if (!g) return fail(PKV_ERR_NULL, "dual step graphs object is NULL");
+    if (B_local < 0 || B_off < 0) return fail(PKV_ERR_INVALID_ARG, "B_local = %d, B_off = %d", B_local, B_off);
+    auto i0 = std::lower_bound(g->caps[0].begin(), g->caps[0].end(), B_local);
+    auto i1 = std::lower_bound(g->caps[1].begin(), g->caps[1].end(), B_off);
+    if (i0 == g->caps[0].end() || i1 == g->caps[1].end())
+        return fail(PKV_ERR_INVALID_ARG, "B_local = %d / B_off = %d exceed the largest capacities %d / %d", B_local,
+                    B_off, g->caps[0].back(), g->caps[1].back());
+    const size_t k = (size_t)(i0 - g->caps[0].begin()) * g->caps[1].size() + (size_t)(i1 - g->caps[1].begin());
+    if (!g->execs[k]) {   // both capacities 0: an empty step
+        pkv::clear_error();
+        return PKV_OK;
+    }
+    const hipError_t e = hipGraphLaunch(g->execs[k], reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "graph launch: %s", hipGetErrorString(e));
+    pkv::clear_error();
+    return PKV_OK;
+}
+
+void pkv_dual_step_graphs_destroy(pkv_dual_step_graphs* g) { delete g; }
+
+}  // extern "C"
