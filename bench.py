@@ -452,6 +452,87 @@ def cufrac_bench(args, torch, pkv, dev, lib) -> int:
     return 0
 
 
+def dual_bench(args, torch, pkv, dev) -> int:
+    """A local and an offloaded attention batch per step ([P2] section 3.2.1: the decode
+    instance's own attention and the attention it offloaded run at the same time), replayed
+    from pkv_dual_step_graphs captured as two parallel branches, against the same two steps
+    captured one after the other and against each alone.  Each variant cycles over R copies
+    of both batches' inputs (at least 1 GiB of K/V reads per cycle, so none is cached); one
+    graph launch per step, K steps, timed with events on the launch stream."""
+    from workloads import get_config, make_workload, step_bytes
+    from workloads.device import upload
+
+    cfgs = [get_config(args.local), get_config(args.offloaded)]
+    ws = [make_workload(c, (args.seed or 0) + 500 + i, append=True) for i, c in enumerate(cfgs)]
+    ctx_cap = max(int(w.max_context_len) for w in ws)
+    ctx_cap = -(-ctx_cap // 16) * 16
+    sb = [step_bytes(c, w.context_lens, True) for c, w in zip(cfgs, ws)]
+    per_step = sum(x["total"] for x in sb)
+    reads = sum(x["kv_history"] for x in sb)
+    R = max(2, math.ceil((1 << 30) / reads))
+
+    def branch(w, cfg):
+        d = upload(w, dev)
+        W = w.block_tables.shape[1]
+        bt = torch.full((cfg.B, -(-ctx_cap // 16)), -1, dtype=torch.int32, device=dev)
+        bt[:, :W] = d["block_tables"]
+        b = {"q": d["q"], "k_new": d["k_new"], "v_new": d["v_new"], "k_pool": d["k_pool"], "v_pool": d["v_pool"],
+             "block_tables": bt, "positions": d["positions"],
+             "out": torch.empty((cfg.B, cfg.H_q, cfg.D), dtype=torch.float32, device=dev),
+             "partition_size": cfg.partition_size}
+        if cfg.fp8 or cfg.mxfp4:
+            b["k_scale"], b["v_scale"] = d["k_scale"], d["v_scale"]
+        return b
+
+    sets = [[branch(w, c) for w, c in zip(ws, cfgs)] for _ in range(R)]
+    B0, B1 = cfgs[0].B, cfgs[1].B
+    stream = torch.cuda.current_stream(dev)
+    scale = float(ws[0].scale)
+    if float(ws[1].scale) != scale:
+        raise SystemExit("both batches need the same head dim (one scale)")
+
+    def time_variant(caps0, caps1, parallel, n0, n1):
+        objs = [pkv.DualStepGraphs(s[0], s[1], scale, caps0, caps1, ctx_cap, parallel=parallel) for s in sets]
+        for k in range(2 * R):
+            objs[k % R].launch(n0, n1, stream=stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for k in range(args.steps):
+            objs[k % R].launch(n0, n1, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        gpu = e0.elapsed_time(e1) / 1e3
+        for o in objs:
+            o.close()
+        return gpu / args.steps, wall / args.steps
+
+    res = {}
+    for name, c0, c1, par, n0, n1 in (("parallel", [B0], [B1], True, B0, B1),
+                                      ("serialized", [B0], [B1], False, B0, B1),
+                                      ("local_alone", [B0], [0], True, B0, 0),
+                                      ("offloaded_alone", [0], [B1], True, 0, B1)):
+        g, wall = time_variant(c0, c1, par, n0, n1)
+        byt = (sb[0]["total"] if n0 else 0) + (sb[1]["total"] if n1 else 0)
+        res[name] = {"us_per_step": round(g * 1e6, 2), "wall_us_per_step": round(wall * 1e6, 2),
+                     "GBps": round(byt / g / 1e9, 1)}
+        print(json.dumps({"variant": name, **res[name]}), file=sys.stderr, flush=True)
+    print(json.dumps({
+        "mode": "dual", "metric": "decode step with a local and an offloaded attention batch (HBM GB/s)",
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "config": {"local": workload_label(cfgs[0], "fused append + attention"),
+                   "offloaded": workload_label(cfgs[1], "fused append + attention"),
+                   "ctx_cap": ctx_cap, "input_rotation_sets": R, "algorithmic_bytes_per_step": int(per_step),
+                   "graphs": "one pkv_dual_step_graphs launch per step (parallel or serialized branches)"},
+        "variants": res,
+        "overlap_gain": round(res["serialized"]["us_per_step"] / res["parallel"]["us_per_step"], 3),
+        "data": "synthetic (seeded; resident in HBM, rotated past the Infinity Cache)",
+    }))
+    return 0
+
+
 def loop_bench(args, torch, pkv, dev) -> int:
     """A decode loop driven by the library's block manager.
 
@@ -638,7 +719,9 @@ def main(argv=None):
     ap.add_argument("--no-graph", action="store_true", help="launch every step eagerly (for counter runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times (scales HBM byte counters)")
-    ap.add_argument("--mode", default="step", choices=["step", "loop", "cumask", "cufrac"],
+    ap.add_argument("--local", default="c2", help="dual mode: the local batch's workload")
+    ap.add_argument("--offloaded", default="c2", help="dual mode: the offloaded batch's workload")
+    ap.add_argument("--mode", default="step", choices=["step", "loop", "cumask", "cufrac", "dual"],
                     help="step: the headline step over resident inputs; loop: a block-manager-driven decode loop")
     ap.add_argument("--graphs", action="store_true", help="loop mode: replay captured step graphs")
     ap.add_argument("--native", action="store_true", help="loop mode: one pkv_decoder_step call per step")
@@ -687,6 +770,8 @@ def main(argv=None):
         return 0
     if args.mode == "loop":
         return loop_bench(args, torch, pkv, dev)
+    if args.mode == "dual":
+        return dual_bench(args, torch, pkv, dev)
     if args.mode == "cufrac":
         return cufrac_bench(args, torch, pkv, dev, lib)
 

@@ -696,7 +696,12 @@ void pkv_step_graphs_destroy(pkv_step_graphs* g);
  * pkv_dual_step_graphs_launch(B_local, B_off) replays the smallest fitting pair
  * (nothing, if both are 0); padding rows as for pkv_step_graphs.  Buffers stay
  * allocated for the object's lifetime; launch is asynchronous and
- * allocation-free; not thread-safe per object.
+ * allocation-free; not thread-safe per object.  Both branches read HBM at close
+ * to its rate, so running them side by side cannot beat the sum of their bytes
+ * at that rate: on MI355X the parallel form gained 3% for a long GQA batch beside
+ * a long MHA one and lost up to 17% for two short batches (the second branch
+ * starts later, on another hardware queue, and the join costs a few
+ * microseconds); pick the form by measuring the pair.
  */
 typedef struct pkv_dual_step_graphs pkv_dual_step_graphs;
 
