@@ -11,7 +11,9 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
 #include <mutex>
+#include <tuple>
 
 #include "pkv.h"
 #include "pkv_host.h"
@@ -68,17 +70,37 @@ struct Plan {
     int kind;         // grouped path: 0 = loads through registers, 1 = through an LDS ring
     int nw, ch, pf;   // waves per workgroup, blocks per chunk, chunks (or ring slots) in flight per wave
     int32_t wave_tokens;  // grouped kernel: > 0 = each wave streams one partition of this many tokens
+    int32_t even_waves;   // grouped kernel: > 0 = even split of the batch over at most this many waves
     int wpe;          // grouped FP8 kernel: waves per SIMD its registers are sized for
     int kd;           // grouped FP8 kernel: K tiles staged through LDS (1) or loaded into registers (0)
     unsigned grid;
     size_t ws_o, ws_lse, ws_total;
 };
 
+// Waves of the even-split kernel variant resident on the current device at once
+// (occupancy per CU times CUs), cached per device; 0 if the runtime cannot say.
+int64_t even_resident_waves(int dtype, int32_t D, int nw, int pf, bool fused) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    static std::mutex mu;
+    static std::map<std::tuple<int, int, int, int, int, bool>, int64_t> cache;
+    const auto key = std::make_tuple(dev, dtype, (int)D, nw, pf, fused);
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+    const int64_t w = (int64_t)pkv::gqa_even_wgs_per_cu(dtype, D, nw, pf, fused) * cus * nw;
+    cache[key] = w;
+    return w;
+}
+
 // Launch geometry.  Unsplit: one partition spanning the padded context.
 // `spans`: the kernel the plan is for implements one partition per wave (the 16-bit
-// per-head and grouped kernels, not the persistent, FP8 or MXFP4 ones).
+// per-head and grouped kernels, not the persistent, FP8 or MXFP4 ones); `fused`: the
+// call appends (picks the kernel instantiation whose occupancy sizes an even split).
 Plan make_plan(int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t max_ctx, int32_t partition_size,
-               bool fp8 = false, bool spans = false) {
+               bool fp8 = false, bool spans = false, bool fused = false) {
     Plan p{};
     const int32_t padded = max_ctx <= 0 ? pkv::kBlockSize
                                         : (max_ctx + pkv::kBlockSize - 1) / pkv::kBlockSize * pkv::kBlockSize;
@@ -126,6 +148,34 @@ Plan make_plan(int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32
         p.ch = env_int("PKV_GQA_CH", 1);
         p.pf = env_int("PKV_GQA_PF", 1);
         if (!pkv::gqa_variant_exists(p.kind, p.nw, p.ch, p.pf)) { p.kind = 2; p.nw = 4; p.ch = 1; p.pf = 1; }
+        // A split step over a batch of mixed lengths: the even split (kernel 1e) cuts the
+        // batch's blocks into equal runs, one wave per (run, KV head), one resident round of
+        // waves for the whole batch.  Its pieces and the merge's prefix fit the split's
+        // workspace: pieces <= (runs + B) * H_kv, G rows each, after B + 3 ints.
+        const int even_nw = env_int("PKV_GQA_EVEN_NW", 4), even_pf = env_int("PKV_GQA_EVEN_PF", 1);
+        if (spans && p.n_parts > 1 && p.kind == 2 && env_int("PKV_GQA_EVEN", 1) && B <= pkv::kEvenMaxBatch &&
+            pkv::gqa_even_variant_exists(even_nw, even_pf)) {
+            const int64_t worst = (int64_t)B * ((max_ctx + pkv::kBlockSize - 1) / pkv::kBlockSize);   // per head
+            const int64_t cap = ((int64_t)B * H_q * p.n_parts - B - 3) / H_q - B;
+            const int64_t need = (worst + pkv::kEvenMaxWaveBlocks - 1) / pkv::kEvenMaxWaveBlocks;
+            const int64_t resident = even_resident_waves(dtype, D, even_nw, even_pf, fused) / H_kv;
+            const int64_t want = std::max(resident * std::max(1, env_int("PKV_GQA_EVEN_ROUNDS", 1)), need);
+            const int64_t runs = std::min(want, cap);
+            // a few long requests: each row would be merged from dozens of pieces (slower
+            // than nw-partition spans on MI355X for B <= 4 of 8 KV heads); and a workspace
+            // too small for most of a round of runs: far fewer waves than the GPU holds.  The
+            // even split takes batches with at most ~16 runs per request on average and at
+            // least 3/4 of a round.
+            const bool fits = ((int64_t)B * 16 >= runs && 4 * runs >= 3 * want) || env_int("PKV_GQA_EVEN", 1) == 2;
+            if (resident > 0 && fits && runs >= need && runs >= 1 && worst < (int64_t)1 << 30 &&
+                runs * H_kv < (int64_t)1 << 30) {
+                p.nw = even_nw;
+                p.ch = 1;
+                p.pf = even_pf;
+                p.even_waves = (int32_t)(runs * H_kv);
+                p.grid = (unsigned)((runs * H_kv + even_nw - 1) / even_nw);
+            }
+        }
         // A split context: one workgroup spans nw consecutive partitions and wave w streams
         // partition w alone, so each wave's softmax state is its partition's and the
         // workgroup's closing merge of the waves is the log-sum-exp merge of those
@@ -134,13 +184,13 @@ Plan make_plan(int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32
         // partitions shared round-robin).  Kernel 1 only, a span within one window of
         // block ids, whole chunks per partition.
         const int32_t span = p.nw * partition_size;
-        if (spans && p.n_parts > 1 && p.kind != 1 && env_int("PKV_GQA_BLOCKED", 1) &&
+        if (!p.even_waves && spans && p.n_parts > 1 && p.kind != 1 && env_int("PKV_GQA_BLOCKED", 1) &&
             span <= pkv::kGqaSpanTokens && (partition_size / pkv::kBlockSize) % p.ch == 0) {
             p.wave_tokens = partition_size;
             p.part_tokens = span;
             p.n_parts = (max_ctx + span - 1) / span;
         }
-        p.grid = (unsigned)((int64_t)p.n_parts * B * H_kv);
+        if (!p.even_waves) p.grid = (unsigned)((int64_t)p.n_parts * B * H_kv);
     } else {
         // a PF-deep load pipeline pays where a workgroup walks a long unsplit context
         int nw = 4, ch = 2, pf = 1;
@@ -256,7 +306,7 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
     // one partition per wave: the 16-bit per-head and grouped kernels implement it (on the
     // grouped FP8 kernel it measured slower: c5f8 0.602 vs 0.621 of 8 TB/s)
     Plan p = make_plan(dtype, B, H_q, H_kv, D, max_ctx, partition_size, fp8 != nullptr,
-                       !fp8 && !mx4 && !persistent_wgs);
+                       !fp8 && !mx4 && !persistent_wgs, fused);
     if (mx4) {
         // kind 1: one workgroup per KV head and its G <= 16 query heads on MFMA (f16/bf16 q),
         // reading each K/V block once for the group; kind 0: one workgroup per query head on the
@@ -318,6 +368,11 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
     a.part_tokens = p.part_tokens;
     a.n_parts = p.n_parts;
     a.wave_tokens = p.wave_tokens;
+    if (p.even_waves) {   // the lse area starts with the merge's prefix: [tw, waves, blocks before b (B + 1)]
+        a.even_waves = p.even_waves;
+        a.even_meta = reinterpret_cast<int32_t*>(a.part_lse);
+        a.part_lse += B + 3;
+    }
     a.scale_log2 = scale * pkv::kLog2e;
     if (fp8) {
         a.k_scale = fp8->k;
@@ -366,6 +421,8 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
         e = pkv::launch_decode_gqa_fp8(dtype, D, p.nw, p.ch, p.pf, p.wpe, p.kd, a, p.grid, s);
     } else if (fp8) {
         e = pkv::launch_decode_fp8(dtype, D, p.nw, p.ch, p.pf, fused, a, p.grid, s);
+    } else if (p.grouped && p.even_waves) {
+        e = pkv::launch_decode_gqa_even(dtype, D, p.nw, p.pf, fused, a, p.grid, s);
     } else if (p.grouped) {
         e = pkv::launch_decode_gqa(dtype, D, p.kind, p.nw, p.ch, p.pf, fused, a, p.grid, s);
     } else if (persistent_wgs) {
@@ -387,6 +444,8 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
         m.n_parts = p.n_parts;
         m.part_tokens = p.part_tokens;
         m.max_context_len = max_ctx;
+        m.even_meta = a.even_meta;
+        m.H_kv = H_kv;
         e = pkv::launch_lse_merge(D, m, s);
         if (e != hipSuccess) return fail(PKV_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
     }
@@ -402,9 +461,11 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
     } else {
         char wt[32] = "";
         if (p.wave_tokens) snprintf(wt, sizeof wt, " wave_tokens=%d", p.wave_tokens);
+        if (p.even_waves) snprintf(wt, sizeof wt, " even_waves=%d", p.even_waves);
         snprintf(g_launch, sizeof g_launch, "%s dtype=%d D=%d nw=%d ch=%d pf=%d%s grid=%u part_tokens=%d n_parts=%d%s%s",
                  fp8 ? (p.grouped ? "gqa_mfma_fp8" : "fp8")
-                     : p.grouped ? (p.kind == 1 ? "gqa_mfma_lds" : p.kind == 2 ? "gqa_mfma_kdma" : "gqa_mfma")
+                     : p.grouped ? (p.even_waves ? "gqa_mfma_even"
+                                   : p.kind == 1 ? "gqa_mfma_lds" : p.kind == 2 ? "gqa_mfma_kdma" : "gqa_mfma")
                                  : "mha",
                  dtype, D, p.nw, p.ch, p.pf,
                  (fp8 && p.grouped)

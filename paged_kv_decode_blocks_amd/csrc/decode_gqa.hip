@@ -637,6 +637,245 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_kernel(const AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Kernel 1e: kernel 1's per-wave pipeline (K staged in LDS by DMA, V in
+// registers, one block per chunk) over an even split of the whole batch.
+//
+// The requests' blocks are laid end to end (request order) and cut into `runs`
+// equal runs of tw blocks; wave v streams run r = v / H_kv for KV head
+// g = v % H_kv.  Every wave gets the same number of blocks whatever the length
+// mix, so no workgroup is left running alone at the end, and the H_kv waves of a
+// run read the same blocks at the same time (their tiles are neighbours in each
+// pool block).  A wave walks the pieces of its run (its overlap with each
+// request) with a fresh softmax state per piece and writes each piece as
+// (o / l, log2 l + m) for its G query heads, or the output itself when the piece
+// is the request's whole context.  The log-sum-exp merge of a row's pieces
+// (lse_merge.hip) is the same exact regrouping of the softmax sum as for split
+// partitions.
+//
+// Piece of run r in request b for KV head g: id (r + b) H_kv + g (a run and a
+// request meet in one interval, and along the end-to-end order r and b only
+// grow, so r + b names each meeting once); its rows are part_o[(((r + b) H_kv +
+// g) G + h) D ...] and part_lse[((r + b) H_kv + g) G + h].
+//
+// Every workgroup prefix-sums the requests' block counts in LDS (lengths out of
+// range count as empty: the merge writes their NaN rows, and empty rows' zeros);
+// workgroup 0 also stores tw, the runs used and the prefix for the merge.
+// ---------------------------------------------------------------------------
+template <int DT, int D, int NW, int PF, bool APPEND>
+__global__ __launch_bounds__(NW * 64) void decode_gqa_even_kernel(const AttnArgs a) {
+    using L = GqaLane<DT, D, APPEND>;
+    constexpr int KS = L::KS, NWORD = L::NWORD, ES = L::ES, VT = L::VT;
+    constexpr int R = PF + 1;                  // ring slots per wave
+    constexpr int TILE = kBlockSize * D * ES;  // bytes of one (block, head) K tile
+    constexpr int CPR = D * ES / 16;           // 16-byte chunks per K row
+    constexpr int NDMA = TILE / 1024;          // DMA instructions per tile
+    constexpr int LPC = NDMA + 4;              // vmcnt units per block: K DMAs, then 4 V rows
+    constexpr int T = NW * 64;
+    constexpr int PER = kEvenMaxBatch / T + 1; // requests per thread in the prefix sum (covers index B)
+    static_assert(R <= 4 && PF * LPC < 64, "ring depth / vmcnt range");
+    __shared__ __attribute__((aligned(16))) char s_ring[NW * R * TILE];
+    __shared__ int32_t s_pre[PER * T];
+    __shared__ int32_t s_scan[T];
+    __shared__ int32_t s_wid[NW][kEvenMaxWaveBlocks];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // block counts of requests tid * PER ..., prefix-summed over the workgroup
+    int loc[PER];
+    int sum = 0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int b = tid * PER + k;
+        int nb = 0;
+        if (b < a.B) {
+            const int n = APPEND ? a.positions[b] + 1 : a.context_lens[b];
+            const bool bad = APPEND ? (n < 1 || n > a.max_context_len) : (n < 0 || n > a.max_context_len);
+            nb = bad ? 0 : (n + kBlockSize - 1) / kBlockSize;
+        }
+        loc[k] = sum;
+        sum += nb;
+    }
+    s_scan[tid] = sum;
+    __syncthreads();
+#pragma unroll
+    for (int off = 1; off < T; off <<= 1) {
+        const int x = tid >= off ? s_scan[tid - off] : 0;
+        __syncthreads();
+        s_scan[tid] += x;
+        __syncthreads();
+    }
+    const int excl = s_scan[tid] - sum;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) s_pre[tid * PER + k] = excl + loc[k];
+    __syncthreads();
+
+    const int total = s_pre[a.B];   // blocks per KV head over the batch (the host keeps it below 2^30)
+    const int runs = max(1, min(a.even_waves / a.H_kv, (total + kEvenMinWaveBlocks - 1) / kEvenMinWaveBlocks));
+    const int tw = max(1, (total + runs - 1) / runs);   // <= kEvenMaxWaveBlocks (host sizing)
+    if (blockIdx.x == 0) {
+        for (int b = tid; b <= a.B; b += T) a.even_meta[2 + b] = s_pre[b];
+        if (tid == 0) {
+            a.even_meta[0] = tw;
+            a.even_meta[1] = runs;
+        }
+    }
+    const int v = blockIdx.x * NW + w;
+    const int run = v / a.H_kv, g = v - run * a.H_kv;
+    int x0 = run * tw;
+    const int x1 = min(x0 + tw, total);
+    if (run >= runs || x0 >= x1) return;   // no barrier follows
+
+    // the request holding block x0: the last one whose blocks start at or before it
+    int b;
+    {
+        int lo = 0, hi = a.B - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_pre[mid] <= x0) lo = mid;
+            else hi = mid - 1;
+        }
+        b = __builtin_amdgcn_readfirstlane(lo);
+    }
+
+    const size_t blk_bytes = (size_t)a.H_kv * kBlockSize * D * ES;
+    const size_t head_bytes = (size_t)g * kBlockSize * D * ES;
+    const char* kpool = a.k_pool + head_bytes;
+    const char* vpool = a.v_pool + head_bytes;
+    char* ring = s_ring + w * R * TILE;
+    int32_t* wid = s_wid[w];
+    int kdma[NDMA], kread[KS];
+    L st;
+    while (x0 < x1) {
+        const int seg0 = __builtin_amdgcn_readfirstlane(s_pre[b]);
+        const int nbb = __builtin_amdgcn_readfirstlane(s_pre[b + 1]) - seg0;
+        const int pend = min(x1, seg0 + nbb);
+        const int blk0 = x0 - seg0, np = pend - x0;   // the piece: blocks [blk0, blk0 + np) of request b
+        const bool whole = blk0 == 0 && np == nbb;
+        const int piece = (run + b) * a.H_kv + g;
+        const int n = APPEND ? a.positions[b] + 1 : a.context_lens[b];
+        const int lim = APPEND ? n - 1 : n;   // tokens below lim come from the pools
+        const int pos_new = (APPEND && blk0 + np == nbb) ? n - 1 : -1;
+
+        st.init(a, lane, b, g);   // q of the row's G heads; fresh softmax state
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) {
+            const int slot16 = i * 64 + lane;
+            const int row = slot16 / CPR, p = slot16 % CPR;
+            kdma[i] = row * D * ES + ((p ^ (row % CPR)) * 16);
+        }
+#pragma unroll
+        for (int q = 0; q < KS; ++q) kread[q] = st.tau * D * ES + (((4 * q + st.j) ^ (st.tau % CPR)) * 16);
+
+        // the piece's block ids, range-checked, into the wave's LDS list
+        const int32_t* table = a.block_tables + (int64_t)b * a.bt_stride + blk0;
+        bool bad_lane = false;
+        for (int t = lane; t < np; t += 64) {
+            int id = table[t];
+            if ((unsigned)id >= (unsigned)a.n_blocks) {
+                bad_lane = true;
+                id = 0;
+            }
+            wid[t] = id;
+        }
+        const bool bad = __builtin_amdgcn_ballot_w64(bad_lane) != 0;
+        // the wave's LDS operations complete in order; the fence keeps the compiler from
+        // moving the list's reads above its writes
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+
+        const size_t new_off = ((size_t)b * a.new_row_stride + (size_t)g * D) * ES;
+        struct Buf {
+            uint4 k[1][KS];
+            VRow<NWORD> v[1][4];
+        };
+        auto load_blk = [&](int slot, Buf& bf, int i) {
+            const size_t id = (size_t)__builtin_amdgcn_readfirstlane(wid[i]);
+#pragma unroll
+            for (int q = 0; q < NDMA; ++q) dma16(kpool + id * blk_bytes + kdma[q], ring + slot * TILE + q * 1024);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) bf.v[0][r] = ldv<NWORD>(vpool + id * blk_bytes + st.voff[r]);
+        };
+        bool all_valid[1][4] = {{true, true, true, true}};
+        // steady: exactly PF later blocks' loads were issued after this block's
+        auto consume = [&](int slot, Buf& bf, bool steady) {
+            if (steady) wait_vmcnt<PF * LPC>();
+            else wait_vmcnt<0>();
+            lds_read16x<KS>(ring + slot * TILE, kread, bf.k[0]);
+            st.template accumulate<1>(bf.k, bf.v, all_valid);
+        };
+
+        // blocks wholly below lim, pipelined; block i lives in buffer and ring slot i % R
+        const int nf = max(0, min(blk0 + np, lim / kBlockSize) - blk0);
+        Buf buf[R];
+        int i = 0;
+        if (nf >= R + PF) {
+#pragma unroll
+            for (int u = 0; u < PF; ++u) load_blk(u, buf[u], u);
+            for (; i + R + PF <= nf; i += R) {
+#pragma unroll
+                for (int u = 0; u < R; ++u) {
+                    load_blk((u + PF) % R, buf[(u + PF) % R], i + u + PF);
+                    consume(u, buf[u], true);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < PF; ++u)
+                if (u < nf) load_blk(u, buf[u], u);
+        }
+        for (; i < nf; i += R) {
+#pragma unroll
+            for (int u = 0; u < R; ++u) {
+                if (i + u < nf) {
+                    if (i + u + PF < nf) load_blk((u + PF) % R, buf[(u + PF) % R], i + u + PF);
+                    consume(u, buf[u], false);
+                }
+            }
+        }
+        // the rest (the row's last block, holding the length boundary and the new token)
+        for (int k = nf; k < np; ++k) {
+            const int id = __builtin_amdgcn_readfirstlane(wid[k]);
+            const char* kb = a.k_pool + (size_t)id * blk_bytes + head_bytes;
+            const char* vb = a.v_pool + (size_t)id * blk_bytes + head_bytes;
+            st.partial_block(a, kb, vb, (blk0 + k) * kBlockSize, lim, pos_new, new_off, !bad);
+        }
+
+        // the piece's result for its G heads (lane (j, col): head col, d = (4 j + i) VT + t)
+        float l = st.l;
+        l += __shfl_xor(l, 16, 64);
+        l += __shfl_xor(l, 32, 64);
+        if (st.col < a.G) {
+            const size_t row = (size_t)b * a.H_q + (size_t)g * a.G + st.col;
+            float* dst = whole ? a.out + row * D : a.part_o + ((size_t)piece * a.G + st.col) * D;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float* o = dst + (4 * st.j + r) * VT;
+#pragma unroll
+                for (int t = 0; t < VT; t += 4) {
+                    floatx4 val;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) val[e] = bad ? __builtin_nanf("") : st.acc[t + e][r] / l;
+                    *reinterpret_cast<floatx4*>(o + t) = val;
+                }
+            }
+            // v_log_f32 is log base 2, matching the log2-domain scores
+            if (!whole && st.j == 0)
+                a.part_lse[(size_t)piece * a.G + st.col] = bad ? __builtin_nanf("") : st.m + __builtin_amdgcn_logf(l);
+        }
+
+        x0 = pend;
+        if (x0 < x1) {   // the next request with blocks
+            do {
+                ++b;
+            } while (s_pre[b + 1] == s_pre[b]);
+            b = __builtin_amdgcn_readfirstlane(b);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Kernel 2: loads through LDS.  Each wave owns a ring of S slots; a slot holds
 // one block's K tile (chunk-swizzled rows) followed by its V tile.
 // ---------------------------------------------------------------------------
@@ -866,6 +1105,62 @@ hipError_t launch_decode_gqa(int dtype, int D, int kind, int nw, int ch, int pf,
     case DT_BF16 * 1000 + 128: return launch_gqa_d<DT_BF16, 128>(kind, nw, ch, pf, append, a, grid, stream);
     default: return hipErrorInvalidValue;
     }
+}
+
+// (waves, blocks ahead) of the even-split kernel
+#define PKV_GQA_EVEN_VARIANTS(X) X(4, 1) X(2, 1) X(8, 1)
+
+template <int DT, int D, int NW, int PF>
+static const void* gqa_even_fn(bool append) {
+    return append ? reinterpret_cast<const void*>(&decode_gqa_even_kernel<DT, D, NW, PF, true>)
+                  : reinterpret_cast<const void*>(&decode_gqa_even_kernel<DT, D, NW, PF, false>);
+}
+
+template <int DT, int D>
+static const void* gqa_even_fn_d(int nw, int pf, bool append) {
+    switch (nw * 10 + pf) {
+#define PKV_CASE(NW_, PF_) \
+    case NW_ * 10 + PF_: return gqa_even_fn<DT, D, NW_, PF_>(append);
+        PKV_GQA_EVEN_VARIANTS(PKV_CASE)
+#undef PKV_CASE
+    default: return nullptr;
+    }
+}
+
+static const void* gqa_even_kernel_fn(int dtype, int D, int nw, int pf, bool append) {
+    switch (dtype * 1000 + D) {
+    case DT_F16 * 1000 + 64: return gqa_even_fn_d<DT_F16, 64>(nw, pf, append);
+    case DT_F16 * 1000 + 128: return gqa_even_fn_d<DT_F16, 128>(nw, pf, append);
+    case DT_BF16 * 1000 + 64: return gqa_even_fn_d<DT_BF16, 64>(nw, pf, append);
+    case DT_BF16 * 1000 + 128: return gqa_even_fn_d<DT_BF16, 128>(nw, pf, append);
+    default: return nullptr;
+    }
+}
+
+hipError_t launch_decode_gqa_even(int dtype, int D, int nw, int pf, bool append, const AttnArgs& a, unsigned grid,
+                                  hipStream_t stream) {
+    const void* fn = gqa_even_kernel_fn(dtype, D, nw, pf, append);
+    if (!fn || !a.even_meta || a.even_waves <= 0 || a.B > kEvenMaxBatch) return hipErrorInvalidValue;
+    void* args[] = {const_cast<AttnArgs*>(&a)};
+    return hipLaunchKernel(fn, dim3(grid), dim3(nw * 64), args, 0, stream);
+}
+
+bool gqa_even_variant_exists(int nw, int pf) {
+    switch (nw * 10 + pf) {
+#define PKV_CASE(NW_, PF_) case NW_ * 10 + PF_:
+        PKV_GQA_EVEN_VARIANTS(PKV_CASE)
+#undef PKV_CASE
+        return true;
+    default: return false;
+    }
+}
+
+int gqa_even_wgs_per_cu(int dtype, int D, int nw, int pf, bool append) {
+    const void* fn = gqa_even_kernel_fn(dtype, D, nw, pf, append);
+    if (!fn) return 0;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, nw * 64, 0) != hipSuccess) return 0;
+    return n;
 }
 
 bool gqa_variant_exists(int kind, int nw, int ch, int pf) {

@@ -16,6 +16,10 @@ constexpr int kBlockSize = 16;   // tokens per physical KV block (the only size 
 constexpr int kGqaWindowTokens = 256 * kBlockSize;   // block ids a grouped workgroup stages in LDS at a time
 constexpr int kGqaSpanTokens = 512 * kBlockSize;     // the same for the 16-bit grouped kernel with K in LDS
 constexpr int kMhaWindowTokens = 256 * kBlockSize;   // the same for the per-head kernel
+// Even split of a grouped batch (one run of blocks per wave, see decode_gqa.hip):
+constexpr int kEvenMaxBatch = 1024;       // requests whose block counts a workgroup prefix-sums in LDS
+constexpr int kEvenMaxWaveBlocks = 256;   // longest run of blocks one wave takes
+constexpr int kEvenMinWaveBlocks = 16;    // shortest run worth a wave of its own
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -3.0e38f;   // "no score yet": exp2(kNegBig - m) == 0 for any real m
 
@@ -212,6 +216,10 @@ struct AttnArgs {
     int32_t wave_tokens;           // grouped kernel: 0 = the waves share the span's chunks round-robin;
                                    // > 0 = the span is part_tokens / wave_tokens partitions of this many
                                    // tokens and wave w streams partition w alone
+    int32_t even_waves;            // grouped kernel with K in LDS: > 0 = even split over at most this many
+                                   // waves (part_o / part_lse then hold one row per piece and head)
+    int32_t* even_meta;            // even split: [0] blocks per wave, [1] waves used, [2 + b] blocks of
+                                   // requests 0 .. b-1 (b = 0 .. B)
     float scale_log2;              // scale * log2(e)
 };
 

@@ -27,6 +27,8 @@ struct MergeArgs {
     const int32_t* context_lens;   // plain call
     const int32_t* positions;      // fused call (n = positions + 1); context_lens unused
     int32_t BH, H_q, n_parts, part_tokens, max_context_len;
+    const int32_t* even_meta;      // even split (see AttnArgs): pieces instead of partitions
+    int32_t H_kv;                  // even split only
 };
 
 // pool[dst[i]] = pool[src[i]] for both pools; a block is block_bytes contiguous bytes
@@ -104,6 +106,13 @@ hipError_t launch_decode_mha_persistent(int dtype, int D, bool append, const Att
 hipError_t launch_decode_gqa(int dtype, int D, int kind, int nw, int ch, int pf, bool append, const AttnArgs& a,
                              unsigned grid, hipStream_t stream);
 hipError_t launch_lse_merge(int D, const MergeArgs& a, hipStream_t stream);
+// even split of a grouped 16-bit batch: grid = ceil(a.even_waves / nw) workgroups of nw waves, pf blocks
+// ahead per wave; then launch_lse_merge with m.even_meta set
+hipError_t launch_decode_gqa_even(int dtype, int D, int nw, int pf, bool append, const AttnArgs& a, unsigned grid,
+                                  hipStream_t stream);
+bool gqa_even_variant_exists(int nw, int pf);
+// workgroups of that variant resident on one CU of the current device (0 on error)
+int gqa_even_wgs_per_cu(int dtype, int D, int nw, int pf, bool append);
 hipError_t launch_stream_read(const void* buf, size_t bytes, unsigned* sink, int grid, hipStream_t stream);
 // `grid` 16-wave workgroups, one per CU, each running bf16 MFMA chains for `iterations` rounds
 hipError_t launch_mfma_burn(int grid, int iterations, unsigned* sink, hipStream_t stream);

@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 
 TOL = {"f32": (1e-5, 1e-5), "f16": (2e-3, 1e-2), "bf16": (2e-3, 1e-2)}
 # the kernel each workload's step must run (prefix of pkv.last_launch())
-KERNEL = {"c1": "mha ", "c2": "mha ", "c3": "mha ", "c4": "mha ", "c5": "gqa_mfma_kdma ", "c3f8": "fp8 ",
+KERNEL = {"c1": "mha ", "c2": "mha ", "c3": "mha ", "c4": "mha ", "c5": "gqa_mfma_even ", "c3f8": "fp8 ",
           "c5f8": "gqa_mfma_fp8 ", "c3f4": "mxfp4 ", "c5f4": "mxfp4_mfma "}
 
 

@@ -331,7 +331,7 @@ def test_gqa_launch_variants(torch_dev, variant, dtype, D):
                                       pool=("factor", 1.2)), seed=32)
     ref_attn = oracle.paged_decode_attention(dtype, w_attn.q, w_attn.k_pool, w_attn.v_pool, w_attn.block_tables,
                                              w_attn.context_lens, w_attn.scale)
-    env = {"PKV_GQA_KIND": kind, "PKV_GQA_NW": nw, "PKV_GQA_CH": ch, "PKV_GQA_PF": pf}
+    env = {"PKV_GQA_KIND": kind, "PKV_GQA_NW": nw, "PKV_GQA_CH": ch, "PKV_GQA_PF": pf, "PKV_GQA_EVEN": 0}
     for P in (0, 512):
         got = _with_env(env, lambda: run_attention(torch_dev, w_attn, w_attn.k_pool, w_attn.v_pool, P))
         launch = pkv.last_launch()

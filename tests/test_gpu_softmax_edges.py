@@ -56,8 +56,10 @@ FAMILIES = [
     ("mha_f32_grouped", "", "f32", 8, {}, "mha "),
     ("gqa_regs_bf16", "", "bf16", 8, {"PKV_GQA_KIND": "0"}, "gqa_mfma "),
     ("gqa_lds_f16", "", "f16", 8, {"PKV_GQA_KIND": "1", "PKV_GQA_PF": "2"}, "gqa_mfma_lds "),
-    ("gqa_kdma_bf16", "", "bf16", 8, {}, "gqa_mfma_kdma "),
-    ("gqa_kdma_f16", "", "f16", 8, {}, "gqa_mfma_kdma "),
+    ("gqa_kdma_bf16", "", "bf16", 8, {"PKV_GQA_EVEN": "0"}, "gqa_mfma_kdma "),
+    ("gqa_kdma_f16", "", "f16", 8, {"PKV_GQA_EVEN": "0"}, "gqa_mfma_kdma "),
+    ("gqa_even_bf16", "", "bf16", 8, {"PKV_GQA_EVEN": "2"}, "gqa_mfma_even "),
+    ("gqa_even_f16", "", "f16", 8, {"PKV_GQA_EVEN": "2"}, "gqa_mfma_even "),
     ("fp8_f16", "fp8", "f16", 1, {}, "fp8 "),
     ("fp8_f32_grouped", "fp8", "f32", 2, {}, "fp8 "),
     ("fp8_grouped_bf16", "fp8", "bf16", 8, {}, "gqa_mfma_fp8 "),
@@ -234,6 +236,12 @@ def assert_pools(w, d, kp, vp):
         assert bits_equal(to_numpy_bits(d["v_pool"], w.cfg.dtype), vp)
 
 
+def expect(prefix, P):
+    """The launch-string prefix a family shows at partition size P (the even split is a
+    split-step plan: unsplit, the same family runs the grouped kernel with K in LDS)."""
+    return "gqa_mfma_kdma " if prefix == "gqa_mfma_even " and P == 0 else prefix
+
+
 def _setenv(monkeypatch, env):
     for k, v in env.items():
         monkeypatch.setenv(k, v)
@@ -254,7 +262,7 @@ def test_climbing_scores(torch_dev, monkeypatch, family, P, append):
         assert_climbs(w, kp, P)
     got, d = run(torch_dev, w, P, append)
     launch = pkv.last_launch()
-    assert launch.startswith(prefix), launch
+    assert launch.startswith(expect(prefix, P)), launch
     assert_close(got, ref, dtype, f"{family[0]} P={P} append={append} [{launch}]")
     if append:
         assert_pools(w, d, kp, vp)
@@ -295,7 +303,7 @@ def test_huge_logits_give_the_argmax_row(torch_dev, monkeypatch, family, P, appe
     ref, kp, vp = oracle.run_step(w)
     got, d = run(torch_dev, w, P, append)
     launch = pkv.last_launch()
-    assert launch.startswith(prefix), launch
+    assert launch.startswith(expect(prefix, P)), launch
     kf, vf = dequantized(w, kp, vp)
     if dtype == "f32":
         # f32 q: scores of ~10^3 carry float32 rounding of ~10^-4 (a correctly rounded float32
@@ -331,7 +339,8 @@ def test_huge_logits_give_the_argmax_row(torch_dev, monkeypatch, family, P, appe
     assert n_checked >= cfg.H_q * cfg.B // 2
 
 
-VARIANT_CASES = ([("gqa", v) for v in GQA_VARIANTS] + [("mha", v) for v in MHA_VARIANTS]
+VARIANT_CASES = ([("gqa", v) for v in GQA_VARIANTS] + [("even", v) for v in ("4,1", "2,1", "8,1")]
+                 + [("mha", v) for v in MHA_VARIANTS]
                  + [("fp8g", v) for v in GQA8_VARIANTS] + [("mx4", v) for v in MX4_VARIANTS]
                  + [("fp8", v) for v in ("4,2,1", "4,2,2", "8,2,2", "4,4,1")])
 
@@ -339,8 +348,11 @@ VARIANT_CASES = ([("gqa", v) for v in GQA_VARIANTS] + [("mha", v) for v in MHA_V
 def _variant_env(kind, v):
     if kind == "gqa":
         k, nw, ch, pf = v
-        return {"PKV_GQA_KIND": str(k), "PKV_GQA_NW": str(nw), "PKV_GQA_CH": str(ch), "PKV_GQA_PF": str(pf)}, \
-            f"nw={nw} ch={ch} pf={pf}"
+        return {"PKV_GQA_KIND": str(k), "PKV_GQA_NW": str(nw), "PKV_GQA_CH": str(ch), "PKV_GQA_PF": str(pf),
+                "PKV_GQA_EVEN": "0"}, f"nw={nw} ch={ch} pf={pf}"
+    if kind == "even":
+        nw, pf = v.split(",")
+        return {"PKV_GQA_EVEN": "2", "PKV_GQA_EVEN_NW": nw, "PKV_GQA_EVEN_PF": pf}, f"nw={nw} ch=1 pf={pf}"
     if kind == "mha":
         nw, ch, pf = v
         return {"PKV_MHA_NW": str(nw), "PKV_MHA_CH": str(ch), "PKV_MHA_PF": str(pf)}, f"nw={nw} ch={ch} pf={pf}"
@@ -364,9 +376,9 @@ def test_climbing_scores_every_launch_variant(torch_dev, monkeypatch, kind, vari
     G = 1 if kind in ("mha", "fp8") or (kind == "mx4" and variant.startswith("0")) else 8
     for dtype in ("bf16", "f16"):
         w, ref, kp, vp = climbing(kv, dtype, G, True)
-        for P in (0, 512):
+        for P in ((32, 512) if kind == "even" else (0, 512)):   # the even split is a split-step plan
             got, d = run(torch_dev, w, P, True)
             launch = pkv.last_launch()
-            assert tag in launch, launch
+            assert tag in launch and (kind != "even" or launch.startswith("gqa_mfma_even ")), launch
             assert_close(got, ref, dtype, f"{kind} {variant} {dtype} P={P} [{launch}]")
             assert_pools(w, d, kp, vp)
