@@ -365,8 +365,9 @@ template <bool PAIR = false>
 __device__ __forceinline__ void gqa_indices(const AttnArgs& a, GqaUnit& u) {
     const int BG = a.B * a.H_kv;
     const int x = PAIR ? xcd_pair_unit(blockIdx.x, a.n_parts * BG) : (int)blockIdx.x;
-    u.part = x / BG;
-    const int bg = x - u.part * BG;
+    const int pg = x / BG;
+    u.part = unit_part(a, pg);
+    const int bg = x - pg * BG;
     u.b = bg / a.H_kv;
     u.g = bg - u.b * a.H_kv;
     u.first_blk = u.part * (a.part_tokens / kBlockSize);

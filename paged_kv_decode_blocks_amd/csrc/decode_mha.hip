@@ -55,8 +55,9 @@ __device__ __forceinline__ void mha_unit(const AttnArgs& a, const int unit) {
     const int c = lane % LPT;
 
     const int BH = a.B * a.H_q;
-    const int part = unit / BH;
-    const int bh = unit - part * BH;
+    const int pg = unit / BH;
+    const int part = unit_part(a, pg);
+    const int bh = unit - pg * BH;
     const int b = bh / a.H_q;
     const int h = bh - b * a.H_q;
     const int g = h / a.G;

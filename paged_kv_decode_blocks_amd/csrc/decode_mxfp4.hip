@@ -123,8 +123,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mxfp4_kernel(const AttnArgs a)
 
     const int BH = a.B * a.H_q;
     const int unit = xcd_pair_unit(blockIdx.x, a.n_parts * BH);
-    const int part = unit / BH;
-    const int bh = unit - part * BH;
+    const int pg = unit / BH;
+    const int part = unit_part(a, pg);
+    const int bh = unit - pg * BH;
     const int b = bh / a.H_q;
     const int h = bh - b * a.H_q;
     const int g = h / a.G;

@@ -481,8 +481,9 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
 
     const int BG = a.B * a.H_kv;
     const int unit = xcd_pair_unit(blockIdx.x, a.n_parts * BG);
-    const int part = unit / BG;
-    const int bg = unit - part * BG;
+    const int pg = unit / BG;
+    const int part = unit_part(a, pg);
+    const int bg = unit - pg * BG;
     const int b = bg / a.H_kv;
     const int g = bg - b * a.H_kv;
     const int lane = threadIdx.x & 63;

@@ -216,11 +216,18 @@ struct AttnArgs {
     int32_t wave_tokens;           // grouped kernel: 0 = the waves share the span's chunks round-robin;
                                    // > 0 = the span is part_tokens / wave_tokens partitions of this many
                                    // tokens and wave w streams partition w alone
+    int32_t part_rev;              // split kernels: 1 = deal partitions from the last to the first
     int32_t even_waves;            // grouped kernel with K in LDS: > 0 = even split over at most this many
                                    // waves (part_o / part_lse then hold one row per piece and head)
     int32_t* even_meta;            // even split: [0] blocks per wave, [1] waves used, [2 + b] blocks of
                                    // requests 0 .. b-1 (b = 0 .. B)
     float scale_log2;              // scale * log2(e)
 };
+
+// Partition of the p-th group of work units (units are numbered partition-major, so the
+// dispatcher starts them in that order).  With part_rev the last partitions -- present only
+// for the longest requests -- start first and every request's first partitions end the
+// launch, so its final round is the batch's densest set of equal units.
+__device__ __forceinline__ int unit_part(const AttnArgs& a, int p) { return a.part_rev ? a.n_parts - 1 - p : p; }
 
 }  // namespace pkv

@@ -370,3 +370,45 @@ def test_mha_launch_variants(torch_dev, variant, dtype, D):
         launch = pkv.last_launch()
         assert f"nw={nw} ch={ch} pf={pf}" in launch, launch
         assert_close(got, ref, dtype, f"mha {variant} P={P} [{launch}]")
+
+
+@pytest.mark.parametrize("name,P,env", [
+    ("c4", 256, {}), ("c5", 1024, {"PKV_GQA_EVEN": 0}), ("c5f8", 1024, {}), ("c5f4", 1024, {}),
+    ("c3f8", 512, {}), ("c3f4", 512, {}), ("c5", 512, {"PKV_GQA_EVEN": 0, "PKV_GQA_KIND": 1}),
+    ("c5", 512, {"PKV_GQA_EVEN": 0, "PKV_GQA_KIND": 0})])
+def test_partition_order_is_bit_identical(torch_dev, name, P, env):
+    """Dealing partitions last-first (the default) or first-first changes only the dispatch
+    order: every partition is the same work and the merge adds them in index order, so the
+    outputs and pools agree bit for bit, and match the oracle."""
+    import os
+    torch = torch_dev
+    over = dict(B=6, lengths=("fixed", (1, 700, 5000, 33, 4096, 2047)), append=True)
+    w = make_workload(get_config(name, **over), seed=61)
+    ref = oracle.run_step(w)[0]
+    outs = []
+    for rev in (1, 0):
+        def step():
+            d = upload(w)
+            kw = dict(partition_size=P)
+            if w.cfg.kv_dtype == "fp8":
+                o = pkv.append_decode_attention_fp8(d["q"], d["k_new"], d["v_new"], d["k_pool"], d["v_pool"],
+                                                    d["k_scale"], d["v_scale"], d["block_tables"], d["positions"],
+                                                    float(w.scale), int(w.context_lens.max()), **kw)
+            elif w.cfg.kv_dtype == "mxfp4":
+                o = pkv.append_decode_attention_mxfp4(d["q"], d["k_new"], d["v_new"], d["k_pool"], d["v_pool"],
+                                                      d["k_scale"], d["v_scale"], d["block_tables"], d["positions"],
+                                                      float(w.scale), int(w.context_lens.max()), **kw)
+            else:
+                o = pkv.append_decode_attention(d["q"], d["k_new"], d["v_new"], d["k_pool"], d["v_pool"],
+                                                d["block_tables"], d["positions"], float(w.scale),
+                                                int(w.context_lens.max()), **kw)
+            torch.cuda.synchronize()
+            pools = ("k_pool", "v_pool") + (("k_scale", "v_scale") if w.cfg.kv_dtype else ())
+            return o.cpu().numpy(), {k: d[k].cpu() for k in pools}, pkv.last_launch()
+        outs.append(_with_env({**env, "PKV_PART_REV": rev}, step))
+    (o1, p1, l1), (o0, p0, l0) = outs
+    assert l1 == l0 and "n_parts=1 " not in l1, l1
+    assert np.array_equal(o1.view(np.uint32), o0.view(np.uint32)), l1
+    for k in p1:
+        assert torch.equal(p1[k].view(torch.uint8), p0[k].view(torch.uint8)), k
+    assert_close(o1, ref, w.cfg.dtype, f"{name} P={P} [{l1}]")
