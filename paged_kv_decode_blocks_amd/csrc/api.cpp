@@ -77,6 +77,9 @@ struct Plan {
     size_t ws_o, ws_lse, ws_total;
 };
 
+int32_t coarsen_partitions(Plan& p, int32_t B, int32_t H_kv, int32_t max_ctx, int32_t partition_size,
+                           int min_wgs_per_cu);
+
 // Waves of the even-split kernel variant resident on the current device at once
 // (occupancy per CU times CUs), cached per device; 0 if the runtime cannot say.
 int64_t even_resident_waves(int dtype, int32_t D, int nw, int pf, bool fused) {
@@ -129,7 +132,7 @@ Plan make_plan(int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32
         if (!pkv::gqa_fp8_variant_exists(p.nw, p.ch, p.pf, p.wpe, p.kd)) {
             p.nw = 2; p.ch = 1; p.pf = 1; p.wpe = 2; p.kd = 1;
         }
-        p.grid = (unsigned)wgs;
+        p.grid = 0;   // after the partitions are final (below)
     } else if (fp8) {
         // launch-shape sweep on MI355X (c3-shaped FP8 batch): 4-wave workgroups with 2-block
         // chunks beat 8 waves (the decode work per byte keeps register use high) and deeper pipelines
@@ -223,7 +226,49 @@ Plan make_plan(int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32
         p.ws_lse = align_up((size_t)B * H_q * p.n_parts * sizeof(float), 256);
     }
     p.ws_total = p.ws_o + p.ws_lse;
+    if (fp8 && p.grouped) {
+        coarsen_partitions(p, B, H_kv, max_ctx, partition_size, 8);
+        p.grid = (unsigned)((int64_t)p.n_parts * B * H_kv);
+    }
     return p;
+}
+
+// Compute units of the current device (cached per device; 0 if the runtime cannot say).
+int device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    static std::mutex mu;
+    static int cached[64] = {};
+    std::lock_guard<std::mutex> lock(mu);
+    if (!cached[dev]) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) cached[dev] = cus;
+    }
+    return cached[dev];
+}
+
+// The grouped FP8 and MXFP4 kernels split at no less than a floor of tokens, 2048 by default
+// (a multiple of the caller's partition: fewer, longer workgroups and fewer partial rows,
+// which the caller's workspace holds).  Measured on MI355X with the caller's 1024 (512):
+// grouped MXFP4 +5 % on c5-shaped batches, +12-24 % on 1-128 requests; grouped FP8 +3-6 % on
+// c5-shaped batches but -10 % where the coarser grid drops below two rounds of its resident
+// 2-wave workgroups, so there the floor needs min_wgs_per_cu workgroups per CU.  Returns the
+// partition in force (0 = the caller's).
+int32_t coarsen_partitions(Plan& p, int32_t B, int32_t H_kv, int32_t max_ctx, int32_t partition_size,
+                           int min_wgs_per_cu) {
+    const int32_t floor_tokens = env_int("PKV_LP_MIN_PART", 2048);
+    if (p.n_parts <= 1 || floor_tokens <= partition_size) return 0;
+    const int32_t k = (floor_tokens + partition_size - 1) / partition_size;
+    const int64_t pt = (int64_t)k * partition_size;
+    const int32_t n_parts = pt >= max_ctx ? 1 : (int32_t)((max_ctx + pt - 1) / pt);
+    if (min_wgs_per_cu > 0 && (int64_t)n_parts * B * H_kv < (int64_t)min_wgs_per_cu * device_cus()) return 0;
+    if (n_parts == 1) {
+        p.part_tokens = (max_ctx + pkv::kBlockSize - 1) / pkv::kBlockSize * pkv::kBlockSize;
+    } else {
+        p.part_tokens = (int32_t)pt;
+    }
+    p.n_parts = n_parts;
+    return (int32_t)pt;
 }
 
 int check_common(int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t block_size, int32_t n_blocks,
@@ -322,6 +367,7 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
             p.ch = 1;
             p.pf = env_int("PKV_MX4_PF", 1);
             if (!pkv::mxfp4_mfma_variant_exists(p.nw, p.pf)) { p.nw = 4; p.pf = 1; }
+            coarsen_partitions(p, B, H_kv, max_ctx, partition_size, 0);
             p.grid = (unsigned)((int64_t)p.n_parts * B * H_kv);
         } else {
             p.nw = env_int("PKV_MX4_NW", 4);

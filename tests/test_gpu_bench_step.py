@@ -53,6 +53,8 @@ def test_bench_step_parity(torch_dev, name):
     torch.cuda.synchronize()
     got = sets[0]["out"].cpu().numpy()
     assert launch.startswith(KERNEL[name]) and "fused_append" in launch, launch
+    if name in ("c5f8", "c5f4"):            # the grouped low-precision kernels' 2048-token floor
+        assert "part_tokens=2048 " in launch, launch
 
     ref, kp, vp = oracle.run_step(w)
     atol, rtol = TOL[cfg.dtype]

@@ -17,6 +17,13 @@ from workloads.device import to_numpy_bits, to_tensor, upload
 
 pytestmark = pytest.mark.gpu
 
+
+@pytest.fixture(autouse=True)
+def small_partitions(monkeypatch):
+    """The grouped low-precision kernels split at no less than 2048 tokens by default; these
+    tests exercise the caller's own small partitions (the floor has its own tests)."""
+    monkeypatch.setenv("PKV_LP_MIN_PART", "0")
+
 TOL = {"f32": (1e-5, 1e-5), "f16": (2e-3, 1e-2), "bf16": (2e-3, 1e-2)}
 EDGE_LENS = (1, 2, 15, 16, 17, 31, 33, 64, 255, 257, 700)
 

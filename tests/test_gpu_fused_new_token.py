@@ -17,6 +17,13 @@ from workloads.device import upload
 
 pytestmark = pytest.mark.gpu
 
+
+@pytest.fixture(autouse=True)
+def small_partitions(monkeypatch):
+    """The grouped low-precision kernels split at no less than 2048 tokens by default; these
+    tests exercise the caller's own small partitions (the floor has its own tests)."""
+    monkeypatch.setenv("PKV_LP_MIN_PART", "0")
+
 TOL = {"f16": (2e-3, 1e-2), "bf16": (2e-3, 1e-2)}
 # context lengths n: the new token sits at n - 1
 LENS = (1, 2, 16, 17, 32, 33, 48, 49, 64, 65, 100)

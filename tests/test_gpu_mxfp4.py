@@ -17,6 +17,13 @@ from workloads.device import to_tensor, upload
 
 pytestmark = pytest.mark.gpu
 
+
+@pytest.fixture(autouse=True)
+def small_partitions(monkeypatch):
+    """The grouped low-precision kernels split at no less than 2048 tokens by default; these
+    tests exercise the caller's own small partitions (the floor has its own tests)."""
+    monkeypatch.setenv("PKV_LP_MIN_PART", "0")
+
 TOL = {"f32": (1e-5, 1e-5), "f16": (2e-3, 1e-2), "bf16": (2e-3, 1e-2)}
 EDGE_LENS = (1, 2, 15, 16, 17, 31, 33, 64, 255, 257, 700)
 # (kernel kind, waves, blocks per chunk or in flight): kind 0 = per-head vector-unit kernel
@@ -229,3 +236,27 @@ def test_mxfp4_bad_metadata_gives_nan_rows(torch_dev):
     t.cuda.synchronize()
     o = out.cpu().numpy()
     assert np.all(np.isfinite(o[0])) and np.all(np.isnan(o[1])) and np.all(np.isnan(o[2]))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_grouped_partition_floor(torch_dev, monkeypatch, dtype):
+    """Default plan: the grouped MXFP4 kernel splits at no less than 2048 tokens (a multiple of
+    the caller's partition), unsplit when that covers every context; both it and the caller's
+    own partitions (PKV_LP_MIN_PART=0) match the oracle, fused step pools bit-exact."""
+    torch = torch_dev
+    lens = (1, 17, 2047, 2048, 2049, 4500, 700)
+    for P, want in ((32, 2048), (1024, 2048), (3008, 3008)):
+        cfg = cfg_for(dtype, 128, 16, 2, lens, P=P, append=True)
+        w = make_workload(cfg, seed=81 + P)
+        ref, kp, vp = oracle.run_step(w)
+        for floor in (None, "0"):
+            if floor is None:
+                monkeypatch.delenv("PKV_LP_MIN_PART", raising=False)
+            else:
+                monkeypatch.setenv("PKV_LP_MIN_PART", floor)
+            got, d = run(torch, w, P, True)
+            launch = pkv.last_launch()
+            part = want if floor is None else P
+            assert launch.startswith("mxfp4_mfma ") and f"part_tokens={part} " in launch, launch
+            assert_close(got, ref, dtype, f"P={P} floor={floor} [{launch}]")
+            assert pools_equal(d, kp, vp), launch

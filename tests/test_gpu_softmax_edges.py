@@ -62,12 +62,13 @@ FAMILIES = [
     ("gqa_even_f16", "", "f16", 8, {"PKV_GQA_EVEN": "2"}, "gqa_mfma_even "),
     ("fp8_f16", "fp8", "f16", 1, {}, "fp8 "),
     ("fp8_f32_grouped", "fp8", "f32", 2, {}, "fp8 "),
-    ("fp8_grouped_bf16", "fp8", "bf16", 8, {}, "gqa_mfma_fp8 "),
+    ("fp8_grouped_bf16", "fp8", "bf16", 8, {"PKV_LP_MIN_PART": "0"}, "gqa_mfma_fp8 "),
     ("fp8_grouped_regk_f16", "fp8", "f16", 8, {"PKV_GQA8_KDMA": "0"}, "gqa_mfma_fp8 "),
     ("mxfp4_head_bf16", "mxfp4", "bf16", 1, {}, "mxfp4 "),
     ("mxfp4_head_f32", "mxfp4", "f32", 2, {}, "mxfp4 "),
-    ("mxfp4_mfma_bf16", "mxfp4", "bf16", 8, {}, "mxfp4_mfma "),
-    ("mxfp4_mfma_f16", "mxfp4", "f16", 8, {}, "mxfp4_mfma "),
+    ("mxfp4_mfma_bf16", "mxfp4", "bf16", 8, {"PKV_LP_MIN_PART": "0"}, "mxfp4_mfma "),
+    ("mxfp4_mfma_f16", "mxfp4", "f16", 8, {"PKV_LP_MIN_PART": "0"}, "mxfp4_mfma "),
+    ("mxfp4_mfma_floor_bf16", "mxfp4", "bf16", 8, {}, "mxfp4_mfma "),
 ]
 
 
@@ -358,13 +359,15 @@ def _variant_env(kind, v):
         return {"PKV_MHA_NW": str(nw), "PKV_MHA_CH": str(ch), "PKV_MHA_PF": str(pf)}, f"nw={nw} ch={ch} pf={pf}"
     if kind == "fp8g":
         nw, ch, pf, wpe, kd = v.split(",")
-        return ({"PKV_GQA8_NW": nw, "PKV_GQA8_CH": ch, "PKV_GQA8_PF": pf, "PKV_GQA8_WPE": wpe, "PKV_GQA8_KDMA": kd},
+        return ({"PKV_GQA8_NW": nw, "PKV_GQA8_CH": ch, "PKV_GQA8_PF": pf, "PKV_GQA8_WPE": wpe, "PKV_GQA8_KDMA": kd,
+                 "PKV_LP_MIN_PART": "0"},
                 f"nw={nw} ch={ch} pf={pf} wpe={wpe}" + (" kdma" if kd == "1" else "") + " ")
     if kind == "fp8":
         nw, ch, pf = v.split(",")
         return {"PKV_FP8_NW": nw, "PKV_FP8_CH": ch, "PKV_FP8_PF": pf}, f"nw={nw} ch={ch} pf={pf}"
     k, nw, x = v.split(",")
-    env = {"PKV_MX4_KIND": k, "PKV_MX4_NW": nw, ("PKV_MX4_PF" if k == "1" else "PKV_MX4_CH"): x}
+    env = {"PKV_MX4_KIND": k, "PKV_MX4_NW": nw, ("PKV_MX4_PF" if k == "1" else "PKV_MX4_CH"): x,
+           "PKV_LP_MIN_PART": "0"}
     return env, (f"nw={nw} ch=1 pf={x} " if k == "1" else f"nw={nw} ch={x} ")
 
 
