@@ -286,7 +286,9 @@ def cumask_bench(args) -> int:
     cmd = [prog, "sweep", cfg.dtype, str(cfg.B), str(cfg.H_q), str(cfg.H_kv), str(cfg.D), str(P),
            "1" if append else "0", repr(float(factor)), str(seed), str(max(args.steps // 4, 20)),
            ",".join(str(int(x)) for x in lens)]
-    r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=900)
+    # the program's own RUNPATH ($ORIGIN, /opt/rocm/lib) picks its libraries, not an inherited search path
+    env = {k: v for k, v in os.environ.items() if k != "LD_LIBRARY_PATH"}
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=900, env=env)
     if r.returncode != 0:
         print(json.dumps({"error": f"pkv_cumask exited with {r.returncode}"}))
         return r.returncode

@@ -9,6 +9,7 @@ touches the GPU and sends it one JSON request per line,
 {"rc": ..., "stdout": ..., "stderr": ...}.
 """
 import json
+import os
 import subprocess
 import sys
 
@@ -17,7 +18,9 @@ def main():
     for line in sys.stdin:
         req = json.loads(line)
         try:
-            r = subprocess.run(req["cmd"], capture_output=True, text=True, timeout=req.get("timeout", 120))
+            # the program's own RUNPATH picks its libraries, not an inherited search path
+            env = {k: v for k, v in os.environ.items() if k != "LD_LIBRARY_PATH"}
+            r = subprocess.run(req["cmd"], capture_output=True, text=True, timeout=req.get("timeout", 120), env=env)
             res = {"rc": r.returncode, "stdout": r.stdout, "stderr": r.stderr}
         except subprocess.TimeoutExpired as e:
             res = {"rc": 124, "stdout": e.stdout or "", "stderr": f"timed out after {e.timeout} s"}
