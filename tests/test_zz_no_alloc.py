@@ -55,9 +55,16 @@ PAIRS = [
 ]
 
 
-@pytest.mark.parametrize("pair", PAIRS, ids=[f"{a[0]}-{b[0]}" for a, b in PAIRS])
-def test_noalloc_matches_workspace_entry_point(torch_dev, pair):
+# the even split of the grouped kernel keeps its prefix and pieces in the array too
+EVEN = [(("c5", dict(B=12, lengths=("uniform", 4096, 16384)), 1024), ("c5", dict(B=5, lengths=("fixed", (1, 17, 700, 3000, 5000))), 256))]
+
+
+@pytest.mark.parametrize("pair,env", [(p, {}) for p in PAIRS] + [(p, {"PKV_GQA_EVEN": "2"}) for p in EVEN],
+                         ids=[f"{a[0]}-{b[0]}" for a, b in PAIRS] + ["c5-c5-even"])
+def test_noalloc_matches_workspace_entry_point(torch_dev, monkeypatch, pair, env):
     torch = torch_dev
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
     lib = pkv.load_library()
     for name, over, P in pair:
         cfg = get_config(name, append=True, **over)
@@ -71,6 +78,7 @@ def test_noalloc_matches_workspace_entry_point(torch_dev, pair):
         print(f"{name} B={cfg.B} P={P} partials={need} B", flush=True)
         assert _call(lib, lib.pkv_append_decode_attention, w, d1, P, out1, ws) == 0
         launch = pkv.last_launch()
+        assert ("gqa_mfma_even " in launch) == bool(env), launch
         rc = _call(lib, lib.pkv_append_decode_attention_noalloc, w, d2, P, out2)
         assert rc == 0, lib.pkv_last_error().decode()
         assert pkv.last_launch() == launch
