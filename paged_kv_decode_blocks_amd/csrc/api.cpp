@@ -153,30 +153,35 @@ Plan make_plan(int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32
         if (!pkv::gqa_variant_exists(p.kind, p.nw, p.ch, p.pf)) { p.kind = 2; p.nw = 4; p.ch = 1; p.pf = 1; }
         // A split step over a batch of mixed lengths: the even split (kernel 1e) cuts the
         // batch's blocks into equal runs, one wave per (run, KV head), one resident round of
-        // waves for the whole batch.  Its pieces and the merge's prefix fit the split's
-        // workspace: pieces <= (runs + B) * H_kv, G rows each, after B + 3 ints.
+        // waves for the whole batch, nw runs (a super-run) per workgroup.  Its pieces and the
+        // merge's prefix fit the split's workspace: pieces <= (super-runs + B) * H_kv, G rows
+        // each, after B + 3 ints.
         const int even_nw = env_int("PKV_GQA_EVEN_NW", 4), even_pf = env_int("PKV_GQA_EVEN_PF", 1);
         if (spans && p.n_parts > 1 && p.kind == 2 && env_int("PKV_GQA_EVEN", 1) && B <= pkv::kEvenMaxBatch &&
             pkv::gqa_even_variant_exists(even_nw, even_pf)) {
             const int64_t worst = (int64_t)B * ((max_ctx + pkv::kBlockSize - 1) / pkv::kBlockSize);   // per head
-            const int64_t cap = ((int64_t)B * H_q * p.n_parts - B - 3) / H_q - B;
+            const int64_t cap = (((int64_t)B * H_q * p.n_parts - B - 3) / H_q - B) * even_nw;
             const int64_t need = (worst + pkv::kEvenMaxWaveBlocks - 1) / pkv::kEvenMaxWaveBlocks;
             const int64_t resident = even_resident_waves(dtype, D, even_nw, even_pf, fused) / H_kv;
             const int64_t want = std::max(resident * std::max(1, env_int("PKV_GQA_EVEN_ROUNDS", 1)), need);
             const int64_t runs = std::min(want, cap);
-            // a few long requests: each row would be merged from dozens of pieces (slower
-            // than nw-partition spans on MI355X for B <= 4 of 8 KV heads); and a workspace
-            // too small for most of a round of runs: far fewer waves than the GPU holds.  The
-            // even split takes batches with at most ~16 runs per request on average and at
-            // least 3/4 of a round.
-            const bool fits = ((int64_t)B * 16 >= runs && 4 * runs >= 3 * want) || env_int("PKV_GQA_EVEN", 1) == 2;
+            // The even split takes batches whose worst case holds at least 64 blocks per run
+            // (shorter runs pay their per-piece start-up and the merge launch: on MI355X 8
+            // requests of 1-16 K tokens, 32 blocks per run, ran 5 % slower, 8 of 4-32 K, 64 per
+            // run, 13 % faster, one or two requests of 32-128 K, 16-32 per run, 3-15 % slower),
+            // room for 3/4 of a round of runs in the workspace, and contexts that the
+            // nw-partition spans would need the merge kernel for anyway (when one span covers
+            // every context they need none: 64 requests of 2048 tokens ran 86 vs 101 us that way).
+            const bool spans_merge = (int64_t)max_ctx > (int64_t)p.nw * partition_size;
+            const bool fits = (worst >= 64 * runs && 4 * runs >= 3 * want && spans_merge) ||
+                              env_int("PKV_GQA_EVEN", 1) == 2;
             if (resident > 0 && fits && runs >= need && runs >= 1 && worst < (int64_t)1 << 30 &&
                 runs * H_kv < (int64_t)1 << 30) {
                 p.nw = even_nw;
                 p.ch = 1;
                 p.pf = even_pf;
                 p.even_waves = (int32_t)(runs * H_kv);
-                p.grid = (unsigned)((runs * H_kv + even_nw - 1) / even_nw);
+                p.grid = (unsigned)((runs + even_nw - 1) / even_nw * H_kv);
             }
         }
         // A split context: one workgroup spans nw consecutive partitions and wave w streams
@@ -419,6 +424,7 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
     a.part_rev = env_int("PKV_PART_REV", 1) != 0;
     if (p.even_waves) {   // the lse area starts with the merge's prefix: [tw, waves, blocks before b (B + 1)]
         a.even_waves = p.even_waves;
+        a.even_min_run = env_int("PKV_GQA_EVEN_MINRUN", pkv::kEvenMinWaveBlocks);
         a.even_meta = reinterpret_cast<int32_t*>(a.part_lse);
         a.part_lse += B + 3;
     }

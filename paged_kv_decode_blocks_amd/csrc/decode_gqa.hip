@@ -642,25 +642,29 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_kernel(const AttnArgs a) {
 // registers, one block per chunk) over an even split of the whole batch.
 //
 // The requests' blocks are laid end to end (request order) and cut into `runs`
-// equal runs of tw blocks; wave v streams run r = v / H_kv for KV head
-// g = v % H_kv.  Every wave gets the same number of blocks whatever the length
-// mix, so no workgroup is left running alone at the end, and the H_kv waves of a
-// run read the same blocks at the same time (their tiles are neighbours in each
-// pool block).  A wave walks the pieces of its run (its overlap with each
-// request) with a fresh softmax state per piece and writes each piece as
-// (o / l, log2 l + m) for its G query heads, or the output itself when the piece
-// is the request's whole context.  The log-sum-exp merge of a row's pieces
-// (lse_merge.hip) is the same exact regrouping of the softmax sum as for split
-// partitions.
+// equal runs of tw blocks.  Workgroup (S, g) takes super-run S -- runs S NW ..
+// S NW + NW - 1 -- for KV head g, wave w streaming run S NW + w: every wave gets
+// the same number of blocks whatever the length mix, so no workgroup is left
+// running alone at the end, and the H_kv workgroups of a super-run (neighbours in
+// the grid, started together) read the same blocks at the same time, their tiles
+// neighbours in each pool block.  A wave walks the pieces of its run (its overlap
+// with each request) with a fresh softmax state each; a piece that is a whole
+// request is written as the output at once.  The others -- a run's first piece,
+// if it starts inside a request, and its last, if it ends inside one -- are kept
+// in LDS, and at the end wave 0 merges them in token order: the pieces of one
+// request within the super-run become one (the log-sum-exp regrouping of the
+// softmax sum, as for split partitions), written as the output if they cover the
+// request, else as the super-run's piece (o / l, log2 l + m) for the merge kernel.
 //
-// Piece of run r in request b for KV head g: id (r + b) H_kv + g (a run and a
-// request meet in one interval, and along the end-to-end order r and b only
-// grow, so r + b names each meeting once); its rows are part_o[(((r + b) H_kv +
-// g) G + h) D ...] and part_lse[((r + b) H_kv + g) G + h].
+// Piece of super-run S in request b for KV head g: id (S + b) H_kv + g (a
+// super-run and a request meet in one interval, and along the end-to-end order S
+// and b only grow, so S + b names each meeting once); its rows are
+// part_o[(((S + b) H_kv + g) G + h) D ...] and part_lse[((S + b) H_kv + g) G + h].
 //
 // Every workgroup prefix-sums the requests' block counts in LDS (lengths out of
 // range count as empty: the merge writes their NaN rows, and empty rows' zeros);
-// workgroup 0 also stores tw, the runs used and the prefix for the merge.
+// workgroup 0 also stores NW tw (the super-run length), the runs used and the
+// prefix for the merge.
 // ---------------------------------------------------------------------------
 template <int DT, int D, int NW, int PF, bool APPEND>
 __global__ __launch_bounds__(NW * 64) void decode_gqa_even_kernel(const AttnArgs a) {
@@ -678,10 +682,22 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_even_kernel(const AttnArgs
     __shared__ int32_t s_pre[PER * T];
     __shared__ int32_t s_scan[T];
     __shared__ int32_t s_wid[NW][kEvenMaxWaveBlocks];
+    // a run's first piece, when it starts inside a request: its state ([VT * 4][64], lane-minor);
+    // its last piece, when it ends inside one, goes to the wave's ring once the wave is done
+    constexpr int STATE = VT * 4 * 64;                      // floats of one piece's state
+    static_assert(R * TILE >= STATE * 4, "a piece's state fits the wave's ring");
+    __shared__ float s_first[NW][STATE];
+    __shared__ float s_ml[NW][2][2][16];                    // [wave][first, last][m, l][head]
+    __shared__ int s_req[NW][2];                            // request of each kept piece, -1 = none
+    __shared__ int s_flags[NW][2];                          // 1 starts the request, 2 ends it, 4 bad id
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (lane == 0) {
+        s_req[w][0] = -1;
+        s_req[w][1] = -1;
+    }
 
     // block counts of requests tid * PER ..., prefix-summed over the workgroup
     int loc[PER];
@@ -713,167 +729,244 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_even_kernel(const AttnArgs
     __syncthreads();
 
     const int total = s_pre[a.B];   // blocks per KV head over the batch (the host keeps it below 2^30)
-    const int runs = max(1, min(a.even_waves / a.H_kv, (total + kEvenMinWaveBlocks - 1) / kEvenMinWaveBlocks));
+    const int min_run = max(kEvenMinWaveBlocks, a.even_min_run);
+    const int runs = max(1, min(a.even_waves / a.H_kv, (total + min_run - 1) / min_run));
     const int tw = max(1, (total + runs - 1) / runs);   // <= kEvenMaxWaveBlocks (host sizing)
     if (blockIdx.x == 0) {
         for (int b = tid; b <= a.B; b += T) a.even_meta[2 + b] = s_pre[b];
         if (tid == 0) {
-            a.even_meta[0] = tw;
+            a.even_meta[0] = NW * tw;
             a.even_meta[1] = runs;
         }
     }
-    const int v = blockIdx.x * NW + w;
-    const int run = v / a.H_kv, g = v - run * a.H_kv;
-    int x0 = run * tw;
+    const int S = blockIdx.x / a.H_kv, g = blockIdx.x - S * a.H_kv;
+    const int run = S * NW + w;
+    const int run0 = run * tw;
+    int x0 = run0;
     const int x1 = min(x0 + tw, total);
-    if (run >= runs || x0 >= x1) return;   // no barrier follows
-
-    // the request holding block x0: the last one whose blocks start at or before it
-    int b;
-    {
-        int lo = 0, hi = a.B - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_pre[mid] <= x0) lo = mid;
-            else hi = mid - 1;
-        }
-        b = __builtin_amdgcn_readfirstlane(lo);
-    }
-
-    const size_t blk_bytes = (size_t)a.H_kv * kBlockSize * D * ES;
     const size_t head_bytes = (size_t)g * kBlockSize * D * ES;
-    const char* kpool = a.k_pool + head_bytes;
-    const char* vpool = a.v_pool + head_bytes;
     char* ring = s_ring + w * R * TILE;
-    int32_t* wid = s_wid[w];
-    int kdma[NDMA], kread[KS];
     L st;
-    while (x0 < x1) {
-        const int seg0 = __builtin_amdgcn_readfirstlane(s_pre[b]);
-        const int nbb = __builtin_amdgcn_readfirstlane(s_pre[b + 1]) - seg0;
-        const int pend = min(x1, seg0 + nbb);
-        const int blk0 = x0 - seg0, np = pend - x0;   // the piece: blocks [blk0, blk0 + np) of request b
-        const bool whole = blk0 == 0 && np == nbb;
-        const int piece = (run + b) * a.H_kv + g;
-        const int n = APPEND ? a.positions[b] + 1 : a.context_lens[b];
-        const int lim = APPEND ? n - 1 : n;   // tokens below lim come from the pools
-        const int pos_new = (APPEND && blk0 + np == nbb) ? n - 1 : -1;
-
-        st.init(a, lane, b, g);   // q of the row's G heads; fresh softmax state
-#pragma unroll
-        for (int i = 0; i < NDMA; ++i) {
-            const int slot16 = i * 64 + lane;
-            const int row = slot16 / CPR, p = slot16 % CPR;
-            kdma[i] = row * D * ES + ((p ^ (row % CPR)) * 16);
-        }
-#pragma unroll
-        for (int q = 0; q < KS; ++q) kread[q] = st.tau * D * ES + (((4 * q + st.j) ^ (st.tau % CPR)) * 16);
-
-        // the piece's block ids, range-checked, into the wave's LDS list
-        const int32_t* table = a.block_tables + (int64_t)b * a.bt_stride + blk0;
-        bool bad_lane = false;
-        for (int t = lane; t < np; t += 64) {
-            int id = table[t];
-            if ((unsigned)id >= (unsigned)a.n_blocks) {
-                bad_lane = true;
-                id = 0;
+    if (run < runs && x0 < x1) {   // else nothing to stream (the workgroup's closing merge follows)
+        // the request holding block x0: the last one whose blocks start at or before it
+        int b;
+        {
+            int lo = 0, hi = a.B - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_pre[mid] <= x0) lo = mid;
+                else hi = mid - 1;
             }
-            wid[t] = id;
+            b = __builtin_amdgcn_readfirstlane(lo);
         }
-        const bool bad = __builtin_amdgcn_ballot_w64(bad_lane) != 0;
-        // the wave's LDS operations complete in order; the fence keeps the compiler from
-        // moving the list's reads above its writes
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();
 
-        const size_t new_off = ((size_t)b * a.new_row_stride + (size_t)g * D) * ES;
-        struct Buf {
-            uint4 k[1][KS];
-            VRow<NWORD> v[1][4];
-        };
-        auto load_blk = [&](int slot, Buf& bf, int i) {
-            const size_t id = (size_t)__builtin_amdgcn_readfirstlane(wid[i]);
-#pragma unroll
-            for (int q = 0; q < NDMA; ++q) dma16(kpool + id * blk_bytes + kdma[q], ring + slot * TILE + q * 1024);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) bf.v[0][r] = ldv<NWORD>(vpool + id * blk_bytes + st.voff[r]);
-        };
-        bool all_valid[1][4] = {{true, true, true, true}};
-        // steady: exactly PF later blocks' loads were issued after this block's
-        auto consume = [&](int slot, Buf& bf, bool steady) {
-            if (steady) wait_vmcnt<PF * LPC>();
-            else wait_vmcnt<0>();
-            lds_read16x<KS>(ring + slot * TILE, kread, bf.k[0]);
-            st.template accumulate<1>(bf.k, bf.v, all_valid);
-        };
+        const size_t blk_bytes = (size_t)a.H_kv * kBlockSize * D * ES;
+        const char* kpool = a.k_pool + head_bytes;
+        const char* vpool = a.v_pool + head_bytes;
+        int32_t* wid = s_wid[w];
+        int kdma[NDMA], kread[KS];
+        while (x0 < x1) {
+            const int seg0 = __builtin_amdgcn_readfirstlane(s_pre[b]);
+            const int nbb = __builtin_amdgcn_readfirstlane(s_pre[b + 1]) - seg0;
+            const int pend = min(x1, seg0 + nbb);
+            const int blk0 = x0 - seg0, np = pend - x0;   // the piece: blocks [blk0, blk0 + np) of request b
+            const bool whole = blk0 == 0 && np == nbb;
+            const int n = APPEND ? a.positions[b] + 1 : a.context_lens[b];
+            const int lim = APPEND ? n - 1 : n;   // tokens below lim come from the pools
+            const int pos_new = (APPEND && blk0 + np == nbb) ? n - 1 : -1;
 
-        // blocks wholly below lim, pipelined; block i lives in buffer and ring slot i % R
-        const int nf = max(0, min(blk0 + np, lim / kBlockSize) - blk0);
-        Buf buf[R];
-        int i = 0;
-        if (nf >= R + PF) {
+            st.init(a, lane, b, g);   // q of the row's G heads; fresh softmax state
 #pragma unroll
-            for (int u = 0; u < PF; ++u) load_blk(u, buf[u], u);
-            for (; i + R + PF <= nf; i += R) {
+            for (int i = 0; i < NDMA; ++i) {
+                const int slot16 = i * 64 + lane;
+                const int row = slot16 / CPR, p = slot16 % CPR;
+                kdma[i] = row * D * ES + ((p ^ (row % CPR)) * 16);
+            }
+#pragma unroll
+            for (int q = 0; q < KS; ++q) kread[q] = st.tau * D * ES + (((4 * q + st.j) ^ (st.tau % CPR)) * 16);
+
+            // the piece's block ids, range-checked, into the wave's LDS list
+            const int32_t* table = a.block_tables + (int64_t)b * a.bt_stride + blk0;
+            bool bad_lane = false;
+            for (int t = lane; t < np; t += 64) {
+                int id = table[t];
+                if ((unsigned)id >= (unsigned)a.n_blocks) {
+                    bad_lane = true;
+                    id = 0;
+                }
+                wid[t] = id;
+            }
+            const bool bad = __builtin_amdgcn_ballot_w64(bad_lane) != 0;
+            // the wave's LDS operations complete in order; the fence keeps the compiler from
+            // moving the list's reads above its writes
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+
+            const size_t new_off = ((size_t)b * a.new_row_stride + (size_t)g * D) * ES;
+            struct Buf {
+                uint4 k[1][KS];
+                VRow<NWORD> v[1][4];
+            };
+            auto load_blk = [&](int slot, Buf& bf, int i) {
+                const size_t id = (size_t)__builtin_amdgcn_readfirstlane(wid[i]);
+#pragma unroll
+                for (int q = 0; q < NDMA; ++q) dma16(kpool + id * blk_bytes + kdma[q], ring + slot * TILE + q * 1024);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) bf.v[0][r] = ldv<NWORD>(vpool + id * blk_bytes + st.voff[r]);
+            };
+            bool all_valid[1][4] = {{true, true, true, true}};
+            // steady: exactly PF later blocks' loads were issued after this block's
+            auto consume = [&](int slot, Buf& bf, bool steady) {
+                if (steady) wait_vmcnt<PF * LPC>();
+                else wait_vmcnt<0>();
+                lds_read16x<KS>(ring + slot * TILE, kread, bf.k[0]);
+                st.template accumulate<1>(bf.k, bf.v, all_valid);
+            };
+
+            // blocks wholly below lim, pipelined; block i lives in buffer and ring slot i % R
+            const int nf = max(0, min(blk0 + np, lim / kBlockSize) - blk0);
+            Buf buf[R];
+            int i = 0;
+            if (nf >= R + PF) {
+#pragma unroll
+                for (int u = 0; u < PF; ++u) load_blk(u, buf[u], u);
+                for (; i + R + PF <= nf; i += R) {
+#pragma unroll
+                    for (int u = 0; u < R; ++u) {
+                        load_blk((u + PF) % R, buf[(u + PF) % R], i + u + PF);
+                        consume(u, buf[u], true);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < PF; ++u)
+                    if (u < nf) load_blk(u, buf[u], u);
+            }
+            for (; i < nf; i += R) {
 #pragma unroll
                 for (int u = 0; u < R; ++u) {
-                    load_blk((u + PF) % R, buf[(u + PF) % R], i + u + PF);
-                    consume(u, buf[u], true);
+                    if (i + u < nf) {
+                        if (i + u + PF < nf) load_blk((u + PF) % R, buf[(u + PF) % R], i + u + PF);
+                        consume(u, buf[u], false);
+                    }
                 }
             }
-        } else {
-#pragma unroll
-            for (int u = 0; u < PF; ++u)
-                if (u < nf) load_blk(u, buf[u], u);
-        }
-        for (; i < nf; i += R) {
-#pragma unroll
-            for (int u = 0; u < R; ++u) {
-                if (i + u < nf) {
-                    if (i + u + PF < nf) load_blk((u + PF) % R, buf[(u + PF) % R], i + u + PF);
-                    consume(u, buf[u], false);
-                }
+            // the rest (the row's last block, holding the length boundary and the new token)
+            for (int k = nf; k < np; ++k) {
+                const int id = __builtin_amdgcn_readfirstlane(wid[k]);
+                const char* kb = a.k_pool + (size_t)id * blk_bytes + head_bytes;
+                const char* vb = a.v_pool + (size_t)id * blk_bytes + head_bytes;
+                st.partial_block(a, kb, vb, (blk0 + k) * kBlockSize, lim, pos_new, new_off, !bad);
             }
-        }
-        // the rest (the row's last block, holding the length boundary and the new token)
-        for (int k = nf; k < np; ++k) {
-            const int id = __builtin_amdgcn_readfirstlane(wid[k]);
-            const char* kb = a.k_pool + (size_t)id * blk_bytes + head_bytes;
-            const char* vb = a.v_pool + (size_t)id * blk_bytes + head_bytes;
-            st.partial_block(a, kb, vb, (blk0 + k) * kBlockSize, lim, pos_new, new_off, !bad);
-        }
 
-        // the piece's result for its G heads (lane (j, col): head col, d = (4 j + i) VT + t)
-        float l = st.l;
-        l += __shfl_xor(l, 16, 64);
-        l += __shfl_xor(l, 32, 64);
-        if (st.col < a.G) {
-            const size_t row = (size_t)b * a.H_q + (size_t)g * a.G + st.col;
-            float* dst = whole ? a.out + row * D : a.part_o + ((size_t)piece * a.G + st.col) * D;
+            // the piece's result for its G heads (lane (j, col): head col, d = (4 j + i) VT + t)
+            float l = st.l;
+            l += __shfl_xor(l, 16, 64);
+            l += __shfl_xor(l, 32, 64);
+            if (whole) {
+                if (st.col < a.G) {
+                    float* o0 = a.out + ((size_t)b * a.H_q + (size_t)g * a.G + st.col) * D;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float* o = dst + (4 * st.j + r) * VT;
+                    for (int r = 0; r < 4; ++r) {
+                        float* o = o0 + (4 * st.j + r) * VT;
 #pragma unroll
-                for (int t = 0; t < VT; t += 4) {
-                    floatx4 val;
+                        for (int t = 0; t < VT; t += 4) {
+                            floatx4 val;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) val[e] = bad ? __builtin_nanf("") : st.acc[t + e][r] / l;
-                    *reinterpret_cast<floatx4*>(o + t) = val;
+                            for (int e = 0; e < 4; ++e) val[e] = bad ? __builtin_nanf("") : st.acc[t + e][r] / l;
+                            *reinterpret_cast<floatx4*>(o + t) = val;
+                        }
+                    }
+                }
+            } else {
+                // the run's first piece (starts the run), or its last (the run ends inside the
+                // request; nothing streams through the ring after it)
+                const int k = x0 == run0 ? 0 : 1;
+                float* dst = k == 0 ? s_first[w] : reinterpret_cast<float*>(ring);
+#pragma unroll
+                for (int t = 0; t < VT; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dst[(t * 4 + r) * 64 + lane] = st.acc[t][r];
+                if (st.j == 0) {
+                    s_ml[w][k][0][st.col] = st.m;
+                    s_ml[w][k][1][st.col] = l;
+                }
+                if (lane == 0) {
+                    s_req[w][k] = b;
+                    s_flags[w][k] = (blk0 == 0 ? 1 : 0) | (blk0 + np == nbb ? 2 : 0) | (bad ? 4 : 0);
                 }
             }
-            // v_log_f32 is log base 2, matching the log2-domain scores
-            if (!whole && st.j == 0)
-                a.part_lse[(size_t)piece * a.G + st.col] = bad ? __builtin_nanf("") : st.m + __builtin_amdgcn_logf(l);
-        }
 
-        x0 = pend;
-        if (x0 < x1) {   // the next request with blocks
-            do {
-                ++b;
-            } while (s_pre[b + 1] == s_pre[b]);
-            b = __builtin_amdgcn_readfirstlane(b);
+            x0 = pend;
+            if (x0 < x1) {   // the next request with blocks
+                do {
+                    ++b;
+                } while (s_pre[b + 1] == s_pre[b]);
+                b = __builtin_amdgcn_readfirstlane(b);
+            }
         }
     }
+
+    // Wave 0 merges the kept pieces in token order (wave by wave, first piece before
+    // last); consecutive pieces of one request combine by the log-sum-exp regrouping.
+    __syncthreads();
+    if (w != 0) return;
+    const int col = lane & 15, j = lane >> 4;
+    floatx4 O[VT];
+    float M = 0.0f, Lsum = 0.0f;
+    int cur = -1, flags = 0;
+    auto flush = [&]() {
+        if (col >= a.G) return;
+        const bool covers = (flags & 3) == 3;     // the pieces start and end the request
+        const bool badr = (flags & 4) != 0;
+        const size_t pid = ((size_t)(S + cur) * a.H_kv + g) * a.G + col;
+        float* o0 = covers ? a.out + ((size_t)cur * a.H_q + (size_t)g * a.G + col) * D : a.part_o + pid * D;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float* o = o0 + (4 * j + r) * VT;
+#pragma unroll
+            for (int t = 0; t < VT; t += 4) {
+                floatx4 val;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) val[e] = badr ? __builtin_nanf("") : O[t + e][r] / Lsum;
+                *reinterpret_cast<floatx4*>(o + t) = val;
+            }
+        }
+        // v_log_f32 is log base 2, matching the log2-domain scores
+        if (!covers && j == 0) a.part_lse[pid] = badr ? __builtin_nanf("") : M + __builtin_amdgcn_logf(Lsum);
+    };
+    for (int ww = 0; ww < NW; ++ww) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int rq = s_req[ww][k];
+            if (rq < 0) continue;
+            const float* src = k == 0 ? s_first[ww] : reinterpret_cast<const float*>(s_ring + ww * R * TILE);
+            const float mi = s_ml[ww][k][0][col], li = s_ml[ww][k][1][col];
+            const int fi = s_flags[ww][k];
+            if (rq != cur) {
+                if (cur >= 0) flush();
+                cur = rq;
+                flags = fi;
+                M = mi;
+                Lsum = li;
+#pragma unroll
+                for (int t = 0; t < VT; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) O[t][r] = src[(t * 4 + r) * 64 + lane];
+            } else {
+                flags = (flags & 1) | (fi & 2) | ((flags | fi) & 4);
+                const float Mn = fmaxf(M, mi);
+                const float c0 = __builtin_amdgcn_exp2f(M - Mn), c1 = __builtin_amdgcn_exp2f(mi - Mn);
+                M = Mn;
+                Lsum = Lsum * c0 + li * c1;
+#pragma unroll
+                for (int t = 0; t < VT; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) O[t][r] = O[t][r] * c0 + src[(t * 4 + r) * 64 + lane] * c1;
+            }
+        }
+    }
+    if (cur >= 0) flush();
 }
 
 // ---------------------------------------------------------------------------

@@ -96,9 +96,9 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeArgs a) {
 }
 
 // Even split (a.even_meta set): four (request, head) rows per 4-wave workgroup.
-// A row's pieces are those of runs r0 .. r1, the runs of tw blocks that meet the
-// request's blocks, with ids (r + b) H_kv + g (g the row's KV head); a row one
-// run covered was written by that run's wave.  Rows of at most kWideMerge pieces
+// A row's pieces are those of super-runs r0 .. r1, the super-runs of tw blocks
+// that meet the request's blocks, with ids (r + b) H_kv + g (g the row's KV
+// head); a row one super-run covered was written by that workgroup.  Rows of at most kWideMerge pieces
 // take a wave each; otherwise (a few long requests: a hundred pieces per row) the
 // four waves share each row in turn, wave w adding pieces w, w + 4, ..., and the
 // four sums are added in wave order.

@@ -19,7 +19,7 @@ constexpr int kMhaWindowTokens = 256 * kBlockSize;   // the same for the per-hea
 // Even split of a grouped batch (one run of blocks per wave, see decode_gqa.hip):
 constexpr int kEvenMaxBatch = 1024;       // requests whose block counts a workgroup prefix-sums in LDS
 constexpr int kEvenMaxWaveBlocks = 256;   // longest run of blocks one wave takes
-constexpr int kEvenMinWaveBlocks = 16;    // shortest run worth a wave of its own
+constexpr int kEvenMinWaveBlocks = 16;    // shortest run worth a wave of its own (default)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -3.0e38f;   // "no score yet": exp2(kNegBig - m) == 0 for any real m
 
@@ -219,8 +219,9 @@ struct AttnArgs {
     int32_t part_rev;              // split kernels: 1 = deal partitions from the last to the first
     int32_t even_waves;            // grouped kernel with K in LDS: > 0 = even split over at most this many
                                    // waves (part_o / part_lse then hold one row per piece and head)
-    int32_t* even_meta;            // even split: [0] blocks per wave, [1] waves used, [2 + b] blocks of
-                                   // requests 0 .. b-1 (b = 0 .. B)
+    int32_t* even_meta;            // even split: [0] blocks per workgroup's super-run, [1] runs used,
+                                   // [2 + b] blocks of requests 0 .. b-1 (b = 0 .. B)
+    int32_t even_min_run;          // even split: shortest run worth a wave of its own (blocks)
     float scale_log2;              // scale * log2(e)
 };
 

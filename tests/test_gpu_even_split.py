@@ -229,15 +229,17 @@ def test_even_split_merge_of_many_pieces_beside_short_rows(torch_dev, dtype, D):
     assert_close(got[good], ref[good], dtype, f"{dtype} D={D} [{launch}]")
 
 
-@pytest.mark.parametrize("B,even", [(32, True), (16, True), (4, False)])
-def test_default_plan_takes_the_even_split_for_enough_requests(torch_dev, monkeypatch, B, even):
-    """Default plan (no override): the even split for batches of at least 16 requests per 256
-    runs (8 KV heads) whose workspace holds 3/4 of a round of runs, nw-partition spans otherwise
-    (B = 4 here: few requests, and at P = 1024 over 8192 tokens room for only 27 runs); both
-    match the oracle.  The larger batches have c5's length range."""
+@pytest.mark.parametrize("B,lo,hi,even", [(32, 4096, 16384, True), (16, 4096, 16384, True), (8, 1024, 16384, False),
+                                           (8, 4096, 32768, True), (4, 4096, 8192, False)])
+def test_default_plan_takes_the_even_split_for_long_runs(torch_dev, monkeypatch, B, lo, hi, even):
+    """Default plan (no override, 8 KV heads, 256 runs of one resident round): the even split
+    when the batch's worst case -- B requests of the longest context -- holds at least 64
+    blocks per run (here B * hi / 16 >= 16384, the longest request being hi tokens), nw-partition
+    spans otherwise; both match the oracle."""
     monkeypatch.delenv("PKV_GQA_EVEN", raising=False)
-    lens = tuple(int(x) for x in np.random.default_rng(B).integers(4096, 16384 if B > 4 else 8192, size=B))
-    cfg = get_config("c5", B=B, lengths=("fixed", lens), pool=("factor", 1.1))
+    lens = [int(x) for x in np.random.default_rng(B + hi).integers(lo, hi, size=B)]
+    lens[0] = hi
+    cfg = get_config("c5", B=B, lengths=("fixed", tuple(lens)), pool=("factor", 1.1))
     w = make_workload(cfg, seed=780 + B)
     ref = oracle.paged_decode_attention("bf16", w.q, w.k_pool, w.v_pool, w.block_tables, w.context_lens, w.scale)
     got = attention(torch_dev, w, 1024)
