@@ -110,7 +110,8 @@ const char* pkv_last_error(void);
  * span of partitions, 1 = the even split of the batch's blocks into equal runs
  * where the plan finds it pays, 2 = wherever it applies) with PKV_GQA_EVEN_{NW,PF};
  * PKV_PART_REV (0 = deal partitions first to last instead of last to first; the
- * results are bit-identical).  A combination the library does not instantiate
+ * results are bit-identical); PKV_LP_MIN_PART (the grouped FP8 and MXFP4 kernels'
+ * smallest partition in tokens, 2048 by default, 0 = the caller's).  A combination the library does not instantiate
  * falls back to the default; results agree to the same tolerance for every
  * instantiated shape. */
 const char* pkv_last_launch(void);
