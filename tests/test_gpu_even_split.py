@@ -246,3 +246,16 @@ def test_default_plan_takes_the_even_split_for_long_runs(torch_dev, monkeypatch,
     launch = pkv.last_launch()
     assert launch.startswith("gqa_mfma_even " if even else "gqa_mfma_kdma "), launch
     assert_close(got, ref, "bf16", f"B={B} [{launch}]")
+
+
+def test_even_split_batch_with_no_blocks(torch_dev):
+    """Every request empty, then every length past max_context_len: the split streams nothing
+    (one run of nothing) and the merge writes zero rows, then NaN rows."""
+    cfg = get_config("c5", B=5, H_q=16, H_kv=2, lengths=("fixed", (40, 40, 40, 40, 40)), pool=("factor", 1.5))
+    w = make_workload(cfg, seed=790)
+    zero = np.zeros(5, dtype=np.int32)
+    got = attention(torch_dev, w, 32, ctx=zero, maxc=40)
+    assert pkv.last_launch().startswith("gqa_mfma_even "), pkv.last_launch()
+    assert np.array_equal(got, np.zeros_like(got))
+    got = attention(torch_dev, w, 32, ctx=np.full(5, 41, dtype=np.int32), maxc=40)
+    assert np.all(np.isnan(got))
