@@ -104,16 +104,18 @@ const char* pkv_last_error(void);
  * PKV_MHA_{NW,CH,PF} (per-head 16-bit), PKV_GQA_{KIND,NW,CH,PF} (grouped 16-bit;
  * KIND 0 = K in registers, 1 = K and V through LDS, 2 = K through LDS),
  * PKV_FP8_{NW,CH,PF} (per-head FP8), PKV_GQA8_{NW,CH,PF,WPE,KDMA} (grouped
- * FP8) and PKV_MX4_{KIND,NW,CH,PF} (MXFP4; KIND 0 = per query head on the
- * vector units, 1 = grouped heads on MFMA; CH for kind 0, PF for kind 1).
- * Split steps: PKV_GQA_EVEN (grouped 16-bit with K in LDS: 0 = one workgroup per
- * span of partitions, 1 = the even split of the batch's blocks into equal runs
- * where the plan finds it pays, 2 = wherever it applies) with PKV_GQA_EVEN_{NW,PF};
+ * FP8) and PKV_MX4_{KIND,NW,CH,PF,HG} (MXFP4; KIND 0 = per query head on the
+ * vector units, 1 = grouped heads on MFMA; CH for kind 0, PF and HG -- KV heads
+ * per workgroup -- for kind 1).
+ * Split steps: PKV_GQA_EVEN (grouped 16-bit with K in LDS) and PKV_MX4_EVEN
+ * (grouped MXFP4): 0 = one workgroup per partition or span of partitions, 1 = the
+ * even split of the batch's blocks into equal runs where the plan finds it pays,
+ * 2 = wherever it applies; with PKV_GQA_EVEN_{NW,PF} and PKV_MX4_EVEN_{NW,PF};
  * PKV_PART_REV (0 = deal partitions first to last instead of last to first; the
  * results are bit-identical); PKV_LP_MIN_PART (the grouped FP8 and MXFP4 kernels'
- * smallest partition in tokens, 2048 by default, 0 = the caller's).  A combination the library does not instantiate
- * falls back to the default; results agree to the same tolerance for every
- * instantiated shape. */
+ * smallest partition in tokens, 2048 by default, 0 = the caller's).  A combination
+ * the library does not instantiate falls back to the default; results agree to the
+ * same tolerance for every instantiated shape. */
 const char* pkv_last_launch(void);
 
 /*

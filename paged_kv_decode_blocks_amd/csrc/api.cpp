@@ -73,6 +73,7 @@ struct Plan {
     int32_t even_waves;   // grouped kernel: > 0 = even split of the batch over at most this many waves
     int wpe;          // grouped FP8 kernel: waves per SIMD its registers are sized for
     int kd;           // grouped FP8 kernel: K tiles staged through LDS (1) or loaded into registers (0)
+    int hg;           // grouped MXFP4 kernel: KV heads per workgroup
     unsigned grid;
     size_t ws_o, ws_lse, ws_total;
 };
@@ -276,6 +277,62 @@ int32_t coarsen_partitions(Plan& p, int32_t B, int32_t H_kv, int32_t max_ctx, in
     return (int32_t)pt;
 }
 
+// Workgroups of the grouped MXFP4 even-split kernel resident on the current device at
+// once (occupancy per CU times CUs), cached per device; 0 if the runtime cannot say.
+int64_t mx4_even_resident_wgs(int dtype, int32_t D, int nw, int pf, int G, bool fused) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    static std::mutex mu;
+    static std::map<std::tuple<int, int, int, int, bool, bool>, int64_t> cache;
+    const auto key = std::make_tuple(dev, dtype * 1000 + (int)D, nw, pf, G <= 8, fused);
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+    const int64_t n = (int64_t)pkv::mxfp4_even_wgs_per_cu(dtype, D, nw, pf, G, fused) * cus;
+    cache[key] = n;
+    return n;
+}
+
+// The grouped MXFP4 kernel's even split of a split step: the batch's blocks cut into
+// equal runs, a workgroup per (run, group of nw KV heads), one resident round (the runs
+// are sized so that a run is at most kEvenMaxWaveBlocks blocks and the pieces, ids
+// (run + request) H_kv + head, fit the caller's workspace).  PKV_MX4_EVEN: 0 never,
+// 2 whenever it fits, 1 (default) when the gate below holds; PKV_MX4_EVEN_NW / _PF pick
+// the variant (default 4 KV heads per workgroup, else 2 with two chunks in flight).
+// Returns whether the plan took it (p: nw, pf, hg, even_waves, grid).
+//
+// Gate, from MI355X against the per-partition kernel at its 2048-token floor (8 KV heads,
+// 64 query heads, D = 128, bf16 q, 4-head workgroups; ctx uniform in the range): 32 x
+// 4096-16384 +2 %, 48 x 4096-16384 +8.5 %, 64 x 1024-8192 +4 %, 24 x 8192-32768 +4 %;
+// 128 x 512-4096 -0.6 %, 32 x 2048-8192 -5 %, 16 x 4096-16384 -12 % (8-head workgroups
+// 0-3 % behind 4-head ones throughout).  The losing batches' worst case (B requests of the
+// longest context) is 64 blocks per run of one resident round, the winning ones' 125 or
+// more.  So: 4-head workgroups, a worst case of at least 96 blocks per run, and a longest
+// context of at least 8192 tokens.
+bool mx4_even_plan(Plan& p, int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t max_ctx,
+                   bool fused) {
+    const int mode = env_int("PKV_MX4_EVEN", 1);
+    if (!mode || p.n_parts <= 1 || B < 1 || B > pkv::kEvenMaxBatch) return false;
+    const int nw = env_int("PKV_MX4_EVEN_NW", H_kv % 4 == 0 ? 4 : 2);
+    const int pf = env_int("PKV_MX4_EVEN_PF", nw == 2 ? 2 : 1);
+    if (nw <= 0 || H_kv % nw || !pkv::mxfp4_even_variant_exists(nw, pf)) return false;
+    const int64_t worst = (int64_t)B * ((max_ctx + pkv::kBlockSize - 1) / pkv::kBlockSize);   // blocks per KV head
+    const int64_t cap = ((int64_t)B * H_q * p.n_parts - B - 3) / H_q - B;                    // runs whose pieces fit
+    const int64_t need = (worst + pkv::kEvenMaxWaveBlocks - 1) / pkv::kEvenMaxWaveBlocks;
+    const int64_t resident = mx4_even_resident_wgs(dtype, D, nw, pf, H_q / H_kv, fused) / (H_kv / nw);
+    const int64_t runs = std::min(std::max(resident, need), cap);
+    const bool fits = mode == 2 || (nw == 4 && pf == 1 && worst >= 96 * runs && max_ctx >= 8192);
+    if (resident <= 0 || runs < need || runs < 1 || worst >= (int64_t)1 << 30 || !fits) return false;
+    p.nw = nw;
+    p.pf = pf;
+    p.hg = nw;
+    p.even_waves = (int32_t)(runs * H_kv);
+    p.grid = (unsigned)(runs * (H_kv / nw));
+    return true;
+}
+
 int check_common(int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t block_size, int32_t n_blocks,
                  int32_t bt_stride, int32_t max_ctx, int32_t partition_size) {
     if (!elem_bytes(dtype)) return fail(PKV_ERR_UNSUPPORTED, "dtype %d is not one of PKV_F32/F16/BF16", dtype);
@@ -371,9 +428,13 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
             p.nw = env_int("PKV_MX4_NW", 4);
             p.ch = 1;
             p.pf = env_int("PKV_MX4_PF", 1);
-            if (!pkv::mxfp4_mfma_variant_exists(p.nw, p.pf)) { p.nw = 4; p.pf = 1; }
-            coarsen_partitions(p, B, H_kv, max_ctx, partition_size, 0);
-            p.grid = (unsigned)((int64_t)p.n_parts * B * H_kv);
+            p.hg = env_int("PKV_MX4_HG", 1);
+            if (p.hg <= 0 || H_kv % p.hg) p.hg = 1;
+            if (!pkv::mxfp4_mfma_variant_exists(p.nw, p.pf, p.hg)) { p.nw = 4; p.pf = 1; p.hg = 1; }
+            if (!mx4_even_plan(p, dtype, B, H_q, H_kv, D, max_ctx, fused)) {
+                coarsen_partitions(p, B, H_kv, max_ctx, partition_size, 0);
+                p.grid = (unsigned)((int64_t)p.n_parts * B * (H_kv / p.hg));
+            }
         } else {
             p.nw = env_int("PKV_MX4_NW", 4);
             p.ch = env_int("PKV_MX4_CH", 2);
@@ -424,7 +485,8 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
     a.part_rev = env_int("PKV_PART_REV", 1) != 0;
     if (p.even_waves) {   // the lse area starts with the merge's prefix: [tw, waves, blocks before b (B + 1)]
         a.even_waves = p.even_waves;
-        a.even_min_run = env_int("PKV_GQA_EVEN_MINRUN", pkv::kEvenMinWaveBlocks);
+        a.even_min_run = std::min(std::max(env_int("PKV_GQA_EVEN_MINRUN", pkv::kEvenMinWaveBlocks),
+                                           pkv::kEvenMinWaveBlocks), pkv::kEvenMaxWaveBlocks);
         a.even_meta = reinterpret_cast<int32_t*>(a.part_lse);
         a.part_lse += B + 3;
     }
@@ -469,7 +531,8 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
             e = pkv::launch_kv_append_mxfp4(dtype, D, ap, s);
             if (e != hipSuccess) return fail(PKV_ERR_HIP, "kv_append_mxfp4 launch: %s", hipGetErrorString(e));
         }
-        e = p.kind == 1 ? pkv::launch_decode_mxfp4_mfma(dtype, D, p.nw, p.pf, a, p.grid, s)
+        e = p.kind == 1 && p.even_waves ? pkv::launch_decode_mxfp4_even(dtype, D, p.nw, p.pf, a, p.grid, s)
+            : p.kind == 1                ? pkv::launch_decode_mxfp4_mfma(dtype, D, p.nw, p.pf, p.hg, a, p.grid, s)
                         : pkv::launch_decode_mxfp4(dtype, D, p.nw, p.ch, a, p.grid, s);
     } else if (fp8 && p.grouped) {
         // in the fused step the kernel quantizes and writes the new rows itself
@@ -505,9 +568,12 @@ int launch_attention(int dtype, float* out, const void* q, int64_t q_row_stride,
         if (e != hipSuccess) return fail(PKV_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
     }
     if (mx4) {
-        snprintf(g_launch, sizeof g_launch, "%s dtype=%d D=%d nw=%d ch=%d pf=%d grid=%u part_tokens=%d n_parts=%d%s",
-                 p.kind == 1 ? "mxfp4_mfma" : "mxfp4", dtype, D, p.nw, p.ch, p.pf, p.grid, p.part_tokens, p.n_parts,
-                 fused ? " fused_append" : "");
+        char hg[48] = "";
+        if (p.kind == 1 && p.even_waves) snprintf(hg, sizeof hg, " hg=%d even_waves=%d", p.hg, p.even_waves);
+        else if (p.kind == 1) snprintf(hg, sizeof hg, " hg=%d", p.hg);
+        snprintf(g_launch, sizeof g_launch, "%s dtype=%d D=%d nw=%d ch=%d pf=%d%s grid=%u part_tokens=%d n_parts=%d%s",
+                 p.kind == 1 ? (p.even_waves ? "mxfp4_mfma_even" : "mxfp4_mfma") : "mxfp4", dtype, D, p.nw, p.ch, p.pf,
+                 hg, p.grid, p.part_tokens, p.n_parts, fused ? " fused_append" : "");
     } else if (persistent_wgs) {
         snprintf(g_launch, sizeof g_launch,
                  "mha_persistent dtype=%d D=%d nw=16 ch=%d pf=1 grid=%u units=%u part_tokens=%d n_parts=%d%s", dtype, D,

@@ -729,7 +729,7 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_even_kernel(const AttnArgs
     __syncthreads();
 
     const int total = s_pre[a.B];   // blocks per KV head over the batch (the host keeps it below 2^30)
-    const int min_run = max(kEvenMinWaveBlocks, a.even_min_run);
+    const int min_run = min(max(kEvenMinWaveBlocks, a.even_min_run), kEvenMaxWaveBlocks);
     const int runs = max(1, min(a.even_waves / a.H_kv, (total + min_run - 1) / min_run));
     const int tw = max(1, (total + runs - 1) / runs);   // <= kEvenMaxWaveBlocks (host sizing)
     if (blockIdx.x == 0) {

@@ -449,15 +449,35 @@ __device__ __forceinline__ void lds_block(uint32_t ka, uint32_t ksa, uint32_t va
 #endif
 }
 
-// Each wave streams its blocks (w, w + NW, ...) through a ring of R = PF + 1 LDS
-// slots, PF blocks ahead of the one it computes.  A slot holds one block of the
-// KV head: K codes placed so that lane l's 16 bytes sit at 16 l (for D = 64 its
-// two words at 4 l and 256 + 4 l) -- the DMA lane that fetches them is lane l, so
-// the read is conflict-free -- then V codes, K scales and V scales in pool order.  Every DMA stays inside the block's rows of this KV head; rows at
-// or past the length are masked after the read, so the last, partial block
-// needs no other path.
-template <int QDT, int D, int NW, int PF, bool LO, bool APPEND>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+// Each wave streams its blocks through a ring of R = PF + 1 LDS chunk slots, PF
+// chunks ahead of the one it computes.  A slot holds one block of the KV head: K
+// codes placed so that lane l's 16 bytes sit at 16 l (for D = 64 its two words at
+// 4 l and 256 + 4 l) -- the DMA lane that fetches them is lane l, so the read is
+// conflict-free -- then V codes, K scales and V scales in pool order.  Every DMA
+// stays inside the block's rows of this KV head; rows at or past the length are
+// masked after the read, so the last, partial block needs no other path.
+//
+// HG: KV heads per workgroup.  Wave w streams head g0 + w % HG over blocks w / HG,
+// w / HG + NW / HG, ... of the partition, so the HG heads' 1 KiB code tiles of a
+// block -- neighbours in the pool -- are read together as one HG KiB piece; HG = 1 is
+// one head per workgroup, its blocks round-robin over the waves.  The waves of a head
+// then merge through LDS.
+//
+// EVEN (HG = NW): the even split of the batch.  The requests' blocks, end to end in
+// request order, are cut into `runs` equal runs of tw blocks; workgroup (S, hg) takes
+// run S for KV heads hg NW .. hg NW + NW - 1, wave w head hg NW + w.  Every wave
+// streams the same number of blocks whatever the length mix, the grid is one resident
+// round, and a block's NW head tiles are read together.  The waves walk the run's
+// pieces (its overlap with each request) in step, each with a fresh softmax state per
+// piece; a piece that is a whole request is written as the output, any other as piece
+// (S + b) H_kv + g of request b -- rows part_o[(((S + b) H_kv + g) G + h) D ...] and
+// part_lse[((S + b) H_kv + g) G + h] -- which the merge kernel combines in run order (a
+// run and a request meet in one interval, and along the end-to-end order S and b only
+// grow, so S + b names each meeting once).  Every workgroup prefix-sums the requests'
+// block counts in LDS (lengths out of range count as empty: the merge writes their
+// rows); workgroup 0 stores tw, the runs used and the prefix for the merge.
+template <int QDT, int D, int NW, int PF, bool LO, bool APPEND, int HG, bool EVEN>
+__global__ __launch_bounds__(NW * 64, 2)
 void decode_mxfp4_mfma_kernel(const AttnArgs a) {
     using Geo = Mx4Geo<D>;
     using L = Mx4Lane<QDT, D, LO>;
@@ -469,93 +489,59 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
     constexpr int LPB = D == 128 ? 3 : 5;                  // DMA instructions per block
     constexpr int LPC = CH * LPB;
     static_assert(PF * LPC < 64, "vmcnt range");
+    static_assert(NW % HG == 0, "a workgroup's waves split evenly over its heads");
+    static_assert(!EVEN || HG == NW, "the even split streams one head per wave");
+    static_assert(kEvenMaxWaveBlocks <= kWin, "a run's block ids fit one window");
+    constexpr int BW = NW / HG;                            // waves per head
+    constexpr int T = NW * 64;
     constexpr int RING = NW * R * CH * SLOT;
-    constexpr int MERGE = NW * 16 * (D + 4) * 4;
+    constexpr int MERGE = EVEN ? 0 : NW * 16 * (D + 4) * 4;
+    constexpr int PER = EVEN ? kEvenMaxBatch / T + 1 : 1;  // requests per thread in the prefix sum (covers index B)
     __shared__ __attribute__((aligned(16))) char s_ring[RING > MERGE ? RING : MERGE];
     __shared__ uint32_t s_ids[kWin];   // block offsets in 256-byte units of the code pools
     __shared__ int s_bad;
-    __shared__ float s_m[NW][16];
-    __shared__ float s_l[NW][16];
-    __shared__ uint8_t s_new[2][APPEND ? D / 2 : 1];    // APPEND: the new K and V rows' codes ...
-    __shared__ uint8_t s_nsc[2][APPEND ? D / 32 : 1];   // ... and scale bytes
+    __shared__ float s_m[EVEN ? 1 : NW][16];
+    __shared__ float s_l[EVEN ? 1 : NW][16];
+    __shared__ uint8_t s_new[HG][2][APPEND ? D / 2 : 1];    // APPEND: per head, the new K and V rows' codes ...
+    __shared__ uint8_t s_nsc[HG][2][APPEND ? D / 32 : 1];   // ... and scale bytes
+    __shared__ int32_t s_pre[EVEN ? PER * T : 1];           // EVEN: blocks before each request
+    __shared__ int32_t s_scan[EVEN ? T : 1];
+    __shared__ int s_badw[EVEN ? NW : 1];                   // EVEN: a wave's lanes saw a bad id
 
-    const int BG = a.B * a.H_kv;
-    const int unit = xcd_pair_unit(blockIdx.x, a.n_parts * BG);
-    const int pg = unit / BG;
-    const int part = unit_part(a, pg);
-    const int bg = unit - pg * BG;
-    const int b = bg / a.H_kv;
-    const int g = bg - b * a.H_kv;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int hs = w % HG;                      // the wave's head slot
+    const int wi = w / HG;                      // ... and its place among that head's waves
+    const int HGS = a.H_kv / HG;                // head groups per request
+    // the workgroup's unit: (partition, request, head group), or EVEN (run, head group)
+    int part = 0, b = 0, S = 0, g0;
+    if constexpr (EVEN) {
+        S = blockIdx.x / HGS;
+        g0 = (blockIdx.x - S * HGS) * HG;
+    } else {
+        const int BG = a.B * HGS;
+        const int unit = xcd_pair_unit(blockIdx.x, a.n_parts * BG);
+        const int pg = unit / BG;
+        part = unit_part(a, pg);
+        const int bg = unit - pg * BG;
+        b = bg / HGS;
+        g0 = (bg - b * HGS) * HG;
+    }
+    const int g = g0 + hs;                      // the wave's KV head
 
     L st;
-    st.init(a, lane, b, g);
-    const int32_t* table = a.block_tables + (int64_t)b * a.bt_stride;
-    const int first_blk = part * (a.part_tokens / kBlockSize);
-    constexpr int PRE = (kWin + NW * 64 - 1) / (NW * 64);
-    int pre[PRE];
-    {
-        const int spec = min(min(a.part_tokens / kBlockSize, kWin), a.bt_stride - first_blk);
-#pragma unroll
-        for (int k = 0; k < PRE; ++k) {
-            const int t = threadIdx.x + k * NW * 64;
-            pre[k] = t < spec ? table[first_blk + t] : 0;
-        }
-    }
-    const int n = APPEND ? a.positions[b] + 1 : a.context_lens[b];
-    const bool bad_len = APPEND ? (n < 1 || n > a.max_context_len) : (n < 0 || n > a.max_context_len);
-    if (bad_len || n == 0) {
-        if (a.n_parts == 1 && part == 0)
-            for (int x = threadIdx.x; x < a.G * D; x += NW * 64)
-                a.out[((size_t)b * a.H_q + (size_t)g * a.G) * D + x] = bad_len ? __builtin_nanf("") : 0.0f;
-        return;
-    }
-    const int start = part * a.part_tokens;
-    if (start >= n) return;
-    const int lim = min(start + a.part_tokens, n);
-    const int nblk = (lim - start + kBlockSize - 1) / kBlockSize;
-    // APPEND: when this partition ends at n, the new token (position n - 1, row
-    // t_new of the partition's last block) is quantized here from k_new / v_new by
-    // the wave that owns that block (blocks go round-robin and a window holds a
-    // multiple of NW blocks), exactly as the append kernel would: it writes the
-    // codes into the block's ring slot before the slot is read, and to the pools
-    // (this workgroup is the only one holding that position of its KV head).
-    const bool holds_new = APPEND && lim == n;
-    const int t_new = (n - 1) % kBlockSize;
-    const bool new_wave = holds_new && w == (nblk - 1) % NW;
-    if constexpr (APPEND) {
-        // quantized now into a small LDS area of the owner wave (lane l: elements 2l
-        // and 2l + 1, one row per pass), copied into the ring slot once the block's
-        // DMAs have landed there
-        if (new_wave) {
-            const bool on = lane < D / 2;
-#pragma unroll
-            for (int which = 0; which < 2; ++which) {
-                float x0 = 0.0f, x1 = 0.0f;
-                if (on) {
-                    const uint32_t u = *reinterpret_cast<const uint32_t*>(
-                        (which ? a.v_new : a.k_new) + ((size_t)b * a.new_row_stride + (size_t)g * D + 2 * lane) * 2);
-                    if constexpr (QDT == DT_F16) {
-                        const half2_t h = __builtin_bit_cast(half2_t, u);
-                        x0 = (float)h.x;
-                        x1 = (float)h.y;
-                    } else {
-                        x0 = __uint_as_float(u << 16);
-                        x1 = __uint_as_float(u & 0xffff0000u);
-                    }
-                }
-                int E;
-                const uint32_t code = mx4_quantize_pair(x0, x1, E);
-                if (on) {
-                    s_new[which][lane] = (uint8_t)code;
-                    if ((lane & 15) == 0) s_nsc[which][lane / 16] = (uint8_t)(E + 127);
-                }
-            }
-        }
-    }
+    // The tokens being streamed: request length n, bound lim (tokens at or past it
+    // are masked), blocks nblk.  APPEND: when they end at n, the new token (position
+    // n - 1, row t_new of the last block) is quantized here from k_new / v_new by the
+    // wave of each head that owns that block (a head's blocks go round-robin over its
+    // BW waves and a window holds a multiple of BW blocks), exactly as the append
+    // kernel would: it writes the codes into the block's ring slot before the slot is
+    // read, and to the pools (this workgroup is the only one holding that position of
+    // its KV heads).
+    int n = 0, lim = 0, nblk = 0, t_new = 0;
+    bool new_wave = false;
 
-    const int j = st.j, c = st.c;
+    const int j = lane >> 4, c = lane & 15;     // the lane's row group and column (as st.init sets them)
     const int tau = 4 * (c & 3) + (c >> 2);
     // DMA sources inside one (block, KV head) tile
     const int kdma = D == 128 ? tau * RB + 16 * j : tau * RB + 8 * j;   // + 4 h for D = 64
@@ -577,6 +563,35 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
     char* my_ring = s_ring + w * R * CH * SLOT;
     const uint32_t my_ring_a = ring0 + w * R * CH * SLOT;
 
+    // APPEND: the new K and V rows of (b, g), quantized into the wave's small LDS area
+    // (lane l: elements 2l and 2l + 1, one row per pass); copied into the ring slot once
+    // the block's DMAs have landed there
+    auto quantize_new = [&]() {
+        const bool on = lane < D / 2;
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+            float x0 = 0.0f, x1 = 0.0f;
+            if (on) {
+                const uint32_t u = *reinterpret_cast<const uint32_t*>(
+                    (which ? a.v_new : a.k_new) + ((size_t)b * a.new_row_stride + (size_t)g * D + 2 * lane) * 2);
+                if constexpr (QDT == DT_F16) {
+                    const half2_t h = __builtin_bit_cast(half2_t, u);
+                    x0 = (float)h.x;
+                    x1 = (float)h.y;
+                } else {
+                    x0 = __uint_as_float(u << 16);
+                    x1 = __uint_as_float(u & 0xffff0000u);
+                }
+            }
+            int E;
+            const uint32_t code = mx4_quantize_pair(x0, x1, E);
+            if (on) {
+                s_new[hs][which][lane] = (uint8_t)code;
+                if ((lane & 15) == 0) s_nsc[hs][which][lane / 16] = (uint8_t)(E + 127);
+            }
+        }
+    };
+
     // APPEND: put the new rows in row t_new of ring slot sl, at the places the
     // block's DMAs fill (after they have landed there); the pools get them after
     // the loop
@@ -586,17 +601,32 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
             const int cn = 4 * (t_new & 3) + (t_new >> 2);   // the lane column whose K row is t_new
             const int kpos = D == 128 ? 256 * (lane / 16) + 16 * cn + (lane % 16)
                                       : 256 * ((lane % 8) / 4) + 4 * (16 * (lane / 8) + cn) + (lane % 4);
-            dst[kpos] = (char)s_new[0][lane];
-            dst[CODES + t_new * RB + lane] = (char)s_new[1][lane];
+            dst[kpos] = (char)s_new[hs][0][lane];
+            dst[CODES + t_new * RB + lane] = (char)s_new[hs][1][lane];
             if ((lane & 15) == 0) {
-                dst[2 * CODES + t_new * SB + lane / 16] = (char)s_nsc[0][lane / 16];
-                dst[2 * CODES + kBlockSize * SB + t_new * SB + lane / 16] = (char)s_nsc[1][lane / 16];
+                dst[2 * CODES + t_new * SB + lane / 16] = (char)s_nsc[hs][0][lane / 16];
+                dst[2 * CODES + kBlockSize * SB + t_new * SB + lane / 16] = (char)s_nsc[hs][1][lane / 16];
             }
         }
         // this wave's LDS writes land before its reads of the slot (in order per wave)
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    // APPEND: the new rows to the pools, from each head's owner wave (s_ids still holds
+    // the window with the new token's block)
+    auto write_new = [&]() {
+        if (lane < D / 2) {
+            const size_t u = s_ids[(nblk - 1) % kWin];
+            const size_t row = (size_t)g * kBlockSize * RB + (u << 8) + (size_t)t_new * RB + lane;
+            reinterpret_cast<uint8_t*>(a.k_pool_w)[row] = s_new[hs][0][lane];
+            reinterpret_cast<uint8_t*>(a.v_pool_w)[row] = s_new[hs][1][lane];
+            if ((lane & 15) == 0) {
+                const size_t srow = (size_t)g * kBlockSize * SB + (u << 4) + (size_t)t_new * SB + lane / 16;
+                a.k_mx_scale_w[srow] = s_nsc[hs][0][lane / 16];
+                a.v_mx_scale_w[srow] = s_nsc[hs][1][lane / 16];
+            }
+        }
     };
 
     auto issue_block = [&](int slot, int blk) {
@@ -614,11 +644,11 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
         }
         if (sc_lane) dma4(sp + so, dst + 2 * CODES);
     };
-    // chunk i of the wave: blocks w + NW (CH i + cb); a block past the window's
+    // chunk i of the wave: blocks wi + BW (CH i + cb); a block past the window's
     // end (the last chunk's second block) is fetched as a copy of the first and
     // masked, so every chunk issues the same number of DMAs
     int nr = 0, r0_cur = 0;   // the current window: its block count and first block
-    auto blk_of = [&](int i, int cb) { return w + NW * (CH * i + cb); };
+    auto blk_of = [&](int i, int cb) { return wi + BW * (CH * i + cb); };
     auto issue = [&](int slot, int i) {
 #pragma unroll
         for (int cb = 0; cb < CH; ++cb) {
@@ -717,37 +747,9 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
         }
     };
 
-    if (threadIdx.x == 0) s_bad = 0;
-    for (int r0 = 0; r0 < nblk; r0 += kWin) {
-        nr = min(kWin, nblk - r0);
-        r0_cur = r0;
-        __syncthreads();
-        if (r0 == 0) {
-#pragma unroll
-            for (int k = 0; k < PRE; ++k) {
-                const int t = threadIdx.x + k * NW * 64;
-                if (t < nr) {
-                    int id = pre[k];
-                    if ((unsigned)id >= (unsigned)a.n_blocks) {
-                        s_bad = 1;
-                        id = 0;
-                    }
-                    s_ids[t] = (uint32_t)id * blk_units;
-                }
-            }
-        } else {
-            for (int t = threadIdx.x; t < nr; t += NW * 64) {
-                int id = table[first_blk + r0 + t];
-                if ((unsigned)id >= (unsigned)a.n_blocks) {
-                    s_bad = 1;
-                    id = 0;
-                }
-                s_ids[t] = (uint32_t)id * blk_units;
-            }
-        }
-        __syncthreads();
-        const int tok_r = start + r0 * kBlockSize;
-        const int nbw = w < nr ? (nr - w + NW - 1) / NW : 0;   // this wave's blocks: w + NW i
+    // the current window's nr blocks (ids in s_ids), the first at token tok_r
+    auto stream = [&](int tok_r) {
+        const int nbw = wi < nr ? (nr - wi + BW - 1) / BW : 0;   // this wave's blocks: wi + BW i
         const int nb = (nbw + CH - 1) / CH;                      // ... in chunks of CH
         if constexpr (LO) {
             // chunk i is read from slot i % R; the DMAs of chunk i + PF go into the slot
@@ -792,7 +794,7 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
                 ps[0] = ps[1];
             }
             if (nb > 0) st.pair_finish(ps[0]);
-            continue;
+            return;
         }
         int i = 0;
         if (nb >= R + PF) {
@@ -823,114 +825,342 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
                 }
             }
         }
-    }
+    };
 
-    if constexpr (APPEND) {
-        // the new rows to the pools, from the owner wave (s_ids still holds the last
-        // window, which has the new token's block; an out-of-range id writes nothing)
-        if (new_wave && lane < D / 2 && s_bad == 0) {
-            const size_t u = s_ids[(nblk - 1) % kWin];
-            const size_t row = (size_t)g * kBlockSize * RB + (u << 8) + (size_t)t_new * RB + lane;
-            reinterpret_cast<uint8_t*>(a.k_pool_w)[row] = s_new[0][lane];
-            reinterpret_cast<uint8_t*>(a.v_pool_w)[row] = s_new[1][lane];
-            if ((lane & 15) == 0) {
-                const size_t srow = (size_t)g * kBlockSize * SB + (u << 4) + (size_t)t_new * SB + lane / 16;
-                a.k_mx_scale_w[srow] = s_nsc[0][lane / 16];
-                a.v_mx_scale_w[srow] = s_nsc[1][lane / 16];
+    if constexpr (!EVEN) {
+        st.init(a, lane, b, g);
+        const int32_t* table = a.block_tables + (int64_t)b * a.bt_stride;
+        const int first_blk = part * (a.part_tokens / kBlockSize);
+        constexpr int PRE = (kWin + T - 1) / T;
+        int pre[PRE];
+        {
+            const int spec = min(min(a.part_tokens / kBlockSize, kWin), a.bt_stride - first_blk);
+#pragma unroll
+            for (int k = 0; k < PRE; ++k) {
+                const int t = threadIdx.x + k * T;
+                pre[k] = t < spec ? table[first_blk + t] : 0;
+            }
+        }
+        n = APPEND ? a.positions[b] + 1 : a.context_lens[b];
+        const bool bad_len = APPEND ? (n < 1 || n > a.max_context_len) : (n < 0 || n > a.max_context_len);
+        if (bad_len || n == 0) {
+            if (a.n_parts == 1 && part == 0)   // the rows of all HG heads
+                for (int x = threadIdx.x; x < HG * a.G * D; x += T)
+                    a.out[((size_t)b * a.H_q + (size_t)g0 * a.G) * D + x] = bad_len ? __builtin_nanf("") : 0.0f;
+            return;
+        }
+        const int start = part * a.part_tokens;
+        if (start >= n) return;
+        lim = min(start + a.part_tokens, n);
+        nblk = (lim - start + kBlockSize - 1) / kBlockSize;
+        t_new = (n - 1) % kBlockSize;
+        new_wave = APPEND && lim == n && wi == (nblk - 1) % BW;
+        if constexpr (APPEND) {
+            if (new_wave) quantize_new();
+        }
+
+        if (threadIdx.x == 0) s_bad = 0;
+        for (int r0 = 0; r0 < nblk; r0 += kWin) {
+            nr = min(kWin, nblk - r0);
+            r0_cur = r0;
+            __syncthreads();
+            if (r0 == 0) {
+#pragma unroll
+                for (int k = 0; k < PRE; ++k) {
+                    const int t = threadIdx.x + k * T;
+                    if (t < nr) {
+                        int id = pre[k];
+                        if ((unsigned)id >= (unsigned)a.n_blocks) {
+                            s_bad = 1;
+                            id = 0;
+                        }
+                        s_ids[t] = (uint32_t)id * blk_units;
+                    }
+                }
+            } else {
+                for (int t = threadIdx.x; t < nr; t += T) {
+                    int id = table[first_blk + r0 + t];
+                    if ((unsigned)id >= (unsigned)a.n_blocks) {
+                        s_bad = 1;
+                        id = 0;
+                    }
+                    s_ids[t] = (uint32_t)id * blk_units;
+                }
+            }
+            __syncthreads();
+            stream(start + r0 * kBlockSize);
+        }
+        // an out-of-range id writes nothing
+        if constexpr (APPEND) {
+            if (new_wave && s_bad == 0) write_new();
+        }
+
+        // merge each head's waves through LDS (the ring is free once every wave is past here)
+        const float l = sum_groups(st.l);
+        __syncthreads();
+        float (*s_o)[16][D + 4] = reinterpret_cast<float (*)[16][D + 4]>(s_ring);
+        if (j == 0) {
+            s_m[w][c] = st.m;
+            s_l[w][c] = l;
+        }
+#pragma unroll
+        for (int t = 0; t < VT; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) s_o[w][c][(4 * j + q) * VT + t] = st.acc[t][q];
+        __syncthreads();
+        const bool bad = s_bad != 0;
+        const int G = a.G;
+        for (int x = threadIdx.x; x < HG * G * D; x += T) {
+            const int hr = x / D;         // head slot hr / G, query row hh of that head
+            const int d = x - hr * D;
+            const int h0 = hr / G;
+            const int hh = hr - h0 * G;
+            float M = s_m[h0][hh];
+#pragma unroll
+            for (int k = 1; k < BW; ++k) M = fmaxf(M, s_m[h0 + HG * k][hh]);
+            float Ls = 0.0f, O = 0.0f;
+#pragma unroll
+            for (int k = 0; k < BW; ++k) {
+                const int q = h0 + HG * k;   // the head's k-th wave
+                const float f = __builtin_amdgcn_exp2f(s_m[q][hh] - M);
+                Ls += s_l[q][hh] * f;
+                O += (LO ? s_o[q][hh][d] + s_o[q][hh + G][d] : s_o[q][hh][d]) * f;   // hi + lo columns
+            }
+            const size_t row = (size_t)b * a.H_q + (size_t)g0 * G + hr;
+            const float val = bad ? __builtin_nanf("") : O / Ls;
+            if (a.n_parts == 1) {
+                a.out[row * D + d] = val;
+            } else {
+                a.part_o[(row * a.n_parts + part) * D + d] = val;
+                if (d == 0)
+                    a.part_lse[row * a.n_parts + part] = bad ? __builtin_nanf("") : M + __builtin_amdgcn_logf(Ls);
+            }
+        }
+    } else {
+        // block counts of requests tid * PER ..., prefix-summed over the workgroup
+        const int tid = threadIdx.x;
+        int loc[PER];
+        int sum = 0;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int bb = tid * PER + k;
+            int nbk = 0;
+            if (bb < a.B) {
+                const int nn = APPEND ? a.positions[bb] + 1 : a.context_lens[bb];
+                const bool bad = APPEND ? (nn < 1 || nn > a.max_context_len) : (nn < 0 || nn > a.max_context_len);
+                nbk = bad ? 0 : (nn + kBlockSize - 1) / kBlockSize;
+            }
+            loc[k] = sum;
+            sum += nbk;
+        }
+        s_scan[tid] = sum;
+        __syncthreads();
+#pragma unroll
+        for (int off = 1; off < T; off <<= 1) {
+            const int x = tid >= off ? s_scan[tid - off] : 0;
+            __syncthreads();
+            s_scan[tid] += x;
+            __syncthreads();
+        }
+        const int excl = s_scan[tid] - sum;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) s_pre[tid * PER + k] = excl + loc[k];
+        __syncthreads();
+
+        const int total = s_pre[a.B];   // blocks per KV head over the batch (the host keeps it below 2^30)
+        const int min_run = min(max(kEvenMinWaveBlocks, a.even_min_run), kEvenMaxWaveBlocks);
+        const int runs = max(1, min(a.even_waves / a.H_kv, (total + min_run - 1) / min_run));
+        const int tw = max(1, (total + runs - 1) / runs);   // <= kEvenMaxWaveBlocks (host sizing)
+        if (blockIdx.x == 0) {
+            for (int bb = tid; bb <= a.B; bb += T) a.even_meta[2 + bb] = s_pre[bb];
+            if (tid == 0) {
+                a.even_meta[0] = tw;
+                a.even_meta[1] = runs;
+            }
+        }
+        int x0 = S * tw;
+        const int x1 = min(x0 + tw, total);
+        if (S >= runs || x0 >= x1) return;   // workgroup-uniform: nothing to stream
+        // the request holding block x0: the last one whose blocks start at or before it
+        {
+            int lo = 0, hi = a.B - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_pre[mid] <= x0) lo = mid;
+                else hi = mid - 1;
+            }
+            b = __builtin_amdgcn_readfirstlane(lo);
+        }
+        // the waves walk the same pieces: the workgroup's barriers below are uniform
+        while (x0 < x1) {
+            const int seg0 = __builtin_amdgcn_readfirstlane(s_pre[b]);
+            const int nbb = __builtin_amdgcn_readfirstlane(s_pre[b + 1]) - seg0;
+            const int pend = min(x1, seg0 + nbb);
+            const int blk0 = x0 - seg0, np = pend - x0;   // the piece: blocks [blk0, blk0 + np) of request b
+            const bool whole = blk0 == 0 && np == nbb;
+            n = APPEND ? a.positions[b] + 1 : a.context_lens[b];
+            lim = n;
+            nblk = np;
+            nr = np;
+            r0_cur = 0;
+            t_new = (n - 1) % kBlockSize;
+            new_wave = APPEND && blk0 + np == nbb;
+            st.init(a, lane, b, g);   // q of the row's G heads; fresh softmax state
+            if constexpr (APPEND) {
+                if (new_wave) quantize_new();
+            }
+            // the piece's block ids, range-checked, staged for the workgroup
+            __syncthreads();   // every wave is past the previous piece's ids
+            const int32_t* table = a.block_tables + (int64_t)b * a.bt_stride + blk0;
+            bool bad_lane = false;
+            for (int t = tid; t < np; t += T) {
+                int id = table[t];
+                if ((unsigned)id >= (unsigned)a.n_blocks) {
+                    bad_lane = true;
+                    id = 0;
+                }
+                s_ids[t] = (uint32_t)id * blk_units;
+            }
+            const bool wave_bad = __builtin_amdgcn_ballot_w64(bad_lane) != 0;
+            if (lane == 0) s_badw[w] = wave_bad ? 1 : 0;
+            __syncthreads();
+            bool bad = false;
+#pragma unroll
+            for (int q = 0; q < NW; ++q) bad = bad || s_badw[q] != 0;
+            stream(blk0 * kBlockSize);
+            if constexpr (APPEND) {
+                if (new_wave && !bad) write_new();   // an out-of-range id writes nothing
+            }
+
+            // the piece's result for its G heads: lane (j, col) holds head col, elements
+            // d = (4 j + q) VT + t; LO: column col + G holds the lo half of head col
+            const float l = sum_groups(st.l);
+            const int G = a.G;
+            float o[VT][4];
+#pragma unroll
+            for (int t = 0; t < VT; ++t)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float v = st.acc[t][q];
+                    if constexpr (LO) v += __shfl(v, lane + G, 64);
+                    o[t][q] = v;
+                }
+            if (c < G) {
+                const size_t pid = (((size_t)S + b) * a.H_kv + g) * G + c;
+                float* o0 = whole ? a.out + ((size_t)b * a.H_q + (size_t)g * G + c) * D : a.part_o + pid * D;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float* op = o0 + (4 * j + q) * VT;
+#pragma unroll
+                    for (int t = 0; t < VT; t += 4) {
+                        floatx4 val;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) val[e] = bad ? __builtin_nanf("") : o[t + e][q] / l;
+                        *reinterpret_cast<floatx4*>(op + t) = val;
+                    }
+                }
+                // v_log_f32 is log base 2, matching the log2-domain scores
+                if (!whole && j == 0) a.part_lse[pid] = bad ? __builtin_nanf("") : st.m + __builtin_amdgcn_logf(l);
+            }
+
+            x0 = pend;
+            if (x0 < x1) {   // the next request with blocks
+                do {
+                    ++b;
+                } while (s_pre[b + 1] == s_pre[b]);
+                b = __builtin_amdgcn_readfirstlane(b);
             }
         }
     }
-
-    // merge the waves through LDS (the ring is free once every wave is past here)
-    const float l = sum_groups(st.l);
-    __syncthreads();
-    float (*s_o)[16][D + 4] = reinterpret_cast<float (*)[16][D + 4]>(s_ring);
-    if (j == 0) {
-        s_m[w][c] = st.m;
-        s_l[w][c] = l;
-    }
-#pragma unroll
-    for (int t = 0; t < VT; ++t)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) s_o[w][c][(4 * j + q) * VT + t] = st.acc[t][q];
-    __syncthreads();
-    const bool bad = s_bad != 0;
-    const int G = a.G;
-    for (int x = threadIdx.x; x < G * D; x += NW * 64) {
-        const int hh = x / D;
-        const int d = x - hh * D;
-        float M = s_m[0][hh];
-#pragma unroll
-        for (int q = 1; q < NW; ++q) M = fmaxf(M, s_m[q][hh]);
-        float Ls = 0.0f, O = 0.0f;
-#pragma unroll
-        for (int q = 0; q < NW; ++q) {
-            const float f = __builtin_amdgcn_exp2f(s_m[q][hh] - M);
-            Ls += s_l[q][hh] * f;
-            O += (LO ? s_o[q][hh][d] + s_o[q][hh + G][d] : s_o[q][hh][d]) * f;   // hi + lo columns
-        }
-        const size_t row = (size_t)b * a.H_q + (size_t)g * G + hh;
-        const float val = bad ? __builtin_nanf("") : O / Ls;
-        if (a.n_parts == 1) {
-            a.out[row * D + d] = val;
-        } else {
-            a.part_o[(row * a.n_parts + part) * D + d] = val;
-            if (d == 0) a.part_lse[row * a.n_parts + part] = bad ? __builtin_nanf("") : M + __builtin_amdgcn_logf(Ls);
-        }
-    }
 }
 
-template <int QDT, int D, int NW, int PF>
-static hipError_t launch_t(const AttnArgs& a, unsigned grid, hipStream_t stream) {
-    // the fused step passes positions instead of context_lens
-    const bool append = a.context_lens == nullptr;
-    if (a.G <= 8) {
-        if (append)
-            hipLaunchKernelGGL((decode_mxfp4_mfma_kernel<QDT, D, NW, PF, true, true>), dim3(grid), dim3(NW * 64), 0,
-                               stream, a);
-        else
-            hipLaunchKernelGGL((decode_mxfp4_mfma_kernel<QDT, D, NW, PF, true, false>), dim3(grid), dim3(NW * 64), 0,
-                               stream, a);
-    } else {
-        if (append)
-            hipLaunchKernelGGL((decode_mxfp4_mfma_kernel<QDT, D, NW, PF, false, true>), dim3(grid), dim3(NW * 64), 0,
-                               stream, a);
-        else
-            hipLaunchKernelGGL((decode_mxfp4_mfma_kernel<QDT, D, NW, PF, false, false>), dim3(grid), dim3(NW * 64),
-                               0, stream, a);
-    }
-    return hipGetLastError();
+template <int QDT, int D, int NW, int PF, int HG, bool EVEN>
+static const void* kernel_ptr(bool lo, bool append) {
+    if (lo)
+        return append ? reinterpret_cast<const void*>(&decode_mxfp4_mfma_kernel<QDT, D, NW, PF, true, true, HG, EVEN>)
+                      : reinterpret_cast<const void*>(&decode_mxfp4_mfma_kernel<QDT, D, NW, PF, true, false, HG, EVEN>);
+    return append ? reinterpret_cast<const void*>(&decode_mxfp4_mfma_kernel<QDT, D, NW, PF, false, true, HG, EVEN>)
+                  : reinterpret_cast<const void*>(&decode_mxfp4_mfma_kernel<QDT, D, NW, PF, false, false, HG, EVEN>);
 }
 
-// (waves, chunks in flight per wave; a chunk is two blocks when G <= 8, else one)
-#define PKV_MX4_MFMA_VARIANTS(X) X(4, 1) X(4, 2) X(4, 3) X(2, 2) X(2, 4)
+// the fused step passes positions instead of context_lens; two blocks per output
+// product (LO) when G <= 8
+static hipError_t launch_fn(const void* fn, int nw, const AttnArgs& a, unsigned grid, hipStream_t stream) {
+    AttnArgs args = a;
+    void* params[] = {&args};
+    const hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(nw * 64), params, 0, stream);
+    return e != hipSuccess ? e : hipGetLastError();
+}
+
+// (waves, chunks in flight per wave, KV heads per workgroup; a chunk is two blocks when
+// G <= 8, else one)
+#define PKV_MX4_MFMA_VARIANTS(X) \
+    X(4, 1, 1) X(4, 2, 1) X(4, 3, 1) X(2, 2, 1) X(2, 4, 1) X(4, 1, 2) X(4, 2, 2) X(4, 1, 4) X(4, 2, 4) X(8, 1, 4) \
+    X(8, 2, 4) X(8, 2, 8) X(8, 3, 8) X(8, 1, 8)
+// even split: (waves = KV heads per workgroup, chunks in flight per wave)
+#define PKV_MX4_EVEN_VARIANTS(X) X(8, 1) X(4, 1) X(4, 2) X(2, 2)
 
 template <int QDT, int D>
-static hipError_t launch_d(int nw, int pf, const AttnArgs& a, unsigned grid, hipStream_t s) {
+static const void* find_kernel(bool even, int nw, int pf, int hg, bool lo, bool append) {
+    if (even) {
 #define X(NW_, PF_) \
-    if (nw == NW_ && pf == PF_) return launch_t<QDT, D, NW_, PF_>(a, grid, s);
+    if (nw == NW_ && pf == PF_) return kernel_ptr<QDT, D, NW_, PF_, NW_, true>(lo, append);
+        PKV_MX4_EVEN_VARIANTS(X)
+#undef X
+        return nullptr;
+    }
+#define X(NW_, PF_, HG_) \
+    if (nw == NW_ && pf == PF_ && hg == HG_) return kernel_ptr<QDT, D, NW_, PF_, HG_, false>(lo, append);
     PKV_MX4_MFMA_VARIANTS(X)
 #undef X
-    return hipErrorInvalidValue;
+    return nullptr;
 }
 
-hipError_t launch_decode_mxfp4_mfma(int q_dtype, int D, int nw, int pf, const AttnArgs& a, unsigned grid,
-                                    hipStream_t stream) {
+static const void* find_kernel(int q_dtype, int D, bool even, int nw, int pf, int hg, bool lo, bool append) {
     switch (q_dtype * 1000 + D) {
-    case DT_F16 * 1000 + 64: return launch_d<DT_F16, 64>(nw, pf, a, grid, stream);
-    case DT_F16 * 1000 + 128: return launch_d<DT_F16, 128>(nw, pf, a, grid, stream);
-    case DT_BF16 * 1000 + 64: return launch_d<DT_BF16, 64>(nw, pf, a, grid, stream);
-    case DT_BF16 * 1000 + 128: return launch_d<DT_BF16, 128>(nw, pf, a, grid, stream);
-    default: return hipErrorInvalidValue;
+    case DT_F16 * 1000 + 64: return find_kernel<DT_F16, 64>(even, nw, pf, hg, lo, append);
+    case DT_F16 * 1000 + 128: return find_kernel<DT_F16, 128>(even, nw, pf, hg, lo, append);
+    case DT_BF16 * 1000 + 64: return find_kernel<DT_BF16, 64>(even, nw, pf, hg, lo, append);
+    case DT_BF16 * 1000 + 128: return find_kernel<DT_BF16, 128>(even, nw, pf, hg, lo, append);
+    default: return nullptr;
     }
 }
 
-bool mxfp4_mfma_variant_exists(int nw, int pf) {
-#define X(NW_, PF_) \
-    if (nw == NW_ && pf == PF_) return true;
+hipError_t launch_decode_mxfp4_mfma(int q_dtype, int D, int nw, int pf, int hg, const AttnArgs& a, unsigned grid,
+                                    hipStream_t stream) {
+    if (hg <= 0 || a.H_kv % hg) return hipErrorInvalidValue;
+    const void* fn = find_kernel(q_dtype, D, false, nw, pf, hg, a.G <= 8, a.context_lens == nullptr);
+    return fn ? launch_fn(fn, nw, a, grid, stream) : hipErrorInvalidValue;
+}
+
+bool mxfp4_mfma_variant_exists(int nw, int pf, int hg) {
+#define X(NW_, PF_, HG_) \
+    if (nw == NW_ && pf == PF_ && hg == HG_) return true;
     PKV_MX4_MFMA_VARIANTS(X)
 #undef X
     return false;
+}
+
+hipError_t launch_decode_mxfp4_even(int q_dtype, int D, int nw, int pf, const AttnArgs& a, unsigned grid,
+                                    hipStream_t stream) {
+    if (a.H_kv % nw || !a.even_meta || a.B > kEvenMaxBatch) return hipErrorInvalidValue;
+    const void* fn = find_kernel(q_dtype, D, true, nw, pf, nw, a.G <= 8, a.context_lens == nullptr);
+    return fn ? launch_fn(fn, nw, a, grid, stream) : hipErrorInvalidValue;
+}
+
+bool mxfp4_even_variant_exists(int nw, int pf) {
+#define X(NW_, PF_) \
+    if (nw == NW_ && pf == PF_) return true;
+    PKV_MX4_EVEN_VARIANTS(X)
+#undef X
+    return false;
+}
+
+int mxfp4_even_wgs_per_cu(int q_dtype, int D, int nw, int pf, int G, bool fused) {
+    const void* fn = find_kernel(q_dtype, D, true, nw, pf, nw, G <= 8, fused);
+    int n = 0;
+    if (!fn || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, nw * 64, 0) != hipSuccess) return 0;
+    return n;
 }
 
 }  // namespace pkv

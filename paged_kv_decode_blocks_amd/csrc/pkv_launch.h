@@ -79,11 +79,19 @@ hipError_t launch_kv_append_mxfp4(int src_dtype, int D, const AppendMx4Args& a, 
 hipError_t launch_decode_mxfp4(int q_dtype, int D, int nw, int ch, const AttnArgs& a, unsigned grid,
                                hipStream_t stream);
 bool mxfp4_variant_exists(int nw, int ch);
-// grouped MXFP4 attention on MFMA (f16/bf16 q, G <= 16): grid = n_parts * B * H_kv;
-// nw waves per workgroup, pf blocks in flight per wave
-hipError_t launch_decode_mxfp4_mfma(int q_dtype, int D, int nw, int pf, const AttnArgs& a, unsigned grid,
+// grouped MXFP4 attention on MFMA (f16/bf16 q, G <= 16): grid = n_parts * B * H_kv / hg;
+// nw waves per workgroup, pf blocks in flight per wave, hg KV heads per workgroup (hg
+// divides H_kv and nw)
+hipError_t launch_decode_mxfp4_mfma(int q_dtype, int D, int nw, int pf, int hg, const AttnArgs& a, unsigned grid,
                                     hipStream_t stream);
-bool mxfp4_mfma_variant_exists(int nw, int pf);
+bool mxfp4_mfma_variant_exists(int nw, int pf, int hg);
+// grouped MXFP4 attention over an even split of the batch (a.even_waves, a.even_meta set):
+// grid = ceil-runs * H_kv / nw workgroups of nw waves, one KV head per wave (nw divides H_kv)
+hipError_t launch_decode_mxfp4_even(int q_dtype, int D, int nw, int pf, const AttnArgs& a, unsigned grid,
+                                    hipStream_t stream);
+bool mxfp4_even_variant_exists(int nw, int pf);
+// resident workgroups per CU of that kernel (0 if the runtime cannot say)
+int mxfp4_even_wgs_per_cu(int q_dtype, int D, int nw, int pf, int G, bool fused);
 // per query head; q (and new rows) in q_dtype, K/V codes + scales in the AttnArgs pools
 hipError_t launch_decode_fp8(int q_dtype, int D, int nw, int ch, int pf, bool append, const AttnArgs& a,
                              unsigned grid, hipStream_t stream);

@@ -142,3 +142,110 @@ def test_random_batches(seed):
                     rng.choice([2, 4, 8]), rng.choice([2048, 64, 8]))
         done += res is not None
     assert done >= 15
+
+
+# The grouped MXFP4 kernel's even split: one run per workgroup, streamed for nw KV heads at
+# once (a wave per head), so a run's pieces go straight to the workspace (no in-workgroup
+# merge) and the merge kernel's super-run is the run itself.
+
+def plan_mx4(B, H_q, H_kv, max_ctx, P, resident_wgs, nw):
+    """Runs and grid of the MXFP4 even split, or None when the plan cannot take it (the
+    host's sizing; the performance gate is not modelled)."""
+    padded = -(-max_ctx // 16) * 16
+    n_parts = -(-max_ctx // P) if 0 < P < padded else 1
+    if n_parts <= 1 or B < 1 or B > MAX_BATCH or H_kv % nw:
+        return None
+    worst = B * -(-max_ctx // 16)
+    cap = (B * H_q * n_parts - B - 3) // H_q - B
+    need = -(-worst // MAX_RUN)
+    resident = resident_wgs // (H_kv // nw)
+    runs = min(max(resident, need), cap)
+    if not (resident > 0 and runs >= need and runs >= 1):
+        return None
+    return {"even_waves": runs * H_kv, "grid": runs * (H_kv // nw)}
+
+
+def model_mx4(B, H_q, H_kv, D, max_ctx, P, lens, fused, nw, resident_wgs):
+    pl = plan_mx4(B, H_q, H_kv, max_ctx, P, resident_wgs, nw)
+    if pl is None:
+        return None
+    G = H_q // H_kv
+    ws_floats = pkv.decode_workspace_bytes(B, H_q, D, max_ctx, P) // 4
+    nb = [0 if ((n < 1 or n > max_ctx) if fused else (n < 0 or n > max_ctx)) else -(-n // 16) for n in lens]
+    pre = [0]
+    for x in nb:
+        pre.append(pre[-1] + x)
+    total = pre[B]
+    runs = max(1, min(pl["even_waves"] // H_kv, -(-total // MIN_RUN)))
+    tw = max(1, -(-total // runs))
+    assert tw <= MAX_RUN
+    streamed, written = set(), {}
+    for wg in range(pl["grid"]):
+        S, hgi = divmod(wg, H_kv // nw)
+        x0 = S * tw
+        x1 = min(x0 + tw, total)
+        if S >= runs or x0 >= x1:
+            continue
+        b = max(i for i in range(B) if pre[i] <= x0)
+        while x0 < x1:
+            seg0, nbb = pre[b], pre[b + 1] - pre[b]
+            pend = min(x1, seg0 + nbb)
+            blk0, np_ = x0 - seg0, pend - x0
+            assert 1 <= np_ <= MAX_RUN                     # the piece's ids fit the window
+            for g in range(hgi * nw, hgi * nw + nw):
+                for k in range(blk0, blk0 + np_):
+                    assert (b, g, k) not in streamed
+                    streamed.add((b, g, k))
+                if blk0 == 0 and np_ == nbb:
+                    written.setdefault((b, g), []).append(None)
+                else:
+                    pid = (S + b) * H_kv + g
+                    assert (pid + 1) * G * D <= ws_floats
+                    assert B + 3 + (pid + 1) * G <= ws_floats
+                    written.setdefault((b, g), []).append((S, pid))
+            x0 = pend
+            if x0 < x1:
+                b += 1
+                while pre[b + 1] == pre[b]:
+                    b += 1
+    for b in range(B):                                     # the merge kernel's view: super-run = run
+        if nb[b] == 0:
+            continue
+        r0, r1 = pre[b] // tw, (pre[b] + nb[b] - 1) // tw
+        for g in range(H_kv):
+            got = written[(b, g)]
+            if r0 == r1:
+                assert got == [None], (b, g, got)
+            else:
+                assert sorted(got) == [(r, (r + b) * H_kv + g) for r in range(r0, r1 + 1)], (b, g, got)
+    assert len(streamed) == total * H_kv
+    return runs, tw
+
+
+def test_mx4_c5_shaped_batch():
+    rng = random.Random(7)
+    lens = [rng.randint(4096, 16384) for _ in range(32)]
+    runs, tw = model_mx4(32, 64, 8, 128, 16384, 1024, lens, True, 8, 256)
+    assert runs == 256 and tw == -(-sum(-(-n // 16) for n in lens) // 256)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_mx4_random_batches(seed):
+    rng = random.Random(100 + seed)
+    done = 0
+    for _ in range(60):
+        nw = rng.choice([2, 4, 8])
+        H_kv = nw * rng.choice([1, 2, 3])
+        G = rng.choice([1, 2, 4, 8, 16])
+        B = rng.choice([1, 2, 3, 7, 32, 100, rng.randint(1, 1100)])
+        max_ctx = rng.choice([1, 16, 17, 100, 512, 2048, 5000])
+        P = rng.choice([16, 32, 256, 1024])
+        fused = rng.random() < 0.5
+        lens = []
+        for _ in range(B):
+            r = rng.random()
+            lens.append(0 if r < 0.05 else max_ctx + 1 if r < 0.08 else -3 if r < 0.1 else rng.randint(1, max_ctx))
+        res = model_mx4(B, G * H_kv, H_kv, rng.choice([64, 128]), max_ctx, P, lens, fused, nw,
+                        rng.choice([512, 256, 64, 3]))
+        done += res is not None
+    assert done >= 15

@@ -35,6 +35,7 @@ CASES = [
     ("fp8", "bf16", 64, 8, 1024, "gqa_mfma_fp8"),
     ("mx4", "f16", 8, 8, 0, "mxfp4 "),
     ("mx4", "bf16", 64, 8, 1024, "mxfp4_mfma "),
+    ("mx4_even", "bf16", 64, 8, 1024, "mxfp4_mfma_even "),   # the grouped MXFP4 kernel's even split, forced
 ]
 
 
@@ -78,9 +79,12 @@ def poison_intact(torch, t, lo, hi, poison):
 
 
 @pytest.mark.parametrize("kv,dtype,H_q,H_kv,P,prefix", CASES)
-def test_pool_above_4gib(torch_dev, kv, dtype, H_q, H_kv, P, prefix):
+def test_pool_above_4gib(torch_dev, monkeypatch, kv, dtype, H_q, H_kv, P, prefix):
     torch = torch_dev
     D = 128
+    if kv == "mx4_even":
+        monkeypatch.setenv("PKV_MX4_EVEN", "2")
+        kv = "mx4"
     base = {"16": "c3", "fp8": "c3f8", "mx4": "c3f4"}[kv]
     cfg = get_config(base, dtype=dtype, D=D, H_q=H_q, H_kv=H_kv, B=len(LENS), lengths=("fixed", LENS),
                      pool=("factor", 1.3), append=True, partition_size=P)

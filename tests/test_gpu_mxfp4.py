@@ -29,7 +29,25 @@ EDGE_LENS = (1, 2, 15, 16, 17, 31, 33, 64, 255, 257, 700)
 # (kernel kind, waves, blocks per chunk or in flight): kind 0 = per-head vector-unit kernel
 # (blocks per chunk), kind 1 = grouped MFMA kernel over an LDS ring (f16/bf16 q, G <= 16;
 # chunks in flight per wave)
-MX4_VARIANTS = ["0,4,2", "0,8,2", "1,4,1", "1,4,2", "1,4,3", "1,2,2", "1,2,4"]
+# kind 0: (nw, ch); kind 1: (nw, pf[, KV heads per workgroup])
+MX4_VARIANTS = ["0,4,2", "0,8,2", "1,4,1", "1,4,2", "1,4,3", "1,2,2", "1,2,4", "1,4,1,2", "1,4,2,2", "1,4,1,4",
+                "1,4,2,4", "1,8,1,4", "1,8,2,4", "1,8,1,8", "1,8,2,8", "1,8,3,8"]
+
+
+def mx4_variant_env(variant, H_kv):
+    """(environment, launch-string tag) of a variant.  A kind-1 variant whose heads per workgroup
+    do not divide H_kv runs with one head per workgroup, and if that shape is not built, as the
+    default (4 waves, 1 chunk in flight)."""
+    kind, nw, x, *hg = variant.split(",")
+    if kind == "0":
+        return {"PKV_MX4_KIND": kind, "PKV_MX4_NW": nw, "PKV_MX4_CH": x}, f"nw={nw} ch={x} "
+    hg = int(hg[0]) if hg else 1
+    env = {"PKV_MX4_KIND": kind, "PKV_MX4_NW": nw, "PKV_MX4_PF": x, "PKV_MX4_HG": str(hg)}
+    if H_kv % hg:
+        hg = 1
+        if f"1,{nw},{x}" not in MX4_VARIANTS:
+            nw, x = "4", "1"
+    return env, f"nw={nw} ch=1 pf={x} hg={hg} "
 
 
 @pytest.fixture(scope="module")
@@ -200,18 +218,18 @@ def test_mxfp4_attention_parity(torch_dev, dtype, D, H_q, H_kv, P, append):
 
 @pytest.mark.parametrize("variant", MX4_VARIANTS)
 def test_mxfp4_every_launch_variant(torch_dev, monkeypatch, variant):
-    kind, nw, x = variant.split(",")
-    monkeypatch.setenv("PKV_MX4_KIND", kind)
-    monkeypatch.setenv("PKV_MX4_NW", nw)
-    monkeypatch.setenv("PKV_MX4_PF" if kind == "1" else "PKV_MX4_CH", x)
+    kind = variant.split(",")[0]
     name = "mxfp4_mfma " if kind == "1" else "mxfp4 "
-    tag = f"nw={nw} ch=1 pf={x} " if kind == "1" else f"nw={nw} ch={x} "
-    # 4500 tokens unsplit: more than one 256-block window of ids per workgroup
+    # 4500 tokens unsplit: more than one 256-block window of ids per workgroup; 8 KV heads:
+    # every heads-per-workgroup count divides them
     cases = [("f16", 128, 0, 4, 4, True), ("bf16", 64, 64, 8, 2, True), ("bf16", 128, 256, 16, 1, False),
-             ("f16", 64, 0, 6, 2, False)]
+             ("f16", 64, 0, 6, 2, False), ("bf16", 128, 512, 32, 8, True), ("f16", 64, 0, 64, 8, False)]
     if kind == "0":
         cases.append(("f32", 128, 256, 4, 2, False))
     for dtype, D, P, H_q, H_kv, append in cases:
+        env, tag = mx4_variant_env(variant, H_kv)
+        for k, v in env.items():
+            monkeypatch.setenv(k, v)
         cfg = cfg_for(dtype, D, H_q, H_kv, (1, 17, 200, 1000, 2049, 4500), P=P, append=append)
         w = make_workload(cfg, 41)
         ref, pk, pv = oracle.run_step(w)

@@ -36,7 +36,7 @@ import oracle
 import paged_kv_decode_blocks_amd as pkv
 from tests.test_gpu_decode_loop import bits_equal
 from tests.test_gpu_fp8 import GQA8_VARIANTS
-from tests.test_gpu_mxfp4 import MX4_VARIANTS
+from tests.test_gpu_mxfp4 import MX4_VARIANTS, mx4_variant_env
 from tests.test_gpu_parity import GQA_VARIANTS, MHA_VARIANTS
 from workloads import get_config, make_peaked_workload, make_workload
 from workloads.device import to_numpy_bits, upload
@@ -69,6 +69,8 @@ FAMILIES = [
     ("mxfp4_mfma_bf16", "mxfp4", "bf16", 8, {"PKV_LP_MIN_PART": "0"}, "mxfp4_mfma "),
     ("mxfp4_mfma_f16", "mxfp4", "f16", 8, {"PKV_LP_MIN_PART": "0"}, "mxfp4_mfma "),
     ("mxfp4_mfma_floor_bf16", "mxfp4", "bf16", 8, {}, "mxfp4_mfma "),
+    ("mxfp4_even_bf16", "mxfp4", "bf16", 8, {"PKV_MX4_EVEN": "2"}, "mxfp4_mfma_even "),
+    ("mxfp4_even_f16", "mxfp4", "f16", 8, {"PKV_MX4_EVEN": "2"}, "mxfp4_mfma_even "),
 ]
 
 
@@ -238,9 +240,11 @@ def assert_pools(w, d, kp, vp):
 
 
 def expect(prefix, P):
-    """The launch-string prefix a family shows at partition size P (the even split is a
-    split-step plan: unsplit, the same family runs the grouped kernel with K in LDS)."""
-    return "gqa_mfma_kdma " if prefix == "gqa_mfma_even " and P == 0 else prefix
+    """The launch-string prefix a family shows at partition size P (the even splits are
+    split-step plans: unsplit, the same family runs the per-partition grouped kernel)."""
+    if P == 0:
+        return {"gqa_mfma_even ": "gqa_mfma_kdma ", "mxfp4_mfma_even ": "mxfp4_mfma "}.get(prefix, prefix)
+    return prefix
 
 
 def _setenv(monkeypatch, env):
@@ -365,10 +369,8 @@ def _variant_env(kind, v):
     if kind == "fp8":
         nw, ch, pf = v.split(",")
         return {"PKV_FP8_NW": nw, "PKV_FP8_CH": ch, "PKV_FP8_PF": pf}, f"nw={nw} ch={ch} pf={pf}"
-    k, nw, x = v.split(",")
-    env = {"PKV_MX4_KIND": k, "PKV_MX4_NW": nw, ("PKV_MX4_PF" if k == "1" else "PKV_MX4_CH"): x,
-           "PKV_LP_MIN_PART": "0"}
-    return env, (f"nw={nw} ch=1 pf={x} " if k == "1" else f"nw={nw} ch={x} ")
+    env, tag = mx4_variant_env(v, H_KV)
+    return {**env, "PKV_LP_MIN_PART": "0"}, tag
 
 
 @pytest.mark.parametrize("kind,variant", VARIANT_CASES, ids=[f"{k}-{v}" for k, v in VARIANT_CASES])
