@@ -64,6 +64,46 @@ __device__ __forceinline__ float merge_accumulate(const float* lse, int ls, cons
     return L;
 }
 
+// Rows of at most kFewPieces partial rows (the common case) are merged in one pass:
+// every lse and every partial row is loaded at once -- one round trip to memory instead
+// of one for the lse values and another for the rows -- and the rows are added in index
+// order with the weights merge_accumulate would use.
+constexpr int kFewPieces = 8;
+
+// acc += sum_p 2^(lse_p - M) o_p over np <= kFewPieces partial rows (lse at lse[p * ls], o_p
+// at po[p * os ..], lane l holding elements l, l + 64, ...); returns the sum of the weights,
+// sets M's NaN test in nan.
+template <int D>
+__device__ __forceinline__ float merge_few(const float* lse, int ls, const float* po, size_t os, int np, int lane,
+                                           float (&acc)[D / 64], bool& nan) {
+    constexpr int PER = D / 64;
+    float l[kFewPieces];
+    float v[kFewPieces][PER];
+#pragma unroll
+    for (int u = 0; u < kFewPieces; ++u) {
+        l[u] = u < np ? lse[(size_t)u * ls] : -__builtin_inff();
+#pragma unroll
+        for (int k = 0; k < PER; ++k) v[u][k] = u < np ? po[(size_t)u * os + lane + 64 * k] : 0.0f;
+    }
+    float M = l[0];
+    bool bad = l[0] != l[0];
+#pragma unroll
+    for (int u = 1; u < kFewPieces; ++u) {
+        M = fmaxf(M, l[u]);
+        bad |= l[u] != l[u];
+    }
+    nan = bad;
+    float L = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kFewPieces; ++u) {
+        const float w = u < np ? __builtin_amdgcn_exp2f(l[u] - M) : 0.0f;
+        L += w;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) acc[k] = fmaf(w, v[u][k], acc[k]);
+    }
+    return L;
+}
+
 // Split partitions: one wave per (request, head) row, row-contiguous partials.
 template <int D>
 __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeArgs a) {
@@ -86,11 +126,17 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeArgs a) {
     const float* lse = a.part_lse + (size_t)row * a.n_parts;
     const float* po = a.part_o + (size_t)row * a.n_parts * D;
     bool nan;
-    const float M = merge_max(lse, 1, np, lane, nan);
     float acc[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
-    const float inv = 1.0f / merge_accumulate<D>(lse, 1, po, D, np, M, lane, acc);
+    float L;
+    if (np <= kFewPieces) {
+        L = merge_few<D>(lse, 1, po, D, np, lane, acc, nan);
+    } else {
+        const float M = merge_max(lse, 1, np, lane, nan);
+        L = merge_accumulate<D>(lse, 1, po, D, np, M, lane, acc);
+    }
+    const float inv = 1.0f / L;
 #pragma unroll
     for (int k = 0; k < PER; ++k) o[lane + 64 * k] = nan ? __builtin_nanf("") : acc[k] * inv;
 }
@@ -156,12 +202,19 @@ __global__ __launch_bounds__(256) void lse_merge_even_kernel(const MergeArgs a) 
         }
         if (e.np == 0) return;
         bool nan;
-        const float M = merge_max(a.part_lse + e.first, a.H_q, e.np, lane, nan);
         float acc[PER];
 #pragma unroll
         for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
-        const float inv = 1.0f / merge_accumulate<D>(a.part_lse + e.first, a.H_q, a.part_o + e.first * D,
-                                                     (size_t)a.H_q * D, e.np, M, lane, acc);
+        float L;
+        if (e.np <= kFewPieces) {
+            L = merge_few<D>(a.part_lse + e.first, a.H_q, a.part_o + e.first * D, (size_t)a.H_q * D, e.np, lane, acc,
+                             nan);
+        } else {
+            const float M = merge_max(a.part_lse + e.first, a.H_q, e.np, lane, nan);
+            L = merge_accumulate<D>(a.part_lse + e.first, a.H_q, a.part_o + e.first * D, (size_t)a.H_q * D, e.np, M,
+                                    lane, acc);
+        }
+        const float inv = 1.0f / L;
 #pragma unroll
         for (int k = 0; k < PER; ++k) o[lane + 64 * k] = nan ? __builtin_nanf("") : acc[k] * inv;
         return;
