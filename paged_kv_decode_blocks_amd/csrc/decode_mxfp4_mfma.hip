@@ -1,6 +1,7 @@
 // decode_mxfp4_mfma.hip -- paged decode attention over an MXFP4 K/V cache on the
-// gfx950 matrix cores, one workgroup per (partition, request, KV head) serving
-// its G <= 16 query heads.
+// gfx950 matrix cores, one workgroup per (partition, request, group of KV heads)
+// -- or, for an even split of the batch, per (run of blocks, group of KV heads) --
+// each KV head serving its G <= 16 query heads.
 //
 // A 4-bit cache with fine-grained block scales ("从 PagedAttention 到
 // Prefill-Decode 分离的深度解析", section 6.2) quarters the bytes a step
@@ -32,7 +33,7 @@
 // m of output tile T is d = m D/16 + T, so V is never transposed.
 //
 // Softmax is online per query head in the log2 domain with the lazy rescale of
-// the 16-bit grouped kernel; waves merge through LDS; the partition's result
+// the 16-bit grouped kernel; the waves of a head merge through LDS; the result
 // goes to the output or, when split, to the log-sum-exp merge.  In the fused
 // step the new token is quantized inside the kernel, in the wave whose ring slot
 // holds its block (see APPEND below), so the step is one launch plus the merge.
