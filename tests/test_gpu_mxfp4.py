@@ -221,9 +221,11 @@ def test_mxfp4_every_launch_variant(torch_dev, monkeypatch, variant):
     kind = variant.split(",")[0]
     name = "mxfp4_mfma " if kind == "1" else "mxfp4 "
     # 4500 tokens unsplit: more than one 256-block window of ids per workgroup; 8 KV heads:
-    # every heads-per-workgroup count divides them
+    # every heads-per-workgroup count divides them; G = 16 on 4 KV heads: head groups on the
+    # one-block-per-product path
     cases = [("f16", 128, 0, 4, 4, True), ("bf16", 64, 64, 8, 2, True), ("bf16", 128, 256, 16, 1, False),
-             ("f16", 64, 0, 6, 2, False), ("bf16", 128, 512, 32, 8, True), ("f16", 64, 0, 64, 8, False)]
+             ("f16", 64, 0, 6, 2, False), ("bf16", 128, 512, 32, 8, True), ("f16", 64, 0, 64, 8, False),
+             ("bf16", 128, 256, 64, 4, True)]
     if kind == "0":
         cases.append(("f32", 128, 256, 4, 2, False))
     for dtype, D, P, H_q, H_kv, append in cases:
