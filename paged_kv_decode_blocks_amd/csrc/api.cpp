@@ -124,14 +124,19 @@ Plan make_plan(int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32
     // latency; a long unsplit context per workgroup spreads over more waves.
     const int64_t wgs = (int64_t)p.n_parts * B * (p.grouped ? H_kv : H_q);
     if (fp8 && p.grouped) {
+        // 4-wave workgroups, one block ahead per wave, K staged through LDS (whose slots also
+        // hold the closing merge: 35.6 KB, three workgroups per CU).  Against 2-wave ones on
+        // MI355X (8 KV heads, 64 query heads, D = 128, bf16 q): 32 x 4096-16384 +2.4 %,
+        // 128 x 512-4096 +5.9 %, 64 x 1024-8192 +3.7 %, 4 x 4096-16384 +28 %, 8 x 4096-32768
+        // even; two or three blocks ahead were slower.
         p.kind = 2;   // grouped heads on MFMA over FP8 codes
-        p.nw = env_int("PKV_GQA8_NW", 2);
+        p.nw = env_int("PKV_GQA8_NW", 4);
         p.ch = env_int("PKV_GQA8_CH", 1);
         p.pf = env_int("PKV_GQA8_PF", 1);
         p.wpe = env_int("PKV_GQA8_WPE", 2);
         p.kd = env_int("PKV_GQA8_KDMA", 1);
         if (!pkv::gqa_fp8_variant_exists(p.nw, p.ch, p.pf, p.wpe, p.kd)) {
-            p.nw = 2; p.ch = 1; p.pf = 1; p.wpe = 2; p.kd = 1;
+            p.nw = 4; p.ch = 1; p.pf = 1; p.wpe = 2; p.kd = 1;
         }
         p.grid = 0;   // after the partitions are final (below)
     } else if (fp8) {

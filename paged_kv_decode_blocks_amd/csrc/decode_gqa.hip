@@ -1518,16 +1518,19 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_gqa_fp8_kernel(const Attn
     static_assert(R <= 4, "ring depth");
     static_assert(!KDMA || PF * LPC < 64, "vmcnt range");
     // one LDS object per ring slot, so that alias analysis can tell a read of one
-    // slot from the DMAs still in flight into the others
-    __shared__ __attribute__((aligned(16))) char s_k0[KDMA ? NW * SLOT : 16];
-    __shared__ __attribute__((aligned(16))) char s_k1[KDMA ? NW * SLOT : 16];
+    // slot from the DMAs still in flight into the others; with KDMA the closing merge
+    // of the waves reuses the first two, sized for half of it each
+    constexpr int MERGE_HALF = (NW + 1) / 2 * 16 * (D + 4) * 4;
+    constexpr int S01 = !KDMA ? 16 : NW * SLOT > MERGE_HALF ? NW * SLOT : MERGE_HALF;
+    __shared__ __attribute__((aligned(16))) char s_k0[S01];
+    __shared__ __attribute__((aligned(16))) char s_k1[S01];
     __shared__ __attribute__((aligned(16))) char s_k2[KDMA && R > 2 ? NW * SLOT : 16];
     __shared__ __attribute__((aligned(16))) char s_k3[KDMA && R > 3 ? NW * SLOT : 16];
     __shared__ int32_t s_ids[kWindowBlocksG];
     __shared__ int s_bad;
     __shared__ float s_m[NW][16];
     __shared__ float s_l[NW][16];
-    __shared__ float s_o[NW * 16 * (D + 4)];
+    __shared__ float s_o[KDMA ? 4 : NW * 16 * (D + 4)];
 
     GqaUnit u;
     gqa_indices<true>(a, u);
@@ -1754,8 +1757,14 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_gqa_fp8_kernel(const Attn
         for (int q = 0; q < KL; ++q) kc[0][q] = c[0].k[q];
         st.template accumulate8<1>(kc, c, valid);
     }
-    st.template finish<NW, D + 4>(a, s_m, s_l, s_o, s_o + (NW + 1) / 2 * 16 * (D + 4), w, u.b, u.g, u.part,
-                                  s_bad != 0);
+    if constexpr (KDMA) {
+        __syncthreads();   // every wave is done with its ring slots: the merge reuses them
+        st.template finish<NW, D + 4>(a, s_m, s_l, reinterpret_cast<float*>(s_k0), reinterpret_cast<float*>(s_k1),
+                                      w, u.b, u.g, u.part, s_bad != 0);
+    } else {
+        st.template finish<NW, D + 4>(a, s_m, s_l, s_o, s_o + (NW + 1) / 2 * 16 * (D + 4), w, u.b, u.g, u.part,
+                                      s_bad != 0);
+    }
 }
 
 #define PKV_GQA_FP8_VARIANTS(X)                                                                       \
