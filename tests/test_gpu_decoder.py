@@ -36,9 +36,16 @@ def torch_dev():
     ("bf16", 8, 2, 128, 32, True, 307, "mx4"),     # grouped MFMA kernel, split, graphs
     ("f16", 4, 4, 128, 0, False, 308, "mx4"),      # per-head kernel, eager
     ("f32", 4, 2, 64, 64, True, 309, "mx4"),       # per-head kernel (f32 q), split, graphs
+    ("bf16", 8, 2, 128, 32, True, 310, "mx4_even"),   # grouped MXFP4 even split (forced), graphs
+    ("bf16", 16, 2, 128, 32, True, 311, "16_even"),   # grouped 16-bit even split (forced), graphs
 ])
-def test_decoder_matches_oracle(torch_dev, dtype, H_q, H_kv, D, P, graphs, seed, kv):
+def test_decoder_matches_oracle(torch_dev, monkeypatch, dtype, H_q, H_kv, D, P, graphs, seed, kv):
     t = torch_dev
+    even = kv.endswith("_even")
+    if even:   # the plans' even splits, wherever they fit (graph captures included)
+        kv = kv[:-len("_even")]
+        monkeypatch.setenv("PKV_MX4_EVEN" if kv == "mx4" else "PKV_GQA_EVEN", "2")
+    launches = set()
     fp8, mx4 = kv == "fp8", kv == "mx4"
     print(f"decoder {dtype} H_q={H_q} H_kv={H_kv} D={D} P={P} graphs={graphs} seed={seed} kv={kv}", flush=True)
     rng = np.random.default_rng(seed)
@@ -123,6 +130,7 @@ def test_decoder_matches_oracle(torch_dev, dtype, H_q, H_kv, D, P, graphs, seed,
         kn_buf[:B].copy_(to_tensor(kn, dtype, "cuda"))
         vn_buf[:B].copy_(to_tensor(vn, dtype, "cuda"))
         n_copies = dec.step(ids)
+        launches.add(pkv.last_launch().split(" ")[0])
 
         tables, positions, copies = ora.append_batch(ids, W)
         assert n_copies == len(copies)
@@ -150,6 +158,8 @@ def test_decoder_matches_oracle(torch_dev, dtype, H_q, H_kv, D, P, graphs, seed,
         for sid in ids:
             assert list(bm.block_table(sid)) == ora.block_table(sid)
     assert total_copies > 0, "the stream never exercised copy-on-write"
+    if even:
+        assert {"mxfp4_mfma_even", "gqa_mfma_even"} & launches, launches
     if fp8 or mx4:
         assert bits_equal(k.cpu().numpy(), kp) and bits_equal(v.cpu().numpy(), vp)
         assert bits_equal(ks_d.cpu().numpy(), ksc) and bits_equal(vs_d.cpu().numpy(), vsc)
