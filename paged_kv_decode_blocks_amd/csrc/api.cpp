@@ -126,9 +126,10 @@ Plan make_plan(int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32
     if (fp8 && p.grouped) {
         // 4-wave workgroups, one block ahead per wave, K staged through LDS (whose slots also
         // hold the closing merge: 35.6 KB, three workgroups per CU).  Against 2-wave ones on
-        // MI355X (8 KV heads, 64 query heads, D = 128, bf16 q): 32 x 4096-16384 +2.4 %,
-        // 128 x 512-4096 +5.9 %, 64 x 1024-8192 +3.7 %, 4 x 4096-16384 +28 %, 8 x 4096-32768
-        // even; two or three blocks ahead were slower.
+        // MI355X (8 KV heads, 64 query heads, D = 128, bf16 q; variants interleaved): 32 x
+        // 4096-16384 +2.3 %, 64 x 1024-8192 +3.8 %, 128 x 512-4096 +5.8 %, 4 x 4096-16384
+        // +26 %, 32 x 2048-8192 +0.8 %; 16 x 4096-16384 -0.7 %, 64 x 2048 -1.0 %, 8 x
+        // 4096-32768 -0.6 %.  Two or three blocks ahead were slower.
         p.kind = 2;   // grouped heads on MFMA over FP8 codes
         p.nw = env_int("PKV_GQA8_NW", 4);
         p.ch = env_int("PKV_GQA8_CH", 1);
@@ -309,13 +310,13 @@ int64_t mx4_even_resident_wgs(int dtype, int32_t D, int nw, int pf, int G, bool 
 // Returns whether the plan took it (p: nw, pf, hg, even_waves, grid).
 //
 // Gate, from MI355X against the per-partition kernel at its 2048-token floor (8 KV heads,
-// 64 query heads, D = 128, bf16 q, 4-head workgroups; ctx uniform in the range): 32 x
-// 4096-16384 +2 %, 48 x 4096-16384 +8.5 %, 64 x 1024-8192 +4 %, 24 x 8192-32768 +4 %;
-// 128 x 512-4096 -0.6 %, 32 x 2048-8192 -5 %, 16 x 4096-16384 -12 % (8-head workgroups
-// 0-3 % behind 4-head ones throughout).  The losing batches' worst case (B requests of the
-// longest context) is 64 blocks per run of one resident round, the winning ones' 125 or
-// more.  So: 4-head workgroups, a worst case of at least 96 blocks per run, and a longest
-// context of at least 8192 tokens.
+// 64 query heads, D = 128, bf16 q, 4-head workgroups; ctx uniform in the range; variants
+// interleaved): 48 x 4096-16384 +6.2 %, 64 x 1024-8192 +2.2 %, 24 x 8192-32768 +0.5 %,
+// 32 x 4096-16384 -0.2 %; 128 x 512-4096 -2.2 %, 32 x 2048-8192 -8 %, 16 x 4096-16384
+// -17 % (8-head workgroups 0-3 % behind 4-head ones).  The losing batches' worst case (B
+// requests of the longest context) is 64 blocks per run of one resident round, or their
+// contexts are short; the others' 125 or more.  So: 4-head workgroups, a worst case of at
+// least 96 blocks per run, and a longest context of at least 8192 tokens.
 bool mx4_even_plan(Plan& p, int dtype, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t max_ctx,
                    bool fused) {
     const int mode = env_int("PKV_MX4_EVEN", 1);
