@@ -12,6 +12,10 @@ request gets either one output or its super-runs' pieces, exactly the ids the me
 kernel reads; piece rows and the prefix fit the workspace that pkv_decode_workspace_bytes
 sizes for the caller's partition.  The plan's sizing (runs, the workspace cap) is the
 library's, restated.
+
+The grouped MXFP4 kernel's even split is modelled the same way (plan_mx4, model_mx4): one run per
+workgroup, streamed for nw KV heads at once (a wave per head), its pieces written straight to the
+workspace with the run as the merge kernel's super-run.
 """
 import random
 
