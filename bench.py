@@ -256,6 +256,92 @@ def resident_steps(lib, torch, pkv, dev, w, append: bool, P: int, R: int):
     return calls, sets
 
 
+# (pattern, tile bytes, scale tiles, paths, teams, depths): the per-(block, KV head) reads of the
+# grouped kernels at D = 128 -- MXFP4 codes 1 KiB per tile, FP8 codes 2 KiB, bf16 4 KiB; scale
+# tiles 64 bytes per pool; paths bit 1 / 2 / 4 moves K / V / scales by DMA into LDS; depth =
+# items in flight per wave.  The grouped MXFP4 kernel moves all three by DMA, one head per wave
+# or a team of neighbouring heads (K, or K and V, into registers beside it for comparison); the
+# FP8 kernel moves K by DMA and V and the scales into registers; the bf16 kernel has both.
+TILE_PATTERNS = (
+    ("mxfp4_registers", 1024, True, 0, (1, 4), (2, 4, 8)),
+    ("mxfp4_dma", 1024, True, 7, (1, 4), (2, 4, 8)),
+    ("mxfp4_k_registers", 1024, True, 6, (1, 4), (2, 4, 8)),
+    ("mxfp4_kv_registers", 1024, True, 4, (1, 4), (2, 4, 8)),
+    ("fp8_k_dma", 2048, True, 1, (1, 2, 4), (4,)),
+    ("bf16_registers", 4096, False, 0, (1,), (4,)),
+    ("bf16_k_dma", 4096, False, 1, (1,), (4,)),
+)
+
+
+def tileprobe_bench(args, torch, pkv, dev) -> int:
+    """The read rate of the grouped kernels' access patterns without their arithmetic
+    (pkv_probe_tile_read), beside the plain streaming read: K/V pools of 512 Ki blocks x 8 KV
+    heads (4, 8 or 16 GiB each, by tile size), about 1 GiB read per launch, item t reading block
+    ids[t] for head group t mod (8 / team) with no tile read twice in one launch; four id sets
+    rotate.  Each (pattern, team, depth, grid) point: four untimed launches, then 16 timed with events
+    on the launch stream.  Grids of 512 .. 2048 four-wave workgroups put 8 .. 32 waves on each
+    of the 256 CUs where the probe's registers and LDS let them be resident."""
+    heads, n_blocks, reps, target = 8, 512 << 10, 16, 1 << 30
+    big = n_blocks * heads * 4096
+    kp = torch.zeros(big // 4, dtype=torch.int32, device=dev)
+    vp = torch.zeros(big // 4, dtype=torch.int32, device=dev)
+    ks = torch.zeros(n_blocks * heads * 64 // 4, dtype=torch.int32, device=dev)
+    vs = torch.zeros_like(ks)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    rng = np.random.default_rng(args.seed or 7)
+    ceiling = read_ceiling(pkv, torch, dev)
+    grids = (512, 768, 1024, 2048)
+    results = []
+
+    def id_sets(tile, scales, team):
+        groups = heads // team
+        n = target // (team * (2 * tile + (128 if scales else 0))) // groups * groups
+        out = []
+        for _ in range(4):
+            # item t takes head group t mod groups: per group, distinct blocks
+            per = rng.permuted(np.tile(np.arange(n_blocks, dtype=np.int32), (groups, 1)), axis=1)[:, :n // groups]
+            ids = np.ascontiguousarray(per.T).reshape(-1)
+            assert ids.size == n and ids.min() >= 0 and ids.max() < n_blocks
+            out.append(torch.from_numpy(ids).to(dev))
+        return out
+
+    def launch(sets, k, tile, scales, team, paths, depth, grid):
+        return pkv.probe_tile_read(kp, vp, sets[k % 4], sink, heads=heads, tile_bytes=tile, team=team, paths=paths,
+                                   depth=depth, k_scale=ks if scales else None, v_scale=vs if scales else None,
+                                   grid=grid, stream=stream)
+
+    first = True
+    cached = {}
+    for name, tile, scales, paths, teams, depths in TILE_PATTERNS:
+        for team in teams:
+            if (tile, scales, team) not in cached:
+                cached[(tile, scales, team)] = id_sets(tile, scales, team)
+            sets = cached[(tile, scales, team)]
+            for depth in depths:
+                for grid in grids:
+                    for k in range(8 if first else 4):      # the first point of a process runs slow: warm up longer
+                        launch(sets, k, tile, scales, team, paths, depth, grid)
+                    first = False
+                    torch.cuda.synchronize()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    nbytes = 0
+                    for k in range(reps):
+                        nbytes += launch(sets, k, tile, scales, team, paths, depth, grid)
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    sec = e0.elapsed_time(e1) / 1e3
+                    results.append({"pattern": name, "tile_bytes": tile, "scales": scales, "paths": paths,
+                                    "team": team, "depth": depth, "grid": grid,
+                                    "us_per_launch": round(sec / reps * 1e6, 2), "GBps": round(nbytes / sec / 1e9, 1)})
+                    print(json.dumps(results[-1]), file=sys.stderr, flush=True)
+    print(json.dumps({"mode": "tileprobe", "unit": "GB/s", "stream_read_GBps": round(ceiling, 1),
+                      "heads": heads, "n_blocks": n_blocks, "bytes_per_launch_approx": target, "timed_launches": reps,
+                      "results": results}))
+    return 0
+
+
 def cumask_bench(args) -> int:
     """Decode-step bandwidth on CU-limited streams, alone and beside a GEMM.
 
@@ -723,7 +809,7 @@ def main(argv=None):
                     help="only run a plain device copy of BYTES bytes 5 times (scales HBM byte counters)")
     ap.add_argument("--local", default="c2", help="dual mode: the local batch's workload")
     ap.add_argument("--offloaded", default="c2", help="dual mode: the offloaded batch's workload")
-    ap.add_argument("--mode", default="step", choices=["step", "loop", "cumask", "cufrac", "dual"],
+    ap.add_argument("--mode", default="step", choices=["step", "loop", "cumask", "cufrac", "dual", "tileprobe"],
                     help="step: the headline step over resident inputs; loop: a block-manager-driven decode loop")
     ap.add_argument("--graphs", action="store_true", help="loop mode: replay captured step graphs")
     ap.add_argument("--native", action="store_true", help="loop mode: one pkv_decoder_step call per step")
@@ -776,6 +862,8 @@ def main(argv=None):
         return dual_bench(args, torch, pkv, dev)
     if args.mode == "cufrac":
         return cufrac_bench(args, torch, pkv, dev, lib)
+    if args.mode == "tileprobe":
+        return tileprobe_bench(args, torch, pkv, dev)
 
     names = [args.config] + [c for c in (args.also.split(",") if args.also not in ("", "none") else [])
                              if c and c != args.config]

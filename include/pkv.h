@@ -324,6 +324,42 @@ int pkv_append_decode_attention_persistent(int dtype,
 int pkv_probe_stream_read(const void* buf, size_t bytes, void* sink, int32_t grid, void* stream);
 
 /*
+ * probe_tile_read -- measurement aid, not part of the decode step: the reads a
+ * paged decode kernel makes of its KV cache, without the arithmetic, so that the
+ * rate of a kernel's own access pattern can be timed next to the plain stream.
+ * A request's history sits in fixed-size blocks of a shared pool at places its
+ * page table gives ("从 PagedAttention 到 Prefill-Decode 分离的深度解析",
+ * section 2.2); here the block ids are the caller's, random in a measurement.
+ *   k_pool, v_pool    device, [n_blocks][heads][tile_bytes], 16-byte aligned.
+ *   k_scale, v_scale  device, [n_blocks][heads][64 bytes], or both NULL (no
+ *                     scale reads); 4-byte aligned.
+ *   block_ids         device int32 [n_items]; an id outside [0, n_blocks) reads
+ *                     block 0.
+ *   team              1, 2 or 4 waves of one workgroup (4 waves, 256 threads)
+ *                     take an item together: block block_ids[t] and the team's
+ *                     neighbouring heads team (t mod heads/team) + 0 .. team-1,
+ *                     one head per wave.  heads % team == 0.
+ *   paths             bit 1: K tiles, bit 2: V tiles, bit 4: scale tiles go
+ *                     global -> LDS (global_load_lds); otherwise register
+ *                     loads.
+ *   depth             items whose loads each wave has in flight at once.
+ *                     Built: depth 4 with tile_bytes 1024, 2048, 4096 and paths
+ *                     0, 1, 5, with 1024 and 2048 and paths 7, and with 1024
+ *                     and paths 4, 6; depths 2 and 8 with tile_bytes 1024 and
+ *                     paths 0, 4, 6, 7 (PKV_ERR_UNSUPPORTED otherwise).
+ *   grid              1 .. 65536 workgroups; teams walk the items grid-stride.
+ *   sink              device word written only if the loaded data fold to one
+ *                     particular value.
+ * Bytes read: n_items * team * (2 tile_bytes + 128 if scales).  n_items = 0
+ * launches nothing.  Errors: PKV_ERR_NULL, PKV_ERR_INVALID_ARG (alignment,
+ * ranges, team), PKV_ERR_UNSUPPORTED, PKV_ERR_HIP (launch).
+ */
+int pkv_probe_tile_read(const void* k_pool, const void* v_pool, const void* k_scale, const void* v_scale,
+                        int32_t n_blocks, int32_t heads, int32_t tile_bytes, const int32_t* block_ids,
+                        int32_t n_items, int32_t team, int32_t paths, int32_t depth, void* sink, int32_t grid,
+                        void* stream);
+
+/*
  * probe_mfma_burn -- measurement aid, not part of the decode step: a compute-
  * bound neighbour for the step on a share of the CUs ("Injecting Adrenaline
  * into LLM Serving" review, section 3.3.1: decode attention beside compute-bound

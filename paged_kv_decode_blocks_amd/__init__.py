@@ -49,7 +49,7 @@ EXPORTED_SYMBOLS = (
     "pkv_append_decode_attention_persistent", "pkv_append_decode_attention_noalloc", "pkv_check_step_metadata",
     "pkv_probe_mfma_burn", "pkv_probe_gemm_bf16", "pkv_dual_step_graphs_create", "pkv_dual_step_graphs_launch",
     "pkv_dual_step_graphs_destroy",
-    "pkv_probe_stream_read", "pkv_copy_blocks", "pkv_copy_blocks_fp8", "pkv_kv_append_fp8", "pkv_paged_decode_attention_fp8",
+    "pkv_probe_stream_read", "pkv_probe_tile_read", "pkv_copy_blocks", "pkv_copy_blocks_fp8", "pkv_kv_append_fp8", "pkv_paged_decode_attention_fp8",
     "pkv_append_decode_attention_fp8", "pkv_kv_append_mxfp4", "pkv_paged_decode_attention_mxfp4",
     "pkv_append_decode_attention_mxfp4", "pkv_copy_blocks_mxfp4",
     "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add_sequence", "pkv_bm_add_sequence_shared", "pkv_bm_fork",
@@ -148,6 +148,8 @@ def load_library(path: Optional[str] = None):
     lib.pkv_probe_gemm_bf16.restype = ctypes.c_int
     lib.pkv_probe_stream_read.argtypes = [P, SZ, P, I32, P]
     lib.pkv_probe_stream_read.restype = ctypes.c_int
+    lib.pkv_probe_tile_read.argtypes = [P, P, P, P, I32, I32, I32, P, I32, I32, I32, I32, P, I32, P]
+    lib.pkv_probe_tile_read.restype = ctypes.c_int
     lib.pkv_kv_append_fp8.argtypes = [ctypes.c_int, P, P, I64, P, P, P, P, P, I32, P, I32, I32, I32, I32, I32, P]
     lib.pkv_kv_append_fp8.restype = ctypes.c_int
     lib.pkv_paged_decode_attention_fp8.argtypes = [ctypes.c_int, P, P, I64, P, P, P, P, P, I32, P,
@@ -256,6 +258,29 @@ def probe_stream_read(buf, sink, grid: int = 16384, *, nbytes: Optional[int] = N
     _require(0 <= nbytes <= total, "nbytes exceeds the buffer")
     _check(load_library().pkv_probe_stream_read(_ptr(buf), nbytes, _ptr(sink), int(grid), _stream(stream)),
            "probe_stream_read")
+
+
+def probe_tile_read(k_pool, v_pool, block_ids, sink, *, heads: int, tile_bytes: int, team: int = 1,
+                    paths: int = 0, depth: int = 4, k_scale=None, v_scale=None, n_items: Optional[int] = None,
+                    grid: int = 1024, stream=None):
+    """Launch the tile-read measurement kernel: item t reads `team` neighbouring heads of block
+    block_ids[t] from K/V pools viewed as [n_blocks][heads][tile_bytes] (and 64-byte scale tiles
+    if k_scale / v_scale are given); `paths` bit 1 / 2 / 4 moves K / V / scale tiles by DMA into
+    LDS; each wave keeps `depth` items in flight.  Returns the bytes read."""
+    torch = _torch()
+    nbytes = lambda t: t.numel() * t.element_size()
+    _require(block_ids.dtype == torch.int32 and block_ids.is_contiguous(), "block_ids int32, contiguous")
+    _require((k_scale is None) == (v_scale is None), "k_scale and v_scale: both or neither")
+    n_blocks = min(nbytes(k_pool), nbytes(v_pool)) // (int(heads) * int(tile_bytes))
+    if k_scale is not None:
+        n_blocks = min(n_blocks, min(nbytes(k_scale), nbytes(v_scale)) // (int(heads) * 64))
+    n_items = block_ids.numel() if n_items is None else int(n_items)
+    _require(0 <= n_items <= block_ids.numel(), "n_items exceeds block_ids")
+    _check(load_library().pkv_probe_tile_read(_ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), n_blocks,
+                                              int(heads), int(tile_bytes), _ptr(block_ids), n_items, int(team),
+                                              int(paths), int(depth), _ptr(sink), int(grid), _stream(stream)),
+           "probe_tile_read")
+    return n_items * int(team) * (2 * int(tile_bytes) + (128 if k_scale is not None else 0))
 
 
 def probe_gemm_bf16(a, b_t, c, n_workgroups: int, *, stream=None):

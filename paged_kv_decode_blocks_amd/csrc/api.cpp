@@ -894,6 +894,50 @@ int pkv_probe_stream_read(const void* buf, size_t bytes, void* sink, int32_t gri
     return PKV_OK;
 }
 
+int pkv_probe_tile_read(const void* k_pool, const void* v_pool, const void* k_scale, const void* v_scale,
+                        int32_t n_blocks, int32_t heads, int32_t tile_bytes, const int32_t* block_ids,
+                        int32_t n_items, int32_t team, int32_t paths, int32_t depth, void* sink, int32_t grid,
+                        void* stream) {
+    if (!k_pool || !v_pool || !block_ids || !sink)
+        return fail(PKV_ERR_NULL, "k_pool, v_pool, block_ids and sink must not be NULL");
+    if (!k_scale != !v_scale) return fail(PKV_ERR_NULL, "k_scale and v_scale: both or neither");
+    if (!aligned16(k_pool) || !aligned16(v_pool) || (reinterpret_cast<uintptr_t>(k_scale) & 3u) ||
+        (reinterpret_cast<uintptr_t>(v_scale) & 3u) || (reinterpret_cast<uintptr_t>(block_ids) & 3u) ||
+        (reinterpret_cast<uintptr_t>(sink) & 3u))
+        return fail(PKV_ERR_INVALID_ARG, "pools must be 16-byte aligned; scales, block_ids and sink 4-byte aligned");
+    if (n_blocks <= 0 || heads <= 0 || n_items < 0 || n_items > (1 << 30) || grid <= 0 || grid > 65536)
+        return fail(PKV_ERR_INVALID_ARG, "n_blocks = %d, heads = %d, n_items = %d, grid = %d", n_blocks, heads,
+                    n_items, grid);
+    if (team != 1 && team != 2 && team != 4)
+        return fail(PKV_ERR_INVALID_ARG, "team = %d (1, 2 or 4 waves)", team);
+    if (heads % team) return fail(PKV_ERR_INVALID_ARG, "heads = %d is not a multiple of team = %d", heads, team);
+    if ((paths & 4) && !k_scale) return fail(PKV_ERR_INVALID_ARG, "paths = %d moves scales but there are none", paths);
+    if (!pkv::tile_read_variant_exists(tile_bytes, paths, team, depth))
+        return fail(PKV_ERR_UNSUPPORTED, "tile_bytes = %d, paths = %d, depth = %d (built: depth 4 with tiles 1024, "
+                    "2048, 4096 and paths 0, 1, 5, tiles up to 2048 also 7, 1024 also 4, 6; depths 2 and 8 with "
+                    "tiles 1024 and paths 0, 4, 6, 7)", tile_bytes, paths, depth);
+    if (n_items == 0) {
+        g_err[0] = 0;
+        return PKV_OK;
+    }
+    pkv::TileReadArgs a{};
+    a.k_pool = static_cast<const char*>(k_pool);
+    a.v_pool = static_cast<const char*>(v_pool);
+    a.k_scale = static_cast<const char*>(k_scale);
+    a.v_scale = static_cast<const char*>(v_scale);
+    a.ids = block_ids;
+    a.sink = reinterpret_cast<unsigned*>(sink);
+    a.n_blocks = n_blocks;
+    a.heads = heads;
+    a.n_items = n_items;
+    a.scales = k_scale != nullptr;
+    hipError_t e = pkv::launch_tile_read(a, tile_bytes, paths, team, depth, grid,
+                                         reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "probe launch: %s", hipGetErrorString(e));
+    g_err[0] = 0;
+    return PKV_OK;
+}
+
 int pkv_copy_blocks(int dtype, void* k_pool, void* v_pool, const int32_t* src, const int32_t* dst, int32_t n,
                     int32_t H_kv, int32_t D, int32_t block_size, int32_t n_blocks, void* stream) {
     const int eb = elem_bytes(dtype);

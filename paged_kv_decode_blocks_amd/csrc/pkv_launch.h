@@ -122,6 +122,21 @@ bool gqa_even_variant_exists(int nw, int pf);
 // workgroups of that variant resident on one CU of the current device (0 on error)
 int gqa_even_wgs_per_cu(int dtype, int D, int nw, int pf, bool append);
 hipError_t launch_stream_read(const void* buf, size_t bytes, unsigned* sink, int grid, hipStream_t stream);
+// reads of [n_blocks][heads][tile] K/V pools (and [..][64] scale pools) in a decode kernel's pattern
+struct TileReadArgs {
+    const char* k_pool;
+    const char* v_pool;
+    const char* k_scale;   // both scale pools, or neither (scales = 0)
+    const char* v_scale;
+    const int32_t* ids;    // [n_items] block ids; one outside [0, n_blocks) reads block 0
+    unsigned* sink;
+    int32_t n_blocks, heads, n_items, scales;
+};
+bool tile_read_variant_exists(int tile_bytes, int paths, int team, int depth);
+// `grid` workgroups of 4 waves; teams of `team` waves; `paths` bit 1 K, 2 V, 4 scales by DMA into LDS;
+// `depth` items in flight per wave
+hipError_t launch_tile_read(const TileReadArgs& a, int tile_bytes, int paths, int team, int depth, int grid,
+                            hipStream_t stream);
 // `grid` 16-wave workgroups, one per CU, each running bf16 MFMA chains for `iterations` rounds
 hipError_t launch_mfma_burn(int grid, int iterations, unsigned* sink, hipStream_t stream);
 struct GemmArgs {

@@ -35,6 +35,123 @@ hipError_t launch_stream_read(const void* buf, size_t bytes, unsigned* sink, int
     return hipGetLastError();
 }
 
+// The per-(block, KV head) reads of a paged decode kernel, without its
+// arithmetic: K and V pools of [n_blocks][heads][TILE bytes] and, optionally,
+// K and V scale pools of [n_blocks][heads][64 bytes].  A team of TEAM waves of
+// one workgroup (4 waves) takes item t: block ids[t] and the TEAM neighbouring
+// heads that start at TEAM (t mod heads / TEAM), one head per wave, so that the
+// team's K (and V) tiles are TEAM TILE contiguous bytes.  Teams walk the items
+// grid-stride, NI items in flight per wave.  Each path is a register load
+// (16 bytes per lane, the scales 4 bytes per lane on lanes 0..31) or, where the
+// PATHS bit is set (1 K, 2 V, 4 scales), global_load_lds into a per-wave LDS
+// ring slot -- the two ways the decode kernels move a tile.  Loaded data fold
+// into one word that is written to `sink` only if it hits one value.
+namespace {
+__device__ __forceinline__ void probe_dma(const void* src, void* lds_base, int bytes16) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    if (bytes16)
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+    else
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
+#else
+    (void)src;
+    (void)lds_base;
+    (void)bytes16;
+#endif
+}
+}  // namespace
+
+template <int TILE, int PATHS, int TEAM, int NI>
+__global__ __launch_bounds__(256) void tile_read_kernel(const TileReadArgs a) {
+    constexpr bool KD = PATHS & 1, VD = PATHS & 2, SD = PATHS & 4;
+    constexpr int NL = TILE / 1024;            // 16-byte loads per lane per tile
+    constexpr int SLOT = (KD ? TILE : 0) + (VD ? TILE : 0) + (SD ? 128 : 0);
+    constexpr int TPW = 4 / TEAM;              // teams per workgroup
+    __shared__ __attribute__((aligned(16))) char ring[4][NI][SLOT > 0 ? SLOT : 16];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int team = blockIdx.x * TPW + w / TEAM;
+    const int n_teams = gridDim.x * TPW;
+    const int groups = a.heads / TEAM;
+    const char* sp = lane < 16 ? a.k_scale : a.v_scale;
+    unsigned acc = 0;
+    for (int t0 = team; t0 < a.n_items; t0 += NI * n_teams) {
+        u32x4_t k[NI][KD ? 1 : NL], v[NI][VD ? 1 : NL];
+        unsigned s[NI];
+#pragma unroll
+        for (int u = 0; u < NI; ++u) {
+            // an item past the end re-reads item t0 (whose tiles are then in the caches)
+            const int t = t0 + u * n_teams < a.n_items ? t0 + u * n_teams : t0;
+            int id = a.ids[t];
+            id = (unsigned)id < (unsigned)a.n_blocks ? id : 0;
+            const size_t tile = (size_t)id * a.heads + (size_t)(t % groups) * TEAM + w % TEAM;
+            const char* kt = a.k_pool + tile * TILE + 16 * lane;
+            const char* vt = a.v_pool + tile * TILE + 16 * lane;
+            char* dst = ring[w][u];
+#pragma unroll
+            for (int j = 0; j < NL; ++j) {
+                if constexpr (KD) probe_dma(kt + 1024 * j, dst + 1024 * j, 1);
+                else k[u][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kt + 1024 * j));
+                if constexpr (VD) probe_dma(vt + 1024 * j, dst + (KD ? TILE : 0) + 1024 * j, 1);
+                else v[u][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vt + 1024 * j));
+            }
+            s[u] = 0;
+            if (a.scales && lane < 32) {
+                const char* st = sp + tile * 64 + 4 * (lane & 15);
+                if constexpr (SD) probe_dma(st, dst + (KD ? TILE : 0) + (VD ? TILE : 0), 0);
+                else s[u] = *reinterpret_cast<const unsigned*>(st);
+            }
+        }
+        if constexpr (PATHS != 0) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        }
+#pragma unroll
+        for (int u = 0; u < NI; ++u) {
+            acc ^= s[u];
+            if constexpr (PATHS != 0) acc ^= *reinterpret_cast<const unsigned*>(ring[w][u] + 4 * lane);
+#pragma unroll
+            for (int j = 0; j < (KD ? 0 : NL); ++j) acc ^= k[u][j].x ^ k[u][j].y ^ k[u][j].z ^ k[u][j].w;
+#pragma unroll
+            for (int j = 0; j < (VD ? 0 : NL); ++j) acc ^= v[u][j].x ^ v[u][j].y ^ v[u][j].z ^ v[u][j].w;
+        }
+        if constexpr (PATHS != 0) __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    }
+    if (acc == 0x9E3779B9u) a.sink[0] = acc;
+}
+
+// built (tile bytes, paths, items in flight per wave): every tile with paths 0, 1, 5 at depth 4;
+// up to 2 KiB tiles also paths 7; 1 KiB tiles also paths 4 and 6 (K, or K and V, into registers
+// beside DMA'd scales), and at depths 2 and 8 as well
+#define PKV_TILE_READ_VARIANTS(X) \
+    X(1024, 0, 2) X(1024, 4, 2) X(1024, 6, 2) X(1024, 7, 2) \
+    X(1024, 0, 4) X(1024, 1, 4) X(1024, 4, 4) X(1024, 5, 4) X(1024, 6, 4) X(1024, 7, 4) \
+    X(1024, 0, 8) X(1024, 4, 8) X(1024, 6, 8) X(1024, 7, 8) \
+    X(2048, 0, 4) X(2048, 1, 4) X(2048, 5, 4) X(2048, 7, 4) X(4096, 0, 4) X(4096, 1, 4) X(4096, 5, 4)
+
+bool tile_read_variant_exists(int tile_bytes, int paths, int team, int depth) {
+    if (team != 1 && team != 2 && team != 4) return false;
+#define PKV_X(T, P, N) if (tile_bytes == T && paths == P && depth == N) return true;
+    PKV_TILE_READ_VARIANTS(PKV_X)
+#undef PKV_X
+    return false;
+}
+
+hipError_t launch_tile_read(const TileReadArgs& a, int tile_bytes, int paths, int team, int depth, int grid,
+                            hipStream_t stream) {
+#define PKV_X(T, P, N)                                                                                   \
+    if (tile_bytes == T && paths == P && depth == N) {                                                   \
+        if (team == 1) hipLaunchKernelGGL((tile_read_kernel<T, P, 1, N>), dim3(grid), dim3(256), 0, stream, a); \
+        else if (team == 2) hipLaunchKernelGGL((tile_read_kernel<T, P, 2, N>), dim3(grid), dim3(256), 0, stream, a); \
+        else if (team == 4) hipLaunchKernelGGL((tile_read_kernel<T, P, 4, N>), dim3(grid), dim3(256), 0, stream, a); \
+        else return hipErrorInvalidValue;                                                                \
+        return hipGetLastError();                                                                        \
+    }
+    PKV_TILE_READ_VARIANTS(PKV_X)
+#undef PKV_X
+    return hipErrorInvalidValue;
+}
+
 // A compute-bound neighbour for measurements of the decode step on a share of
 // the CUs.  Each workgroup is 16 waves and holds 100 KiB of LDS, so neither a
 // second workgroup of this kernel nor one of the persistent decode step fits

@@ -157,6 +157,39 @@ def test_mfma_burn_validation(lib):
         assert f(n_wg, iters, FAKE, None) == E_ARG
 
 
+def test_tile_read_probe_validation(lib):
+    f = lib.pkv_probe_tile_read
+    # k_pool, v_pool, k_scale, v_scale, n_blocks, heads, tile_bytes, ids, n_items, team, paths, depth, sink, grid,
+    # stream
+    args = [FAKE, FAKE, FAKE, FAKE, 64, 8, 1024, FAKE, 0, 4, 7, 4, FAKE, 1024, None]
+    assert f(*args) == OK                       # no items: nothing launched
+
+    def call(**kw):
+        names = ("k", "v", "ks", "vs", "n_blocks", "heads", "tile", "ids", "n", "team", "paths", "depth", "sink",
+                 "grid")
+        a = list(args)
+        for key, val in kw.items():
+            a[names.index(key)] = val
+        return f(*a)
+
+    for key in ("k", "v", "ids", "sink", "ks"):
+        assert call(**{key: None}) == E_NULL, key
+    assert call(ks=None, vs=None, paths=1) == OK   # no scale pools: scales are not read
+    assert call(ks=None, vs=None) == E_ARG         # paths 7 moves scale tiles that are not there
+    assert call(k=FAKE + 8) == E_ARG
+    assert call(ks=FAKE + 2) == E_ARG
+    for key, val in (("n", -1), ("n", (1 << 30) + 1), ("grid", 0), ("grid", 65537), ("n_blocks", 0),
+                     ("heads", 0), ("team", 3), ("team", 8)):
+        assert call(**{key: val}) == E_ARG, (key, val)
+    assert call(heads=6) == E_ARG               # 6 heads are not a multiple of a 4-wave team
+    assert call(heads=6, team=2) == OK
+    for tile, paths, depth in ((4096, 7, 4), (512, 0, 4), (1024, 2, 4), (1024, 3, 4), (2048, 6, 4), (8192, 0, 4),
+                               (1024, 1, 2), (1024, 7, 3), (1024, 7, 16), (2048, 0, 8), (4096, 0, 2)):
+        assert call(tile=tile, paths=paths, depth=depth) == E_UNSUP, (tile, paths, depth)
+    for depth in (2, 8):
+        assert call(depth=depth) == OK
+
+
 def test_mxfp4_validation(lib):
     ap = lib.pkv_kv_append_mxfp4
     args = [1, FAKE, FAKE, 8 * 128, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 4, 8, 128, 16, 1024, None]

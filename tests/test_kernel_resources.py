@@ -39,3 +39,21 @@ def test_headline_kernels_keep_their_occupancy(usage):
     for k, occ in want.items():
         assert k in usage, k
         assert usage[k]["Occupancy"] >= occ, (k, usage[k])
+
+
+def test_tile_read_probe_occupancy(usage):
+    """The read probe's waves per SIMD for the grouped kernels' patterns, as the compiler counts
+    them (4 items in flight per wave: an LDS ring for the DMA paths, registers for the rest): the resident
+    waves per CU are 4x these, which caps what a larger grid adds."""
+    want = {
+        (1024, 0): 8,    # MXFP4 codes and scales into registers
+        (1024, 7): 4,    # MXFP4 codes and scales by DMA: 34 KiB of LDS per workgroup
+        (2048, 1): 5,    # FP8: K by DMA (32 KiB), V and scales into registers
+        (4096, 0): 3,    # bf16 into registers
+        (4096, 1): 2,    # bf16, K by DMA (64 KiB)
+    }
+    for (tile, paths), occ in want.items():
+        for team in (1, 2, 4):
+            k = f"void pkv::tile_read_kernel<{tile}, {paths}, {team}, 4>(pkv::TileReadArgs)"
+            assert k in usage, k
+            assert usage[k]["Occupancy"] == occ, (k, usage[k])
