@@ -68,7 +68,7 @@ __device__ __forceinline__ float merge_accumulate(const float* lse, int ls, cons
 // every lse and every partial row is loaded at once -- one round trip to memory instead
 // of one for the lse values and another for the rows -- and the rows are added in index
 // order with the weights merge_accumulate would use.
-constexpr int kFewPieces = 8;
+constexpr int kFewPieces = 16;
 
 // acc += sum_p 2^(lse_p - M) o_p over np <= kFewPieces partial rows (lse at lse[p * ls], o_p
 // at po[p * os ..], lane l holding elements l, l + 64, ...); returns the sum of the weights,
