@@ -273,6 +273,16 @@ TILE_PATTERNS = (
 )
 
 
+def tile_probe_ids(rng, n_blocks: int, heads: int, team: int, n: int):
+    """Block ids for one launch of the tile-read probe: about n items (rounded down to whole
+    rounds of the heads / team head groups), item t reading head group t mod (heads / team), and
+    within each head group every block at most once, so that no tile is read twice."""
+    groups = heads // team
+    per_group = min(n // groups, n_blocks)
+    per = rng.permuted(np.tile(np.arange(n_blocks, dtype=np.int32), (groups, 1)), axis=1)[:, :per_group]
+    return np.ascontiguousarray(per.T).reshape(-1)
+
+
 def tileprobe_bench(args, torch, pkv, dev) -> int:
     """The read rate of the grouped kernels' access patterns without their arithmetic
     (pkv_probe_tile_read), beside the plain streaming read: K/V pools of 512 Ki blocks x 8 KV
@@ -295,16 +305,8 @@ def tileprobe_bench(args, torch, pkv, dev) -> int:
     results = []
 
     def id_sets(tile, scales, team):
-        groups = heads // team
-        n = target // (team * (2 * tile + (128 if scales else 0))) // groups * groups
-        out = []
-        for _ in range(4):
-            # item t takes head group t mod groups: per group, distinct blocks
-            per = rng.permuted(np.tile(np.arange(n_blocks, dtype=np.int32), (groups, 1)), axis=1)[:, :n // groups]
-            ids = np.ascontiguousarray(per.T).reshape(-1)
-            assert ids.size == n and ids.min() >= 0 and ids.max() < n_blocks
-            out.append(torch.from_numpy(ids).to(dev))
-        return out
+        n = target // (team * (2 * tile + (128 if scales else 0)))
+        return [torch.from_numpy(tile_probe_ids(rng, n_blocks, heads, team, n)).to(dev) for _ in range(4)]
 
     def launch(sets, k, tile, scales, team, paths, depth, grid):
         return pkv.probe_tile_read(kp, vp, sets[k % 4], sink, heads=heads, tile_bytes=tile, team=team, paths=paths,

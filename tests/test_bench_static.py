@@ -41,3 +41,24 @@ def _undefined_names(path):
 
 def test_bench_has_no_undefined_names():
     assert _undefined_names(os.path.join(ROOT, "bench.py")) == {}
+
+
+def test_tile_probe_ids_read_no_tile_twice():
+    """The tile-read probe's block ids: in range, whole rounds of head groups, and within each
+    head group (item t reads group t mod heads / team) every block at most once -- so a launch
+    reads each of its (block, head) tiles once and the caches cannot serve a repeat."""
+    import numpy as np
+    import bench
+
+    rng = np.random.default_rng(0)
+    for n_blocks, heads, team, n in ((1000, 8, 1, 6000), (1000, 8, 4, 1999), (300, 8, 2, 5000), (64, 6, 2, 100)):
+        ids = bench.tile_probe_ids(rng, n_blocks, heads, team, n)
+        groups = heads // team
+        assert ids.dtype == np.int32 and ids.size % groups == 0
+        assert ids.size == min(n // groups, n_blocks) * groups
+        assert ids.min() >= 0 and ids.max() < n_blocks
+        for g in range(groups):
+            mine = ids[g::groups]
+            assert np.unique(mine).size == mine.size, (n_blocks, heads, team, g)
+        tiles = ids.astype(np.int64) * heads + (np.arange(ids.size) % groups) * team   # first head of each item
+        assert np.unique(tiles).size == tiles.size
