@@ -388,6 +388,63 @@ __device__ __forceinline__ void wait_chunks(int n) {
     wait_vm<0>();
 }
 
+template <int N>
+struct SlotTag {
+    static constexpr int value = N;
+};
+// f(SlotTag<s>{}) for a wave-uniform ring slot s < R: a chain of uniform branches
+// that folds away where s is a constant, so that per-slot registers are never
+// indexed at run time
+template <int R, int N = R - 1, typename F>
+__device__ __forceinline__ void on_slot(int s, F&& f) {
+    static_assert(N >= 0 && N < R, "ring slot");
+    if constexpr (N == 0) {
+        f(SlotTag<0>{});
+    } else {
+        if (s == N) {
+            f(SlotTag<N>{});
+            return;
+        }
+        on_slot<R, N - 1>(s, f);
+    }
+}
+
+// One block's loads in flight through registers (register staging): K codes (16
+// bytes per lane, 8 for D = 64), V codes (16, or two words), the lane's scale word.
+struct Mx4Stage {
+    uint32_t k[4], v[4], s;
+};
+// Up to ten stages as named members: reached through at<I>() with a constant I,
+// never through an index, so that they stay in registers.
+struct Mx4StageRing {
+    Mx4Stage x0, x1, x2, x3, x4, x5, x6, x7, x8, x9;
+    template <int I>
+    __device__ __forceinline__ Mx4Stage& at() {
+        static_assert(I >= 0 && I < 10, "stage");
+        if constexpr (I == 0) return x0;
+        else if constexpr (I == 1) return x1;
+        else if constexpr (I == 2) return x2;
+        else if constexpr (I == 3) return x3;
+        else if constexpr (I == 4) return x4;
+        else if constexpr (I == 5) return x5;
+        else if constexpr (I == 6) return x6;
+        else if constexpr (I == 7) return x7;
+        else if constexpr (I == 8) return x8;
+        else return x9;
+    }
+};
+
+// Register staging: a block's codes and scales are loaded into registers and written
+// into its ring slot by the wave itself, at the places a DMA would have filled, once
+// the chunk's loads have landed.  At two waves per SIMD a wave stream that moves
+// every piece by global_load_lds reads markedly slower than one that loads into
+// registers (the tile-read probe), so the loads go through registers -- for one chunk
+// in flight (PF = 1); two or more do not fit beside the kernel's other registers and
+// keep the DMA.  Every load of a chunk is issued by every lane, none behind a branch:
+// the compiler counts outstanding loads exactly only then, and otherwise waits for
+// some of the next chunk's loads before writing this one (which undid the gain).
+constexpr bool kMx4RegisterStaging = true;
+
 // One block of the ring -> registers in the MFMA layout, completed before return.
 // Issued as inline asm: the compiler cannot tell this slot from the DMAs still in
 // flight into the other slots and would drain every load before a plain LDS read;
@@ -451,12 +508,14 @@ __device__ __forceinline__ void lds_block(uint32_t ka, uint32_t ksa, uint32_t va
 }
 
 // Each wave streams its blocks through a ring of R = PF + 1 LDS chunk slots, PF
-// chunks ahead of the one it computes.  A slot holds one block of the KV head: K
-// codes placed so that lane l's 16 bytes sit at 16 l (for D = 64 its two words at
-// 4 l and 256 + 4 l) -- the DMA lane that fetches them is lane l, so the read is
-// conflict-free -- then V codes, K scales and V scales in pool order.  Every DMA
-// stays inside the block's rows of this KV head; rows at or past the length are
-// masked after the read, so the last, partial block needs no other path.
+// chunks ahead of the one it computes (for PF = 1 the loads go through registers
+// and the wave writes them into the slot, kMx4RegisterStaging; deeper rings load by
+// DMA).  A slot holds one block of the KV head: K codes placed so that lane l's 16
+// bytes sit at 16 l (for D = 64 its two words at 4 l and 256 + 4 l) -- the lane that
+// fetches them is lane l, so the read is conflict-free -- then V codes, K scales and
+// V scales in pool order.  Every load stays inside the block's rows of this KV head;
+// rows at or past the length are masked after the read, so the last, partial block
+// needs no other path.
 //
 // HG: KV heads per workgroup.  Wave w streams head g0 + w % HG over blocks w / HG,
 // w / HG + NW / HG, ... of the partition, so the HG heads' 1 KiB code tiles of a
@@ -487,7 +546,8 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
     constexpr int R = PF + 1;                              // chunk slots per wave
     constexpr int CODES = kBlockSize * RB;                 // bytes of one tile of codes
     constexpr int SLOT = 2 * CODES + 2 * kBlockSize * SB;  // K codes, V codes, K scales, V scales
-    constexpr int LPB = D == 128 ? 3 : 5;                  // DMA instructions per block
+    constexpr bool RS = kMx4RegisterStaging && PF == 1;   // deeper rings do not fit the registers
+    constexpr int LPB = D == 128 ? 3 : RS ? 4 : 5;         // load instructions per block
     constexpr int LPC = CH * LPB;
     static_assert(PF * LPC < 64, "vmcnt range");
     static_assert(NW % HG == 0, "a workgroup's waves split evenly over its heads");
@@ -630,6 +690,56 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
         }
     };
 
+    // RS: R slots of CH blocks in flight through registers
+    static_assert(!RS || R * CH <= 10, "stage ring");
+    static_assert((8 * SB & (8 * SB - 1)) == 0, "scale lanes a power of two");
+    const int l_sc = lane & (8 * SB - 1);   // the scale lane this lane repeats
+    const uint8_t* sp_all = (l_sc < 4 * SB ? a.k_mx_scale : a.v_mx_scale) + (size_t)g * kBlockSize * SB +
+                            4 * (l_sc & (4 * SB - 1));
+    Mx4StageRing stg;
+    auto load_block = [&](Mx4Stage& sg, int blk) __attribute__((always_inline)) {
+        const uint64_t u = (uint32_t)__builtin_amdgcn_readfirstlane(s_ids[blk]);
+        const uint64_t co = u << 8, so = u << 4;
+        if constexpr (D == 128) {
+            const u32x4_t kk = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kp + co + kdma));
+            const u32x4_t vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vp + co + 16 * lane));
+            sg.k[0] = kk.x; sg.k[1] = kk.y; sg.k[2] = kk.z; sg.k[3] = kk.w;
+            sg.v[0] = vv.x; sg.v[1] = vv.y; sg.v[2] = vv.z; sg.v[3] = vv.w;
+        } else {   // the lane's two K words are adjacent (kdma is a multiple of 8)
+            const u32x2_t kk = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(kp + co + kdma));
+            sg.k[0] = kk.x; sg.k[1] = kk.y;
+            sg.v[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vp + co + 4 * lane));
+            sg.v[1] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vp + co + 256 + 4 * lane));
+        }
+        // every lane loads a scale word (lanes past the first 8 SB repeat theirs), so that no
+        // load sits behind a branch the compiler's wait counting must allow for
+        sg.s = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(sp_all + so));
+    };
+    auto land_block = [&](const Mx4Stage& sg, int flat) __attribute__((always_inline)) {
+        char* dst = my_ring + flat * SLOT;
+        if constexpr (D == 128) {
+            *reinterpret_cast<u32x4_t*>(dst + 16 * lane) = u32x4_t{sg.k[0], sg.k[1], sg.k[2], sg.k[3]};
+            *reinterpret_cast<u32x4_t*>(dst + CODES + 16 * lane) = u32x4_t{sg.v[0], sg.v[1], sg.v[2], sg.v[3]};
+        } else {
+            *reinterpret_cast<uint32_t*>(dst + 4 * lane) = sg.k[0];
+            *reinterpret_cast<uint32_t*>(dst + 256 + 4 * lane) = sg.k[1];
+            *reinterpret_cast<uint32_t*>(dst + CODES + 4 * lane) = sg.v[0];
+            *reinterpret_cast<uint32_t*>(dst + CODES + 256 + 4 * lane) = sg.v[1];
+        }
+        *reinterpret_cast<uint32_t*>(dst + 2 * CODES + 4 * (lane & (8 * SB - 1))) = sg.s;   // repeats: same value
+    };
+    // RS: chunk slot `slot`'s registers into its LDS blocks (the caller has waited for
+    // its loads); this wave's writes land before its reads of the slot
+    auto land = [&](int slot) __attribute__((always_inline)) {
+        on_slot<R>(slot, [&](auto tag) __attribute__((always_inline)) {
+            constexpr int s0 = decltype(tag)::value;
+            land_block(stg.template at<CH * s0>(), CH * s0);
+            if constexpr (CH == 2) land_block(stg.template at<CH * s0 + 1>(), CH * s0 + 1);
+        });
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
     auto issue_block = [&](int slot, int blk) {
         const uint64_t u = (uint32_t)__builtin_amdgcn_readfirstlane(s_ids[blk]);
         const uint64_t co = u << 8, so = u << 4;
@@ -650,11 +760,22 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
     // masked, so every chunk issues the same number of DMAs
     int nr = 0, r0_cur = 0;   // the current window: its block count and first block
     auto blk_of = [&](int i, int cb) { return wi + BW * (CH * i + cb); };
-    auto issue = [&](int slot, int i) {
+    auto issue = [&](int slot, int i) __attribute__((always_inline)) {
+        if constexpr (RS) {
+            on_slot<R>(slot, [&](auto tag) __attribute__((always_inline)) {
+                constexpr int s0 = decltype(tag)::value;
+                load_block(stg.template at<CH * s0>(), blk_of(i, 0));
+                if constexpr (CH == 2) {
+                    const int blk = blk_of(i, 1);
+                    load_block(stg.template at<CH * s0 + 1>(), blk < nr ? blk : blk_of(i, 0));
+                }
+            });
+        } else {
 #pragma unroll
-        for (int cb = 0; cb < CH; ++cb) {
-            const int blk = blk_of(i, cb);
-            issue_block(CH * slot + cb, blk < nr ? blk : blk_of(i, 0));
+            for (int cb = 0; cb < CH; ++cb) {
+                const int blk = blk_of(i, cb);
+                issue_block(CH * slot + cb, blk < nr ? blk : blk_of(i, 0));
+            }
         }
     };
     // one chunk from its slots: read, mask rows at or past lim, accumulate
@@ -670,6 +791,7 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
             nfull += tbs[cb] + kBlockSize <= lim;
         }
         const bool full = __builtin_amdgcn_readfirstlane(nfull) == CH;   // wave-uniform
+        if constexpr (RS) land(slot);
 #pragma unroll
         for (int cb = 0; cb < CH; ++cb) {
             const uint32_t base = my_ring_a + (CH * slot + cb) * SLOT;
@@ -715,6 +837,7 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
     auto stage_scores = [&](int slot, int i, int tok_r, typename L::PairStage& ps, auto mask) {
         constexpr bool MASK = decltype(mask)::value;
         Mx4Chunk<D, 2> ck;
+        if constexpr (RS) land(slot);
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
             const uint32_t base = my_ring_a + (2 * slot + cb) * SLOT;
@@ -787,12 +910,19 @@ void decode_mxfp4_mfma_kernel(const AttnArgs a) {
                 wait_chunks<LPC, PF>(min(nb - 1, PF));
                 stage_scores(0, 0, tok_r, ps[0], Flag<true>{});
             }
-            for (; i < nb; ++i) {   // the last chunks: wait for chunk i only
-                if (i + PF < nb) issue((i + PF) % R, i + PF);
-                wait_chunks<LPC, PF>(min(nb - 1 - i, PF));
-                stage_scores(i % R, i, tok_r, ps[1], Flag<true>{});
-                st.pair_finish(ps[0]);
-                ps[0] = ps[1];
+            // the last chunks, waiting for chunk i + v only; i = 1 mod R here (either branch
+            // above), so chunk i + v sits in slot (1 + v) % R and chunk i + v + PF goes to slot v
+            for (; i < nb; i += R) {
+#pragma unroll
+                for (int v = 0; v < R; ++v) {
+                    if (i + v < nb) {
+                        if (i + v + PF < nb) issue(v, i + v + PF);
+                        wait_chunks<LPC, PF>(min(nb - 1 - (i + v), PF));
+                        stage_scores((1 + v) % R, i + v, tok_r, ps[1], Flag<true>{});
+                        st.pair_finish(ps[0]);
+                        ps[0] = ps[1];
+                    }
+                }
             }
             if (nb > 0) st.pair_finish(ps[0]);
             return;
