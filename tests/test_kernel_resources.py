@@ -28,13 +28,18 @@ def test_no_kernel_uses_scratch(usage):
 
 
 def test_headline_kernels_keep_their_occupancy(usage):
-    """The kernels the five workloads' steps run, at the waves per SIMD their launch shapes
-    were measured with (registers and LDS both counted by the compiler)."""
+    """The kernels the workloads' steps run, at the waves per SIMD their launch shapes were
+    measured with (registers and LDS both counted by the compiler)."""
     want = {
         "void pkv::decode_mha_kernel<1, 128, 4, 2, 1, true>(pkv::AttnArgs)": 4,     # c2
         "void pkv::decode_mha_kernel<1, 128, 8, 2, 2, true>(pkv::AttnArgs)": 2,     # c3
         "void pkv::decode_mha_kernel<2, 128, 4, 2, 1, true>(pkv::AttnArgs)": 3,     # c4
         "void pkv::decode_gqa_kernel<2, 128, 4, 1, 1, true, true>(pkv::AttnArgs)": 2,   # c5
+        "void pkv::decode_fp8_kernel<1, 128, 4, 2, 1, true>(pkv::AttnArgs)": 3,         # c3f8
+        "void pkv::decode_gqa_fp8_kernel<2, 128, 4, 1, 1, 2, true>(pkv::AttnArgs)": 3,  # c5f8
+        "void pkv::decode_mxfp4_kernel<1, 128, 4, 2>(pkv::AttnArgs)": 3,                # c3f4 attention
+        # c5f4: the even split with its one-chunk ring staged through registers (209 VGPRs of 256)
+        "void pkv::decode_mxfp4_mfma_kernel<2, 128, 4, 1, true, true, 4, true>(pkv::AttnArgs)": 2,
     }
     for k, occ in want.items():
         assert k in usage, k
