@@ -261,13 +261,15 @@ def resident_steps(lib, torch, pkv, dev, w, append: bool, P: int, R: int):
 # tiles 64 bytes per pool; paths bit 1 / 2 / 4 moves K / V / scales by DMA into LDS; depth =
 # items in flight per wave.  The grouped MXFP4 kernel moves all three by DMA, one head per wave
 # or a team of neighbouring heads (K, or K and V, into registers beside it for comparison); the
-# FP8 kernel moves K by DMA and V and the scales into registers; the bf16 kernel has both.
+# FP8 kernel moves K by DMA and V and the scales into registers (all into registers beside it for
+# comparison); the bf16 kernel has both.
 TILE_PATTERNS = (
     ("mxfp4_registers", 1024, True, 0, (1, 4), (2, 4, 8)),
     ("mxfp4_dma", 1024, True, 7, (1, 4), (2, 4, 8)),
     ("mxfp4_k_registers", 1024, True, 6, (1, 4), (2, 4, 8)),
     ("mxfp4_kv_registers", 1024, True, 4, (1, 4), (2, 4, 8)),
     ("fp8_k_dma", 2048, True, 1, (1, 2, 4), (4,)),
+    ("fp8_registers", 2048, True, 0, (1, 4), (4,)),
     ("bf16_registers", 4096, False, 0, (1,), (4,)),
     ("bf16_k_dma", 4096, False, 1, (1,), (4,)),
 )
