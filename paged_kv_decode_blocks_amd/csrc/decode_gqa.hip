@@ -1504,6 +1504,12 @@ struct GqaLaneF8 : GqaLane<DT, D, false> {
 // of 16 rows) into a per-wave ring of R chunk slots, rows stored with an XOR
 // chunk swizzle so the MFMA-layout reads (16 rows, one chunk each) are
 // conflict-free; V and the scales stay register loads (already whole lines).
+// KDMA with register staging: each K piece is loaded into a register from the address
+// its DMA would read and written by the wave into the LDS place that DMA would fill,
+// just before the slot's MFMA-layout reads (all V, scale and K loads then go through
+// registers, which a wave streams faster than global_load_lds pieces).
+constexpr bool kFp8RegisterStaging = true;
+
 template <int DT, int D, int NW, int CH, int PF, int WPE, bool KDMA>
 __global__ __launch_bounds__(NW * 64, WPE) void decode_gqa_fp8_kernel(const AttnArgs a) {
     using L = GqaLaneF8<DT, D>;
@@ -1515,6 +1521,8 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_gqa_fp8_kernel(const Attn
     constexpr int NDMA = TILE / 1024;         // DMA instructions per tile
     constexpr int SLOT = CH * TILE;           // one chunk's K tiles
     constexpr int LPC = CH * (NDMA + 6);      // vmcnt units per chunk: K DMAs, 4 V rows, 2 scale loads
+    constexpr bool RS = KDMA && kFp8RegisterStaging && PF == 1;   // deeper rings do not fit the registers
+    static_assert(NDMA == KL, "a K piece per register of the chunk's codes");
     static_assert(R <= 4, "ring depth");
     static_assert(!KDMA || PF * LPC < 64, "vmcnt range");
     // one LDS object per ring slot, so that alias analysis can tell a read of one
@@ -1612,7 +1620,12 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_gqa_fp8_kernel(const Attn
         size_t id[CH];
 #pragma unroll
         for (int cb = 0; cb < CH; ++cb) id[cb] = (size_t)__builtin_amdgcn_readfirstlane(s_ids[cb0 + cb]);
-        if constexpr (KDMA) {   // the chunk's DMAs first: a wait that leaves later loads pending covers them
+        if constexpr (RS) {   // K pieces into registers, written into the slot when the chunk is used
+#pragma unroll
+            for (int cb = 0; cb < CH; ++cb)
+#pragma unroll
+                for (int i = 0; i < NDMA; ++i) c[cb].k[i] = ld16(kpool + id[cb] * blk_codes + kdma[i]);
+        } else if constexpr (KDMA) {   // the chunk's DMAs first: a wait that leaves later loads pending covers them
 #pragma unroll
             for (int cb = 0; cb < CH; ++cb)
 #pragma unroll
@@ -1633,6 +1646,18 @@ __global__ __launch_bounds__(NW * 64, WPE) void decode_gqa_fp8_kernel(const Attn
             if (steady) wait_vmcnt<KDMA ? PF * LPC : 0>();
             else wait_vmcnt<0>();
             const char* sl = slot_of(v);
+            if constexpr (RS) {   // lane l's piece i goes where DMA lane l of instruction i would put it
+                char* slw = slot_of(v);
+#pragma unroll
+                for (int cb = 0; cb < CH; ++cb)
+#pragma unroll
+                    for (int i = 0; i < NDMA; ++i)
+                        *reinterpret_cast<uint4*>(slw + cb * TILE + i * 1024 + 16 * lane) = c[cb].k[i];
+                // this wave's LDS writes land before its reads of the slot (in order per wave)
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
 #pragma unroll
             for (int cb = 0; cb < CH; ++cb) lds_read16x<KL>(sl + cb * TILE, kread, kc[cb]);
         } else {
